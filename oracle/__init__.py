@@ -1,0 +1,261 @@
+"""CPU oracle for the width-sharded convolution -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never does, and this
+package imports nothing from the product: the two share no code.  Inputs come
+from the seeded generators in ``spatially_sharded_cnn_amd.workloads`` (which
+hold no convolution arithmetic) or from the tests themselves.
+
+What is computed, and where it is defined:
+
+* ``conv_fwd`` / ``conv_bwd_input`` / ``conv_bwd_weight`` -- the plain
+  definitions of PyTorch ``conv2d`` and its two gradients (cross-correlation,
+  zero padding, square kernel, stride, groups), in double precision, on the
+  GLOBAL unsharded tensors, restricted to a column range.  NVIDIA blog
+  "Perception Model Training for Autonomous Vehicles with Tensor Parallelism",
+  DTensor section (placement rules of aten.convolution and
+  aten.convolution_backward): the sharded result equals the unsharded one
+  column-for-column, and grad_weight / grad_bias are partial sums.
+* ``halo_columns`` -- what the halo exchange delivers to a shard: the
+  neighbours' edge columns, zeros beyond the global edge (same blog, Figure 1:
+  a 5x5 kernel with padding 2 and stride 1 needs 2 columns from each
+  neighbour; kwkr.cn retelling, section 2.2).
+* ``reduce_partials`` -- the sum that turns _Partial gradients into
+  Replicate ones (blog, DTensor section; kwkr.cn retelling, section 2.2).
+* ``stack_forward`` / ``stack_backward`` -- a chain of the above for a
+  ConvNeXt-style convolution stack.
+
+The C part (``oracle.c``) is built with plain ``gcc -O2 -fopenmp``; ``build()``
+compiles it, and the loaders compile it once if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import pathlib
+import subprocess
+
+import numpy as np
+
+_HERE = pathlib.Path(__file__).resolve().parent
+_SRC = _HERE / "oracle.c"
+_LIB_PATH = _HERE / "liboracle.so"
+_lib = None
+
+
+def build(force: bool = True) -> pathlib.Path:
+    """Compile oracle.c into liboracle.so (plain gcc, OpenMP)."""
+    if force or not _LIB_PATH.exists() or _LIB_PATH.stat().st_mtime < _SRC.stat().st_mtime:
+        tmp = _LIB_PATH.with_suffix(".so.tmp%d" % os.getpid())
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+               "-Wall", "-Wextra", "-o", str(tmp), str(_SRC)]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I64 = ctypes.POINTER(ctypes.c_int64)
+_i = ctypes.c_int
+_l = ctypes.c_int64
+
+
+def bind(path) -> ctypes.CDLL:
+    """Load a compiled oracle library from path and declare its signatures."""
+    lib = ctypes.CDLL(str(path))
+    lib.oracle_out_size.argtypes = [_i, _i, _i, _i]
+    lib.oracle_out_size.restype = _i
+    lib.oracle_conv_fwd.argtypes = [_D, _i, _i, _i, _i, _D, _i, _i, _i, _i, _i, _D, _i, _i, _D]
+    lib.oracle_conv_fwd_at.argtypes = [_D, _i, _i, _i, _i, _D, _i, _i, _i, _i, _i, _D, _l, _I64, _D]
+    lib.oracle_conv_bwd_input.argtypes = [_D, _i, _i, _i, _i, _D, _i, _i, _i, _i, _i, _i, _i, _i, _D]
+    lib.oracle_conv_bwd_input_at.argtypes = [_D, _i, _i, _i, _i, _D, _i, _i, _i, _i, _i, _i, _l, _I64, _D]
+    lib.oracle_conv_bwd_weight.argtypes = [_D, _D, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _D, _D]
+    lib.oracle_conv_bwd_weight_at.argtypes = [_D, _D, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _l, _I64, _D]
+    for f in (lib.oracle_conv_fwd, lib.oracle_conv_fwd_at, lib.oracle_conv_bwd_input,
+              lib.oracle_conv_bwd_input_at, lib.oracle_conv_bwd_weight,
+              lib.oracle_conv_bwd_weight_at):
+        f.restype = None
+    lib.oracle_num_threads.restype = _i
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        _lib = bind(_LIB_PATH)
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(_D)
+
+
+def out_size(n_in: int, k: int, stride: int, pad: int) -> int:
+    """Output extent along one axis: floor((n_in + 2*pad - k) / stride) + 1."""
+    return (n_in + 2 * pad - k) // stride + 1
+
+
+def num_threads() -> int:
+    """Threads the C oracle runs on (OpenMP)."""
+    return int(_load().oracle_num_threads())
+
+
+def _idx(idx) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(idx, dtype=np.int64).reshape(-1, 4))
+    return a
+
+
+def conv_fwd(x, wt, bias, stride: int, pad: int, groups: int, cols=None) -> np.ndarray:
+    """Forward conv on the global input x (N, Ci, H, W); returns float64
+    (N, Co, Ho, j1 - j0) for output columns cols = (j0, j1) (default: all)."""
+    x, wt = _f64(x), _f64(wt)
+    b = None if bias is None else _f64(bias)
+    n, ci, h, w = x.shape
+    co, cig, k, k2 = wt.shape
+    assert k == k2 and cig * groups == ci and co % groups == 0
+    ho, wo = out_size(h, k, stride, pad), out_size(w, k, stride, pad)
+    j0, j1 = (0, wo) if cols is None else cols
+    y = np.empty((n, co, ho, j1 - j0), dtype=np.float64)
+    _load().oracle_conv_fwd(_p(x), n, ci, h, w, _p(wt), co, k, stride, pad, groups,
+                            _p(b), j0, j1, _p(y))
+    return y
+
+
+def conv_fwd_at(x, wt, bias, stride: int, pad: int, groups: int, idx) -> np.ndarray:
+    """Forward outputs at global positions idx (rows of (n, o, i, j))."""
+    x, wt = _f64(x), _f64(wt)
+    b = None if bias is None else _f64(bias)
+    n, ci, h, w = x.shape
+    co, _, k, _ = wt.shape
+    ix = _idx(idx)
+    out = np.empty(len(ix), dtype=np.float64)
+    _load().oracle_conv_fwd_at(_p(x), n, ci, h, w, _p(wt), co, k, stride, pad, groups,
+                               _p(b), len(ix), ix.ctypes.data_as(_I64), _p(out))
+    return out
+
+
+def conv_bwd_input(g, wt, in_shape, stride: int, pad: int, groups: int, cols=None) -> np.ndarray:
+    """grad_input from the global grad_output g (N, Co, Ho, Wo) for an input of
+    shape in_shape = (N, Ci, H, W), over input columns cols = (x0, x1)."""
+    g, wt = _f64(g), _f64(wt)
+    n, co, ho, wo = g.shape
+    _, ci, h, w = in_shape
+    k = wt.shape[2]
+    assert wt.shape[0] == co and wt.shape[1] * groups == ci
+    assert ho == out_size(h, k, stride, pad) and wo == out_size(w, k, stride, pad)
+    x0, x1 = (0, w) if cols is None else cols
+    dx = np.empty((n, ci, h, x1 - x0), dtype=np.float64)
+    _load().oracle_conv_bwd_input(_p(g), n, co, ho, wo, _p(wt), ci, h, k, stride, pad,
+                                  groups, x0, x1, _p(dx))
+    return dx
+
+
+def conv_bwd_input_at(g, wt, in_shape, stride: int, pad: int, groups: int, idx) -> np.ndarray:
+    """grad_input at global positions idx (rows of (n, c, y, x))."""
+    g, wt = _f64(g), _f64(wt)
+    n, co, ho, wo = g.shape
+    _, ci, h, w = in_shape
+    k = wt.shape[2]
+    ix = _idx(idx)
+    out = np.empty(len(ix), dtype=np.float64)
+    _load().oracle_conv_bwd_input_at(_p(g), n, co, ho, wo, _p(wt), ci, h, k, stride, pad,
+                                     groups, len(ix), ix.ctypes.data_as(_I64), _p(out))
+    return out
+
+
+def conv_bwd_weight(x, g, k: int, stride: int, pad: int, groups: int, cols=None):
+    """(grad_weight, grad_bias) summed over output columns cols = (j0, j1)
+    (default: all, i.e. the full gradient)."""
+    x, g = _f64(x), _f64(g)
+    n, ci, h, w = x.shape
+    co = g.shape[1]
+    ho, wo = out_size(h, k, stride, pad), out_size(w, k, stride, pad)
+    assert g.shape == (n, co, ho, wo)
+    j0, j1 = (0, wo) if cols is None else cols
+    gw = np.empty((co, ci // groups, k, k), dtype=np.float64)
+    gb = np.empty((co,), dtype=np.float64)
+    _load().oracle_conv_bwd_weight(_p(x), _p(g), n, ci, h, w, co, k, stride, pad, groups,
+                                   j0, j1, _p(gw), _p(gb))
+    return gw, gb
+
+
+def conv_bwd_weight_at(x, g, k: int, stride: int, pad: int, groups: int, idx, cols=None) -> np.ndarray:
+    """grad_weight at positions idx (rows of (o, c, kh, kw)) over columns cols."""
+    x, g = _f64(x), _f64(g)
+    n, ci, h, w = x.shape
+    co = g.shape[1]
+    wo = out_size(w, k, stride, pad)
+    j0, j1 = (0, wo) if cols is None else cols
+    ix = _idx(idx)
+    out = np.empty(len(ix), dtype=np.float64)
+    _load().oracle_conv_bwd_weight_at(_p(x), _p(g), n, ci, h, w, co, k, stride, pad, groups,
+                                      j0, j1, len(ix), ix.ctypes.data_as(_I64), _p(out))
+    return out
+
+
+def shard_columns(t, num_shards: int, shard: int) -> np.ndarray:
+    """Shard(3): the shard-th of num_shards equal slices of t along W."""
+    w = t.shape[3]
+    assert w % num_shards == 0
+    wl = w // num_shards
+    return t[:, :, :, shard * wl:(shard + 1) * wl]
+
+
+def halo_columns(t, num_shards: int, shard: int, hl: int, hr: int) -> np.ndarray:
+    """The halo a shard receives: columns [s*Wl - hl, s*Wl) then
+    [(s+1)*Wl, (s+1)*Wl + hr) of the global tensor t, zero where they fall
+    outside [0, W).  Returned in the compact layout (N, C, H, hl + hr)."""
+    n, c, h, w = t.shape
+    wl = w // num_shards
+    out = np.zeros((n, c, h, hl + hr), dtype=t.dtype)
+    for e in range(hl):
+        q = shard * wl - hl + e
+        if 0 <= q < w:
+            out[:, :, :, e] = t[:, :, :, q]
+    for e in range(hr):
+        q = (shard + 1) * wl + e
+        if 0 <= q < w:
+            out[:, :, :, hl + e] = t[:, :, :, q]
+    return out
+
+
+def reduce_partials(parts) -> np.ndarray:
+    """Sum of the per-shard partial gradients, in shard order, in double."""
+    acc = np.zeros(np.asarray(parts[0]).shape, dtype=np.float64)
+    for p in parts:
+        acc = acc + np.asarray(p, dtype=np.float64)
+    return acc
+
+
+# --- convolution stack (chain of the definitions above) -------------------
+
+def stack_forward(x, layers):
+    """Run a chain of convolutions on the global input.  layers is a list of
+    dicts with keys wt, b, k, stride, pad, groups.  Returns the list of layer
+    inputs acts[0..L] (acts[0] = x, acts[l+1] = output of layer l), float64."""
+    acts = [_f64(x)]
+    for L in layers:
+        acts.append(conv_fwd(acts[-1], L["wt"], L["b"], L["stride"], L["pad"], L["groups"]))
+    return acts
+
+
+def stack_backward(acts, layers, g_final):
+    """Backward through the chain seeded with g_final (grad of the last
+    output).  Returns, per layer l, (g_out_l, dx_l, gw_l, gb_l) in float64,
+    where g_out_l is the gradient arriving at layer l's output and dx_l the
+    gradient it passes to its input (dx_l == g_out_{l-1})."""
+    out = [None] * len(layers)
+    g = _f64(g_final)
+    for l in range(len(layers) - 1, -1, -1):
+        L = layers[l]
+        x = acts[l]
+        dx = conv_bwd_input(g, L["wt"], x.shape, L["stride"], L["pad"], L["groups"])
+        gw, gb = conv_bwd_weight(x, g, L["k"], L["stride"], L["pad"], L["groups"])
+        out[l] = (g, dx, gw, gb)
+        g = dx
+    return out

@@ -1,0 +1,146 @@
+"""Seeded synthetic workloads for the width-sharded convolution.
+
+This module is shared by the product's tests and benchmark and by the oracle
+side of those tests.  It holds NO convolution arithmetic: every tensor shape
+(including each grad_output shape) is written out in the tables below, and the
+only computation here is drawing seeded random numbers.
+
+Values: numpy ``default_rng(seed)`` (PCG64), float32.  Draw order within a
+workload: input X (global), then per layer (weight, bias) in chain order, then
+grad_output G (global).  Distributions: U[-1, 1] for the tiny dense case;
+otherwise activations and grad_output N(0, 1) and every weight and bias
+N(0, 0.02) (standard normal float32 draws scaled by float32 0.02).
+
+The shapes follow the pages: a (7, 3, 512, 2048) input split four ways on W
+into (7, 3, 512, 512) slices, the 5x5 / pad 2 / stride 1 halo example, and the
+(7, 3, 512, 4096) input of the 4-GPU run (NVIDIA blog "Perception Model
+Training for Autonomous Vehicles with Tensor Parallelism", DTensor section and
+results section).  The pages train on camera images that are not available;
+seeded tensors of the same shapes stand in, since the cost of the path depends
+only on shapes.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional, Tuple
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Layer:
+    """One convolution: square kernel k, stride, pad, groups, channels in/out,
+    and the global input / output shapes it maps between."""
+    name: str
+    ci: int
+    co: int
+    k: int
+    stride: int
+    pad: int
+    groups: int
+    in_shape: Tuple[int, int, int, int]    # global (N, Ci, H, W)
+    out_shape: Tuple[int, int, int, int]   # global (N, Co, Ho, Wo)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    layers: Tuple[Layer, ...]
+    num_shards: int
+    shard: int           # the shard whose share is measured
+    seed: int
+    dist: str            # "uniform" or "normal"
+    description: str
+
+    @property
+    def x_shape(self):
+        return self.layers[0].in_shape
+
+    @property
+    def g_shape(self):
+        return self.layers[-1].out_shape
+
+
+def _layer(name, ci, co, k, stride, pad, groups, in_shape, out_shape):
+    return Layer(name, ci, co, k, stride, pad, groups, tuple(in_shape), tuple(out_shape))
+
+
+def _convnext_stack(n, w):
+    # Stem 4x4/4 (3 -> 256), then per stage a depthwise 7x7 pad 3 and a 2x2/2
+    # downsample (C doubles), ending with the stage-4 depthwise conv.
+    h = 512
+    return (
+        _layer("stem", 3, 256, 4, 4, 0, 1, (n, 3, h, w), (n, 256, 128, w // 4)),
+        _layer("dw1", 256, 256, 7, 1, 3, 256, (n, 256, 128, w // 4), (n, 256, 128, w // 4)),
+        _layer("ds1", 256, 512, 2, 2, 0, 1, (n, 256, 128, w // 4), (n, 512, 64, w // 8)),
+        _layer("dw2", 512, 512, 7, 1, 3, 512, (n, 512, 64, w // 8), (n, 512, 64, w // 8)),
+        _layer("ds2", 512, 1024, 2, 2, 0, 1, (n, 512, 64, w // 8), (n, 1024, 32, w // 16)),
+        _layer("dw3", 1024, 1024, 7, 1, 3, 1024, (n, 1024, 32, w // 16), (n, 1024, 32, w // 16)),
+        _layer("ds3", 1024, 2048, 2, 2, 0, 1, (n, 1024, 32, w // 16), (n, 2048, 16, w // 32)),
+        _layer("dw4", 2048, 2048, 7, 1, 3, 2048, (n, 2048, 16, w // 32), (n, 2048, 16, w // 32)),
+    )
+
+
+WORKLOADS = {
+    "dense5x5_tiny": Workload(
+        "dense5x5_tiny",
+        (_layer("conv", 3, 8, 5, 1, 2, 1, (1, 3, 32, 64), (1, 8, 32, 64)),),
+        num_shards=4, shard=1, seed=1001, dist="uniform",
+        description="dense 5x5 s1 p2 conv 3->8 on (1,3,32,64), four 16-wide slices, 2-column halos"),
+    "dw7_c256": Workload(
+        "dw7_c256",
+        (_layer("dw", 256, 256, 7, 1, 3, 256, (7, 256, 128, 256), (7, 256, 128, 256)),),
+        num_shards=4, shard=1, seed=1002, dist="normal",
+        description="depthwise 7x7 s1 p3 C=256: shard (7,256,128,64) of a (7,256,128,256) map, 3-column halos"),
+    "dense5x5_c256": Workload(
+        "dense5x5_c256",
+        (_layer("conv", 256, 256, 5, 1, 2, 1, (7, 256, 128, 512), (7, 256, 128, 512)),),
+        num_shards=4, shard=1, seed=1003, dist="normal",
+        description="dense 5x5 s1 p2 conv 256->256: shard (7,256,128,128) of a (7,256,128,512) map, 2-column halos"),
+    "convnext_xl_w2048": Workload(
+        "convnext_xl_w2048", _convnext_stack(7, 2048),
+        num_shards=4, shard=1, seed=1004, dist="normal",
+        description="ConvNeXt-XL conv stack on shard (7,3,512,512) of a (7,3,512,2048) input"),
+    "convnext_xl_w4096": Workload(
+        "convnext_xl_w4096", _convnext_stack(7, 4096),
+        num_shards=4, shard=1, seed=1005, dist="normal",
+        description="ConvNeXt-XL conv stack on shard (7,3,512,1024) of a (7,3,512,4096) input"),
+}
+
+
+@dataclasses.dataclass
+class Tensors:
+    x: np.ndarray                  # global input (N, Ci, H, W)
+    weights: List[np.ndarray]      # per layer (Co, Ci/groups, K, K)
+    biases: List[np.ndarray]       # per layer (Co,)
+    g: np.ndarray                  # global grad of the last output
+
+
+def _draw(rng, shape, dist, scale=1.0):
+    if dist == "uniform":
+        return rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
+    a = rng.standard_normal(size=shape, dtype=np.float32)
+    if scale != 1.0:
+        a *= np.float32(scale)
+    return a
+
+
+def generate(wl: Workload, seed: Optional[int] = None) -> Tensors:
+    """Draw the workload's tensors (host, float32) from its seed."""
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    act_scale, par_scale = (1.0, 1.0) if wl.dist == "uniform" else (1.0, 0.02)
+    x = _draw(rng, wl.x_shape, wl.dist, act_scale)
+    ws, bs = [], []
+    for L in wl.layers:
+        ws.append(_draw(rng, (L.co, L.ci // L.groups, L.k, L.k), wl.dist, par_scale))
+        bs.append(_draw(rng, (L.co,), wl.dist, par_scale))
+    g = _draw(rng, wl.g_shape, wl.dist, act_scale)
+    return Tensors(x, ws, bs, g)
+
+
+def custom(name, n, ci, co, h, w, k, stride, pad, groups, ho, wo, num_shards,
+           shard=1, seed=7, dist="normal") -> Workload:
+    """A one-layer workload with explicit shapes (for parity cases that span
+    several tiles and ragged tails)."""
+    L = _layer("conv", ci, co, k, stride, pad, groups, (n, ci, h, w), (n, co, ho, wo))
+    return Workload(name, (L,), num_shards, shard, seed, dist, name)
