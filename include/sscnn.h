@@ -1,0 +1,210 @@
+/*
+ * sscnn.h -- C ABI of the width-sharded 2-D convolution library (libsscnn.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method.  A convolution's activations are split along W into S equal
+ * slices, one per shard; weight and bias are replicated on every shard (NVIDIA
+ * blog "Perception Model Training for Autonomous Vehicles with Tensor
+ * Parallelism", DTensor section: input and output Shard(3), weight and bias
+ * Replicate).  Each shard fetches the edge columns its outputs need from its
+ * two W-neighbours (the halo; same blog, Figure 1: a 5x5 kernel, padding 2,
+ * stride 1 needs 2 columns from each side), convolves its slice extended by
+ * those columns, and keeps only the columns it owns (kwkr.cn retelling,
+ * section 2.2: exchange, concatenate, convolve, crop).  In backward the
+ * grad_output is exchanged the same way, grad_input comes out sharded like the
+ * input, and grad_weight / grad_bias come out as per-shard partial sums that a
+ * reduction turns into the replicated gradient (blog, DTensor section:
+ * convolution_backward rule with _Partial grad_weight and grad_bias).
+ *
+ * This library computes ONE shard's share on one GPU.  The neighbours' slices
+ * are ordinary device buffers; halo_gather reads their edge columns where a
+ * multi-GPU run would receive them over the fabric, and partial_reduce sums
+ * the shards' partial gradients where a multi-GPU run would all-reduce them.
+ *
+ * Conventions for every call below.
+ *  - Tensors are float32, contiguous, row-major: activations NCHW, weights
+ *    OIHW with I = c_in / groups.  All tensor pointers are DEVICE pointers to
+ *    memory the caller allocated and owns; the library allocates nothing and
+ *    keeps no pointer after a call returns.  Pointers must be 16-byte aligned.
+ *  - Outputs are overwritten, never accumulated into.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *    the default stream).  A call returns after launching; results are ready
+ *    when the stream is synchronised.  Faults inside a kernel surface at that
+ *    synchronisation.
+ *  - Every call validates its arguments on the host before launching anything.
+ *    It returns SSCNN_OK (0) or a negative status; on error nothing has been
+ *    launched and no output was touched.  sscnn_last_error() gives a message
+ *    for the calling thread's most recent failure.
+ *  - No global mutable state apart from the per-thread error message: calls
+ *    may be made concurrently from several threads on different streams.
+ *  - All reductions run in a fixed order: results are bitwise reproducible
+ *    from run to run on the same device.
+ */
+#ifndef SSCNN_H
+#define SSCNN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSCNN_ABI_VERSION 1
+
+/* Status codes. */
+#define SSCNN_OK 0
+#define SSCNN_EINVAL (-1)        /* bad argument: NULL pointer, inconsistent shape, misalignment */
+#define SSCNN_EUNSUPPORTED (-2)  /* a shape the sharding method cannot express (see sscnn_conv_init) */
+#define SSCNN_EWORKSPACE (-3)    /* workspace missing or smaller than the query returned */
+#define SSCNN_EHIP (-4)          /* the HIP runtime reported an error while launching */
+
+/* Which tensor a halo is gathered for. */
+#define SSCNN_HALO_INPUT 0        /* forward input X: slices (N, c_in, h, w_local) */
+#define SSCNN_HALO_GRAD_OUTPUT 1  /* grad_output G: slices (N, c_out, h_out, w_out_local) */
+
+/*
+ * One convolution layer as seen by one shard.
+ *
+ * Caller sets the first block; sscnn_conv_init validates it and fills the
+ * derived block.  The layer is the PyTorch conv2d (cross-correlation, zero
+ * padding `pad` on all four sides of the GLOBAL image, square kernel k,
+ * stride, groups, no dilation) applied to a global input of width
+ * w_local * num_shards, whose output columns are split into num_shards equal
+ * slices of w_out_local = w_local / stride columns.
+ */
+typedef struct sscnn_conv {
+    /* set by the caller */
+    int32_t n;            /* batch */
+    int32_t c_in;         /* input channels */
+    int32_t c_out;        /* output channels */
+    int32_t h;            /* input height (never sharded) */
+    int32_t w_local;      /* input columns held by this shard */
+    int32_t k;            /* kernel size (k x k) */
+    int32_t stride;       /* stride on both axes */
+    int32_t pad;          /* zero padding on both axes */
+    int32_t groups;       /* channel groups (groups == c_in == c_out: depthwise) */
+    int32_t shard;        /* this shard's index s, 0 <= s < num_shards */
+    int32_t num_shards;   /* S */
+    /* filled by sscnn_conv_init */
+    int32_t h_out;        /* (h + 2*pad - k) / stride + 1 */
+    int32_t w_out_local;  /* w_local / stride: output columns owned by this shard */
+    int32_t halo_l;       /* input columns needed from the left neighbour:  pad */
+    int32_t halo_r;       /* input columns needed from the right neighbour: max(0, k - stride - pad) */
+    int32_t ghalo_l;      /* grad_output columns needed from the left:  (k - 1 - pad) / stride */
+    int32_t ghalo_r;      /* grad_output columns needed from the right: ceil(pad / stride) */
+} sscnn_conv_t;
+
+/*
+ * Validate a layer description and fill its derived fields.
+ * Requirements (else SSCNN_EINVAL): all sizes positive, 0 <= pad < k,
+ * c_in % groups == 0, c_out % groups == 0, 0 <= shard < num_shards,
+ * h + 2*pad >= k.  Requirements of the sharding itself (else
+ * SSCNN_EUNSUPPORTED): w_local % stride == 0; the global output width
+ * (S*w_local + 2*pad - k)/stride + 1 equals S * w_local / stride, so that
+ * output columns split evenly; every halo is no wider than one slice
+ * (halo_l, halo_r <= w_local and ghalo_l, ghalo_r <= w_out_local), since a
+ * shard only talks to its two nearest neighbours.
+ */
+int sscnn_conv_init(sscnn_conv_t *conv);
+
+/*
+ * Halo exchange, single-GPU form (blog, Figure 1 and Figure 2 text; kwkr.cn
+ * retelling, section 2.2).
+ *
+ * For which == SSCNN_HALO_INPUT the slices are (n, c_in, h, w_local) and the
+ * widths (hl, hr) = (halo_l, halo_r); for SSCNN_HALO_GRAD_OUTPUT the slices
+ * are (n, c_out, h_out, w_out_local) and the widths (ghalo_l, ghalo_r).
+ * Writes halo, shape (n, C, rows, hl + hr): per row, first the LAST hl columns
+ * of the left neighbour's slice, then the FIRST hr columns of the right
+ * neighbour's slice.  At the global edges there is no neighbour and the
+ * columns are zeros (the original zero padding): left_nbr must be NULL exactly
+ * when shard == 0 and right_nbr exactly when shard == num_shards - 1
+ * (SSCNN_EINVAL otherwise).  If hl + hr == 0 nothing is launched and halo may
+ * be NULL.
+ */
+int sscnn_halo_gather(const sscnn_conv_t *conv, int32_t which,
+                      const float *left_nbr, const float *right_nbr,
+                      float *halo, void *stream);
+
+/*
+ * Forward of this shard (blog, DTensor section: aten.convolution with input
+ * and output Shard(3); kwkr.cn retelling, sections 2.2 and 3.2).
+ *   x      (n, c_in, h, w_local)            this shard's input slice
+ *   x_halo (n, c_in, h, halo_l + halo_r)    from sscnn_halo_gather(INPUT);
+ *                                           may be NULL when both widths are 0
+ *   weight (c_out, c_in/groups, k, k)       replicated
+ *   bias   (c_out) or NULL for no bias      replicated
+ *   y      (n, c_out, h_out, w_out_local)   output: the global output's
+ *                                           columns [s*w_out_local, (s+1)*w_out_local)
+ */
+int sscnn_conv_fwd(const sscnn_conv_t *conv, const float *x, const float *x_halo,
+                   const float *weight, const float *bias, float *y, void *stream);
+
+/*
+ * grad_input of this shard (blog, DTensor section: convolution_backward with
+ * grad_output and grad_input Shard(3); kwkr.cn retelling, section 2.2).  The
+ * grad_output halo is pulled from the neighbours, so every grad_input column
+ * is finished locally and nothing is sent back.
+ *   grad_y      (n, c_out, h_out, w_out_local)        this shard's grad_output
+ *   grad_y_halo (n, c_out, h_out, ghalo_l + ghalo_r)  from sscnn_halo_gather(GRAD_OUTPUT);
+ *                                                     may be NULL when both widths are 0
+ *   weight      (c_out, c_in/groups, k, k)
+ *   grad_x      (n, c_in, h, w_local)                 output: columns
+ *                                                     [s*w_local, (s+1)*w_local) of the global grad_input
+ */
+int sscnn_conv_bwd_input(const sscnn_conv_t *conv, const float *grad_y,
+                         const float *grad_y_halo, const float *weight,
+                         float *grad_x, void *stream);
+
+/*
+ * Workspace, in bytes, that sscnn_conv_bwd_weight_partial needs for this
+ * layer (split reductions).  0 means none.  Returns 0 as well for an invalid
+ * descriptor; the call itself then reports the error.
+ */
+size_t sscnn_conv_bwd_weight_workspace_bytes(const sscnn_conv_t *conv);
+
+/*
+ * _Partial grad_weight and grad_bias of this shard (blog, DTensor section:
+ * grad_weight and grad_bias placed _Partial; kwkr.cn retelling, section 2.2):
+ * the sums over this shard's OWN output columns only, so that the partials of
+ * all shards add up to the full gradients.
+ *   x           (n, c_in, h, w_local)                   forward input slice
+ *   x_halo      (n, c_in, h, halo_l + halo_r)           the forward's input halo, reused
+ *   grad_y      (n, c_out, h_out, w_out_local)          this shard's grad_output
+ *   grad_w_part (c_out, c_in/groups, k, k)              output
+ *   grad_b_part (c_out) or NULL to skip the bias gradient  output
+ *   workspace   device scratch of workspace_bytes >= sscnn_conv_bwd_weight_workspace_bytes()
+ *               (may be NULL when that is 0); contents are scratch on return
+ */
+int sscnn_conv_bwd_weight_partial(const sscnn_conv_t *conv, const float *x,
+                                  const float *x_halo, const float *grad_y,
+                                  float *grad_w_part, float *grad_b_part,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+/*
+ * Reduction of partial gradients into the replicated gradient (blog, DTensor
+ * section: _Partial reduced to Replicate; kwkr.cn retelling, section 2.2):
+ *   out[i] = parts[0][i] + parts[1][i] + ... + parts[nparts-1][i]
+ * summed left to right in float32, for 0 <= i < count.
+ *   parts   HOST array of nparts DEVICE pointers, 1 <= nparts <= 64
+ *   out     device, count floats; may alias none of the parts
+ */
+int sscnn_partial_reduce(const float *const *parts, int32_t nparts, int64_t count,
+                         float *out, void *stream);
+
+/* Static text for a status code. */
+const char *sscnn_status_string(int status);
+
+/* Message describing the calling thread's most recent failed call ("" if none). */
+const char *sscnn_last_error(void);
+
+/* SSCNN_ABI_VERSION of the built library. */
+int sscnn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSCNN_H */

@@ -75,6 +75,8 @@ def bind(path) -> ctypes.CDLL:
               lib.oracle_conv_bwd_input_at, lib.oracle_conv_bwd_weight,
               lib.oracle_conv_bwd_weight_at):
         f.restype = None
+    lib.oracle_conv_bwd_bias.argtypes = [_D, _i, _i, _i, _i, _i, _i, _D]
+    lib.oracle_conv_bwd_bias.restype = None
     lib.oracle_num_threads.restype = _i
     return lib
 
@@ -182,6 +184,16 @@ def conv_bwd_weight(x, g, k: int, stride: int, pad: int, groups: int, cols=None)
     _load().oracle_conv_bwd_weight(_p(x), _p(g), n, ci, h, w, co, k, stride, pad, groups,
                                    j0, j1, _p(gw), _p(gb))
     return gw, gb
+
+
+def conv_bwd_bias(g, cols=None) -> np.ndarray:
+    """grad_bias over output columns cols = (j0, j1) of the global grad_output g."""
+    g = _f64(g)
+    n, co, ho, wo = g.shape
+    j0, j1 = (0, wo) if cols is None else cols
+    gb = np.empty((co,), dtype=np.float64)
+    _load().oracle_conv_bwd_bias(_p(g), n, co, ho, wo, j0, j1, _p(gb))
+    return gb
 
 
 def conv_bwd_weight_at(x, g, k: int, stride: int, pad: int, groups: int, idx, cols=None) -> np.ndarray:

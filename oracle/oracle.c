@@ -223,6 +223,15 @@ void oracle_conv_bwd_weight(const double *x, const double *g, int n, int ci,
     }
 }
 
+/* grad_bias alone (Co) over output columns [j0, j1). */
+void oracle_conv_bwd_bias(const double *g, int n, int co, int ho, int wo,
+                          int j0, int j1, double *gb)
+{
+#pragma omp parallel for
+    for (int o = 0; o < co; o++)
+        gb[o] = bwd_bias_elem(g, n, co, ho, wo, j0, j1, o);
+}
+
 /* grad_weight at listed positions idx[4*s ..] = (o, c, kh, kw), summed over
  * output columns [j0, j1). */
 void oracle_conv_bwd_weight_at(const double *x, const double *g, int n, int ci,

@@ -1,0 +1,241 @@
+// api.cpp -- the C ABI of libsscnn (declared in include/sscnn.h): host-side
+// validation of every argument, then dispatch to the kernel family that fits
+// the layer.  Nothing here allocates device memory.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+#include "kernels.h"
+
+namespace sscnn {
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_status(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return SSCNN_OK;
+    return fail(SSCNN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Derived fields of a layer; returns a status and fills *out.
+int derive(const sscnn_conv_t& c, sscnn_conv_t* out)
+{
+    if (c.n <= 0 || c.c_in <= 0 || c.c_out <= 0 || c.h <= 0 || c.w_local <= 0 || c.k <= 0 ||
+        c.stride <= 0 || c.groups <= 0 || c.num_shards <= 0)
+        return fail(SSCNN_EINVAL, "sizes must be positive (n=%d c_in=%d c_out=%d h=%d w_local=%d "
+                    "k=%d stride=%d groups=%d num_shards=%d)", c.n, c.c_in, c.c_out, c.h, c.w_local,
+                    c.k, c.stride, c.groups, c.num_shards);
+    if (c.pad < 0 || c.pad >= c.k) return fail(SSCNN_EINVAL, "pad=%d must satisfy 0 <= pad < k=%d", c.pad, c.k);
+    if (c.c_in % c.groups || c.c_out % c.groups)
+        return fail(SSCNN_EINVAL, "groups=%d must divide c_in=%d and c_out=%d", c.groups, c.c_in, c.c_out);
+    if (c.shard < 0 || c.shard >= c.num_shards)
+        return fail(SSCNN_EINVAL, "shard=%d outside [0, %d)", c.shard, c.num_shards);
+    if (c.h + 2 * c.pad < c.k) return fail(SSCNN_EINVAL, "h=%d too small for k=%d pad=%d", c.h, c.k, c.pad);
+    const int64_t elems_in = (int64_t)c.n * c.c_in * c.h * c.w_local;
+    if (elems_in > ((int64_t)1 << 40)) return fail(SSCNN_EINVAL, "tensor too large");
+    if (c.w_local % c.stride)
+        return fail(SSCNN_EUNSUPPORTED, "w_local=%d is not a multiple of stride=%d", c.w_local, c.stride);
+    const int64_t w_global = (int64_t)c.w_local * c.num_shards;
+    const int64_t wo_global = (w_global + 2 * c.pad - c.k) / c.stride + 1;
+    if (wo_global != w_global / c.stride)
+        return fail(SSCNN_EUNSUPPORTED, "global output width %lld != %lld: output columns do not "
+                    "split evenly over the shards", (long long)wo_global, (long long)(w_global / c.stride));
+    sscnn_conv_t d = c;
+    d.h_out = (c.h + 2 * c.pad - c.k) / c.stride + 1;
+    d.w_out_local = c.w_local / c.stride;
+    d.halo_l = c.pad;
+    d.halo_r = c.k - c.stride - c.pad > 0 ? c.k - c.stride - c.pad : 0;
+    d.ghalo_l = (c.k - 1 - c.pad) / c.stride;
+    d.ghalo_r = (c.pad + c.stride - 1) / c.stride;
+    if (d.halo_l > c.w_local || d.halo_r > c.w_local || d.ghalo_l > d.w_out_local ||
+        d.ghalo_r > d.w_out_local)
+        return fail(SSCNN_EUNSUPPORTED, "halo wider than one slice (halo %d/%d, grad halo %d/%d, "
+                    "w_local %d)", d.halo_l, d.halo_r, d.ghalo_l, d.ghalo_r, c.w_local);
+    *out = d;
+    return SSCNN_OK;
+}
+
+// Re-derive and compare, so a descriptor edited after sscnn_conv_init is caught.
+int check(const sscnn_conv_t* conv, Geom* g)
+{
+    if (!conv) return fail(SSCNN_EINVAL, "conv is NULL");
+    sscnn_conv_t d;
+    int st = derive(*conv, &d);
+    if (st) return st;
+    if (d.h_out != conv->h_out || d.w_out_local != conv->w_out_local || d.halo_l != conv->halo_l ||
+        d.halo_r != conv->halo_r || d.ghalo_l != conv->ghalo_l || d.ghalo_r != conv->ghalo_r)
+        return fail(SSCNN_EINVAL, "descriptor not initialised by sscnn_conv_init (or edited since)");
+    g->n = d.n; g->ci = d.c_in; g->co = d.c_out; g->h = d.h; g->wl = d.w_local; g->k = d.k;
+    g->stride = d.stride; g->pad = d.pad; g->groups = d.groups; g->ho = d.h_out;
+    g->wol = d.w_out_local; g->hl = d.halo_l; g->hr = d.halo_r; g->ghl = d.ghalo_l;
+    g->ghr = d.ghalo_r; g->cig = d.c_in / d.groups; g->cog = d.c_out / d.groups;
+    return SSCNN_OK;
+}
+
+int need(const void* p, const char* name)
+{
+    if (!p) return fail(SSCNN_EINVAL, "%s is NULL", name);
+    if (!aligned16(p)) return fail(SSCNN_EINVAL, "%s is not 16-byte aligned", name);
+    return SSCNN_OK;
+}
+
+int optional(const void* p, const char* name)
+{
+    if (p && !aligned16(p)) return fail(SSCNN_EINVAL, "%s is not 16-byte aligned", name);
+    return SSCNN_OK;
+}
+
+#define TRY(expr)                  \
+    do {                           \
+        int st_ = (expr);          \
+        if (st_) return st_;       \
+    } while (0)
+
+}  // namespace
+}  // namespace sscnn
+
+using namespace sscnn;
+
+extern "C" {
+
+int sscnn_abi_version(void) { return SSCNN_ABI_VERSION; }
+
+const char* sscnn_status_string(int status)
+{
+    switch (status) {
+        case SSCNN_OK: return "ok";
+        case SSCNN_EINVAL: return "invalid argument";
+        case SSCNN_EUNSUPPORTED: return "unsupported layer for width sharding";
+        case SSCNN_EWORKSPACE: return "workspace missing or too small";
+        case SSCNN_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* sscnn_last_error(void) { return g_last_error; }
+
+int sscnn_conv_init(sscnn_conv_t* conv)
+{
+    if (!conv) return fail(SSCNN_EINVAL, "conv is NULL");
+    sscnn_conv_t d;
+    TRY(derive(*conv, &d));
+    *conv = d;
+    return SSCNN_OK;
+}
+
+int sscnn_halo_gather(const sscnn_conv_t* conv, int32_t which, const float* left_nbr,
+                      const float* right_nbr, float* halo, void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    int64_t planes;
+    int rows, width, hl, hr;
+    if (which == SSCNN_HALO_INPUT) {
+        planes = (int64_t)g.n * g.ci; rows = g.h; width = g.wl; hl = g.hl; hr = g.hr;
+    } else if (which == SSCNN_HALO_GRAD_OUTPUT) {
+        planes = (int64_t)g.n * g.co; rows = g.ho; width = g.wol; hl = g.ghl; hr = g.ghr;
+    } else {
+        return fail(SSCNN_EINVAL, "which=%d is neither SSCNN_HALO_INPUT nor SSCNN_HALO_GRAD_OUTPUT", which);
+    }
+    const bool first = conv->shard == 0, last = conv->shard == conv->num_shards - 1;
+    if (first != (left_nbr == nullptr))
+        return fail(SSCNN_EINVAL, "left_nbr must be NULL exactly for shard 0 (shard=%d)", conv->shard);
+    if (last != (right_nbr == nullptr))
+        return fail(SSCNN_EINVAL, "right_nbr must be NULL exactly for the last shard (shard=%d)", conv->shard);
+    TRY(optional(left_nbr, "left_nbr"));
+    TRY(optional(right_nbr, "right_nbr"));
+    if (hl + hr == 0) return SSCNN_OK;
+    TRY(need(halo, "halo"));
+    return hip_status(launch_halo_gather(hl ? left_nbr : nullptr, hr ? right_nbr : nullptr, planes,
+                                         rows, width, hl, hr, halo, (hipStream_t)stream),
+                      "halo_gather launch");
+}
+
+int sscnn_conv_fwd(const sscnn_conv_t* conv, const float* x, const float* x_halo,
+                   const float* weight, const float* bias, float* y, void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    TRY(need(x, "x"));
+    if (g.hl + g.hr) TRY(need(x_halo, "x_halo")); else TRY(optional(x_halo, "x_halo"));
+    TRY(need(weight, "weight"));
+    TRY(optional(bias, "bias"));
+    TRY(need(y, "y"));
+    return hip_status(kernels_conv_fwd(g, x, x_halo, weight, bias, y, (hipStream_t)stream),
+                      "conv_fwd launch");
+}
+
+int sscnn_conv_bwd_input(const sscnn_conv_t* conv, const float* grad_y, const float* grad_y_halo,
+                         const float* weight, float* grad_x, void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    TRY(need(grad_y, "grad_y"));
+    if (g.ghl + g.ghr) TRY(need(grad_y_halo, "grad_y_halo")); else TRY(optional(grad_y_halo, "grad_y_halo"));
+    TRY(need(weight, "weight"));
+    TRY(need(grad_x, "grad_x"));
+    return hip_status(kernels_conv_bwd_input(g, grad_y, grad_y_halo, weight, grad_x,
+                                             (hipStream_t)stream),
+                      "conv_bwd_input launch");
+}
+
+size_t sscnn_conv_bwd_weight_workspace_bytes(const sscnn_conv_t* conv)
+{
+    Geom g;
+    if (check(conv, &g)) return 0;
+    return kernels_bwd_weight_workspace_bytes(g);
+}
+
+int sscnn_conv_bwd_weight_partial(const sscnn_conv_t* conv, const float* x, const float* x_halo,
+                                  const float* grad_y, float* grad_w_part, float* grad_b_part,
+                                  void* workspace, size_t workspace_bytes, void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    TRY(need(x, "x"));
+    if (g.hl + g.hr) TRY(need(x_halo, "x_halo")); else TRY(optional(x_halo, "x_halo"));
+    TRY(need(grad_y, "grad_y"));
+    TRY(need(grad_w_part, "grad_w_part"));
+    TRY(optional(grad_b_part, "grad_b_part"));
+    const size_t ws_need = kernels_bwd_weight_workspace_bytes(g);
+    if (ws_need) {
+        if (!workspace || workspace_bytes < ws_need)
+            return fail(SSCNN_EWORKSPACE, "workspace of %zu bytes given, %zu needed",
+                        workspace ? workspace_bytes : (size_t)0, ws_need);
+        TRY(need(workspace, "workspace"));
+    }
+    return hip_status(kernels_conv_bwd_weight(g, x, x_halo, grad_y, grad_w_part, grad_b_part,
+                                              ws_need ? workspace : nullptr, (hipStream_t)stream),
+                      "conv_bwd_weight_partial launch");
+}
+
+int sscnn_partial_reduce(const float* const* parts, int32_t nparts, int64_t count, float* out,
+                         void* stream)
+{
+    if (!parts) return fail(SSCNN_EINVAL, "parts is NULL");
+    if (nparts < 1 || nparts > kMaxParts)
+        return fail(SSCNN_EINVAL, "nparts=%d outside [1, %d]", nparts, kMaxParts);
+    if (count < 0) return fail(SSCNN_EINVAL, "count=%lld is negative", (long long)count);
+    if (!out) return fail(SSCNN_EINVAL, "out is NULL");
+    for (int s = 0; s < nparts; ++s) {
+        if (!parts[s]) return fail(SSCNN_EINVAL, "parts[%d] is NULL", s);
+        if (parts[s] == out) return fail(SSCNN_EINVAL, "out aliases parts[%d]", s);
+    }
+    return hip_status(launch_partial_reduce(parts, nparts, count, out, (hipStream_t)stream),
+                      "partial_reduce launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// dispatch.cpp -- choose the kernel family for a layer.
+//
+//   direct     any layer (one thread per output element)
+#include "kernels.h"
+
+namespace sscnn {
+
+hipError_t kernels_conv_fwd(const Geom& g, const float* x, const float* xh, const float* w,
+                            const float* b, float* y, hipStream_t st)
+{
+    return launch_direct_fwd(g, x, xh, w, b, y, st);
+}
+
+hipError_t kernels_conv_bwd_input(const Geom& g, const float* gy, const float* gyh,
+                                  const float* w, float* gx, hipStream_t st)
+{
+    return launch_direct_bwd_input(g, gy, gyh, w, gx, st);
+}
+
+size_t kernels_bwd_weight_workspace_bytes(const Geom& g)
+{
+    (void)g;
+    return 0;
+}
+
+hipError_t kernels_conv_bwd_weight(const Geom& g, const float* x, const float* xh,
+                                   const float* gy, float* gw, float* gb, void* ws,
+                                   hipStream_t st)
+{
+    (void)ws;
+    return launch_direct_bwd_weight(g, x, xh, gy, gw, gb, st);
+}
+
+}  // namespace sscnn

@@ -1,0 +1,44 @@
+// internal.h -- declarations shared by the host layer (api.cpp) and the
+// kernel translation units of libsscnn.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "sscnn.h"
+
+namespace sscnn {
+
+// Everything a kernel needs about one shard's layer, passed by value.
+struct Geom {
+    int n, ci, co, h, wl, k, stride, pad, groups;
+    int ho, wol;         // output rows, output columns owned by the shard
+    int hl, hr;          // input halo widths (left, right)
+    int ghl, ghr;        // grad_output halo widths (left, right)
+    int cig, cog;        // channels per group, in and out
+};
+
+// --- halo.hip ---------------------------------------------------------------
+// halo[p, r, e] for p < planes, r < rows, e < hl + hr (see sscnn_halo_gather).
+hipError_t launch_halo_gather(const float* left, const float* right, int64_t planes, int rows,
+                              int width, int hl, int hr, float* halo, hipStream_t st);
+// out[i] = sum over parts in order (see sscnn_partial_reduce).
+constexpr int kMaxParts = 64;
+hipError_t launch_partial_reduce(const float* const* parts, int nparts, int64_t count, float* out,
+                                 hipStream_t st);
+// out[i] = sum_{s < nsplit} ws[s * count + i], fixed order: the second pass of
+// a split reduction.
+hipError_t launch_split_reduce(const float* ws, int nsplit, int64_t count, float* out,
+                               hipStream_t st);
+
+// --- direct.hip: one thread per output element, any shape ----------------------
+hipError_t launch_direct_fwd(const Geom& g, const float* x, const float* xh, const float* w,
+                             const float* b, float* y, hipStream_t st);
+hipError_t launch_direct_bwd_input(const Geom& g, const float* gy, const float* gyh,
+                                   const float* w, float* gx, hipStream_t st);
+hipError_t launch_direct_bwd_weight(const Geom& g, const float* x, const float* xh,
+                                    const float* gy, float* gw, float* gb, hipStream_t st);
+
+}  // namespace sscnn

@@ -1,0 +1,220 @@
+"""Thin ctypes binding of libsscnn (include/sscnn.h).
+
+Function names are the C names without the ``sscnn_`` prefix.  This module only
+marshals arguments: it checks that each torch tensor is a contiguous float32
+CUDA/HIP tensor of the size the layer descriptor implies, passes its device
+pointer and the current stream, and turns a non-zero status into an
+exception.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback: if libsscnn.so has not been built, or the GPU is
+missing, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+from typing import Optional, Sequence
+
+_PKG = pathlib.Path(__file__).resolve().parent
+LIB_PATH = _PKG / "lib" / "libsscnn.so"
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+HALO_INPUT, HALO_GRAD_OUTPUT = 0, 1
+
+EXPORTED = (
+    "sscnn_conv_init", "sscnn_halo_gather", "sscnn_conv_fwd", "sscnn_conv_bwd_input",
+    "sscnn_conv_bwd_weight_workspace_bytes", "sscnn_conv_bwd_weight_partial",
+    "sscnn_partial_reduce", "sscnn_status_string", "sscnn_last_error", "sscnn_abi_version",
+)
+
+
+class SscnnError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status}: {detail}")
+        self.status = status
+
+
+class Conv(ctypes.Structure):
+    """Mirror of sscnn_conv_t."""
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "n", "c_in", "c_out", "h", "w_local", "k", "stride", "pad", "groups", "shard",
+        "num_shards", "h_out", "w_out_local", "halo_l", "halo_r", "ghalo_l", "ghalo_r")]
+
+    def __repr__(self):
+        return "Conv(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+    # shapes implied by the descriptor
+    @property
+    def x_shape(self):
+        return (self.n, self.c_in, self.h, self.w_local)
+
+    @property
+    def y_shape(self):
+        return (self.n, self.c_out, self.h_out, self.w_out_local)
+
+    @property
+    def w_shape(self):
+        return (self.c_out, self.c_in // self.groups, self.k, self.k)
+
+    def halo_shape(self, which: int):
+        if which == HALO_INPUT:
+            return (self.n, self.c_in, self.h, self.halo_l + self.halo_r)
+        return (self.n, self.c_out, self.h_out, self.ghalo_l + self.ghalo_r)
+
+
+_lib = None
+_vp = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m spatially_sharded_cnn_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(str(LIB_PATH))
+        P = ctypes.POINTER(Conv)
+        L.sscnn_conv_init.argtypes = [P]
+        L.sscnn_halo_gather.argtypes = [P, ctypes.c_int32, _vp, _vp, _vp, _vp]
+        L.sscnn_conv_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.sscnn_conv_bwd_input.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
+        L.sscnn_conv_bwd_weight_workspace_bytes.argtypes = [P]
+        L.sscnn_conv_bwd_weight_workspace_bytes.restype = ctypes.c_size_t
+        L.sscnn_conv_bwd_weight_partial.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.sscnn_partial_reduce.argtypes = [ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int64, _vp, _vp]
+        L.sscnn_status_string.argtypes = [ctypes.c_int]
+        L.sscnn_status_string.restype = ctypes.c_char_p
+        L.sscnn_last_error.restype = ctypes.c_char_p
+        for f in ("sscnn_conv_init", "sscnn_halo_gather", "sscnn_conv_fwd", "sscnn_conv_bwd_input",
+                  "sscnn_conv_bwd_weight_partial", "sscnn_partial_reduce", "sscnn_abi_version"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        L = lib()
+        raise SscnnError(status, where, (L.sscnn_last_error() or b"").decode() or
+                         L.sscnn_status_string(status).decode())
+
+
+def status_string(status: int) -> str:
+    return lib().sscnn_status_string(status).decode()
+
+
+def last_error() -> str:
+    return (lib().sscnn_last_error() or b"").decode()
+
+
+def abi_version() -> int:
+    return lib().sscnn_abi_version()
+
+
+def conv_init(n, c_in, c_out, h, w_local, k, stride, pad, groups, shard, num_shards) -> Conv:
+    """Build and validate a layer descriptor (sscnn_conv_init)."""
+    c = Conv(n, c_in, c_out, h, w_local, k, stride, pad, groups, shard, num_shards)
+    _check(lib().sscnn_conv_init(ctypes.byref(c)), "conv_init")
+    return c
+
+
+# --- tensor marshalling ------------------------------------------------------
+
+def _ptr(t, shape, name, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor (got {t.device})")
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name}: must be float32 (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    numel = 1
+    for d in shape:
+        numel *= d
+    if t.numel() != numel:
+        raise ValueError(f"{name}: has {t.numel()} elements, layer needs {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return getattr(stream, "cuda_stream", stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def halo_gather(conv: Conv, which: int, left_nbr, right_nbr, halo, stream=None):
+    """sscnn_halo_gather: left_nbr / right_nbr are the neighbours' slices (None
+    at a global edge); halo receives (N, C, rows, hl + hr)."""
+    if which == HALO_INPUT:
+        sl = conv.x_shape
+    else:
+        sl = conv.y_shape
+    hs = conv.halo_shape(which)
+    _check(lib().sscnn_halo_gather(ctypes.byref(conv), which,
+                                   _ptr(left_nbr, sl, "left_nbr", True),
+                                   _ptr(right_nbr, sl, "right_nbr", True),
+                                   _ptr(halo, hs, "halo", hs[3] == 0), _stream(stream)),
+           "halo_gather")
+
+
+def conv_fwd(conv: Conv, x, x_halo, weight, bias, y, stream=None):
+    hs = conv.halo_shape(HALO_INPUT)
+    _check(lib().sscnn_conv_fwd(ctypes.byref(conv), _ptr(x, conv.x_shape, "x"),
+                                _ptr(x_halo, hs, "x_halo", hs[3] == 0),
+                                _ptr(weight, conv.w_shape, "weight"),
+                                _ptr(bias, (conv.c_out,), "bias", True),
+                                _ptr(y, conv.y_shape, "y"), _stream(stream)), "conv_fwd")
+
+
+def conv_bwd_input(conv: Conv, grad_y, grad_y_halo, weight, grad_x, stream=None):
+    hs = conv.halo_shape(HALO_GRAD_OUTPUT)
+    _check(lib().sscnn_conv_bwd_input(ctypes.byref(conv), _ptr(grad_y, conv.y_shape, "grad_y"),
+                                      _ptr(grad_y_halo, hs, "grad_y_halo", hs[3] == 0),
+                                      _ptr(weight, conv.w_shape, "weight"),
+                                      _ptr(grad_x, conv.x_shape, "grad_x"), _stream(stream)),
+           "conv_bwd_input")
+
+
+def conv_bwd_weight_workspace_bytes(conv: Conv) -> int:
+    return int(lib().sscnn_conv_bwd_weight_workspace_bytes(ctypes.byref(conv)))
+
+
+def conv_bwd_weight_partial(conv: Conv, x, x_halo, grad_y, grad_w_part, grad_b_part,
+                            workspace=None, stream=None):
+    """workspace: a uint8/float CUDA tensor of at least
+    conv_bwd_weight_workspace_bytes(conv) bytes, or None when that is 0."""
+    hs = conv.halo_shape(HALO_INPUT)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib().sscnn_conv_bwd_weight_partial(
+        ctypes.byref(conv), _ptr(x, conv.x_shape, "x"), _ptr(x_halo, hs, "x_halo", hs[3] == 0),
+        _ptr(grad_y, conv.y_shape, "grad_y"), _ptr(grad_w_part, conv.w_shape, "grad_w_part"),
+        _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True), ws_ptr, ws_bytes, _stream(stream)),
+        "conv_bwd_weight_partial")
+
+
+def partial_reduce(parts: Sequence, out, stream=None):
+    """sscnn_partial_reduce: out = parts[0] + parts[1] + ... (in order)."""
+    n = out.numel()
+    ptrs = (_vp * len(parts))(*[_ptr(p, (n,), f"parts[{i}]") for i, p in enumerate(parts)])
+    _check(lib().sscnn_partial_reduce(ptrs, len(parts), n, _ptr(out, (n,), "out"), _stream(stream)),
+           "partial_reduce")
+
+
+def new_workspace(conv: Conv, device="cuda"):
+    """Allocate (with torch) the bwd-weight workspace a layer needs, or None."""
+    nbytes = conv_bwd_weight_workspace_bytes(conv)
+    if nbytes == 0:
+        return None
+    import torch
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)

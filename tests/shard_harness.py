@@ -1,0 +1,81 @@
+"""Helpers for the GPU parity tests: run one shard's share of a layer through
+the C ABI and fetch the results, and compare against the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from spatially_sharded_cnn_amd import sscnn
+
+DEV = "cuda"
+
+
+def to_dev(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").numpy()
+
+
+def slices(a: np.ndarray, num_shards: int):
+    """Shard(3): the num_shards contiguous W-slices of a global host array, as
+    separately allocated device buffers (one per shard, as on separate GPUs)."""
+    w = a.shape[3]
+    wl = w // num_shards
+    return [to_dev(a[:, :, :, s * wl:(s + 1) * wl]) for s in range(num_shards)]
+
+
+def layer_conv(L, num_shards: int, shard: int) -> sscnn.Conv:
+    n, ci, h, w = L.in_shape
+    return sscnn.conv_init(n, ci, L.co, h, w // num_shards, L.k, L.stride, L.pad, L.groups,
+                           shard, num_shards)
+
+
+def run_shard(L, num_shards: int, shard: int, x_sl, g_sl, wt: torch.Tensor, b, stream=None):
+    """One shard's unit: halo_gather(X), conv_fwd, halo_gather(G),
+    conv_bwd_input, conv_bwd_weight_partial.  x_sl / g_sl are the lists of all
+    shards' device slices (the neighbours supply the halos)."""
+    c = layer_conv(L, num_shards, shard)
+    left = (lambda sl: sl[shard - 1] if shard > 0 else None)
+    right = (lambda sl: sl[shard + 1] if shard < num_shards - 1 else None)
+    xh = torch.empty(c.halo_shape(sscnn.HALO_INPUT), device=DEV)
+    gh = torch.empty(c.halo_shape(sscnn.HALO_GRAD_OUTPUT), device=DEV)
+    y = torch.empty(c.y_shape, device=DEV)
+    dx = torch.empty(c.x_shape, device=DEV)
+    gw = torch.empty(c.w_shape, device=DEV)
+    gb = torch.empty((c.c_out,), device=DEV)
+    ws = sscnn.new_workspace(c)
+    sscnn.halo_gather(c, sscnn.HALO_INPUT, left(x_sl), right(x_sl), xh, stream)
+    sscnn.conv_fwd(c, x_sl[shard], xh, wt, b, y, stream)
+    sscnn.halo_gather(c, sscnn.HALO_GRAD_OUTPUT, left(g_sl), right(g_sl), gh, stream)
+    sscnn.conv_bwd_input(c, g_sl[shard], gh, wt, dx, stream)
+    sscnn.conv_bwd_weight_partial(c, x_sl[shard], xh, g_sl[shard], gw, gb, ws, stream)
+    return dict(conv=c, x_halo=xh, y=y, g_halo=gh, dx=dx, gw=gw, gb=gb)
+
+
+def normwise_error(got, ref) -> float:
+    """max |got - ref| / max |ref| (inf for non-finite values)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    if scale == 0.0:
+        return 0.0 if err == 0.0 else float("inf")
+    return err / scale
+
+
+def assert_close(got, ref, tol, what):
+    e = normwise_error(got, ref)
+    assert e <= tol, f"{what}: normwise error {e:.3e} > {tol:.0e}"
+    return e
+
+
+# Tolerances (normwise, relative to max |ref|): forward and grad_input 1e-5,
+# grad_weight / grad_bias 1e-4 (long float32 reductions).
+TOL_FWD = 1e-5
+TOL_DX = 1e-5
+TOL_GW = 1e-4

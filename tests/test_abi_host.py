@@ -1,0 +1,187 @@
+"""Host-side tests of the C ABI (no GPU needed, no kernel is launched).
+
+* the library loads and exports every function include/sscnn.h declares;
+* sscnn_conv_init derives the halo widths the pages give (5x5 / pad 2 /
+  stride 1 -> 2 columns each side: NVIDIA blog "Perception Model Training for
+  Autonomous Vehicles with Tensor Parallelism", Figure 1 text) and, for every
+  other layer kind, the widths a brute-force enumeration of the taps gives;
+* every call validates its arguments before launching and reports errors.
+"""
+import ctypes
+import json
+import pathlib
+import re
+
+import pytest
+
+from spatially_sharded_cnn_amd import sscnn
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "sscnn.h"
+GOLDEN = ROOT / "tests" / "golden" / "page_facts.json"
+
+
+def _declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sscnn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = sscnn.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(L, name), f"{name} declared in sscnn.h but not exported"
+    assert set(declared) == set(sscnn.EXPORTED)
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define SSCNN_ABI_VERSION (\d+)", HEADER.read_text())
+    assert sscnn.abi_version() == int(m.group(1))
+
+
+def test_status_codes_match_header():
+    text = HEADER.read_text()
+    for name, val in [("SSCNN_OK", 0), ("SSCNN_EINVAL", -1), ("SSCNN_EUNSUPPORTED", -2),
+                      ("SSCNN_EWORKSPACE", -3), ("SSCNN_EHIP", -4)]:
+        assert re.search(rf"#define {name} \(?{val}\)?", text), name
+    assert sscnn.status_string(0) == "ok"
+    assert "invalid" in sscnn.status_string(-1)
+
+
+def _brute_force_halos(k, s, p, wl, num_shards=3, shard=1):
+    """Columns outside the shard that its outputs read (forward), and
+    grad_output columns outside its output range that its grad_input reads."""
+    w = wl * num_shards
+    wo = (w + 2 * p - k) // s + 1
+    wol = wo // num_shards
+    lo_in, hi_in = shard * wl, (shard + 1) * wl
+    reads = set()
+    for j in range(shard * wol, (shard + 1) * wol):
+        for kw in range(k):
+            reads.add(j * s + kw - p)
+    hl = max([lo_in - q for q in reads if q < lo_in] + [0])
+    hr = max([q - hi_in + 1 for q in reads if q >= hi_in] + [0])
+    greads = set()
+    for x in range(lo_in, hi_in):
+        for kw in range(k):
+            u = x + p - kw
+            if u % s == 0:
+                greads.add(u // s)
+    lo_o, hi_o = shard * wol, (shard + 1) * wol
+    ghl = max([lo_o - j for j in greads if j < lo_o] + [0])
+    ghr = max([j - hi_o + 1 for j in greads if j >= hi_o] + [0])
+    return hl, hr, ghl, ghr
+
+
+@pytest.mark.parametrize("k,s,p", [(5, 1, 2), (7, 1, 3), (3, 1, 1), (1, 1, 0), (4, 4, 0),
+                                   (2, 2, 0), (3, 2, 1), (5, 2, 2), (6, 2, 2)])
+def test_conv_init_halo_widths_match_brute_force(k, s, p):
+    wl = 8 * s
+    c = sscnn.conv_init(2, 4, 6, 10, wl, k, s, p, 1, 1, 3)
+    assert (c.halo_l, c.halo_r, c.ghalo_l, c.ghalo_r) == _brute_force_halos(k, s, p, wl)
+    assert c.w_out_local == wl // s
+    assert c.h_out == (10 + 2 * p - k) // s + 1
+
+
+def test_conv_init_matches_page_example():
+    facts = json.loads(GOLDEN.read_text())
+    for ex in facts["halo_examples"]:
+        c = sscnn.conv_init(1, 3, 8, 32, 16, ex["kernel"], ex["stride"], ex["pad"], 1, 1, 4)
+        n = ex["halo_columns_each_side"]
+        assert (c.halo_l, c.halo_r) == (n, n)
+        assert (c.ghalo_l, c.ghalo_r) == (n, n)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 3, 8, 8, 16, 5, 1, 5, 1, 0, 2), sscnn.EINVAL),        # pad >= k
+    ((1, 3, 8, 8, 16, 5, 1, 2, 2, 0, 2), sscnn.EINVAL),        # groups does not divide c_in
+    ((1, 4, 8, 8, 16, 5, 1, 2, 1, 2, 2), sscnn.EINVAL),        # shard out of range
+    ((0, 4, 8, 8, 16, 5, 1, 2, 1, 0, 2), sscnn.EINVAL),        # empty batch
+    ((1, 4, 8, 2, 16, 7, 1, 1, 1, 0, 2), sscnn.EINVAL),        # image smaller than kernel
+    ((1, 4, 8, 8, 15, 2, 2, 0, 1, 0, 2), sscnn.EUNSUPPORTED),  # w_local % stride
+    ((1, 4, 8, 8, 2, 7, 1, 3, 1, 0, 2), sscnn.EUNSUPPORTED),   # halo wider than a slice
+    ((1, 4, 8, 8, 16, 3, 2, 0, 1, 0, 2), sscnn.EUNSUPPORTED),  # output columns do not split evenly
+    ((1, 4, 8, 8, 16, 5, 1, 0, 1, 0, 2), sscnn.EUNSUPPORTED),  # 'valid' conv shrinks W
+])
+def test_conv_init_rejects(args, status):
+    with pytest.raises(sscnn.SscnnError) as ei:
+        sscnn.conv_init(*args)
+    assert ei.value.status == status
+    assert sscnn.last_error()
+
+
+# Raw calls with fake, never-dereferenced device addresses: every case below
+# fails validation before anything is launched.
+FAKE = 0x10000
+
+
+def _conv(shard=1, num_shards=4):
+    return sscnn.conv_init(1, 3, 8, 32, 16, 5, 1, 2, 1, shard, num_shards)
+
+
+def test_calls_reject_null_and_misaligned_pointers():
+    L = sscnn.lib()
+    c = _conv()
+    r = ctypes.byref(c)
+    assert L.sscnn_conv_fwd(r, None, FAKE, FAKE, None, FAKE, None) == sscnn.EINVAL
+    assert L.sscnn_conv_fwd(r, FAKE, None, FAKE, None, FAKE, None) == sscnn.EINVAL  # halo needed
+    assert L.sscnn_conv_fwd(r, FAKE + 4, FAKE, FAKE, None, FAKE, None) == sscnn.EINVAL
+    assert "aligned" in sscnn.last_error()
+    assert L.sscnn_conv_fwd(None, FAKE, FAKE, FAKE, None, FAKE, None) == sscnn.EINVAL
+    assert L.sscnn_conv_bwd_input(r, FAKE, None, FAKE, FAKE, None) == sscnn.EINVAL
+    assert L.sscnn_conv_bwd_input(r, FAKE, FAKE, None, FAKE, None) == sscnn.EINVAL
+    assert L.sscnn_conv_bwd_weight_partial(r, FAKE, FAKE, FAKE, None, None, None, 0, None) == sscnn.EINVAL
+    assert L.sscnn_conv_bwd_weight_partial(r, FAKE, FAKE, FAKE, FAKE, FAKE + 8, None, 0, None) == sscnn.EINVAL
+
+
+def test_halo_gather_neighbour_rules():
+    L = sscnn.lib()
+    first, mid, last = _conv(0), _conv(1), _conv(3)
+    # shard 0 has no left neighbour, the last shard no right one
+    assert L.sscnn_halo_gather(ctypes.byref(first), 0, FAKE, FAKE, FAKE, None) == sscnn.EINVAL
+    assert L.sscnn_halo_gather(ctypes.byref(mid), 0, None, FAKE, FAKE, None) == sscnn.EINVAL
+    assert L.sscnn_halo_gather(ctypes.byref(mid), 0, FAKE, None, FAKE, None) == sscnn.EINVAL
+    assert L.sscnn_halo_gather(ctypes.byref(last), 0, FAKE, FAKE, FAKE, None) == sscnn.EINVAL
+    assert L.sscnn_halo_gather(ctypes.byref(mid), 7, FAKE, FAKE, FAKE, None) == sscnn.EINVAL
+    assert L.sscnn_halo_gather(ctypes.byref(mid), 0, FAKE, FAKE, None, None) == sscnn.EINVAL
+
+
+def test_patchify_layer_needs_no_halo_and_launches_nothing_for_it():
+    L = sscnn.lib()
+    c = sscnn.conv_init(1, 3, 16, 16, 16, 4, 4, 0, 1, 1, 4)
+    assert (c.halo_l, c.halo_r, c.ghalo_l, c.ghalo_r) == (0, 0, 0, 0)
+    # zero-width halo: returns OK without launching (halo may be NULL)
+    assert L.sscnn_halo_gather(ctypes.byref(c), 0, FAKE, FAKE, None, None) == sscnn.OK
+
+
+def test_edited_descriptor_is_rejected():
+    L = sscnn.lib()
+    c = _conv()
+    c.halo_l = 3   # derived field no longer matches the layer
+    assert L.sscnn_conv_fwd(ctypes.byref(c), FAKE, FAKE, FAKE, None, FAKE, None) == sscnn.EINVAL
+    assert "sscnn_conv_init" in sscnn.last_error()
+    assert L.sscnn_conv_bwd_weight_workspace_bytes(ctypes.byref(c)) == 0
+
+
+def test_partial_reduce_validation():
+    L = sscnn.lib()
+    vp = ctypes.c_void_p
+    ptrs = (vp * 2)(FAKE, FAKE + 4096)
+    assert L.sscnn_partial_reduce(None, 2, 16, FAKE + 8192, None) == sscnn.EINVAL
+    assert L.sscnn_partial_reduce(ptrs, 0, 16, FAKE + 8192, None) == sscnn.EINVAL
+    assert L.sscnn_partial_reduce(ptrs, 65, 16, FAKE + 8192, None) == sscnn.EINVAL
+    assert L.sscnn_partial_reduce(ptrs, 2, -1, FAKE + 8192, None) == sscnn.EINVAL
+    assert L.sscnn_partial_reduce(ptrs, 2, 16, None, None) == sscnn.EINVAL
+    assert L.sscnn_partial_reduce(ptrs, 2, 16, FAKE, None) == sscnn.EINVAL   # aliasing
+    nulls = (vp * 2)(FAKE, None)
+    assert L.sscnn_partial_reduce(nulls, 2, 16, FAKE + 8192, None) == sscnn.EINVAL
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    c = _conv()
+    x = torch.zeros(c.x_shape)
+    with pytest.raises(ValueError):
+        sscnn.conv_fwd(c, x, None, None, None, None)

@@ -220,6 +220,9 @@ def test_bias_grad_closed_form(case):
     n, ci, co, h, w, k, s, p, g = case
     _, gb = oracle.conv_bwd_weight(x, gy, k, s, p, g)
     _close(gb, gy.sum(axis=(0, 2, 3)))
+    wo = gy.shape[3]
+    _close(oracle.conv_bwd_bias(gy), gb)
+    _close(oracle.conv_bwd_bias(gy, cols=(1, wo)), gy[..., 1:].sum(axis=(0, 2, 3)))
 
 
 @pytest.mark.parametrize("d", [-2, -1, 0, 1, 2])
