@@ -1,25 +1,30 @@
 // dispatch.cpp -- choose the kernel family for a layer.
 //
-//   direct     any layer (one thread per output element)
+//   depthwise  groups == channels, stride 1, k in {3,5,7}, pad k/2, w_local % 16 == 0
+//   direct     any other layer (one thread per output element)
 #include "kernels.h"
+
+#include "depthwise.h"
 
 namespace sscnn {
 
 hipError_t kernels_conv_fwd(const Geom& g, const float* x, const float* xh, const float* w,
                             const float* b, float* y, hipStream_t st)
 {
+    if (dw_supported(g)) return launch_dw_fwd(g, x, xh, w, b, y, st);
     return launch_direct_fwd(g, x, xh, w, b, y, st);
 }
 
 hipError_t kernels_conv_bwd_input(const Geom& g, const float* gy, const float* gyh,
                                   const float* w, float* gx, hipStream_t st)
 {
+    if (dw_supported(g)) return launch_dw_bwd_input(g, gy, gyh, w, gx, st);
     return launch_direct_bwd_input(g, gy, gyh, w, gx, st);
 }
 
 size_t kernels_bwd_weight_workspace_bytes(const Geom& g)
 {
-    (void)g;
+    if (dw_supported(g)) return dw_wgrad_workspace_bytes(g);
     return 0;
 }
 
@@ -27,7 +32,7 @@ hipError_t kernels_conv_bwd_weight(const Geom& g, const float* x, const float* x
                                    const float* gy, float* gw, float* gb, void* ws,
                                    hipStream_t st)
 {
-    (void)ws;
+    if (dw_supported(g)) return launch_dw_bwd_weight(g, x, xh, gy, gw, gb, ws, st);
     return launch_direct_bwd_weight(g, x, xh, gy, gw, gb, st);
 }
 

@@ -17,13 +17,16 @@ namespace sscnn {
 namespace {
 
 // One thread per halo element; consecutive threads write consecutive halo
-// floats (fully coalesced writes).  Reads touch hl (or hr) contiguous floats
-// per row of the neighbour.
+// floats (fully coalesced writes).  For the common widths hl + hr is a
+// template constant (HW), so the row / column split is a multiply-shift;
+// HW == 0 takes the width at run time.  Reads touch hl (or hr) contiguous
+// floats per row of the neighbour.
+template <int HW>
 __global__ void __launch_bounds__(256)
 halo_gather_kernel(const float* __restrict__ left, const float* __restrict__ right,
-                   int64_t total_rows, int width, int hl, int hr, float* __restrict__ halo)
+                   int64_t total_rows, int width, int hl, int hw_rt, float* __restrict__ halo)
 {
-    const int hw = hl + hr;
+    const int hw = HW ? HW : hw_rt;
     const int64_t total = total_rows * hw;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
          t += (int64_t)gridDim.x * blockDim.x) {
@@ -96,10 +99,21 @@ hipError_t launch_halo_gather(const float* left, const float* right, int64_t pla
                               int width, int hl, int hr, float* halo, hipStream_t st)
 {
     const int64_t total_rows = planes * rows;
-    const int64_t total = total_rows * (hl + hr);
-    if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL(halo_gather_kernel, dim3(grid_for(total, 256)), dim3(256), 0, st, left,
-                       right, total_rows, width, hl, hr, halo);
+    if (total_rows == 0 || hl + hr == 0) return hipSuccess;
+    const int hw = hl + hr;
+    const int grid = grid_for(total_rows * hw, 256);
+    switch (hw) {
+#define SSCNN_HALO_CASE(HW)                                                                  \
+    case HW:                                                                                 \
+        hipLaunchKernelGGL(halo_gather_kernel<HW>, dim3(grid), dim3(256), 0, st, left, right, \
+                           total_rows, width, hl, hw, halo);                                 \
+        break;
+        SSCNN_HALO_CASE(2) SSCNN_HALO_CASE(4) SSCNN_HALO_CASE(6)
+#undef SSCNN_HALO_CASE
+        default:
+            hipLaunchKernelGGL(halo_gather_kernel<0>, dim3(grid), dim3(256), 0, st, left, right,
+                               total_rows, width, hl, hw, halo);
+    }
     return hipGetLastError();
 }
 

@@ -11,6 +11,31 @@
 
 namespace sscnn {
 
+// Workgroup barrier for LDS hand-offs only.  The fences are scoped to the
+// workgroup AND to the LDS address space, so they order LDS accesses around
+// s_barrier (and wait for this wave's LDS operations) without the global
+// memory part of __syncthreads()'s fences, which would also wait for every
+// outstanding global load and store -- including prefetches meant to stay in
+// flight across the barrier.  Use it only where the waves exchange data
+// through LDS and not through global memory.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Read-only data that every lane of a wave reads at the same address (a
+// plane's filter taps, a bias): viewed through the constant address space,
+// such loads become scalar-cache loads (s_load), which complete on their own
+// counter and never wait behind the wave's outstanding vector loads.  Only
+// for buffers the kernel does not write.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* as_const(const T* p)
+{
+    return (const __attribute__((address_space(4))) T*)(p);
+}
+
 // Everything a kernel needs about one shard's layer, passed by value.
 struct Geom {
     int n, ci, co, h, wl, k, stride, pad, groups;

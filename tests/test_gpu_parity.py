@@ -35,6 +35,12 @@ SMALL = [
     ("dw7_ragged", 2, 37, 37, 45, 4 * 50, 7, 1, 3, 37, 4),
     ("dw7_single_shard", 1, 16, 16, 20, 64, 7, 1, 3, 16, 1),
     ("dw3_two_shards", 2, 10, 10, 7, 2 * 9, 3, 1, 1, 10, 2),
+    ("dw7_coltiles_raggedrows", 2, 19, 19, 45, 3 * 128, 7, 1, 3, 19, 3),
+    ("dw7_h130", 1, 6, 6, 130, 2 * 64, 7, 1, 3, 6, 2),
+    ("dw5_w32", 1, 8, 8, 70, 2 * 32, 5, 1, 2, 8, 2),
+    ("dw3_w16", 2, 5, 5, 17, 4 * 16, 3, 1, 1, 5, 4),
+    ("dw7_w48", 1, 7, 7, 33, 3 * 48, 7, 1, 3, 7, 3),
+    ("dw7_w256", 1, 4, 4, 20, 2 * 256, 7, 1, 3, 4, 2),
     ("dense5x5_ragged", 2, 40, 72, 13, 3 * 37, 5, 1, 2, 1, 3),
     ("dense5x5_tiles", 1, 64, 64, 20, 2 * 96, 5, 1, 2, 1, 2),
     ("dense3x3", 2, 24, 40, 9, 2 * 30, 3, 1, 1, 1, 2),
