@@ -42,6 +42,9 @@ SMALL = [
     ("dw7_w48", 1, 7, 7, 33, 3 * 48, 7, 1, 3, 7, 3),
     ("dw7_w256", 1, 4, 4, 20, 2 * 256, 7, 1, 3, 4, 2),
     ("dense5x5_ragged", 2, 40, 72, 13, 3 * 37, 5, 1, 2, 1, 3),
+    ("mfma5x5_ragged_channels", 2, 44, 72, 13, 3 * 36, 5, 1, 2, 1, 3),
+    ("mfma5x5_two_segments", 1, 16, 20, 6, 2 * 132, 5, 1, 2, 1, 2),
+    ("mfma3x3_c96_c128", 1, 96, 128, 9, 2 * 64, 3, 1, 1, 1, 2),
     ("dense5x5_tiles", 1, 64, 64, 20, 2 * 96, 5, 1, 2, 1, 2),
     ("dense3x3", 2, 24, 40, 9, 2 * 30, 3, 1, 1, 1, 2),
     ("stem4x4s4", 2, 3, 64, 32, 4 * 64, 4, 4, 0, 1, 4),
