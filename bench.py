@@ -4,32 +4,49 @@
 One step is one pass of the whole path for the measured shard (shard 1 of 4)
 of a layer: halo_gather(X) -> conv_fwd -> halo_gather(G) -> conv_bwd_input ->
 conv_bwd_weight_partial -> partial_reduce (grad_weight and grad_bias of the
-four shards).  Inputs are seeded synthetic tensors already resident in HBM;
-each step uses the next of several independent buffer sets so that the
-256 MB last-level cache cannot serve one step's data to the next.
+four shards, one call over a contiguous [gW | gB] buffer).  Inputs are seeded
+synthetic tensors already resident in HBM; each step uses the next of several
+independent buffer sets so that the 256 MB last-level cache cannot hand one
+step's data to the next.
 
 Prints ONE JSON line.  `value` is the algorithmic GB/s of a step:
-  forward  X_ext + W + b + Y
-  backward G_ext + X_ext + W + dX + gW + gB
-  reduce   (S + 1) * (|gW| + |gB|)
+  forward   X_ext + W + b + Y
+  backward  G_ext + X_ext + W + dX + gW + gB
+  reduce    (S + 1) * (|gW| + |gB|)
 (halo copies are inside the timed step but not counted as useful bytes).
+
+`roofline` is for the dominant operation of the step, timed on its own over
+back-to-back calls with events on the stream the kernels run on; its bound is
+whichever of HBM bytes / 8 TB/s and FLOPs / compute peak is larger, with the
+compute peak of the unit it runs on: the FP32 matrix cores (157.3 TFLOP/s)
+for the dense layers, the FP32 vector FMA (78.6 TFLOP/s: 256 CUs x 4 SIMDs x
+16 lanes x 2 FLOP x 2.4 GHz; the library is built without packed FP32 math)
+for the depthwise ones.
+
+    python bench.py [--workload dw7_c256|dense5x5_c256|dense5x5_tiny] [--steps K] [--warmup W]
+    python bench.py --summarize DIR   # text summary of a rocprofv3 output directory
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import pathlib
 import platform
 import sys
 import time
 
 import numpy as np
 
+ROOT = pathlib.Path(__file__).resolve().parent
 METRIC = "W-shard conv fwd+bwd GB/s & TFLOP/s FP32; % of HBM/MFMA roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X dense FP32 matrix
-# FP32 vector FMA without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz.
-VALU_F32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+VALU_F32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12   # 78.6, non-packed FP32 FMA
+COPY_CAL_BYTES = 256 << 20       # plain device copy used to calibrate FETCH_SIZE / WRITE_SIZE
 
 
 def _parse():
@@ -40,12 +57,41 @@ def _parse():
     ap.add_argument("--workload", default="dw7_c256",
                     help="dw7_c256 (default), dense5x5_c256 or dense5x5_tiny")
     ap.add_argument("--sets", type=int, default=3, help="independent buffer sets rotated per step")
+    ap.add_argument("--op-reps", type=int, default=20, help="back-to-back calls per operation timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR", help="summarize a rocprofv3 output directory and exit")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """Hash of the library sources: a recorded traffic figure is valid only for it."""
+    h = hashlib.sha256()
+    for p in sorted((ROOT / "spatially_sharded_cnn_amd" / "csrc").glob("*")):
+        if p.suffix in (".hip", ".cpp", ".h"):
+            h.update(p.name.encode())
+            h.update(p.read_bytes())
+    h.update((ROOT / "include" / "sscnn.h").read_bytes())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """Counter-measured HBM bytes per launch of the dominant operation, from
+    profiles/traffic_<workload>.md, if recorded for the current sources."""
+    p = ROOT / "profiles" / f"traffic_{workload}.md"
+    if not p.exists():
+        return None
+    for line in p.read_text().splitlines():
+        if line.startswith("traffic_json:"):
+            rec = json.loads(line.split(":", 1)[1])
+            if rec.get("source_hash") == kernel_source_hash():
+                return rec
+    return None
 
 
 def main():
     args = _parse()
+    if args.summarize:
+        return summarize(args.summarize)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU's share of the sharded path; --gpus {args.gpus} "
@@ -70,19 +116,28 @@ def main():
         w = a.shape[3] // S
         return np.ascontiguousarray(a[:, :, :, i * w:(i + 1) * w])
 
-    c = sscnn.conv_init(L.in_shape[0], L.ci, L.co, L.in_shape[2], L.in_shape[3] // S, L.k, L.stride,
-                        L.pad, L.groups, s, S)
+    def conv_of(i):
+        return sscnn.conv_init(L.in_shape[0], L.ci, L.co, L.in_shape[2], L.in_shape[3] // S, L.k,
+                               L.stride, L.pad, L.groups, i, S)
+
+    c = conv_of(s)
     left, right = s - 1 if s > 0 else None, s + 1 if s < S - 1 else None
     wt = torch.from_numpy(T.weights[0]).to(dev)
     b = torch.from_numpy(T.biases[0]).to(dev)
+    nw, nb = int(np.prod(c.w_shape)), c.c_out
 
     def dev_of(a):
         return torch.from_numpy(a).to(dev)
 
+    def grads():
+        buf = torch.empty(nw + nb, device=dev)      # [gW | gB], reduced with one call
+        return buf, buf[:nw].view(c.w_shape), buf[nw:]
+
     xs_h = {i: shard_of(T.x, i) for i in range(S)}
     gs_h = {i: shard_of(T.g, i) for i in range(S)}
     sets = []
-    for k in range(args.sets):
+    for _ in range(args.sets):
+        gbuf, gw, gb = grads()
         st = dict(
             x=dev_of(xs_h[s]), g=dev_of(gs_h[s]),
             xl=dev_of(xs_h[left]) if left is not None else None,
@@ -92,63 +147,59 @@ def main():
             xh=torch.empty(c.halo_shape(sscnn.HALO_INPUT), device=dev),
             gh=torch.empty(c.halo_shape(sscnn.HALO_GRAD_OUTPUT), device=dev),
             y=torch.empty(c.y_shape, device=dev), dx=torch.empty(c.x_shape, device=dev),
-            gw=torch.empty(c.w_shape, device=dev), gb=torch.empty((c.c_out,), device=dev),
-            gw_red=torch.empty(c.w_shape, device=dev), gb_red=torch.empty((c.c_out,), device=dev),
+            gbuf=gbuf, gw=gw, gb=gb, red=torch.empty(nw + nb, device=dev),
         )
         sets.append(st)
     ws = sscnn.new_workspace(c)
     del xs_h, gs_h
 
-    # The other shards' partial gradients (computed once, untimed): partial_reduce
-    # sums all four in shard order, this shard's fresh partial in its slot.
-    other_gw, other_gb = {}, {}
+    # The other shards' partial gradients (computed once, untimed): the step's
+    # partial_reduce sums all four in shard order, this shard's fresh partial in its slot.
+    others = {}
     for i in range(S):
         if i == s:
             continue
-        ci_ = sscnn.conv_init(L.in_shape[0], L.ci, L.co, L.in_shape[2], L.in_shape[3] // S, L.k,
-                              L.stride, L.pad, L.groups, i, S)
+        ci_ = conv_of(i)
         xi, gi = dev_of(shard_of(T.x, i)), dev_of(shard_of(T.g, i))
         li = dev_of(shard_of(T.x, i - 1)) if i > 0 else None
         ri = dev_of(shard_of(T.x, i + 1)) if i < S - 1 else None
         xhi = torch.empty(ci_.halo_shape(sscnn.HALO_INPUT), device=dev)
         sscnn.halo_gather(ci_, sscnn.HALO_INPUT, li, ri, xhi)
-        gwi, gbi = torch.empty(c.w_shape, device=dev), torch.empty((c.c_out,), device=dev)
-        sscnn.conv_bwd_weight_partial(ci_, xi, xhi, gi, gwi, gbi, sscnn.new_workspace(ci_))
-        other_gw[i], other_gb[i] = gwi, gbi
+        gbuf, gw, gb = grads()
+        sscnn.conv_bwd_weight_partial(ci_, xi, xhi, gi, gw, gb, sscnn.new_workspace(ci_))
+        others[i] = gbuf
         del xi, gi, li, ri, xhi
     torch.cuda.synchronize()
 
-    names = ["halo_gather_x", "conv_fwd", "halo_gather_g", "conv_bwd_input",
-             "conv_bwd_weight_partial", "partial_reduce"]
+    ops = {
+        "halo_gather_x": lambda st: sscnn.halo_gather(c, sscnn.HALO_INPUT, st["xl"], st["xr"], st["xh"]),
+        "conv_fwd": lambda st: sscnn.conv_fwd(c, st["x"], st["xh"], wt, b, st["y"]),
+        "halo_gather_g": lambda st: sscnn.halo_gather(c, sscnn.HALO_GRAD_OUTPUT, st["gl"], st["gr"], st["gh"]),
+        "conv_bwd_input": lambda st: sscnn.conv_bwd_input(c, st["g"], st["gh"], wt, st["dx"]),
+        "conv_bwd_weight_partial": lambda st: sscnn.conv_bwd_weight_partial(
+            c, st["x"], st["xh"], st["g"], st["gw"], st["gb"], ws),
+        "partial_reduce": lambda st: sscnn.partial_reduce(
+            [st["gbuf"] if i == s else others[i] for i in range(S)], st["red"]),
+    }
 
-    def step(st, ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record()
-        mark(0)
-        sscnn.halo_gather(c, sscnn.HALO_INPUT, st["xl"], st["xr"], st["xh"])
-        mark(1)
-        sscnn.conv_fwd(c, st["x"], st["xh"], wt, b, st["y"])
-        mark(2)
-        sscnn.halo_gather(c, sscnn.HALO_GRAD_OUTPUT, st["gl"], st["gr"], st["gh"])
-        mark(3)
-        sscnn.conv_bwd_input(c, st["g"], st["gh"], wt, st["dx"])
-        mark(4)
-        sscnn.conv_bwd_weight_partial(c, st["x"], st["xh"], st["g"], st["gw"], st["gb"], ws)
-        mark(5)
-        parts_w = [st["gw"] if i == s else other_gw[i] for i in range(S)]
-        parts_b = [st["gb"] if i == s else other_gb[i] for i in range(S)]
-        sscnn.partial_reduce(parts_w, st["gw_red"])
-        sscnn.partial_reduce(parts_b, st["gb_red"])
-        mark(6)
+    def step(st):
+        for f in ops.values():
+            f(st)
+
+    # A plain device copy of known size (untimed): the reference that calibrates
+    # the FETCH_SIZE / WRITE_SIZE counters in a counter run of this command.
+    cal_src = torch.empty(COPY_CAL_BYTES // 4, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
 
     for i in range(args.warmup):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
 
-    # Timed region: K steps, events only at the ends.
+    # Timed region: K steps, events at the ends only.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     w0 = time.perf_counter()
     e0.record()
     for i in range(args.steps):
@@ -158,16 +209,18 @@ def main():
     wall = time.perf_counter() - w0
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # Per-call durations: the same K steps again with an event pair around
-    # every call, on the stream the kernels run on (torch's current stream).
-    per = {n: [] for n in names}
-    for i in range(args.steps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
-        step(sets[i % len(sets)], ev)
+    # Each operation on its own: back-to-back calls between two events.
+    op_us = {}
+    for name, f in ops.items():
+        f(sets[0])
         torch.cuda.synchronize()
-        for j, n in enumerate(names):
-            per[n].append(ev[j].elapsed_time(ev[j + 1]))
-    per_us = {n: 1e3 * float(np.mean(v)) for n, v in per.items()}
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for i in range(args.op_reps):
+            f(sets[i % len(sets)])
+        a1.record()
+        torch.cuda.synchronize()
+        op_us[name] = 1e3 * a0.elapsed_time(a1) / args.op_reps
 
     # Algorithmic work.
     f4 = 4
@@ -175,65 +228,68 @@ def main():
     co, ho, wol = c.c_out, c.h_out, c.w_out_local
     x_ext = n * ci * h * (wl_ + c.halo_l + c.halo_r) * f4
     g_ext = n * co * ho * (wol + c.ghalo_l + c.ghalo_r) * f4
-    x_b, y_b, g_b = n * ci * h * wl_ * f4, n * co * ho * wol * f4, n * co * ho * wol * f4
-    w_b = co * (ci // c.groups) * c.k * c.k * f4
-    b_b = co * f4
+    x_b, y_b = n * ci * h * wl_ * f4, n * co * ho * wol * f4
+    w_b, b_b = nw * f4, nb * f4
     red_b = (S + 1) * (w_b + b_b)
     bytes_fwd = x_ext + w_b + b_b + y_b
     bytes_bwd = g_ext + x_ext + w_b + x_b + w_b + b_b
     step_bytes = bytes_fwd + bytes_bwd + red_b
     flops_pass = 2 * (ci // c.groups) * c.k * c.k * n * co * ho * wol
     step_flops = 3 * flops_pass
-    kern_bytes = {
+    op_bytes = {
         "halo_gather_x": 2 * n * ci * h * (c.halo_l + c.halo_r) * f4,
         "conv_fwd": x_ext + w_b + b_b + y_b,
         "halo_gather_g": 2 * n * co * ho * (c.ghalo_l + c.ghalo_r) * f4,
         "conv_bwd_input": g_ext + w_b + x_b,
-        "conv_bwd_weight_partial": x_ext + g_b + w_b + b_b,
+        "conv_bwd_weight_partial": x_ext + y_b + w_b + b_b,
         "partial_reduce": red_b,
     }
-    kern_flops = {"conv_fwd": flops_pass, "conv_bwd_input": flops_pass, "conv_bwd_weight_partial": flops_pass}
+    op_flops = {"conv_fwd": flops_pass, "conv_bwd_input": flops_pass, "conv_bwd_weight_partial": flops_pass}
     dense = c.groups == 1 and min(c.c_in, c.c_out) >= 16
     compute_peak = MFMA_F32_PEAK_TFLOPS if dense else VALU_F32_PEAK_TFLOPS
-    dom = max(per_us, key=per_us.get)
-    t_hbm = kern_bytes[dom] / (HBM_PEAK_GBS * 1e9)
-    t_cmp = kern_flops.get(dom, 0) / (compute_peak * 1e12)
+
+    def roof_time(k):
+        return max(op_bytes[k] / (HBM_PEAK_GBS * 1e9), op_flops.get(k, 0) / (compute_peak * 1e12))
+
+    dom = max(op_us, key=op_us.get)
+    t_hbm = op_bytes[dom] / (HBM_PEAK_GBS * 1e9)
+    t_cmp = op_flops.get(dom, 0) / (compute_peak * 1e12)
     if t_cmp > t_hbm:
-        achieved = kern_flops[dom] / (per_us[dom] * 1e-6) / 1e12
-        roof = {"bound": "mfma" if dense else "alu", "achieved": round(achieved, 3),
+        achieved = op_flops[dom] / (op_us[dom] * 1e-6) / 1e12
+        roof = {"bound": "mfma" if dense else "alu", "achieved": round(achieved, 2),
                 "peak": round(compute_peak, 1), "unit": "TFLOP/s"}
     else:
-        achieved = kern_bytes[dom] / (per_us[dom] * 1e-6) / 1e9
+        achieved = op_bytes[dom] / (op_us[dom] * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
-    roof["kernel"] = dom
-    roof["avg_us"] = round(per_us[dom], 2)
+    tr = recorded_traffic(wl.name)
+    roof["traffic"] = (tr["fetch_bytes"] + tr["write_bytes"]) if tr and tr.get("op") == dom else None
+    roof["op"] = dom
+    roof["avg_us"] = round(op_us[dom], 2)
+    roof["algorithmic_bytes"] = op_bytes[dom]
+    roof["algorithmic_flops"] = op_flops.get(dom, 0)
 
     step_s = ms_per_step * 1e-3
-    value = step_bytes / step_s / 1e9
-    step_roof_s = sum(max(kern_bytes[k] / (HBM_PEAK_GBS * 1e9),
-                          kern_flops.get(k, 0) / (compute_peak * 1e12)) for k in kern_bytes)
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "metric": METRIC, "value": round(step_bytes / step_s / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description, "shard": f"{s} of {S}",
                    "shard_input": list(c.x_shape), "weight": list(c.w_shape),
                    "buffer_sets": args.sets},
-        "tflops": round(step_flops / step_s / 1e12, 3),
+        "tflops": round(step_flops / step_s / 1e12, 2),
         "step_bytes": step_bytes, "step_flops": step_flops,
         "hbm_roofline_frac": round(step_bytes / (HBM_PEAK_GBS * 1e9) / step_s, 4),
-        "roofline_frac_step": round(step_roof_s / step_s, 4),
+        "compute_roofline_frac": round(step_flops / (compute_peak * 1e12) / step_s, 4),
+        "roofline_frac_step": round(sum(roof_time(k) for k in op_bytes) / step_s, 4),
         "roofline": roof,
-        "kernels_us": {k: round(v, 2) for k, v in per_us.items()},
+        "ops_us": {k: round(v, 2) for k, v in op_us.items()},
         "wall_s_timed": round(wall, 4),
+        "source_hash": kernel_source_hash(),
     }
-
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, T, L, S, s)
-
     print(json.dumps(out), flush=True)
     return 0
 
@@ -271,6 +327,35 @@ def cpu_baseline(wl, T, L, S, s):
             "sample": f"images 0..{imgs - 1} of {n}, rows 0..{rows - 1} of {h_full}, shard {s} of {S}: "
                       "forward + grad_input + grad_weight/grad_bias partial (C, double, OpenMP)",
             "cpu": platform.processor() or platform.machine()}
+
+
+def summarize(d):
+    """Text summary of a rocprofv3 output directory (kernel stats and/or
+    counter collection CSVs), for the files committed under profiles/."""
+    d = pathlib.Path(d)
+    stats = sorted(glob.glob(str(d / "**" / "*kernel_stats.csv"), recursive=True))
+    for f in stats:
+        print(f"## kernel statistics ({pathlib.Path(f).name})\n")
+        print("| kernel | calls | average us | min us | max us | share |")
+        print("|---|---:|---:|---:|---:|---:|")
+        for r in csv.DictReader(open(f)):
+            print(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+        print()
+    cc = sorted(glob.glob(str(d / "**" / "*counter_collection.csv"), recursive=True))
+    if cc:
+        agg = {}
+        for f in cc:
+            for r in csv.DictReader(open(f)):
+                k = (r["Kernel_Name"], r["Counter_Name"])
+                agg.setdefault(k, []).append(float(r["Counter_Value"]))
+        print("## counters (mean per dispatch)\n")
+        print("| kernel | counter | mean | dispatches |")
+        print("|---|---|---:|---:|")
+        for (kname, cname), v in sorted(agg.items()):
+            print(f"| `{kname[:110]}` | {cname} | {sum(v) / len(v):.1f} | {len(v)} |")
+        print()
+    return 0
 
 
 if __name__ == "__main__":
