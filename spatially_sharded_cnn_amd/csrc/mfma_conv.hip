@@ -242,10 +242,21 @@ mfma_conv_kernel(MfArgs a)
     __shared__ __align__(16) float ws[S::WS_FLOATS];
     __shared__ __align__(16) float xs[S::XS_FLOATS];
 
-    // tile -> (output-channel block, image, row block, column block)
+    // tile -> (output-channel block, image, row block, column block).  Workgroups
+    // are dealt round-robin to the 8 XCDs (each with its own L2); when the pixel
+    // tiles split evenly, each XCD takes a contiguous range of pixel tiles with
+    // all their output-channel blocks, so the input rows a tile shares with its
+    // channel blocks and its neighbouring row tiles stay in one L2.
     const int bid = blockIdx.x;
-    const int ot = bid % a.tiles_o;
-    int mt = bid / a.tiles_o;
+    int ot, mt;
+    if (a.tiles_m % 8 == 0) {
+        const int xcd = bid % 8, j = bid / 8;
+        ot = j % a.tiles_o;
+        mt = xcd * (a.tiles_m / 8) + j / a.tiles_o;
+    } else {
+        ot = bid % a.tiles_o;
+        mt = bid / a.tiles_o;
+    }
     const int tw = mt % a.tiles_w;
     mt /= a.tiles_w;
     const int th = mt % a.tiles_h;

@@ -177,8 +177,16 @@ mfma_wgrad_kernel(WgArgs a)
     __shared__ __align__(16) float gs[S::G_FLOATS];
     __shared__ __align__(16) float xs[S::X_FLOATS];
 
-    // workgroup -> (split, kh, input-channel tile, output-channel tile)
+    // workgroup -> (split, kh, input-channel tile, output-channel tile).  When
+    // the splits divide evenly over the 8 XCDs (workgroups are dealt to them
+    // round-robin), all tiles of a split run on one XCD, so the grad_output and
+    // input rows they share stay in one L2.
     int b = blockIdx.x;
+    const int per_split = a.tiles_o * a.tiles_c * K;
+    if (a.splits % 8 == 0) {
+        const int xcd = b % 8, j = b / 8;
+        b = (xcd * (a.splits / 8) + j / per_split) * per_split + j % per_split;
+    }
     const int ot = b % a.tiles_o;
     b /= a.tiles_o;
     const int ct = b % a.tiles_c;

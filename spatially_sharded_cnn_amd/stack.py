@@ -1,0 +1,115 @@
+"""Stack schedule of a W-sharded convolution stack (ConvNeXt-style) on one GPU.
+
+The pages train a ConvNeXt-XL whose activations stay width-sharded through
+the network (NVIDIA blog "Perception Model Training for Autonomous Vehicles
+with Tensor Parallelism", DTensor section: input and activations Shard(3),
+weights Replicate).  Here all S shards of every activation are separate
+buffers of one device.  Forward runs layer by layer, each layer on all shards
+before the next (so every shard's halo is gathered from its neighbours' real
+outputs); backward runs the layers in reverse from the last layer's
+grad_output, reusing each layer's saved input halo, and reduces the shards'
+partial weight / bias gradients.
+
+This module only sequences calls of the C ABI (spatially_sharded_cnn_amd.sscnn);
+every operation runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import torch
+
+from . import sscnn
+
+
+@dataclasses.dataclass
+class LayerState:
+    convs: list                 # per shard sscnn.Conv
+    x: list                     # per shard input slice
+    x_halo: list                # per shard input halo (kept for grad_weight)
+    y: list = None              # per shard output slice
+    g: list = None              # per shard grad of the output
+    g_halo: list = None
+    dx: list = None             # per shard grad of the input
+    gw_parts: list = None       # per shard partial grad_weight
+    gb_parts: list = None       # per shard partial grad_bias
+    gw: torch.Tensor = None     # reduced grad_weight
+    gb: torch.Tensor = None     # reduced grad_bias
+
+
+class ShardedStack:
+    """Runs a chain of convolutions (workloads.Layer list) on S W-shards."""
+
+    def __init__(self, layers, num_shards: int, weights, biases, device="cuda", stream=None):
+        self.layers = list(layers)
+        self.S = num_shards
+        self.device = device
+        self.stream = stream
+        self.w = [t if isinstance(t, torch.Tensor) else torch.from_numpy(t).to(device) for t in weights]
+        self.b = [None if t is None else (t if isinstance(t, torch.Tensor) else torch.from_numpy(t).to(device))
+                  for t in biases]
+        self.state: List[Optional[LayerState]] = [None] * len(self.layers)
+
+    def _convs(self, L):
+        n, ci, h, w = L.in_shape
+        if w % self.S:
+            raise ValueError(f"layer {L.name}: width {w} does not split into {self.S} shards")
+        return [sscnn.conv_init(n, ci, L.co, h, w // self.S, L.k, L.stride, L.pad, L.groups, s, self.S)
+                for s in range(self.S)]
+
+    def _nbrs(self, lst, s):
+        return (lst[s - 1] if s > 0 else None), (lst[s + 1] if s < self.S - 1 else None)
+
+    def forward(self, x_slices):
+        """x_slices: per shard (N, 3, H, W/S) device tensors.  Returns the last
+        layer's per-shard outputs."""
+        cur = list(x_slices)
+        for l, L in enumerate(self.layers):
+            convs = self._convs(L)
+            c0 = convs[0]
+            st = LayerState(convs=convs, x=cur, x_halo=[], y=[])
+            for s, c in enumerate(convs):
+                h = torch.empty(c.halo_shape(sscnn.HALO_INPUT), device=self.device)
+                left, right = self._nbrs(cur, s)
+                sscnn.halo_gather(c, sscnn.HALO_INPUT, left, right, h, self.stream)
+                st.x_halo.append(h)
+            for s, c in enumerate(convs):
+                y = torch.empty(c0.y_shape, device=self.device)
+                sscnn.conv_fwd(c, cur[s], st.x_halo[s], self.w[l], self.b[l], y, self.stream)
+                st.y.append(y)
+            self.state[l] = st
+            cur = st.y
+        return cur
+
+    def backward(self, g_slices, need_input_grad: bool = True):
+        """g_slices: per shard grad of the last output.  Fills each layer's
+        dx, partial and reduced weight / bias gradients.  The first layer's
+        dx is computed too when need_input_grad."""
+        cur = list(g_slices)
+        for l in range(len(self.layers) - 1, -1, -1):
+            st = self.state[l]
+            convs = st.convs
+            c0 = convs[0]
+            st.g, st.g_halo, st.dx, st.gw_parts, st.gb_parts = cur, [], [], [], []
+            for s, c in enumerate(convs):
+                h = torch.empty(c.halo_shape(sscnn.HALO_GRAD_OUTPUT), device=self.device)
+                left, right = self._nbrs(cur, s)
+                sscnn.halo_gather(c, sscnn.HALO_GRAD_OUTPUT, left, right, h, self.stream)
+                st.g_halo.append(h)
+            ws = sscnn.new_workspace(c0, self.device)
+            nw = c0.w_shape[0] * c0.w_shape[1] * c0.w_shape[2] * c0.w_shape[3]
+            for s, c in enumerate(convs):
+                if l > 0 or need_input_grad:
+                    dx = torch.empty(c0.x_shape, device=self.device)
+                    sscnn.conv_bwd_input(c, cur[s], st.g_halo[s], self.w[l], dx, self.stream)
+                    st.dx.append(dx)
+                buf = torch.empty(nw + c0.c_out, device=self.device)    # [gW | gB]
+                sscnn.conv_bwd_weight_partial(c, st.x[s], st.x_halo[s], cur[s], buf[:nw].view(c0.w_shape),
+                                              buf[nw:], ws, self.stream)
+                st.gw_parts.append(buf)
+            red = torch.empty(nw + c0.c_out, device=self.device)
+            sscnn.partial_reduce(st.gw_parts, red, self.stream)
+            st.gw, st.gb = red[:nw].view(c0.w_shape), red[nw:]
+            cur = st.dx
+        return cur

@@ -1,9 +1,10 @@
 """Seeded synthetic workloads for the width-sharded convolution.
 
 This module is shared by the product's tests and benchmark and by the oracle
-side of those tests.  It holds NO convolution arithmetic: every tensor shape
-(including each grad_output shape) is written out in the tables below, and the
-only computation here is drawing seeded random numbers.
+side of those tests.  It holds NO convolution arithmetic: tensor shapes are
+written out (the stack's maps are the input's divided by the 4x4/4 stem and
+halved by each 2x2/2 downsample), and the only computation here is drawing
+seeded random numbers.
 
 Values: numpy ``default_rng(seed)`` (PCG64), float32.  Draw order within a
 workload: input X (global), then per layer (weight, bias) in chain order, then
@@ -65,20 +66,22 @@ def _layer(name, ci, co, k, stride, pad, groups, in_shape, out_shape):
     return Layer(name, ci, co, k, stride, pad, groups, tuple(in_shape), tuple(out_shape))
 
 
-def _convnext_stack(n, w):
-    # Stem 4x4/4 (3 -> 256), then per stage a depthwise 7x7 pad 3 and a 2x2/2
-    # downsample (C doubles), ending with the stage-4 depthwise conv.
-    h = 512
-    return (
-        _layer("stem", 3, 256, 4, 4, 0, 1, (n, 3, h, w), (n, 256, 128, w // 4)),
-        _layer("dw1", 256, 256, 7, 1, 3, 256, (n, 256, 128, w // 4), (n, 256, 128, w // 4)),
-        _layer("ds1", 256, 512, 2, 2, 0, 1, (n, 256, 128, w // 4), (n, 512, 64, w // 8)),
-        _layer("dw2", 512, 512, 7, 1, 3, 512, (n, 512, 64, w // 8), (n, 512, 64, w // 8)),
-        _layer("ds2", 512, 1024, 2, 2, 0, 1, (n, 512, 64, w // 8), (n, 1024, 32, w // 16)),
-        _layer("dw3", 1024, 1024, 7, 1, 3, 1024, (n, 1024, 32, w // 16), (n, 1024, 32, w // 16)),
-        _layer("ds3", 1024, 2048, 2, 2, 0, 1, (n, 1024, 32, w // 16), (n, 2048, 16, w // 32)),
-        _layer("dw4", 2048, 2048, 7, 1, 3, 2048, (n, 2048, 16, w // 32), (n, 2048, 16, w // 32)),
-    )
+def convnext_stack(n, w, h=512, dims=(256, 512, 1024, 2048), name_prefix=""):
+    """Layers of a ConvNeXt-style convolution stack on a global (n, 3, h, w)
+    input: stem 4x4/4 (3 -> dims[0]), then per stage a depthwise 7x7 pad 3
+    and a 2x2/2 downsample to the next stage's width, ending with the last
+    stage's depthwise conv."""
+    layers = []
+    c, hh, ww = dims[0], h // 4, w // 4
+    layers.append(_layer(name_prefix + "stem", 3, c, 4, 4, 0, 1, (n, 3, h, w), (n, c, hh, ww)))
+    for st, cn in enumerate(dims):
+        layers.append(_layer(f"{name_prefix}dw{st + 1}", cn, cn, 7, 1, 3, cn, (n, cn, hh, ww), (n, cn, hh, ww)))
+        if st + 1 < len(dims):
+            nxt = dims[st + 1]
+            layers.append(_layer(f"{name_prefix}ds{st + 1}", cn, nxt, 2, 2, 0, 1, (n, cn, hh, ww),
+                                 (n, nxt, hh // 2, ww // 2)))
+            hh, ww = hh // 2, ww // 2
+    return tuple(layers)
 
 
 WORKLOADS = {
@@ -98,11 +101,11 @@ WORKLOADS = {
         num_shards=4, shard=1, seed=1003, dist="normal",
         description="dense 5x5 s1 p2 conv 256->256: shard (7,256,128,128) of a (7,256,128,512) map, 2-column halos"),
     "convnext_xl_w2048": Workload(
-        "convnext_xl_w2048", _convnext_stack(7, 2048),
+        "convnext_xl_w2048", convnext_stack(7, 2048),
         num_shards=4, shard=1, seed=1004, dist="normal",
         description="ConvNeXt-XL conv stack on shard (7,3,512,512) of a (7,3,512,2048) input"),
     "convnext_xl_w4096": Workload(
-        "convnext_xl_w4096", _convnext_stack(7, 4096),
+        "convnext_xl_w4096", convnext_stack(7, 4096),
         num_shards=4, shard=1, seed=1005, dist="normal",
         description="ConvNeXt-XL conv stack on shard (7,3,512,1024) of a (7,3,512,4096) input"),
 }
@@ -136,6 +139,11 @@ def generate(wl: Workload, seed: Optional[int] = None) -> Tensors:
         bs.append(_draw(rng, (L.co,), wl.dist, par_scale))
     g = _draw(rng, wl.g_shape, wl.dist, act_scale)
     return Tensors(x, ws, bs, g)
+
+
+def stack(name, layers, num_shards, shard=1, seed=11, dist="normal") -> Workload:
+    """A multi-layer workload (e.g. a smaller ConvNeXt-style stack)."""
+    return Workload(name, tuple(layers), num_shards, shard, seed, dist, name)
 
 
 def custom(name, n, ci, co, h, w, k, stride, pad, groups, ho, wo, num_shards,
