@@ -22,12 +22,18 @@
 //    flipped in both axes (stride 1, pad k/2, so the grad_output halo has the
 //    same widths as the input halo);
 //  * grad_weight: each thread accumulates all k*k taps over its RH x 4 outputs
-//    (its grad_output block is prefetched alongside the input tile), the
-//    workgroup reduces them through LDS in a fixed order and writes one
-//    partial per tile; a second kernel sums a channel's tiles in tile order.
+//    (its grad_output block is prefetched alongside the input tile) and keeps
+//    them across the consecutive tiles of one channel that its workgroup
+//    owns; at a channel change the waves reduce them with cross-lane swaps,
+//    the workgroup adds the waves' totals in a fixed order and writes one
+//    partial; a second kernel sums a channel's partials in workgroup order.
 //    No atomics: results are bitwise reproducible.
 #include "internal.h"
 #include "depthwise.h"
+
+#ifndef SSCNN_DW_WGRAD_WAVES
+#define SSCNN_DW_WGRAD_WAVES 3
+#endif
 
 namespace sscnn {
 namespace {
@@ -39,8 +45,8 @@ struct DwArgs {
     const float* b;      // (C) or null
     float* y;            // (N*C, H, W)
     const float* g;      // grad_output (N*C, H, W) for grad_weight
-    float* ws;           // grad_weight tile partials (C, N * tiles_h * tiles_w, k*k + 1)
-    int H, W, C, tiles_h, tiles_w, ntiles;   // ntiles = N * C * tiles_h * tiles_w
+    float* ws;           // grad_weight partials (C, up to N * tiles_h * tiles_w, k*k + 1)
+    int H, W, C, N, tiles_h, tiles_w, ntiles;   // ntiles = N * C * tiles_h * tiles_w
 };
 
 // Tile t -> (plane, tile row, tile column), column fastest.
@@ -227,24 +233,128 @@ dw_conv_kernel(DwArgs a)
     }
 }
 
-// grad_weight partial of one tile: sum over the tile's outputs (i, j) of
+// Sum of N per-lane values over the 64 lanes of a wave, leaving one total per
+// lane (a reduce-scatter): stage k pairs lanes that differ in one lane bit
+// (32, 16, 8, 4, 2, 1) and halves the list, the lower lane of a pair keeping
+// the first half of the list and the upper lane the second half.  Bits 5 and
+// 4 are exchanged with the gfx950 lane-swap instructions, bits 3..0 with DPP
+// (row mirror, half-row mirror, quad permutations; the pairings they make
+// split the lanes by the same bits).  wave_sum_index() names the value a lane
+// ends with.  Cost ~2.6 VALU per value instead of a 64-step loop per value.
+__device__ __forceinline__ float lane_swap_sum(float x, float y, bool bit16)
+{
+    const auto r = bit16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false)
+                         : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_pair_sum(float x, float y, bool upper)
+{
+    const float send = upper ? x : y;
+    const float keep = upper ? y : x;
+    return keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), CTRL, 0xf, 0xf, false));
+}
+
+template <int N, int STAGE>
+__device__ __forceinline__ float wave_sum_stage(const float (&v)[N], int lane)
+{
+    constexpr int H = (N + 1) / 2;
+    float u[H];
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+        const float x = v[i], y = (i + H < N) ? v[i + H] : 0.f;
+        if constexpr (STAGE == 0) u[i] = lane_swap_sum(x, y, false);
+        else if constexpr (STAGE == 1) u[i] = lane_swap_sum(x, y, true);
+        else if constexpr (STAGE == 2) u[i] = dpp_pair_sum<0x140>(x, y, lane & 8);   // row mirror
+        else if constexpr (STAGE == 3) u[i] = dpp_pair_sum<0x141>(x, y, lane & 4);   // half-row mirror
+        else if constexpr (STAGE == 4) u[i] = dpp_pair_sum<0x4E>(x, y, lane & 2);    // quad [2,3,0,1]
+        else u[i] = dpp_pair_sum<0xB1>(x, y, lane & 1);                               // quad [1,0,3,2]
+    }
+    if constexpr (STAGE == 5) {
+        static_assert(H == 1, "64 lanes reduce at most 64 values");
+        return u[0];
+    } else {
+        return wave_sum_stage<H, STAGE + 1>(u, lane);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ float wave_sum_scatter(const float (&v)[N], int lane)
+{
+    static_assert(N >= 2 && N <= 64, "values per lane");
+    return wave_sum_stage<N, 0>(v, lane);
+}
+
+// Index of the total that lane holds after wave_sum_scatter<N>, or -1.
+template <int N>
+__device__ __forceinline__ int wave_sum_index(int lane)
+{
+    int n[7];
+    n[0] = N;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) n[k + 1] = (n[k] + 1) / 2;
+    const int bit[6] = {32, 16, 8, 4, 2, 1};
+    int j = 0;
+#pragma unroll
+    for (int k = 5; k >= 0; --k) {
+        if (lane & bit[k]) j += n[k + 1];
+        if (j >= n[k]) return -1;
+    }
+    return j;
+}
+
+// grad_weight partial, tile by tile: the sum over a tile's outputs (i, j) of
 // G[i, j] * Xext[i - P + kh, j + kw] for every tap, plus sum G (grad_bias).
+// Tiles are numbered channel-major (c, n, tile row, tile column) and each
+// workgroup takes one contiguous run of them, so consecutive tiles usually
+// share a channel: a thread keeps its k*k + 1 sums in registers across them
+// and the workgroup reduces only when the channel changes or its run ends.
+// One reduction writes one partial; the partials of channel c are numbered by
+// workgroup from the one that owns the channel's first tile.
+__device__ __forceinline__ int64_t tile_owner(int64_t t, int64_t T, int64_t G)
+{
+    return ((t + 1) * G - 1) / T;     // the workgroup w with floor(wT/G) <= t < floor((w+1)T/G)
+}
+
 template <int K, int TX, int TY, int RH>
-__global__ void __launch_bounds__(TX * TY)
+__global__ void __launch_bounds__(TX * TY) __attribute__((amdgpu_waves_per_eu(SSCNN_DW_WGRAD_WAVES)))
 dw_wgrad_kernel(DwArgs a)
 {
     using T = Tile<K, TX, TY, RH>;
     constexpr int P = T::P;
     constexpr int KK = K * K;
-    constexpr int RS = KK + 3;                  // LDS row per thread for the reduction (KK+1 used)
-    constexpr int RED = T::NT * RS;
-    constexpr int SH = T::FLOATS > RED ? T::FLOATS : RED;
-    __shared__ __align__(16) float sh[SH];
+    constexpr int NV = KK + 1;                  // taps + bias
+    constexpr int NWAVE = T::NT / 64;
+    static_assert(T::NT % 64 == 0, "whole waves");
+    __shared__ __align__(16) float sh[T::FLOATS];
+    __shared__ float red[NWAVE][NV + 2];
     typename T::Regs R;
     float4 gnext[RH];
     const int tx = threadIdx.x % TX, ty = threadIdx.x / TX;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tiles_c = a.ntiles / a.C;         // N * tiles_h * tiles_w
+    const int64_t G = gridDim.x;
+    const int beg = (int)((int64_t)blockIdx.x * a.ntiles / G);
+    const int end = (int)((int64_t)(blockIdx.x + 1) * a.ntiles / G);
+    if (beg >= end) return;
 
-    auto fetch_g = [&](const TileIdx& d) {
+    auto decode_cm = [&](int t) {
+        TileIdx d;
+        d.tcol = t % a.tiles_w;
+        t /= a.tiles_w;
+        d.trow = t % a.tiles_h;
+        t /= a.tiles_h;
+        d.n = t % a.N;
+        d.c = t / a.N;
+        d.plane = d.n * a.C + d.c;
+        d.i0 = d.trow * T::TH;
+        d.j0 = d.tcol * T::TW;
+        return d;
+    };
+    auto fetch_all = [&](const TileIdx& d) {
+        T::fetch(R, a.x + (int64_t)d.plane * a.H * a.W, a.halo + (int64_t)d.plane * a.H * (2 * P),
+                 a.H, a.W, d.i0, d.j0);
         const float* gp = a.g + (int64_t)d.plane * a.H * a.W + d.j0 + 4 * tx;
 #pragma unroll
         for (int i = 0; i < RH; ++i) {
@@ -254,89 +364,83 @@ dw_wgrad_kernel(DwArgs a)
         }
     };
 
-    int t = blockIdx.x;
-    if (t >= a.ntiles) return;
-    {
-        const TileIdx d = decode(a, t, T::TH, T::TW, false);
-        T::fetch(R, a.x + (int64_t)d.plane * a.H * a.W, a.halo + (int64_t)d.plane * a.H * (2 * P),
-                 a.H, a.W, d.i0, d.j0);
-        fetch_g(d);
-    }
-    const int tiles_c = a.ntiles / a.C;    // N * tiles_h * tiles_w
-    for (; t < a.ntiles; t += gridDim.x) {
-        const TileIdx d = decode(a, t, T::TH, T::TW, false);
-        T::put(sh, R);
-        float gv[RH][4];
-        float bsum = 0.f;
+    fetch_all(decode_cm(beg));
+    for (int t = beg; t < end;) {
+        // one run: the workgroup's consecutive tiles of channel c
+        const int c = t / tiles_c;
+        const int run_end = min(end, (c + 1) * tiles_c);
+        float acc[NV];
 #pragma unroll
-        for (int i = 0; i < RH; ++i) {
-            gv[i][0] = gnext[i].x; gv[i][1] = gnext[i].y; gv[i][2] = gnext[i].z; gv[i][3] = gnext[i].w;
-            bsum += (gv[i][0] + gv[i][1]) + (gv[i][2] + gv[i][3]);
-        }
-        lds_barrier();
-        const int tn = t + gridDim.x;
-        if (tn < a.ntiles) {
-            const TileIdx e = decode(a, tn, T::TH, T::TW, false);
-            T::fetch(R, a.x + (int64_t)e.plane * a.H * a.W, a.halo + (int64_t)e.plane * a.H * (2 * P),
-                     a.H, a.W, e.i0, e.j0);
-            fetch_g(e);
-        }
-        float acc[KK];
-#pragma unroll
-        for (int k = 0; k < KK; ++k) acc[k] = 0.f;
-        const float* base = sh + (ty * RH) * T::LS + 4 * tx;
-#pragma unroll
-        for (int r = 0; r < RH + K - 1; ++r) {
-            float in[4 + K - 1];
-            T::read_row(base + r * T::LS, in);
+        for (int k = 0; k < NV; ++k) acc[k] = 0.f;
+        for (; t < run_end; ++t) {
+            T::put(sh, R);
+            float gv[RH][4];
 #pragma unroll
             for (int i = 0; i < RH; ++i) {
-                const int kh = r - i;
-                if (kh < 0 || kh >= K) continue;
-#pragma unroll
-                for (int kw = 0; kw < K; ++kw)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        acc[kh * K + kw] = __builtin_fmaf(gv[i][jj], in[jj + kw], acc[kh * K + kw]);
+                gv[i][0] = gnext[i].x; gv[i][1] = gnext[i].y; gv[i][2] = gnext[i].z; gv[i][3] = gnext[i].w;
+                acc[KK] += (gv[i][0] + gv[i][1]) + (gv[i][2] + gv[i][3]);
             }
-        }
-        // Workgroup reduction in a fixed order: each thread's taps go to an LDS
-        // row; 4 readers per tap sum interleaved quarters of the rows, and the
-        // quarters are combined as (q0 + q1) + (q2 + q3).
-        lds_barrier();
-        float* red = sh;
+            lds_barrier();
+            if (t + 1 < end) fetch_all(decode_cm(t + 1));
+            // Rows are read one ahead of the FMAs that use them; the
+            // scheduling barriers keep the compiler from hoisting every row's
+            // reads to the top, which would need ~100 more registers.
+            const float* base = sh + (ty * RH) * T::LS + 4 * tx;
+            float cur[4 + K - 1], nxt[4 + K - 1];
+            T::read_row(base, cur);
 #pragma unroll
-        for (int k = 0; k < KK; ++k) red[threadIdx.x * RS + k] = acc[k];
-        red[threadIdx.x * RS + KK] = bsum;
+            for (int r = 0; r < RH + K - 1; ++r) {
+                if (r + 1 < RH + K - 1) T::read_row(base + (r + 1) * T::LS, nxt);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < RH; ++i) {
+                    const int kh = r - i;
+                    if (kh < 0 || kh >= K) continue;
+#pragma unroll
+                    for (int kw = 0; kw < K; ++kw)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            acc[kh * K + kw] = __builtin_fmaf(gv[i][jj], cur[jj + kw], acc[kh * K + kw]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int q = 0; q < 4 + K - 1; ++q) cur[q] = nxt[q];
+            }
+            lds_barrier();   // the tile is rewritten by the next put()
+        }
+        // Flush the run: wave totals, then the waves in a fixed order.  red
+        // is rewritten only after the next tile's barrier, which every reader
+        // below has passed.
+        const float s = wave_sum_scatter<NV>(acc, lane);
+        const int idx = wave_sum_index<NV>(lane);
+        if (idx >= 0) red[wave][idx] = s;
         lds_barrier();
-        const int tap = threadIdx.x >> 2, q = threadIdx.x & 3;
-        float s = 0.f;
-        if (tap <= KK) {
-            for (int m = q; m < T::NT; m += 4) s += red[m * RS + tap];
+        if (threadIdx.x < NV) {
+            float tot = red[0][threadIdx.x];
+#pragma unroll
+            for (int w = 1; w < NWAVE; ++w) tot += red[w][threadIdx.x];
+            const int64_t slot = blockIdx.x - tile_owner((int64_t)c * tiles_c, a.ntiles, G);
+            a.ws[((int64_t)c * tiles_c + slot) * NV + threadIdx.x] = tot;
         }
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        if (tap <= KK && q == 0) {
-            const int64_t tile_c = ((int64_t)d.n * a.tiles_h + d.trow) * a.tiles_w + d.tcol;
-            a.ws[((int64_t)d.c * tiles_c + tile_c) * (KK + 1) + tap] = s;
-        }
-        lds_barrier();   // red (aliasing the tile) is rewritten by the next put()
     }
 }
 
-// Second pass: grad_w[c, t] = sum over the channel's tiles, in tile order.
+// Second pass: grad_w[c, tap] = sum of channel c's partials in workgroup
+// order (one per workgroup whose run of tiles meets the channel).
 template <int K>
 __global__ void __launch_bounds__(256)
-dw_wgrad_reduce_kernel(const float* __restrict__ ws, int C, int tiles_c, float* __restrict__ gw,
-                       float* __restrict__ gb)
+dw_wgrad_reduce_kernel(const float* __restrict__ ws, int C, int tiles_c, int64_t ntiles, int64_t grid,
+                       float* __restrict__ gw, float* __restrict__ gb)
 {
-    constexpr int KK1 = K * K + 1;
+    constexpr int NV = K * K + 1;
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= C * KK1) return;
-    const int c = idx / KK1, t = idx - c * KK1;
-    const float* p = ws + (int64_t)c * tiles_c * KK1 + t;
+    if (idx >= C * NV) return;
+    const int c = idx / NV, t = idx - c * NV;
+    const int64_t w0 = tile_owner((int64_t)c * tiles_c, ntiles, grid);
+    const int64_t w1 = tile_owner((int64_t)(c + 1) * tiles_c - 1, ntiles, grid);
+    const float* p = ws + (int64_t)c * tiles_c * NV + t;
     float s = 0.f;
-    for (int k = 0; k < tiles_c; ++k) s += p[(int64_t)k * KK1];
+    for (int64_t k = 0; k <= w1 - w0; ++k) s += p[k * NV];
     if (t < K * K) gw[c * K * K + t] = s;
     else if (gb) gb[c] = s;
 }
@@ -407,7 +511,7 @@ hipError_t launch_wgrad(DwArgs a, int planes, DwShape sh, float* gw, float* gb, 
         const int tiles_c = a.ntiles / a.C;                                                 \
         const int total = a.C * (K * K + 1);                                                \
         hipLaunchKernelGGL((dw_wgrad_reduce_kernel<K>), dim3((total + 255) / 256), dim3(256), \
-                           0, st, a.ws, a.C, tiles_c, gw, gb);                              \
+                           0, st, a.ws, a.C, tiles_c, (int64_t)a.ntiles, (int64_t)grid, gw, gb); \
         return hipGetLastError();                                                           \
     }
     SSCNN_DW_WGRAD(16, 16, 4)
@@ -426,6 +530,7 @@ DwArgs make_args(const Geom& g)
     a.H = g.h;
     a.W = g.wl;
     a.C = g.ci;
+    a.N = g.n;
     return a;
 }
 
