@@ -19,8 +19,8 @@ Prints ONE JSON line.  `value` is the algorithmic GB/s of a step:
 back-to-back calls with events on the stream the kernels run on; its bound is
 whichever of HBM bytes / 8 TB/s and FLOPs / compute peak is larger, with the
 compute peak of the unit it runs on: the FP32 matrix cores (157.3 TFLOP/s)
-for the dense layers, the FP32 vector FMA (78.6 TFLOP/s: 256 CUs x 4 SIMDs x
-16 lanes x 2 FLOP x 2.4 GHz; the library is built without packed FP32 math)
+for the dense layers, the FP32 vector FMA (157.3 TFLOP/s published; plain
+v_fmac_f32 with vector-register operands reaches it without packed math)
 for the depthwise ones.
 
     python bench.py [--workload dw7_c256|dense5x5_c256|dense5x5_tiny] [--steps K] [--warmup W]
@@ -45,7 +45,7 @@ ROOT = pathlib.Path(__file__).resolve().parent
 METRIC = "W-shard conv fwd+bwd GB/s & TFLOP/s FP32; % of HBM/MFMA roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X dense FP32 matrix
-VALU_F32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12   # 78.6, non-packed FP32 FMA
+VALU_F32_PEAK_TFLOPS = 157.3     # MI355X FP32 vector FMA
 COPY_CAL_BYTES = 256 << 20       # plain device copy used to calibrate FETCH_SIZE / WRITE_SIZE
 
 

@@ -77,6 +77,18 @@ __device__ __forceinline__ TileIdx decode(const DwArgs& a, int t, int th, int tw
 // 4 + k - 1 inputs per row start at a 16-byte boundary, so they are read with
 // 16-byte LDS reads (the fill pays unaligned 4-byte writes instead, once per
 // element, against ~2.5 reads per element).
+// LDS row pitch (floats): a multiple of 4 (16-byte aligned rows) such that
+// the TX lanes of a wave that read one tile row and the next TX lanes, RH
+// rows further down, sit a multiple of 4*TX floats apart.  gfx950 serves
+// 16-byte LDS reads of such lane groups at full rate (~240 B/clk per CU,
+// measured) and at half rate for other pitches.
+constexpr int lds_pitch(int lw, int rh, int tx)
+{
+    int ls = (lw + 3) & ~3;
+    while ((rh * ls) % (4 * tx) != 0) ls += 4;
+    return ls;
+}
+
 template <int K, int TX, int TY, int RH>
 struct Tile {
     static constexpr int P = K / 2;
@@ -84,7 +96,7 @@ struct Tile {
     static constexpr int TW = 4 * TX;
     static constexpr int TH = RH * TY;
     static constexpr int LW = TW + K - 1;
-    static constexpr int LS = (LW + 3) & ~3;    // 16-byte aligned rows
+    static constexpr int LS = lds_pitch(LW, RH, TX);
     static constexpr int LH = TH + K - 1;
     static constexpr int FLOATS = LH * LS;
     static constexpr int Q = TW / 4;
@@ -197,10 +209,14 @@ dw_conv_kernel(DwArgs a)
                      a.H, a.W, e.i0, e.j0);
         }
         // the plane's weights: wave-uniform, kept in scalar registers
+        // The plane's weights are wave-uniform: loaded through the scalar
+        // cache, then copied to vector registers, because gfx950 issues
+        // v_fmac_f32 at about twice the rate when no operand is a scalar
+        // register (measured: ~119 vs ~70 TFLOP/s chip-wide).
         float wr[K * K];
         const auto wp = as_const(a.w) + d.c * K * K;
 #pragma unroll
-        for (int k = 0; k < K * K; ++k) wr[k] = wp[FLIP ? K * K - 1 - k : k];
+        for (int k = 0; k < K * K; ++k) wr[k] = to_vgpr(wp[FLIP ? K * K - 1 - k : k]);
         const float bias = a.b ? as_const(a.b)[d.c] : 0.f;
 
         float acc[RH][4];
@@ -208,11 +224,16 @@ dw_conv_kernel(DwArgs a)
         for (int i = 0; i < RH; ++i)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) acc[i][jj] = bias;
+        // Each row is read from LDS one row ahead of its FMAs (a whole row of
+        // FMAs covers the read latency); the scheduling barriers keep that
+        // order, which the compiler would otherwise tighten to a few FMAs.
         const float* base = tile + (ty * RH) * T::LS + 4 * tx;
+        float cur[4 + K - 1], nxt[4 + K - 1];
+        T::read_row(base, cur);
 #pragma unroll
         for (int r = 0; r < RH + K - 1; ++r) {
-            float in[4 + K - 1];
-            T::read_row(base + r * T::LS, in);
+            if (r + 1 < RH + K - 1) T::read_row(base + (r + 1) * T::LS, nxt);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < RH; ++i) {
                 const int kh = r - i;
@@ -221,8 +242,11 @@ dw_conv_kernel(DwArgs a)
                 for (int kw = 0; kw < K; ++kw)
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj)
-                        acc[i][jj] = __builtin_fmaf(wr[kh * K + kw], in[jj + kw], acc[i][jj]);
+                        acc[i][jj] = __builtin_fmaf(wr[kh * K + kw], cur[jj + kw], acc[i][jj]);
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < 4 + K - 1; ++q) cur[q] = nxt[q];
         }
         float* yp = a.y + (int64_t)d.plane * a.H * a.W + d.j0 + 4 * tx;
 #pragma unroll

@@ -30,6 +30,15 @@ __device__ __forceinline__ void lds_barrier()
 // such loads become scalar-cache loads (s_load), which complete on their own
 // counter and never wait behind the wave's outstanding vector loads.  Only
 // for buffers the kernel does not write.
+// A wave-uniform value copied into a vector register (the compiler would
+// otherwise keep it in a scalar register and feed it to VALU ops from there).
+__device__ __forceinline__ float to_vgpr(float s)
+{
+    float v;
+    asm("v_mov_b32 %0, %1" : "=v"(v) : "s"(s));
+    return v;
+}
+
 template <typename T>
 __device__ __forceinline__ const __attribute__((address_space(4))) T* as_const(const T* p)
 {
