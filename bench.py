@@ -2,9 +2,11 @@
 """Benchmark of the width-sharded convolution hot path on one MI355X.
 
 One step is one pass of the whole path for the measured shard (shard 1 of 4)
-of a layer: halo_gather(X) -> conv_fwd -> halo_gather(G) -> conv_bwd_input ->
-conv_bwd_weight_partial -> partial_reduce (grad_weight and grad_bias of the
-four shards, one call over a contiguous [gW | gB] buffer).  Inputs are seeded
+of a layer: halo_gather(X) -> conv_fwd -> halo_gather(G) -> conv_bwd
+(grad_input and the grad_weight / grad_bias partials in one call) ->
+partial_reduce (grad_weight and grad_bias of the four shards, one call over a
+contiguous [gW | gB] buffer).  The separate conv_bwd_input and
+conv_bwd_weight_partial calls are timed on their own as well ("ops_us").  Inputs are seeded
 synthetic tensors already resident in HBM; each step uses the next of several
 independent buffer sets so that the 256 MB last-level cache cannot hand one
 step's data to the next.
@@ -24,7 +26,8 @@ v_fmac_f32 with vector-register operands reaches it without packed math)
 for the depthwise ones.
 
     python bench.py [--workload dw7_c256|dense5x5_c256|dense5x5_tiny] [--steps K] [--warmup W]
-    python bench.py --summarize DIR   # text summary of a rocprofv3 output directory
+    python bench.py --summarize DIR [DIR ...] [--traffic-op OP --traffic-kernels "K1;K2"]
+                                      # text summary of rocprofv3 output directories
 """
 from __future__ import annotations
 
@@ -59,7 +62,11 @@ def _parse():
     ap.add_argument("--sets", type=int, default=3, help="independent buffer sets rotated per step")
     ap.add_argument("--op-reps", type=int, default=20, help="back-to-back calls per operation timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--summarize", metavar="DIR", help="summarize a rocprofv3 output directory and exit")
+    ap.add_argument("--summarize", metavar="DIR", nargs="+",
+                    help="summarize rocprofv3 output directories and exit")
+    ap.add_argument("--traffic-op", help="with --summarize over FETCH_SIZE / WRITE_SIZE runs: the operation "
+                    "whose kernels' calibrated HBM bytes per launch are recorded")
+    ap.add_argument("--traffic-kernels", help="semicolon-separated substrings naming that operation's kernels")
     return ap.parse_args()
 
 
@@ -91,7 +98,7 @@ def recorded_traffic(workload: str):
 def main():
     args = _parse()
     if args.summarize:
-        return summarize(args.summarize)
+        return summarize(args.summarize, args.traffic_op, args.traffic_kernels)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU's share of the sharded path; --gpus {args.gpus} "
@@ -175,11 +182,16 @@ def main():
         "halo_gather_x": lambda st: sscnn.halo_gather(c, sscnn.HALO_INPUT, st["xl"], st["xr"], st["xh"]),
         "conv_fwd": lambda st: sscnn.conv_fwd(c, st["x"], st["xh"], wt, b, st["y"]),
         "halo_gather_g": lambda st: sscnn.halo_gather(c, sscnn.HALO_GRAD_OUTPUT, st["gl"], st["gr"], st["gh"]),
+        "conv_bwd": lambda st: sscnn.conv_bwd(c, st["x"], st["xh"], st["g"], st["gh"], wt, st["dx"],
+                                              st["gw"], st["gb"], ws),
+        "partial_reduce": lambda st: sscnn.partial_reduce(
+            [st["gbuf"] if i == s else others[i] for i in range(S)], st["red"]),
+    }
+    # the same backward as two calls (timed on their own, not part of the step)
+    extra_ops = {
         "conv_bwd_input": lambda st: sscnn.conv_bwd_input(c, st["g"], st["gh"], wt, st["dx"]),
         "conv_bwd_weight_partial": lambda st: sscnn.conv_bwd_weight_partial(
             c, st["x"], st["xh"], st["g"], st["gw"], st["gb"], ws),
-        "partial_reduce": lambda st: sscnn.partial_reduce(
-            [st["gbuf"] if i == s else others[i] for i in range(S)], st["red"]),
     }
 
     def step(st):
@@ -211,7 +223,7 @@ def main():
 
     # Each operation on its own: back-to-back calls between two events.
     op_us = {}
-    for name, f in ops.items():
+    for name, f in list(ops.items()) + list(extra_ops.items()):
         f(sets[0])
         torch.cuda.synchronize()
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -240,18 +252,21 @@ def main():
         "halo_gather_x": 2 * n * ci * h * (c.halo_l + c.halo_r) * f4,
         "conv_fwd": x_ext + w_b + b_b + y_b,
         "halo_gather_g": 2 * n * co * ho * (c.ghalo_l + c.ghalo_r) * f4,
+        "conv_bwd": bytes_bwd,
+        "partial_reduce": red_b,
         "conv_bwd_input": g_ext + w_b + x_b,
         "conv_bwd_weight_partial": x_ext + y_b + w_b + b_b,
-        "partial_reduce": red_b,
     }
-    op_flops = {"conv_fwd": flops_pass, "conv_bwd_input": flops_pass, "conv_bwd_weight_partial": flops_pass}
+    op_flops = {"conv_fwd": flops_pass, "conv_bwd": 2 * flops_pass, "conv_bwd_input": flops_pass,
+                "conv_bwd_weight_partial": flops_pass}
+    step_ops = list(ops)
     dense = c.groups == 1 and min(c.c_in, c.c_out) >= 16
     compute_peak = MFMA_F32_PEAK_TFLOPS if dense else VALU_F32_PEAK_TFLOPS
 
     def roof_time(k):
         return max(op_bytes[k] / (HBM_PEAK_GBS * 1e9), op_flops.get(k, 0) / (compute_peak * 1e12))
 
-    dom = max(op_us, key=op_us.get)
+    dom = max(step_ops, key=op_us.get)
     t_hbm = op_bytes[dom] / (HBM_PEAK_GBS * 1e9)
     t_cmp = op_flops.get(dom, 0) / (compute_peak * 1e12)
     if t_cmp > t_hbm:
@@ -282,7 +297,7 @@ def main():
         "step_bytes": step_bytes, "step_flops": step_flops,
         "hbm_roofline_frac": round(step_bytes / (HBM_PEAK_GBS * 1e9) / step_s, 4),
         "compute_roofline_frac": round(step_flops / (compute_peak * 1e12) / step_s, 4),
-        "roofline_frac_step": round(sum(roof_time(k) for k in op_bytes) / step_s, 4),
+        "roofline_frac_step": round(sum(roof_time(k) for k in step_ops) / step_s, 4),
         "roofline": roof,
         "ops_us": {k: round(v, 2) for k, v in op_us.items()},
         "wall_s_timed": round(wall, 4),
@@ -329,11 +344,21 @@ def cpu_baseline(wl, T, L, S, s):
             "cpu": platform.processor() or platform.machine()}
 
 
-def summarize(d):
-    """Text summary of a rocprofv3 output directory (kernel stats and/or
-    counter collection CSVs), for the files committed under profiles/."""
-    d = pathlib.Path(d)
-    stats = sorted(glob.glob(str(d / "**" / "*kernel_stats.csv"), recursive=True))
+def summarize(dirs, traffic_op=None, traffic_kernels=None):
+    """Text summary of rocprofv3 output directories (kernel stats and/or
+    counter collection CSVs), for the files committed under profiles/.
+
+    With traffic_op / traffic_kernels and FETCH_SIZE / WRITE_SIZE runs of a
+    bench.py command, also the HBM traffic per launch of that operation: each
+    counter's KB per dispatch, scaled by what the same counter reads for the
+    plain device copy of COPY_CAL_BYTES each way that the command runs
+    (`__amd_rocclr_copyBuffer`), summed over the operation's kernels, as a
+    `traffic_json:` line that bench.py reads back while the sources match."""
+    stats, cc = [], []
+    for d in dirs:
+        d = pathlib.Path(d)
+        stats += sorted(glob.glob(str(d / "**" / "*kernel_stats.csv"), recursive=True))
+        cc += sorted(glob.glob(str(d / "**" / "*counter_collection.csv"), recursive=True))
     for f in stats:
         print(f"## kernel statistics ({pathlib.Path(f).name})\n")
         print("| kernel | calls | average us | min us | max us | share |")
@@ -342,19 +367,45 @@ def summarize(d):
             print(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
         print()
-    cc = sorted(glob.glob(str(d / "**" / "*counter_collection.csv"), recursive=True))
-    if cc:
-        agg = {}
-        for f in cc:
-            for r in csv.DictReader(open(f)):
-                k = (r["Kernel_Name"], r["Counter_Name"])
-                agg.setdefault(k, []).append(float(r["Counter_Value"]))
-        print("## counters (mean per dispatch)\n")
-        print("| kernel | counter | mean | dispatches |")
-        print("|---|---|---:|---:|")
-        for (kname, cname), v in sorted(agg.items()):
-            print(f"| `{kname[:110]}` | {cname} | {sum(v) / len(v):.1f} | {len(v)} |")
-        print()
+    if not cc:
+        return 0
+    agg = {}
+    for f in cc:
+        for r in csv.DictReader(open(f)):
+            k = (r["Kernel_Name"], r["Counter_Name"])
+            agg.setdefault(k, []).append(float(r["Counter_Value"]))
+    mean = {k: sum(v) / len(v) for k, v in agg.items()}
+    print("## counters (mean per dispatch)\n")
+    print("| kernel | counter | mean | dispatches |")
+    print("|---|---|---:|---:|")
+    for (kname, cname), v in sorted(agg.items()):
+        print(f"| `{kname[:110]}` | {cname} | {sum(v) / len(v):.1f} | {len(v)} |")
+    print()
+    if not (traffic_op and traffic_kernels):
+        return 0
+    cal = COPY_CAL_BYTES / 1024
+    copy = [k for (k, c) in mean if "copyBuffer" in k]
+    if not copy:
+        print("no calibration copy kernel found")
+        return 1
+    # the calibration copy is the largest copy dispatch (smaller device copies run the same kernel)
+    big = {c: max(agg[(copy[0], c)]) for c in ("FETCH_SIZE", "WRITE_SIZE") if (copy[0], c) in agg}
+    fs = cal / big["FETCH_SIZE"] if "FETCH_SIZE" in big else None
+    wsc = cal / big["WRITE_SIZE"] if "WRITE_SIZE" in big else None
+    subs = [t for t in traffic_kernels.split(";") if t]
+    names = sorted({k for (k, c) in mean if any(t in k for t in subs)})
+    fetch = sum(mean.get((k, "FETCH_SIZE"), 0.0) for k in names) * 1024 * (fs or 0)
+    write = sum(mean.get((k, "WRITE_SIZE"), 0.0) for k in names) * 1024 * (wsc or 0)
+    print(f"Calibration: the {COPY_CAL_BYTES >> 20} MiB device copy reads FETCH_SIZE "
+          f"{big.get('FETCH_SIZE', float('nan')):.1f} KB and WRITE_SIZE "
+          f"{big.get('WRITE_SIZE', float('nan')):.1f} KB, so counter KB are scaled by "
+          f"{fs or float('nan'):.4f} (reads) and {wsc or float('nan'):.4f} (writes).\n")
+    print(f"Operation `{traffic_op}` = " + " + ".join(f"`{k[:80]}`" for k in names) +
+          f": {fetch / 1e6:.1f} MB read + {write / 1e6:.1f} MB written per launch.\n")
+    rec = {"op": traffic_op, "kernels": [k[:120] for k in names], "fetch_bytes": round(fetch),
+           "write_bytes": round(write), "fetch_scale": round(fs or 0, 4), "write_scale": round(wsc or 0, 4),
+           "source_hash": kernel_source_hash()}
+    print("traffic_json: " + json.dumps(rec))
     return 0
 
 

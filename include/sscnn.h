@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSCNN_ABI_VERSION 1
+#define SSCNN_ABI_VERSION 2
 
 /* Status codes. */
 #define SSCNN_OK 0
@@ -182,6 +182,28 @@ int sscnn_conv_bwd_weight_partial(const sscnn_conv_t *conv, const float *x,
                                   float *grad_w_part, float *grad_b_part,
                                   void *workspace, size_t workspace_bytes,
                                   void *stream);
+
+/*
+ * The whole backward of this shard in one call: grad_input as
+ * sscnn_conv_bwd_input and the _Partial grad_weight / grad_bias as
+ * sscnn_conv_bwd_weight_partial (blog, DTensor section: one
+ * convolution_backward produces grad_input, grad_weight and grad_bias from
+ * the same grad_output; kwkr.cn retelling, section 2.2).  Results equal the
+ * two separate calls up to float32 summation order (grad_input is
+ * bitwise equal); for depthwise layers one kernel reads each grad_output tile
+ * once for both gradients.
+ *   x, x_halo             as for sscnn_conv_bwd_weight_partial
+ *   grad_y, grad_y_halo   as for sscnn_conv_bwd_input
+ *   weight                (c_out, c_in/groups, k, k)
+ *   grad_x                output, as for sscnn_conv_bwd_input
+ *   grad_w_part, grad_b_part (nullable), workspace, workspace_bytes
+ *                         as for sscnn_conv_bwd_weight_partial (same workspace size)
+ * grad_x must not alias any input.
+ */
+int sscnn_conv_bwd(const sscnn_conv_t *conv, const float *x, const float *x_halo,
+                   const float *grad_y, const float *grad_y_halo, const float *weight,
+                   float *grad_x, float *grad_w_part, float *grad_b_part,
+                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Reduction of partial gradients into the replicated gradient (blog, DTensor

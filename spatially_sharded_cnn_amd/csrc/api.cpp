@@ -222,6 +222,34 @@ int sscnn_conv_bwd_weight_partial(const sscnn_conv_t* conv, const float* x, cons
                       "conv_bwd_weight_partial launch");
 }
 
+int sscnn_conv_bwd(const sscnn_conv_t* conv, const float* x, const float* x_halo, const float* grad_y,
+                   const float* grad_y_halo, const float* weight, float* grad_x, float* grad_w_part,
+                   float* grad_b_part, void* workspace, size_t workspace_bytes, void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    TRY(need(x, "x"));
+    if (g.hl + g.hr) TRY(need(x_halo, "x_halo")); else TRY(optional(x_halo, "x_halo"));
+    TRY(need(grad_y, "grad_y"));
+    if (g.ghl + g.ghr) TRY(need(grad_y_halo, "grad_y_halo")); else TRY(optional(grad_y_halo, "grad_y_halo"));
+    TRY(need(weight, "weight"));
+    TRY(need(grad_x, "grad_x"));
+    TRY(need(grad_w_part, "grad_w_part"));
+    TRY(optional(grad_b_part, "grad_b_part"));
+    if (grad_x == x || grad_x == x_halo || grad_x == grad_y || grad_x == grad_y_halo)
+        return fail(SSCNN_EINVAL, "grad_x aliases an input");
+    const size_t ws_need = kernels_bwd_weight_workspace_bytes(g);
+    if (ws_need) {
+        if (!workspace || workspace_bytes < ws_need)
+            return fail(SSCNN_EWORKSPACE, "workspace of %zu bytes given, %zu needed",
+                        workspace ? workspace_bytes : (size_t)0, ws_need);
+        TRY(need(workspace, "workspace"));
+    }
+    return hip_status(kernels_conv_bwd(g, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_part,
+                                       grad_b_part, ws_need ? workspace : nullptr, (hipStream_t)stream),
+                      "conv_bwd launch");
+}
+
 int sscnn_partial_reduce(const float* const* parts, int32_t nparts, int64_t count, float* out,
                          void* stream)
 {

@@ -14,5 +14,9 @@ hipError_t launch_dw_bwd_input(const Geom& g, const float* gy, const float* gyh,
                                float* gx, hipStream_t st);
 hipError_t launch_dw_bwd_weight(const Geom& g, const float* x, const float* xh, const float* gy,
                                 float* gw, float* gb, void* ws, hipStream_t st);
+// grad_input and the grad_weight / grad_bias partials in one pass over grad_output
+// (workspace as for launch_dw_bwd_weight).
+hipError_t launch_dw_bwd(const Geom& g, const float* x, const float* xh, const float* gy, const float* gyh,
+                         const float* w, float* gx, float* gw, float* gb, void* ws, hipStream_t st);
 
 }  // namespace sscnn

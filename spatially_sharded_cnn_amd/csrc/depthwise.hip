@@ -7,254 +7,408 @@
 // of compulsory traffic: below the FP32 ridge of the chip, so these are
 // bandwidth kernels.  Their job is to keep HBM busy while the FMAs run:
 //
-//  * persistent workgroups (as many as fit on the chip) walk a list of output
-//    tiles (TH rows x TW columns of one (n, c) plane).  Each tile's input --
-//    the shard's own columns with 16-byte loads, k/2 side columns from the halo
-//    buffer at the shard's edges (or from the slice itself inside the shard),
-//    zero rows above and below the image -- is fetched into registers one tile
-//    AHEAD, so the HBM reads of tile t+1 are in flight while tile t computes;
-//    the registers are then written to an LDS tile;
+//  * persistent workgroups walk a list of output tiles (TH rows x TW columns
+//    of one (n, c) plane).  A tile's extended input lives in LDS as a main
+//    region -- the shard's own TW columns of rows i0-P .. i0+TH+P-1, brought
+//    in by buffer loads that write LDS directly (no registers; rows above and
+//    below the plane fall outside the buffer and read as zeros) -- and a side
+//    region with the P columns on either side (from the halo buffer at the
+//    shard's edges, from the slice itself inside it).  Each workgroup has two
+//    tile buffers: the loads of its next tile run while it computes the
+//    current one, with one barrier per tile; a tile's results are stored
+//    after the next tile's barrier;
 //  * each thread owns RH rows x 4 columns of outputs, slides down its RH+k-1
-//    input rows reading 4+k-1 values per row from LDS (16-byte reads), and
-//    issues k*k*4*RH fused multiply-adds whose weight operand is a scalar
-//    register (the plane's k*k weights are wave-uniform);
-//  * grad_input is the same kernel on the grad_output tile with the kernel
-//    flipped in both axes (stride 1, pad k/2, so the grad_output halo has the
-//    same widths as the input halo);
-//  * grad_weight: each thread accumulates all k*k taps over its RH x 4 outputs
-//    (its grad_output block is prefetched alongside the input tile) and keeps
-//    them across the consecutive tiles of one channel that its workgroup
-//    owns; at a channel change the waves reduce them with cross-lane swaps,
-//    the workgroup adds the waves' totals in a fixed order and writes one
-//    partial; a second kernel sums a channel's partials in workgroup order.
-//    No atomics: results are bitwise reproducible.
+//    input rows reading 4+k-1 values per row from LDS (16-byte reads of rows
+//    whose lane groups sit a multiple of 64 floats apart, which gfx950 serves
+//    at full rate), and issues k*k*4*RH fused multiply-adds with the plane's
+//    weights held in vector registers;
+//  * grad_input is the same computation on the grad_output tile with the
+//    kernel flipped in both axes (stride 1, pad k/2, so the grad_output halo
+//    has the same widths as the input halo);
+//  * grad_weight: each thread accumulates all k*k taps (and the grad_bias
+//    sum) over its RH x 4 outputs and keeps them across the consecutive tiles
+//    of one channel that its workgroup owns; at a channel change the waves
+//    reduce them with cross-lane swaps, the workgroup adds the waves' totals
+//    in a fixed order and writes one partial; a second kernel sums a
+//    channel's partials in workgroup order.  No atomics: results are bitwise
+//    reproducible;
+//  * the fused backward runs both on one grad_output tile: a 512-thread
+//    workgroup whose first half computes grad_input from the grad_output tile
+//    and whose second half accumulates grad_weight from the input tile and
+//    the centre of that same grad_output tile, so grad_output is read from
+//    HBM once for both gradients (the pair that a convolution backward call
+//    returns together).
 #include "internal.h"
 #include "depthwise.h"
-
-#ifndef SSCNN_DW_WGRAD_WAVES
-#define SSCNN_DW_WGRAD_WAVES 3
-#endif
 
 namespace sscnn {
 namespace {
 
 struct DwArgs {
-    const float* x;      // (N*C, H, W) shard slice (input, or grad_output for grad_input)
-    const float* halo;   // (N*C, H, 2P)
+    const float* src;    // (N*C, H, W) tile source: the input (forward), grad_output (grad_input)
+    const float* src_h;  // (N*C, H, 2P) its halo
+    const float* x;      // (N*C, H, W) input, for grad_weight
+    const float* x_h;    // (N*C, H, 2P) its halo
+    const float* g;      // (N*C, H, W) grad_output, for the stand-alone grad_weight kernel
     const float* w;      // (C, k, k)
     const float* b;      // (C) or null
-    float* y;            // (N*C, H, W)
-    const float* g;      // grad_output (N*C, H, W) for grad_weight
+    float* out;          // (N*C, H, W) output or grad_input
     float* ws;           // grad_weight partials (C, up to N * tiles_h * tiles_w, k*k + 1)
     int H, W, C, N, tiles_h, tiles_w, ntiles;   // ntiles = N * C * tiles_h * tiles_w
 };
 
-// Tile t -> (plane, tile row, tile column), column fastest.
+// One tile: its plane and channel, and the rows and columns it covers.  The
+// last tile of a column is moved up to end at row H (i0 = H - TH) so every
+// row it computes is a real row and its stores need no predicate; it then
+// recomputes rows [i0, i_own) of the tile above it bit-identically, and
+// i_own = trow * TH is the first row it owns (grad_weight counts only those).
 struct TileIdx {
-    int plane, c, n, trow, tcol, i0, j0;
+    int plane, c, n, i0, i_own, j0;
 };
 
-// With clamp, the last row tile is moved up to end at row H (it then
-// recomputes some rows of the previous tile, bit-identically), so every row a
-// forward tile computes is a real row and its stores need no predicate.
-__device__ __forceinline__ TileIdx decode(const DwArgs& a, int t, int th, int tw, bool clamp)
+__device__ __forceinline__ void place(TileIdx& d, const DwArgs& a, int trow, int tcol, int th, int tw)
+{
+    d.plane = d.n * a.C + d.c;
+    d.i_own = trow * th;
+    d.i0 = d.i_own + th > a.H ? a.H - th : d.i_own;
+    d.j0 = tcol * tw;
+}
+
+// Plane-major order (forward and grad_input): t = (plane, row, column).
+__device__ __forceinline__ TileIdx decode_plane_major(const DwArgs& a, int t, int th, int tw)
 {
     TileIdx d;
-    d.tcol = t % a.tiles_w;
+    const int tcol = t % a.tiles_w;
     t /= a.tiles_w;
-    d.trow = t % a.tiles_h;
-    d.plane = t / a.tiles_h;
-    d.c = d.plane % a.C;
-    d.n = d.plane / a.C;
-    d.i0 = d.trow * th;
-    if (clamp && d.i0 + th > a.H) d.i0 = a.H - th;
-    d.j0 = d.tcol * tw;
+    const int trow = t % a.tiles_h;
+    const int plane = t / a.tiles_h;
+    d.c = plane % a.C;
+    d.n = plane / a.C;
+    place(d, a, trow, tcol, th, tw);
     return d;
 }
 
-// Input tile.  LDS column cc holds extended column j0 + cc, i.e. shard
-// column j0 + cc - P; tile row rr holds image row i0 - P + rr.  A thread's
-// 4 + k - 1 inputs per row start at a 16-byte boundary, so they are read with
-// 16-byte LDS reads (the fill pays unaligned 4-byte writes instead, once per
-// element, against ~2.5 reads per element).
-// LDS row pitch (floats): a multiple of 4 (16-byte aligned rows) such that
-// the TX lanes of a wave that read one tile row and the next TX lanes, RH
-// rows further down, sit a multiple of 4*TX floats apart.  gfx950 serves
-// 16-byte LDS reads of such lane groups at full rate (~240 B/clk per CU,
-// measured) and at half rate for other pitches.
-constexpr int lds_pitch(int lw, int rh, int tx)
+// Channel-major order (grad_weight): t = (c, n, row, column), so a
+// contiguous run of tiles mostly stays on one channel.
+__device__ __forceinline__ TileIdx decode_channel_major(const DwArgs& a, int t, int th, int tw)
 {
-    int ls = (lw + 3) & ~3;
-    while ((rh * ls) % (4 * tx) != 0) ls += 4;
-    return ls;
+    TileIdx d;
+    const int tcol = t % a.tiles_w;
+    t /= a.tiles_w;
+    const int trow = t % a.tiles_h;
+    t /= a.tiles_h;
+    d.n = t % a.N;
+    d.c = t / a.N;
+    place(d, a, trow, tcol, th, tw);
+    return d;
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource of a plane (stride 0, num_records = bytes): loads at
+// offsets outside [0, bytes) return zeros.  Wave-uniform, in scalar registers.
+__device__ __forceinline__ i32x4 plane_rsrc(const float* base, int bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+    r.z = __builtin_amdgcn_readfirstlane(bytes);
+    r.w = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from the buffer at byte offset voff straight into LDS at
+// lds + 16 * lane (lds wave-uniform).  Issued as inline assembly so that the
+// compiler does not treat every later LDS read as depending on it (it would
+// wait for all outstanding loads first); the kernels wait for these loads
+// themselves with s_waitcnt vmcnt(0) before the barrier that publishes a tile.
+// s_nop: one wait state between writing M0 and the load that reads it.
+__device__ __forceinline__ void dma16(const i32x4& rs, const float* lds, int voff)
+{
+    const int l = __builtin_amdgcn_readfirstlane((int)(uint32_t)reinterpret_cast<uintptr_t>(lds));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :: "v"(voff), "s"(l), "s"(rs) : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_vmem()
+{
+    // gfx9 s_waitcnt: vmcnt = 0, expcnt[6:4] = 7 and lgkmcnt[11:8] = 15 (no wait on those)
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+}
+
+// The extended input of one tile in LDS, for a 256-thread group (TX x TY
+// threads, each owning RH rows x 4 columns of outputs).
+//   main  LH rows x TW floats, pitch TW: main[rr][c] = plane[i0 - P + rr][j0 + c]
+//   side  LH rows x 8 floats:  side[rr][4 - P + e] = column j0 - P + e   (e < P)
+//                              side[rr][4 + e]     = column j0 + TW + e  (e < P)
 template <int K, int TX, int TY, int RH>
 struct Tile {
     static constexpr int P = K / 2;
     static constexpr int NT = TX * TY;
+    static constexpr int NWAVE = NT / 64;
     static constexpr int TW = 4 * TX;
     static constexpr int TH = RH * TY;
-    static constexpr int LW = TW + K - 1;
-    static constexpr int LS = lds_pitch(LW, RH, TX);
     static constexpr int LH = TH + K - 1;
-    static constexpr int FLOATS = LH * LS;
-    static constexpr int Q = TW / 4;
-    static constexpr int NV = (LH * Q + NT - 1) / NT;          // 16-byte loads per thread
-    static constexpr int NS = (LH * 2 * P + NT - 1) / NT;      // side-column loads per thread
+    static constexpr int MAIN = LH * TW;
+    static constexpr int PIECES = LH * TX;                 // 16-byte pieces of the main region
+    static constexpr int NLOAD = (PIECES + 63) / 64;       // 64-lane direct loads per tile
+    static constexpr int SP = 8;
+    static constexpr int FLOATS = MAIN + LH * SP;
+    static constexpr int NS = (LH * 2 * P + NT - 1) / NT;  // side values per thread
+    static_assert(NT % 64 == 0, "whole waves");
+    static_assert((RH * TW) % (4 * TX) == 0, "row groups a multiple of the lane group apart");
 
-    struct Regs {
-        float4 v[NV];
+    struct Side {
         float s[NS];
     };
 
-    // Global -> registers (all loads issued back to back).
-    __device__ static void fetch(Regs& R, const float* __restrict__ xp, const float* __restrict__ hp,
-                                 int H, int W, int i0, int j0)
+    // Main region: buffer loads straight into LDS.  Piece f (lane f % 64 of
+    // load f / 64) is 16 bytes of row f / TX; LDS receives load m's 64 pieces
+    // contiguously, which is exactly main[] since TW = 4 TX.  Rows outside
+    // the plane have offsets outside the buffer (negative offsets wrap to
+    // huge ones) and read as zeros.
+    __device__ static void load_main(float* buf, const float* plane, int H, int W, int i0, int j0, int tid)
     {
-        const int tid = threadIdx.x;
+        const i32x4 rs = plane_rsrc(plane, H * W * 4);
+        const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int idx = tid + k * NT;
-            const int rr = idx / Q, q = idx - rr * Q;
-            const int r = i0 - P + rr;
-            R.v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (idx < LH * Q && r >= 0 && r < H)
-                R.v[k] = *reinterpret_cast<const float4*>(xp + (int64_t)r * W + j0 + 4 * q);
+        for (int k = 0; k < (NLOAD + NWAVE - 1) / NWAVE; ++k) {
+            const int m = wave + k * NWAVE;                    // wave-uniform
+            if (m < NLOAD) {
+                const int f = m * 64 + lane;
+                const int rr = f / TX, q = f - rr * TX;
+                const int off = ((i0 - P + rr) * W + j0 + 4 * q) * 4;
+                if (f < PIECES) dma16(rs, buf + m * 256, off);
+            }
         }
+    }
+
+    // Side columns: ordinary loads into registers, written by put_side().
+    __device__ static void load_side(Side& S, const float* __restrict__ xp, const float* __restrict__ hp,
+                                     int H, int W, int i0, int j0, int tid)
+    {
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
             const int idx = tid + k * NT;
             const int rr = idx / (2 * P), e = idx - rr * (2 * P);
             const int r = i0 - P + rr;
             const int xcol = j0 + (e < P ? e : TW + e) - P;     // shard column, may be < 0 or >= W
-            R.s[k] = 0.f;
+            S.s[k] = 0.f;
             if (idx < LH * 2 * P && r >= 0 && r < H) {
-                if (xcol < 0) R.s[k] = hp[(int64_t)r * (2 * P) + (xcol + P)];
-                else if (xcol >= W) R.s[k] = hp[(int64_t)r * (2 * P) + P + (xcol - W)];
-                else R.s[k] = xp[(int64_t)r * W + xcol];
+                if (xcol < 0) S.s[k] = hp[(int64_t)r * (2 * P) + (xcol + P)];
+                else if (xcol >= W) S.s[k] = hp[(int64_t)r * (2 * P) + P + (xcol - W)];
+                else S.s[k] = xp[(int64_t)r * W + xcol];
             }
         }
     }
 
-    // Registers -> LDS tile.
-    __device__ static void put(float* __restrict__ tile, const Regs& R)
+    __device__ static void put_side(float* buf, const Side& S, int tid)
     {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int idx = tid + k * NT;
-            if (idx < LH * Q) {
-                const int rr = idx / Q, q = idx - rr * Q;
-                float* d = tile + rr * LS + P + 4 * q;
-                d[0] = R.v[k].x;
-                d[1] = R.v[k].y;
-                d[2] = R.v[k].z;
-                d[3] = R.v[k].w;
-            }
-        }
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
             const int idx = tid + k * NT;
             if (idx < LH * 2 * P) {
                 const int rr = idx / (2 * P), e = idx - rr * (2 * P);
-                tile[rr * LS + (e < P ? e : TW + e)] = R.s[k];
+                buf[MAIN + rr * SP + (e < P ? 4 - P + e : 4 + e - P)] = S.s[k];
             }
         }
     }
 
-    // 4 + K - 1 consecutive tile values starting at a 16-byte aligned column.
-    __device__ static void read_row(const float* __restrict__ src, float (&in)[4 + K - 1])
-    {
-        const float4 a = *reinterpret_cast<const float4*>(src);
-        in[0] = a.x; in[1] = a.y; in[2] = a.z; in[3] = a.w;
-        if constexpr (K - 1 >= 4) {
-            const float4 c = *reinterpret_cast<const float4*>(src + 4);
-            in[4] = c.x; in[5] = c.y; in[6] = c.z; in[7] = c.w;
-            if constexpr (K - 1 == 6) {
-                const float2 d = *reinterpret_cast<const float2*>(src + 8);
-                in[8] = d.x; in[9] = d.y;
-            }
-        } else {
-            const float2 d = *reinterpret_cast<const float2*>(src + 4);
-            in[4] = d.x; in[5] = d.y;
+    // Where a thread's window of row R (4 + K - 1 values from column 4 tx - P)
+    // comes from: A = the 4 floats left of its own 4 (side region for tx = 0),
+    // B = its own 4, C = the 4 on the right (side region for tx = TX - 1).
+    // A and C move down by a per-lane pitch; next() advances them one row
+    // at a time (the empty asm keeps the compiler from precomputing and
+    // holding every row's offset).
+    typedef float nf4 __attribute__((ext_vector_type(4)));
+    typedef float nf2 __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) const float lfloat;
+    typedef __attribute__((address_space(3))) const nf4 lfloat4;
+    typedef __attribute__((address_space(3))) const nf2 lfloat2;
+
+    struct Win {
+        lfloat* a;
+        lfloat* b;
+        lfloat* c;
+        int sa, sc;        // row pitches of a and c
+        __device__ void next()
+        {
+            a += sa;
+            c += sc;
+            b += TW;
+            asm volatile("" : "+v"(a), "+v"(c));
         }
+    };
+
+    __device__ static Win window(const float* buf_generic, int tx, int ty)
+    {
+        lfloat* buf = (lfloat*)buf_generic;
+        Win w;
+        const int r0 = ty * RH;
+        w.b = buf + r0 * TW + 4 * tx;
+        if (tx == 0) { w.a = buf + MAIN + r0 * SP; w.sa = SP; }
+        else { w.a = w.b - 4; w.sa = TW; }
+        if (tx == TX - 1) { w.c = buf + MAIN + r0 * SP + 4; w.sc = SP; }
+        else { w.c = w.b + 4; w.sc = TW; }
+        return w;
+    }
+
+    __device__ static void read_row(const Win& w, float (&in)[4 + K - 1])
+    {
+        const nf4 bb = *reinterpret_cast<lfloat4*>(w.b);
+        if constexpr (P == 3) {
+            const nf4 aa = *reinterpret_cast<lfloat4*>(w.a);
+            const nf4 cc = *reinterpret_cast<lfloat4*>(w.c);
+            in[0] = aa.y; in[1] = aa.z; in[2] = aa.w;
+            in[7] = cc.x; in[8] = cc.y; in[9] = cc.z;
+        } else if constexpr (P == 2) {
+            const nf2 aa = *reinterpret_cast<lfloat2*>(w.a + 2);
+            const nf2 cc = *reinterpret_cast<lfloat2*>(w.c);
+            in[0] = aa.x; in[1] = aa.y;
+            in[6] = cc.x; in[7] = cc.y;
+        } else {
+            in[0] = w.a[3];
+            in[5] = w.c[0];
+        }
+        in[P] = bb.x; in[P + 1] = bb.y; in[P + 2] = bb.z; in[P + 3] = bb.w;
     }
 };
 
+// Forward / grad_input on one LDS tile: acc[i][jj] += sum over (kh, kw) of
+// wr[kh*K + kw] * (extended input)[row i + kh, column jj + kw] for the
+// thread's RH x 4 outputs.  Each row is read one row ahead of its FMAs; the
+// scheduling barriers keep that order.
+template <int K, int TX, int TY, int RH>
+__device__ __forceinline__ void conv_tile(const float* buf, const float (&wr)[K * K], float (&acc)[RH][4],
+                                          int tx, int ty)
+{
+    using T = Tile<K, TX, TY, RH>;
+    typename T::Win w = T::window(buf, tx, ty);
+    float cur[4 + K - 1], nxt[4 + K - 1];
+    T::read_row(w, cur);
+#pragma unroll
+    for (int r = 0; r < RH + K - 1; ++r) {
+        if (r + 1 < RH + K - 1) {
+            w.next();
+            T::read_row(w, nxt);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < RH; ++i) {
+            const int kh = r - i;
+            if (kh < 0 || kh >= K) continue;
+#pragma unroll
+            for (int kw = 0; kw < K; ++kw)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    acc[i][jj] = __builtin_fmaf(wr[kh * K + kw], cur[jj + kw], acc[i][jj]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 4 + K - 1; ++q) cur[q] = nxt[q];
+    }
+}
+
+// grad_weight on one LDS input tile: acc[kh*K + kw] += sum over the thread's
+// outputs (i, jj) of gv[i][jj] * (extended input)[row i + kh, column jj + kw].
+template <int K, int TX, int TY, int RH>
+__device__ __forceinline__ void wgrad_tile(const float* buf, const float (&gv)[RH][4],
+                                           float (&acc)[K * K + 1], int tx, int ty)
+{
+    using T = Tile<K, TX, TY, RH>;
+    typename T::Win w = T::window(buf, tx, ty);
+    float cur[4 + K - 1], nxt[4 + K - 1];
+    T::read_row(w, cur);
+#pragma unroll
+    for (int r = 0; r < RH + K - 1; ++r) {
+        if (r + 1 < RH + K - 1) {
+            w.next();
+            T::read_row(w, nxt);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < RH; ++i) {
+            const int kh = r - i;
+            if (kh < 0 || kh >= K) continue;
+#pragma unroll
+            for (int kw = 0; kw < K; ++kw)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    acc[kh * K + kw] = __builtin_fmaf(gv[i][jj], cur[jj + kw], acc[kh * K + kw]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 4 + K - 1; ++q) cur[q] = nxt[q];
+    }
+}
+
+// The plane's weights (flipped in both axes for grad_input) in vector
+// registers: loaded through the scalar cache, then copied, because gfx950
+// issues v_fmac_f32 at about twice the rate when no operand is a scalar
+// register (measured: ~119 vs ~70 TFLOP/s chip-wide).
+template <int K, bool FLIP>
+__device__ __forceinline__ void load_weights(const float* w, int c, float (&wr)[K * K])
+{
+    const auto wp = as_const(w) + c * K * K;
+#pragma unroll
+    for (int k = 0; k < K * K; ++k) wr[k] = to_vgpr(wp[FLIP ? K * K - 1 - k : k]);
+}
+
+template <int RH>
+__device__ __forceinline__ void store_rows(float* out, const TileIdx& d, int H, int W, int tx, int ty,
+                                           const float (&acc)[RH][4])
+{
+    float* yp = out + (int64_t)d.plane * H * W + d.j0 + 4 * tx;
+#pragma unroll
+    for (int i = 0; i < RH; ++i)
+        *reinterpret_cast<float4*>(yp + (int64_t)(d.i0 + ty * RH + i) * W) =
+            make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+}
+
 template <int K, int TX, int TY, int RH, bool FLIP>
-__global__ void __launch_bounds__(TX * TY) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ void __launch_bounds__(TX * TY)
 dw_conv_kernel(DwArgs a)
 {
     using T = Tile<K, TX, TY, RH>;
     constexpr int P = T::P;
-    __shared__ __align__(16) float tile[T::FLOATS];
-    typename T::Regs R;
+    __shared__ __align__(16) float buf[2][T::FLOATS];
+    typename T::Side S;
+    const int tid = threadIdx.x;
+    const int tx = tid % TX, ty = tid / TX;
+    const int64_t HW = (int64_t)a.H * a.W;
+    auto issue = [&](int t, float* b) {
+        const TileIdx e = decode_plane_major(a, t, T::TH, T::TW);
+        T::load_main(b, a.src + e.plane * HW, a.H, a.W, e.i0, e.j0, tid);
+        T::load_side(S, a.src + e.plane * HW, a.src_h + (int64_t)e.plane * a.H * (2 * P), a.H, a.W, e.i0,
+                     e.j0, tid);
+    };
     int t = blockIdx.x;
     if (t >= a.ntiles) return;
-    {
-        const TileIdx d = decode(a, t, T::TH, T::TW, true);
-        T::fetch(R, a.x + (int64_t)d.plane * a.H * a.W, a.halo + (int64_t)d.plane * a.H * (2 * P),
-                 a.H, a.W, d.i0, d.j0);
-    }
-    const int tx = threadIdx.x % TX, ty = threadIdx.x / TX;
-    for (; t < a.ntiles; t += gridDim.x) {
-        const TileIdx d = decode(a, t, T::TH, T::TW, true);
-        T::put(tile, R);
+    issue(t, buf[0]);
+    // A tile's stores are issued after the next tile's barrier, so the wait
+    // before that barrier only covers operations a whole tile old.
+    float acc[RH][4];
+    TileIdx dprev{};
+    for (int it = 0; t < a.ntiles; t += gridDim.x, ++it) {
+        float* cb = buf[it & 1];
+        const TileIdx d = decode_plane_major(a, t, T::TH, T::TW);
+        T::put_side(cb, S, tid);
+        wait_vmem();
         lds_barrier();
-        const int tn = t + gridDim.x;
-        if (tn < a.ntiles) {
-            const TileIdx e = decode(a, tn, T::TH, T::TW, true);
-            T::fetch(R, a.x + (int64_t)e.plane * a.H * a.W, a.halo + (int64_t)e.plane * a.H * (2 * P),
-                     a.H, a.W, e.i0, e.j0);
-        }
-        // the plane's weights: wave-uniform, kept in scalar registers
-        // The plane's weights are wave-uniform: loaded through the scalar
-        // cache, then copied to vector registers, because gfx950 issues
-        // v_fmac_f32 at about twice the rate when no operand is a scalar
-        // register (measured: ~119 vs ~70 TFLOP/s chip-wide).
+        if (it > 0) store_rows<RH>(a.out, dprev, a.H, a.W, tx, ty, acc);
+        if (t + (int)gridDim.x < a.ntiles) issue(t + gridDim.x, buf[(it + 1) & 1]);
         float wr[K * K];
-        const auto wp = as_const(a.w) + d.c * K * K;
-#pragma unroll
-        for (int k = 0; k < K * K; ++k) wr[k] = to_vgpr(wp[FLIP ? K * K - 1 - k : k]);
+        load_weights<K, FLIP>(a.w, d.c, wr);
         const float bias = a.b ? as_const(a.b)[d.c] : 0.f;
-
-        float acc[RH][4];
 #pragma unroll
         for (int i = 0; i < RH; ++i)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) acc[i][jj] = bias;
-        // Each row is read from LDS one row ahead of its FMAs (a whole row of
-        // FMAs covers the read latency); the scheduling barriers keep that
-        // order, which the compiler would otherwise tighten to a few FMAs.
-        const float* base = tile + (ty * RH) * T::LS + 4 * tx;
-        float cur[4 + K - 1], nxt[4 + K - 1];
-        T::read_row(base, cur);
-#pragma unroll
-        for (int r = 0; r < RH + K - 1; ++r) {
-            if (r + 1 < RH + K - 1) T::read_row(base + (r + 1) * T::LS, nxt);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < RH; ++i) {
-                const int kh = r - i;
-                if (kh < 0 || kh >= K) continue;
-#pragma unroll
-                for (int kw = 0; kw < K; ++kw)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        acc[i][jj] = __builtin_fmaf(wr[kh * K + kw], cur[jj + kw], acc[i][jj]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int q = 0; q < 4 + K - 1; ++q) cur[q] = nxt[q];
-        }
-        float* yp = a.y + (int64_t)d.plane * a.H * a.W + d.j0 + 4 * tx;
-#pragma unroll
-        for (int i = 0; i < RH; ++i)
-            *reinterpret_cast<float4*>(yp + (int64_t)(d.i0 + ty * RH + i) * a.W) =
-                make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-        lds_barrier();   // the tile is rewritten by the next iteration's put()
+        conv_tile<K, TX, TY, RH>(cb, wr, acc, tx, ty);
+        dprev = d;
     }
+    store_rows<RH>(a.out, dprev, a.H, a.W, tx, ty, acc);
 }
 
 // Sum of N per-lane values over the 64 lanes of a wave, leaving one total per
@@ -328,123 +482,201 @@ __device__ __forceinline__ int wave_sum_index(int lane)
     return j;
 }
 
-// grad_weight partial, tile by tile: the sum over a tile's outputs (i, j) of
-// G[i, j] * Xext[i - P + kh, j + kw] for every tap, plus sum G (grad_bias).
-// Tiles are numbered channel-major (c, n, tile row, tile column) and each
-// workgroup takes one contiguous run of them, so consecutive tiles usually
-// share a channel: a thread keeps its k*k + 1 sums in registers across them
-// and the workgroup reduces only when the channel changes or its run ends.
-// One reduction writes one partial; the partials of channel c are numbered by
-// workgroup from the one that owns the channel's first tile.
+// Workgroups of the grad_weight kernels take contiguous runs of the
+// channel-major tile list: workgroup w owns tiles [floor(wT/G), floor((w+1)T/G)).
+// One flush per (workgroup, channel) writes one partial; channel c's partials
+// are numbered by workgroup from the one that owns its first tile.
 __device__ __forceinline__ int64_t tile_owner(int64_t t, int64_t T, int64_t G)
 {
     return ((t + 1) * G - 1) / T;     // the workgroup w with floor(wT/G) <= t < floor((w+1)T/G)
 }
 
+// Flush of a run, first step: each wave's totals (a reduce-scatter over its
+// lanes) into red[wave][].
+template <int NV, int NWAVE>
+__device__ __forceinline__ void flush_write(const float (&acc)[NV], float (*red)[NV + 2], int gtid)
+{
+    const int lane = gtid & 63, wave = gtid >> 6;
+    const float s = wave_sum_scatter<NV>(acc, lane);
+    const int idx = wave_sum_index<NV>(lane);
+    if (idx >= 0) red[wave][idx] = s;
+}
+
+// Second step (after a barrier): the waves' totals added in a fixed order.
+template <int NV, int NWAVE>
+__device__ __forceinline__ void flush_sum(float (*red)[NV + 2], int gtid, float* ws, int64_t slot)
+{
+    if (gtid < NV) {
+        float tot = red[0][gtid];
+#pragma unroll
+        for (int w = 1; w < NWAVE; ++w) tot += red[w][gtid];
+        ws[slot * NV + gtid] = tot;
+    }
+}
+
+// grad_weight partial (stand-alone): the input tile comes through LDS, the
+// thread's grad_output block straight from global memory.
 template <int K, int TX, int TY, int RH>
-__global__ void __launch_bounds__(TX * TY) __attribute__((amdgpu_waves_per_eu(SSCNN_DW_WGRAD_WAVES)))
+__global__ void __launch_bounds__(TX * TY) __attribute__((amdgpu_waves_per_eu(3)))
 dw_wgrad_kernel(DwArgs a)
 {
     using T = Tile<K, TX, TY, RH>;
     constexpr int P = T::P;
     constexpr int KK = K * K;
     constexpr int NV = KK + 1;                  // taps + bias
-    constexpr int NWAVE = T::NT / 64;
-    static_assert(T::NT % 64 == 0, "whole waves");
-    __shared__ __align__(16) float sh[T::FLOATS];
+    constexpr int NWAVE = T::NWAVE;
+    __shared__ __align__(16) float buf[2][T::FLOATS];
     __shared__ float red[NWAVE][NV + 2];
-    typename T::Regs R;
+    typename T::Side S;
     float4 gnext[RH];
-    const int tx = threadIdx.x % TX, ty = threadIdx.x / TX;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int tx = tid % TX, ty = tid / TX;
     const int tiles_c = a.ntiles / a.C;         // N * tiles_h * tiles_w
     const int64_t G = gridDim.x;
+    const int64_t HW = (int64_t)a.H * a.W;
     const int beg = (int)((int64_t)blockIdx.x * a.ntiles / G);
     const int end = (int)((int64_t)(blockIdx.x + 1) * a.ntiles / G);
     if (beg >= end) return;
-
-    auto decode_cm = [&](int t) {
-        TileIdx d;
-        d.tcol = t % a.tiles_w;
-        t /= a.tiles_w;
-        d.trow = t % a.tiles_h;
-        t /= a.tiles_h;
-        d.n = t % a.N;
-        d.c = t / a.N;
-        d.plane = d.n * a.C + d.c;
-        d.i0 = d.trow * T::TH;
-        d.j0 = d.tcol * T::TW;
-        return d;
-    };
-    auto fetch_all = [&](const TileIdx& d) {
-        T::fetch(R, a.x + (int64_t)d.plane * a.H * a.W, a.halo + (int64_t)d.plane * a.H * (2 * P),
-                 a.H, a.W, d.i0, d.j0);
-        const float* gp = a.g + (int64_t)d.plane * a.H * a.W + d.j0 + 4 * tx;
+    auto issue = [&](int t, float* b) {
+        const TileIdx e = decode_channel_major(a, t, T::TH, T::TW);
+        T::load_main(b, a.x + e.plane * HW, a.H, a.W, e.i0, e.j0, tid);
+        T::load_side(S, a.x + e.plane * HW, a.x_h + (int64_t)e.plane * a.H * (2 * P), a.H, a.W, e.i0, e.j0,
+                     tid);
+        const float* gp = a.g + e.plane * HW + e.j0 + 4 * tx;
 #pragma unroll
         for (int i = 0; i < RH; ++i) {
-            const int row = d.i0 + ty * RH + i;
-            gnext[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (row < a.H) gnext[i] = *reinterpret_cast<const float4*>(gp + (int64_t)row * a.W);
+            const int row = e.i0 + ty * RH + i;
+            gnext[i] = *reinterpret_cast<const float4*>(gp + (int64_t)row * a.W);
+            const float m = row >= e.i_own ? 1.f : 0.f;       // rows the tile above owns
+            gnext[i].x *= m; gnext[i].y *= m; gnext[i].z *= m; gnext[i].w *= m;
         }
     };
-
-    fetch_all(decode_cm(beg));
+    issue(beg, buf[0]);
+    int it = 0;
     for (int t = beg; t < end;) {
-        // one run: the workgroup's consecutive tiles of channel c
         const int c = t / tiles_c;
         const int run_end = min(end, (c + 1) * tiles_c);
         float acc[NV];
 #pragma unroll
         for (int k = 0; k < NV; ++k) acc[k] = 0.f;
-        for (; t < run_end; ++t) {
-            T::put(sh, R);
+        for (; t < run_end; ++t, ++it) {
+            float* cb = buf[it & 1];
+            T::put_side(cb, S, tid);
             float gv[RH][4];
 #pragma unroll
             for (int i = 0; i < RH; ++i) {
                 gv[i][0] = gnext[i].x; gv[i][1] = gnext[i].y; gv[i][2] = gnext[i].z; gv[i][3] = gnext[i].w;
                 acc[KK] += (gv[i][0] + gv[i][1]) + (gv[i][2] + gv[i][3]);
             }
+            wait_vmem();
             lds_barrier();
-            if (t + 1 < end) fetch_all(decode_cm(t + 1));
-            // Rows are read one ahead of the FMAs that use them; the
-            // scheduling barriers keep the compiler from hoisting every row's
-            // reads to the top, which would need ~100 more registers.
-            const float* base = sh + (ty * RH) * T::LS + 4 * tx;
-            float cur[4 + K - 1], nxt[4 + K - 1];
-            T::read_row(base, cur);
+            if (t + 1 < end) issue(t + 1, buf[(it + 1) & 1]);
+            wgrad_tile<K, TX, TY, RH>(cb, gv, acc, tx, ty);
+        }
+        flush_write<NV, NWAVE>(acc, red, tid);
+        lds_barrier();
+        flush_sum<NV, NWAVE>(red, tid, a.ws, (int64_t)c * tiles_c + blockIdx.x -
+                                                 tile_owner((int64_t)c * tiles_c, a.ntiles, G));
+    }
+}
+
+// Fused backward: threads [0, NT) compute grad_input from the grad_output
+// tile, threads [NT, 2 NT) accumulate grad_weight from the input tile and the
+// grad_output tile's centre.  Both halves walk the same tiles with the same
+// barriers in the same order (two loops with identical barrier sequences, so
+// each half's registers are allocated on their own).
+template <int K, int TX, int TY, int RH>
+__global__ void __launch_bounds__(2 * TX * TY) __attribute__((amdgpu_waves_per_eu(4)))
+dw_bwd_kernel(DwArgs a)
+{
+    using T = Tile<K, TX, TY, RH>;
+    constexpr int P = T::P;
+    constexpr int KK = K * K;
+    constexpr int NV = KK + 1;
+    constexpr int NWAVE = T::NWAVE;
+    __shared__ __align__(16) float bufg[2][T::FLOATS];   // grad_output tiles (extended)
+    __shared__ __align__(16) float bufx[2][T::FLOATS];   // input tiles (extended)
+    __shared__ float red[NWAVE][NV + 2];
+    typename T::Side S;
+    const bool wgrad_half = threadIdx.x >= T::NT;    // wave-uniform
+    const int tid = threadIdx.x - (wgrad_half ? T::NT : 0);
+    const int tx = tid % TX, ty = tid / TX;
+    const int tiles_c = a.ntiles / a.C;
+    const int64_t G = gridDim.x;
+    const int64_t HW = (int64_t)a.H * a.W;
+    const int beg = (int)((int64_t)blockIdx.x * a.ntiles / G);
+    const int end = (int)((int64_t)(blockIdx.x + 1) * a.ntiles / G);
+    if (beg >= end) return;
+    const float* const src = wgrad_half ? a.x : a.src;
+    const float* const src_h = wgrad_half ? a.x_h : a.src_h;
+    float (*const mybuf)[T::FLOATS] = wgrad_half ? bufx : bufg;
+    auto issue = [&](int t, float* b) {
+        const TileIdx e = decode_channel_major(a, t, T::TH, T::TW);
+        T::load_main(b, src + e.plane * HW, a.H, a.W, e.i0, e.j0, tid);
+        T::load_side(S, src + e.plane * HW, src_h + (int64_t)e.plane * a.H * (2 * P), a.H, a.W, e.i0, e.j0,
+                     tid);
+    };
+    issue(beg, mybuf[0]);
+
+    if (!wgrad_half) {
+        int it = 0;
+        float acc[RH][4];
+        TileIdx dprev{};
+        for (int t = beg; t < end;) {
+            const int c = t / tiles_c;
+            const int run_end = min(end, (c + 1) * tiles_c);
+            float wr[KK];
+            load_weights<K, true>(a.w, c, wr);
+            for (; t < run_end; ++t, ++it) {
+                float* cb = bufg[it & 1];
+                const TileIdx d = decode_channel_major(a, t, T::TH, T::TW);
+                T::put_side(cb, S, tid);
+                wait_vmem();
+                lds_barrier();
+                if (it > 0) store_rows<RH>(a.out, dprev, a.H, a.W, tx, ty, acc);   // previous tile's
+                if (t + 1 < end) issue(t + 1, bufg[(it + 1) & 1]);
 #pragma unroll
-            for (int r = 0; r < RH + K - 1; ++r) {
-                if (r + 1 < RH + K - 1) T::read_row(base + (r + 1) * T::LS, nxt);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int i = 0; i < RH; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) acc[i][jj] = 0.f;
+                conv_tile<K, TX, TY, RH>(cb, wr, acc, tx, ty);
+                dprev = d;
+            }
+            lds_barrier();   // the flush's barrier
+        }
+        store_rows<RH>(a.out, dprev, a.H, a.W, tx, ty, acc);
+    } else {
+        int it = 0;
+        for (int t = beg; t < end;) {
+            const int c = t / tiles_c;
+            const int run_end = min(end, (c + 1) * tiles_c);
+            float acc[NV];
+#pragma unroll
+            for (int k = 0; k < NV; ++k) acc[k] = 0.f;
+            for (; t < run_end; ++t, ++it) {
+                float* cb = bufx[it & 1];
+                const TileIdx d = decode_channel_major(a, t, T::TH, T::TW);
+                T::put_side(cb, S, tid);
+                wait_vmem();
+                lds_barrier();
+                if (t + 1 < end) issue(t + 1, bufx[(it + 1) & 1]);
+                // grad_output at the thread's outputs: the centre of this
+                // tile's grad_output buffer (main region row P + i, column j)
+                float gv[RH][4];
+                const float* gp = bufg[it & 1] + (ty * RH + P) * T::TW + 4 * tx;
 #pragma unroll
                 for (int i = 0; i < RH; ++i) {
-                    const int kh = r - i;
-                    if (kh < 0 || kh >= K) continue;
-#pragma unroll
-                    for (int kw = 0; kw < K; ++kw)
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj)
-                            acc[kh * K + kw] = __builtin_fmaf(gv[i][jj], cur[jj + kw], acc[kh * K + kw]);
+                    const float4 v = *reinterpret_cast<const float4*>(gp + i * T::TW);
+                    const float m = d.i0 + ty * RH + i >= d.i_own ? 1.f : 0.f;   // rows the tile above owns
+                    gv[i][0] = v.x * m; gv[i][1] = v.y * m; gv[i][2] = v.z * m; gv[i][3] = v.w * m;
+                    acc[KK] += (gv[i][0] + gv[i][1]) + (gv[i][2] + gv[i][3]);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int q = 0; q < 4 + K - 1; ++q) cur[q] = nxt[q];
+                wgrad_tile<K, TX, TY, RH>(cb, gv, acc, tx, ty);
             }
-            lds_barrier();   // the tile is rewritten by the next put()
-        }
-        // Flush the run: wave totals, then the waves in a fixed order.  red
-        // is rewritten only after the next tile's barrier, which every reader
-        // below has passed.
-        const float s = wave_sum_scatter<NV>(acc, lane);
-        const int idx = wave_sum_index<NV>(lane);
-        if (idx >= 0) red[wave][idx] = s;
-        lds_barrier();
-        if (threadIdx.x < NV) {
-            float tot = red[0][threadIdx.x];
-#pragma unroll
-            for (int w = 1; w < NWAVE; ++w) tot += red[w][threadIdx.x];
-            const int64_t slot = blockIdx.x - tile_owner((int64_t)c * tiles_c, a.ntiles, G);
-            a.ws[((int64_t)c * tiles_c + slot) * NV + threadIdx.x] = tot;
+            flush_write<NV, NWAVE>(acc, red, tid);
+            lds_barrier();
+            flush_sum<NV, NWAVE>(red, tid, a.ws, (int64_t)c * tiles_c + blockIdx.x -
+                                                     tile_owner((int64_t)c * tiles_c, a.ntiles, G));
         }
     }
 }
@@ -483,6 +715,21 @@ DwShape pick_shape(int H, int W)
     return {4, 64, H >= 64 ? 1 : 0};
 }
 
+// The fused backward keeps two rows per thread where the other kernels keep
+// four: each half then fits in 128 registers, so two 512-thread workgroups
+// share a compute unit (four waves per SIMD) without spilling.
+DwShape bwd_shape(int H, int W)
+{
+    DwShape sh = pick_shape(H, W);
+    if (sh.tx == 16 && sh.ty == 16 && sh.rh == 4) sh.rh = 2;
+    return sh;
+}
+
+int64_t tiles_per_channel(int N, int H, int W, DwShape sh)
+{
+    return (int64_t)N * ((H + sh.rh * sh.ty - 1) / (sh.rh * sh.ty)) * (W / (4 * sh.tx));
+}
+
 // Persistent grid: as many workgroups as are resident at once, at most one per tile.
 template <typename Kern>
 int persistent_grid(Kern kern, int block, int ntiles)
@@ -496,25 +743,40 @@ int persistent_grid(Kern kern, int block, int ntiles)
     return (int)(g < ntiles ? g : ntiles);
 }
 
+void set_tiles(DwArgs& a, int planes, int tx, int ty, int rh)
+{
+    a.tiles_w = a.W / (4 * tx);
+    a.tiles_h = (a.H + rh * ty - 1) / (rh * ty);
+    a.ntiles = planes * a.tiles_h * a.tiles_w;
+}
+
+template <int K>
+hipError_t launch_reduce(const DwArgs& a, int grid, float* gw, float* gb, hipStream_t st)
+{
+    const int tiles_c = a.ntiles / a.C;
+    const int total = a.C * (K * K + 1);
+    hipLaunchKernelGGL((dw_wgrad_reduce_kernel<K>), dim3((total + 255) / 256), dim3(256), 0, st, a.ws, a.C,
+                       tiles_c, (int64_t)a.ntiles, (int64_t)grid, gw, gb);
+    return hipGetLastError();
+}
+
+// The instantiated tile shapes (pick_shape() returns one of these).
+#define SSCNN_DW_SHAPES(X) X(16, 16, 4) X(16, 16, 2) X(16, 16, 1) X(8, 32, 2) X(8, 32, 1) X(4, 64, 1)
+// and the ones bwd_shape() returns
+#define SSCNN_DW_BWD_SHAPES(X) X(16, 16, 2) X(16, 16, 1) X(8, 32, 2) X(8, 32, 1) X(4, 64, 1)
+
 template <int K, bool FLIP>
 hipError_t launch_conv(DwArgs a, int planes, DwShape sh, hipStream_t st)
 {
-#define SSCNN_DW_CONV(TX, TY, RH)                                                         \
-    if (sh.tx == TX && sh.ty == TY && sh.rh == RH) {                                      \
-        auto kern = dw_conv_kernel<K, TX, TY, RH, FLIP>;                                  \
-        a.tiles_w = a.W / (4 * TX);                                                       \
-        a.tiles_h = (a.H + RH * TY - 1) / (RH * TY);                                      \
-        a.ntiles = planes * a.tiles_h * a.tiles_w;                                        \
-        const int grid = persistent_grid(kern, TX * TY, a.ntiles);                        \
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(TX * TY), 0, st, a);                    \
-        return hipGetLastError();                                                         \
+#define SSCNN_DW_CONV(TX, TY, RH)                                                  \
+    if (sh.tx == TX && sh.ty == TY && sh.rh == RH) {                               \
+        auto kern = dw_conv_kernel<K, TX, TY, RH, FLIP>;                           \
+        set_tiles(a, planes, TX, TY, RH);                                          \
+        const int grid = persistent_grid(kern, TX * TY, a.ntiles);                 \
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(TX * TY), 0, st, a);             \
+        return hipGetLastError();                                                  \
     }
-    SSCNN_DW_CONV(16, 16, 4)
-    SSCNN_DW_CONV(16, 16, 2)
-    SSCNN_DW_CONV(16, 16, 1)
-    SSCNN_DW_CONV(8, 32, 2)
-    SSCNN_DW_CONV(8, 32, 1)
-    SSCNN_DW_CONV(4, 64, 1)
+    SSCNN_DW_SHAPES(SSCNN_DW_CONV)
 #undef SSCNN_DW_CONV
     return hipErrorInvalidValue;
 }
@@ -522,29 +784,34 @@ hipError_t launch_conv(DwArgs a, int planes, DwShape sh, hipStream_t st)
 template <int K>
 hipError_t launch_wgrad(DwArgs a, int planes, DwShape sh, float* gw, float* gb, hipStream_t st)
 {
-#define SSCNN_DW_WGRAD(TX, TY, RH)                                                          \
-    if (sh.tx == TX && sh.ty == TY && sh.rh == RH) {                                        \
-        auto kern = dw_wgrad_kernel<K, TX, TY, RH>;                                         \
-        a.tiles_w = a.W / (4 * TX);                                                         \
-        a.tiles_h = (a.H + RH * TY - 1) / (RH * TY);                                        \
-        a.ntiles = planes * a.tiles_h * a.tiles_w;                                          \
-        const int grid = persistent_grid(kern, TX * TY, a.ntiles);                          \
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(TX * TY), 0, st, a);                      \
-        hipError_t e = hipGetLastError();                                                   \
-        if (e != hipSuccess) return e;                                                      \
-        const int tiles_c = a.ntiles / a.C;                                                 \
-        const int total = a.C * (K * K + 1);                                                \
-        hipLaunchKernelGGL((dw_wgrad_reduce_kernel<K>), dim3((total + 255) / 256), dim3(256), \
-                           0, st, a.ws, a.C, tiles_c, (int64_t)a.ntiles, (int64_t)grid, gw, gb); \
-        return hipGetLastError();                                                           \
+#define SSCNN_DW_WGRAD(TX, TY, RH)                                                 \
+    if (sh.tx == TX && sh.ty == TY && sh.rh == RH) {                               \
+        auto kern = dw_wgrad_kernel<K, TX, TY, RH>;                                \
+        set_tiles(a, planes, TX, TY, RH);                                          \
+        const int grid = persistent_grid(kern, TX * TY, a.ntiles);                 \
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(TX * TY), 0, st, a);             \
+        const hipError_t e = hipGetLastError();                                    \
+        return e != hipSuccess ? e : launch_reduce<K>(a, grid, gw, gb, st);        \
     }
-    SSCNN_DW_WGRAD(16, 16, 4)
-    SSCNN_DW_WGRAD(16, 16, 2)
-    SSCNN_DW_WGRAD(16, 16, 1)
-    SSCNN_DW_WGRAD(8, 32, 2)
-    SSCNN_DW_WGRAD(8, 32, 1)
-    SSCNN_DW_WGRAD(4, 64, 1)
+    SSCNN_DW_SHAPES(SSCNN_DW_WGRAD)
 #undef SSCNN_DW_WGRAD
+    return hipErrorInvalidValue;
+}
+
+template <int K>
+hipError_t launch_bwd(DwArgs a, int planes, DwShape sh, float* gw, float* gb, hipStream_t st)
+{
+#define SSCNN_DW_BWD(TX, TY, RH)                                                   \
+    if (sh.tx == TX && sh.ty == TY && sh.rh == RH) {                               \
+        auto kern = dw_bwd_kernel<K, TX, TY, RH>;                                  \
+        set_tiles(a, planes, TX, TY, RH);                                          \
+        const int grid = persistent_grid(kern, 2 * TX * TY, a.ntiles);             \
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(2 * TX * TY), 0, st, a);         \
+        const hipError_t e = hipGetLastError();                                    \
+        return e != hipSuccess ? e : launch_reduce<K>(a, grid, gw, gb, st);        \
+    }
+    SSCNN_DW_BWD_SHAPES(SSCNN_DW_BWD)
+#undef SSCNN_DW_BWD
     return hipErrorInvalidValue;
 }
 
@@ -567,10 +834,13 @@ bool dw_supported(const Geom& g)
            pick_shape(g.h, g.wl).rh > 0 && (int64_t)g.n * g.ci * g.h * g.wl < ((int64_t)1 << 31);
 }
 
+// One partial slot per tile of a channel at most, for whichever of the
+// grad_weight kernel and the fused backward has more tiles.
 size_t dw_wgrad_workspace_bytes(const Geom& g)
 {
-    const DwShape sh = pick_shape(g.h, g.wl);
-    const int64_t tiles = (int64_t)g.n * ((g.h + sh.rh * sh.ty - 1) / (sh.rh * sh.ty)) * (g.wl / (4 * sh.tx));
+    const int64_t t1 = tiles_per_channel(g.n, g.h, g.wl, pick_shape(g.h, g.wl));
+    const int64_t t2 = tiles_per_channel(g.n, g.h, g.wl, bwd_shape(g.h, g.wl));
+    const int64_t tiles = t1 > t2 ? t1 : t2;
     return (size_t)(tiles * g.ci * (g.k * g.k + 1)) * sizeof(float);
 }
 
@@ -578,7 +848,7 @@ hipError_t launch_dw_fwd(const Geom& g, const float* x, const float* xh, const f
                          const float* b, float* y, hipStream_t st)
 {
     DwArgs a = make_args(g);
-    a.x = x; a.halo = xh; a.w = w; a.b = b; a.y = y;
+    a.src = x; a.src_h = xh; a.w = w; a.b = b; a.out = y;
     const int planes = g.n * g.ci;
     const DwShape sh = pick_shape(g.h, g.wl);
     switch (g.k) {
@@ -592,7 +862,7 @@ hipError_t launch_dw_bwd_input(const Geom& g, const float* gy, const float* gyh,
                                float* gx, hipStream_t st)
 {
     DwArgs a = make_args(g);
-    a.x = gy; a.halo = gyh; a.w = w; a.b = nullptr; a.y = gx;
+    a.src = gy; a.src_h = gyh; a.w = w; a.b = nullptr; a.out = gx;
     const int planes = g.n * g.ci;
     const DwShape sh = pick_shape(g.h, g.wl);
     switch (g.k) {
@@ -606,13 +876,27 @@ hipError_t launch_dw_bwd_weight(const Geom& g, const float* x, const float* xh, 
                                 float* gw, float* gb, void* ws, hipStream_t st)
 {
     DwArgs a = make_args(g);
-    a.x = x; a.halo = xh; a.g = gy; a.ws = static_cast<float*>(ws);
+    a.x = x; a.x_h = xh; a.g = gy; a.ws = static_cast<float*>(ws);
     const int planes = g.n * g.ci;
     const DwShape sh = pick_shape(g.h, g.wl);
     switch (g.k) {
         case 3: return launch_wgrad<3>(a, planes, sh, gw, gb, st);
         case 5: return launch_wgrad<5>(a, planes, sh, gw, gb, st);
         default: return launch_wgrad<7>(a, planes, sh, gw, gb, st);
+    }
+}
+
+hipError_t launch_dw_bwd(const Geom& g, const float* x, const float* xh, const float* gy, const float* gyh,
+                         const float* w, float* gx, float* gw, float* gb, void* ws, hipStream_t st)
+{
+    DwArgs a = make_args(g);
+    a.src = gy; a.src_h = gyh; a.x = x; a.x_h = xh; a.w = w; a.out = gx; a.ws = static_cast<float*>(ws);
+    const int planes = g.n * g.ci;
+    const DwShape sh = bwd_shape(g.h, g.wl);
+    switch (g.k) {
+        case 3: return launch_bwd<3>(a, planes, sh, gw, gb, st);
+        case 5: return launch_bwd<5>(a, planes, sh, gw, gb, st);
+        default: return launch_bwd<7>(a, planes, sh, gw, gb, st);
     }
 }
 

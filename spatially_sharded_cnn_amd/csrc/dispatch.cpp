@@ -43,4 +43,14 @@ hipError_t kernels_conv_bwd_weight(const Geom& g, const float* x, const float* x
     return launch_direct_bwd_weight(g, x, xh, gy, gw, gb, st);
 }
 
+hipError_t kernels_conv_bwd(const Geom& g, const float* x, const float* xh, const float* gy,
+                            const float* gyh, const float* w, float* gx, float* gw, float* gb,
+                            void* ws, hipStream_t st)
+{
+    if (dw_supported(g)) return launch_dw_bwd(g, x, xh, gy, gyh, w, gx, gw, gb, ws, st);
+    const hipError_t e = kernels_conv_bwd_input(g, gy, gyh, w, gx, st);
+    if (e != hipSuccess) return e;
+    return kernels_conv_bwd_weight(g, x, xh, gy, gw, gb, ws, st);
+}
+
 }  // namespace sscnn

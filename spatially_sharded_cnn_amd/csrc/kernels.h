@@ -14,5 +14,8 @@ size_t kernels_bwd_weight_workspace_bytes(const Geom& g);
 hipError_t kernels_conv_bwd_weight(const Geom& g, const float* x, const float* xh,
                                    const float* gy, float* gw, float* gb, void* ws,
                                    hipStream_t st);
+hipError_t kernels_conv_bwd(const Geom& g, const float* x, const float* xh, const float* gy,
+                            const float* gyh, const float* w, float* gx, float* gw, float* gb,
+                            void* ws, hipStream_t st);
 
 }  // namespace sscnn

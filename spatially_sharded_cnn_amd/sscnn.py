@@ -22,7 +22,7 @@ HALO_INPUT, HALO_GRAD_OUTPUT = 0, 1
 
 EXPORTED = (
     "sscnn_conv_init", "sscnn_halo_gather", "sscnn_conv_fwd", "sscnn_conv_bwd_input",
-    "sscnn_conv_bwd_weight_workspace_bytes", "sscnn_conv_bwd_weight_partial",
+    "sscnn_conv_bwd_weight_workspace_bytes", "sscnn_conv_bwd_weight_partial", "sscnn_conv_bwd",
     "sscnn_partial_reduce", "sscnn_status_string", "sscnn_last_error", "sscnn_abi_version",
 )
 
@@ -81,12 +81,14 @@ def lib() -> ctypes.CDLL:
         L.sscnn_conv_bwd_weight_workspace_bytes.argtypes = [P]
         L.sscnn_conv_bwd_weight_workspace_bytes.restype = ctypes.c_size_t
         L.sscnn_conv_bwd_weight_partial.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.sscnn_conv_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.sscnn_partial_reduce.argtypes = [ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int64, _vp, _vp]
         L.sscnn_status_string.argtypes = [ctypes.c_int]
         L.sscnn_status_string.restype = ctypes.c_char_p
         L.sscnn_last_error.restype = ctypes.c_char_p
         for f in ("sscnn_conv_init", "sscnn_halo_gather", "sscnn_conv_fwd", "sscnn_conv_bwd_input",
-                  "sscnn_conv_bwd_weight_partial", "sscnn_partial_reduce", "sscnn_abi_version"):
+                  "sscnn_conv_bwd_weight_partial", "sscnn_conv_bwd", "sscnn_partial_reduce",
+                  "sscnn_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -201,6 +203,25 @@ def conv_bwd_weight_partial(conv: Conv, x, x_halo, grad_y, grad_w_part, grad_b_p
         _ptr(grad_y, conv.y_shape, "grad_y"), _ptr(grad_w_part, conv.w_shape, "grad_w_part"),
         _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True), ws_ptr, ws_bytes, _stream(stream)),
         "conv_bwd_weight_partial")
+
+
+def conv_bwd(conv: Conv, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_part, grad_b_part,
+             workspace=None, stream=None):
+    """sscnn_conv_bwd: grad_input and the grad_weight / grad_bias partials in one call
+    (workspace as for conv_bwd_weight_partial)."""
+    hs, gs = conv.halo_shape(HALO_INPUT), conv.halo_shape(HALO_GRAD_OUTPUT)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib().sscnn_conv_bwd(
+        ctypes.byref(conv), _ptr(x, conv.x_shape, "x"), _ptr(x_halo, hs, "x_halo", hs[3] == 0),
+        _ptr(grad_y, conv.y_shape, "grad_y"), _ptr(grad_y_halo, gs, "grad_y_halo", gs[3] == 0),
+        _ptr(weight, conv.w_shape, "weight"), _ptr(grad_x, conv.x_shape, "grad_x"),
+        _ptr(grad_w_part, conv.w_shape, "grad_w_part"),
+        _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True), ws_ptr, ws_bytes, _stream(stream)),
+        "conv_bwd")
 
 
 def partial_reduce(parts: Sequence, out, stream=None):

@@ -100,13 +100,16 @@ class ShardedStack:
             ws = sscnn.new_workspace(c0, self.device)
             nw = c0.w_shape[0] * c0.w_shape[1] * c0.w_shape[2] * c0.w_shape[3]
             for s, c in enumerate(convs):
-                if l > 0 or need_input_grad:
-                    dx = torch.empty(c0.x_shape, device=self.device)
-                    sscnn.conv_bwd_input(c, cur[s], st.g_halo[s], self.w[l], dx, self.stream)
-                    st.dx.append(dx)
                 buf = torch.empty(nw + c0.c_out, device=self.device)    # [gW | gB]
-                sscnn.conv_bwd_weight_partial(c, st.x[s], st.x_halo[s], cur[s], buf[:nw].view(c0.w_shape),
-                                              buf[nw:], ws, self.stream)
+                if l > 0 or need_input_grad:
+                    # grad_input and the weight / bias partials in one call
+                    dx = torch.empty(c0.x_shape, device=self.device)
+                    sscnn.conv_bwd(c, st.x[s], st.x_halo[s], cur[s], st.g_halo[s], self.w[l], dx,
+                                   buf[:nw].view(c0.w_shape), buf[nw:], ws, self.stream)
+                    st.dx.append(dx)
+                else:
+                    sscnn.conv_bwd_weight_partial(c, st.x[s], st.x_halo[s], cur[s], buf[:nw].view(c0.w_shape),
+                                                  buf[nw:], ws, self.stream)
                 st.gw_parts.append(buf)
             red = torch.empty(nw + c0.c_out, device=self.device)
             sscnn.partial_reduce(st.gw_parts, red, self.stream)

@@ -34,8 +34,9 @@ def layer_conv(L, num_shards: int, shard: int) -> sscnn.Conv:
 
 def run_shard(L, num_shards: int, shard: int, x_sl, g_sl, wt: torch.Tensor, b, stream=None):
     """One shard's unit: halo_gather(X), conv_fwd, halo_gather(G),
-    conv_bwd_input, conv_bwd_weight_partial.  x_sl / g_sl are the lists of all
-    shards' device slices (the neighbours supply the halos)."""
+    conv_bwd_input, conv_bwd_weight_partial, and the fused conv_bwd (results
+    dx2, gw2, gb2).  x_sl / g_sl are the lists of all shards' device slices
+    (the neighbours supply the halos)."""
     c = layer_conv(L, num_shards, shard)
     left = (lambda sl: sl[shard - 1] if shard > 0 else None)
     right = (lambda sl: sl[shard + 1] if shard < num_shards - 1 else None)
@@ -51,7 +52,9 @@ def run_shard(L, num_shards: int, shard: int, x_sl, g_sl, wt: torch.Tensor, b, s
     sscnn.halo_gather(c, sscnn.HALO_GRAD_OUTPUT, left(g_sl), right(g_sl), gh, stream)
     sscnn.conv_bwd_input(c, g_sl[shard], gh, wt, dx, stream)
     sscnn.conv_bwd_weight_partial(c, x_sl[shard], xh, g_sl[shard], gw, gb, ws, stream)
-    return dict(conv=c, x_halo=xh, y=y, g_halo=gh, dx=dx, gw=gw, gb=gb)
+    dx2, gw2, gb2 = torch.empty_like(dx), torch.empty_like(gw), torch.empty_like(gb)
+    sscnn.conv_bwd(c, x_sl[shard], xh, g_sl[shard], gh, wt, dx2, gw2, gb2, ws, stream)
+    return dict(conv=c, x_halo=xh, y=y, g_halo=gh, dx=dx, gw=gw, gb=gb, dx2=dx2, gw2=gw2, gb2=gb2)
 
 
 def normwise_error(got, ref) -> float:

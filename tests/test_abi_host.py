@@ -136,6 +136,29 @@ def test_calls_reject_null_and_misaligned_pointers():
     assert L.sscnn_conv_bwd_weight_partial(r, FAKE, FAKE, FAKE, FAKE, FAKE + 8, None, 0, None) == sscnn.EINVAL
 
 
+def test_fused_backward_validation():
+    L = sscnn.lib()
+    c = _conv()
+    r = ctypes.byref(c)
+    F = FAKE
+    ok = (F, F + 4096, F + 8192, F + 12288, F + 16384, F + 20480, F + 24576, F + 28672)
+    # every required pointer, one at a time
+    for i in range(7):
+        args = list(ok[:7])
+        args[i] = None
+        assert L.sscnn_conv_bwd(r, *args, None, None, 0, None) == sscnn.EINVAL, i
+    assert L.sscnn_conv_bwd(r, F + 4, *ok[1:7], None, None, 0, None) == sscnn.EINVAL   # misaligned x
+    # grad_x aliasing an input
+    assert L.sscnn_conv_bwd(r, *ok[:5], ok[2], ok[6], None, None, 0, None) == sscnn.EINVAL
+    assert "alias" in sscnn.last_error()
+    # a depthwise layer needs its workspace
+    d = sscnn.conv_init(1, 16, 16, 64, 16, 7, 1, 3, 16, 1, 4)
+    need = L.sscnn_conv_bwd_weight_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    assert L.sscnn_conv_bwd(ctypes.byref(d), *ok[:7], None, None, 0, None) == sscnn.EWORKSPACE
+    assert L.sscnn_conv_bwd(ctypes.byref(d), *ok[:7], None, F + 32768, need - 4, None) == sscnn.EWORKSPACE
+
+
 def test_halo_gather_neighbour_rules():
     L = sscnn.lib()
     first, mid, last = _conv(0), _conv(1), _conv(3)

@@ -1,8 +1,9 @@
 """GPU parity of every ABI call against the CPU oracle (needs an MI355X).
 
 Each case runs shards of a layer through halo_gather -> conv_fwd ->
-halo_gather(grad) -> conv_bwd_input -> conv_bwd_weight_partial ->
-partial_reduce, then compares with the oracle computed on the GLOBAL tensors:
+halo_gather(grad) -> conv_bwd_input -> conv_bwd_weight_partial (and the fused
+conv_bwd) -> partial_reduce, then compares with the oracle computed on the
+GLOBAL tensors:
 
 * halos bit-exact against the neighbours' edge columns (zeros at the edges);
 * forward / grad_input within 1e-5 and grad_weight / grad_bias within 1e-4,
@@ -87,6 +88,10 @@ def _check_all_shards(wl, tensors, shards=None):
         gw_ref, gb_ref = oracle.conv_bwd_weight(x, g, L.k, L.stride, L.pad, L.groups, cols=cols_o)
         assert_close(host(r["gw"]), gw_ref, TOL_GW, f"{wl.name} shard {s} grad_weight partial")
         assert_close(host(r["gb"]), gb_ref, TOL_GW, f"{wl.name} shard {s} grad_bias partial")
+        # the fused backward: the same grad_input bit for bit, the partials to tolerance
+        assert torch.equal(r["dx2"], r["dx"]), f"{wl.name} shard {s}: conv_bwd grad_input != conv_bwd_input"
+        assert_close(host(r["gw2"]), gw_ref, TOL_GW, f"{wl.name} shard {s} conv_bwd grad_weight partial")
+        assert_close(host(r["gb2"]), gb_ref, TOL_GW, f"{wl.name} shard {s} conv_bwd grad_bias partial")
         outs.append(r)
     return outs
 
@@ -155,7 +160,7 @@ def test_dw7_c256_full_shard():
     # bitwise reproducible
     r2 = run_shard(L, S, wl.shard, x_sl, g_sl, wt_d, b_d)
     torch.cuda.synchronize()
-    for key in ("y", "dx", "gw", "gb"):
+    for key in ("y", "dx", "gw", "gb", "dx2", "gw2", "gb2"):
         assert torch.equal(r[key], r2[key]), f"{key} differs between two identical runs"
 
 
