@@ -26,6 +26,7 @@ v_fmac_f32 with vector-register operands reaches it without packed math)
 for the depthwise ones.
 
     python bench.py [--workload dw7_c256|dense5x5_c256|dense5x5_tiny] [--steps K] [--warmup W]
+    python bench.py --workload convnext_xl_w2048|convnext_xl_w4096   # the stack, per layer
     python bench.py --summarize DIR [DIR ...] [--traffic-op OP --traffic-kernels "K1;K2"]
                                       # text summary of rocprofv3 output directories
 """
@@ -52,13 +53,18 @@ VALU_F32_PEAK_TFLOPS = 157.3     # MI355X FP32 vector FMA
 COPY_CAL_BYTES = 256 << 20       # plain device copy used to calibrate FETCH_SIZE / WRITE_SIZE
 
 
+STEPS_DEFAULT, WARMUP_DEFAULT = 50, 5
+STACK_STEPS, STACK_WARMUP = 5, 2   # stack steps run for milliseconds each
+
+
 def _parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=STEPS_DEFAULT)
+    ap.add_argument("--warmup", type=int, default=WARMUP_DEFAULT)
     ap.add_argument("--workload", default="dw7_c256",
-                    help="dw7_c256 (default), dense5x5_c256 or dense5x5_tiny")
+                    help="dw7_c256 (default), dense5x5_c256, dense5x5_tiny, or a stack: "
+                         "convnext_xl_w2048, convnext_xl_w4096")
     ap.add_argument("--sets", type=int, default=3, help="independent buffer sets rotated per step")
     ap.add_argument("--op-reps", type=int, default=20, help="back-to-back calls per operation timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -114,7 +120,8 @@ def main():
         return 1
     dev = "cuda"
     wl = workloads.WORKLOADS[args.workload]
-    assert len(wl.layers) == 1, "bench.py times single-layer workloads"
+    if len(wl.layers) > 1:
+        return stack_bench(args, wl)
     L = wl.layers[0]
     S, s = wl.num_shards, wl.shard
     T = workloads.generate(wl)
@@ -307,6 +314,215 @@ def main():
         out["cpu_baseline"] = cpu_baseline(wl, T, L, S, s)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def _layer_work(c, L):
+    """Algorithmic bytes and FLOPs of one layer's forward, backward (grad_input +
+    grad_weight/grad_bias partial) and partial reduction, for one shard."""
+    f4 = 4
+    n, ci, h, wl_ = c.n, c.c_in, c.h, c.w_local
+    co, ho, wol = c.c_out, c.h_out, c.w_out_local
+    x_ext = n * ci * h * (wl_ + c.halo_l + c.halo_r) * f4
+    g_ext = n * co * ho * (wol + c.ghalo_l + c.ghalo_r) * f4
+    x_b, y_b = n * ci * h * wl_ * f4, n * co * ho * wol * f4
+    w_b, b_b = co * (ci // c.groups) * c.k * c.k * f4, co * f4
+    flops = 2 * (ci // c.groups) * c.k * c.k * n * co * ho * wol
+    return {"fwd": (x_ext + w_b + b_b + y_b, flops),
+            "bwd": (g_ext + x_ext + w_b + x_b + w_b + b_b, 2 * flops),
+            "reduce": ((c.num_shards + 1) * (w_b + b_b), 0),
+            "halo_x": (2 * n * ci * h * (c.halo_l + c.halo_r) * f4, 0),
+            "halo_g": (2 * n * co * ho * (c.ghalo_l + c.ghalo_r) * f4, 0)}
+
+
+def stack_bench(args, wl):
+    """A ConvNeXt-style stack (SURVEY configs 4 and 5): one step is the
+    measured shard's forward chain (halo_gather + conv_fwd per layer, each
+    layer's output feeding the next) and its backward chain in reverse
+    (halo_gather(G) + conv_bwd + partial_reduce per layer, each grad_input
+    feeding the layer below).  The neighbours' activations and gradients and
+    the other shards' partials come from an untimed run of all shards."""
+    import torch
+    from spatially_sharded_cnn_amd import sscnn, workloads
+    from spatially_sharded_cnn_amd.stack import ShardedStack
+
+    dev = "cuda"
+    S, s = wl.num_shards, wl.shard
+    steps = args.steps if args.steps != STEPS_DEFAULT else STACK_STEPS
+    warmup = args.warmup if args.warmup != WARMUP_DEFAULT else STACK_WARMUP
+    T = workloads.generate(wl)
+
+    def slices(a):
+        w = a.shape[3] // S
+        return [torch.from_numpy(np.ascontiguousarray(a[:, :, :, i * w:(i + 1) * w])).to(dev) for i in range(S)]
+
+    xs, gs = slices(T.x), slices(T.g)
+    st = ShardedStack(wl.layers, S, T.weights, T.biases)
+    st.forward(xs)
+    st.backward(gs)
+    torch.cuda.synchronize()
+    nl = len(wl.layers)
+    convs = [st.state[l].convs[s] for l in range(nl)]
+    nbr = lambda lst: (lst[s - 1] if s > 0 else None, lst[s + 1] if s < S - 1 else None)
+    ys = [torch.empty(c.y_shape, device=dev) for c in convs]
+    dxs = [torch.empty(c.x_shape, device=dev) for c in convs]
+    xhs = [torch.empty(c.halo_shape(sscnn.HALO_INPUT), device=dev) if c.halo_l + c.halo_r else None for c in convs]
+    ghs = [torch.empty(c.halo_shape(sscnn.HALO_GRAD_OUTPUT), device=dev) if c.ghalo_l + c.ghalo_r else None
+           for c in convs]
+    nws = [int(np.prod(c.w_shape)) for c in convs]
+    bufs = [torch.empty(nws[l] + convs[l].c_out, device=dev) for l in range(nl)]
+    reds = [torch.empty_like(b) for b in bufs]
+    wss = [sscnn.new_workspace(c) for c in convs]
+    ins = [xs[s]] + ys[:-1]                       # each layer's input: the previous layer's output
+    gouts = dxs[1:] + [gs[s]]                     # each layer's grad_output: the next layer's grad_input
+
+    def op_list():
+        ops = []
+        for l, c in enumerate(convs):
+            if xhs[l] is not None:
+                ops.append((l, "halo_x", lambda l=l, c=c: sscnn.halo_gather(
+                    c, sscnn.HALO_INPUT, *nbr(st.state[l].x), xhs[l])))
+            ops.append((l, "fwd", lambda l=l, c=c: sscnn.conv_fwd(c, ins[l], xhs[l], st.w[l], st.b[l], ys[l])))
+        for l in range(nl - 1, -1, -1):
+            c = convs[l]
+            if ghs[l] is not None:
+                ops.append((l, "halo_g", lambda l=l, c=c: sscnn.halo_gather(
+                    c, sscnn.HALO_GRAD_OUTPUT, *nbr(st.state[l].g), ghs[l])))
+            ops.append((l, "bwd", lambda l=l, c=c: sscnn.conv_bwd(
+                c, ins[l], xhs[l], gouts[l], ghs[l], st.w[l], dxs[l], bufs[l][:nws[l]].view(c.w_shape),
+                bufs[l][nws[l]:], wss[l])))
+            ops.append((l, "reduce", lambda l=l: sscnn.partial_reduce(
+                [bufs[l] if i == s else st.state[l].gw_parts[i] for i in range(S)], reds[l])))
+        return ops
+
+    ops = op_list()
+
+    def step():
+        for _, _, f in ops:
+            f()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = e0.elapsed_time(e1) / steps
+
+    # each operation on its own, back to back
+    op_us = {}
+    for l, name, f in ops:
+        f()
+        torch.cuda.synchronize()
+        reps = max(2, min(args.op_reps, 20))
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(reps):
+            f()
+        a1.record()
+        torch.cuda.synchronize()
+        op_us[(l, name)] = 1e3 * a0.elapsed_time(a1) / reps
+
+    layers = []
+    step_bytes = step_flops = 0
+    dom, dom_t = None, -1.0
+    for l, (L, c) in enumerate(zip(wl.layers, convs)):
+        work = _layer_work(c, L)
+        dense = c.groups == 1
+        peak = MFMA_F32_PEAK_TFLOPS if dense else VALU_F32_PEAK_TFLOPS
+        row = {"layer": L.name, "shard_input": list(c.x_shape), "k": c.k, "stride": c.stride,
+               "groups": c.groups, "bound_unit": "mfma" if dense else "alu"}
+        lay_t = lay_roof = 0.0
+        for name in ("halo_x", "fwd", "halo_g", "bwd", "reduce"):
+            if (l, name) not in op_us:
+                continue
+            b_, f_ = work[name]
+            t = op_us[(l, name)]
+            row[name + "_us"] = round(t, 2)
+            lay_t += t
+            if name in ("fwd", "bwd", "reduce"):
+                step_bytes += b_
+                step_flops += f_
+            lay_roof += max(b_ / (HBM_PEAK_GBS * 1e9), f_ / (peak * 1e12)) * 1e6
+            if name in ("fwd", "bwd") and t > dom_t:
+                dom, dom_t = (l, name, b_, f_, dense, peak), t
+        row["us"] = round(lay_t, 2)
+        row["roofline_us"] = round(lay_roof, 2)
+        row["roofline_frac"] = round(lay_roof / lay_t, 4) if lay_t else None
+        row["gbs"] = round((work["fwd"][0] + work["bwd"][0] + work["reduce"][0]) / (lay_t * 1e-6) / 1e9, 1)
+        row["tflops"] = round((work["fwd"][1] + work["bwd"][1]) / (lay_t * 1e-6) / 1e12, 2)
+        layers.append(row)
+
+    l, name, b_, f_, dense, peak = dom
+    t = op_us[(l, name)]
+    if f_ / (peak * 1e12) > b_ / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma" if dense else "alu", "achieved": round(f_ / (t * 1e-6) / 1e12, 2),
+                "peak": peak, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(b_ / (t * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["op"] = f"{wl.layers[l].name}.conv_{name}"
+    roof["avg_us"] = round(t, 2)
+    roof["algorithmic_bytes"] = b_
+    roof["algorithmic_flops"] = f_
+
+    step_s = ms_per_step * 1e-3
+    out = {
+        "metric": METRIC, "value": round(step_bytes / step_s / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "shard": f"{s} of {S}",
+                   "shard_input": list(convs[0].x_shape), "layers": len(convs)},
+        "tflops": round(step_flops / step_s / 1e12, 2),
+        "step_bytes": step_bytes, "step_flops": step_flops,
+        "roofline_frac_step": round(sum(r["roofline_us"] for r in layers) * 1e-6 / step_s, 4),
+        "roofline": roof,
+        "layers": layers,
+        "wall_s_timed": round(wall, 4),
+        "source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_stack(wl, convs, step_flops)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline_stack(wl, convs, step_flops):
+    """The oracle on the stack's layers for the measured shard, each layer on
+    seeded tensors of its own shapes (the cost does not depend on values),
+    over the first `imgs` images: forward + grad_input + grad_weight/grad_bias
+    partial per layer.  imgs is chosen for roughly 10-20 s of host work."""
+    import oracle
+    S, s = wl.num_shards, wl.shard
+    n = wl.layers[0].in_shape[0]
+    imgs = max(1, min(n, int(round(n * 12.0 / max(step_flops / 30e9, 1e-9)))))
+    rng = np.random.default_rng(7)
+    total_t = total_b = 0.0
+    for L, c in zip(wl.layers, convs):
+        _, ci, h, w = L.in_shape
+        _, co, ho, wo = L.out_shape
+        x = rng.standard_normal((imgs, ci, h, w), dtype=np.float32)
+        g = rng.standard_normal((imgs, co, ho, wo), dtype=np.float32)
+        wt = rng.standard_normal((co, ci // L.groups, L.k, L.k), dtype=np.float32)
+        b = rng.standard_normal((co,), dtype=np.float32)
+        wl_, wol = w // S, wo // S
+        t0 = time.perf_counter()
+        oracle.conv_fwd(x, wt, b, L.stride, L.pad, L.groups, cols=(s * wol, (s + 1) * wol))
+        oracle.conv_bwd_input(g, wt, x.shape, L.stride, L.pad, L.groups, cols=(s * wl_, (s + 1) * wl_))
+        oracle.conv_bwd_weight(x, g, L.k, L.stride, L.pad, L.groups, cols=(s * wol, (s + 1) * wol))
+        total_t += time.perf_counter() - t0
+        work = _layer_work(c, L)
+        total_b += (work["fwd"][0] + work["bwd"][0]) * imgs / n
+    return {"value": round(total_b / total_t / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(total_t, 3),
+            "sample": f"images 0..{imgs - 1} of {n}, every layer of the stack, shard {s} of {S}: forward + "
+                      "grad_input + grad_weight/grad_bias partial per layer (C, double, OpenMP)",
+            "cpu": platform.processor() or platform.machine()}
 
 
 def cpu_baseline(wl, T, L, S, s):

@@ -1,0 +1,19 @@
+// patchify.h -- convolutions whose kernel equals their stride (stem, downsamples)
+// on the FP32 matrix cores.
+#pragma once
+
+#include "internal.h"
+
+namespace sscnn {
+
+// groups == 1, k == stride in {2, 4}, pad 0, c_in*k*k and c_out multiples of 16,
+// output width a multiple of 16.
+bool patch_supported(const Geom& g);
+size_t patch_wgrad_workspace_bytes(const Geom& g);
+hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const float* b, float* y,
+                            hipStream_t st);
+hipError_t launch_patch_bwd_input(const Geom& g, const float* gy, const float* w, float* gx, hipStream_t st);
+hipError_t launch_patch_bwd_weight(const Geom& g, const float* x, const float* gy, float* gw, float* gb,
+                                   void* ws, hipStream_t st);
+
+}  // namespace sscnn

@@ -50,6 +50,11 @@ SMALL = [
     ("dense3x3", 2, 24, 40, 9, 2 * 30, 3, 1, 1, 1, 2),
     ("stem4x4s4", 2, 3, 64, 32, 4 * 64, 4, 4, 0, 1, 4),
     ("ds2x2s2", 2, 64, 96, 16, 4 * 32, 2, 2, 0, 1, 4),
+    # patchify on the matrix cores: ragged row / column tiles, 80 pixels, k = 4 with a long reduction
+    ("patch2_c80_p80", 3, 48, 80, 10, 2 * 32, 2, 2, 0, 1, 2),
+    ("patch4_c48_k512", 2, 32, 48, 16, 4 * 64, 4, 4, 0, 1, 4),
+    ("patch2_c256_tiles", 2, 256, 256, 32, 2 * 128, 2, 2, 0, 1, 2),
+    ("patch2_wo8_direct", 1, 16, 32, 8, 2 * 16, 2, 2, 0, 1, 2),
     ("grouped3x3", 1, 8, 12, 10, 3 * 12, 3, 1, 1, 4, 3),
     ("strided3x3p1", 1, 6, 10, 11, 2 * 16, 3, 2, 1, 1, 2),
 ]
