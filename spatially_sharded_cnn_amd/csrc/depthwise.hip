@@ -711,8 +711,13 @@ struct DwShape {
 DwShape pick_shape(int H, int W)
 {
     if (W % 64 == 0) return {16, 16, H >= 64 ? 4 : (H >= 32 ? 2 : (H >= 16 ? 1 : 0))};
-    if (W % 32 == 0) return {8, 32, H >= 64 ? 2 : (H >= 32 ? 1 : 0)};
-    return {4, 64, H >= 64 ? 1 : 0};
+    if (W % 32 == 0) {
+        if (H >= 64) return {8, 32, 2};
+        if (H >= 32) return {8, 32, 1};
+        return {8, 16, H >= 16 ? 1 : 0};      // 16-row tiles of 128 threads
+    }
+    if (H >= 64) return {4, 64, 1};
+    return {4, 16, H >= 16 ? 1 : 0};          // 16-row tiles of 64 threads
 }
 
 // The fused backward keeps two rows per thread where the other kernels keep
@@ -761,9 +766,11 @@ hipError_t launch_reduce(const DwArgs& a, int grid, float* gw, float* gb, hipStr
 }
 
 // The instantiated tile shapes (pick_shape() returns one of these).
-#define SSCNN_DW_SHAPES(X) X(16, 16, 4) X(16, 16, 2) X(16, 16, 1) X(8, 32, 2) X(8, 32, 1) X(4, 64, 1)
+#define SSCNN_DW_SHAPES(X) X(16, 16, 4) X(16, 16, 2) X(16, 16, 1) X(8, 32, 2) X(8, 32, 1) X(8, 16, 1) \
+    X(4, 64, 1) X(4, 16, 1)
 // and the ones bwd_shape() returns
-#define SSCNN_DW_BWD_SHAPES(X) X(16, 16, 2) X(16, 16, 1) X(8, 32, 2) X(8, 32, 1) X(4, 64, 1)
+#define SSCNN_DW_BWD_SHAPES(X) X(16, 16, 2) X(16, 16, 1) X(8, 32, 2) X(8, 32, 1) X(8, 16, 1) X(4, 64, 1) \
+    X(4, 16, 1)
 
 template <int K, bool FLIP>
 hipError_t launch_conv(DwArgs a, int planes, DwShape sh, hipStream_t st)

@@ -42,6 +42,9 @@ SMALL = [
     ("dw3_w16", 2, 5, 5, 17, 4 * 16, 3, 1, 1, 5, 4),
     ("dw7_w48", 1, 7, 7, 33, 3 * 48, 7, 1, 3, 7, 3),
     ("dw7_w256", 1, 4, 4, 20, 2 * 256, 7, 1, 3, 4, 2),
+    ("dw7_h16_w16", 2, 24, 24, 16, 4 * 16, 7, 1, 3, 24, 4),
+    ("dw7_h16_w32", 2, 12, 12, 16, 3 * 32, 7, 1, 3, 12, 3),
+    ("dw5_h20_w16", 1, 9, 9, 20, 2 * 16, 5, 1, 2, 9, 2),
     ("dense5x5_ragged", 2, 40, 72, 13, 3 * 37, 5, 1, 2, 1, 3),
     ("mfma5x5_ragged_channels", 2, 44, 72, 13, 3 * 36, 5, 1, 2, 1, 3),
     ("mfma5x5_two_segments", 1, 16, 20, 6, 2 * 132, 5, 1, 2, 1, 2),
