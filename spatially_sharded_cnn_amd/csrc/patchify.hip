@@ -16,12 +16,18 @@
 //
 // One kernel template serves the three products: a 256-thread workgroup
 // computes a 128 x 128 tile of the result, each of its 4 waves a 64 x 64
-// block (2 x 2 MFMA blocks of 32 x 32); the reduction runs in chunks of 16
-// staged in LDS (k-major rows), double-buffered with one barrier per chunk,
-// the next chunk's global loads in flight while the current one multiplies.
-// grad_weight splits the pixel reduction over workgroups (fixed split count,
-// partials summed in split order by a second kernel, grad_bias fused into
-// the first column tile): no atomics, bitwise reproducible.
+// block (2 x 2 MFMA blocks of 32 x 32).  The reduction is gathered in
+// sub-chunks of 16 (the unit every operand gather below is written for) and
+// staged in LDS kKS sub-chunks at a time (k-major rows, double-buffered), one
+// barrier per stage, the next stage's global loads in flight while the
+// current one multiplies; a reduction that is not a whole number of stages
+// ends on zero-filled sub-chunks.  One sub-chunk per stage (40 KB of LDS) is
+// the measured best on gfx950: two (80 KB) allow only two workgroups per CU
+// instead of four, and the downsamples ran 5-7% slower.
+// grad_weight splits the pixel reduction over workgroups (a fixed split
+// count; grad_bias fused into the first column tile).  Each split writes one
+// slab of partials, and the slabs are summed in split order, in two
+// fixed-order stages when there are many: no atomics, bitwise reproducible.
 #include "internal.h"
 #include "patchify.h"
 
@@ -33,7 +39,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kNT = 256;
 constexpr int kBM = 128;         // result rows per workgroup
 constexpr int kBN = 128;         // result columns per workgroup
-constexpr int kBK = 16;          // reduction per LDS chunk
+constexpr int kSub = 16;         // reduction per gathered sub-chunk
+constexpr int kKS = 1;           // sub-chunks per LDS stage
+constexpr int kBK = kSub * kKS;  // reduction per LDS stage
 constexpr int kLD = kBM + 32;    // LDS row pitch: the two half-waves (k rows 2s, 2s+1) fall 32 banks apart
 
 enum Mode { FWD = 0, BWI = 1, BWW = 2 };
@@ -43,30 +51,32 @@ struct PArgs {
     const float* g;       // grad_output G (N, Co, Ho, Wo)   BWI, BWW
     const float* w;       // weight (Co, Ci, s, s)           FWD, BWI
     const float* b;       // bias (Co) or null               FWD
-    float* out;           // Y (FWD), dX (BWI), partials (splits, Co, Kt) (BWW)
-    float* outb;          // bias partials (splits, Co) or null (BWW)
+    float* out;           // Y (FWD), dX (BWI), partial slabs (BWW): per split Co * Kt weights then Co biases
     int N, Ci, Co, H, W, Ho, Wo, P, Kt;
     int tiles_m, tiles_n;             // result tiles (columns: pixels of one image for FWD / BWI)
-    int splits, chunks;               // BWW: pixel chunks of kBK, split into `splits` ranges
+    int splits, chunks;               // BWW: pixel sub-chunks of kSub, split into `splits` ranges
+    int with_bias;                    // BWW: also sum grad_output per channel
 };
 
-// Global -> registers for one chunk (8 A values and 8 B values per thread),
-// then registers -> LDS.  Each mode gathers its own operands.
+__device__ __forceinline__ int64_t slab_floats(const PArgs& a) { return (int64_t)a.Co * (a.Kt + 1); }
+
+// Global -> registers for one sub-chunk of kSub reduction rows (8 A values
+// and 8 B values per thread), then registers -> LDS.  Each mode gathers its
+// own operands; a sub-chunk past the end of the reduction (ok_k false) loads
+// zeros.
 template <int MODE, int S>
-struct Stage {
-    static constexpr int GPC = kBK / S;       // K groups (s consecutive K) per chunk   (FWD)
-    static constexpr int GPT = kBN / S;       // K groups per column tile               (BWW)
+struct Sub {
     float ra[8];
     float rb[8];
 
-    // k0: reduction offset of the chunk.  FWD: K; BWI: co; BWW: pixel of image img.
-    __device__ void load(const PArgs& a, int img, int m0, int n0, int k0)
+    // k0: reduction offset.  FWD: K; BWI: co; BWW: pixel of image img.
+    __device__ void load(const PArgs& a, int img, int m0, int n0, int k0, bool ok_k)
     {
         const int t = threadIdx.x;
         if constexpr (MODE == FWD) {
             // A[m][k] = W[m0 + m][k0 + k]: per row 16 contiguous floats, 2 threads a row
             const int m = t >> 1, kh = (t & 1) * 8;
-            const bool ok = m0 + m < a.Co;
+            const bool ok = ok_k && m0 + m < a.Co;
             const float* src = a.w + (int64_t)(m0 + m) * a.Kt + k0 + kh;
             const float4 v0 = ok ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
             const float4 v1 = ok ? *reinterpret_cast<const float4*>(src + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -81,7 +91,7 @@ struct Stage {
                 const int gg = k0 / S + gl;                 // global K group = ci * s + kh
                 const int ci = gg / S, kh = gg - ci * S;
                 const int pp = n0 + p;
-                const bool okp = pp < a.P;
+                const bool okp = ok_k && pp < a.P;
                 const int i = pp / a.Wo, j = pp - i * a.Wo;
                 const float* s_ = xi + ((int64_t)ci * a.H + i * S + kh) * a.W + j * S;
                 if constexpr (S == 2) {
@@ -98,7 +108,7 @@ struct Stage {
             for (int r = 0; r < 2; ++r) {
                 const int idx = t + kNT * r;
                 const int c = idx / 32, m4 = (idx % 32) * 4;
-                const bool ok = m0 + m4 < a.Kt;
+                const bool ok = ok_k && m0 + m4 < a.Kt;
                 const float4 v = ok ? *reinterpret_cast<const float4*>(a.w + (int64_t)(k0 + c) * a.Kt + m0 + m4)
                                     : make_float4(0.f, 0.f, 0.f, 0.f);
                 ra[4 * r] = v.x; ra[4 * r + 1] = v.y; ra[4 * r + 2] = v.z; ra[4 * r + 3] = v.w;
@@ -108,7 +118,7 @@ struct Stage {
             for (int r = 0; r < 2; ++r) {
                 const int idx = t + kNT * r;
                 const int c = idx / 32, p4 = (idx % 32) * 4;
-                const bool ok = n0 + p4 < a.P;
+                const bool ok = ok_k && n0 + p4 < a.P;
                 const float4 v = ok ? *reinterpret_cast<const float4*>(
                                           a.g + ((int64_t)img * a.Co + k0 + c) * a.P + n0 + p4)
                                     : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -120,22 +130,22 @@ struct Stage {
             for (int r = 0; r < 2; ++r) {
                 const int idx = t + kNT * r;
                 const int m = idx / 4, q4 = (idx % 4) * 4;
-                const bool ok = m0 + m < a.Co;
+                const bool ok = ok_k && m0 + m < a.Co;
                 const float4 v = ok ? *reinterpret_cast<const float4*>(
                                           a.g + ((int64_t)img * a.Co + m0 + m) * a.P + k0 + q4)
                                     : make_float4(0.f, 0.f, 0.f, 0.f);
                 ra[4 * r] = v.x; ra[4 * r + 1] = v.y; ra[4 * r + 2] = v.z; ra[4 * r + 3] = v.w;
             }
-            // B[q][n] = Xp[n0 + n][k0 + q]: the 16 pixels of the chunk lie in one output row
+            // B[q][n] = Xp[n0 + n][k0 + q]: the 16 pixels of the sub-chunk lie in one output row
             const int i = k0 / a.Wo, j0 = k0 - i * a.Wo;
             const float* xi = a.x + (int64_t)img * a.Ci * a.H * a.W;
 #pragma unroll
             for (int r = 0; r < 8 / S; ++r) {
                 const int idx = t + kNT * r;
-                const int q = idx % kBK, gl = idx / kBK;
+                const int q = idx % kSub, gl = idx / kSub;
                 const int gg = n0 / S + gl;
                 const int ci = gg / S, kh = gg - ci * S;
-                const bool ok = gg * S < a.Kt;
+                const bool ok = ok_k && gg * S < a.Kt;
                 const float* s_ = xi + ((int64_t)ci * a.H + i * S + kh) * a.W + (j0 + q) * S;
                 if constexpr (S == 2) {
                     const float2 v = ok ? *reinterpret_cast<const float2*>(s_) : make_float2(0.f, 0.f);
@@ -148,7 +158,7 @@ struct Stage {
         }
     }
 
-    // LDS chunk: As[k][m], Bs[k][n] (k-major rows of pitch kLD).
+    // LDS rows of this sub-chunk: As[k][m], Bs[k][n] (k-major rows of pitch kLD).
     __device__ void put(float* __restrict__ As, float* __restrict__ Bs) const
     {
         const int t = threadIdx.x;
@@ -182,7 +192,7 @@ struct Stage {
 #pragma unroll
             for (int r = 0; r < 8 / S; ++r) {
                 const int idx = t + kNT * r;
-                const int q = idx % kBK, gl = idx / kBK;
+                const int q = idx % kSub, gl = idx / kSub;
 #pragma unroll
                 for (int kw = 0; kw < S; ++kw) Bs[q * kLD + gl * S + kw] = rb[S * r + kw];
             }
@@ -206,18 +216,34 @@ patch_kernel(PArgs a)
     const int outer = bid / a.tiles_n;           // image (FWD / BWI) or split (BWW)
     const int m0 = mt * kBM, n0 = nt * kBN;
 
-    // reduction range in chunks of kBK
+    // reduction range in sub-chunks of kSub
     int c_beg, c_end;
-    if constexpr (MODE == FWD) { c_beg = 0; c_end = a.Kt / kBK; }
-    else if constexpr (MODE == BWI) { c_beg = 0; c_end = a.Co / kBK; }
+    if constexpr (MODE == FWD) { c_beg = 0; c_end = a.Kt / kSub; }
+    else if constexpr (MODE == BWI) { c_beg = 0; c_end = a.Co / kSub; }
     else {
         c_beg = (int)((int64_t)outer * a.chunks / a.splits);
         c_end = (int)((int64_t)(outer + 1) * a.chunks / a.splits);
     }
-    const int cpi = a.P / kBK;                   // BWW: chunks per image
-    auto chunk_at = [&](int c, int& img, int& k0) {
-        if constexpr (MODE == BWW) { img = c / cpi; k0 = (c - img * cpi) * kBK; }
-        else { img = outer; k0 = c * kBK; }
+    const int nstage = (c_end - c_beg + kKS - 1) / kKS;
+    const int cpi = a.P / kSub;                  // BWW: sub-chunks per image
+
+    Sub<MODE, S> sub[kKS];
+    auto load_stage = [&](int stg) {
+#pragma unroll
+        for (int u = 0; u < kKS; ++u) {
+            const int c = c_beg + stg * kKS + u;
+            const bool ok = c < c_end;
+            int img, k0;
+            if constexpr (MODE == BWW) {
+                const int cc = ok ? c : c_beg;
+                img = cc / cpi;
+                k0 = (cc - img * cpi) * kSub;
+            } else {
+                img = outer;
+                k0 = (ok ? c : 0) * kSub;
+            }
+            sub[u].load(a, img, m0, n0, k0, ok);
+        }
     };
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -231,40 +257,44 @@ patch_kernel(PArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
     float bias_acc = 0.f;
-    const bool with_bias = MODE == BWW && a.outb && nt == 0;
+    const bool with_bias = MODE == BWW && a.with_bias && nt == 0;
 
-    Stage<MODE, S> st;
-    if (c_beg < c_end) {
-        int img, k0;
-        chunk_at(c_beg, img, k0);
-        st.load(a, img, m0, n0, k0);
-    }
-    for (int c = c_beg, it = 0; c < c_end; ++c, ++it) {
-        float* as = As[it & 1];
-        float* bs = Bs[it & 1];
-        st.put(as, bs);
+    if (nstage > 0) load_stage(0);
+    for (int stg = 0; stg < nstage; ++stg) {
+        float* as = As[stg & 1];
+        float* bs = Bs[stg & 1];
+#pragma unroll
+        for (int u = 0; u < kKS; ++u) sub[u].put(as + u * kSub * kLD, bs + u * kSub * kLD);
         lds_barrier();
-        if (c + 1 < c_end) {
-            int img, k0;
-            chunk_at(c + 1, img, k0);
-            st.load(a, img, m0, n0, k0);
-        }
+        if (stg + 1 < nstage) load_stage(stg + 1);
         if (with_bias && threadIdx.x < kBM) {
 #pragma unroll
             for (int q = 0; q < kBK; ++q) bias_acc += as[q * kLD + threadIdx.x];
         }
+        // operands of step s2 + 1 are read before the MFMAs of step s2 are
+        // issued (the scheduling barriers keep that order), so the LDS
+        // latency overlaps the matrix pipe instead of stalling it
         const float* ap = as + hi * kLD + wm * 64 + l32;
         const float* bp = bs + hi * kLD + wn * 64 + l32;
+        float a0 = ap[0], a1 = ap[32], b0 = bp[0], b1 = bp[32];
 #pragma unroll
         for (int s2 = 0; s2 < kBK / 2; ++s2) {
-            const float a0 = ap[2 * s2 * kLD], a1 = ap[2 * s2 * kLD + 32];
-            const float b0 = bp[2 * s2 * kLD], b1 = bp[2 * s2 * kLD + 32];
+            float na0 = 0.f, na1 = 0.f, nb0 = 0.f, nb1 = 0.f;
+            if (s2 + 1 < kBK / 2) {
+                na0 = ap[2 * (s2 + 1) * kLD];
+                na1 = ap[2 * (s2 + 1) * kLD + 32];
+                nb0 = bp[2 * (s2 + 1) * kLD];
+                nb1 = bp[2 * (s2 + 1) * kLD + 32];
+            }
+            __builtin_amdgcn_sched_barrier(0);
             acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
             acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
             acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
             acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            a0 = na0; a1 = na1; b0 = nb0; b1 = nb1;
         }
-        // the buffer just read is rewritten two chunks later, after the next barrier
+        // the buffer just read is rewritten two stages later, after the next barrier
     }
 
     // D block (x, y): register 4 q + r holds row 4 hi + 8 q + r, column l32
@@ -307,7 +337,7 @@ patch_kernel(PArgs a)
                     }
                 } else {
                     if (col < a.Kt) {
-                        float* wp = a.out + ((int64_t)outer * a.Co) * a.Kt + col;
+                        float* wp = a.out + outer * slab_floats(a) + col;
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             if (row + r < a.Co) wp[(int64_t)(row + r) * a.Kt] = acc[x][y][4 * q + r];
@@ -316,29 +346,42 @@ patch_kernel(PArgs a)
             }
         }
     if (with_bias && threadIdx.x < kBM && m0 + threadIdx.x < a.Co)
-        a.outb[(int64_t)outer * a.Co + m0 + threadIdx.x] = bias_acc;
+        a.out[outer * slab_floats(a) + (int64_t)a.Co * a.Kt + m0 + threadIdx.x] = bias_acc;
 }
 
-// grad_w[co][K] = sum over splits of the partials, in split order (float4 along K).
+// dst[grp][e] = sum of src[k][e] over the slabs k of group grp (slabs
+// [grp * per, min(n, (grp + 1) * per))), added in slab order, in float4
+// units.  The loads of 8 slabs are issued before their adds so that they are
+// in flight together; the order of the adds is unchanged.  With dw non-null
+// (the last stage), element e goes to dw (e < nw4) or db, instead of dst.
 __global__ void __launch_bounds__(256)
-patch_reduce_kernel(const float* __restrict__ ws, const float* __restrict__ wsb, int splits, int Co, int Kt,
-                    float* __restrict__ gw, float* __restrict__ gb)
+slab_sum_kernel(const float4* __restrict__ src, int64_t count4, int n, int per, float4* __restrict__ dst,
+                float4* __restrict__ dw, float4* __restrict__ db, int64_t nw4)
 {
-    const int64_t n4 = (int64_t)Co * Kt / 4;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx < n4) {
-        const float4* p = reinterpret_cast<const float4*>(ws) + idx;
-        float4 s = p[0];
-        for (int k = 1; k < splits; ++k) {
-            const float4 v = p[(int64_t)k * n4];
-            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-        }
-        reinterpret_cast<float4*>(gw)[idx] = s;
-    } else if (gb && idx < n4 + Co) {
-        const int co = (int)(idx - n4);
-        float s = wsb[co];
-        for (int k = 1; k < splits; ++k) s += wsb[(int64_t)k * Co + co];
-        gb[co] = s;
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= count4) return;
+    const int grp = blockIdx.y;
+    const int k0 = grp * per;
+    const int m = (n - k0 < per ? n - k0 : per);
+    const float4* p = src + (int64_t)k0 * count4 + e;
+    float4 s = p[0];
+    int k = 1;
+    for (; k + 8 <= m; k += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(k + u) * count4];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
+    }
+    for (; k < m; ++k) {
+        const float4 v = p[(int64_t)k * count4];
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    if (dw) {
+        if (e < nw4) dw[e] = s;
+        else if (db) db[e - nw4] = s;
+    } else {
+        dst[(int64_t)grp * count4 + e] = s;
     }
 }
 
@@ -357,13 +400,18 @@ PArgs make_args(const Geom& g)
     return a;
 }
 
+constexpr int kSlabsPerGroup = 16;   // first-stage group size of the split sum
+constexpr int kOneStageMax = 32;     // at most this many splits are summed in one stage
+
 int wgrad_splits(const PArgs& a, int tiles)
 {
-    const int chunks = a.N * (a.P / kBK);
+    const int chunks = a.N * (a.P / kSub);
     int s = (1024 + tiles - 1) / tiles;
     if (s > chunks) s = chunks;
     return s < 1 ? 1 : s;
 }
+
+int split_groups(int splits) { return splits > kOneStageMax ? (splits + kSlabsPerGroup - 1) / kSlabsPerGroup : 0; }
 
 template <int MODE>
 hipError_t launch(const PArgs& a, int s, int grid, hipStream_t st)
@@ -379,7 +427,7 @@ bool patch_supported(const Geom& g)
 {
     const int64_t p = (int64_t)g.ho * g.wol;
     return g.groups == 1 && g.pad == 0 && g.k == g.stride && (g.k == 2 || g.k == 4) &&
-           (g.ci * g.k * g.k) % kBK == 0 && g.co % kBK == 0 && g.wol % kBK == 0 && g.h == g.ho * g.k &&
+           (g.ci * g.k * g.k) % kSub == 0 && g.co % kSub == 0 && g.wol % kSub == 0 && g.h == g.ho * g.k &&
            g.wl == g.wol * g.k && (int64_t)g.n * g.ci * g.h * g.wl < ((int64_t)1 << 31) &&
            (int64_t)g.n * g.co * p < ((int64_t)1 << 31);
 }
@@ -389,7 +437,8 @@ size_t patch_wgrad_workspace_bytes(const Geom& g)
     const PArgs a = make_args(g);
     const int tiles = ((a.Co + kBM - 1) / kBM) * ((a.Kt + kBN - 1) / kBN);
     const int64_t s = wgrad_splits(a, tiles);
-    return (size_t)(s * a.Co * (int64_t)(a.Kt + 1)) * sizeof(float);
+    const int64_t slab = (int64_t)a.Co * (a.Kt + 1);
+    return (size_t)((s + split_groups((int)s)) * slab) * sizeof(float);
 }
 
 hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const float* b, float* y,
@@ -418,16 +467,33 @@ hipError_t launch_patch_bwd_weight(const Geom& g, const float* x, const float* g
     a.x = x; a.g = gy;
     a.tiles_m = (a.Co + kBM - 1) / kBM;
     a.tiles_n = (a.Kt + kBN - 1) / kBN;
-    a.chunks = a.N * (a.P / kBK);
+    a.chunks = a.N * (a.P / kSub);
     a.splits = wgrad_splits(a, a.tiles_m * a.tiles_n);
-    float* wsf = static_cast<float*>(ws);
-    a.out = wsf;
-    a.outb = wsf + (int64_t)a.splits * a.Co * a.Kt;
+    a.with_bias = gb != nullptr;
+    float* slabs = static_cast<float*>(ws);
+    a.out = slabs;
     hipError_t e = launch<BWW>(a, g.k, a.tiles_m * a.tiles_n * a.splits, st);
     if (e != hipSuccess) return e;
-    const int64_t total = (int64_t)a.Co * a.Kt / 4 + a.Co;
-    hipLaunchKernelGGL(patch_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a.out, a.outb,
-                       a.splits, a.Co, a.Kt, gw, gb);
+
+    // slab sums: count4 float4 per slab (Co * Kt weights, then Co biases)
+    const int64_t slab = (int64_t)a.Co * (a.Kt + 1);
+    const int64_t count4 = slab / 4, nw4 = (int64_t)a.Co * a.Kt / 4;
+    const unsigned bx = (unsigned)((count4 + 255) / 256);
+    float4* dw = reinterpret_cast<float4*>(gw);
+    float4* db = reinterpret_cast<float4*>(gb);
+    const int groups = split_groups(a.splits);
+    if (groups == 0) {
+        hipLaunchKernelGGL(slab_sum_kernel, dim3(bx, 1), dim3(256), 0, st, reinterpret_cast<const float4*>(slabs),
+                           count4, a.splits, a.splits, nullptr, dw, db, nw4);
+        return hipGetLastError();
+    }
+    float4* mid = reinterpret_cast<float4*>(slabs + a.splits * slab);
+    hipLaunchKernelGGL(slab_sum_kernel, dim3(bx, groups), dim3(256), 0, st, reinterpret_cast<const float4*>(slabs),
+                       count4, a.splits, kSlabsPerGroup, mid, nullptr, nullptr, nw4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(slab_sum_kernel, dim3(bx, 1), dim3(256), 0, st, static_cast<const float4*>(mid), count4,
+                       groups, groups, nullptr, dw, db, nw4);
     return hipGetLastError();
 }
 
