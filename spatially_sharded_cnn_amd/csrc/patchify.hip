@@ -42,7 +42,12 @@ constexpr int kBN = 128;         // result columns per workgroup
 constexpr int kSub = 16;         // reduction per gathered sub-chunk
 constexpr int kKS = 1;           // sub-chunks per LDS stage
 constexpr int kBK = kSub * kKS;  // reduction per LDS stage
-constexpr int kLD = kBM + 32;    // LDS row pitch: the two half-waves (k rows 2s, 2s+1) fall 32 banks apart
+// LDS row pitch (floats), = 4 mod 64 banks.  At MFMA step s the two half-waves
+// read k rows s and s + 8 of a sub-chunk (both operands pair k the same way),
+// which 8 * kLD = 32 mod 64 puts in disjoint banks; and the operand gathers'
+// writes of k rows 4 apart (grad_weight's grad_output tile) or 8 apart (the
+// forward's weight tile) land 16 or 32 banks apart instead of on one bank.
+constexpr int kLD = kBM + 4;
 
 enum Mode { FWD = 0, BWI = 1, BWW = 2 };
 
@@ -274,17 +279,21 @@ patch_kernel(PArgs a)
         // operands of step s2 + 1 are read before the MFMAs of step s2 are
         // issued (the scheduling barriers keep that order), so the LDS
         // latency overlaps the matrix pipe instead of stalling it
-        const float* ap = as + hi * kLD + wm * 64 + l32;
-        const float* bp = bs + hi * kLD + wn * 64 + l32;
+        // k-slot pairing of step s2 in sub-chunk u: rows 16 u + s2 (lanes 0..31)
+        // and 16 u + s2 + 8 (lanes 32..63)
+        const float* ap = as + hi * (kSub / 2) * kLD + wm * 64 + l32;
+        const float* bp = bs + hi * (kSub / 2) * kLD + wn * 64 + l32;
+        auto row = [](int s2) { return (s2 / (kSub / 2)) * kSub + s2 % (kSub / 2); };
         float a0 = ap[0], a1 = ap[32], b0 = bp[0], b1 = bp[32];
 #pragma unroll
         for (int s2 = 0; s2 < kBK / 2; ++s2) {
             float na0 = 0.f, na1 = 0.f, nb0 = 0.f, nb1 = 0.f;
             if (s2 + 1 < kBK / 2) {
-                na0 = ap[2 * (s2 + 1) * kLD];
-                na1 = ap[2 * (s2 + 1) * kLD + 32];
-                nb0 = bp[2 * (s2 + 1) * kLD];
-                nb1 = bp[2 * (s2 + 1) * kLD + 32];
+                const int r = row(s2 + 1) * kLD;
+                na0 = ap[r];
+                na1 = ap[r + 32];
+                nb0 = bp[r];
+                nb1 = bp[r + 32];
             }
             __builtin_amdgcn_sched_barrier(0);
             acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
