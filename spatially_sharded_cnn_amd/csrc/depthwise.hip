@@ -131,28 +131,10 @@ __device__ __forceinline__ void dma16(const i32x4& rs, const float* lds, int vof
                  :: "v"(voff), "s"(l), "s"(rs) : "memory", "m0");
 }
 
-// The same for 4 bytes per lane: lane i writes lds + 4 * lane.
-__device__ __forceinline__ void dma4(const i32x4& rs, const float* lds, int voff)
-{
-    const int l = __builtin_amdgcn_readfirstlane((int)(uint32_t)reinterpret_cast<uintptr_t>(lds));
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, 0 offen lds"
-                 :: "v"(voff), "s"(l), "s"(rs) : "memory", "m0");
-}
-
 __device__ __forceinline__ void wait_vmem()
 {
     // gfx9 s_waitcnt: vmcnt = 0, expcnt[6:4] = 7 and lgkmcnt[11:8] = 15 (no wait on those)
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-}
-
-// Wait until at most N of this wave's vector memory operations are
-// outstanding.  gfx9 retires vector memory operations in issue order, so
-// this waits for everything issued before the last N.
-template <int N>
-__device__ __forceinline__ void wait_vmem_n()
-{
-    static_assert(N >= 0 && N < 64, "6-bit vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // The extended input of one tile in LDS, for a 256-thread group (TX x TY
@@ -217,40 +199,6 @@ struct Tile {
                 if (xcol < 0) S.s[k] = hp[(int64_t)r * (2 * P) + (xcol + P)];
                 else if (xcol >= W) S.s[k] = hp[(int64_t)r * (2 * P) + P + (xcol - W)];
                 else S.s[k] = xp[(int64_t)r * W + xcol];
-            }
-        }
-    }
-
-    // Side columns straight into LDS, 4 bytes per lane: 8-row group g is one
-    // 64-lane load, lane l filling side[8 g + l / 8][l % 8].  Lanes of the
-    // left slots (4 - P .. 3) and right slots (4 .. 3 + P) read the column
-    // from the halo buffer (outside the slice) or from the slice, one load
-    // per source with the other source's lanes inactive (they leave LDS
-    // alone); rows outside the plane read as zeros.  Each wave issues at
-    // least NSG / NWAVE of these per tile.
-    static constexpr int NSG = (LH + 7) / 8;
-    static_assert(SP == 8, "a side group of 8 rows is one 64-lane load");
-    __device__ static void load_side_lds(float* buf, const float* xp, const float* hp, int H, int W, int i0, int j0,
-                                         int tid)
-    {
-        const i32x4 rx = plane_rsrc(xp, H * W * 4);
-        const i32x4 rh = plane_rsrc(hp, H * 2 * P * 4);
-        const int wave = tid >> 6, lane = tid & 63;
-        const int slot = lane & 7;
-        const bool left = slot >= 4 - P && slot < 4, right = slot >= 4 && slot < 4 + P;
-        const int xcol = left ? j0 - P + (slot - (4 - P)) : j0 + TW + (slot - 4);
-        const bool halo = xcol < 0 || xcol >= W;
-        const int hcol = xcol < 0 ? xcol + P : P + xcol - W;
-#pragma unroll
-        for (int k = 0; k < (NSG + NWAVE - 1) / NWAVE; ++k) {
-            const int g = wave + k * NWAVE;                    // wave-uniform
-            if (g < NSG) {
-                const int rr = 8 * g + (lane >> 3);
-                const int r = i0 - P + rr;
-                const bool on = rr < LH && (left || right);
-                float* dst = buf + MAIN + g * 8 * SP;
-                if (on && halo) dma4(rh, dst, (r * 2 * P + hcol) * 4);
-                if (on && !halo) dma4(rx, dst, (r * W + xcol) * 4);
             }
         }
     }
@@ -646,11 +594,10 @@ dw_bwd_kernel(DwArgs a)
     constexpr int KK = K * K;
     constexpr int NV = KK + 1;
     constexpr int NWAVE = T::NWAVE;
-    // vector memory instructions every wave issues for one tile (at least)
-    constexpr int ISSUED = T::NLOAD / NWAVE + T::NSG / NWAVE;
-    __shared__ __align__(16) float bufg[3][T::FLOATS];   // grad_output tiles (extended), a ring of 3
-    __shared__ __align__(16) float bufx[3][T::FLOATS];   // input tiles (extended)
+    __shared__ __align__(16) float bufg[2][T::FLOATS];   // grad_output tiles (extended)
+    __shared__ __align__(16) float bufx[2][T::FLOATS];   // input tiles (extended)
     __shared__ float red[NWAVE][NV + 2];
+    typename T::Side S;
     const bool wgrad_half = threadIdx.x >= T::NT;    // wave-uniform
     const int tid = threadIdx.x - (wgrad_half ? T::NT : 0);
     const int tx = tid % TX, ty = tid / TX;
@@ -666,24 +613,13 @@ dw_bwd_kernel(DwArgs a)
     auto issue = [&](int t, float* b) {
         const TileIdx e = decode_channel_major(a, t, T::TH, T::TW);
         T::load_main(b, src + e.plane * HW, a.H, a.W, e.i0, e.j0, tid);
-        T::load_side_lds(b, src + e.plane * HW, src_h + (int64_t)e.plane * a.H * (2 * P), a.H, a.W, e.i0, e.j0,
-                         tid);
+        T::load_side(S, src + e.plane * HW, src_h + (int64_t)e.plane * a.H * (2 * P), a.H, a.W, e.i0, e.j0,
+                     tid);
     };
-    // Loads run two tiles ahead: tile t + 2 is issued right after the
-    // barrier that publishes tile t (its buffer was last read by tile t - 1,
-    // which every wave finished before that barrier).  Before publishing
-    // tile t a wave waits for all but its last ISSUED operations, which
-    // belong to tile t + 1 when there is one.
     issue(beg, mybuf[0]);
-    if (beg + 1 < end) issue(beg + 1, mybuf[1]);
-    auto publish = [&](int t) {
-        if (t + 1 < end) wait_vmem_n<ISSUED>();
-        else wait_vmem();
-        lds_barrier();
-    };
 
     if (!wgrad_half) {
-        int it = 0, cur = 0;
+        int it = 0;
         float acc[RH][4];
         TileIdx dprev{};
         for (int t = beg; t < end;) {
@@ -692,39 +628,42 @@ dw_bwd_kernel(DwArgs a)
             float wr[KK];
             load_weights<K, true>(a.w, c, wr);
             for (; t < run_end; ++t, ++it) {
-                float* cb = bufg[cur];
+                float* cb = bufg[it & 1];
                 const TileIdx d = decode_channel_major(a, t, T::TH, T::TW);
-                publish(t);
+                T::put_side(cb, S, tid);
+                wait_vmem();
+                lds_barrier();
                 if (it > 0) store_rows<RH>(a.out, dprev, a.H, a.W, tx, ty, acc);   // previous tile's
-                if (t + 2 < end) issue(t + 2, bufg[cur == 0 ? 2 : cur - 1]);
+                if (t + 1 < end) issue(t + 1, bufg[(it + 1) & 1]);
 #pragma unroll
                 for (int i = 0; i < RH; ++i)
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) acc[i][jj] = 0.f;
                 conv_tile<K, TX, TY, RH>(cb, wr, acc, tx, ty);
                 dprev = d;
-                cur = cur == 2 ? 0 : cur + 1;
             }
             lds_barrier();   // the flush's barrier
         }
         store_rows<RH>(a.out, dprev, a.H, a.W, tx, ty, acc);
     } else {
-        int cur = 0;
+        int it = 0;
         for (int t = beg; t < end;) {
             const int c = t / tiles_c;
             const int run_end = min(end, (c + 1) * tiles_c);
             float acc[NV];
 #pragma unroll
             for (int k = 0; k < NV; ++k) acc[k] = 0.f;
-            for (; t < run_end; ++t) {
-                float* cb = bufx[cur];
+            for (; t < run_end; ++t, ++it) {
+                float* cb = bufx[it & 1];
                 const TileIdx d = decode_channel_major(a, t, T::TH, T::TW);
-                publish(t);
-                if (t + 2 < end) issue(t + 2, bufx[cur == 0 ? 2 : cur - 1]);
+                T::put_side(cb, S, tid);
+                wait_vmem();
+                lds_barrier();
+                if (t + 1 < end) issue(t + 1, bufx[(it + 1) & 1]);
                 // grad_output at the thread's outputs: the centre of this
                 // tile's grad_output buffer (main region row P + i, column j)
                 float gv[RH][4];
-                const float* gp = bufg[cur] + (ty * RH + P) * T::TW + 4 * tx;
+                const float* gp = bufg[it & 1] + (ty * RH + P) * T::TW + 4 * tx;
 #pragma unroll
                 for (int i = 0; i < RH; ++i) {
                     const float4 v = *reinterpret_cast<const float4*>(gp + i * T::TW);
@@ -733,7 +672,6 @@ dw_bwd_kernel(DwArgs a)
                     acc[KK] += (gv[i][0] + gv[i][1]) + (gv[i][2] + gv[i][3]);
                 }
                 wgrad_tile<K, TX, TY, RH>(cb, gv, acc, tx, ty);
-                cur = cur == 2 ? 0 : cur + 1;
             }
             flush_write<NV, NWAVE>(acc, red, tid);
             lds_barrier();
