@@ -37,17 +37,17 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kNT = 256;
-constexpr int kBM = 128;         // result rows per workgroup
-constexpr int kBN = 128;         // result columns per workgroup
 constexpr int kSub = 16;         // reduction per gathered sub-chunk
 constexpr int kKS = 1;           // sub-chunks per LDS stage
 constexpr int kBK = kSub * kKS;  // reduction per LDS stage
-// LDS row pitch (floats), = 4 mod 64 banks.  At MFMA step s the two half-waves
-// read k rows s and s + 8 of a sub-chunk (both operands pair k the same way),
-// which 8 * kLD = 32 mod 64 puts in disjoint banks; and the operand gathers'
-// writes of k rows 4 apart (grad_weight's grad_output tile) or 8 apart (the
-// forward's weight tile) land 16 or 32 banks apart instead of on one bank.
-constexpr int kLD = kBM + 4;
+// A workgroup computes a TM x TN tile of the result (TM, TN in {64, 128}).
+// LDS rows of an operand tile of width T have a pitch of T + 4 floats (4 mod
+// 64 banks).  At MFMA step s the two half-waves read k rows s and s + 8 of a
+// sub-chunk (both operands pair k the same way), which 8 * (T + 4) = 32 mod 64
+// puts in disjoint banks; and the operand gathers' writes of k rows 4 apart
+// (grad_weight's grad_output tile) or 8 apart (the forward's weight tile) land
+// 16 or 32 banks apart instead of on one bank.
+constexpr int pitch(int width) { return width + 4; }
 
 enum Mode { FWD = 0, BWI = 1, BWW = 2 };
 
@@ -69,8 +69,13 @@ __device__ __forceinline__ int64_t slab_floats(const PArgs& a) { return (int64_t
 // and 8 B values per thread), then registers -> LDS.  Each mode gathers its
 // own operands; a sub-chunk past the end of the reduction (ok_k false) loads
 // zeros.
-template <int MODE, int S>
+template <int MODE, int S, int TM, int TN>
 struct Sub {
+    static constexpr int LDA = pitch(TM), LDB = pitch(TN);
+    // the narrow (64) tile is only the K = (ci, kh, kw) side of grad_input (TM)
+    // and grad_weight (TN), for layers with ci * k * k <= 64
+    static_assert((MODE == FWD && TM == 128 && TN == 128) || (MODE == BWI && TN == 128) ||
+                      (MODE == BWW && TM == 128), "tile shape");
     float ra[8];
     float rb[8];
 
@@ -92,7 +97,7 @@ struct Sub {
 #pragma unroll
             for (int r = 0; r < 8 / S; ++r) {
                 const int idx = t + kNT * r;
-                const int gl = idx / kBN, p = idx % kBN;
+                const int gl = idx / TN, p = idx % TN;
                 const int gg = k0 / S + gl;                 // global K group = ci * s + kh
                 const int ci = gg / S, kh = gg - ci * S;
                 const int pp = n0 + p;
@@ -110,9 +115,9 @@ struct Sub {
         } else if constexpr (MODE == BWI) {
             // A[m][c] = W[k0 + c][m0 + m] (the weight read transposed): rows along m
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
+            for (int r = 0; r < TM / 64; ++r) {
                 const int idx = t + kNT * r;
-                const int c = idx / 32, m4 = (idx % 32) * 4;
+                const int c = idx / (TM / 4), m4 = (idx % (TM / 4)) * 4;
                 const bool ok = ok_k && m0 + m4 < a.Kt;
                 const float4 v = ok ? *reinterpret_cast<const float4*>(a.w + (int64_t)(k0 + c) * a.Kt + m0 + m4)
                                     : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -145,7 +150,7 @@ struct Sub {
             const int i = k0 / a.Wo, j0 = k0 - i * a.Wo;
             const float* xi = a.x + (int64_t)img * a.Ci * a.H * a.W;
 #pragma unroll
-            for (int r = 0; r < 8 / S; ++r) {
+            for (int r = 0; r < TN / (16 * S); ++r) {
                 const int idx = t + kNT * r;
                 const int q = idx % kSub, gl = idx / kSub;
                 const int gg = n0 / S + gl;
@@ -163,28 +168,33 @@ struct Sub {
         }
     }
 
-    // LDS rows of this sub-chunk: As[k][m], Bs[k][n] (k-major rows of pitch kLD).
+    // LDS rows of this sub-chunk: As[k][m], Bs[k][n] (k-major rows of pitch LDA, LDB).
     __device__ void put(float* __restrict__ As, float* __restrict__ Bs) const
     {
         const int t = threadIdx.x;
         if constexpr (MODE == FWD) {
             const int m = t >> 1, kh = (t & 1) * 8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) As[(kh + e) * kLD + m] = ra[e];
+            for (int e = 0; e < 8; ++e) As[(kh + e) * LDA + m] = ra[e];
 #pragma unroll
             for (int r = 0; r < 8 / S; ++r) {
                 const int idx = t + kNT * r;
-                const int gl = idx / kBN, p = idx % kBN;
+                const int gl = idx / TN, p = idx % TN;
 #pragma unroll
-                for (int kw = 0; kw < S; ++kw) Bs[(gl * S + kw) * kLD + p] = rb[S * r + kw];
+                for (int kw = 0; kw < S; ++kw) Bs[(gl * S + kw) * LDB + p] = rb[S * r + kw];
             }
         } else if constexpr (MODE == BWI) {
+#pragma unroll
+            for (int r = 0; r < TM / 64; ++r) {
+                const int idx = t + kNT * r;
+                const int c = idx / (TM / 4), x4 = (idx % (TM / 4)) * 4;
+                *reinterpret_cast<float4*>(As + c * LDA + x4) = make_float4(ra[4 * r], ra[4 * r + 1], ra[4 * r + 2], ra[4 * r + 3]);
+            }
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 const int idx = t + kNT * r;
                 const int c = idx / 32, x4 = (idx % 32) * 4;
-                *reinterpret_cast<float4*>(As + c * kLD + x4) = make_float4(ra[4 * r], ra[4 * r + 1], ra[4 * r + 2], ra[4 * r + 3]);
-                *reinterpret_cast<float4*>(Bs + c * kLD + x4) = make_float4(rb[4 * r], rb[4 * r + 1], rb[4 * r + 2], rb[4 * r + 3]);
+                *reinterpret_cast<float4*>(Bs + c * LDB + x4) = make_float4(rb[4 * r], rb[4 * r + 1], rb[4 * r + 2], rb[4 * r + 3]);
             }
         } else {
 #pragma unroll
@@ -192,25 +202,28 @@ struct Sub {
                 const int idx = t + kNT * r;
                 const int m = idx / 4, q4 = (idx % 4) * 4;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) As[(q4 + e) * kLD + m] = ra[4 * r + e];
+                for (int e = 0; e < 4; ++e) As[(q4 + e) * LDA + m] = ra[4 * r + e];
             }
 #pragma unroll
-            for (int r = 0; r < 8 / S; ++r) {
+            for (int r = 0; r < TN / (16 * S); ++r) {
                 const int idx = t + kNT * r;
                 const int q = idx % kSub, gl = idx / kSub;
 #pragma unroll
-                for (int kw = 0; kw < S; ++kw) Bs[q * kLD + gl * S + kw] = rb[S * r + kw];
+                for (int kw = 0; kw < S; ++kw) Bs[q * LDB + gl * S + kw] = rb[S * r + kw];
             }
         }
     }
 };
 
-template <int MODE, int S>
+template <int MODE, int S, int TM, int TN>
 __global__ void __launch_bounds__(kNT, 2)
 patch_kernel(PArgs a)
 {
-    __shared__ __align__(16) float As[2][kBK * kLD];
-    __shared__ __align__(16) float Bs[2][kBK * kLD];
+    using Stage = Sub<MODE, S, TM, TN>;
+    constexpr int LDA = Stage::LDA, LDB = Stage::LDB;
+    constexpr int XB = TM / 64, YB = TN / 64;    // 32 x 32 MFMA blocks per wave (waves in a 2 x 2 grid)
+    __shared__ __align__(16) float As[2][kBK * LDA];
+    __shared__ __align__(16) float Bs[2][kBK * LDB];
 
     // tile -> (img or split, m tile, n tile); m fastest, so workgroups that
     // share the large operand (the pixels) run side by side
@@ -219,7 +232,7 @@ patch_kernel(PArgs a)
     bid /= a.tiles_m;
     const int nt = bid % a.tiles_n;
     const int outer = bid / a.tiles_n;           // image (FWD / BWI) or split (BWW)
-    const int m0 = mt * kBM, n0 = nt * kBN;
+    const int m0 = mt * TM, n0 = nt * TN;
 
     // reduction range in sub-chunks of kSub
     int c_beg, c_end;
@@ -232,7 +245,7 @@ patch_kernel(PArgs a)
     const int nstage = (c_end - c_beg + kKS - 1) / kKS;
     const int cpi = a.P / kSub;                  // BWW: sub-chunks per image
 
-    Sub<MODE, S> sub[kKS];
+    Stage sub[kKS];
     auto load_stage = [&](int stg) {
 #pragma unroll
         for (int u = 0; u < kKS; ++u) {
@@ -254,11 +267,11 @@ patch_kernel(PArgs a)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int hi = lane >> 5, l32 = lane & 31;
-    f32x16 acc[2][2];
+    f32x16 acc[XB][YB];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int x = 0; x < XB; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
+        for (int y = 0; y < YB; ++y)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
     float bias_acc = 0.f;
@@ -269,50 +282,55 @@ patch_kernel(PArgs a)
         float* as = As[stg & 1];
         float* bs = Bs[stg & 1];
 #pragma unroll
-        for (int u = 0; u < kKS; ++u) sub[u].put(as + u * kSub * kLD, bs + u * kSub * kLD);
+        for (int u = 0; u < kKS; ++u) sub[u].put(as + u * kSub * LDA, bs + u * kSub * LDB);
         lds_barrier();
         if (stg + 1 < nstage) load_stage(stg + 1);
-        if (with_bias && threadIdx.x < kBM) {
+        if (with_bias && threadIdx.x < TM) {
 #pragma unroll
-            for (int q = 0; q < kBK; ++q) bias_acc += as[q * kLD + threadIdx.x];
+            for (int q = 0; q < kBK; ++q) bias_acc += as[q * LDA + threadIdx.x];
         }
         // operands of step s2 + 1 are read before the MFMAs of step s2 are
         // issued (the scheduling barriers keep that order), so the LDS
         // latency overlaps the matrix pipe instead of stalling it
         // k-slot pairing of step s2 in sub-chunk u: rows 16 u + s2 (lanes 0..31)
         // and 16 u + s2 + 8 (lanes 32..63)
-        const float* ap = as + hi * (kSub / 2) * kLD + wm * 64 + l32;
-        const float* bp = bs + hi * (kSub / 2) * kLD + wn * 64 + l32;
+        const float* ap = as + hi * (kSub / 2) * LDA + wm * (TM / 2) + l32;
+        const float* bp = bs + hi * (kSub / 2) * LDB + wn * (TN / 2) + l32;
         auto row = [](int s2) { return (s2 / (kSub / 2)) * kSub + s2 % (kSub / 2); };
-        float a0 = ap[0], a1 = ap[32], b0 = bp[0], b1 = bp[32];
+        float av[XB], bv[YB];
+#pragma unroll
+        for (int x = 0; x < XB; ++x) av[x] = ap[32 * x];
+#pragma unroll
+        for (int y = 0; y < YB; ++y) bv[y] = bp[32 * y];
 #pragma unroll
         for (int s2 = 0; s2 < kBK / 2; ++s2) {
-            float na0 = 0.f, na1 = 0.f, nb0 = 0.f, nb1 = 0.f;
-            if (s2 + 1 < kBK / 2) {
-                const int r = row(s2 + 1) * kLD;
-                na0 = ap[r];
-                na1 = ap[r + 32];
-                nb0 = bp[r];
-                nb1 = bp[r + 32];
-            }
+            float na[XB], nb[YB];
+#pragma unroll
+            for (int x = 0; x < XB; ++x) na[x] = s2 + 1 < kBK / 2 ? ap[row(s2 + 1) * LDA + 32 * x] : 0.f;
+#pragma unroll
+            for (int y = 0; y < YB; ++y) nb[y] = s2 + 1 < kBK / 2 ? bp[row(s2 + 1) * LDB + 32 * y] : 0.f;
             __builtin_amdgcn_sched_barrier(0);
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+#pragma unroll
+            for (int x = 0; x < XB; ++x)
+#pragma unroll
+                for (int y = 0; y < YB; ++y)
+                    acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[x], bv[y], acc[x][y], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            a0 = na0; a1 = na1; b0 = nb0; b1 = nb1;
+#pragma unroll
+            for (int x = 0; x < XB; ++x) av[x] = na[x];
+#pragma unroll
+            for (int y = 0; y < YB; ++y) bv[y] = nb[y];
         }
         // the buffer just read is rewritten two stages later, after the next barrier
     }
 
     // D block (x, y): register 4 q + r holds row 4 hi + 8 q + r, column l32
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int x = 0; x < XB; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-            const int rb = m0 + wm * 64 + x * 32;     // block's first row (a multiple of 4)
-            const int col = n0 + wn * 64 + y * 32 + l32;
+        for (int y = 0; y < YB; ++y) {
+            const int rb = m0 + wm * (TM / 2) + x * 32;     // block's first row (a multiple of 4)
+            const int col = n0 + wn * (TN / 2) + y * 32 + l32;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int row = rb + 4 * hi + 8 * q;  // rows row .. row + 3 in registers 4q .. 4q + 3
@@ -354,7 +372,7 @@ patch_kernel(PArgs a)
                 }
             }
         }
-    if (with_bias && threadIdx.x < kBM && m0 + threadIdx.x < a.Co)
+    if (with_bias && threadIdx.x < TM && m0 + threadIdx.x < a.Co)
         a.out[outer * slab_floats(a) + (int64_t)a.Co * a.Kt + m0 + threadIdx.x] = bias_acc;
 }
 
@@ -422,13 +440,17 @@ int wgrad_splits(const PArgs& a, int tiles)
 
 int split_groups(int splits) { return splits > kOneStageMax ? (splits + kSlabsPerGroup - 1) / kSlabsPerGroup : 0; }
 
-template <int MODE>
+template <int MODE, int TM, int TN>
 hipError_t launch(const PArgs& a, int s, int grid, hipStream_t st)
 {
-    if (s == 2) hipLaunchKernelGGL((patch_kernel<MODE, 2>), dim3(grid), dim3(kNT), 0, st, a);
-    else hipLaunchKernelGGL((patch_kernel<MODE, 4>), dim3(grid), dim3(kNT), 0, st, a);
+    if (s == 2) hipLaunchKernelGGL((patch_kernel<MODE, 2, TM, TN>), dim3(grid), dim3(kNT), 0, st, a);
+    else hipLaunchKernelGGL((patch_kernel<MODE, 4, TM, TN>), dim3(grid), dim3(kNT), 0, st, a);
     return hipGetLastError();
 }
+
+// The K = (ci, kh, kw) side of grad_input (rows) and grad_weight (columns) is
+// tiled by 64 when ci * k * k <= 64 (the 3-channel stem: 48), by 128 otherwise.
+constexpr int kNarrowK = 64;
 
 }  // namespace
 
@@ -444,7 +466,8 @@ bool patch_supported(const Geom& g)
 size_t patch_wgrad_workspace_bytes(const Geom& g)
 {
     const PArgs a = make_args(g);
-    const int tiles = ((a.Co + kBM - 1) / kBM) * ((a.Kt + kBN - 1) / kBN);
+    const int tn = a.Kt <= kNarrowK ? kNarrowK : 128;
+    const int tiles = ((a.Co + 127) / 128) * ((a.Kt + tn - 1) / tn);
     const int64_t s = wgrad_splits(a, tiles);
     const int64_t slab = (int64_t)a.Co * (a.Kt + 1);
     return (size_t)((s + split_groups((int)s)) * slab) * sizeof(float);
@@ -455,18 +478,22 @@ hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const
 {
     PArgs a = make_args(g);
     a.x = x; a.w = w; a.b = b; a.out = y;
-    a.tiles_m = (a.Co + kBM - 1) / kBM;
-    a.tiles_n = (a.P + kBN - 1) / kBN;
-    return launch<FWD>(a, g.k, a.tiles_m * a.tiles_n * a.N, st);
+    a.tiles_m = (a.Co + 127) / 128;
+    a.tiles_n = (a.P + 127) / 128;
+    return launch<FWD, 128, 128>(a, g.k, a.tiles_m * a.tiles_n * a.N, st);
 }
 
 hipError_t launch_patch_bwd_input(const Geom& g, const float* gy, const float* w, float* gx, hipStream_t st)
 {
     PArgs a = make_args(g);
     a.g = gy; a.w = w; a.out = gx;
-    a.tiles_m = (a.Kt + kBM - 1) / kBM;
-    a.tiles_n = (a.P + kBN - 1) / kBN;
-    return launch<BWI>(a, g.k, a.tiles_m * a.tiles_n * a.N, st);
+    a.tiles_n = (a.P + 127) / 128;
+    if (a.Kt <= kNarrowK) {
+        a.tiles_m = 1;
+        return launch<BWI, kNarrowK, 128>(a, g.k, a.tiles_n * a.N, st);
+    }
+    a.tiles_m = (a.Kt + 127) / 128;
+    return launch<BWI, 128, 128>(a, g.k, a.tiles_m * a.tiles_n * a.N, st);
 }
 
 hipError_t launch_patch_bwd_weight(const Geom& g, const float* x, const float* gy, float* gw, float* gb,
@@ -474,14 +501,16 @@ hipError_t launch_patch_bwd_weight(const Geom& g, const float* x, const float* g
 {
     PArgs a = make_args(g);
     a.x = x; a.g = gy;
-    a.tiles_m = (a.Co + kBM - 1) / kBM;
-    a.tiles_n = (a.Kt + kBN - 1) / kBN;
+    const bool narrow = a.Kt <= kNarrowK;
+    a.tiles_m = (a.Co + 127) / 128;
+    a.tiles_n = narrow ? 1 : (a.Kt + 127) / 128;
     a.chunks = a.N * (a.P / kSub);
     a.splits = wgrad_splits(a, a.tiles_m * a.tiles_n);
     a.with_bias = gb != nullptr;
     float* slabs = static_cast<float*>(ws);
     a.out = slabs;
-    hipError_t e = launch<BWW>(a, g.k, a.tiles_m * a.tiles_n * a.splits, st);
+    const int grid = a.tiles_m * a.tiles_n * a.splits;
+    hipError_t e = narrow ? launch<BWW, 128, kNarrowK>(a, g.k, grid, st) : launch<BWW, 128, 128>(a, g.k, grid, st);
     if (e != hipSuccess) return e;
 
     // slab sums: count4 float4 per slab (Co * Kt weights, then Co biases)
