@@ -1,0 +1,154 @@
+"""Autograd layer over the W-sharded convolution ABI.
+
+The pages train ConvNeXt with every activation sharded along W and the
+parameters replicated (NVIDIA blog "Perception Model Training for Autonomous
+Vehicles with Tensor Parallelism", DTensor section: activations Shard(3),
+weights Replicate; the kwkr.cn retelling, section 3.2, wraps the halo exchange
+in an autograd function).  Here an activation is a list of S contiguous
+(N, C, H, W/S) float32 tensors on one device, one per shard, as they would sit
+on S GPUs, and `ShardedConv2d` is a module over such lists:
+
+* forward: each shard gathers its halo columns from its two neighbours, then
+  convolves its slice (output: the shard's own columns);
+* backward: grad_output halos are gathered the same way; each shard computes
+  its grad_input slice and its partial grad_weight / grad_bias over its own
+  output columns; the partials are summed in shard order (the reduction that
+  turns the _Partial gradients into replicated ones).
+
+This file only marshals tensors and calls the C ABI (`sscnn`); every step runs
+in the library's kernels, and there is no fallback when the library is
+missing.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Sequence
+
+import torch
+
+from . import sscnn
+
+
+def shard(x: torch.Tensor, num_shards: int) -> List[torch.Tensor]:
+    """Split an (N, C, H, W) tensor into num_shards contiguous W-slices."""
+    if x.dim() != 4 or x.shape[3] % num_shards:
+        raise ValueError(f"cannot split width {tuple(x.shape)} into {num_shards} shards")
+    w = x.shape[3] // num_shards
+    return [x[..., s * w:(s + 1) * w].contiguous() for s in range(num_shards)]
+
+
+def unshard(xs: Sequence[torch.Tensor]) -> torch.Tensor:
+    """Concatenate W-shards back into one tensor."""
+    return torch.cat(list(xs), dim=3)
+
+
+class _ShardedConv(torch.autograd.Function):
+    """Arguments: (layer, weight, bias or None, *x_shards) -> tuple of y shards."""
+
+    @staticmethod
+    def forward(ctx, layer, weight, bias, *xs):
+        S = len(xs)
+        convs = layer._descriptors(xs)
+        dev = xs[0].device
+        halos = []
+        for s, c in enumerate(convs):
+            h = torch.empty(c.halo_shape(sscnn.HALO_INPUT), device=dev, dtype=torch.float32)
+            sscnn.halo_gather(c, sscnn.HALO_INPUT, xs[s - 1] if s > 0 else None, xs[s + 1] if s + 1 < S else None, h)
+            halos.append(h)
+        ys = []
+        for s, c in enumerate(convs):
+            y = torch.empty(c.y_shape, device=dev, dtype=torch.float32)
+            sscnn.conv_fwd(c, xs[s], halos[s], weight, bias, y)
+            ys.append(y)
+        ctx.convs = convs
+        ctx.has_bias = bias is not None
+        ctx.save_for_backward(weight, *xs, *halos)
+        return tuple(ys)
+
+    @staticmethod
+    def backward(ctx, *gys):
+        convs = ctx.convs
+        S = len(convs)
+        saved = ctx.saved_tensors
+        weight, xs, halos = saved[0], saved[1:1 + S], saved[1 + S:1 + 2 * S]
+        dev = weight.device
+        gys = [torch.zeros(c.y_shape, device=dev, dtype=torch.float32) if g is None else g.contiguous()
+               for g, c in zip(gys, convs)]
+        need_dx = any(ctx.needs_input_grad[3:])
+        ghalos = []
+        for s, c in enumerate(convs):
+            h = torch.empty(c.halo_shape(sscnn.HALO_GRAD_OUTPUT), device=dev, dtype=torch.float32)
+            sscnn.halo_gather(c, sscnn.HALO_GRAD_OUTPUT, gys[s - 1] if s > 0 else None,
+                              gys[s + 1] if s + 1 < S else None, h)
+            ghalos.append(h)
+        nw, co = weight.numel(), weight.shape[0]
+        parts = [torch.empty(nw + co, device=dev, dtype=torch.float32) for _ in range(S)]
+        workspace = sscnn.new_workspace(convs[0], device=dev)   # shards share a geometry; calls run in order
+        dxs = []
+        for s, c in enumerate(convs):
+            gw_part, gb_part = parts[s][:nw].view(weight.shape), parts[s][nw:]
+            if need_dx:
+                dx = torch.empty(c.x_shape, device=dev, dtype=torch.float32)
+                sscnn.conv_bwd(c, xs[s], halos[s], gys[s], ghalos[s], weight, dx, gw_part, gb_part, workspace)
+                dxs.append(dx)
+            else:
+                sscnn.conv_bwd_weight_partial(c, xs[s], halos[s], gys[s], gw_part, gb_part, workspace)
+                dxs.append(None)
+        reduced = torch.empty(nw + co, device=dev, dtype=torch.float32)
+        sscnn.partial_reduce(parts, reduced)
+        grad_w = reduced[:nw].view(weight.shape)
+        grad_b = reduced[nw:] if ctx.has_bias else None
+        return (None, grad_w, grad_b, *dxs)
+
+
+class ShardedConv2d(torch.nn.Module):
+    """A 2-D convolution (cross-correlation, zero padding, square kernel) on
+    W-sharded activations: forward(list of S shards) -> list of S shards.
+
+    Parameters are replicated (one weight / bias tensor); their gradients are
+    the reduced sums of the shards' partials.  Initialisation matches
+    torch.nn.Conv2d's defaults."""
+
+    def __init__(self, in_channels: int, out_channels: int, kernel_size: int, stride: int = 1,
+                 padding: int = 0, groups: int = 1, bias: bool = True, device="cuda"):
+        super().__init__()
+        if in_channels % groups or out_channels % groups:
+            raise ValueError("groups must divide in_channels and out_channels")
+        self.in_channels, self.out_channels = in_channels, out_channels
+        self.kernel_size, self.stride, self.padding, self.groups = kernel_size, stride, padding, groups
+        self.weight = torch.nn.Parameter(torch.empty(out_channels, in_channels // groups, kernel_size, kernel_size,
+                                                     device=device, dtype=torch.float32))
+        self.bias = (torch.nn.Parameter(torch.empty(out_channels, device=device, dtype=torch.float32))
+                     if bias else None)
+        self.reset_parameters()
+        self._cache = {}
+
+    def reset_parameters(self):
+        torch.nn.init.kaiming_uniform_(self.weight, a=math.sqrt(5))
+        if self.bias is not None:
+            fan_in = self.weight.shape[1] * self.kernel_size * self.kernel_size
+            bound = 1.0 / math.sqrt(fan_in)
+            torch.nn.init.uniform_(self.bias, -bound, bound)
+
+    def _descriptors(self, xs):
+        shapes = tuple(tuple(x.shape) for x in xs)
+        if len(set(shapes)) != 1:
+            raise ValueError(f"shards must have one shape, got {shapes}")
+        key = shapes[0] + (len(xs),)
+        if key not in self._cache:
+            n, c, h, w = shapes[0]
+            if c != self.in_channels:
+                raise ValueError(f"expected {self.in_channels} channels, got {c}")
+            self._cache[key] = [sscnn.conv_init(n, c, self.out_channels, h, w, self.kernel_size, self.stride,
+                                                self.padding, self.groups, s, len(xs)) for s in range(len(xs))]
+        return self._cache[key]
+
+    def forward(self, xs: Sequence[torch.Tensor]) -> List[torch.Tensor]:
+        xs = list(xs)
+        if not xs:
+            raise ValueError("no shards")
+        return list(_ShardedConv.apply(self, self.weight, self.bias, *xs))
+
+    def extra_repr(self):
+        return (f"{self.in_channels}, {self.out_channels}, kernel_size={self.kernel_size}, stride={self.stride}, "
+                f"padding={self.padding}, groups={self.groups}, bias={self.bias is not None}")

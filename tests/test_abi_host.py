@@ -208,3 +208,20 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(c.x_shape)
     with pytest.raises(ValueError):
         sscnn.conv_fwd(c, x, None, None, None, None)
+
+
+def test_autograd_shard_round_trip_and_host_tensors_rejected():
+    """The autograd layer marshals only: shard / unshard are exact, and host
+    tensors are refused before anything is launched."""
+    import torch
+    from spatially_sharded_cnn_amd import autograd as sa
+    x = torch.arange(2 * 3 * 4 * 12, dtype=torch.float32).reshape(2, 3, 4, 12)
+    xs = sa.shard(x, 4)
+    assert [tuple(t.shape) for t in xs] == [(2, 3, 4, 3)] * 4 and all(t.is_contiguous() for t in xs)
+    assert torch.equal(sa.unshard(xs), x)
+    with pytest.raises(ValueError):
+        sa.shard(x, 5)
+    layer = sa.ShardedConv2d(3, 6, 3, padding=1, device="cpu")
+    assert layer.weight.shape == (6, 3, 3, 3) and layer.bias.shape == (6,)
+    with pytest.raises(ValueError):
+        layer(xs)
