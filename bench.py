@@ -335,7 +335,7 @@ def _layer_work(c, L):
 
 
 def stack_bench(args, wl):
-    """A ConvNeXt-style stack (SURVEY configs 4 and 5): one step is the
+    """A ConvNeXt-style stack (on (7,3,512,2048) or (7,3,512,4096) inputs): one step is the
     measured shard's forward chain (halo_gather + conv_fwd per layer, each
     layer's output feeding the next) and its backward chain in reverse
     (halo_gather(G) + conv_bwd + partial_reduce per layer, each grad_input
