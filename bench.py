@@ -87,6 +87,40 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def step_spread(step, n):
+    """Median and minimum of n single steps, each between its own pair of
+    events (a pass after the timed region; the reported value comes from the
+    timed region)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        step(i)
+        b.record()
+    torch.cuda.synchronize()
+    us = sorted(1e3 * a.elapsed_time(b) for a, b in ev)
+    return {"step_us_median": round(us[len(us) // 2], 2), "step_us_min": round(us[0], 2), "samples": n}
+
+
+def gpu_clocks():
+    """The current shader and memory clock levels of the GPUs the driver
+    lists, read from sysfs (the level marked '*' in pp_dpm_sclk / pp_dpm_mclk),
+    or None where those files are not readable."""
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        rec = {}
+        for clk in ("sclk", "mclk"):
+            try:
+                cur = [ln for ln in pathlib.Path(dev, f"pp_dpm_{clk}").read_text().splitlines() if "*" in ln]
+            except OSError:
+                continue
+            if cur:
+                rec[clk] = cur[0].split(":", 1)[-1].replace("*", "").strip()
+        if rec:
+            out[pathlib.Path(dev).parent.name] = rec
+    return out or None
+
+
 def recorded_traffic(workload: str):
     """Counter-measured HBM bytes per launch of the dominant operation, from
     profiles/traffic_<workload>.md, if recorded for the current sources."""
@@ -228,6 +262,8 @@ def main():
     wall = time.perf_counter() - w0
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
+    spread = step_spread(lambda i: step(sets[i % len(sets)]), args.steps)
+
     # Each operation on its own: back-to-back calls between two events.
     op_us = {}
     for name, f in list(ops.items()) + list(extra_ops.items()):
@@ -307,7 +343,9 @@ def main():
         "roofline_frac_step": round(sum(roof_time(k) for k in step_ops) / step_s, 4),
         "roofline": roof,
         "ops_us": {k: round(v, 2) for k, v in op_us.items()},
+        "step_spread": spread,
         "wall_s_timed": round(wall, 4),
+        "gpu_clocks": gpu_clocks(),
         "source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
@@ -413,6 +451,8 @@ def stack_bench(args, wl):
     wall = time.perf_counter() - w0
     ms_per_step = e0.elapsed_time(e1) / steps
 
+    spread = step_spread(lambda i: step(), steps)
+
     # each operation on its own, back to back
     op_us = {}
     for l, name, f in ops:
@@ -483,7 +523,9 @@ def stack_bench(args, wl):
         "roofline_frac_step": round(sum(r["roofline_us"] for r in layers) * 1e-6 / step_s, 4),
         "roofline": roof,
         "layers": layers,
+        "step_spread": spread,
         "wall_s_timed": round(wall, 4),
+        "gpu_clocks": gpu_clocks(),
         "source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
