@@ -72,10 +72,10 @@ __device__ __forceinline__ int64_t slab_floats(const PArgs& a) { return (int64_t
 template <int MODE, int S, int TM, int TN>
 struct Sub {
     static constexpr int LDA = pitch(TM), LDB = pitch(TN);
-    // the narrow (64) tile is only the K = (ci, kh, kw) side of grad_input (TM)
-    // and grad_weight (TN), for layers with ci * k * k <= 64
-    static_assert((MODE == FWD && TM == 128 && TN == 128) || (MODE == BWI && TN == 128) ||
-                      (MODE == BWW && TM == 128), "tile shape");
+    // 64-wide tiles: the output channels of the forward (TM), and the K =
+    // (ci, kh, kw) side of grad_input (TM) and grad_weight (TN)
+    static_assert((MODE == FWD && TN == 128) || (MODE == BWI && TN == 128) || (MODE == BWW && TM == 128),
+                  "tile shape");
     float ra[8];
     float rb[8];
 
@@ -84,14 +84,16 @@ struct Sub {
     {
         const int t = threadIdx.x;
         if constexpr (MODE == FWD) {
-            // A[m][k] = W[m0 + m][k0 + k]: per row 16 contiguous floats, 2 threads a row
-            const int m = t >> 1, kh = (t & 1) * 8;
+            // A[m][k] = W[m0 + m][k0 + k]: per row 16 contiguous floats, 256 / TM threads a row
+            constexpr int TPR = kNT / TM, PER = kSub / TPR;          // threads per row, floats per thread
+            const int m = t / TPR, kh = (t % TPR) * PER;
             const bool ok = ok_k && m0 + m < a.Co;
             const float* src = a.w + (int64_t)(m0 + m) * a.Kt + k0 + kh;
-            const float4 v0 = ok ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
-            const float4 v1 = ok ? *reinterpret_cast<const float4*>(src + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-            ra[0] = v0.x; ra[1] = v0.y; ra[2] = v0.z; ra[3] = v0.w;
-            ra[4] = v1.x; ra[5] = v1.y; ra[6] = v1.z; ra[7] = v1.w;
+#pragma unroll
+            for (int v = 0; v < PER / 4; ++v) {
+                const float4 q = ok ? *reinterpret_cast<const float4*>(src + 4 * v) : make_float4(0.f, 0.f, 0.f, 0.f);
+                ra[4 * v] = q.x; ra[4 * v + 1] = q.y; ra[4 * v + 2] = q.z; ra[4 * v + 3] = q.w;
+            }
             // B[k][p] = X[img][ci][i*s + kh][j*s + kw]: item (group, pixel) = s floats
             const float* xi = a.x + (int64_t)img * a.Ci * a.H * a.W;
 #pragma unroll
@@ -173,9 +175,10 @@ struct Sub {
     {
         const int t = threadIdx.x;
         if constexpr (MODE == FWD) {
-            const int m = t >> 1, kh = (t & 1) * 8;
+            constexpr int TPR = kNT / TM, PER = kSub / TPR;
+            const int m = t / TPR, kh = (t % TPR) * PER;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) As[(kh + e) * LDA + m] = ra[e];
+            for (int e = 0; e < PER; ++e) As[(kh + e) * LDA + m] = ra[e];
 #pragma unroll
             for (int r = 0; r < 8 / S; ++r) {
                 const int idx = t + kNT * r;
@@ -452,6 +455,21 @@ hipError_t launch(const PArgs& a, int s, int grid, hipStream_t st)
 // tiled by 64 when ci * k * k <= 64 (the 3-channel stem: 48), by 128 otherwise.
 constexpr int kNarrowK = 64;
 
+// The forward's output channels are tiled by 64 instead of 128 when that
+// spreads the work more evenly over the CUs: when the busiest CU's share,
+// counted in 64-row tiles, is smaller (ceil(T64 / CUs) < 2 ceil(T128 / CUs)),
+// or when 128-row tiles would leave CUs idle.  Measured on the ConvNeXt-XL
+// downsamples: 64 rows for 896 or 224 tiles of 128 rows, 128 rows for 448.
+bool fwd_narrow(const PArgs& a)
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t cols = (int64_t)((a.P + 127) / 128) * a.N;
+    const int64_t wide = (int64_t)((a.Co + 127) / 128) * cols, narrow = (int64_t)((a.Co + 63) / 64) * cols;
+    const int64_t per_wide = (wide + cus - 1) / cus, per_narrow = (narrow + cus - 1) / cus;
+    return per_narrow < 2 * per_wide || wide < cus;
+}
+
 }  // namespace
 
 bool patch_supported(const Geom& g)
@@ -478,8 +496,12 @@ hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const
 {
     PArgs a = make_args(g);
     a.x = x; a.w = w; a.b = b; a.out = y;
-    a.tiles_m = (a.Co + 127) / 128;
     a.tiles_n = (a.P + 127) / 128;
+    if (fwd_narrow(a)) {
+        a.tiles_m = (a.Co + 63) / 64;
+        return launch<FWD, 64, 128>(a, g.k, a.tiles_m * a.tiles_n * a.N, st);
+    }
+    a.tiles_m = (a.Co + 127) / 128;
     return launch<FWD, 128, 128>(a, g.k, a.tiles_m * a.tiles_n * a.N, st);
 }
 

@@ -61,6 +61,8 @@ SMALL = [
     # ci * k * k <= 64: the 64-wide K tile of grad_input / grad_weight (K = 64 and 32; co not a multiple of 128)
     ("patch2_k64_narrow", 2, 16, 48, 32, 2 * 64, 2, 2, 0, 1, 2),
     ("patch2_k32_narrow", 1, 8, 160, 16, 2 * 32, 2, 2, 0, 1, 2),
+    # enough 128 x 128 forward tiles (512) for the 128-row forward tile
+    ("patch2_wide_fwd", 2, 16, 128, 256, 2 * 512, 2, 2, 0, 1, 2),
     ("grouped3x3", 1, 8, 12, 10, 3 * 12, 3, 1, 1, 4, 3),
     ("strided3x3p1", 1, 6, 10, 11, 2 * 16, 3, 2, 1, 1, 2),
 ]
