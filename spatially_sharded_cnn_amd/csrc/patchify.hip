@@ -455,17 +455,18 @@ hipError_t launch(const PArgs& a, int s, int grid, hipStream_t st)
 // tiled by 64 when ci * k * k <= 64 (the 3-channel stem: 48), by 128 otherwise.
 constexpr int kNarrowK = 64;
 
-// The forward's output channels are tiled by 64 instead of 128 when that
-// spreads the work more evenly over the CUs: when the busiest CU's share,
-// counted in 64-row tiles, is smaller (ceil(T64 / CUs) < 2 ceil(T128 / CUs)),
-// or when 128-row tiles would leave CUs idle.  Measured on the ConvNeXt-XL
-// downsamples: 64 rows for 896 or 224 tiles of 128 rows, 128 rows for 448.
-bool fwd_narrow(const PArgs& a)
+// The rows of the forward (output channels) and of grad_input (K) are tiled
+// by 64 instead of 128 when that spreads the work more evenly over the CUs:
+// when the busiest CU's share, counted in 64-row tiles, is smaller
+// (ceil(T64 / CUs) < 2 ceil(T128 / CUs)), or when 128-row tiles would leave
+// CUs idle.  Measured on the ConvNeXt-XL downsamples' forward: 64 rows for
+// 896 or 224 tiles of 128 rows, 128 rows for 448.
+bool rows_narrow(int rows, const PArgs& a)
 {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int64_t cols = (int64_t)((a.P + 127) / 128) * a.N;
-    const int64_t wide = (int64_t)((a.Co + 127) / 128) * cols, narrow = (int64_t)((a.Co + 63) / 64) * cols;
+    const int64_t wide = (int64_t)((rows + 127) / 128) * cols, narrow = (int64_t)((rows + 63) / 64) * cols;
     const int64_t per_wide = (wide + cus - 1) / cus, per_narrow = (narrow + cus - 1) / cus;
     return per_narrow < 2 * per_wide || wide < cus;
 }
@@ -497,7 +498,7 @@ hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const
     PArgs a = make_args(g);
     a.x = x; a.w = w; a.b = b; a.out = y;
     a.tiles_n = (a.P + 127) / 128;
-    if (fwd_narrow(a)) {
+    if (rows_narrow(a.Co, a)) {
         a.tiles_m = (a.Co + 63) / 64;
         return launch<FWD, 64, 128>(a, g.k, a.tiles_m * a.tiles_n * a.N, st);
     }
@@ -510,9 +511,9 @@ hipError_t launch_patch_bwd_input(const Geom& g, const float* gy, const float* w
     PArgs a = make_args(g);
     a.g = gy; a.w = w; a.out = gx;
     a.tiles_n = (a.P + 127) / 128;
-    if (a.Kt <= kNarrowK) {
-        a.tiles_m = 1;
-        return launch<BWI, kNarrowK, 128>(a, g.k, a.tiles_n * a.N, st);
+    if (a.Kt <= kNarrowK || rows_narrow(a.Kt, a)) {
+        a.tiles_m = (a.Kt + 63) / 64;
+        return launch<BWI, 64, 128>(a, g.k, a.tiles_m * a.tiles_n * a.N, st);
     }
     a.tiles_m = (a.Kt + 127) / 128;
     return launch<BWI, 128, 128>(a, g.k, a.tiles_m * a.tiles_n * a.N, st);
