@@ -40,6 +40,9 @@ constexpr int kNT = 256;
 constexpr int kSub = 16;         // reduction per gathered sub-chunk
 constexpr int kKS = 1;           // sub-chunks per LDS stage
 constexpr int kBK = kSub * kKS;  // reduction per LDS stage
+// The K = (ci, kh, kw) side of grad_input (rows) and grad_weight (columns) is
+// tiled by 64 when ci * k * k <= 64 (the 3-channel stem: 48), by 128 otherwise.
+constexpr int kNarrowK = 64;
 // A workgroup computes a TM x TN tile of the result (TM, TN in {64, 128}).
 // LDS rows of an operand tile of width T have a pitch of T + 4 floats (4 mod
 // 64 banks).  At MFMA step s the two half-waves read k rows s and s + 8 of a
@@ -74,10 +77,10 @@ struct Sub {
     static constexpr int LDA = pitch(TM), LDB = pitch(TN);
     // 64-wide tiles: the output channels of the forward (TM), and the K =
     // (ci, kh, kw) side of grad_input (TM) and grad_weight (TN)
-    static_assert((MODE == FWD && TN == 128) || (MODE == BWI && TN == 128) || (MODE == BWW && TM == 128),
+    static_assert((MODE == FWD && TN == 128) || (MODE == BWI && TN == 128) || (MODE == BWW && TM >= 128),
                   "tile shape");
-    float ra[8];
-    float rb[8];
+    float ra[TM / 16];       // kSub x TM operand values over 256 threads
+    float rb[TN / 16];
 
     // k0: reduction offset.  FWD: K; BWI: co; BWW: pixel of image img.
     __device__ void load(const PArgs& a, int img, int m0, int n0, int k0, bool ok_k)
@@ -139,7 +142,7 @@ struct Sub {
         } else {
             // A[m][q] = G[img][m0 + m][k0 + q]: per row 16 contiguous floats (pixels)
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
+            for (int r = 0; r < TM / 64; ++r) {
                 const int idx = t + kNT * r;
                 const int m = idx / 4, q4 = (idx % 4) * 4;
                 const bool ok = ok_k && m0 + m < a.Co;
@@ -201,7 +204,7 @@ struct Sub {
             }
         } else {
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
+            for (int r = 0; r < TM / 64; ++r) {
                 const int idx = t + kNT * r;
                 const int m = idx / 4, q4 = (idx % 4) * 4;
 #pragma unroll
@@ -433,12 +436,29 @@ PArgs make_args(const Geom& g)
 constexpr int kSlabsPerGroup = 16;   // first-stage group size of the split sum
 constexpr int kOneStageMax = 32;     // at most this many splits are summed in one stage
 
-int wgrad_splits(const PArgs& a, int tiles)
+// grad_weight's tiling: the K side is 64 wide for ci * k * k <= 64; the
+// output-channel side is 256 (waves of 128 x 64, two workgroups per CU) when
+// there are at least 256 channels, else 128.  The pixel reduction is split so
+// that there are about two (256-row tiles) or four (128-row tiles) workgroups
+// per CU.
+struct WgradPlan {
+    int tm, tn, tiles_m, tiles_n, splits;
+};
+
+WgradPlan wgrad_plan(const PArgs& a)
 {
+    WgradPlan p;
+    p.tn = a.Kt <= kNarrowK ? kNarrowK : 128;
+    p.tm = (p.tn == 128 && a.Co >= 256) ? 256 : 128;
+    p.tiles_m = (a.Co + p.tm - 1) / p.tm;
+    p.tiles_n = (a.Kt + p.tn - 1) / p.tn;
+    const int target = p.tm == 256 ? 512 : 1024;
+    const int tiles = p.tiles_m * p.tiles_n;
     const int chunks = a.N * (a.P / kSub);
-    int s = (1024 + tiles - 1) / tiles;
+    int s = (target + tiles - 1) / tiles;
     if (s > chunks) s = chunks;
-    return s < 1 ? 1 : s;
+    p.splits = s < 1 ? 1 : s;
+    return p;
 }
 
 int split_groups(int splits) { return splits > kOneStageMax ? (splits + kSlabsPerGroup - 1) / kSlabsPerGroup : 0; }
@@ -451,9 +471,6 @@ hipError_t launch(const PArgs& a, int s, int grid, hipStream_t st)
     return hipGetLastError();
 }
 
-// The K = (ci, kh, kw) side of grad_input (rows) and grad_weight (columns) is
-// tiled by 64 when ci * k * k <= 64 (the 3-channel stem: 48), by 128 otherwise.
-constexpr int kNarrowK = 64;
 
 // The rows of the forward (output channels) and of grad_input (K) are tiled
 // by 64 instead of 128 when that spreads the work more evenly over the CUs:
@@ -485,9 +502,7 @@ bool patch_supported(const Geom& g)
 size_t patch_wgrad_workspace_bytes(const Geom& g)
 {
     const PArgs a = make_args(g);
-    const int tn = a.Kt <= kNarrowK ? kNarrowK : 128;
-    const int tiles = ((a.Co + 127) / 128) * ((a.Kt + tn - 1) / tn);
-    const int64_t s = wgrad_splits(a, tiles);
+    const int64_t s = wgrad_plan(a).splits;
     const int64_t slab = (int64_t)a.Co * (a.Kt + 1);
     return (size_t)((s + split_groups((int)s)) * slab) * sizeof(float);
 }
@@ -524,16 +539,18 @@ hipError_t launch_patch_bwd_weight(const Geom& g, const float* x, const float* g
 {
     PArgs a = make_args(g);
     a.x = x; a.g = gy;
-    const bool narrow = a.Kt <= kNarrowK;
-    a.tiles_m = (a.Co + 127) / 128;
-    a.tiles_n = narrow ? 1 : (a.Kt + 127) / 128;
+    const WgradPlan plan = wgrad_plan(a);
+    a.tiles_m = plan.tiles_m;
+    a.tiles_n = plan.tiles_n;
     a.chunks = a.N * (a.P / kSub);
-    a.splits = wgrad_splits(a, a.tiles_m * a.tiles_n);
+    a.splits = plan.splits;
     a.with_bias = gb != nullptr;
     float* slabs = static_cast<float*>(ws);
     a.out = slabs;
     const int grid = a.tiles_m * a.tiles_n * a.splits;
-    hipError_t e = narrow ? launch<BWW, 128, kNarrowK>(a, g.k, grid, st) : launch<BWW, 128, 128>(a, g.k, grid, st);
+    hipError_t e = plan.tn == kNarrowK ? launch<BWW, 128, kNarrowK>(a, g.k, grid, st)
+                   : plan.tm == 256    ? launch<BWW, 256, 128>(a, g.k, grid, st)
+                                       : launch<BWW, 128, 128>(a, g.k, grid, st);
     if (e != hipSuccess) return e;
 
     // slab sums: count4 float4 per slab (Co * Kt weights, then Co biases)
