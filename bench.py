@@ -6,7 +6,10 @@ of a layer: halo_gather(X) -> conv_fwd -> halo_gather(G) -> conv_bwd
 (grad_input and the grad_weight / grad_bias partials in one call) ->
 partial_reduce (grad_weight and grad_bias of the four shards, one call over a
 contiguous [gW | gB] buffer).  The separate conv_bwd_input and
-conv_bwd_weight_partial calls are timed on their own as well ("ops_us").  Inputs are seeded
+conv_bwd_weight_partial calls are timed on their own as well ("ops_us"), and so
+is the layer as an interior/edge split ("split": each interior and edge call,
+the split step on one stream, and with the halo gathers on a second stream
+beside the interior calls; not part of `value`).  Inputs are seeded
 synthetic tensors already resident in HBM; each step uses the next of several
 independent buffer sets so that the 256 MB last-level cache cannot hand one
 step's data to the next.
@@ -277,6 +280,8 @@ def main():
         torch.cuda.synchronize()
         op_us[name] = 1e3 * a0.elapsed_time(a1) / args.op_reps
 
+    split = split_bench(args, c, sets, ops, wt, b, ws, op_us)
+
     # Algorithmic work.
     f4 = 4
     n, ci, h, wl_ = c.n, c.c_in, c.h, c.w_local
@@ -344,6 +349,7 @@ def main():
         "roofline": roof,
         "ops_us": {k: round(v, 2) for k, v in op_us.items()},
         "step_spread": spread,
+        "split": split,
         "wall_s_timed": round(wall, 4),
         "gpu_clocks": gpu_clocks(),
         "source_hash": kernel_source_hash(),
@@ -352,6 +358,77 @@ def main():
         out["cpu_baseline"] = cpu_baseline(wl, T, L, S, s)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def split_bench(args, c, sets, ops, wt, b, ws, op_us):
+    """The layer as an interior/edge split (kwkr.cn retelling, section 5.2):
+    each split call timed on its own; the split step with every call on one
+    stream; and the split step with the two halo gathers on a second stream,
+    running beside the interior calls, which is what a multi-GPU run does
+    with its halo exchange.  compute_cost is (interior + edge calls) over the
+    monolithic conv_fwd + conv_bwd, minus one."""
+    import torch
+    from spatially_sharded_cnn_amd import sscnn
+
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    sops = {
+        "conv_fwd_interior": lambda st: sscnn.conv_fwd_interior(c, st["x"], wt, b, st["y"]),
+        "conv_fwd_edge": lambda st: sscnn.conv_fwd_edge(c, st["xh"], wt, st["y"]),
+        "conv_bwd_interior": lambda st: sscnn.conv_bwd_interior(c, st["x"], st["g"], wt, st["dx"], st["gw"],
+                                                                st["gb"], ws),
+        "conv_bwd_input_edge": lambda st: sscnn.conv_bwd_input_edge(c, st["gh"], wt, st["dx"]),
+        "conv_bwd_weight_edge": lambda st: sscnn.conv_bwd_weight_edge(c, st["xh"], st["g"], st["gw"]),
+    }
+
+    def serial(st):
+        ops["halo_gather_x"](st)
+        sops["conv_fwd_interior"](st)
+        sops["conv_fwd_edge"](st)
+        ops["halo_gather_g"](st)
+        sops["conv_bwd_interior"](st)
+        sops["conv_bwd_input_edge"](st)
+        sops["conv_bwd_weight_edge"](st)
+        ops["partial_reduce"](st)
+
+    def overlapped(st):
+        start = torch.cuda.Event()
+        start.record(main)
+        side.wait_event(start)
+        with torch.cuda.stream(side):
+            ops["halo_gather_x"](st)
+            x_ready = torch.cuda.Event()
+            x_ready.record(side)
+            ops["halo_gather_g"](st)
+            g_ready = torch.cuda.Event()
+            g_ready.record(side)
+        sops["conv_fwd_interior"](st)
+        main.wait_event(x_ready)
+        sops["conv_fwd_edge"](st)
+        sops["conv_bwd_interior"](st)
+        main.wait_event(g_ready)
+        sops["conv_bwd_input_edge"](st)
+        sops["conv_bwd_weight_edge"](st)
+        ops["partial_reduce"](st)
+
+    def timed(step, reps):
+        for i in range(args.warmup):
+            step(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for i in range(reps):
+            step(sets[i % len(sets)])
+        a1.record()
+        torch.cuda.synchronize()
+        return 1e3 * a0.elapsed_time(a1) / reps
+
+    sus = {name: round(timed(f, args.op_reps), 2) for name, f in sops.items()}
+    split_us = sum(sus.values())
+    mono_us = op_us["conv_fwd"] + op_us["conv_bwd"]
+    return {"ops_us": sus,
+            "step_us_serial": round(timed(serial, args.steps), 2),
+            "step_us_overlapped": round(timed(overlapped, args.steps), 2),
+            "compute_cost": round(split_us / mono_us - 1.0, 4)}
 
 
 def _layer_work(c, L):

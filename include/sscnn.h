@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSCNN_ABI_VERSION 2
+#define SSCNN_ABI_VERSION 3
 
 /* Status codes. */
 #define SSCNN_OK 0
@@ -204,6 +204,69 @@ int sscnn_conv_bwd(const sscnn_conv_t *conv, const float *x, const float *x_halo
                    const float *grad_y, const float *grad_y_halo, const float *weight,
                    float *grad_x, float *grad_w_part, float *grad_b_part,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Split convolution: interior and edge halves (kwkr.cn retelling, section
+ * 5.2: the computation that does not depend on the halo overlaps its
+ * exchange).  The halo is needed only by the few output columns next to the
+ * shard's edges, so a layer can be computed in two steps ordered on the
+ * caller's streams:
+ *
+ *   1. an INTERIOR call, which needs no halo and may run while the halo is
+ *      being exchanged: the matching monolithic call with every halo column
+ *      read as zero.  Columns away from the edges are then final; the edge
+ *      columns lack the terms that involve halo columns;
+ *   2. after the exchange, an EDGE call, which ADDS exactly those terms in
+ *      place.
+ *
+ * interior + edge equals the monolithic call up to float32 rounding (the edge
+ * sums are added once, to the interior results), and is bitwise reproducible.
+ * For layers whose halo has zero width (k == stride, pad 0) the edge calls
+ * launch nothing and the interior calls are the monolithic ones.  Arguments,
+ * shapes and workspace rules are those of the monolithic calls above; the
+ * edge calls' outputs must hold the interior results (they are read and
+ * updated, so they must not alias an input).
+ */
+
+/* sscnn_conv_fwd with x_halo read as zeros. */
+int sscnn_conv_fwd_interior(const sscnn_conv_t *conv, const float *x, const float *weight,
+                            const float *bias, float *y, void *stream);
+
+/* y += the forward's terms that read x_halo (n, c_in, h, halo_l + halo_r).
+ * Touches only the output columns [0, ceil(halo_l/stride)) and those whose
+ * last tap reaches the right halo.  x_halo may be NULL when both widths are 0. */
+int sscnn_conv_fwd_edge(const sscnn_conv_t *conv, const float *x_halo, const float *weight,
+                        float *y, void *stream);
+
+/* sscnn_conv_bwd_input with grad_y_halo read as zeros. */
+int sscnn_conv_bwd_input_interior(const sscnn_conv_t *conv, const float *grad_y,
+                                  const float *weight, float *grad_x, void *stream);
+
+/* grad_x += grad_input's terms that read grad_y_halo (n, c_out, h_out,
+ * ghalo_l + ghalo_r): at most k - 1 - pad columns on the left and pad on the
+ * right.  grad_y_halo may be NULL when both widths are 0. */
+int sscnn_conv_bwd_input_edge(const sscnn_conv_t *conv, const float *grad_y_halo,
+                              const float *weight, float *grad_x, void *stream);
+
+/* sscnn_conv_bwd_weight_partial with x_halo read as zeros (grad_b_part is
+ * already complete: the bias gradient needs no halo). */
+int sscnn_conv_bwd_weight_partial_interior(const sscnn_conv_t *conv, const float *x,
+                                           const float *grad_y, float *grad_w_part,
+                                           float *grad_b_part, void *workspace,
+                                           size_t workspace_bytes, void *stream);
+
+/* grad_w_part += the products, over this shard's own output columns, of
+ * grad_y with the x_halo columns their taps read.  x_halo may be NULL when both
+ * widths are 0. */
+int sscnn_conv_bwd_weight_edge(const sscnn_conv_t *conv, const float *x_halo,
+                               const float *grad_y, float *grad_w_part, void *stream);
+
+/* sscnn_conv_bwd with both halos read as zeros; finish it with
+ * sscnn_conv_bwd_input_edge and sscnn_conv_bwd_weight_edge. */
+int sscnn_conv_bwd_interior(const sscnn_conv_t *conv, const float *x, const float *grad_y,
+                            const float *weight, float *grad_x, float *grad_w_part,
+                            float *grad_b_part, void *workspace, size_t workspace_bytes,
+                            void *stream);
 
 /*
  * Reduction of partial gradients into the replicated gradient (blog, DTensor

@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "edge.h"
 #include "internal.h"
 #include "kernels.h"
 
@@ -82,6 +83,20 @@ int check(const sscnn_conv_t* conv, Geom* g)
     g->stride = d.stride; g->pad = d.pad; g->groups = d.groups; g->ho = d.h_out;
     g->wol = d.w_out_local; g->hl = d.halo_l; g->hr = d.halo_r; g->ghl = d.ghalo_l;
     g->ghr = d.ghalo_r; g->cig = d.c_in / d.groups; g->cog = d.c_out / d.groups;
+    return SSCNN_OK;
+}
+
+// The workspace check shared by the grad_weight calls.
+int need_workspace(const Geom& g, void* workspace, size_t workspace_bytes, size_t* ws_need)
+{
+    *ws_need = kernels_bwd_weight_workspace_bytes(g);
+    if (*ws_need) {
+        if (!workspace || workspace_bytes < *ws_need)
+            return fail(SSCNN_EWORKSPACE, "workspace of %zu bytes given, %zu needed",
+                        workspace ? workspace_bytes : (size_t)0, *ws_need);
+        if (reinterpret_cast<uintptr_t>(workspace) & 15u)
+            return fail(SSCNN_EINVAL, "workspace is not 16-byte aligned");
+    }
     return SSCNN_OK;
 }
 
@@ -210,13 +225,8 @@ int sscnn_conv_bwd_weight_partial(const sscnn_conv_t* conv, const float* x, cons
     TRY(need(grad_y, "grad_y"));
     TRY(need(grad_w_part, "grad_w_part"));
     TRY(optional(grad_b_part, "grad_b_part"));
-    const size_t ws_need = kernels_bwd_weight_workspace_bytes(g);
-    if (ws_need) {
-        if (!workspace || workspace_bytes < ws_need)
-            return fail(SSCNN_EWORKSPACE, "workspace of %zu bytes given, %zu needed",
-                        workspace ? workspace_bytes : (size_t)0, ws_need);
-        TRY(need(workspace, "workspace"));
-    }
+    size_t ws_need;
+    TRY(need_workspace(g, workspace, workspace_bytes, &ws_need));
     return hip_status(kernels_conv_bwd_weight(g, x, x_halo, grad_y, grad_w_part, grad_b_part,
                                               ws_need ? workspace : nullptr, (hipStream_t)stream),
                       "conv_bwd_weight_partial launch");
@@ -238,13 +248,8 @@ int sscnn_conv_bwd(const sscnn_conv_t* conv, const float* x, const float* x_halo
     TRY(optional(grad_b_part, "grad_b_part"));
     if (grad_x == x || grad_x == x_halo || grad_x == grad_y || grad_x == grad_y_halo)
         return fail(SSCNN_EINVAL, "grad_x aliases an input");
-    const size_t ws_need = kernels_bwd_weight_workspace_bytes(g);
-    if (ws_need) {
-        if (!workspace || workspace_bytes < ws_need)
-            return fail(SSCNN_EWORKSPACE, "workspace of %zu bytes given, %zu needed",
-                        workspace ? workspace_bytes : (size_t)0, ws_need);
-        TRY(need(workspace, "workspace"));
-    }
+    size_t ws_need;
+    TRY(need_workspace(g, workspace, workspace_bytes, &ws_need));
     return hip_status(kernels_conv_bwd(g, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_part,
                                        grad_b_part, ws_need ? workspace : nullptr, (hipStream_t)stream),
                       "conv_bwd launch");
@@ -264,6 +269,121 @@ int sscnn_partial_reduce(const float* const* parts, int32_t nparts, int64_t coun
     }
     return hip_status(launch_partial_reduce(parts, nparts, count, out, (hipStream_t)stream),
                       "partial_reduce launch");
+}
+
+// --- split convolution: interior calls (halo read as zeros) and edge calls ---
+
+int sscnn_conv_fwd_interior(const sscnn_conv_t* conv, const float* x, const float* weight,
+                            const float* bias, float* y, void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    TRY(need(x, "x"));
+    TRY(need(weight, "weight"));
+    TRY(optional(bias, "bias"));
+    TRY(need(y, "y"));
+    return hip_status(kernels_conv_fwd(g, x, nullptr, weight, bias, y, (hipStream_t)stream),
+                      "conv_fwd_interior launch");
+}
+
+int sscnn_conv_fwd_edge(const sscnn_conv_t* conv, const float* x_halo, const float* weight, float* y,
+                        void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    if (g.hl + g.hr == 0) {
+        TRY(optional(x_halo, "x_halo"));
+        return SSCNN_OK;
+    }
+    TRY(need(x_halo, "x_halo"));
+    TRY(need(weight, "weight"));
+    TRY(need(y, "y"));
+    if (y == x_halo) return fail(SSCNN_EINVAL, "y aliases x_halo");
+    return hip_status(launch_edge_fwd(g, x_halo, weight, y, (hipStream_t)stream), "conv_fwd_edge launch");
+}
+
+int sscnn_conv_bwd_input_interior(const sscnn_conv_t* conv, const float* grad_y, const float* weight,
+                                  float* grad_x, void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    TRY(need(grad_y, "grad_y"));
+    TRY(need(weight, "weight"));
+    TRY(need(grad_x, "grad_x"));
+    return hip_status(kernels_conv_bwd_input(g, grad_y, nullptr, weight, grad_x, (hipStream_t)stream),
+                      "conv_bwd_input_interior launch");
+}
+
+int sscnn_conv_bwd_input_edge(const sscnn_conv_t* conv, const float* grad_y_halo, const float* weight,
+                              float* grad_x, void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    if (g.ghl + g.ghr == 0) {
+        TRY(optional(grad_y_halo, "grad_y_halo"));
+        return SSCNN_OK;
+    }
+    TRY(need(grad_y_halo, "grad_y_halo"));
+    TRY(need(weight, "weight"));
+    TRY(need(grad_x, "grad_x"));
+    if (grad_x == grad_y_halo) return fail(SSCNN_EINVAL, "grad_x aliases grad_y_halo");
+    return hip_status(launch_edge_bwd_input(g, grad_y_halo, weight, grad_x, (hipStream_t)stream),
+                      "conv_bwd_input_edge launch");
+}
+
+int sscnn_conv_bwd_weight_partial_interior(const sscnn_conv_t* conv, const float* x, const float* grad_y,
+                                           float* grad_w_part, float* grad_b_part, void* workspace,
+                                           size_t workspace_bytes, void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    TRY(need(x, "x"));
+    TRY(need(grad_y, "grad_y"));
+    TRY(need(grad_w_part, "grad_w_part"));
+    TRY(optional(grad_b_part, "grad_b_part"));
+    size_t ws_need;
+    TRY(need_workspace(g, workspace, workspace_bytes, &ws_need));
+    return hip_status(kernels_conv_bwd_weight(g, x, nullptr, grad_y, grad_w_part, grad_b_part,
+                                              ws_need ? workspace : nullptr, (hipStream_t)stream),
+                      "conv_bwd_weight_partial_interior launch");
+}
+
+int sscnn_conv_bwd_weight_edge(const sscnn_conv_t* conv, const float* x_halo, const float* grad_y,
+                               float* grad_w_part, void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    if (g.hl + g.hr == 0) {
+        TRY(optional(x_halo, "x_halo"));
+        return SSCNN_OK;
+    }
+    TRY(need(x_halo, "x_halo"));
+    TRY(need(grad_y, "grad_y"));
+    TRY(need(grad_w_part, "grad_w_part"));
+    if (grad_w_part == x_halo || grad_w_part == grad_y)
+        return fail(SSCNN_EINVAL, "grad_w_part aliases an input");
+    return hip_status(launch_edge_bwd_weight(g, x_halo, grad_y, grad_w_part, (hipStream_t)stream),
+                      "conv_bwd_weight_edge launch");
+}
+
+int sscnn_conv_bwd_interior(const sscnn_conv_t* conv, const float* x, const float* grad_y,
+                            const float* weight, float* grad_x, float* grad_w_part, float* grad_b_part,
+                            void* workspace, size_t workspace_bytes, void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    TRY(need(x, "x"));
+    TRY(need(grad_y, "grad_y"));
+    TRY(need(weight, "weight"));
+    TRY(need(grad_x, "grad_x"));
+    TRY(need(grad_w_part, "grad_w_part"));
+    TRY(optional(grad_b_part, "grad_b_part"));
+    if (grad_x == x || grad_x == grad_y) return fail(SSCNN_EINVAL, "grad_x aliases an input");
+    size_t ws_need;
+    TRY(need_workspace(g, workspace, workspace_bytes, &ws_need));
+    return hip_status(kernels_conv_bwd(g, x, nullptr, grad_y, nullptr, weight, grad_x, grad_w_part,
+                                       grad_b_part, ws_need ? workspace : nullptr, (hipStream_t)stream),
+                      "conv_bwd_interior launch");
 }
 
 }  // extern "C"

@@ -46,9 +46,9 @@ namespace {
 
 struct DwArgs {
     const float* src;    // (N*C, H, W) tile source: the input (forward), grad_output (grad_input)
-    const float* src_h;  // (N*C, H, 2P) its halo
+    const float* src_h;  // (N*C, H, 2P) its halo, or null (kernels instantiated without halo)
     const float* x;      // (N*C, H, W) input, for grad_weight
-    const float* x_h;    // (N*C, H, 2P) its halo
+    const float* x_h;    // (N*C, H, 2P) its halo, or null (kernels instantiated without halo)
     const float* g;      // (N*C, H, W) grad_output, for the stand-alone grad_weight kernel
     const float* w;      // (C, k, k)
     const float* b;      // (C) or null
@@ -185,6 +185,9 @@ struct Tile {
     }
 
     // Side columns: ordinary loads into registers, written by put_side().
+    // Without a halo (HALO false: the interior half of a split convolution)
+    // the columns beyond the slice are zeros.
+    template <bool HALO>
     __device__ static void load_side(Side& S, const float* __restrict__ xp, const float* __restrict__ hp,
                                      int H, int W, int i0, int j0, int tid)
     {
@@ -196,9 +199,13 @@ struct Tile {
             const int xcol = j0 + (e < P ? e : TW + e) - P;     // shard column, may be < 0 or >= W
             S.s[k] = 0.f;
             if (idx < LH * 2 * P && r >= 0 && r < H) {
-                if (xcol < 0) S.s[k] = hp[(int64_t)r * (2 * P) + (xcol + P)];
-                else if (xcol >= W) S.s[k] = hp[(int64_t)r * (2 * P) + P + (xcol - W)];
-                else S.s[k] = xp[(int64_t)r * W + xcol];
+                if (xcol < 0) {
+                    if constexpr (HALO) S.s[k] = hp[(int64_t)r * (2 * P) + (xcol + P)];
+                } else if (xcol >= W) {
+                    if constexpr (HALO) S.s[k] = hp[(int64_t)r * (2 * P) + P + (xcol - W)];
+                } else {
+                    S.s[k] = xp[(int64_t)r * W + xcol];
+                }
             }
         }
     }
@@ -366,7 +373,7 @@ __device__ __forceinline__ void store_rows(float* out, const TileIdx& d, int H, 
             make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
 }
 
-template <int K, int TX, int TY, int RH, bool FLIP>
+template <int K, int TX, int TY, int RH, bool FLIP, bool HALO>
 __global__ void __launch_bounds__(TX * TY)
 dw_conv_kernel(DwArgs a)
 {
@@ -380,7 +387,7 @@ dw_conv_kernel(DwArgs a)
     auto issue = [&](int t, float* b) {
         const TileIdx e = decode_plane_major(a, t, T::TH, T::TW);
         T::load_main(b, a.src + e.plane * HW, a.H, a.W, e.i0, e.j0, tid);
-        T::load_side(S, a.src + e.plane * HW, a.src_h + (int64_t)e.plane * a.H * (2 * P), a.H, a.W, e.i0,
+        T::template load_side<HALO>(S, a.src + e.plane * HW, HALO ? a.src_h + (int64_t)e.plane * a.H * (2 * P) : nullptr, a.H, a.W, e.i0,
                      e.j0, tid);
     };
     int t = blockIdx.x;
@@ -516,7 +523,7 @@ __device__ __forceinline__ void flush_sum(float (*red)[NV + 2], int gtid, float*
 
 // grad_weight partial (stand-alone): the input tile comes through LDS, the
 // thread's grad_output block straight from global memory.
-template <int K, int TX, int TY, int RH>
+template <int K, int TX, int TY, int RH, bool HALO>
 __global__ void __launch_bounds__(TX * TY) __attribute__((amdgpu_waves_per_eu(3)))
 dw_wgrad_kernel(DwArgs a)
 {
@@ -540,7 +547,7 @@ dw_wgrad_kernel(DwArgs a)
     auto issue = [&](int t, float* b) {
         const TileIdx e = decode_channel_major(a, t, T::TH, T::TW);
         T::load_main(b, a.x + e.plane * HW, a.H, a.W, e.i0, e.j0, tid);
-        T::load_side(S, a.x + e.plane * HW, a.x_h + (int64_t)e.plane * a.H * (2 * P), a.H, a.W, e.i0, e.j0,
+        T::template load_side<HALO>(S, a.x + e.plane * HW, HALO ? a.x_h + (int64_t)e.plane * a.H * (2 * P) : nullptr, a.H, a.W, e.i0, e.j0,
                      tid);
         const float* gp = a.g + e.plane * HW + e.j0 + 4 * tx;
 #pragma unroll
@@ -585,7 +592,7 @@ dw_wgrad_kernel(DwArgs a)
 // grad_output tile's centre.  Both halves walk the same tiles with the same
 // barriers in the same order (two loops with identical barrier sequences, so
 // each half's registers are allocated on their own).
-template <int K, int TX, int TY, int RH>
+template <int K, int TX, int TY, int RH, bool HALO>
 __global__ void __launch_bounds__(2 * TX * TY) __attribute__((amdgpu_waves_per_eu(4)))
 dw_bwd_kernel(DwArgs a)
 {
@@ -613,7 +620,7 @@ dw_bwd_kernel(DwArgs a)
     auto issue = [&](int t, float* b) {
         const TileIdx e = decode_channel_major(a, t, T::TH, T::TW);
         T::load_main(b, src + e.plane * HW, a.H, a.W, e.i0, e.j0, tid);
-        T::load_side(S, src + e.plane * HW, src_h + (int64_t)e.plane * a.H * (2 * P), a.H, a.W, e.i0, e.j0,
+        T::template load_side<HALO>(S, src + e.plane * HW, HALO ? src_h + (int64_t)e.plane * a.H * (2 * P) : nullptr, a.H, a.W, e.i0, e.j0,
                      tid);
     };
     issue(beg, mybuf[0]);
@@ -772,12 +779,12 @@ hipError_t launch_reduce(const DwArgs& a, int grid, float* gw, float* gb, hipStr
 #define SSCNN_DW_BWD_SHAPES(X) X(16, 16, 2) X(16, 16, 1) X(8, 32, 2) X(8, 32, 1) X(8, 16, 1) X(4, 64, 1) \
     X(4, 16, 1)
 
-template <int K, bool FLIP>
+template <int K, bool FLIP, bool HALO>
 hipError_t launch_conv(DwArgs a, int planes, DwShape sh, hipStream_t st)
 {
 #define SSCNN_DW_CONV(TX, TY, RH)                                                  \
     if (sh.tx == TX && sh.ty == TY && sh.rh == RH) {                               \
-        auto kern = dw_conv_kernel<K, TX, TY, RH, FLIP>;                           \
+        auto kern = dw_conv_kernel<K, TX, TY, RH, FLIP, HALO>;                     \
         set_tiles(a, planes, TX, TY, RH);                                          \
         const int grid = persistent_grid(kern, TX * TY, a.ntiles);                 \
         hipLaunchKernelGGL(kern, dim3(grid), dim3(TX * TY), 0, st, a);             \
@@ -788,12 +795,12 @@ hipError_t launch_conv(DwArgs a, int planes, DwShape sh, hipStream_t st)
     return hipErrorInvalidValue;
 }
 
-template <int K>
+template <int K, bool HALO>
 hipError_t launch_wgrad(DwArgs a, int planes, DwShape sh, float* gw, float* gb, hipStream_t st)
 {
 #define SSCNN_DW_WGRAD(TX, TY, RH)                                                 \
     if (sh.tx == TX && sh.ty == TY && sh.rh == RH) {                               \
-        auto kern = dw_wgrad_kernel<K, TX, TY, RH>;                                \
+        auto kern = dw_wgrad_kernel<K, TX, TY, RH, HALO>;                          \
         set_tiles(a, planes, TX, TY, RH);                                          \
         const int grid = persistent_grid(kern, TX * TY, a.ntiles);                 \
         hipLaunchKernelGGL(kern, dim3(grid), dim3(TX * TY), 0, st, a);             \
@@ -805,12 +812,12 @@ hipError_t launch_wgrad(DwArgs a, int planes, DwShape sh, float* gw, float* gb, 
     return hipErrorInvalidValue;
 }
 
-template <int K>
+template <int K, bool HALO>
 hipError_t launch_bwd(DwArgs a, int planes, DwShape sh, float* gw, float* gb, hipStream_t st)
 {
 #define SSCNN_DW_BWD(TX, TY, RH)                                                   \
     if (sh.tx == TX && sh.ty == TY && sh.rh == RH) {                               \
-        auto kern = dw_bwd_kernel<K, TX, TY, RH>;                                  \
+        auto kern = dw_bwd_kernel<K, TX, TY, RH, HALO>;                            \
         set_tiles(a, planes, TX, TY, RH);                                          \
         const int grid = persistent_grid(kern, 2 * TX * TY, a.ntiles);             \
         hipLaunchKernelGGL(kern, dim3(grid), dim3(2 * TX * TY), 0, st, a);         \
@@ -859,9 +866,9 @@ hipError_t launch_dw_fwd(const Geom& g, const float* x, const float* xh, const f
     const int planes = g.n * g.ci;
     const DwShape sh = pick_shape(g.h, g.wl);
     switch (g.k) {
-        case 3: return launch_conv<3, false>(a, planes, sh, st);
-        case 5: return launch_conv<5, false>(a, planes, sh, st);
-        default: return launch_conv<7, false>(a, planes, sh, st);
+        case 3: return xh ? launch_conv<3, false, true>(a, planes, sh, st) : launch_conv<3, false, false>(a, planes, sh, st);
+        case 5: return xh ? launch_conv<5, false, true>(a, planes, sh, st) : launch_conv<5, false, false>(a, planes, sh, st);
+        default: return xh ? launch_conv<7, false, true>(a, planes, sh, st) : launch_conv<7, false, false>(a, planes, sh, st);
     }
 }
 
@@ -873,9 +880,9 @@ hipError_t launch_dw_bwd_input(const Geom& g, const float* gy, const float* gyh,
     const int planes = g.n * g.ci;
     const DwShape sh = pick_shape(g.h, g.wl);
     switch (g.k) {
-        case 3: return launch_conv<3, true>(a, planes, sh, st);
-        case 5: return launch_conv<5, true>(a, planes, sh, st);
-        default: return launch_conv<7, true>(a, planes, sh, st);
+        case 3: return gyh ? launch_conv<3, true, true>(a, planes, sh, st) : launch_conv<3, true, false>(a, planes, sh, st);
+        case 5: return gyh ? launch_conv<5, true, true>(a, planes, sh, st) : launch_conv<5, true, false>(a, planes, sh, st);
+        default: return gyh ? launch_conv<7, true, true>(a, planes, sh, st) : launch_conv<7, true, false>(a, planes, sh, st);
     }
 }
 
@@ -887,9 +894,9 @@ hipError_t launch_dw_bwd_weight(const Geom& g, const float* x, const float* xh, 
     const int planes = g.n * g.ci;
     const DwShape sh = pick_shape(g.h, g.wl);
     switch (g.k) {
-        case 3: return launch_wgrad<3>(a, planes, sh, gw, gb, st);
-        case 5: return launch_wgrad<5>(a, planes, sh, gw, gb, st);
-        default: return launch_wgrad<7>(a, planes, sh, gw, gb, st);
+        case 3: return xh ? launch_wgrad<3, true>(a, planes, sh, gw, gb, st) : launch_wgrad<3, false>(a, planes, sh, gw, gb, st);
+        case 5: return xh ? launch_wgrad<5, true>(a, planes, sh, gw, gb, st) : launch_wgrad<5, false>(a, planes, sh, gw, gb, st);
+        default: return xh ? launch_wgrad<7, true>(a, planes, sh, gw, gb, st) : launch_wgrad<7, false>(a, planes, sh, gw, gb, st);
     }
 }
 
@@ -900,10 +907,11 @@ hipError_t launch_dw_bwd(const Geom& g, const float* x, const float* xh, const f
     a.src = gy; a.src_h = gyh; a.x = x; a.x_h = xh; a.w = w; a.out = gx; a.ws = static_cast<float*>(ws);
     const int planes = g.n * g.ci;
     const DwShape sh = bwd_shape(g.h, g.wl);
+    if ((xh == nullptr) != (gyh == nullptr)) return hipErrorInvalidValue;   // both halos or neither
     switch (g.k) {
-        case 3: return launch_bwd<3>(a, planes, sh, gw, gb, st);
-        case 5: return launch_bwd<5>(a, planes, sh, gw, gb, st);
-        default: return launch_bwd<7>(a, planes, sh, gw, gb, st);
+        case 3: return xh ? launch_bwd<3, true>(a, planes, sh, gw, gb, st) : launch_bwd<3, false>(a, planes, sh, gw, gb, st);
+        case 5: return xh ? launch_bwd<5, true>(a, planes, sh, gw, gb, st) : launch_bwd<5, false>(a, planes, sh, gw, gb, st);
+        default: return xh ? launch_bwd<7, true>(a, planes, sh, gw, gb, st) : launch_bwd<7, false>(a, planes, sh, gw, gb, st);
     }
 }
 

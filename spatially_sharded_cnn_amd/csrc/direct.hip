@@ -15,13 +15,14 @@
 namespace sscnn {
 namespace {
 
-// Extended-row load: column e of the row (plane, r) of [halo_l | local | halo_r].
+// Extended-row load: column e of the row (plane, r) of [halo_l | local | halo_r];
+// a null halo reads as zeros (the interior half of a split convolution).
 __device__ __forceinline__ float ext_load(const float* __restrict__ loc, const float* __restrict__ halo,
                                           int64_t plane_row, int wl, int hl, int hw, int e)
 {
-    if (e < hl) return halo[plane_row * hw + e];
-    if (e < hl + wl) return loc[plane_row * wl + (e - hl)];
-    return halo[plane_row * hw + (e - wl)];
+    if (e >= hl && e < hl + wl) return loc[plane_row * wl + (e - hl)];
+    if (!halo) return 0.0f;
+    return e < hl ? halo[plane_row * hw + e] : halo[plane_row * hw + (e - wl)];
 }
 
 // y[b, o, i, j] for j < wol (shard-local):  input column of tap kw is global

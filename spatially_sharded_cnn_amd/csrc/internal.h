@@ -45,6 +45,19 @@ __device__ __forceinline__ const __attribute__((address_space(4))) T* as_const(c
     return (const __attribute__((address_space(4))) T*)(p);
 }
 
+// Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8, each XCD with its own L2).  xcd_order maps them to logical indices so
+// that XCD x takes one contiguous range, [x q + min(x, r), ...) of q or q + 1
+// indices (q = G / 8, r = G % 8): workgroups next to each other in logical
+// order -- ones that read the same operand tiles -- share an L2.  A bijection
+// for any G.
+__device__ __forceinline__ int xcd_order(int b, int G)
+{
+    const int x = b % 8, slot = b / 8;
+    const int q = G / 8, r = G % 8;
+    return x * q + (x < r ? x : r) + slot;
+}
+
 // Everything a kernel needs about one shard's layer, passed by value.
 struct Geom {
     int n, ci, co, h, wl, k, stride, pad, groups;

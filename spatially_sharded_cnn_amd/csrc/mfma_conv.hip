@@ -42,7 +42,7 @@ constexpr int kCK = 4;      // reduction channels per chunk
 
 struct MfArgs {
     const float* x;      // GEMM input activation (N, C, H, W): X (forward) or G (grad_input)
-    const float* halo;   // (N, C, H, hl + hr)
+    const float* halo;   // (N, C, H, hl + hr); null with hl = hr = 0 when absent
     const float* w;      // weight (Co, Ci, k, k) as given
     const float* b;      // bias (O) or null
     float* y;            // (N, O, H, W)
@@ -363,7 +363,8 @@ hipError_t launch_mfma_fwd(const Geom& g, const float* x, const float* xh, const
 {
     MfArgs a{};
     a.x = x; a.halo = xh; a.w = w; a.b = b; a.y = y;
-    a.N = g.n; a.C = g.ci; a.O = g.co; a.H = g.h; a.W = g.wl; a.hl = g.hl; a.hr = g.hr;
+    a.N = g.n; a.C = g.ci; a.O = g.co; a.H = g.h; a.W = g.wl;
+    a.hl = xh ? g.hl : 0; a.hr = xh ? g.hr : 0;     // no halo: ext_at() reads zeros beyond the slice
     a.wci = g.ci;
     return launch_k<false>(a, g.k, st);
 }
@@ -373,7 +374,8 @@ hipError_t launch_mfma_bwd_input(const Geom& g, const float* gy, const float* gy
 {
     MfArgs a{};
     a.x = gy; a.halo = gyh; a.w = w; a.b = nullptr; a.y = gx;
-    a.N = g.n; a.C = g.co; a.O = g.ci; a.H = g.ho; a.W = g.wol; a.hl = g.ghl; a.hr = g.ghr;
+    a.N = g.n; a.C = g.co; a.O = g.ci; a.H = g.ho; a.W = g.wol;
+    a.hl = gyh ? g.ghl : 0; a.hr = gyh ? g.ghr : 0;
     a.wci = g.ci;
     return launch_k<true>(a, g.k, st);
 }

@@ -39,7 +39,7 @@ constexpr int kSW = 128;    // pixels of a row per stage
 
 struct WgArgs {
     const float* x;      // (N, Ci, H, W) input slice
-    const float* halo;   // (N, Ci, H, hl + hr)
+    const float* halo;   // (N, Ci, H, hl + hr); null with hl = hr = 0 when absent
     const float* g;      // (N, Co, H, W) grad_output slice
     float* ws;           // [splits][k*k][Co][Ci] partial grad_weight, then [splits][Co] grad_bias
     int N, Ci, Co, H, W, hl, hr;
@@ -314,7 +314,8 @@ hipError_t launch(const Geom& g, const float* x, const float* xh, const float* g
     const Plan p = plan(g);
     WgArgs a{};
     a.x = x; a.halo = xh; a.g = gy; a.ws = ws;
-    a.N = g.n; a.Ci = g.ci; a.Co = g.co; a.H = g.h; a.W = g.wl; a.hl = g.hl; a.hr = g.hr;
+    a.N = g.n; a.Ci = g.ci; a.Co = g.co; a.H = g.h; a.W = g.wl;
+    a.hl = xh ? g.hl : 0; a.hr = xh ? g.hr : 0;     // no halo: xext() reads zeros beyond the slice
     a.tiles_o = p.tiles_o; a.tiles_c = p.tiles_c; a.segs = p.segs; a.rows = p.rows;
     a.splits = p.splits; a.rows_per_split = p.rows_per_split;
     const int64_t grid = (int64_t)p.splits * K * p.tiles_c * p.tiles_o;

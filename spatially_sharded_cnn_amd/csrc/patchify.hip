@@ -68,19 +68,6 @@ struct PArgs {
 
 __device__ __forceinline__ int64_t slab_floats(const PArgs& a) { return (int64_t)a.Co * (a.Kt + 1); }
 
-// Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
-// b % 8, each XCD with its own L2).  This maps them to logical tile indices so
-// that XCD x takes one contiguous range, [x q + min(x, r), ...) of q or q + 1
-// indices (q = G / 8, r = G % 8): tiles next to each other in logical order
-// -- the row tiles of one pixel tile, the tiles of one grad_weight split,
-// which read the same operand tiles -- share an L2.  A bijection for any G.
-__device__ __forceinline__ int xcd_order(int b, int G)
-{
-    const int x = b % 8, slot = b / 8;
-    const int q = G / 8, r = G % 8;
-    return x * q + (x < r ? x : r) + slot;
-}
-
 // Global -> registers for one sub-chunk of kSub reduction rows (8 A values
 // and 8 B values per thread), then registers -> LDS.  Each mode gathers its
 // own operands; a sub-chunk past the end of the reduction (ok_k false) loads

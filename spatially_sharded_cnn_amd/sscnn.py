@@ -24,6 +24,9 @@ EXPORTED = (
     "sscnn_conv_init", "sscnn_halo_gather", "sscnn_conv_fwd", "sscnn_conv_bwd_input",
     "sscnn_conv_bwd_weight_workspace_bytes", "sscnn_conv_bwd_weight_partial", "sscnn_conv_bwd",
     "sscnn_partial_reduce", "sscnn_status_string", "sscnn_last_error", "sscnn_abi_version",
+    "sscnn_conv_fwd_interior", "sscnn_conv_fwd_edge", "sscnn_conv_bwd_input_interior",
+    "sscnn_conv_bwd_input_edge", "sscnn_conv_bwd_weight_partial_interior", "sscnn_conv_bwd_weight_edge",
+    "sscnn_conv_bwd_interior",
 )
 
 
@@ -83,12 +86,22 @@ def lib() -> ctypes.CDLL:
         L.sscnn_conv_bwd_weight_partial.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.sscnn_conv_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.sscnn_partial_reduce.argtypes = [ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int64, _vp, _vp]
+        L.sscnn_conv_fwd_interior.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
+        L.sscnn_conv_fwd_edge.argtypes = [P, _vp, _vp, _vp, _vp]
+        L.sscnn_conv_bwd_input_interior.argtypes = [P, _vp, _vp, _vp, _vp]
+        L.sscnn_conv_bwd_input_edge.argtypes = [P, _vp, _vp, _vp, _vp]
+        L.sscnn_conv_bwd_weight_partial_interior.argtypes = [P, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.sscnn_conv_bwd_weight_edge.argtypes = [P, _vp, _vp, _vp, _vp]
+        L.sscnn_conv_bwd_interior.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.sscnn_status_string.argtypes = [ctypes.c_int]
         L.sscnn_status_string.restype = ctypes.c_char_p
         L.sscnn_last_error.restype = ctypes.c_char_p
         for f in ("sscnn_conv_init", "sscnn_halo_gather", "sscnn_conv_fwd", "sscnn_conv_bwd_input",
                   "sscnn_conv_bwd_weight_partial", "sscnn_conv_bwd", "sscnn_partial_reduce",
-                  "sscnn_abi_version"):
+                  "sscnn_abi_version", "sscnn_conv_fwd_interior", "sscnn_conv_fwd_edge",
+                  "sscnn_conv_bwd_input_interior", "sscnn_conv_bwd_input_edge",
+                  "sscnn_conv_bwd_weight_partial_interior", "sscnn_conv_bwd_weight_edge",
+                  "sscnn_conv_bwd_interior"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -188,16 +201,20 @@ def conv_bwd_weight_workspace_bytes(conv: Conv) -> int:
     return int(lib().sscnn_conv_bwd_weight_workspace_bytes(ctypes.byref(conv)))
 
 
+def _workspace(workspace):
+    if workspace is None:
+        return None, 0
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def conv_bwd_weight_partial(conv: Conv, x, x_halo, grad_y, grad_w_part, grad_b_part,
                             workspace=None, stream=None):
     """workspace: a uint8/float CUDA tensor of at least
     conv_bwd_weight_workspace_bytes(conv) bytes, or None when that is 0."""
     hs = conv.halo_shape(HALO_INPUT)
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        if workspace.device.type != "cuda" or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous GPU tensor")
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _workspace(workspace)
     _check(lib().sscnn_conv_bwd_weight_partial(
         ctypes.byref(conv), _ptr(x, conv.x_shape, "x"), _ptr(x_halo, hs, "x_halo", hs[3] == 0),
         _ptr(grad_y, conv.y_shape, "grad_y"), _ptr(grad_w_part, conv.w_shape, "grad_w_part"),
@@ -210,11 +227,7 @@ def conv_bwd(conv: Conv, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_
     """sscnn_conv_bwd: grad_input and the grad_weight / grad_bias partials in one call
     (workspace as for conv_bwd_weight_partial)."""
     hs, gs = conv.halo_shape(HALO_INPUT), conv.halo_shape(HALO_GRAD_OUTPUT)
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        if workspace.device.type != "cuda" or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous GPU tensor")
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _workspace(workspace)
     _check(lib().sscnn_conv_bwd(
         ctypes.byref(conv), _ptr(x, conv.x_shape, "x"), _ptr(x_halo, hs, "x_halo", hs[3] == 0),
         _ptr(grad_y, conv.y_shape, "grad_y"), _ptr(grad_y_halo, gs, "grad_y_halo", gs[3] == 0),
@@ -222,6 +235,64 @@ def conv_bwd(conv: Conv, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_
         _ptr(grad_w_part, conv.w_shape, "grad_w_part"),
         _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True), ws_ptr, ws_bytes, _stream(stream)),
         "conv_bwd")
+
+
+# --- split convolution (interior: halo read as zeros; edge: adds the halo terms) ---
+
+def conv_fwd_interior(conv: Conv, x, weight, bias, y, stream=None):
+    _check(lib().sscnn_conv_fwd_interior(ctypes.byref(conv), _ptr(x, conv.x_shape, "x"),
+                                         _ptr(weight, conv.w_shape, "weight"),
+                                         _ptr(bias, (conv.c_out,), "bias", True),
+                                         _ptr(y, conv.y_shape, "y"), _stream(stream)), "conv_fwd_interior")
+
+
+def conv_fwd_edge(conv: Conv, x_halo, weight, y, stream=None):
+    hs = conv.halo_shape(HALO_INPUT)
+    _check(lib().sscnn_conv_fwd_edge(ctypes.byref(conv), _ptr(x_halo, hs, "x_halo", hs[3] == 0),
+                                     _ptr(weight, conv.w_shape, "weight", hs[3] == 0),
+                                     _ptr(y, conv.y_shape, "y", hs[3] == 0), _stream(stream)), "conv_fwd_edge")
+
+
+def conv_bwd_input_interior(conv: Conv, grad_y, weight, grad_x, stream=None):
+    _check(lib().sscnn_conv_bwd_input_interior(ctypes.byref(conv), _ptr(grad_y, conv.y_shape, "grad_y"),
+                                               _ptr(weight, conv.w_shape, "weight"),
+                                               _ptr(grad_x, conv.x_shape, "grad_x"), _stream(stream)),
+           "conv_bwd_input_interior")
+
+
+def conv_bwd_input_edge(conv: Conv, grad_y_halo, weight, grad_x, stream=None):
+    gs = conv.halo_shape(HALO_GRAD_OUTPUT)
+    _check(lib().sscnn_conv_bwd_input_edge(ctypes.byref(conv), _ptr(grad_y_halo, gs, "grad_y_halo", gs[3] == 0),
+                                           _ptr(weight, conv.w_shape, "weight", gs[3] == 0),
+                                           _ptr(grad_x, conv.x_shape, "grad_x", gs[3] == 0), _stream(stream)),
+           "conv_bwd_input_edge")
+
+
+def conv_bwd_weight_partial_interior(conv: Conv, x, grad_y, grad_w_part, grad_b_part, workspace=None,
+                                     stream=None):
+    ws_ptr, ws_bytes = _workspace(workspace)
+    _check(lib().sscnn_conv_bwd_weight_partial_interior(
+        ctypes.byref(conv), _ptr(x, conv.x_shape, "x"), _ptr(grad_y, conv.y_shape, "grad_y"),
+        _ptr(grad_w_part, conv.w_shape, "grad_w_part"), _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True),
+        ws_ptr, ws_bytes, _stream(stream)), "conv_bwd_weight_partial_interior")
+
+
+def conv_bwd_weight_edge(conv: Conv, x_halo, grad_y, grad_w_part, stream=None):
+    hs = conv.halo_shape(HALO_INPUT)
+    _check(lib().sscnn_conv_bwd_weight_edge(ctypes.byref(conv), _ptr(x_halo, hs, "x_halo", hs[3] == 0),
+                                            _ptr(grad_y, conv.y_shape, "grad_y", hs[3] == 0),
+                                            _ptr(grad_w_part, conv.w_shape, "grad_w_part", hs[3] == 0),
+                                            _stream(stream)), "conv_bwd_weight_edge")
+
+
+def conv_bwd_interior(conv: Conv, x, grad_y, weight, grad_x, grad_w_part, grad_b_part, workspace=None,
+                      stream=None):
+    ws_ptr, ws_bytes = _workspace(workspace)
+    _check(lib().sscnn_conv_bwd_interior(
+        ctypes.byref(conv), _ptr(x, conv.x_shape, "x"), _ptr(grad_y, conv.y_shape, "grad_y"),
+        _ptr(weight, conv.w_shape, "weight"), _ptr(grad_x, conv.x_shape, "grad_x"),
+        _ptr(grad_w_part, conv.w_shape, "grad_w_part"), _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True),
+        ws_ptr, ws_bytes, _stream(stream)), "conv_bwd_interior")
 
 
 def partial_reduce(parts: Sequence, out, stream=None):

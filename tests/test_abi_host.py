@@ -225,3 +225,41 @@ def test_autograd_shard_round_trip_and_host_tensors_rejected():
     assert layer.weight.shape == (6, 3, 3, 3) and layer.bias.shape == (6,)
     with pytest.raises(ValueError):
         layer(xs)
+
+
+def test_split_calls_validate_before_launching():
+    """The interior / edge halves of a split convolution check their own
+    arguments; an edge call of a layer without halo columns returns OK with
+    nothing to launch."""
+    L = sscnn.lib()
+    c = _conv()
+    r = ctypes.byref(c)
+    F = FAKE
+    # interior calls need no halo, but every other operand
+    assert L.sscnn_conv_fwd_interior(r, None, F, None, F + 4096, None) == sscnn.EINVAL
+    assert L.sscnn_conv_fwd_interior(r, F, None, None, F + 4096, None) == sscnn.EINVAL
+    assert L.sscnn_conv_fwd_interior(r, F, F, F + 4, F + 4096, None) == sscnn.EINVAL       # misaligned bias
+    assert L.sscnn_conv_bwd_input_interior(r, F, F, None, None) == sscnn.EINVAL
+    assert L.sscnn_conv_bwd_weight_partial_interior(r, F, F, None, None, None, 0, None) == sscnn.EINVAL
+    assert L.sscnn_conv_bwd_interior(r, F, F, F, F, F + 4096, None, None, 0, None) == sscnn.EINVAL  # grad_x is x
+    assert "alias" in sscnn.last_error()
+    assert L.sscnn_conv_bwd_interior(r, F, F + 4096, F + 8192, F + 12288, None, None, None, 0, None) == sscnn.EINVAL
+    # edge calls need the halo and refuse outputs that alias it
+    assert L.sscnn_conv_fwd_edge(r, None, F, F + 4096, None) == sscnn.EINVAL
+    assert L.sscnn_conv_fwd_edge(r, F, F + 4096, F, None) == sscnn.EINVAL
+    assert L.sscnn_conv_bwd_input_edge(r, None, F, F + 4096, None) == sscnn.EINVAL
+    assert L.sscnn_conv_bwd_input_edge(r, F, F + 4096, None, None) == sscnn.EINVAL
+    assert L.sscnn_conv_bwd_weight_edge(r, None, F, F + 4096, None) == sscnn.EINVAL
+    assert L.sscnn_conv_bwd_weight_edge(r, F, F + 4096, F, None) == sscnn.EINVAL
+    # a depthwise layer's interior grad_weight still needs its workspace
+    d = sscnn.conv_init(1, 16, 16, 64, 16, 7, 1, 3, 16, 1, 4)
+    assert L.sscnn_conv_bwd_weight_partial_interior(ctypes.byref(d), F, F + 4096, F + 8192, None, None, 0,
+                                                    None) == sscnn.EWORKSPACE
+    assert L.sscnn_conv_bwd_interior(ctypes.byref(d), F, F + 4096, F + 8192, F + 12288, F + 16384, None,
+                                     None, 0, None) == sscnn.EWORKSPACE
+    # patchify: no halo columns, so the edge calls have nothing to add
+    p = sscnn.conv_init(1, 3, 16, 16, 16, 4, 4, 0, 1, 1, 4)
+    rp = ctypes.byref(p)
+    assert L.sscnn_conv_fwd_edge(rp, None, None, None, None) == sscnn.OK
+    assert L.sscnn_conv_bwd_input_edge(rp, None, None, None, None) == sscnn.OK
+    assert L.sscnn_conv_bwd_weight_edge(rp, None, None, None, None) == sscnn.OK
