@@ -71,6 +71,7 @@ def _parse():
     ap.add_argument("--sets", type=int, default=3, help="independent buffer sets rotated per step")
     ap.add_argument("--op-reps", type=int, default=20, help="back-to-back calls per operation timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-split", action="store_true", help="skip the interior/edge split timings")
     ap.add_argument("--summarize", metavar="DIR", nargs="+",
                     help="summarize rocprofv3 output directories and exit")
     ap.add_argument("--traffic-op", help="with --summarize over FETCH_SIZE / WRITE_SIZE runs: the operation "
@@ -280,7 +281,7 @@ def main():
         torch.cuda.synchronize()
         op_us[name] = 1e3 * a0.elapsed_time(a1) / args.op_reps
 
-    split = split_bench(args, c, sets, ops, wt, b, ws, op_us)
+    split = None if args.no_split else split_bench(args, c, sets, ops, wt, b, ws, op_us)
 
     # Algorithmic work.
     f4 = 4
