@@ -29,6 +29,7 @@ v_fmac_f32 with vector-register operands reaches it without packed math)
 for the depthwise ones.
 
     python bench.py [--workload dw7_c256|dense5x5_c256|dense5x5_tiny] [--steps K] [--warmup W]
+    python bench.py --workload dw7_c256_hshard   # the same step on a split along H (row halos)
     python bench.py --workload convnext_xl_w2048|convnext_xl_w4096   # the stack, per layer
     python bench.py --summarize DIR [DIR ...] [--traffic-op OP --traffic-kernels "K1;K2"]
                                       # text summary of rocprofv3 output directories
@@ -66,8 +67,8 @@ def _parse():
     ap.add_argument("--steps", type=int, default=STEPS_DEFAULT)
     ap.add_argument("--warmup", type=int, default=WARMUP_DEFAULT)
     ap.add_argument("--workload", default="dw7_c256",
-                    help="dw7_c256 (default), dense5x5_c256, dense5x5_tiny, or a stack: "
-                         "convnext_xl_w2048, convnext_xl_w4096")
+                    help="dw7_c256 (default), dense5x5_c256, dense5x5_tiny, dw7_c256_hshard (the same "
+                         "depthwise map split along H), or a stack: convnext_xl_w2048, convnext_xl_w4096")
     ap.add_argument("--sets", type=int, default=3, help="independent buffer sets rotated per step")
     ap.add_argument("--op-reps", type=int, default=20, help="back-to-back calls per operation timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -163,12 +164,20 @@ def main():
     L = wl.layers[0]
     S, s = wl.num_shards, wl.shard
     T = workloads.generate(wl)
+    hsplit = wl.axis == 2           # Shard(2): the same step on a split along H (row halos)
+    A = _HOps(sscnn) if hsplit else _WOps(sscnn)
 
     def shard_of(a, i):
+        if hsplit:
+            h = a.shape[2] // S
+            return np.ascontiguousarray(a[:, :, i * h:(i + 1) * h, :])
         w = a.shape[3] // S
         return np.ascontiguousarray(a[:, :, :, i * w:(i + 1) * w])
 
     def conv_of(i):
+        if hsplit:
+            return sscnn.hconv_init(L.in_shape[0], L.ci, L.co, L.in_shape[2] // S, L.in_shape[3], L.k,
+                                    L.stride, L.pad, L.groups, i, S)
         return sscnn.conv_init(L.in_shape[0], L.ci, L.co, L.in_shape[2], L.in_shape[3] // S, L.k,
                                L.stride, L.pad, L.groups, i, S)
 
@@ -202,7 +211,7 @@ def main():
             gbuf=gbuf, gw=gw, gb=gb, red=torch.empty(nw + nb, device=dev),
         )
         sets.append(st)
-    ws = sscnn.new_workspace(c)
+    ws = A.new_workspace(c)
     del xs_h, gs_h
 
     # The other shards' partial gradients (computed once, untimed): the step's
@@ -216,26 +225,26 @@ def main():
         li = dev_of(shard_of(T.x, i - 1)) if i > 0 else None
         ri = dev_of(shard_of(T.x, i + 1)) if i < S - 1 else None
         xhi = torch.empty(ci_.halo_shape(sscnn.HALO_INPUT), device=dev)
-        sscnn.halo_gather(ci_, sscnn.HALO_INPUT, li, ri, xhi)
+        A.halo_gather(ci_, sscnn.HALO_INPUT, li, ri, xhi)
         gbuf, gw, gb = grads()
-        sscnn.conv_bwd_weight_partial(ci_, xi, xhi, gi, gw, gb, sscnn.new_workspace(ci_))
+        A.conv_bwd_weight_partial(ci_, xi, xhi, gi, gw, gb, A.new_workspace(ci_))
         others[i] = gbuf
         del xi, gi, li, ri, xhi
     torch.cuda.synchronize()
 
     ops = {
-        "halo_gather_x": lambda st: sscnn.halo_gather(c, sscnn.HALO_INPUT, st["xl"], st["xr"], st["xh"]),
-        "conv_fwd": lambda st: sscnn.conv_fwd(c, st["x"], st["xh"], wt, b, st["y"]),
-        "halo_gather_g": lambda st: sscnn.halo_gather(c, sscnn.HALO_GRAD_OUTPUT, st["gl"], st["gr"], st["gh"]),
-        "conv_bwd": lambda st: sscnn.conv_bwd(c, st["x"], st["xh"], st["g"], st["gh"], wt, st["dx"],
-                                              st["gw"], st["gb"], ws),
+        "halo_gather_x": lambda st: A.halo_gather(c, sscnn.HALO_INPUT, st["xl"], st["xr"], st["xh"]),
+        "conv_fwd": lambda st: A.conv_fwd(c, st["x"], st["xh"], wt, b, st["y"]),
+        "halo_gather_g": lambda st: A.halo_gather(c, sscnn.HALO_GRAD_OUTPUT, st["gl"], st["gr"], st["gh"]),
+        "conv_bwd": lambda st: A.conv_bwd(c, st["x"], st["xh"], st["g"], st["gh"], wt, st["dx"],
+                                          st["gw"], st["gb"], ws),
         "partial_reduce": lambda st: sscnn.partial_reduce(
             [st["gbuf"] if i == s else others[i] for i in range(S)], st["red"]),
     }
     # the same backward as two calls (timed on their own, not part of the step)
     extra_ops = {
-        "conv_bwd_input": lambda st: sscnn.conv_bwd_input(c, st["g"], st["gh"], wt, st["dx"]),
-        "conv_bwd_weight_partial": lambda st: sscnn.conv_bwd_weight_partial(
+        "conv_bwd_input": lambda st: A.conv_bwd_input(c, st["g"], st["gh"], wt, st["dx"]),
+        "conv_bwd_weight_partial": lambda st: A.conv_bwd_weight_partial(
             c, st["x"], st["xh"], st["g"], st["gw"], st["gb"], ws),
     }
 
@@ -281,14 +290,24 @@ def main():
         torch.cuda.synchronize()
         op_us[name] = 1e3 * a0.elapsed_time(a1) / args.op_reps
 
-    split = None if args.no_split else split_bench(args, c, sets, ops, wt, b, ws, op_us)
+    split = None if (args.no_split or hsplit) else split_bench(args, c, sets, ops, wt, b, ws, op_us)
 
     # Algorithmic work.
     f4 = 4
-    n, ci, h, wl_ = c.n, c.c_in, c.h, c.w_local
-    co, ho, wol = c.c_out, c.h_out, c.w_out_local
-    x_ext = n * ci * h * (wl_ + c.halo_l + c.halo_r) * f4
-    g_ext = n * co * ho * (wol + c.ghalo_l + c.ghalo_r) * f4
+    if hsplit:
+        n, ci, h, wl_ = c.n, c.c_in, c.h_local, c.w
+        co, ho, wol = c.c_out, c.h_out_local, c.w_out
+        x_ext = n * ci * (h + c.halo_u + c.halo_d) * wl_ * f4
+        g_ext = n * co * (ho + c.ghalo_u + c.ghalo_d) * wol * f4
+        halo_x_b = 2 * n * ci * (c.halo_u + c.halo_d) * wl_ * f4
+        halo_g_b = 2 * n * co * (c.ghalo_u + c.ghalo_d) * wol * f4
+    else:
+        n, ci, h, wl_ = c.n, c.c_in, c.h, c.w_local
+        co, ho, wol = c.c_out, c.h_out, c.w_out_local
+        x_ext = n * ci * h * (wl_ + c.halo_l + c.halo_r) * f4
+        g_ext = n * co * ho * (wol + c.ghalo_l + c.ghalo_r) * f4
+        halo_x_b = 2 * n * ci * h * (c.halo_l + c.halo_r) * f4
+        halo_g_b = 2 * n * co * ho * (c.ghalo_l + c.ghalo_r) * f4
     x_b, y_b = n * ci * h * wl_ * f4, n * co * ho * wol * f4
     w_b, b_b = nw * f4, nb * f4
     red_b = (S + 1) * (w_b + b_b)
@@ -298,9 +317,9 @@ def main():
     flops_pass = 2 * (ci // c.groups) * c.k * c.k * n * co * ho * wol
     step_flops = 3 * flops_pass
     op_bytes = {
-        "halo_gather_x": 2 * n * ci * h * (c.halo_l + c.halo_r) * f4,
+        "halo_gather_x": halo_x_b,
         "conv_fwd": x_ext + w_b + b_b + y_b,
-        "halo_gather_g": 2 * n * co * ho * (c.ghalo_l + c.ghalo_r) * f4,
+        "halo_gather_g": halo_g_b,
         "conv_bwd": bytes_bwd,
         "partial_reduce": red_b,
         "conv_bwd_input": g_ext + w_b + x_b,
@@ -340,6 +359,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description, "shard": f"{s} of {S}",
+                   "split_axis": "H" if hsplit else "W",
                    "shard_input": list(c.x_shape), "weight": list(c.w_shape),
                    "buffer_sets": args.sets},
         "tflops": round(step_flops / step_s / 1e12, 2),
@@ -355,10 +375,32 @@ def main():
         "gpu_clocks": gpu_clocks(),
         "source_hash": kernel_source_hash(),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not hsplit:
         out["cpu_baseline"] = cpu_baseline(wl, T, L, S, s)
     print(json.dumps(out), flush=True)
     return 0
+
+
+class _WOps:
+    """The step's calls for a split along W (Shard(3))."""
+    def __init__(self, sscnn):
+        self.halo_gather = sscnn.halo_gather
+        self.conv_fwd = sscnn.conv_fwd
+        self.conv_bwd = sscnn.conv_bwd
+        self.conv_bwd_input = sscnn.conv_bwd_input
+        self.conv_bwd_weight_partial = sscnn.conv_bwd_weight_partial
+        self.new_workspace = sscnn.new_workspace
+
+
+class _HOps:
+    """The same calls for a split along H (Shard(2)): row halos."""
+    def __init__(self, sscnn):
+        self.halo_gather = sscnn.row_halo_gather
+        self.conv_fwd = sscnn.hconv_fwd
+        self.conv_bwd = sscnn.hconv_bwd
+        self.conv_bwd_input = sscnn.hconv_bwd_input
+        self.conv_bwd_weight_partial = sscnn.hconv_bwd_weight_partial
+        self.new_workspace = sscnn.new_hworkspace
 
 
 def split_bench(args, c, sets, ops, wt, b, ws, op_us):

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSCNN_ABI_VERSION 3
+#define SSCNN_ABI_VERSION 4
 
 /* Status codes. */
 #define SSCNN_OK 0
@@ -267,6 +267,88 @@ int sscnn_conv_bwd_interior(const sscnn_conv_t *conv, const float *x, const floa
                             const float *weight, float *grad_x, float *grad_w_part,
                             float *grad_b_part, void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/*
+ * Height sharding (kwkr.cn retelling, section 5.2: for very high input
+ * resolutions the sharded dimension becomes the height, Shard(2)).  The
+ * activation's rows are split into num_shards equal slices of full width;
+ * weight and bias stay replicated; a shard exchanges ROWS with the shards
+ * above and below it: the row halo.  Rows are contiguous in memory, so the
+ * exchange moves whole rows.  Each call convolves the local slice as its own
+ * image (the interior) and then adds the terms that read a row halo; results
+ * equal the unsharded layer's rows [s*h_out_local, (s+1)*h_out_local) up to
+ * float32 rounding, and the grad_weight / grad_bias partials sum, over the
+ * shards, to the full gradients.  Conventions are those of the calls above.
+ */
+typedef struct sscnn_hconv {
+    /* set by the caller */
+    int32_t n;            /* batch */
+    int32_t c_in;         /* input channels */
+    int32_t c_out;        /* output channels */
+    int32_t h_local;      /* input rows held by this shard */
+    int32_t w;            /* input width (not sharded) */
+    int32_t k;            /* kernel size (k x k) */
+    int32_t stride;       /* stride on both axes */
+    int32_t pad;          /* zero padding on both axes of the GLOBAL image */
+    int32_t groups;       /* channel groups */
+    int32_t shard;        /* this shard's index s, 0 <= s < num_shards (top to bottom) */
+    int32_t num_shards;   /* S */
+    /* filled by sscnn_hconv_init */
+    int32_t h_out_local;  /* h_local / stride: output rows owned by this shard */
+    int32_t w_out;        /* w / stride */
+    int32_t halo_u;       /* input rows needed from the shard above: pad */
+    int32_t halo_d;       /* input rows needed from the shard below: max(0, k - stride - pad) */
+    int32_t ghalo_u;      /* grad_output rows needed from above: (k - 1 - pad) / stride */
+    int32_t ghalo_d;      /* grad_output rows needed from below: ceil(pad / stride) */
+} sscnn_hconv_t;
+
+/*
+ * Validate and fill the derived fields.  Requirements as for
+ * sscnn_conv_init with the roles of rows and columns exchanged, plus
+ * (SSCNN_EUNSUPPORTED otherwise) w % stride == 0 and (w + 2*pad - k)/stride
+ * + 1 == w / stride, the output width the kernels produce.
+ */
+int sscnn_hconv_init(sscnn_hconv_t *conv);
+
+/*
+ * Row halo exchange, single-GPU form.  For which == SSCNN_HALO_INPUT the
+ * slices are (n, c_in, h_local, w) and the heights (halo_u, halo_d); for
+ * SSCNN_HALO_GRAD_OUTPUT they are (n, c_out, h_out_local, w_out) and
+ * (ghalo_u, ghalo_d).  Writes halo, shape (n, C, hu + hd, width): per plane,
+ * the LAST hu rows of up_nbr's slice, then the FIRST hd rows of down_nbr's
+ * slice; zeros at the global top and bottom.  up_nbr must be NULL exactly
+ * when shard == 0 and down_nbr exactly when shard == num_shards - 1.  If
+ * hu + hd == 0 nothing is launched and halo may be NULL.
+ */
+int sscnn_row_halo_gather(const sscnn_hconv_t *conv, int32_t which, const float *up_nbr,
+                          const float *down_nbr, float *halo, void *stream);
+
+/* Forward of an H-shard: x (n, c_in, h_local, w), x_halo from
+ * sscnn_row_halo_gather(INPUT) (may be NULL when both heights are 0),
+ * y (n, c_out, h_out_local, w_out). */
+int sscnn_hconv_fwd(const sscnn_hconv_t *conv, const float *x, const float *x_halo,
+                    const float *weight, const float *bias, float *y, void *stream);
+
+/* grad_input of an H-shard: grad_y (n, c_out, h_out_local, w_out),
+ * grad_y_halo from sscnn_row_halo_gather(GRAD_OUTPUT), grad_x (n, c_in, h_local, w). */
+int sscnn_hconv_bwd_input(const sscnn_hconv_t *conv, const float *grad_y,
+                          const float *grad_y_halo, const float *weight, float *grad_x,
+                          void *stream);
+
+/* Workspace bytes for sscnn_hconv_bwd_weight_partial and sscnn_hconv_bwd. */
+size_t sscnn_hconv_bwd_weight_workspace_bytes(const sscnn_hconv_t *conv);
+
+/* _Partial grad_weight / grad_bias of an H-shard: sums over its OWN output rows. */
+int sscnn_hconv_bwd_weight_partial(const sscnn_hconv_t *conv, const float *x,
+                                   const float *x_halo, const float *grad_y,
+                                   float *grad_w_part, float *grad_b_part,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* grad_input and the partials in one call (one pass over grad_output for depthwise layers). */
+int sscnn_hconv_bwd(const sscnn_hconv_t *conv, const float *x, const float *x_halo,
+                    const float *grad_y, const float *grad_y_halo, const float *weight,
+                    float *grad_x, float *grad_w_part, float *grad_b_part,
+                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Reduction of partial gradients into the replicated gradient (blog, DTensor

@@ -20,6 +20,10 @@ What is computed, and where it is defined:
   neighbours' edge columns, zeros beyond the global edge (same blog, Figure 1:
   a 5x5 kernel with padding 2 and stride 1 needs 2 columns from each
   neighbour; kwkr.cn retelling, section 2.2).
+* ``shard_rows`` / ``halo_rows`` / ``conv_bwd_weight_rows`` -- the same for
+  a split along H (kwkr.cn retelling, section 5.2: Shard(2) for very high
+  resolutions): the row slices, the neighbours' edge rows, and the partial
+  gradients summed over a shard's own output rows.
 * ``reduce_partials`` -- the sum that turns _Partial gradients into
   Replicate ones (blog, DTensor section; kwkr.cn retelling, section 2.2).
 * ``stack_forward`` / ``stack_backward`` -- a chain of the above for a
@@ -234,6 +238,42 @@ def halo_columns(t, num_shards: int, shard: int, hl: int, hr: int) -> np.ndarray
         if 0 <= q < w:
             out[:, :, :, hl + e] = t[:, :, :, q]
     return out
+
+
+def shard_rows(t, num_shards: int, shard: int) -> np.ndarray:
+    """Shard(2): the shard-th of num_shards equal slices of t along H (the
+    height split of kwkr.cn retelling, section 5.2)."""
+    h = t.shape[2]
+    assert h % num_shards == 0
+    hl = h // num_shards
+    return t[:, :, shard * hl:(shard + 1) * hl, :]
+
+
+def halo_rows(t, num_shards: int, shard: int, hu: int, hd: int) -> np.ndarray:
+    """The row halo an H-shard receives: rows [s*Hl - hu, s*Hl) then
+    [(s+1)*Hl, (s+1)*Hl + hd) of the global tensor t, zero where they fall
+    outside [0, H).  Returned as (N, C, hu + hd, W)."""
+    n, c, h, w = t.shape
+    hl = h // num_shards
+    out = np.zeros((n, c, hu + hd, w), dtype=t.dtype)
+    for e in range(hu):
+        q = shard * hl - hu + e
+        if 0 <= q < h:
+            out[:, :, e, :] = t[:, :, q, :]
+    for e in range(hd):
+        q = (shard + 1) * hl + e
+        if 0 <= q < h:
+            out[:, :, hu + e, :] = t[:, :, q, :]
+    return out
+
+
+def conv_bwd_weight_rows(x, g, k: int, stride: int, pad: int, groups: int, rows):
+    """grad_weight / grad_bias summed over the output rows [rows[0], rows[1])
+    only: an H-shard's _Partial gradients.  The sum over a subset of the
+    outputs is the gradient with grad_output zero elsewhere."""
+    gm = np.zeros_like(np.asarray(g, dtype=np.float64))
+    gm[:, :, rows[0]:rows[1], :] = np.asarray(g, dtype=np.float64)[:, :, rows[0]:rows[1], :]
+    return conv_bwd_weight(x, gm, k, stride, pad, groups)
 
 
 def reduce_partials(parts) -> np.ndarray:

@@ -8,6 +8,7 @@
 #include "edge.h"
 #include "internal.h"
 #include "kernels.h"
+#include "rowedge.h"
 
 namespace sscnn {
 namespace {
@@ -86,10 +87,71 @@ int check(const sscnn_conv_t* conv, Geom* g)
     return SSCNN_OK;
 }
 
-// The workspace check shared by the grad_weight calls.
-int need_workspace(const Geom& g, void* workspace, size_t workspace_bytes, size_t* ws_need)
+// Height sharding: validate an H-shard descriptor and derive its fields.
+int derive_h(const sscnn_hconv_t& c, sscnn_hconv_t* out)
+{
+    if (c.n <= 0 || c.c_in <= 0 || c.c_out <= 0 || c.h_local <= 0 || c.w <= 0 || c.k <= 0 || c.stride <= 0 ||
+        c.groups <= 0 || c.num_shards <= 0)
+        return fail(SSCNN_EINVAL, "sizes must be positive (n=%d c_in=%d c_out=%d h_local=%d w=%d k=%d "
+                    "stride=%d groups=%d num_shards=%d)", c.n, c.c_in, c.c_out, c.h_local, c.w, c.k, c.stride,
+                    c.groups, c.num_shards);
+    if (c.pad < 0 || c.pad >= c.k) return fail(SSCNN_EINVAL, "pad=%d must satisfy 0 <= pad < k=%d", c.pad, c.k);
+    if (c.c_in % c.groups || c.c_out % c.groups)
+        return fail(SSCNN_EINVAL, "groups=%d must divide c_in=%d and c_out=%d", c.groups, c.c_in, c.c_out);
+    if (c.shard < 0 || c.shard >= c.num_shards)
+        return fail(SSCNN_EINVAL, "shard=%d outside [0, %d)", c.shard, c.num_shards);
+    if (c.w + 2 * c.pad < c.k) return fail(SSCNN_EINVAL, "w=%d too small for k=%d pad=%d", c.w, c.k, c.pad);
+    if ((int64_t)c.n * c.c_in * c.h_local * c.w > ((int64_t)1 << 40)) return fail(SSCNN_EINVAL, "tensor too large");
+    if (c.h_local % c.stride || c.w % c.stride)
+        return fail(SSCNN_EUNSUPPORTED, "h_local=%d and w=%d must be multiples of stride=%d", c.h_local, c.w,
+                    c.stride);
+    const int64_t h_global = (int64_t)c.h_local * c.num_shards;
+    if ((h_global + 2 * c.pad - c.k) / c.stride + 1 != h_global / c.stride)
+        return fail(SSCNN_EUNSUPPORTED, "output rows do not split evenly over the shards");
+    if ((c.w + 2 * c.pad - c.k) / c.stride + 1 != c.w / c.stride)
+        return fail(SSCNN_EUNSUPPORTED, "output width %d != w / stride = %d", (c.w + 2 * c.pad - c.k) / c.stride + 1,
+                    c.w / c.stride);
+    sscnn_hconv_t d = c;
+    d.h_out_local = c.h_local / c.stride;
+    d.w_out = c.w / c.stride;
+    d.halo_u = c.pad;
+    d.halo_d = c.k - c.stride - c.pad > 0 ? c.k - c.stride - c.pad : 0;
+    d.ghalo_u = (c.k - 1 - c.pad) / c.stride;
+    d.ghalo_d = (c.pad + c.stride - 1) / c.stride;
+    if (d.halo_u > c.h_local || d.halo_d > c.h_local || d.ghalo_u > d.h_out_local || d.ghalo_d > d.h_out_local)
+        return fail(SSCNN_EUNSUPPORTED, "row halo taller than one slice (halo %d/%d, grad halo %d/%d, h_local %d)",
+                    d.halo_u, d.halo_d, d.ghalo_u, d.ghalo_d, c.h_local);
+    *out = d;
+    return SSCNN_OK;
+}
+
+// The slice as its own image (the interior of an H-shard), for the ordinary
+// kernels; its column halos are never passed (read as zeros: the image's
+// padding).
+int check_h(const sscnn_hconv_t* conv, Geom* g)
+{
+    if (!conv) return fail(SSCNN_EINVAL, "conv is NULL");
+    sscnn_hconv_t d;
+    int st = derive_h(*conv, &d);
+    if (st) return st;
+    if (d.h_out_local != conv->h_out_local || d.w_out != conv->w_out || d.halo_u != conv->halo_u ||
+        d.halo_d != conv->halo_d || d.ghalo_u != conv->ghalo_u || d.ghalo_d != conv->ghalo_d)
+        return fail(SSCNN_EINVAL, "descriptor not initialised by sscnn_hconv_init (or edited since)");
+    g->n = d.n; g->ci = d.c_in; g->co = d.c_out; g->h = d.h_local; g->wl = d.w; g->k = d.k;
+    g->stride = d.stride; g->pad = d.pad; g->groups = d.groups; g->ho = d.h_out_local; g->wol = d.w_out;
+    g->hl = d.pad; g->hr = d.k - d.stride - d.pad > 0 ? d.k - d.stride - d.pad : 0;
+    g->ghl = (d.k - 1 - d.pad) / d.stride; g->ghr = (d.pad + d.stride - 1) / d.stride;
+    g->cig = d.c_in / d.groups; g->cog = d.c_out / d.groups;
+    return SSCNN_OK;
+}
+
+// The workspace check shared by the grad_weight calls (rows: also the
+// row-edge grad_weight's scratch, used after the interior call is done with
+// its own).
+int need_workspace(const Geom& g, void* workspace, size_t workspace_bytes, size_t* ws_need, bool rows = false)
 {
     *ws_need = kernels_bwd_weight_workspace_bytes(g);
+    if (rows && row_edge_workspace_bytes(g) > *ws_need) *ws_need = row_edge_workspace_bytes(g);
     if (*ws_need) {
         if (!workspace || workspace_bytes < *ws_need)
             return fail(SSCNN_EWORKSPACE, "workspace of %zu bytes given, %zu needed",
@@ -384,6 +446,134 @@ int sscnn_conv_bwd_interior(const sscnn_conv_t* conv, const float* x, const floa
     return hip_status(kernels_conv_bwd(g, x, nullptr, grad_y, nullptr, weight, grad_x, grad_w_part,
                                        grad_b_part, ws_need ? workspace : nullptr, (hipStream_t)stream),
                       "conv_bwd_interior launch");
+}
+
+// --- height sharding -----------------------------------------------------
+
+int sscnn_hconv_init(sscnn_hconv_t* conv)
+{
+    if (!conv) return fail(SSCNN_EINVAL, "conv is NULL");
+    sscnn_hconv_t d;
+    TRY(derive_h(*conv, &d));
+    *conv = d;
+    return SSCNN_OK;
+}
+
+int sscnn_row_halo_gather(const sscnn_hconv_t* conv, int32_t which, const float* up_nbr, const float* down_nbr,
+                          float* halo, void* stream)
+{
+    Geom g;
+    TRY(check_h(conv, &g));
+    int64_t planes;
+    int rows, width, hu, hd;
+    if (which == SSCNN_HALO_INPUT) {
+        planes = (int64_t)g.n * g.ci; rows = g.h; width = g.wl; hu = conv->halo_u; hd = conv->halo_d;
+    } else if (which == SSCNN_HALO_GRAD_OUTPUT) {
+        planes = (int64_t)g.n * g.co; rows = g.ho; width = g.wol; hu = conv->ghalo_u; hd = conv->ghalo_d;
+    } else {
+        return fail(SSCNN_EINVAL, "which=%d is neither SSCNN_HALO_INPUT nor SSCNN_HALO_GRAD_OUTPUT", which);
+    }
+    const bool first = conv->shard == 0, last = conv->shard == conv->num_shards - 1;
+    if (first != (up_nbr == nullptr))
+        return fail(SSCNN_EINVAL, "up_nbr must be NULL exactly for shard 0 (shard=%d)", conv->shard);
+    if (last != (down_nbr == nullptr))
+        return fail(SSCNN_EINVAL, "down_nbr must be NULL exactly for the last shard (shard=%d)", conv->shard);
+    TRY(optional(up_nbr, "up_nbr"));
+    TRY(optional(down_nbr, "down_nbr"));
+    if (hu + hd == 0) return SSCNN_OK;
+    TRY(need(halo, "halo"));
+    return hip_status(launch_row_halo_gather(hu ? up_nbr : nullptr, hd ? down_nbr : nullptr, planes, rows, width,
+                                             hu, hd, halo, (hipStream_t)stream),
+                      "row_halo_gather launch");
+}
+
+int sscnn_hconv_fwd(const sscnn_hconv_t* conv, const float* x, const float* x_halo, const float* weight,
+                    const float* bias, float* y, void* stream)
+{
+    Geom g;
+    TRY(check_h(conv, &g));
+    TRY(need(x, "x"));
+    const int hu = conv->halo_u, hd = conv->halo_d;
+    if (hu + hd) TRY(need(x_halo, "x_halo")); else TRY(optional(x_halo, "x_halo"));
+    TRY(need(weight, "weight"));
+    TRY(optional(bias, "bias"));
+    TRY(need(y, "y"));
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e = kernels_conv_fwd(g, x, nullptr, weight, bias, y, st);
+    if (e == hipSuccess) e = launch_row_edge_fwd(g, hu, hd, x_halo, weight, y, st);
+    return hip_status(e, "hconv_fwd launch");
+}
+
+int sscnn_hconv_bwd_input(const sscnn_hconv_t* conv, const float* grad_y, const float* grad_y_halo,
+                          const float* weight, float* grad_x, void* stream)
+{
+    Geom g;
+    TRY(check_h(conv, &g));
+    TRY(need(grad_y, "grad_y"));
+    const int ghu = conv->ghalo_u, ghd = conv->ghalo_d;
+    if (ghu + ghd) TRY(need(grad_y_halo, "grad_y_halo")); else TRY(optional(grad_y_halo, "grad_y_halo"));
+    TRY(need(weight, "weight"));
+    TRY(need(grad_x, "grad_x"));
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e = kernels_conv_bwd_input(g, grad_y, nullptr, weight, grad_x, st);
+    if (e == hipSuccess) e = launch_row_edge_bwd_input(g, ghu, ghd, grad_y_halo, weight, grad_x, st);
+    return hip_status(e, "hconv_bwd_input launch");
+}
+
+size_t sscnn_hconv_bwd_weight_workspace_bytes(const sscnn_hconv_t* conv)
+{
+    Geom g;
+    if (check_h(conv, &g)) return 0;
+    const size_t a = kernels_bwd_weight_workspace_bytes(g), b = row_edge_workspace_bytes(g);
+    return a > b ? a : b;
+}
+
+int sscnn_hconv_bwd_weight_partial(const sscnn_hconv_t* conv, const float* x, const float* x_halo,
+                                   const float* grad_y, float* grad_w_part, float* grad_b_part, void* workspace,
+                                   size_t workspace_bytes, void* stream)
+{
+    Geom g;
+    TRY(check_h(conv, &g));
+    TRY(need(x, "x"));
+    const int hu = conv->halo_u, hd = conv->halo_d;
+    if (hu + hd) TRY(need(x_halo, "x_halo")); else TRY(optional(x_halo, "x_halo"));
+    TRY(need(grad_y, "grad_y"));
+    TRY(need(grad_w_part, "grad_w_part"));
+    TRY(optional(grad_b_part, "grad_b_part"));
+    size_t ws_need;
+    TRY(need_workspace(g, workspace, workspace_bytes, &ws_need, true));
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e = kernels_conv_bwd_weight(g, x, nullptr, grad_y, grad_w_part, grad_b_part,
+                                           ws_need ? workspace : nullptr, st);
+    if (e == hipSuccess) e = launch_row_edge_bwd_weight(g, hu, hd, x_halo, grad_y, grad_w_part, workspace, st);
+    return hip_status(e, "hconv_bwd_weight_partial launch");
+}
+
+int sscnn_hconv_bwd(const sscnn_hconv_t* conv, const float* x, const float* x_halo, const float* grad_y,
+                    const float* grad_y_halo, const float* weight, float* grad_x, float* grad_w_part,
+                    float* grad_b_part, void* workspace, size_t workspace_bytes, void* stream)
+{
+    Geom g;
+    TRY(check_h(conv, &g));
+    TRY(need(x, "x"));
+    const int hu = conv->halo_u, hd = conv->halo_d, ghu = conv->ghalo_u, ghd = conv->ghalo_d;
+    if (hu + hd) TRY(need(x_halo, "x_halo")); else TRY(optional(x_halo, "x_halo"));
+    TRY(need(grad_y, "grad_y"));
+    if (ghu + ghd) TRY(need(grad_y_halo, "grad_y_halo")); else TRY(optional(grad_y_halo, "grad_y_halo"));
+    TRY(need(weight, "weight"));
+    TRY(need(grad_x, "grad_x"));
+    TRY(need(grad_w_part, "grad_w_part"));
+    TRY(optional(grad_b_part, "grad_b_part"));
+    if (grad_x == x || grad_x == x_halo || grad_x == grad_y || grad_x == grad_y_halo)
+        return fail(SSCNN_EINVAL, "grad_x aliases an input");
+    size_t ws_need;
+    TRY(need_workspace(g, workspace, workspace_bytes, &ws_need, true));
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e = kernels_conv_bwd(g, x, nullptr, grad_y, nullptr, weight, grad_x, grad_w_part, grad_b_part,
+                                    ws_need ? workspace : nullptr, st);
+    if (e == hipSuccess) e = launch_row_edge_bwd_input(g, ghu, ghd, grad_y_halo, weight, grad_x, st);
+    if (e == hipSuccess) e = launch_row_edge_bwd_weight(g, hu, hd, x_halo, grad_y, grad_w_part, workspace, st);
+    return hip_status(e, "hconv_bwd launch");
 }
 
 }  // extern "C"

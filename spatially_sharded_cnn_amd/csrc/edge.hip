@@ -26,6 +26,7 @@
 // column (xx + pad - kw)/stride + ghalo_l where the division is exact.
 #include "internal.h"
 #include "edge.h"
+#include "wavesum.h"
 
 namespace sscnn {
 namespace {
@@ -262,20 +263,19 @@ dw_edge_conv_kernel(const float* __restrict__ sh, const float* __restrict__ w, f
 
 // Depthwise grad_weight: one 256-thread block per channel; each thread sums
 // its rows (n, i) for the taps that read a halo (kw < P: left, kw > P:
-// right), then the block adds the threads' sums in thread order.
+// right), then each wave adds its lanes' sums (a fixed-order cross-lane
+// reduce-scatter) and the block adds the four waves' totals in order.
 template <int K>
 __global__ void __launch_bounds__(256)
 dw_edge_wgrad_kernel(const float* __restrict__ xh, const float* __restrict__ gy, float* __restrict__ gw,
                      int N, int C, int H, int W)
 {
-    constexpr int P = K / 2, HW2 = 2 * P, NA = K * HW2;   // acc[kh][q]: kw = q (q < P) or q + 1 (q >= P)
-    __shared__ float red[256 * (NA + 1)];
+    constexpr int P = K / 2, HW2 = 2 * P, NA = K * HW2;   // acc[kh * 2P + q]: kw = q (q < P) or q + 1 (q >= P)
+    __shared__ float red[4][NA];
     const int c = blockIdx.x, tid = threadIdx.x;
-    float acc[K][HW2];
+    float acc[NA];
 #pragma unroll
-    for (int kh = 0; kh < K; ++kh)
-#pragma unroll
-        for (int q = 0; q < HW2; ++q) acc[kh][q] = 0.0f;
+    for (int a = 0; a < NA; ++a) acc[a] = 0.0f;
     for (int row = tid; row < N * H; row += 256) {
         const int n = row / H, i = row - n * H;
         const int64_t plane = (int64_t)n * C + c;
@@ -297,21 +297,23 @@ dw_edge_wgrad_kernel(const float* __restrict__ xh, const float* __restrict__ gy,
 #pragma unroll
             for (int kw = 0; kw < P; ++kw)
 #pragma unroll
-                for (int j = 0; j < P - kw; ++j) acc[kh][kw] = fmaf(g[j], h[j + kw], acc[kh][kw]);
+                for (int j = 0; j < P - kw; ++j) acc[kh * HW2 + kw] = fmaf(g[j], h[j + kw], acc[kh * HW2 + kw]);
 #pragma unroll
             for (int kw = P + 1; kw < K; ++kw)
 #pragma unroll
-                for (int m = 2 * P - kw; m < P; ++m) acc[kh][kw - 1] = fmaf(g[P + m], h[m + kw - P], acc[kh][kw - 1]);
+                for (int m = 2 * P - kw; m < P; ++m)
+                    acc[kh * HW2 + kw - 1] = fmaf(g[P + m], h[m + kw - P], acc[kh * HW2 + kw - 1]);
         }
     }
-#pragma unroll
-    for (int kh = 0; kh < K; ++kh)
-#pragma unroll
-        for (int q = 0; q < HW2; ++q) red[tid * (NA + 1) + kh * HW2 + q] = acc[kh][q];
+    {
+        const int lane = tid & 63, wave = tid >> 6;
+        const float s = wave_sum_scatter<NA>(acc, lane);
+        const int idx = wave_sum_index<NA>(lane);
+        if (idx >= 0) red[wave][idx] = s;
+    }
     __syncthreads();
     if (tid < NA) {
-        float sum = 0.0f;
-        for (int t = 0; t < 256; ++t) sum += red[t * (NA + 1) + tid];
+        const float sum = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
         const int kh = tid / HW2, q = tid - kh * HW2;
         const int kw = q < P ? q : q + 1;
         gw[((int64_t)c * K + kh) * K + kw] += sum;

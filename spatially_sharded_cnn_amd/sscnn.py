@@ -27,6 +27,8 @@ EXPORTED = (
     "sscnn_conv_fwd_interior", "sscnn_conv_fwd_edge", "sscnn_conv_bwd_input_interior",
     "sscnn_conv_bwd_input_edge", "sscnn_conv_bwd_weight_partial_interior", "sscnn_conv_bwd_weight_edge",
     "sscnn_conv_bwd_interior",
+    "sscnn_hconv_init", "sscnn_row_halo_gather", "sscnn_hconv_fwd", "sscnn_hconv_bwd_input",
+    "sscnn_hconv_bwd_weight_workspace_bytes", "sscnn_hconv_bwd_weight_partial", "sscnn_hconv_bwd",
 )
 
 
@@ -64,6 +66,33 @@ class Conv(ctypes.Structure):
         return (self.n, self.c_out, self.h_out, self.ghalo_l + self.ghalo_r)
 
 
+class HConv(ctypes.Structure):
+    """Mirror of sscnn_hconv_t (height sharding)."""
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "n", "c_in", "c_out", "h_local", "w", "k", "stride", "pad", "groups", "shard", "num_shards",
+        "h_out_local", "w_out", "halo_u", "halo_d", "ghalo_u", "ghalo_d")]
+
+    def __repr__(self):
+        return "HConv(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+    @property
+    def x_shape(self):
+        return (self.n, self.c_in, self.h_local, self.w)
+
+    @property
+    def y_shape(self):
+        return (self.n, self.c_out, self.h_out_local, self.w_out)
+
+    @property
+    def w_shape(self):
+        return (self.c_out, self.c_in // self.groups, self.k, self.k)
+
+    def halo_shape(self, which: int):
+        if which == HALO_INPUT:
+            return (self.n, self.c_in, self.halo_u + self.halo_d, self.w)
+        return (self.n, self.c_out, self.ghalo_u + self.ghalo_d, self.w_out)
+
+
 _lib = None
 _vp = ctypes.c_void_p
 
@@ -93,6 +122,15 @@ def lib() -> ctypes.CDLL:
         L.sscnn_conv_bwd_weight_partial_interior.argtypes = [P, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.sscnn_conv_bwd_weight_edge.argtypes = [P, _vp, _vp, _vp, _vp]
         L.sscnn_conv_bwd_interior.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        HP = ctypes.POINTER(HConv)
+        L.sscnn_hconv_init.argtypes = [HP]
+        L.sscnn_row_halo_gather.argtypes = [HP, ctypes.c_int32, _vp, _vp, _vp, _vp]
+        L.sscnn_hconv_fwd.argtypes = [HP, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.sscnn_hconv_bwd_input.argtypes = [HP, _vp, _vp, _vp, _vp, _vp]
+        L.sscnn_hconv_bwd_weight_workspace_bytes.argtypes = [HP]
+        L.sscnn_hconv_bwd_weight_workspace_bytes.restype = ctypes.c_size_t
+        L.sscnn_hconv_bwd_weight_partial.argtypes = [HP, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.sscnn_hconv_bwd.argtypes = [HP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.sscnn_status_string.argtypes = [ctypes.c_int]
         L.sscnn_status_string.restype = ctypes.c_char_p
         L.sscnn_last_error.restype = ctypes.c_char_p
@@ -101,7 +139,8 @@ def lib() -> ctypes.CDLL:
                   "sscnn_abi_version", "sscnn_conv_fwd_interior", "sscnn_conv_fwd_edge",
                   "sscnn_conv_bwd_input_interior", "sscnn_conv_bwd_input_edge",
                   "sscnn_conv_bwd_weight_partial_interior", "sscnn_conv_bwd_weight_edge",
-                  "sscnn_conv_bwd_interior"):
+                  "sscnn_conv_bwd_interior", "sscnn_hconv_init", "sscnn_row_halo_gather", "sscnn_hconv_fwd",
+                  "sscnn_hconv_bwd_input", "sscnn_hconv_bwd_weight_partial", "sscnn_hconv_bwd"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -293,6 +332,77 @@ def conv_bwd_interior(conv: Conv, x, grad_y, weight, grad_x, grad_w_part, grad_b
         _ptr(weight, conv.w_shape, "weight"), _ptr(grad_x, conv.x_shape, "grad_x"),
         _ptr(grad_w_part, conv.w_shape, "grad_w_part"), _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True),
         ws_ptr, ws_bytes, _stream(stream)), "conv_bwd_interior")
+
+
+# --- height sharding ---------------------------------------------------------
+
+def hconv_init(n, c_in, c_out, h_local, w, k, stride, pad, groups, shard, num_shards) -> HConv:
+    """Build and validate an H-shard descriptor (sscnn_hconv_init)."""
+    c = HConv(n, c_in, c_out, h_local, w, k, stride, pad, groups, shard, num_shards)
+    _check(lib().sscnn_hconv_init(ctypes.byref(c)), "hconv_init")
+    return c
+
+
+def row_halo_gather(conv: HConv, which: int, up_nbr, down_nbr, halo, stream=None):
+    """sscnn_row_halo_gather: up_nbr / down_nbr are the neighbours' slices (None at
+    the global top / bottom); halo receives (N, C, hu + hd, width)."""
+    sl = conv.x_shape if which == HALO_INPUT else conv.y_shape
+    hs = conv.halo_shape(which)
+    _check(lib().sscnn_row_halo_gather(ctypes.byref(conv), which, _ptr(up_nbr, sl, "up_nbr", True),
+                                       _ptr(down_nbr, sl, "down_nbr", True), _ptr(halo, hs, "halo", hs[2] == 0),
+                                       _stream(stream)), "row_halo_gather")
+
+
+def hconv_fwd(conv: HConv, x, x_halo, weight, bias, y, stream=None):
+    hs = conv.halo_shape(HALO_INPUT)
+    _check(lib().sscnn_hconv_fwd(ctypes.byref(conv), _ptr(x, conv.x_shape, "x"),
+                                 _ptr(x_halo, hs, "x_halo", hs[2] == 0), _ptr(weight, conv.w_shape, "weight"),
+                                 _ptr(bias, (conv.c_out,), "bias", True), _ptr(y, conv.y_shape, "y"),
+                                 _stream(stream)), "hconv_fwd")
+
+
+def hconv_bwd_input(conv: HConv, grad_y, grad_y_halo, weight, grad_x, stream=None):
+    gs = conv.halo_shape(HALO_GRAD_OUTPUT)
+    _check(lib().sscnn_hconv_bwd_input(ctypes.byref(conv), _ptr(grad_y, conv.y_shape, "grad_y"),
+                                       _ptr(grad_y_halo, gs, "grad_y_halo", gs[2] == 0),
+                                       _ptr(weight, conv.w_shape, "weight"), _ptr(grad_x, conv.x_shape, "grad_x"),
+                                       _stream(stream)), "hconv_bwd_input")
+
+
+def hconv_bwd_weight_workspace_bytes(conv: HConv) -> int:
+    return int(lib().sscnn_hconv_bwd_weight_workspace_bytes(ctypes.byref(conv)))
+
+
+def hconv_bwd_weight_partial(conv: HConv, x, x_halo, grad_y, grad_w_part, grad_b_part, workspace=None,
+                             stream=None):
+    hs = conv.halo_shape(HALO_INPUT)
+    ws_ptr, ws_bytes = _workspace(workspace)
+    _check(lib().sscnn_hconv_bwd_weight_partial(
+        ctypes.byref(conv), _ptr(x, conv.x_shape, "x"), _ptr(x_halo, hs, "x_halo", hs[2] == 0),
+        _ptr(grad_y, conv.y_shape, "grad_y"), _ptr(grad_w_part, conv.w_shape, "grad_w_part"),
+        _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True), ws_ptr, ws_bytes, _stream(stream)),
+        "hconv_bwd_weight_partial")
+
+
+def hconv_bwd(conv: HConv, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_part, grad_b_part,
+              workspace=None, stream=None):
+    hs, gs = conv.halo_shape(HALO_INPUT), conv.halo_shape(HALO_GRAD_OUTPUT)
+    ws_ptr, ws_bytes = _workspace(workspace)
+    _check(lib().sscnn_hconv_bwd(
+        ctypes.byref(conv), _ptr(x, conv.x_shape, "x"), _ptr(x_halo, hs, "x_halo", hs[2] == 0),
+        _ptr(grad_y, conv.y_shape, "grad_y"), _ptr(grad_y_halo, gs, "grad_y_halo", gs[2] == 0),
+        _ptr(weight, conv.w_shape, "weight"), _ptr(grad_x, conv.x_shape, "grad_x"),
+        _ptr(grad_w_part, conv.w_shape, "grad_w_part"), _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True),
+        ws_ptr, ws_bytes, _stream(stream)), "hconv_bwd")
+
+
+def new_hworkspace(conv: HConv, device="cuda"):
+    """Allocate (with torch) the bwd-weight workspace an H-shard layer needs, or None."""
+    nbytes = hconv_bwd_weight_workspace_bytes(conv)
+    if nbytes == 0:
+        return None
+    import torch
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def partial_reduce(parts: Sequence, out, stream=None):

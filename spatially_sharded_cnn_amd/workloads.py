@@ -52,6 +52,7 @@ class Workload:
     seed: int
     dist: str            # "uniform" or "normal"
     description: str
+    axis: int = 3        # the sharded dimension: 3 = W (Shard(3)), 2 = H (Shard(2))
 
     @property
     def x_shape(self):
@@ -95,6 +96,12 @@ WORKLOADS = {
         (_layer("dw", 256, 256, 7, 1, 3, 256, (7, 256, 128, 256), (7, 256, 128, 256)),),
         num_shards=4, shard=1, seed=1002, dist="normal",
         description="depthwise 7x7 s1 p3 C=256: shard (7,256,128,64) of a (7,256,128,256) map, 3-column halos"),
+    "dw7_c256_hshard": Workload(
+        "dw7_c256_hshard",
+        (_layer("dw", 256, 256, 7, 1, 3, 256, (7, 256, 128, 256), (7, 256, 128, 256)),),
+        num_shards=4, shard=1, seed=1002, dist="normal",
+        description="depthwise 7x7 s1 p3 C=256 split along H: shard (7,256,32,256) of the same (7,256,128,256) "
+                    "map, 3-row halos", axis=2),
     "dense5x5_c256": Workload(
         "dense5x5_c256",
         (_layer("conv", 256, 256, 5, 1, 2, 1, (7, 256, 128, 512), (7, 256, 128, 512)),),

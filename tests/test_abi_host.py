@@ -263,3 +263,58 @@ def test_split_calls_validate_before_launching():
     assert L.sscnn_conv_fwd_edge(rp, None, None, None, None) == sscnn.OK
     assert L.sscnn_conv_bwd_input_edge(rp, None, None, None, None) == sscnn.OK
     assert L.sscnn_conv_bwd_weight_edge(rp, None, None, None, None) == sscnn.OK
+
+
+@pytest.mark.parametrize("k,s,p", [(5, 1, 2), (7, 1, 3), (3, 1, 1), (1, 1, 0), (4, 4, 0),
+                                   (2, 2, 0), (3, 2, 1), (5, 2, 2), (6, 2, 2)])
+def test_hconv_init_row_halos_match_brute_force(k, s, p):
+    """Height sharding: the row halos are the column halos' rule along H (the
+    same brute-force enumeration of the taps, with rows for columns)."""
+    hl = 8 * s
+    c = sscnn.hconv_init(2, 4, 6, hl, 12 * s, k, s, p, 1, 1, 3)
+    assert (c.halo_u, c.halo_d, c.ghalo_u, c.ghalo_d) == _brute_force_halos(k, s, p, hl)
+    assert c.h_out_local == hl // s and c.w_out == 12
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 3, 8, 16, 8, 5, 1, 5, 1, 0, 2), sscnn.EINVAL),        # pad >= k
+    ((1, 3, 8, 16, 8, 5, 1, 2, 2, 0, 2), sscnn.EINVAL),        # groups does not divide c_in
+    ((1, 4, 8, 16, 8, 5, 1, 2, 1, 2, 2), sscnn.EINVAL),        # shard out of range
+    ((1, 4, 8, 16, 2, 7, 1, 1, 1, 0, 2), sscnn.EINVAL),        # image narrower than the kernel
+    ((1, 4, 8, 15, 8, 2, 2, 0, 1, 0, 2), sscnn.EUNSUPPORTED),  # h_local % stride
+    ((1, 4, 8, 2, 8, 7, 1, 3, 1, 0, 2), sscnn.EUNSUPPORTED),   # row halo taller than a slice
+    ((1, 4, 8, 16, 8, 5, 1, 0, 1, 0, 2), sscnn.EUNSUPPORTED),  # 'valid' conv shrinks H
+])
+def test_hconv_init_rejects(args, status):
+    with pytest.raises(sscnn.SscnnError) as ei:
+        sscnn.hconv_init(*args)
+    assert ei.value.status == status
+
+
+def test_hconv_calls_validate_before_launching():
+    L = sscnn.lib()
+    F = FAKE
+    first, mid, last = (sscnn.hconv_init(1, 3, 8, 16, 32, 5, 1, 2, 1, s, 4) for s in (0, 1, 3))
+    r = ctypes.byref(mid)
+    # neighbour rules of the row exchange
+    assert L.sscnn_row_halo_gather(ctypes.byref(first), 0, F, F, F, None) == sscnn.EINVAL
+    assert L.sscnn_row_halo_gather(r, 0, None, F, F, None) == sscnn.EINVAL
+    assert L.sscnn_row_halo_gather(r, 0, F, None, F, None) == sscnn.EINVAL
+    assert L.sscnn_row_halo_gather(ctypes.byref(last), 0, F, F, F, None) == sscnn.EINVAL
+    assert L.sscnn_row_halo_gather(r, 5, F, F, F, None) == sscnn.EINVAL
+    assert L.sscnn_row_halo_gather(r, 0, F, F, None, None) == sscnn.EINVAL
+    # every required operand
+    assert L.sscnn_hconv_fwd(r, None, F, F, None, F, None) == sscnn.EINVAL
+    assert L.sscnn_hconv_fwd(r, F, None, F, None, F, None) == sscnn.EINVAL     # row halo needed
+    assert L.sscnn_hconv_fwd(r, F + 4, F, F, None, F, None) == sscnn.EINVAL
+    assert L.sscnn_hconv_bwd_input(r, F, None, F, F, None) == sscnn.EINVAL
+    assert L.sscnn_hconv_bwd_weight_partial(r, F, F, F, None, None, None, 0, None) == sscnn.EINVAL
+    assert L.sscnn_hconv_bwd(r, F, F, F, F, F, F, F + 4096, None, None, 0, None) == sscnn.EINVAL   # grad_x is x
+    # an edited descriptor
+    mid.halo_u = 1
+    assert L.sscnn_hconv_fwd(r, F, F, F, None, F, None) == sscnn.EINVAL
+    assert "sscnn_hconv_init" in sscnn.last_error()
+    # patchify: no row halo, nothing to launch for the exchange
+    p = sscnn.hconv_init(1, 3, 16, 16, 16, 4, 4, 0, 1, 1, 4)
+    assert (p.halo_u, p.halo_d, p.ghalo_u, p.ghalo_d) == (0, 0, 0, 0)
+    assert L.sscnn_row_halo_gather(ctypes.byref(p), 0, F, F, None, None) == sscnn.OK

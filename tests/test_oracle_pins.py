@@ -379,6 +379,39 @@ def test_page_pipeline_equals_oracle_columns(case, num_shards):
             _close(dx.numpy(), dxs, 1e-10)
 
 
+@pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[2], CASES[5]])
+@pytest.mark.parametrize("num_shards", [2, 3])
+def test_row_pipeline_equals_oracle_rows(case, num_shards):
+    """The same method along H (Shard(2), kwkr.cn retelling, section 5.2):
+    gather row halos, stack them on the local rows, convolve 'valid' along H
+    (zero padding along W) -- torch's conv2d and autograd -- and compare with
+    the oracle's unsharded rows and its row-restricted partial gradients."""
+    n, ci, co, h, w, k, s, p, g = case
+    h = h - h % (num_shards * s) + num_shards * s  # make H divisible
+    case = (n, ci, co, h, w, k, s, p, g)
+    x, wt, b, gy = _case_tensors(case, seed=22)
+    hl, hol = h // num_shards, (h // s) // num_shards
+    hu, hd = p, max(0, k - s - p)
+    y_full = oracle.conv_fwd(x, wt, b, s, p, g)
+    for sh in range(num_shards):
+        xs = oracle.shard_rows(x, num_shards, sh)
+        rh = oracle.halo_rows(x, num_shards, sh, hu, hd)
+        ext_t = torch.tensor(np.concatenate([rh[:, :, :hu], xs, rh[:, :, hu:]], axis=2), requires_grad=True)
+        wt_t = torch.tensor(wt, requires_grad=True)
+        b_t = torch.tensor(b, requires_grad=True)
+        y = F.conv2d(ext_t, wt_t, b_t, stride=s, padding=(0, p), groups=g)
+        rows = (sh * hol, (sh + 1) * hol)
+        _close(y.detach().numpy(), y_full[:, :, rows[0]:rows[1], :], 1e-10)
+        y.backward(torch.tensor(np.ascontiguousarray(gy[:, :, rows[0]:rows[1], :])))
+        gw_s, gb_s = oracle.conv_bwd_weight_rows(x, gy, k, s, p, g, rows)
+        _close(wt_t.grad.numpy(), gw_s, 1e-10)
+        _close(b_t.grad.numpy(), gb_s, 1e-10)
+    # the row partials sum to the full gradient
+    parts = [oracle.conv_bwd_weight_rows(x, gy, k, s, p, g, (sh * hol, (sh + 1) * hol))[0]
+             for sh in range(num_shards)]
+    _close(oracle.reduce_partials(parts), oracle.conv_bwd_weight(x, gy, k, s, p, g)[0], 1e-10)
+
+
 # --- mutation check ---------------------------------------------------------
 
 MUTANTS = {
