@@ -15,6 +15,9 @@ on S GPUs, and `ShardedConv2d` is a module over such lists:
   output columns; the partials are summed in shard order (the reduction that
   turns the _Partial gradients into replicated ones).
 
+With dim=2 the shards are slices of rows instead (Shard(2), the height split
+of kwkr.cn retelling, section 5.2): the same steps with row halos.
+
 This file only marshals tensors and calls the C ABI (`sscnn`); every step runs
 in the library's kernels, and there is no fallback when the library is
 missing.
@@ -29,17 +32,38 @@ import torch
 from . import sscnn
 
 
-def shard(x: torch.Tensor, num_shards: int) -> List[torch.Tensor]:
-    """Split an (N, C, H, W) tensor into num_shards contiguous W-slices."""
-    if x.dim() != 4 or x.shape[3] % num_shards:
-        raise ValueError(f"cannot split width {tuple(x.shape)} into {num_shards} shards")
-    w = x.shape[3] // num_shards
-    return [x[..., s * w:(s + 1) * w].contiguous() for s in range(num_shards)]
+def shard(x: torch.Tensor, num_shards: int, dim: int = 3) -> List[torch.Tensor]:
+    """Split an (N, C, H, W) tensor into num_shards contiguous slices along W
+    (dim=3) or H (dim=2)."""
+    if x.dim() != 4 or dim not in (2, 3) or x.shape[dim] % num_shards:
+        raise ValueError(f"cannot split {tuple(x.shape)} into {num_shards} shards along dim {dim}")
+    w = x.shape[dim] // num_shards
+    return [x.narrow(dim, s * w, w).contiguous() for s in range(num_shards)]
 
 
-def unshard(xs: Sequence[torch.Tensor]) -> torch.Tensor:
-    """Concatenate W-shards back into one tensor."""
-    return torch.cat(list(xs), dim=3)
+def unshard(xs: Sequence[torch.Tensor], dim: int = 3) -> torch.Tensor:
+    """Concatenate shards back into one tensor."""
+    return torch.cat(list(xs), dim=dim)
+
+
+class _WCalls:
+    """The ABI calls of a W-split layer."""
+    halo_gather = staticmethod(sscnn.halo_gather)
+    conv_fwd = staticmethod(sscnn.conv_fwd)
+    conv_bwd = staticmethod(sscnn.conv_bwd)
+    conv_bwd_weight_partial = staticmethod(sscnn.conv_bwd_weight_partial)
+    new_workspace = staticmethod(sscnn.new_workspace)
+    init = staticmethod(sscnn.conv_init)
+
+
+class _HCalls:
+    """The ABI calls of an H-split layer (row halos)."""
+    halo_gather = staticmethod(sscnn.row_halo_gather)
+    conv_fwd = staticmethod(sscnn.hconv_fwd)
+    conv_bwd = staticmethod(sscnn.hconv_bwd)
+    conv_bwd_weight_partial = staticmethod(sscnn.hconv_bwd_weight_partial)
+    new_workspace = staticmethod(sscnn.new_hworkspace)
+    init = staticmethod(sscnn.hconv_init)
 
 
 class _ShardedConv(torch.autograd.Function):
@@ -49,18 +73,20 @@ class _ShardedConv(torch.autograd.Function):
     def forward(ctx, layer, weight, bias, *xs):
         S = len(xs)
         convs = layer._descriptors(xs)
+        A = layer._calls
         dev = xs[0].device
         halos = []
         for s, c in enumerate(convs):
             h = torch.empty(c.halo_shape(sscnn.HALO_INPUT), device=dev, dtype=torch.float32)
-            sscnn.halo_gather(c, sscnn.HALO_INPUT, xs[s - 1] if s > 0 else None, xs[s + 1] if s + 1 < S else None, h)
+            A.halo_gather(c, sscnn.HALO_INPUT, xs[s - 1] if s > 0 else None, xs[s + 1] if s + 1 < S else None, h)
             halos.append(h)
         ys = []
         for s, c in enumerate(convs):
             y = torch.empty(c.y_shape, device=dev, dtype=torch.float32)
-            sscnn.conv_fwd(c, xs[s], halos[s], weight, bias, y)
+            A.conv_fwd(c, xs[s], halos[s], weight, bias, y)
             ys.append(y)
         ctx.convs = convs
+        ctx.calls = A
         ctx.has_bias = bias is not None
         ctx.save_for_backward(weight, *xs, *halos)
         return tuple(ys)
@@ -68,6 +94,7 @@ class _ShardedConv(torch.autograd.Function):
     @staticmethod
     def backward(ctx, *gys):
         convs = ctx.convs
+        A = ctx.calls
         S = len(convs)
         saved = ctx.saved_tensors
         weight, xs, halos = saved[0], saved[1:1 + S], saved[1 + S:1 + 2 * S]
@@ -78,21 +105,21 @@ class _ShardedConv(torch.autograd.Function):
         ghalos = []
         for s, c in enumerate(convs):
             h = torch.empty(c.halo_shape(sscnn.HALO_GRAD_OUTPUT), device=dev, dtype=torch.float32)
-            sscnn.halo_gather(c, sscnn.HALO_GRAD_OUTPUT, gys[s - 1] if s > 0 else None,
-                              gys[s + 1] if s + 1 < S else None, h)
+            A.halo_gather(c, sscnn.HALO_GRAD_OUTPUT, gys[s - 1] if s > 0 else None,
+                          gys[s + 1] if s + 1 < S else None, h)
             ghalos.append(h)
         nw, co = weight.numel(), weight.shape[0]
         parts = [torch.empty(nw + co, device=dev, dtype=torch.float32) for _ in range(S)]
-        workspace = sscnn.new_workspace(convs[0], device=dev)   # shards share a geometry; calls run in order
+        workspace = A.new_workspace(convs[0], device=dev)   # shards share a geometry; calls run in order
         dxs = []
         for s, c in enumerate(convs):
             gw_part, gb_part = parts[s][:nw].view(weight.shape), parts[s][nw:]
             if need_dx:
                 dx = torch.empty(c.x_shape, device=dev, dtype=torch.float32)
-                sscnn.conv_bwd(c, xs[s], halos[s], gys[s], ghalos[s], weight, dx, gw_part, gb_part, workspace)
+                A.conv_bwd(c, xs[s], halos[s], gys[s], ghalos[s], weight, dx, gw_part, gb_part, workspace)
                 dxs.append(dx)
             else:
-                sscnn.conv_bwd_weight_partial(c, xs[s], halos[s], gys[s], gw_part, gb_part, workspace)
+                A.conv_bwd_weight_partial(c, xs[s], halos[s], gys[s], gw_part, gb_part, workspace)
                 dxs.append(None)
         reduced = torch.empty(nw + co, device=dev, dtype=torch.float32)
         sscnn.partial_reduce(parts, reduced)
@@ -103,15 +130,20 @@ class _ShardedConv(torch.autograd.Function):
 
 class ShardedConv2d(torch.nn.Module):
     """A 2-D convolution (cross-correlation, zero padding, square kernel) on
-    W-sharded activations: forward(list of S shards) -> list of S shards.
+    sharded activations: forward(list of S shards) -> list of S shards, the
+    shards being slices along W (dim=3, the default) or H (dim=2).
 
     Parameters are replicated (one weight / bias tensor); their gradients are
     the reduced sums of the shards' partials.  Initialisation matches
     torch.nn.Conv2d's defaults."""
 
     def __init__(self, in_channels: int, out_channels: int, kernel_size: int, stride: int = 1,
-                 padding: int = 0, groups: int = 1, bias: bool = True, device="cuda"):
+                 padding: int = 0, groups: int = 1, bias: bool = True, device="cuda", dim: int = 3):
         super().__init__()
+        if dim not in (2, 3):
+            raise ValueError("dim must be 2 (H) or 3 (W)")
+        self.dim = dim
+        self._calls = _HCalls if dim == 2 else _WCalls
         if in_channels % groups or out_channels % groups:
             raise ValueError("groups must divide in_channels and out_channels")
         self.in_channels, self.out_channels = in_channels, out_channels
@@ -139,8 +171,8 @@ class ShardedConv2d(torch.nn.Module):
             n, c, h, w = shapes[0]
             if c != self.in_channels:
                 raise ValueError(f"expected {self.in_channels} channels, got {c}")
-            self._cache[key] = [sscnn.conv_init(n, c, self.out_channels, h, w, self.kernel_size, self.stride,
-                                                self.padding, self.groups, s, len(xs)) for s in range(len(xs))]
+            self._cache[key] = [self._calls.init(n, c, self.out_channels, h, w, self.kernel_size, self.stride,
+                                                 self.padding, self.groups, s, len(xs)) for s in range(len(xs))]
         return self._cache[key]
 
     def forward(self, xs: Sequence[torch.Tensor]) -> List[torch.Tensor]:
@@ -151,4 +183,4 @@ class ShardedConv2d(torch.nn.Module):
 
     def extra_repr(self):
         return (f"{self.in_channels}, {self.out_channels}, kernel_size={self.kernel_size}, stride={self.stride}, "
-                f"padding={self.padding}, groups={self.groups}, bias={self.bias is not None}")
+                f"padding={self.padding}, groups={self.groups}, bias={self.bias is not None}, dim={self.dim}")

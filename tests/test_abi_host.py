@@ -225,6 +225,16 @@ def test_autograd_shard_round_trip_and_host_tensors_rejected():
     assert layer.weight.shape == (6, 3, 3, 3) and layer.bias.shape == (6,)
     with pytest.raises(ValueError):
         layer(xs)
+    rows = sa.shard(x, 2, dim=2)
+    assert [tuple(t.shape) for t in rows] == [(2, 3, 2, 12)] * 2 and all(t.is_contiguous() for t in rows)
+    assert torch.equal(sa.unshard(rows, dim=2), x)
+    with pytest.raises(ValueError):
+        sa.shard(x, 3, dim=2)
+    with pytest.raises(ValueError):
+        sa.ShardedConv2d(3, 6, 3, padding=1, device="cpu", dim=1)
+    hlayer = sa.ShardedConv2d(3, 6, 3, padding=1, device="cpu", dim=2)
+    with pytest.raises(ValueError):
+        hlayer(rows)
 
 
 def test_split_calls_validate_before_launching():

@@ -1,6 +1,6 @@
 """GPU parity of the autograd layer (needs an MI355X).
 
-`ShardedConv2d` runs on lists of W-shards; a loss sum_s <y_s, g_s> makes the
+`ShardedConv2d` runs on lists of W-shards (or, with dim=2, H-shards); a loss sum_s <y_s, g_s> makes the
 gradient arriving at the outputs exactly g, so the input, weight and bias
 gradients autograd returns are compared with the oracle's grad_input,
 grad_weight and grad_bias of the unsharded layer (or chain), computed on the
@@ -145,3 +145,38 @@ def test_gradients_are_bitwise_reproducible():
                        [m.bias.grad.clone() for m in mods])
     for a, b in zip(*results):
         assert torch.equal(a, b)
+
+
+# (name, global input shape, co, k, stride, pad, groups, S): H-shards (dim=2)
+HLAYERS = [
+    ("depthwise7_rows", (2, 12, 4 * 16, 40), 12, 7, 1, 3, 12, 4),
+    ("dense3x3_rows", (1, 16, 2 * 24, 36), 24, 3, 1, 1, 1, 2),
+    ("strided3x3_rows", (1, 6, 2 * 16, 22), 10, 3, 2, 1, 1, 2),
+]
+
+
+@pytest.mark.parametrize("case", HLAYERS, ids=[c[0] for c in HLAYERS])
+def test_row_sharded_layer_gradients_match_oracle(case):
+    """The same check with the activations split along H (Shard(2))."""
+    name, shape, co, k, s, p, g, S = case
+    _say(f"  {name}: input {shape} co={co} k={k} s={s} p={p} g={g} S={S} (H-shards)")
+    rng = np.random.default_rng(3005)
+    x = _draw(rng, shape)
+    w = _draw(rng, (co, shape[1] // g, k, k), 0.05)
+    b = _draw(rng, (co,), 0.05)
+    layer = sa.ShardedConv2d(shape[1], co, k, stride=s, padding=p, groups=g, dim=2)
+    with torch.no_grad():
+        layer.weight.copy_(to_dev(w))
+        layer.bias.copy_(to_dev(b))
+    xs = [t.requires_grad_() for t in sa.shard(to_dev(x), S, dim=2)]
+    ys = layer(xs)
+    gout = _draw(rng, tuple(sa.unshard(ys, dim=2).shape))
+    _loss(ys, sa.shard(to_dev(gout), S, dim=2)).backward()
+    torch.cuda.synchronize()
+
+    assert_close(host(sa.unshard(ys, dim=2)), oracle.conv_fwd(x, w, b, s, p, g), TOL_FWD, f"{name} forward")
+    dx_ref = oracle.conv_bwd_input(gout, w, x.shape, s, p, g)
+    assert_close(np.concatenate([host(t.grad) for t in xs], axis=2), dx_ref, TOL_DX, f"{name} grad_input")
+    gw_ref, gb_ref = oracle.conv_bwd_weight(x, gout, k, s, p, g)
+    assert_close(host(layer.weight.grad), gw_ref, TOL_GW, f"{name} grad_weight")
+    assert_close(host(layer.bias.grad), gb_ref, TOL_GW, f"{name} grad_bias")
