@@ -45,6 +45,11 @@ SMALL = [
     ("dw7_h16_w16", 2, 24, 24, 16, 4 * 16, 7, 1, 3, 24, 4),
     ("dw7_h16_w32", 2, 12, 12, 16, 3 * 32, 7, 1, 3, 12, 3),
     ("dw5_h20_w16", 1, 9, 9, 20, 2 * 16, 5, 1, 2, 9, 2),
+    # widths that are multiples of 64 (the register-window kernels): k = 3, a slice
+    # of three 64-column blocks with a ragged strip group, a plane under one strip
+    ("dw3_w64", 2, 6, 6, 23, 2 * 64, 3, 1, 1, 6, 2),
+    ("dw5_w192_h70", 1, 5, 5, 70, 2 * 192, 5, 1, 2, 5, 2),
+    ("dw7_h5_w64", 1, 3, 3, 5, 3 * 64, 7, 1, 3, 3, 3),
     ("dense5x5_ragged", 2, 40, 72, 13, 3 * 37, 5, 1, 2, 1, 3),
     ("mfma5x5_ragged_channels", 2, 44, 72, 13, 3 * 36, 5, 1, 2, 1, 3),
     ("mfma5x5_two_segments", 1, 16, 20, 6, 2 * 132, 5, 1, 2, 1, 2),
