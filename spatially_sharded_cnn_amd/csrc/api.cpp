@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "depthwise.h"
 #include "edge.h"
 #include "internal.h"
 #include "kernels.h"
@@ -499,6 +500,8 @@ int sscnn_hconv_fwd(const sscnn_hconv_t* conv, const float* x, const float* x_ha
     TRY(optional(bias, "bias"));
     TRY(need(y, "y"));
     const hipStream_t st = (hipStream_t)stream;
+    if (dw_supported(g))   // depthwise: the tiles read the row halo themselves
+        return hip_status(launch_dw_fwd_rows(g, x, x_halo, hu, hd, weight, bias, y, st), "hconv_fwd launch");
     hipError_t e = kernels_conv_fwd(g, x, nullptr, weight, bias, y, st);
     if (e == hipSuccess) e = launch_row_edge_fwd(g, hu, hd, x_halo, weight, y, st);
     return hip_status(e, "hconv_fwd launch");
@@ -515,6 +518,9 @@ int sscnn_hconv_bwd_input(const sscnn_hconv_t* conv, const float* grad_y, const 
     TRY(need(weight, "weight"));
     TRY(need(grad_x, "grad_x"));
     const hipStream_t st = (hipStream_t)stream;
+    if (dw_supported(g))
+        return hip_status(launch_dw_bwd_input_rows(g, grad_y, grad_y_halo, ghu, ghd, weight, grad_x, st),
+                          "hconv_bwd_input launch");
     hipError_t e = kernels_conv_bwd_input(g, grad_y, nullptr, weight, grad_x, st);
     if (e == hipSuccess) e = launch_row_edge_bwd_input(g, ghu, ghd, grad_y_halo, weight, grad_x, st);
     return hip_status(e, "hconv_bwd_input launch");
@@ -543,6 +549,10 @@ int sscnn_hconv_bwd_weight_partial(const sscnn_hconv_t* conv, const float* x, co
     size_t ws_need;
     TRY(need_workspace(g, workspace, workspace_bytes, &ws_need, true));
     const hipStream_t st = (hipStream_t)stream;
+    if (dw_supported(g))
+        return hip_status(launch_dw_bwd_weight_rows(g, x, x_halo, hu, hd, grad_y, grad_w_part, grad_b_part,
+                                                    workspace, st),
+                          "hconv_bwd_weight_partial launch");
     hipError_t e = kernels_conv_bwd_weight(g, x, nullptr, grad_y, grad_w_part, grad_b_part,
                                            ws_need ? workspace : nullptr, st);
     if (e == hipSuccess) e = launch_row_edge_bwd_weight(g, hu, hd, x_halo, grad_y, grad_w_part, workspace, st);
@@ -569,6 +579,10 @@ int sscnn_hconv_bwd(const sscnn_hconv_t* conv, const float* x, const float* x_ha
     size_t ws_need;
     TRY(need_workspace(g, workspace, workspace_bytes, &ws_need, true));
     const hipStream_t st = (hipStream_t)stream;
+    if (dw_supported(g))
+        return hip_status(launch_dw_bwd_rows(g, x, x_halo, hu, hd, grad_y, grad_y_halo, ghu, ghd, weight, grad_x,
+                                             grad_w_part, grad_b_part, workspace, st),
+                          "hconv_bwd launch");
     hipError_t e = kernels_conv_bwd(g, x, nullptr, grad_y, nullptr, weight, grad_x, grad_w_part, grad_b_part,
                                     ws_need ? workspace : nullptr, st);
     if (e == hipSuccess) e = launch_row_edge_bwd_input(g, ghu, ghd, grad_y_halo, weight, grad_x, st);

@@ -19,4 +19,17 @@ hipError_t launch_dw_bwd_weight(const Geom& g, const float* x, const float* xh, 
 hipError_t launch_dw_bwd(const Geom& g, const float* x, const float* xh, const float* gy, const float* gyh,
                          const float* w, float* gx, float* gw, float* gb, void* ws, hipStream_t st);
 
+// Height sharding: the same kernels with the rows beyond the slice's top and
+// bottom read from row halos (N*C, up + down, W), up rows first (the layout
+// of sscnn_row_halo_gather); no column halo.  Same workspace as above.
+hipError_t launch_dw_fwd_rows(const Geom& g, const float* x, const float* x_rh, int up, int down,
+                              const float* w, const float* b, float* y, hipStream_t st);
+hipError_t launch_dw_bwd_input_rows(const Geom& g, const float* gy, const float* gy_rh, int up, int down,
+                                    const float* w, float* gx, hipStream_t st);
+hipError_t launch_dw_bwd_weight_rows(const Geom& g, const float* x, const float* x_rh, int up, int down,
+                                     const float* gy, float* gw, float* gb, void* ws, hipStream_t st);
+hipError_t launch_dw_bwd_rows(const Geom& g, const float* x, const float* x_rh, int x_up, int x_down,
+                              const float* gy, const float* gy_rh, int g_up, int g_down, const float* w, float* gx,
+                              float* gw, float* gb, void* ws, hipStream_t st);
+
 }  // namespace sscnn

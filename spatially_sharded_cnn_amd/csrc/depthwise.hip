@@ -56,7 +56,24 @@ struct DwArgs {
     float* out;          // (N*C, H, W) output or grad_input
     float* ws;           // grad_weight partials (C, up to N * tiles_h * tiles_w, k*k + 1)
     int H, W, C, N, tiles_h, tiles_w, ntiles;   // ntiles = N * C * tiles_h * tiles_w
+    // Height sharding (kernels instantiated with ROWH): the rows above and
+    // below the slice, (N*C, up + down, W) -- up rows first, then down rows.
+    const float* src_rh;
+    const float* x_rh;
+    int src_up, src_down, x_up, x_down;
 };
+
+// One plane's rows beyond the slice (height sharding): rows -up .. -1 are
+// p[0 .. up), rows H .. H + down - 1 are p[up .. up + down).
+struct RowHalo {
+    const float* p;
+    int up, down;
+};
+
+__device__ __forceinline__ RowHalo row_halo(const float* base, int64_t plane, int up, int down, int W)
+{
+    return RowHalo{base + plane * (up + down) * W, up, down};
+}
 
 // One tile: its plane and channel, and the rows and columns it covers.  The
 // last tile of a column is moved up to end at row H (i0 = H - TH) so every
@@ -169,9 +186,16 @@ struct Tile {
     // contiguously, which is exactly main[] since TW = 4 TX.  Rows outside
     // the plane have offsets outside the buffer (negative offsets wrap to
     // huge ones) and read as zeros.
-    __device__ static void load_main(float* buf, const float* plane, int H, int W, int i0, int j0, int tid)
+    // ROWH (height sharding): rows above and below the slice come from its
+    // row halo instead; those loads are issued by the lanes they concern, so
+    // each piece of LDS is still written by exactly one load.
+    template <bool ROWH>
+    __device__ static void load_main(float* buf, const float* plane, int H, int W, int i0, int j0, int tid,
+                                     const RowHalo& rh)
     {
         const i32x4 rs = plane_rsrc(plane, H * W * 4);
+        i32x4 rsh{};
+        if constexpr (ROWH) rsh = plane_rsrc(rh.p, (rh.up + rh.down) * W * 4);
         const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
         for (int k = 0; k < (NLOAD + NWAVE - 1) / NWAVE; ++k) {
@@ -179,8 +203,21 @@ struct Tile {
             if (m < NLOAD) {
                 const int f = m * 64 + lane;
                 const int rr = f / TX, q = f - rr * TX;
-                const int off = ((i0 - P + rr) * W + j0 + 4 * q) * 4;
-                if (f < PIECES) dma16(rs, buf + m * 256, off);
+                const int r = i0 - P + rr;
+                const int off = (r * W + j0 + 4 * q) * 4;
+                if (f < PIECES) {
+                    if constexpr (ROWH) {
+                        if ((unsigned)r < (unsigned)H) {
+                            dma16(rs, buf + m * 256, off);
+                        } else {
+                            // halo row; rows beyond it fall outside the halo buffer and read zeros
+                            const int hr = r < 0 ? rh.up + r : rh.up + (r - H);
+                            dma16(rsh, buf + m * 256, (hr * W + j0 + 4 * q) * 4);
+                        }
+                    } else {
+                        dma16(rs, buf + m * 256, off);
+                    }
+                }
             }
         }
     }
@@ -188,9 +225,10 @@ struct Tile {
     // Side columns: ordinary loads into registers, written by put_side().
     // Without a halo (HALO false: the interior half of a split convolution)
     // the columns beyond the slice are zeros.
-    template <bool HALO>
+    // ROWH: rows beyond the slice take their columns from its row halo.
+    template <bool HALO, bool ROWH>
     __device__ static void load_side(Side& S, const float* __restrict__ xp, const float* __restrict__ hp,
-                                     int H, int W, int i0, int j0, int tid)
+                                     int H, int W, int i0, int j0, int tid, const RowHalo& rh)
     {
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
@@ -207,6 +245,10 @@ struct Tile {
                 } else {
                     S.s[k] = xp[(int64_t)r * W + xcol];
                 }
+            } else if constexpr (ROWH) {
+                const int hr = r < 0 ? rh.up + r : rh.up + (r - H);
+                if (idx < LH * 2 * P && xcol >= 0 && xcol < W && hr >= 0 && hr < rh.up + rh.down)
+                    S.s[k] = rh.p[(int64_t)hr * W + xcol];
             }
         }
     }
@@ -374,8 +416,8 @@ __device__ __forceinline__ void store_rows(float* out, const TileIdx& d, int H, 
             make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
 }
 
-template <int K, int TX, int TY, int RH, bool FLIP, bool HALO>
-__global__ void __launch_bounds__(TX * TY)
+template <int K, int TX, int TY, int RH, bool FLIP, bool HALO, bool ROWH>
+__global__ void __launch_bounds__(TX * TY) __attribute__((amdgpu_waves_per_eu(4)))
 dw_conv_kernel(DwArgs a)
 {
     using T = Tile<K, TX, TY, RH>;
@@ -387,9 +429,11 @@ dw_conv_kernel(DwArgs a)
     const int64_t HW = (int64_t)a.H * a.W;
     auto issue = [&](int t, float* b) {
         const TileIdx e = decode_plane_major(a, t, T::TH, T::TW);
-        T::load_main(b, a.src + e.plane * HW, a.H, a.W, e.i0, e.j0, tid);
-        T::template load_side<HALO>(S, a.src + e.plane * HW, HALO ? a.src_h + (int64_t)e.plane * a.H * (2 * P) : nullptr, a.H, a.W, e.i0,
-                     e.j0, tid);
+        const RowHalo rh = ROWH ? row_halo(a.src_rh, e.plane, a.src_up, a.src_down, a.W) : RowHalo{};
+        T::template load_main<ROWH>(b, a.src + e.plane * HW, a.H, a.W, e.i0, e.j0, tid, rh);
+        T::template load_side<HALO, ROWH>(S, a.src + e.plane * HW,
+                                          HALO ? a.src_h + (int64_t)e.plane * a.H * (2 * P) : nullptr, a.H, a.W,
+                                          e.i0, e.j0, tid, rh);
     };
     int t = blockIdx.x;
     if (t >= a.ntiles) return;
@@ -453,7 +497,7 @@ __device__ __forceinline__ void flush_sum(float (*red)[NV + 2], int gtid, float*
 
 // grad_weight partial (stand-alone): the input tile comes through LDS, the
 // thread's grad_output block straight from global memory.
-template <int K, int TX, int TY, int RH, bool HALO>
+template <int K, int TX, int TY, int RH, bool HALO, bool ROWH>
 __global__ void __launch_bounds__(TX * TY) __attribute__((amdgpu_waves_per_eu(3)))
 dw_wgrad_kernel(DwArgs a)
 {
@@ -476,9 +520,11 @@ dw_wgrad_kernel(DwArgs a)
     if (beg >= end) return;
     auto issue = [&](int t, float* b) {
         const TileIdx e = decode_channel_major(a, t, T::TH, T::TW);
-        T::load_main(b, a.x + e.plane * HW, a.H, a.W, e.i0, e.j0, tid);
-        T::template load_side<HALO>(S, a.x + e.plane * HW, HALO ? a.x_h + (int64_t)e.plane * a.H * (2 * P) : nullptr, a.H, a.W, e.i0, e.j0,
-                     tid);
+        const RowHalo rh = ROWH ? row_halo(a.x_rh, e.plane, a.x_up, a.x_down, a.W) : RowHalo{};
+        T::template load_main<ROWH>(b, a.x + e.plane * HW, a.H, a.W, e.i0, e.j0, tid, rh);
+        T::template load_side<HALO, ROWH>(S, a.x + e.plane * HW,
+                                          HALO ? a.x_h + (int64_t)e.plane * a.H * (2 * P) : nullptr, a.H, a.W,
+                                          e.i0, e.j0, tid, rh);
         const float* gp = a.g + e.plane * HW + e.j0 + 4 * tx;
 #pragma unroll
         for (int i = 0; i < RH; ++i) {
@@ -522,7 +568,7 @@ dw_wgrad_kernel(DwArgs a)
 // grad_output tile's centre.  Both halves walk the same tiles with the same
 // barriers in the same order (two loops with identical barrier sequences, so
 // each half's registers are allocated on their own).
-template <int K, int TX, int TY, int RH, bool HALO>
+template <int K, int TX, int TY, int RH, bool HALO, bool ROWH>
 __global__ void __launch_bounds__(2 * TX * TY) __attribute__((amdgpu_waves_per_eu(4)))
 dw_bwd_kernel(DwArgs a)
 {
@@ -546,12 +592,16 @@ dw_bwd_kernel(DwArgs a)
     if (beg >= end) return;
     const float* const src = wgrad_half ? a.x : a.src;
     const float* const src_h = wgrad_half ? a.x_h : a.src_h;
+    const float* const src_rh = wgrad_half ? a.x_rh : a.src_rh;
+    const int up = wgrad_half ? a.x_up : a.src_up, down = wgrad_half ? a.x_down : a.src_down;
     float (*const mybuf)[T::FLOATS] = wgrad_half ? bufx : bufg;
     auto issue = [&](int t, float* b) {
         const TileIdx e = decode_channel_major(a, t, T::TH, T::TW);
-        T::load_main(b, src + e.plane * HW, a.H, a.W, e.i0, e.j0, tid);
-        T::template load_side<HALO>(S, src + e.plane * HW, HALO ? src_h + (int64_t)e.plane * a.H * (2 * P) : nullptr, a.H, a.W, e.i0, e.j0,
-                     tid);
+        const RowHalo rh = ROWH ? row_halo(src_rh, e.plane, up, down, a.W) : RowHalo{};
+        T::template load_main<ROWH>(b, src + e.plane * HW, a.H, a.W, e.i0, e.j0, tid, rh);
+        T::template load_side<HALO, ROWH>(S, src + e.plane * HW,
+                                          HALO ? src_h + (int64_t)e.plane * a.H * (2 * P) : nullptr, a.H, a.W,
+                                          e.i0, e.j0, tid, rh);
     };
     issue(beg, mybuf[0]);
 
@@ -709,12 +759,12 @@ hipError_t launch_reduce(const DwArgs& a, int grid, float* gw, float* gb, hipStr
 #define SSCNN_DW_BWD_SHAPES(X) X(16, 16, 2) X(16, 16, 1) X(8, 32, 2) X(8, 32, 1) X(8, 16, 1) X(4, 64, 1) \
     X(4, 16, 1)
 
-template <int K, bool FLIP, bool HALO>
+template <int K, bool FLIP, bool HALO, bool ROWH>
 hipError_t launch_conv(DwArgs a, int planes, DwShape sh, hipStream_t st)
 {
 #define SSCNN_DW_CONV(TX, TY, RH)                                                  \
     if (sh.tx == TX && sh.ty == TY && sh.rh == RH) {                               \
-        auto kern = dw_conv_kernel<K, TX, TY, RH, FLIP, HALO>;                     \
+        auto kern = dw_conv_kernel<K, TX, TY, RH, FLIP, HALO, ROWH>;               \
         set_tiles(a, planes, TX, TY, RH);                                          \
         const int grid = persistent_grid(kern, TX * TY, a.ntiles);                 \
         hipLaunchKernelGGL(kern, dim3(grid), dim3(TX * TY), 0, st, a);             \
@@ -725,12 +775,12 @@ hipError_t launch_conv(DwArgs a, int planes, DwShape sh, hipStream_t st)
     return hipErrorInvalidValue;
 }
 
-template <int K, bool HALO>
+template <int K, bool HALO, bool ROWH>
 hipError_t launch_wgrad(DwArgs a, int planes, DwShape sh, float* gw, float* gb, hipStream_t st)
 {
 #define SSCNN_DW_WGRAD(TX, TY, RH)                                                 \
     if (sh.tx == TX && sh.ty == TY && sh.rh == RH) {                               \
-        auto kern = dw_wgrad_kernel<K, TX, TY, RH, HALO>;                          \
+        auto kern = dw_wgrad_kernel<K, TX, TY, RH, HALO, ROWH>;                    \
         set_tiles(a, planes, TX, TY, RH);                                          \
         const int grid = persistent_grid(kern, TX * TY, a.ntiles);                 \
         hipLaunchKernelGGL(kern, dim3(grid), dim3(TX * TY), 0, st, a);             \
@@ -742,12 +792,12 @@ hipError_t launch_wgrad(DwArgs a, int planes, DwShape sh, float* gw, float* gb, 
     return hipErrorInvalidValue;
 }
 
-template <int K, bool HALO>
+template <int K, bool HALO, bool ROWH>
 hipError_t launch_bwd(DwArgs a, int planes, DwShape sh, float* gw, float* gb, hipStream_t st)
 {
 #define SSCNN_DW_BWD(TX, TY, RH)                                                   \
     if (sh.tx == TX && sh.ty == TY && sh.rh == RH) {                               \
-        auto kern = dw_bwd_kernel<K, TX, TY, RH, HALO>;                            \
+        auto kern = dw_bwd_kernel<K, TX, TY, RH, HALO, ROWH>;                      \
         set_tiles(a, planes, TX, TY, RH);                                          \
         const int grid = persistent_grid(kern, 2 * TX * TY, a.ntiles);             \
         hipLaunchKernelGGL(kern, dim3(grid), dim3(2 * TX * TY), 0, st, a);         \
@@ -796,9 +846,9 @@ hipError_t launch_dw_fwd(const Geom& g, const float* x, const float* xh, const f
     const int planes = g.n * g.ci;
     const DwShape sh = pick_shape(g.h, g.wl);
     switch (g.k) {
-        case 3: return xh ? launch_conv<3, false, true>(a, planes, sh, st) : launch_conv<3, false, false>(a, planes, sh, st);
-        case 5: return xh ? launch_conv<5, false, true>(a, planes, sh, st) : launch_conv<5, false, false>(a, planes, sh, st);
-        default: return xh ? launch_conv<7, false, true>(a, planes, sh, st) : launch_conv<7, false, false>(a, planes, sh, st);
+        case 3: return xh ? launch_conv<3, false, true, false>(a, planes, sh, st) : launch_conv<3, false, false, false>(a, planes, sh, st);
+        case 5: return xh ? launch_conv<5, false, true, false>(a, planes, sh, st) : launch_conv<5, false, false, false>(a, planes, sh, st);
+        default: return xh ? launch_conv<7, false, true, false>(a, planes, sh, st) : launch_conv<7, false, false, false>(a, planes, sh, st);
     }
 }
 
@@ -810,9 +860,9 @@ hipError_t launch_dw_bwd_input(const Geom& g, const float* gy, const float* gyh,
     const int planes = g.n * g.ci;
     const DwShape sh = pick_shape(g.h, g.wl);
     switch (g.k) {
-        case 3: return gyh ? launch_conv<3, true, true>(a, planes, sh, st) : launch_conv<3, true, false>(a, planes, sh, st);
-        case 5: return gyh ? launch_conv<5, true, true>(a, planes, sh, st) : launch_conv<5, true, false>(a, planes, sh, st);
-        default: return gyh ? launch_conv<7, true, true>(a, planes, sh, st) : launch_conv<7, true, false>(a, planes, sh, st);
+        case 3: return gyh ? launch_conv<3, true, true, false>(a, planes, sh, st) : launch_conv<3, true, false, false>(a, planes, sh, st);
+        case 5: return gyh ? launch_conv<5, true, true, false>(a, planes, sh, st) : launch_conv<5, true, false, false>(a, planes, sh, st);
+        default: return gyh ? launch_conv<7, true, true, false>(a, planes, sh, st) : launch_conv<7, true, false, false>(a, planes, sh, st);
     }
 }
 
@@ -824,9 +874,9 @@ hipError_t launch_dw_bwd_weight(const Geom& g, const float* x, const float* xh, 
     const int planes = g.n * g.ci;
     const DwShape sh = pick_shape(g.h, g.wl);
     switch (g.k) {
-        case 3: return xh ? launch_wgrad<3, true>(a, planes, sh, gw, gb, st) : launch_wgrad<3, false>(a, planes, sh, gw, gb, st);
-        case 5: return xh ? launch_wgrad<5, true>(a, planes, sh, gw, gb, st) : launch_wgrad<5, false>(a, planes, sh, gw, gb, st);
-        default: return xh ? launch_wgrad<7, true>(a, planes, sh, gw, gb, st) : launch_wgrad<7, false>(a, planes, sh, gw, gb, st);
+        case 3: return xh ? launch_wgrad<3, true, false>(a, planes, sh, gw, gb, st) : launch_wgrad<3, false, false>(a, planes, sh, gw, gb, st);
+        case 5: return xh ? launch_wgrad<5, true, false>(a, planes, sh, gw, gb, st) : launch_wgrad<5, false, false>(a, planes, sh, gw, gb, st);
+        default: return xh ? launch_wgrad<7, true, false>(a, planes, sh, gw, gb, st) : launch_wgrad<7, false, false>(a, planes, sh, gw, gb, st);
     }
 }
 
@@ -839,9 +889,70 @@ hipError_t launch_dw_bwd(const Geom& g, const float* x, const float* xh, const f
     const DwShape sh = bwd_shape(g.h, g.wl);
     if ((xh == nullptr) != (gyh == nullptr)) return hipErrorInvalidValue;   // both halos or neither
     switch (g.k) {
-        case 3: return xh ? launch_bwd<3, true>(a, planes, sh, gw, gb, st) : launch_bwd<3, false>(a, planes, sh, gw, gb, st);
-        case 5: return xh ? launch_bwd<5, true>(a, planes, sh, gw, gb, st) : launch_bwd<5, false>(a, planes, sh, gw, gb, st);
-        default: return xh ? launch_bwd<7, true>(a, planes, sh, gw, gb, st) : launch_bwd<7, false>(a, planes, sh, gw, gb, st);
+        case 3: return xh ? launch_bwd<3, true, false>(a, planes, sh, gw, gb, st) : launch_bwd<3, false, false>(a, planes, sh, gw, gb, st);
+        case 5: return xh ? launch_bwd<5, true, false>(a, planes, sh, gw, gb, st) : launch_bwd<5, false, false>(a, planes, sh, gw, gb, st);
+        default: return xh ? launch_bwd<7, true, false>(a, planes, sh, gw, gb, st) : launch_bwd<7, false, false>(a, planes, sh, gw, gb, st);
+    }
+}
+
+// Height sharding: rows beyond the slice's top and bottom from its row halos
+// (N*C, up + down, W); the slice spans the whole width, so no column halo.
+hipError_t launch_dw_fwd_rows(const Geom& g, const float* x, const float* x_rh, int up, int down,
+                              const float* w, const float* b, float* y, hipStream_t st)
+{
+    DwArgs a = make_args(g);
+    a.src = x; a.src_rh = x_rh; a.src_up = up; a.src_down = down; a.w = w; a.b = b; a.out = y;
+    const int planes = g.n * g.ci;
+    const DwShape sh = pick_shape(g.h, g.wl);
+    switch (g.k) {
+        case 3: return launch_conv<3, false, false, true>(a, planes, sh, st);
+        case 5: return launch_conv<5, false, false, true>(a, planes, sh, st);
+        default: return launch_conv<7, false, false, true>(a, planes, sh, st);
+    }
+}
+
+hipError_t launch_dw_bwd_input_rows(const Geom& g, const float* gy, const float* gy_rh, int up, int down,
+                                    const float* w, float* gx, hipStream_t st)
+{
+    DwArgs a = make_args(g);
+    a.src = gy; a.src_rh = gy_rh; a.src_up = up; a.src_down = down; a.w = w; a.b = nullptr; a.out = gx;
+    const int planes = g.n * g.ci;
+    const DwShape sh = pick_shape(g.h, g.wl);
+    switch (g.k) {
+        case 3: return launch_conv<3, true, false, true>(a, planes, sh, st);
+        case 5: return launch_conv<5, true, false, true>(a, planes, sh, st);
+        default: return launch_conv<7, true, false, true>(a, planes, sh, st);
+    }
+}
+
+hipError_t launch_dw_bwd_weight_rows(const Geom& g, const float* x, const float* x_rh, int up, int down,
+                                     const float* gy, float* gw, float* gb, void* ws, hipStream_t st)
+{
+    DwArgs a = make_args(g);
+    a.x = x; a.x_rh = x_rh; a.x_up = up; a.x_down = down; a.g = gy; a.ws = static_cast<float*>(ws);
+    const int planes = g.n * g.ci;
+    const DwShape sh = pick_shape(g.h, g.wl);
+    switch (g.k) {
+        case 3: return launch_wgrad<3, false, true>(a, planes, sh, gw, gb, st);
+        case 5: return launch_wgrad<5, false, true>(a, planes, sh, gw, gb, st);
+        default: return launch_wgrad<7, false, true>(a, planes, sh, gw, gb, st);
+    }
+}
+
+hipError_t launch_dw_bwd_rows(const Geom& g, const float* x, const float* x_rh, int x_up, int x_down,
+                              const float* gy, const float* gy_rh, int g_up, int g_down, const float* w, float* gx,
+                              float* gw, float* gb, void* ws, hipStream_t st)
+{
+    DwArgs a = make_args(g);
+    a.src = gy; a.src_rh = gy_rh; a.src_up = g_up; a.src_down = g_down;
+    a.x = x; a.x_rh = x_rh; a.x_up = x_up; a.x_down = x_down;
+    a.w = w; a.out = gx; a.ws = static_cast<float*>(ws);
+    const int planes = g.n * g.ci;
+    const DwShape sh = bwd_shape(g.h, g.wl);
+    switch (g.k) {
+        case 3: return launch_bwd<3, false, true>(a, planes, sh, gw, gb, st);
+        case 5: return launch_bwd<5, false, true>(a, planes, sh, gw, gb, st);
+        default: return launch_bwd<7, false, true>(a, planes, sh, gw, gb, st);
     }
 }
 
