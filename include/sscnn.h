@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSCNN_ABI_VERSION 4
+#define SSCNN_ABI_VERSION 5
 
 /* Status codes. */
 #define SSCNN_OK 0
@@ -360,6 +360,61 @@ int sscnn_hconv_bwd(const sscnn_hconv_t *conv, const float *x, const float *x_ha
  */
 int sscnn_partial_reduce(const float *const *parts, int32_t nparts, int64_t count,
                          float *out, void *stream);
+
+/*
+ * The ConvNeXt block's other steps, on one shard's activations.  They look at
+ * one pixel (or one sample) at a time, so a shard runs them on its own slice
+ * with no halo; their weight gradients are per-shard partial sums, reduced
+ * with sscnn_partial_reduce like the convolutions'.  The distributed DropPath
+ * layer keeps its random draws consistent across shards (kwkr.cn retelling,
+ * sections 3.1 and 6.1; NVIDIA blog, ConvNeXt-XL paragraph: DropPath's
+ * Bernoulli draws must agree on every GPU).  Shapes: x, y, dy, dx and h are
+ * (n, c, h, w) slices; the calls need n, c, h, w >= 1, and the two layer-scale
+ * calls also h * w % 4 == 0.
+ */
+
+/* LayerNorm over channels (each pixel normalised over its c values):
+ *   y = (x - mean) * rstd * gamma[c] + beta[c],  rstd = 1 / sqrt(var + eps),
+ * with the population variance.  mean and rstd (n, h, w) are written for the
+ * backward.  gamma, beta: (c). */
+int sscnn_layernorm_fwd(int32_t n, int32_t c, int32_t h, int32_t w, float eps, const float *x,
+                        const float *gamma, const float *beta, float *y, float *mean, float *rstd,
+                        void *stream);
+
+/* Its gradients from the saved mean / rstd: dx (nullable: skipped), and the
+ * partial sums over this slice's pixels dgamma = sum dy * xhat and
+ * dbeta = sum dy (each nullable). */
+int sscnn_layernorm_bwd(int32_t n, int32_t c, int32_t h, int32_t w, const float *x, const float *dy,
+                        const float *gamma, const float *mean, const float *rstd, float *dx,
+                        float *dgamma, float *dbeta, void *stream);
+
+/* GELU, y = x * Phi(x) (the exact form, Phi the standard normal CDF), and its
+ * gradient dx = dy * (Phi(x) + x * phi(x)); count elements. */
+int sscnn_gelu_fwd(int64_t count, const float *x, float *y, void *stream);
+int sscnn_gelu_bwd(int64_t count, const float *x, const float *dy, float *dx, void *stream);
+
+/* DropPath (stochastic depth) factors for n samples: scales[i] = 1 / keep_prob
+ * if sample i is kept, else 0; keep_prob >= 1 gives all ones.  Sample i is
+ * kept when the first word of Philox4x32-10 (Salmon et al., SC'11) of the
+ * counter (i, offset low, offset high, 0) under the key (seed low, seed high)
+ * is below floor(keep_prob * 2^32) (at most 2^32 - 1).  The factors depend on
+ * (seed, offset, i) only, so every shard computes the same ones; a caller
+ * gives each DropPath call a distinct offset.  0 < keep_prob required. */
+int sscnn_droppath_scales(uint64_t seed, uint64_t offset, int32_t n, double keep_prob,
+                          float *scales, void *stream);
+
+/* The block's tail: out = x + scales[n] * (gamma[c] * hb) (layer scale, then
+ * DropPath, then the residual).  scales (n) nullable: all ones. */
+int sscnn_layer_scale_residual_fwd(int32_t n, int32_t c, int32_t h, int32_t w, const float *x,
+                                   const float *hb, const float *gamma, const float *scales,
+                                   float *out, void *stream);
+
+/* Its gradients: dh = (scales[n] * dout) * gamma[c] (nullable: skipped) and
+ * the partial dgamma = sum over this slice of (scales[n] * dout) * hb
+ * (nullable); the gradient of x is dout itself. */
+int sscnn_layer_scale_residual_bwd(int32_t n, int32_t c, int32_t h, int32_t w, const float *hb,
+                                   const float *dout, const float *gamma, const float *scales,
+                                   float *dh, float *dgamma, void *stream);
 
 /* Static text for a status code. */
 const char *sscnn_status_string(int status);

@@ -1,10 +1,12 @@
 // api.cpp -- the C ABI of libsscnn (declared in include/sscnn.h): host-side
 // validation of every argument, then dispatch to the kernel family that fits
 // the layer.  Nothing here allocates device memory.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 
+#include "blockops.h"
 #include "depthwise.h"
 #include "edge.h"
 #include "internal.h"
@@ -332,6 +334,130 @@ int sscnn_partial_reduce(const float* const* parts, int32_t nparts, int64_t coun
     }
     return hip_status(launch_partial_reduce(parts, nparts, count, out, (hipStream_t)stream),
                       "partial_reduce launch");
+}
+
+// --- the ConvNeXt block's other steps ------------------------------------------
+
+}  // extern "C"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 38;
+
+int check_dims(int32_t n, int32_t c, int32_t h, int32_t w, bool quads)
+{
+    if (n < 1 || c < 1 || h < 1 || w < 1)
+        return fail(SSCNN_EINVAL, "dims n=%d c=%d h=%d w=%d must all be >= 1", n, c, h, w);
+    if ((int64_t)n * c * h * w >= kMaxElems) return fail(SSCNN_EINVAL, "tensor of n*c*h*w elements is too large");
+    if (quads && ((int64_t)h * w) % 4) return fail(SSCNN_EINVAL, "h*w=%lld is not a multiple of 4", (long long)h * w);
+    return SSCNN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sscnn_layernorm_fwd(int32_t n, int32_t c, int32_t h, int32_t w, float eps, const float* x, const float* gamma,
+                        const float* beta, float* y, float* mean, float* rstd, void* stream)
+{
+    TRY(check_dims(n, c, h, w, false));
+    if (!(eps > 0.f) || !std::isfinite(eps)) return fail(SSCNN_EINVAL, "eps must be positive and finite");
+    TRY(need(x, "x"));
+    TRY(need(gamma, "gamma"));
+    TRY(need(beta, "beta"));
+    TRY(need(y, "y"));
+    TRY(need(mean, "mean"));
+    TRY(need(rstd, "rstd"));
+    if (mean == rstd || (const float*)mean == x || (const float*)rstd == x || mean == y || rstd == y)
+        return fail(SSCNN_EINVAL, "mean / rstd alias each other or a tensor");
+    return hip_status(launch_layernorm_fwd(n, c, (int64_t)h * w, eps, x, gamma, beta, y, mean, rstd,
+                                           (hipStream_t)stream),
+                      "layernorm_fwd launch");
+}
+
+int sscnn_layernorm_bwd(int32_t n, int32_t c, int32_t h, int32_t w, const float* x, const float* dy,
+                        const float* gamma, const float* mean, const float* rstd, float* dx, float* dgamma,
+                        float* dbeta, void* stream)
+{
+    TRY(check_dims(n, c, h, w, false));
+    TRY(need(x, "x"));
+    TRY(need(dy, "dy"));
+    TRY(need(gamma, "gamma"));
+    TRY(need(mean, "mean"));
+    TRY(need(rstd, "rstd"));
+    TRY(optional(dx, "dx"));
+    TRY(optional(dgamma, "dgamma"));
+    TRY(optional(dbeta, "dbeta"));
+    if (dx && ((const float*)dx == x || (const float*)dx == dy))
+        return fail(SSCNN_EINVAL, "dx aliases x or dy");
+    if (dgamma && dgamma == dbeta) return fail(SSCNN_EINVAL, "dgamma aliases dbeta");
+    return hip_status(launch_layernorm_bwd(n, c, (int64_t)h * w, x, dy, gamma, mean, rstd, dx, dgamma, dbeta,
+                                           (hipStream_t)stream),
+                      "layernorm_bwd launch");
+}
+
+int sscnn_gelu_fwd(int64_t count, const float* x, float* y, void* stream)
+{
+    if (count < 0 || count >= kMaxElems) return fail(SSCNN_EINVAL, "count=%lld out of range", (long long)count);
+    if (count == 0) return SSCNN_OK;
+    TRY(need(x, "x"));
+    TRY(need(y, "y"));
+    return hip_status(launch_gelu_fwd(count, x, y, (hipStream_t)stream), "gelu_fwd launch");
+}
+
+int sscnn_gelu_bwd(int64_t count, const float* x, const float* dy, float* dx, void* stream)
+{
+    if (count < 0 || count >= kMaxElems) return fail(SSCNN_EINVAL, "count=%lld out of range", (long long)count);
+    if (count == 0) return SSCNN_OK;
+    TRY(need(x, "x"));
+    TRY(need(dy, "dy"));
+    TRY(need(dx, "dx"));
+    return hip_status(launch_gelu_bwd(count, x, dy, dx, (hipStream_t)stream), "gelu_bwd launch");
+}
+
+int sscnn_droppath_scales(uint64_t seed, uint64_t offset, int32_t n, double keep_prob, float* scales, void* stream)
+{
+    if (n < 0) return fail(SSCNN_EINVAL, "n=%d is negative", n);
+    if (!(keep_prob > 0.0) || !std::isfinite(keep_prob))
+        return fail(SSCNN_EINVAL, "keep_prob must be positive and finite");
+    if (n == 0) return SSCNN_OK;
+    TRY(need(scales, "scales"));
+    const bool draw = keep_prob < 1.0;
+    const double t = std::floor(keep_prob * 4294967296.0);
+    const uint32_t thr = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+    const float inv = (float)(1.0 / keep_prob);
+    return hip_status(launch_droppath_scales(n, seed, offset, thr, inv, draw, scales, (hipStream_t)stream),
+                      "droppath_scales launch");
+}
+
+int sscnn_layer_scale_residual_fwd(int32_t n, int32_t c, int32_t h, int32_t w, const float* x, const float* hb,
+                                   const float* gamma, const float* scales, float* out, void* stream)
+{
+    TRY(check_dims(n, c, h, w, true));
+    TRY(need(x, "x"));
+    TRY(need(hb, "hb"));
+    TRY(need(gamma, "gamma"));
+    TRY(optional(scales, "scales"));
+    TRY(need(out, "out"));
+    return hip_status(launch_scale_residual_fwd(n, c, (int64_t)h * w, x, hb, gamma, scales, out, (hipStream_t)stream),
+                      "layer_scale_residual_fwd launch");
+}
+
+int sscnn_layer_scale_residual_bwd(int32_t n, int32_t c, int32_t h, int32_t w, const float* hb, const float* dout,
+                                   const float* gamma, const float* scales, float* dh, float* dgamma, void* stream)
+{
+    TRY(check_dims(n, c, h, w, true));
+    TRY(need(hb, "hb"));
+    TRY(need(dout, "dout"));
+    TRY(need(gamma, "gamma"));
+    TRY(optional(scales, "scales"));
+    TRY(optional(dh, "dh"));
+    TRY(optional(dgamma, "dgamma"));
+    if (dh && dgamma && ((const float*)dh == hb || (const float*)dh == dout))
+        return fail(SSCNN_EINVAL, "dh aliases hb or dout while dgamma is requested");
+    return hip_status(launch_scale_residual_bwd(n, c, (int64_t)h * w, hb, dout, gamma, scales, dh, dgamma,
+                                                (hipStream_t)stream),
+                      "layer_scale_residual_bwd launch");
 }
 
 // --- split convolution: interior calls (halo read as zeros) and edge calls ---

@@ -1,0 +1,335 @@
+// blockops.hip -- the ConvNeXt block's steps other than its convolutions, on
+// one shard's NCHW activations: LayerNorm over channels, GELU, layer scale
+// with DropPath and the residual add, and the DropPath factors themselves.
+// None of them looks across pixels, so a W- (or H-) shard runs them on its
+// own slice with no halo; their weight gradients are per-shard partial sums,
+// reduced like the convolutions' (kwkr.cn retelling, section 3.1: the
+// DropPath layer is distributed with its random state kept consistent).
+//
+//  * LayerNorm: one thread per pixel walks its C values (stride H*W, so the
+//    threads of a wave read consecutive pixels of one channel row: coalesced),
+//    twice for the mean and the variance and once to write; the backward
+//    recomputes x-hat from the saved mean and rstd.  The per-channel weight
+//    and bias gradients are a second kernel, one workgroup per channel,
+//    reduced in a fixed order (bitwise reproducible).
+//  * GELU: elementwise, 4 values per thread, with the device library's erff
+//    and expf.
+//  * DropPath factors: Philox4x32-10 (Salmon et al., SC'11) of the counter
+//    (sample, offset low, offset high, 0) under the key (seed low, seed high),
+//    kept when the first word is below a threshold the host computes; every
+//    shard gets the same factors because they depend on the sample index
+//    only (NVIDIA blog "Perception Model Training for Autonomous Vehicles with
+//    Tensor Parallelism": DropPath's Bernoulli draws must agree across GPUs).
+#include "internal.h"
+#include "blockops.h"
+
+namespace sscnn {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---- LayerNorm over channels ------------------------------------------------
+
+__global__ void __launch_bounds__(kThreads)
+ln_fwd_kernel(const float* __restrict__ x, const float* __restrict__ gamma, const float* __restrict__ beta,
+              float* __restrict__ y, float* __restrict__ mean_out, float* __restrict__ rstd_out, int C, int64_t HW,
+              int64_t npix, float eps)
+{
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t >= npix) return;
+    const int64_t n = t / HW, p = t - n * HW;
+    const float* xp = x + n * C * HW + p;
+    float s = 0.f;
+#pragma unroll 8
+    for (int c = 0; c < C; ++c) s += xp[c * HW];
+    const float mean = s / (float)C;
+    float v = 0.f;
+#pragma unroll 8
+    for (int c = 0; c < C; ++c) {
+        const float d = xp[c * HW] - mean;
+        v = __builtin_fmaf(d, d, v);
+    }
+    const float rstd = 1.f / sqrtf(v / (float)C + eps);
+    float* yp = y + n * C * HW + p;
+#pragma unroll 8
+    for (int c = 0; c < C; ++c) yp[c * HW] = __builtin_fmaf((xp[c * HW] - mean) * rstd, gamma[c], beta[c]);
+    mean_out[t] = mean;
+    rstd_out[t] = rstd;
+}
+
+// dx = rstd * (dxhat - mean_c(dxhat) - xhat * mean_c(dxhat * xhat)), dxhat = dy * gamma.
+// No implicit FMA contraction here: dxhat is then the same rounded product in
+// both passes (with one channel dx is exactly 0); the explicit FMAs stay.
+__global__ void __launch_bounds__(kThreads)
+ln_bwd_kernel(const float* __restrict__ x, const float* __restrict__ dy, const float* __restrict__ gamma,
+              const float* __restrict__ mean_in, const float* __restrict__ rstd_in, float* __restrict__ dx, int C,
+              int64_t HW, int64_t npix)
+{
+#pragma clang fp contract(off)
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t >= npix) return;
+    const int64_t n = t / HW, p = t - n * HW;
+    const int64_t base = n * C * HW + p;
+    const float mean = mean_in[t], rstd = rstd_in[t];
+    float a = 0.f, b = 0.f;
+#pragma unroll 8
+    for (int c = 0; c < C; ++c) {
+        const float g = dy[base + c * HW] * gamma[c];
+        a += g;
+        b = __builtin_fmaf(g, (x[base + c * HW] - mean) * rstd, b);
+    }
+    a /= (float)C;
+    b /= (float)C;
+#pragma unroll 8
+    for (int c = 0; c < C; ++c) {
+        const float g = dy[base + c * HW] * gamma[c];
+        const float xh = (x[base + c * HW] - mean) * rstd;
+        dx[base + c * HW] = rstd * (g - a - xh * b);
+    }
+}
+
+// Fixed-order sum of a workgroup's per-thread values (LDS tree).
+__device__ __forceinline__ float block_sum(float v, float* red)
+{
+    red[threadIdx.x] = v;
+    __syncthreads();
+#pragma unroll
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+        __syncthreads();
+    }
+    const float r = red[0];
+    __syncthreads();
+    return r;
+}
+
+// dgamma[c] = sum over the pixels of dy * xhat, dbeta[c] = sum of dy; one workgroup per channel.
+__global__ void __launch_bounds__(kThreads)
+ln_params_kernel(const float* __restrict__ x, const float* __restrict__ dy, const float* __restrict__ mean_in,
+                 const float* __restrict__ rstd_in, float* __restrict__ dgamma, float* __restrict__ dbeta, int N,
+                 int C, int64_t HW)
+{
+    __shared__ float red[kThreads];
+    const int c = blockIdx.x;
+    float sg = 0.f, sb = 0.f;
+    for (int n = 0; n < N; ++n) {
+        const int64_t base = ((int64_t)n * C + c) * HW;
+        for (int64_t p = threadIdx.x; p < HW; p += kThreads) {
+            const float d = dy[base + p];
+            sg = __builtin_fmaf(d, (x[base + p] - mean_in[n * HW + p]) * rstd_in[n * HW + p], sg);
+            sb += d;
+        }
+    }
+    sg = block_sum(sg, red);
+    sb = block_sum(sb, red);
+    if (threadIdx.x == 0) {
+        if (dgamma) dgamma[c] = sg;
+        if (dbeta) dbeta[c] = sb;
+    }
+}
+
+// ---- GELU ---------------------------------------------------------------------
+
+__device__ __forceinline__ float gelu(float v)
+{
+    return 0.5f * v * (1.f + erff(v * 0.70710678118654752f));
+}
+
+__device__ __forceinline__ float gelu_grad(float v)
+{
+    const float cdf = 0.5f * (1.f + erff(v * 0.70710678118654752f));
+    const float pdf = 0.39894228040143268f * expf(-0.5f * v * v);
+    return __builtin_fmaf(v, pdf, cdf);
+}
+
+__global__ void __launch_bounds__(kThreads)
+gelu_fwd_kernel(const float* __restrict__ x, float* __restrict__ y, int64_t count)
+{
+    const int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x;   // group of 4 values
+    const int64_t i = q * 4;
+    if (i + 4 <= count) {
+        const float4 v = *reinterpret_cast<const float4*>(x + i);
+        *reinterpret_cast<float4*>(y + i) = make_float4(gelu(v.x), gelu(v.y), gelu(v.z), gelu(v.w));
+    } else {
+        for (int64_t k = i; k < count; ++k) y[k] = gelu(x[k]);
+    }
+}
+
+__global__ void __launch_bounds__(kThreads)
+gelu_bwd_kernel(const float* __restrict__ x, const float* __restrict__ dy, float* __restrict__ dx, int64_t count)
+{
+    const int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t i = q * 4;
+    if (i + 4 <= count) {
+        const float4 v = *reinterpret_cast<const float4*>(x + i);
+        const float4 d = *reinterpret_cast<const float4*>(dy + i);
+        *reinterpret_cast<float4*>(dx + i) = make_float4(d.x * gelu_grad(v.x), d.y * gelu_grad(v.y),
+                                                         d.z * gelu_grad(v.z), d.w * gelu_grad(v.w));
+    } else {
+        for (int64_t k = i; k < count; ++k) dx[k] = dy[k] * gelu_grad(x[k]);
+    }
+}
+
+// ---- DropPath factors (Philox4x32-10) -----------------------------------------------
+
+__device__ __forceinline__ uint32_t philox_first_word(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                      uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    }
+    return c0;
+}
+
+__global__ void __launch_bounds__(kThreads)
+droppath_kernel(int n, uint32_t seed_lo, uint32_t seed_hi, uint32_t off_lo, uint32_t off_hi, uint32_t thr,
+                float inv_keep, int draw, float* __restrict__ scales)
+{
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    if (!draw) {
+        scales[i] = 1.f;
+        return;
+    }
+    const uint32_t w = philox_first_word((uint32_t)i, off_lo, off_hi, 0u, seed_lo, seed_hi);
+    scales[i] = w < thr ? inv_keep : 0.f;
+}
+
+// ---- layer scale, DropPath and the residual --------------------------------------------
+
+// out = x + s[n] * (gamma[c] * h), 4 values per thread (HW a multiple of 4).
+__global__ void __launch_bounds__(kThreads)
+scale_residual_fwd_kernel(const float* __restrict__ x, const float* __restrict__ h, const float* __restrict__ gamma,
+                          const float* __restrict__ scales, float* __restrict__ out, int C, int64_t HW,
+                          int64_t count)
+{
+    const int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+    if (i >= count) return;
+    const int64_t nc = i / HW;
+    const int c = (int)(nc % C);
+    const float s = scales ? scales[nc / C] : 1.f, g = gamma[c];
+    const float4 xv = *reinterpret_cast<const float4*>(x + i);
+    const float4 hv = *reinterpret_cast<const float4*>(h + i);
+    *reinterpret_cast<float4*>(out + i) = make_float4(__builtin_fmaf(s, g * hv.x, xv.x), __builtin_fmaf(s, g * hv.y, xv.y),
+                                                      __builtin_fmaf(s, g * hv.z, xv.z), __builtin_fmaf(s, g * hv.w, xv.w));
+}
+
+// dh = (s[n] * dout) * gamma[c]
+__global__ void __launch_bounds__(kThreads)
+scale_residual_bwd_kernel(const float* __restrict__ dout, const float* __restrict__ gamma,
+                          const float* __restrict__ scales, float* __restrict__ dh, int C, int64_t HW, int64_t count)
+{
+    const int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+    if (i >= count) return;
+    const int64_t nc = i / HW;
+    const int c = (int)(nc % C);
+    const float s = scales ? scales[nc / C] : 1.f, g = gamma[c];
+    const float4 d = *reinterpret_cast<const float4*>(dout + i);
+    *reinterpret_cast<float4*>(dh + i) = make_float4(s * d.x * g, s * d.y * g, s * d.z * g, s * d.w * g);
+}
+
+// dgamma[c] = sum over n and pixels of (s[n] * dout) * h; one workgroup per channel.
+__global__ void __launch_bounds__(kThreads)
+scale_params_kernel(const float* __restrict__ h, const float* __restrict__ dout, const float* __restrict__ scales,
+                    float* __restrict__ dgamma, int N, int C, int64_t HW)
+{
+    __shared__ float red[kThreads];
+    const int c = blockIdx.x;
+    float sg = 0.f;
+    for (int n = 0; n < N; ++n) {
+        const float s = scales ? scales[n] : 1.f;
+        const int64_t base = ((int64_t)n * C + c) * HW;
+        for (int64_t p = threadIdx.x; p < HW; p += kThreads) sg = __builtin_fmaf(s * dout[base + p], h[base + p], sg);
+    }
+    sg = block_sum(sg, red);
+    if (threadIdx.x == 0) dgamma[c] = sg;
+}
+
+int blocks(int64_t work)
+{
+    return (int)((work + kThreads - 1) / kThreads);
+}
+
+}  // namespace
+
+hipError_t launch_layernorm_fwd(int n, int c, int64_t hw, float eps, const float* x, const float* gamma,
+                                const float* beta, float* y, float* mean, float* rstd, hipStream_t st)
+{
+    const int64_t npix = (int64_t)n * hw;
+    hipLaunchKernelGGL(ln_fwd_kernel, dim3(blocks(npix)), dim3(kThreads), 0, st, x, gamma, beta, y, mean, rstd, c, hw,
+                       npix, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_layernorm_bwd(int n, int c, int64_t hw, const float* x, const float* dy, const float* gamma,
+                                const float* mean, const float* rstd, float* dx, float* dgamma, float* dbeta,
+                                hipStream_t st)
+{
+    const int64_t npix = (int64_t)n * hw;
+    if (dx) {
+        hipLaunchKernelGGL(ln_bwd_kernel, dim3(blocks(npix)), dim3(kThreads), 0, st, x, dy, gamma, mean, rstd, dx, c,
+                           hw, npix);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (dgamma || dbeta)
+        hipLaunchKernelGGL(ln_params_kernel, dim3(c), dim3(kThreads), 0, st, x, dy, mean, rstd, dgamma, dbeta, n, c,
+                           hw);
+    return hipGetLastError();
+}
+
+hipError_t launch_gelu_fwd(int64_t count, const float* x, float* y, hipStream_t st)
+{
+    hipLaunchKernelGGL(gelu_fwd_kernel, dim3(blocks((count + 3) / 4)), dim3(kThreads), 0, st, x, y, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_gelu_bwd(int64_t count, const float* x, const float* dy, float* dx, hipStream_t st)
+{
+    hipLaunchKernelGGL(gelu_bwd_kernel, dim3(blocks((count + 3) / 4)), dim3(kThreads), 0, st, x, dy, dx, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_droppath_scales(int n, uint64_t seed, uint64_t offset, uint32_t thr, float inv_keep, bool draw,
+                                  float* scales, hipStream_t st)
+{
+    hipLaunchKernelGGL(droppath_kernel, dim3(blocks(n)), dim3(kThreads), 0, st, n, (uint32_t)seed,
+                       (uint32_t)(seed >> 32), (uint32_t)offset, (uint32_t)(offset >> 32), thr, inv_keep, draw ? 1 : 0,
+                       scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_residual_fwd(int n, int c, int64_t hw, const float* x, const float* h, const float* gamma,
+                                     const float* scales, float* out, hipStream_t st)
+{
+    const int64_t count = (int64_t)n * c * hw;
+    hipLaunchKernelGGL(scale_residual_fwd_kernel, dim3(blocks(count / 4)), dim3(kThreads), 0, st, x, h, gamma, scales,
+                       out, c, hw, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_residual_bwd(int n, int c, int64_t hw, const float* h, const float* dout, const float* gamma,
+                                     const float* scales, float* dh, float* dgamma, hipStream_t st)
+{
+    const int64_t count = (int64_t)n * c * hw;
+    if (dh) {
+        hipLaunchKernelGGL(scale_residual_bwd_kernel, dim3(blocks(count / 4)), dim3(kThreads), 0, st, dout, gamma,
+                           scales, dh, c, hw, count);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (dgamma)
+        hipLaunchKernelGGL(scale_params_kernel, dim3(c), dim3(kThreads), 0, st, h, dout, scales, dgamma, n, c, hw);
+    return hipGetLastError();
+}
+
+}  // namespace sscnn

@@ -29,6 +29,8 @@ EXPORTED = (
     "sscnn_conv_bwd_interior",
     "sscnn_hconv_init", "sscnn_row_halo_gather", "sscnn_hconv_fwd", "sscnn_hconv_bwd_input",
     "sscnn_hconv_bwd_weight_workspace_bytes", "sscnn_hconv_bwd_weight_partial", "sscnn_hconv_bwd",
+    "sscnn_layernorm_fwd", "sscnn_layernorm_bwd", "sscnn_gelu_fwd", "sscnn_gelu_bwd", "sscnn_droppath_scales",
+    "sscnn_layer_scale_residual_fwd", "sscnn_layer_scale_residual_bwd",
 )
 
 
@@ -131,6 +133,14 @@ def lib() -> ctypes.CDLL:
         L.sscnn_hconv_bwd_weight_workspace_bytes.restype = ctypes.c_size_t
         L.sscnn_hconv_bwd_weight_partial.argtypes = [HP, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.sscnn_hconv_bwd.argtypes = [HP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        i32, i64, u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+        L.sscnn_layernorm_fwd.argtypes = [i32, i32, i32, i32, ctypes.c_float] + [_vp] * 7
+        L.sscnn_layernorm_bwd.argtypes = [i32, i32, i32, i32] + [_vp] * 9
+        L.sscnn_gelu_fwd.argtypes = [i64, _vp, _vp, _vp]
+        L.sscnn_gelu_bwd.argtypes = [i64, _vp, _vp, _vp, _vp]
+        L.sscnn_droppath_scales.argtypes = [u64, u64, i32, ctypes.c_double, _vp, _vp]
+        L.sscnn_layer_scale_residual_fwd.argtypes = [i32, i32, i32, i32] + [_vp] * 6
+        L.sscnn_layer_scale_residual_bwd.argtypes = [i32, i32, i32, i32] + [_vp] * 7
         L.sscnn_status_string.argtypes = [ctypes.c_int]
         L.sscnn_status_string.restype = ctypes.c_char_p
         L.sscnn_last_error.restype = ctypes.c_char_p
@@ -140,7 +150,9 @@ def lib() -> ctypes.CDLL:
                   "sscnn_conv_bwd_input_interior", "sscnn_conv_bwd_input_edge",
                   "sscnn_conv_bwd_weight_partial_interior", "sscnn_conv_bwd_weight_edge",
                   "sscnn_conv_bwd_interior", "sscnn_hconv_init", "sscnn_row_halo_gather", "sscnn_hconv_fwd",
-                  "sscnn_hconv_bwd_input", "sscnn_hconv_bwd_weight_partial", "sscnn_hconv_bwd"):
+                  "sscnn_hconv_bwd_input", "sscnn_hconv_bwd_weight_partial", "sscnn_hconv_bwd",
+                  "sscnn_layernorm_fwd", "sscnn_layernorm_bwd", "sscnn_gelu_fwd", "sscnn_gelu_bwd",
+                  "sscnn_droppath_scales", "sscnn_layer_scale_residual_fwd", "sscnn_layer_scale_residual_bwd"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -411,6 +423,74 @@ def partial_reduce(parts: Sequence, out, stream=None):
     ptrs = (_vp * len(parts))(*[_ptr(p, (n,), f"parts[{i}]") for i, p in enumerate(parts)])
     _check(lib().sscnn_partial_reduce(ptrs, len(parts), n, _ptr(out, (n,), "out"), _stream(stream)),
            "partial_reduce")
+
+
+# --- the ConvNeXt block's other steps ----------------------------------------------
+
+def _nchw(t, name):
+    if t is None or t.dim() != 4:
+        raise ValueError(f"{name}: expected an (N, C, H, W) tensor")
+    return tuple(t.shape)
+
+
+def layernorm_fwd(x, gamma, beta, y, mean, rstd, eps: float = 1e-6, stream=None):
+    """sscnn_layernorm_fwd: LayerNorm over the channels of an (N, C, H, W) slice;
+    mean / rstd receive (N, H, W)."""
+    n, c, h, w = _nchw(x, "x")
+    _check(lib().sscnn_layernorm_fwd(n, c, h, w, eps, _ptr(x, (n, c, h, w), "x"), _ptr(gamma, (c,), "gamma"),
+                                     _ptr(beta, (c,), "beta"), _ptr(y, (n, c, h, w), "y"),
+                                     _ptr(mean, (n, h, w), "mean"), _ptr(rstd, (n, h, w), "rstd"), _stream(stream)),
+           "layernorm_fwd")
+
+
+def layernorm_bwd(x, dy, gamma, mean, rstd, dx, dgamma, dbeta, stream=None):
+    """sscnn_layernorm_bwd: dx (or None) and this slice's partial dgamma / dbeta (or None)."""
+    n, c, h, w = _nchw(x, "x")
+    _check(lib().sscnn_layernorm_bwd(n, c, h, w, _ptr(x, (n, c, h, w), "x"), _ptr(dy, (n, c, h, w), "dy"),
+                                     _ptr(gamma, (c,), "gamma"), _ptr(mean, (n, h, w), "mean"),
+                                     _ptr(rstd, (n, h, w), "rstd"), _ptr(dx, (n, c, h, w), "dx", optional=True),
+                                     _ptr(dgamma, (c,), "dgamma", optional=True),
+                                     _ptr(dbeta, (c,), "dbeta", optional=True), _stream(stream)),
+           "layernorm_bwd")
+
+
+def gelu_fwd(x, y, stream=None):
+    """sscnn_gelu_fwd on tensors of the same shape."""
+    _check(lib().sscnn_gelu_fwd(x.numel(), _ptr(x, tuple(x.shape), "x"), _ptr(y, tuple(x.shape), "y"),
+                                _stream(stream)), "gelu_fwd")
+
+
+def gelu_bwd(x, dy, dx, stream=None):
+    shape = tuple(x.shape)
+    _check(lib().sscnn_gelu_bwd(x.numel(), _ptr(x, shape, "x"), _ptr(dy, shape, "dy"), _ptr(dx, shape, "dx"),
+                                _stream(stream)), "gelu_bwd")
+
+
+def droppath_scales(seed: int, offset: int, keep_prob: float, scales, stream=None):
+    """sscnn_droppath_scales: per-sample DropPath factors into scales (n,)."""
+    n = scales.numel()
+    _check(lib().sscnn_droppath_scales(seed, offset, n, keep_prob, _ptr(scales, (n,), "scales"), _stream(stream)),
+           "droppath_scales")
+
+
+def layer_scale_residual_fwd(x, hb, gamma, scales, out, stream=None):
+    """sscnn_layer_scale_residual_fwd: out = x + scales[n] * (gamma[c] * hb); scales may be None."""
+    n, c, h, w = _nchw(x, "x")
+    sh = (n, c, h, w)
+    _check(lib().sscnn_layer_scale_residual_fwd(n, c, h, w, _ptr(x, sh, "x"), _ptr(hb, sh, "hb"),
+                                                _ptr(gamma, (c,), "gamma"), _ptr(scales, (n,), "scales", optional=True),
+                                                _ptr(out, sh, "out"), _stream(stream)), "layer_scale_residual_fwd")
+
+
+def layer_scale_residual_bwd(hb, dout, gamma, scales, dh, dgamma, stream=None):
+    """sscnn_layer_scale_residual_bwd: dh (or None) and this slice's partial dgamma (or None)."""
+    n, c, h, w = _nchw(hb, "hb")
+    sh = (n, c, h, w)
+    _check(lib().sscnn_layer_scale_residual_bwd(n, c, h, w, _ptr(hb, sh, "hb"), _ptr(dout, sh, "dout"),
+                                                _ptr(gamma, (c,), "gamma"), _ptr(scales, (n,), "scales", optional=True),
+                                                _ptr(dh, sh, "dh", optional=True),
+                                                _ptr(dgamma, (c,), "dgamma", optional=True), _stream(stream)),
+           "layer_scale_residual_bwd")
 
 
 def new_workspace(conv: Conv, device="cuda"):

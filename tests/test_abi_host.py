@@ -328,3 +328,43 @@ def test_hconv_calls_validate_before_launching():
     p = sscnn.hconv_init(1, 3, 16, 16, 16, 4, 4, 0, 1, 1, 4)
     assert (p.halo_u, p.halo_d, p.ghalo_u, p.ghalo_d) == (0, 0, 0, 0)
     assert L.sscnn_row_halo_gather(ctypes.byref(p), 0, F, F, None, None) == sscnn.OK
+
+
+def test_block_op_calls_validate_before_launching():
+    """The ConvNeXt block's other steps check shapes, pointers and aliasing on
+    the host and launch nothing when they fail; empty work returns OK."""
+    L = sscnn.lib()
+    F, G = FAKE, FAKE + 4096
+    eps = ctypes.c_float(1e-6)
+    # LayerNorm: dims, eps, required pointers, misalignment, aliasing of the saved statistics
+    assert L.sscnn_layernorm_fwd(0, 4, 2, 2, eps, F, F, F, F, F + 64, F + 128, None) == sscnn.EINVAL
+    assert L.sscnn_layernorm_fwd(1, 4, 2, 2, ctypes.c_float(0.0), F, F, F, G, F + 64, F + 128, None) == sscnn.EINVAL
+    assert L.sscnn_layernorm_fwd(1, 4, 2, 2, eps, None, F, F, G, F + 64, F + 128, None) == sscnn.EINVAL
+    assert L.sscnn_layernorm_fwd(1, 4, 2, 2, eps, F + 4, F, F, G, F + 64, F + 128, None) == sscnn.EINVAL
+    assert L.sscnn_layernorm_fwd(1, 4, 2, 2, eps, F, F, F, G, F + 64, F + 64, None) == sscnn.EINVAL
+    assert L.sscnn_layernorm_bwd(1, 4, 2, 2, F, G, F, F, F, F, None, None, None) == sscnn.EINVAL   # dx is x
+    assert L.sscnn_layernorm_bwd(1, 4, 2, 2, F, G, F, F, F, None, F + 64, F + 64, None) == sscnn.EINVAL
+    # GELU: negative count; zero count is a no-op even with no pointers
+    assert L.sscnn_gelu_fwd(-1, F, F, None) == sscnn.EINVAL
+    assert L.sscnn_gelu_fwd(0, None, None, None) == sscnn.OK
+    assert L.sscnn_gelu_bwd(16, F, None, F, None) == sscnn.EINVAL
+    # DropPath factors: keep_prob in (0, inf), n >= 0
+    assert L.sscnn_droppath_scales(1, 0, 4, 0.0, F, None) == sscnn.EINVAL
+    assert L.sscnn_droppath_scales(1, 0, 4, float("nan"), F, None) == sscnn.EINVAL
+    assert L.sscnn_droppath_scales(1, 0, -1, 0.5, F, None) == sscnn.EINVAL
+    assert L.sscnn_droppath_scales(1, 0, 0, 0.5, None, None) == sscnn.OK
+    assert L.sscnn_droppath_scales(1, 0, 4, 0.5, None, None) == sscnn.EINVAL
+    # layer scale + residual: h*w a multiple of 4, required pointers, dh aliasing what dgamma reads
+    assert L.sscnn_layer_scale_residual_fwd(1, 4, 3, 3, F, F, F, None, G, None) == sscnn.EINVAL
+    assert L.sscnn_layer_scale_residual_fwd(1, 4, 2, 2, F, None, F, None, G, None) == sscnn.EINVAL
+    assert L.sscnn_layer_scale_residual_bwd(1, 4, 2, 2, F, G, F, None, G, F + 64, None) == sscnn.EINVAL
+    assert "aliases" in sscnn.last_error()
+
+
+def test_block_op_bindings_refuse_host_tensors():
+    import torch
+    x = torch.zeros(1, 4, 2, 2)
+    with pytest.raises(ValueError):
+        sscnn.layernorm_fwd(x, torch.ones(4), torch.zeros(4), x.clone(), torch.zeros(1, 2, 2), torch.zeros(1, 2, 2))
+    with pytest.raises(ValueError):
+        sscnn.gelu_fwd(x, x.clone())
