@@ -184,3 +184,153 @@ class ShardedConv2d(torch.nn.Module):
     def extra_repr(self):
         return (f"{self.in_channels}, {self.out_channels}, kernel_size={self.kernel_size}, stride={self.stride}, "
                 f"padding={self.padding}, groups={self.groups}, bias={self.bias is not None}, dim={self.dim}")
+
+
+# --- the ConvNeXt block on sharded activations ---------------------------------------
+#
+# The block (depthwise 7x7 -> LayerNorm over channels -> 1x1 expansion -> GELU
+# -> 1x1 projection -> layer scale -> DropPath -> residual) with every step in
+# the library: the convolutions through ShardedConv2d, the rest through the
+# per-pixel block calls, which need no halo.  Weight gradients of the per-pixel
+# steps are partial sums per shard, reduced like the convolutions'.  DropPath
+# draws its per-sample factors from a counter-based generator keyed by (seed,
+# call counter), so every shard drops the same samples (kwkr.cn retelling,
+# sections 3.1 and 6.1; NVIDIA blog, ConvNeXt-XL paragraph).
+
+def _zeros_if_none(gs, like):
+    return [torch.zeros_like(x) if g is None else g.contiguous() for g, x in zip(gs, like)]
+
+
+class _ChannelLayerNorm(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, weight, bias, eps, *xs):
+        ys, stats = [], []
+        for x in xs:
+            n, c, h, w = x.shape
+            y = torch.empty_like(x)
+            mean = torch.empty((n, h, w), device=x.device, dtype=torch.float32)
+            rstd = torch.empty((n, h, w), device=x.device, dtype=torch.float32)
+            sscnn.layernorm_fwd(x, weight, bias, y, mean, rstd, eps)
+            ys.append(y)
+            stats += [mean, rstd]
+        ctx.save_for_backward(weight, *xs, *stats)
+        ctx.nshards = len(xs)
+        return tuple(ys)
+
+    @staticmethod
+    def backward(ctx, *gys):
+        S = ctx.nshards
+        saved = ctx.saved_tensors
+        weight, xs, stats = saved[0], saved[1:1 + S], saved[1 + S:]
+        gys = _zeros_if_none(gys, xs)
+        c = weight.shape[0]
+        need_dx = any(ctx.needs_input_grad[3:])
+        dxs, parts = [], []
+        for s, x in enumerate(xs):
+            part = torch.empty(2 * c, device=x.device, dtype=torch.float32)
+            dx = torch.empty_like(x) if need_dx else None
+            sscnn.layernorm_bwd(x, gys[s], weight, stats[2 * s], stats[2 * s + 1], dx, part[:c], part[c:])
+            dxs.append(dx)
+            parts.append(part)
+        red = torch.empty(2 * c, device=weight.device, dtype=torch.float32)
+        sscnn.partial_reduce(parts, red)
+        return (red[:c], red[c:], None, *dxs)
+
+
+class _Gelu(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, *xs):
+        ys = []
+        for x in xs:
+            y = torch.empty_like(x)
+            sscnn.gelu_fwd(x, y)
+            ys.append(y)
+        ctx.save_for_backward(*xs)
+        return tuple(ys)
+
+    @staticmethod
+    def backward(ctx, *gys):
+        xs = ctx.saved_tensors
+        gys = _zeros_if_none(gys, xs)
+        dxs = []
+        for x, g in zip(xs, gys):
+            dx = torch.empty_like(x)
+            sscnn.gelu_bwd(x, g, dx)
+            dxs.append(dx)
+        return tuple(dxs)
+
+
+class _LayerScaleResidual(torch.autograd.Function):
+    """out_s = x_s + scales[n] * (gamma[c] * h_s) for every shard s."""
+
+    @staticmethod
+    def forward(ctx, gamma, scales, *xs_hs):
+        S = len(xs_hs) // 2
+        xs, hs = xs_hs[:S], xs_hs[S:]
+        outs = []
+        for x, h in zip(xs, hs):
+            out = torch.empty_like(x)
+            sscnn.layer_scale_residual_fwd(x, h, gamma, scales, out)
+            outs.append(out)
+        ctx.save_for_backward(gamma, *hs)
+        ctx.scales = scales
+        ctx.nshards = S
+        return tuple(outs)
+
+    @staticmethod
+    def backward(ctx, *gos):
+        S = ctx.nshards
+        saved = ctx.saved_tensors
+        gamma, hs = saved[0], saved[1:]
+        gos = _zeros_if_none(gos, hs)
+        c = gamma.shape[0]
+        dhs, parts = [], []
+        for h, go in zip(hs, gos):
+            dh = torch.empty_like(h)
+            part = torch.empty(c, device=h.device, dtype=torch.float32)
+            sscnn.layer_scale_residual_bwd(h, go, gamma, ctx.scales, dh, part)
+            dhs.append(dh)
+            parts.append(part)
+        dgamma = torch.empty(c, device=gamma.device, dtype=torch.float32)
+        sscnn.partial_reduce(parts, dgamma)
+        dxs = list(gos) if any(ctx.needs_input_grad[2:2 + S]) else [None] * S
+        return (dgamma, None, *dxs, *dhs)
+
+
+class ShardedConvNeXtBlock(torch.nn.Module):
+    """One ConvNeXt block over a list of S shards (W slices, or H slices with
+    dim=2): x + DropPath(gamma * pw2(GELU(pw1(LN(dw7x7(x)))))).
+
+    DropPath is active in training mode when drop_path > 0; its per-sample
+    factors come from sscnn_droppath_scales with this block's seed and a call
+    counter.  They depend on those two numbers and the sample index only, so a
+    shard on a GPU of its own would compute the same factors; here they are
+    computed once per call and used by every shard."""
+
+    def __init__(self, dim: int, drop_path: float = 0.0, layer_scale_init: float = 1e-6, eps: float = 1e-6,
+                 seed: int = 0, device="cuda", shard_dim: int = 3):
+        super().__init__()
+        if not 0.0 <= drop_path < 1.0:
+            raise ValueError("drop_path must be in [0, 1)")
+        self.dim, self.drop_path, self.eps, self.seed = dim, drop_path, eps, seed
+        self.dwconv = ShardedConv2d(dim, dim, 7, padding=3, groups=dim, device=device, dim=shard_dim)
+        self.norm_weight = torch.nn.Parameter(torch.ones(dim, device=device))
+        self.norm_bias = torch.nn.Parameter(torch.zeros(dim, device=device))
+        self.pwconv1 = ShardedConv2d(dim, 4 * dim, 1, device=device, dim=shard_dim)
+        self.pwconv2 = ShardedConv2d(4 * dim, dim, 1, device=device, dim=shard_dim)
+        self.gamma = torch.nn.Parameter(torch.full((dim,), layer_scale_init, device=device))
+        self.calls = 0      # DropPath call counter: the generator's offset
+
+    def forward(self, xs: Sequence[torch.Tensor]) -> List[torch.Tensor]:
+        xs = list(xs)
+        h = self.dwconv(xs)
+        h = list(_ChannelLayerNorm.apply(self.norm_weight, self.norm_bias, self.eps, *h))
+        h = self.pwconv1(h)
+        h = list(_Gelu.apply(*h))
+        h = self.pwconv2(h)
+        scales = None
+        if self.training and self.drop_path > 0.0:
+            scales = torch.empty(xs[0].shape[0], device=xs[0].device, dtype=torch.float32)
+            sscnn.droppath_scales(self.seed, self.calls, 1.0 - self.drop_path, scales)
+            self.calls += 1
+        return list(_LayerScaleResidual.apply(self.gamma, scales, *xs, *h))
