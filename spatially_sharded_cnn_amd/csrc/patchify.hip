@@ -3,7 +3,8 @@
 // the 4x4/4 stem and the 2x2/2 downsamples of the ConvNeXt-style stack that
 // the pages shard (NVIDIA blog "Perception Model Training for Autonomous
 // Vehicles with Tensor Parallelism", DTensor section: ConvNeXt-XL trained with
-// Shard(3) activations).  Such a layer needs no halo (its patches never
+// Shard(3) activations), and the 1x1 expansion and projection of the
+// ConvNeXt block (k = s = 1).  Such a layer needs no halo (its patches never
 // straddle a shard edge), and it is a matrix product after a reshape: with
 // K = (ci, kh, kw) and the output pixels p = (i, j) of one image,
 //     forward       Y[co][p]   = b[co] + sum_K W[co][K] * Xp[K][p]
@@ -109,7 +110,9 @@ struct Sub {
                 const bool okp = ok_k && pp < a.P;
                 const int i = pp / a.Wo, j = pp - i * a.Wo;
                 const float* s_ = xi + ((int64_t)ci * a.H + i * S + kh) * a.W + j * S;
-                if constexpr (S == 2) {
+                if constexpr (S == 1) {
+                    rb[r] = okp ? *s_ : 0.f;
+                } else if constexpr (S == 2) {
                     const float2 v = okp ? *reinterpret_cast<const float2*>(s_) : make_float2(0.f, 0.f);
                     rb[2 * r] = v.x; rb[2 * r + 1] = v.y;
                 } else {
@@ -162,7 +165,9 @@ struct Sub {
                 const int ci = gg / S, kh = gg - ci * S;
                 const bool ok = ok_k && gg * S < a.Kt;
                 const float* s_ = xi + ((int64_t)ci * a.H + i * S + kh) * a.W + (j0 + q) * S;
-                if constexpr (S == 2) {
+                if constexpr (S == 1) {
+                    rb[r] = ok ? *s_ : 0.f;
+                } else if constexpr (S == 2) {
                     const float2 v = ok ? *reinterpret_cast<const float2*>(s_) : make_float2(0.f, 0.f);
                     rb[2 * r] = v.x; rb[2 * r + 1] = v.y;
                 } else {
@@ -353,7 +358,12 @@ patch_kernel(PArgs a)
                     if (col < a.P && row < a.Kt) {
                         const int i = col / a.Wo, j = col - i * a.Wo;
                         float* dxi = a.out + (int64_t)outer * a.Ci * a.H * a.W;
-                        if constexpr (S == 4) {
+                        if constexpr (S == 1) {
+                            // rows are input channels: 4 channels of one pixel
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                dxi[((int64_t)(row + r) * a.H + i) * a.W + j] = acc[x][y][4 * q + r];
+                        } else if constexpr (S == 4) {
                             const int ci = row / 16, kh = (row / 4) % 4;
                             *reinterpret_cast<float4*>(dxi + ((int64_t)ci * a.H + i * 4 + kh) * a.W + j * 4) =
                                 make_float4(acc[x][y][4 * q], acc[x][y][4 * q + 1], acc[x][y][4 * q + 2],
@@ -466,7 +476,8 @@ int split_groups(int splits) { return splits > kOneStageMax ? (splits + kSlabsPe
 template <int MODE, int TM, int TN>
 hipError_t launch(const PArgs& a, int s, int grid, hipStream_t st)
 {
-    if (s == 2) hipLaunchKernelGGL((patch_kernel<MODE, 2, TM, TN>), dim3(grid), dim3(kNT), 0, st, a);
+    if (s == 1) hipLaunchKernelGGL((patch_kernel<MODE, 1, TM, TN>), dim3(grid), dim3(kNT), 0, st, a);
+    else if (s == 2) hipLaunchKernelGGL((patch_kernel<MODE, 2, TM, TN>), dim3(grid), dim3(kNT), 0, st, a);
     else hipLaunchKernelGGL((patch_kernel<MODE, 4, TM, TN>), dim3(grid), dim3(kNT), 0, st, a);
     return hipGetLastError();
 }
@@ -493,7 +504,7 @@ bool rows_narrow(int rows, const PArgs& a)
 bool patch_supported(const Geom& g)
 {
     const int64_t p = (int64_t)g.ho * g.wol;
-    return g.groups == 1 && g.pad == 0 && g.k == g.stride && (g.k == 2 || g.k == 4) &&
+    return g.groups == 1 && g.pad == 0 && g.k == g.stride && (g.k == 1 || g.k == 2 || g.k == 4) &&
            (g.ci * g.k * g.k) % kSub == 0 && g.co % kSub == 0 && g.wol % kSub == 0 && g.h == g.ho * g.k &&
            g.wl == g.wol * g.k && (int64_t)g.n * g.ci * g.h * g.wl < ((int64_t)1 << 31) &&
            (int64_t)g.n * g.co * p < ((int64_t)1 << 31);

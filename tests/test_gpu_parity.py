@@ -50,6 +50,9 @@ SMALL = [
     ("dw3_w64", 2, 6, 6, 23, 2 * 64, 3, 1, 1, 6, 2),
     ("dw5_w192_h70", 1, 5, 5, 70, 2 * 192, 5, 1, 2, 5, 2),
     ("dw7_h5_w64", 1, 3, 3, 5, 3 * 64, 7, 1, 3, 3, 3),
+    # 1x1 convolutions (the ConvNeXt block's expansion and projection) on the matrix cores
+    ("pw1x1_expand", 2, 32, 128, 12, 2 * 64, 1, 1, 0, 1, 2),
+    ("pw1x1_project", 1, 128, 32, 9, 4 * 16, 1, 1, 0, 1, 4),
     ("dense5x5_ragged", 2, 40, 72, 13, 3 * 37, 5, 1, 2, 1, 3),
     ("mfma5x5_ragged_channels", 2, 44, 72, 13, 3 * 36, 5, 1, 2, 1, 3),
     ("mfma5x5_two_segments", 1, 16, 20, 6, 2 * 132, 5, 1, 2, 1, 2),
