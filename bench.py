@@ -31,6 +31,7 @@ for the depthwise ones.
     python bench.py [--workload dw7_c256|dense5x5_c256|dense5x5_tiny] [--steps K] [--warmup W]
     python bench.py --workload dw7_c256_hshard   # the same step on a split along H (row halos)
     python bench.py --workload convnext_xl_w2048|convnext_xl_w4096   # the stack, per layer
+    python bench.py --workload convnext_block_c256   # a whole ConvNeXt block on the C=256 shard, per op
     python bench.py --summarize DIR [DIR ...] [--traffic-op OP --traffic-kernels "K1;K2"]
                                       # text summary of rocprofv3 output directories
 """
@@ -68,7 +69,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=WARMUP_DEFAULT)
     ap.add_argument("--workload", default="dw7_c256",
                     help="dw7_c256 (default), dense5x5_c256, dense5x5_tiny, dw7_c256_hshard (the same "
-                         "depthwise map split along H), or a stack: convnext_xl_w2048, convnext_xl_w4096")
+                         "depthwise map split along H), a stack: convnext_xl_w2048, convnext_xl_w4096, or a "
+                         "ConvNeXt block: convnext_block_c256")
     ap.add_argument("--sets", type=int, default=3, help="independent buffer sets rotated per step")
     ap.add_argument("--op-reps", type=int, default=20, help="back-to-back calls per operation timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -159,6 +161,8 @@ def main():
         return 1
     dev = "cuda"
     wl = workloads.WORKLOADS[args.workload]
+    if wl.kind == "block":
+        return block_bench(args, wl)
     if len(wl.layers) > 1:
         return stack_bench(args, wl)
     L = wl.layers[0]
@@ -490,6 +494,166 @@ def _layer_work(c, L):
             "reduce": ((c.num_shards + 1) * (w_b + b_b), 0),
             "halo_x": (2 * n * ci * h * (c.halo_l + c.halo_r) * f4, 0),
             "halo_g": (2 * n * co * ho * (c.ghalo_l + c.ghalo_r) * f4, 0)}
+
+
+def block_bench(args, wl):
+    """A ConvNeXt block on the measured shard (the depthwise, LayerNorm, 1x1,
+    GELU, 1x1, layer scale + DropPath + residual steps): one step is its
+    forward and its backward, each weight gradient reduced over the shards
+    like the convolutions'.  The neighbours' slices come from the global input
+    (and, for the grad_output halo of the depthwise layer, from a synthetic
+    gradient of the same shape); the other shards' partials are synthetic."""
+    import torch
+    from spatially_sharded_cnn_amd import sscnn, workloads
+
+    dev = "cuda"
+    S, s = wl.num_shards, wl.shard
+    steps = args.steps if args.steps != STEPS_DEFAULT else 20
+    warmup = args.warmup
+    T = workloads.generate(wl)
+    dw, pw1, pw2 = wl.layers
+    n, C, H, Wg = dw.in_shape
+    wl_ = Wg // S
+    P = H * wl_
+    keep = 0.9
+    rng = np.random.default_rng(wl.seed + 1)
+
+    def dev_t(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    def slices(a):
+        return [dev_t(a[..., i * wl_:(i + 1) * wl_]) for i in range(S)]
+
+    xs = slices(T.x)
+    g_dw_nbrs = slices(rng.standard_normal(T.x.shape).astype(np.float32))   # grad at the dw output, neighbours
+    gout = slices(T.g)[s]
+    convs = [sscnn.conv_init(n, L.ci, L.co, H, wl_, L.k, L.stride, L.pad, L.groups, s, S) for L in wl.layers]
+    cdw, c1, c2 = convs
+    wts = [dev_t(w) for w in T.weights]
+    bss = [dev_t(b) for b in T.biases]
+    ln_w, ln_b = dev_t(1 + 0.02 * rng.standard_normal(C)), dev_t(0.02 * rng.standard_normal(C))
+    gamma = dev_t(np.full(C, 1e-6))
+    nbr = lambda lst: (lst[s - 1] if s > 0 else None, lst[s + 1] if s < S - 1 else None)
+    e = lambda shape: torch.empty(shape, device=dev)
+    x = xs[s]
+    xh, y_dw, y_ln = e(cdw.halo_shape(sscnn.HALO_INPUT)), e(cdw.y_shape), e(cdw.y_shape)
+    mean, rstd = e((n, H, wl_)), e((n, H, wl_))
+    y1, a1, y2, scales, out = e(c1.y_shape), e(c1.y_shape), e(c2.y_shape), e((n,)), e(c2.y_shape)
+    dh2, da1, dy1, dln, ddw, dx = e(c2.y_shape), e(c1.y_shape), e(c1.y_shape), e(cdw.y_shape), e(cdw.y_shape), e(
+        cdw.x_shape)
+    gh = e(cdw.halo_shape(sscnn.HALO_GRAD_OUTPUT))
+    parts = {name: [e((cnt,)) for _ in range(S)] for name, cnt in
+             (("gamma", C), ("pw2", int(np.prod(c2.w_shape)) + c2.c_out), ("pw1", int(np.prod(c1.w_shape)) + c1.c_out),
+              ("ln", 2 * C), ("dw", int(np.prod(cdw.w_shape)) + cdw.c_out))}
+    for lst in parts.values():
+        for t in lst:
+            t.normal_()
+    reds = {k: e(v[0].shape) for k, v in parts.items()}
+    ws = {k: sscnn.new_workspace(c) for k, c in (("dw", cdw), ("pw1", c1), ("pw2", c2))}
+
+    def wparts(name, c):
+        t = parts[name][s]
+        nw = int(np.prod(c.w_shape))
+        return t[:nw].view(c.w_shape), t[nw:]
+
+    f4 = 4
+    act, act4 = n * C * P * f4, n * 4 * C * P * f4
+    wk = {k: _layer_work(c, L) for k, c, L in (("dw", cdw, dw), ("pw1", c1, pw1), ("pw2", c2, pw2))}
+    red_b = lambda name: ((S + 1) * parts[name][0].numel() * f4, 0)
+    # (name, call, algorithmic bytes, flops, dense)
+    ops = [
+        ("dw.halo_x", lambda: sscnn.halo_gather(cdw, sscnn.HALO_INPUT, *nbr(xs), xh), *wk["dw"]["halo_x"], False),
+        ("dw.fwd", lambda: sscnn.conv_fwd(cdw, x, xh, wts[0], bss[0], y_dw), *wk["dw"]["fwd"], False),
+        ("ln.fwd", lambda: sscnn.layernorm_fwd(y_dw, ln_w, ln_b, y_ln, mean, rstd), 2 * act + 2 * n * P * f4, 0,
+         False),
+        ("pw1.fwd", lambda: sscnn.conv_fwd(c1, y_ln, None, wts[1], bss[1], y1), *wk["pw1"]["fwd"], True),
+        ("gelu.fwd", lambda: sscnn.gelu_fwd(y1, a1), 2 * act4, 0, False),
+        ("pw2.fwd", lambda: sscnn.conv_fwd(c2, a1, None, wts[2], bss[2], y2), *wk["pw2"]["fwd"], True),
+        ("droppath", lambda: sscnn.droppath_scales(wl.seed, 0, keep, scales), n * f4, 0, False),
+        ("scale.fwd", lambda: sscnn.layer_scale_residual_fwd(x, y2, gamma, scales, out), 3 * act, 0, False),
+        ("scale.bwd", lambda: sscnn.layer_scale_residual_bwd(y2, gout, gamma, scales, dh2, parts["gamma"][s]),
+         3 * act, 0, False),
+        ("scale.reduce", lambda: sscnn.partial_reduce(parts["gamma"], reds["gamma"]), *red_b("gamma"), False),
+        ("pw2.bwd", lambda: sscnn.conv_bwd(c2, a1, None, dh2, None, wts[2], da1, *wparts("pw2", c2), ws["pw2"]),
+         *wk["pw2"]["bwd"], True),
+        ("pw2.reduce", lambda: sscnn.partial_reduce(parts["pw2"], reds["pw2"]), *red_b("pw2"), False),
+        ("gelu.bwd", lambda: sscnn.gelu_bwd(y1, da1, dy1), 3 * act4, 0, False),
+        ("pw1.bwd", lambda: sscnn.conv_bwd(c1, y_ln, None, dy1, None, wts[1], dln, *wparts("pw1", c1), ws["pw1"]),
+         *wk["pw1"]["bwd"], True),
+        ("pw1.reduce", lambda: sscnn.partial_reduce(parts["pw1"], reds["pw1"]), *red_b("pw1"), False),
+        ("ln.bwd", lambda: sscnn.layernorm_bwd(y_dw, dln, ln_w, mean, rstd, ddw, parts["ln"][s][:C],
+                                               parts["ln"][s][C:]), 3 * act + 2 * n * P * f4, 0, False),
+        ("ln.reduce", lambda: sscnn.partial_reduce(parts["ln"], reds["ln"]), *red_b("ln"), False),
+        ("dw.halo_g", lambda: sscnn.halo_gather(cdw, sscnn.HALO_GRAD_OUTPUT, *nbr(g_dw_nbrs), gh),
+         *wk["dw"]["halo_g"], False),
+        ("dw.bwd", lambda: sscnn.conv_bwd(cdw, x, xh, ddw, gh, wts[0], dx, *wparts("dw", cdw), ws["dw"]),
+         *wk["dw"]["bwd"], False),
+        ("dw.reduce", lambda: sscnn.partial_reduce(parts["dw"], reds["dw"]), *red_b("dw"), False),
+    ]
+
+    def step():
+        for op in ops:
+            op[1]()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = e0.elapsed_time(e1) / steps
+    spread = step_spread(lambda i: step(), steps)
+
+    rows, step_bytes, step_flops, dom = [], 0, 0, None
+    for name, f, b_, f_, dense in ops:
+        f()
+        torch.cuda.synchronize()
+        reps = max(2, min(args.op_reps, 20))
+        a0, a1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(reps):
+            f()
+        a1_.record()
+        torch.cuda.synchronize()
+        t = 1e3 * a0.elapsed_time(a1_) / reps
+        peak = MFMA_F32_PEAK_TFLOPS if dense else VALU_F32_PEAK_TFLOPS
+        t_mem, t_fl = b_ / (HBM_PEAK_GBS * 1e9), f_ / (peak * 1e12)
+        bound = ("mfma" if dense else "alu") if t_fl > t_mem else "hbm"
+        row = {"op": name, "us": round(t, 2), "bound": bound,
+               "gbs": round(b_ / (t * 1e-6) / 1e9, 1), "tflops": round(f_ / (t * 1e-6) / 1e12, 2),
+               "roofline_frac": round(max(t_mem, t_fl) / (t * 1e-6), 4)}
+        rows.append(row)
+        if not name.endswith(("halo_x", "halo_g")):
+            step_bytes += b_
+            step_flops += f_
+        if dom is None or t > dom[1]:
+            dom = (name, t, b_, f_, dense, bound)
+    name, t, b_, f_, dense, bound = dom
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(b_ / (t * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        peak = MFMA_F32_PEAK_TFLOPS if dense else VALU_F32_PEAK_TFLOPS
+        roof = {"bound": bound, "achieved": round(f_ / (t * 1e-6) / 1e12, 2), "peak": peak, "unit": "TFLOP/s"}
+    roof.update(frac=round(roof["achieved"] / roof["peak"], 4), traffic=None, op=name, avg_us=round(t, 2),
+                algorithmic_bytes=b_, algorithmic_flops=f_)
+    step_s = ms_per_step * 1e-3
+    out_d = {
+        "metric": METRIC, "value": round(step_bytes / step_s / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "shard": f"{s} of {S}",
+                   "shard_input": list(cdw.x_shape), "drop_path": round(1 - keep, 3)},
+        "tflops": round(step_flops / step_s / 1e12, 2), "step_bytes": step_bytes, "step_flops": step_flops,
+        "roofline": roof, "ops": rows, "step_spread": spread, "wall_s_timed": round(wall, 4),
+        "gpu_clocks": gpu_clocks(), "source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(out_d), flush=True)
+    return 0
 
 
 def stack_bench(args, wl):

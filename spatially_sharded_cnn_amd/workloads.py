@@ -53,6 +53,7 @@ class Workload:
     dist: str            # "uniform" or "normal"
     description: str
     axis: int = 3        # the sharded dimension: 3 = W (Shard(3)), 2 = H (Shard(2))
+    kind: str = "conv"   # "conv" (one layer or a stack of convolutions) or "block" (a ConvNeXt block)
 
     @property
     def x_shape(self):
@@ -102,6 +103,15 @@ WORKLOADS = {
         num_shards=4, shard=1, seed=1002, dist="normal",
         description="depthwise 7x7 s1 p3 C=256 split along H: shard (7,256,32,256) of the same (7,256,128,256) "
                     "map, 3-row halos", axis=2),
+    "convnext_block_c256": Workload(
+        "convnext_block_c256",
+        (_layer("dw", 256, 256, 7, 1, 3, 256, (7, 256, 128, 256), (7, 256, 128, 256)),
+         _layer("pw1", 256, 1024, 1, 1, 0, 1, (7, 256, 128, 256), (7, 1024, 128, 256)),
+         _layer("pw2", 1024, 256, 1, 1, 0, 1, (7, 1024, 128, 256), (7, 256, 128, 256))),
+        num_shards=4, shard=1, seed=1006, dist="normal",
+        description="ConvNeXt block at C=256 (dw 7x7, LayerNorm, 1x1 256->1024, GELU, 1x1 1024->256, layer "
+                    "scale, DropPath 0.1, residual): shard (7,256,128,64) of a (7,256,128,256) map",
+        kind="block"),
     "dense5x5_c256": Workload(
         "dense5x5_c256",
         (_layer("conv", 256, 256, 5, 1, 2, 1, (7, 256, 128, 512), (7, 256, 128, 512)),),
