@@ -100,6 +100,20 @@ struct Sub {
             }
             // B[k][p] = X[img][ci][i*s + kh][j*s + kw]: item (group, pixel) = s floats
             const float* xi = a.x + (int64_t)img * a.Ci * a.H * a.W;
+            if constexpr (S == 1) {
+                // 1x1: B[k][p] = X[img][k0 + k][p], 4 consecutive pixels (one row: Wo % 16 == 0) per item
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int idx = t + kNT * r;
+                    const int k = idx / 32, p4 = (idx % 32) * 4;
+                    const int pp = n0 + p4;
+                    const bool okp = ok_k && pp < a.P;
+                    const float4 v = okp ? *reinterpret_cast<const float4*>(xi + (int64_t)(k0 + k) * a.P + pp)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+                    rb[4 * r] = v.x; rb[4 * r + 1] = v.y; rb[4 * r + 2] = v.z; rb[4 * r + 3] = v.w;
+                }
+                return;
+            }
 #pragma unroll
             for (int r = 0; r < 8 / S; ++r) {
                 const int idx = t + kNT * r;
@@ -110,9 +124,7 @@ struct Sub {
                 const bool okp = ok_k && pp < a.P;
                 const int i = pp / a.Wo, j = pp - i * a.Wo;
                 const float* s_ = xi + ((int64_t)ci * a.H + i * S + kh) * a.W + j * S;
-                if constexpr (S == 1) {
-                    rb[r] = okp ? *s_ : 0.f;
-                } else if constexpr (S == 2) {
+                if constexpr (S == 2) {
                     const float2 v = okp ? *reinterpret_cast<const float2*>(s_) : make_float2(0.f, 0.f);
                     rb[2 * r] = v.x; rb[2 * r + 1] = v.y;
                 } else {
@@ -157,6 +169,20 @@ struct Sub {
             // B[q][n] = Xp[n0 + n][k0 + q]: the 16 pixels of the sub-chunk lie in one output row
             const int i = k0 / a.Wo, j0 = k0 - i * a.Wo;
             const float* xi = a.x + (int64_t)img * a.Ci * a.H * a.W;
+            if constexpr (S == 1) {
+                // 1x1: n is the input channel; 4 consecutive pixels per item
+#pragma unroll
+                for (int r = 0; r < TN / 64; ++r) {
+                    const int idx = t + kNT * r;
+                    const int nn = idx / 4, q4 = (idx % 4) * 4;
+                    const int ci = n0 + nn;
+                    const bool ok = ok_k && ci < a.Kt;
+                    const float4 v = ok ? *reinterpret_cast<const float4*>(xi + ((int64_t)ci * a.H + i) * a.W + j0 + q4)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+                    rb[4 * r] = v.x; rb[4 * r + 1] = v.y; rb[4 * r + 2] = v.z; rb[4 * r + 3] = v.w;
+                }
+                return;
+            }
 #pragma unroll
             for (int r = 0; r < TN / (16 * S); ++r) {
                 const int idx = t + kNT * r;
@@ -165,9 +191,7 @@ struct Sub {
                 const int ci = gg / S, kh = gg - ci * S;
                 const bool ok = ok_k && gg * S < a.Kt;
                 const float* s_ = xi + ((int64_t)ci * a.H + i * S + kh) * a.W + (j0 + q) * S;
-                if constexpr (S == 1) {
-                    rb[r] = ok ? *s_ : 0.f;
-                } else if constexpr (S == 2) {
+                if constexpr (S == 2) {
                     const float2 v = ok ? *reinterpret_cast<const float2*>(s_) : make_float2(0.f, 0.f);
                     rb[2 * r] = v.x; rb[2 * r + 1] = v.y;
                 } else {
@@ -187,6 +211,16 @@ struct Sub {
             const int m = t / TPR, kh = (t % TPR) * PER;
 #pragma unroll
             for (int e = 0; e < PER; ++e) As[(kh + e) * LDA + m] = ra[e];
+            if constexpr (S == 1) {
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int idx = t + kNT * r;
+                    const int k = idx / 32, p4 = (idx % 32) * 4;
+                    *reinterpret_cast<float4*>(Bs + k * LDB + p4) =
+                        make_float4(rb[4 * r], rb[4 * r + 1], rb[4 * r + 2], rb[4 * r + 3]);
+                }
+                return;
+            }
 #pragma unroll
             for (int r = 0; r < 8 / S; ++r) {
                 const int idx = t + kNT * r;
@@ -214,6 +248,16 @@ struct Sub {
                 const int m = idx / 4, q4 = (idx % 4) * 4;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) As[(q4 + e) * LDA + m] = ra[4 * r + e];
+            }
+            if constexpr (S == 1) {
+#pragma unroll
+                for (int r = 0; r < TN / 64; ++r) {
+                    const int idx = t + kNT * r;
+                    const int nn = idx / 4, q4 = (idx % 4) * 4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Bs[(q4 + e) * LDB + nn] = rb[4 * r + e];
+                }
+                return;
             }
 #pragma unroll
             for (int r = 0; r < TN / (16 * S); ++r) {
