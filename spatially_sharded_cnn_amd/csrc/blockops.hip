@@ -6,12 +6,12 @@
 // reduced like the convolutions' (kwkr.cn retelling, section 3.1: the
 // DropPath layer is distributed with its random state kept consistent).
 //
-//  * LayerNorm: one thread per pixel walks its C values (stride H*W, so the
-//    threads of a wave read consecutive pixels of one channel row: coalesced),
-//    twice for the mean and the variance and once to write; the backward
-//    recomputes x-hat from the saved mean and rstd.  The per-channel weight
-//    and bias gradients are a second kernel, one workgroup per channel,
-//    reduced in a fixed order (bitwise reproducible).
+//  * LayerNorm: a workgroup takes 64 consecutive pixels and its 4 waves split
+//    the C values of each (so every load is a 256-byte run of one channel
+//    row), twice for the mean and the variance and once to write; the
+//    backward recomputes x-hat from the saved mean and rstd.  The per-channel
+//    weight and bias gradients are a second kernel, one workgroup per
+//    channel, reduced in a fixed order (bitwise reproducible).
 //  * GELU: elementwise, 4 values per thread, with the device library's erff
 //    and expf.
 //  * DropPath factors: Philox4x32-10 (Salmon et al., SC'11) of the counter
@@ -29,72 +29,108 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---- LayerNorm over channels ------------------------------------------------
+//
+// A workgroup takes 64 consecutive pixels; its 4 waves split the channels
+// (wave g takes channels g, g + 4, ...), so every load is one 256-byte run of
+// a channel row and there are 4 times as many waves in flight as pixels / 64.
+// The per-pixel sums of the 4 waves meet in LDS and are added in wave order.
 
-__global__ void __launch_bounds__(kThreads)
+constexpr int kPix = 64, kGroups = 4;
+
+// sum over the 4 waves of v for this lane's pixel, in wave order
+__device__ __forceinline__ float pixel_sum(float v, float (*red)[kPix], int g, int lane)
+{
+    red[g][lane] = v;
+    __syncthreads();
+    const float r = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    __syncthreads();
+    return r;
+}
+
+__global__ void __launch_bounds__(kPix * kGroups)
 ln_fwd_kernel(const float* __restrict__ x, const float* __restrict__ gamma, const float* __restrict__ beta,
               float* __restrict__ y, float* __restrict__ mean_out, float* __restrict__ rstd_out, int C, int64_t HW,
               int64_t npix, float eps)
 {
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (t >= npix) return;
-    const int64_t n = t / HW, p = t - n * HW;
+    __shared__ float red[kGroups][kPix];
+    const int lane = threadIdx.x % kPix, g = threadIdx.x / kPix;
+    const int64_t t = (int64_t)blockIdx.x * kPix + lane;
+    const bool live = t < npix;
+    const int64_t tt = live ? t : 0;
+    const int64_t n = tt / HW, p = tt - n * HW;
     const float* xp = x + n * C * HW + p;
     float s = 0.f;
+    if (live) {
 #pragma unroll 8
-    for (int c = 0; c < C; ++c) s += xp[c * HW];
-    const float mean = s / (float)C;
-    float v = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < C; ++c) {
-        const float d = xp[c * HW] - mean;
-        v = __builtin_fmaf(d, d, v);
+        for (int c = g; c < C; c += kGroups) s += xp[c * HW];
     }
-    const float rstd = 1.f / sqrtf(v / (float)C + eps);
+    const float mean = pixel_sum(s, red, g, lane) / (float)C;
+    float v = 0.f;
+    if (live) {
+#pragma unroll 8
+        for (int c = g; c < C; c += kGroups) {
+            const float d = xp[c * HW] - mean;
+            v = __builtin_fmaf(d, d, v);
+        }
+    }
+    const float rstd = 1.f / sqrtf(pixel_sum(v, red, g, lane) / (float)C + eps);
+    if (!live) return;
     float* yp = y + n * C * HW + p;
 #pragma unroll 8
-    for (int c = 0; c < C; ++c) yp[c * HW] = __builtin_fmaf((xp[c * HW] - mean) * rstd, gamma[c], beta[c]);
-    mean_out[t] = mean;
-    rstd_out[t] = rstd;
+    for (int c = g; c < C; c += kGroups) yp[c * HW] = __builtin_fmaf((xp[c * HW] - mean) * rstd, gamma[c], beta[c]);
+    if (g == 0) {
+        mean_out[t] = mean;
+        rstd_out[t] = rstd;
+    }
 }
 
 // dx = rstd * (dxhat - mean_c(dxhat) - xhat * mean_c(dxhat * xhat)), dxhat = dy * gamma.
 // No implicit FMA contraction here: dxhat is then the same rounded product in
 // both passes (with one channel dx is exactly 0); the explicit FMAs stay.
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kPix * kGroups)
 ln_bwd_kernel(const float* __restrict__ x, const float* __restrict__ dy, const float* __restrict__ gamma,
               const float* __restrict__ mean_in, const float* __restrict__ rstd_in, float* __restrict__ dx, int C,
               int64_t HW, int64_t npix)
 {
 #pragma clang fp contract(off)
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (t >= npix) return;
-    const int64_t n = t / HW, p = t - n * HW;
+    __shared__ float red[kGroups][kPix];
+    const int lane = threadIdx.x % kPix, g = threadIdx.x / kPix;
+    const int64_t t = (int64_t)blockIdx.x * kPix + lane;
+    const bool live = t < npix;
+    const int64_t tt = live ? t : 0;
+    const int64_t n = tt / HW, p = tt - n * HW;
     const int64_t base = n * C * HW + p;
-    const float mean = mean_in[t], rstd = rstd_in[t];
+    const float mean = mean_in[tt], rstd = rstd_in[tt];
     float a = 0.f, b = 0.f;
+    if (live) {
 #pragma unroll 8
-    for (int c = 0; c < C; ++c) {
-        const float g = dy[base + c * HW] * gamma[c];
-        a += g;
-        b = __builtin_fmaf(g, (x[base + c * HW] - mean) * rstd, b);
+        for (int c = g; c < C; c += kGroups) {
+            const float gg = dy[base + c * HW] * gamma[c];
+            a += gg;
+            b = __builtin_fmaf(gg, (x[base + c * HW] - mean) * rstd, b);
+        }
     }
-    a /= (float)C;
-    b /= (float)C;
+    a = pixel_sum(a, red, g, lane) / (float)C;
+    b = pixel_sum(b, red, g, lane) / (float)C;
+    if (!live) return;
 #pragma unroll 8
-    for (int c = 0; c < C; ++c) {
-        const float g = dy[base + c * HW] * gamma[c];
+    for (int c = g; c < C; c += kGroups) {
+        const float gg = dy[base + c * HW] * gamma[c];
         const float xh = (x[base + c * HW] - mean) * rstd;
-        dx[base + c * HW] = rstd * (g - a - xh * b);
+        dx[base + c * HW] = rstd * (gg - a - xh * b);
     }
 }
 
-// Fixed-order sum of a workgroup's per-thread values (LDS tree).
+// Per-channel sums over every pixel: one 1024-thread workgroup per channel,
+// 4 loads in flight per thread, reduced in a fixed order (LDS tree).
+constexpr int kRedThreads = 1024;
+
 __device__ __forceinline__ float block_sum(float v, float* red)
 {
     red[threadIdx.x] = v;
     __syncthreads();
 #pragma unroll
-    for (int s = kThreads / 2; s > 0; s >>= 1) {
+    for (int s = kRedThreads / 2; s > 0; s >>= 1) {
         if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
         __syncthreads();
     }
@@ -103,18 +139,19 @@ __device__ __forceinline__ float block_sum(float v, float* red)
     return r;
 }
 
-// dgamma[c] = sum over the pixels of dy * xhat, dbeta[c] = sum of dy; one workgroup per channel.
-__global__ void __launch_bounds__(kThreads)
+// dgamma[c] = sum over the pixels of dy * xhat, dbeta[c] = sum of dy.
+__global__ void __launch_bounds__(kRedThreads)
 ln_params_kernel(const float* __restrict__ x, const float* __restrict__ dy, const float* __restrict__ mean_in,
                  const float* __restrict__ rstd_in, float* __restrict__ dgamma, float* __restrict__ dbeta, int N,
                  int C, int64_t HW)
 {
-    __shared__ float red[kThreads];
+    __shared__ float red[kRedThreads];
     const int c = blockIdx.x;
     float sg = 0.f, sb = 0.f;
     for (int n = 0; n < N; ++n) {
         const int64_t base = ((int64_t)n * C + c) * HW;
-        for (int64_t p = threadIdx.x; p < HW; p += kThreads) {
+#pragma unroll 4
+        for (int64_t p = threadIdx.x; p < HW; p += kRedThreads) {
             const float d = dy[base + p];
             sg = __builtin_fmaf(d, (x[base + p] - mean_in[n * HW + p]) * rstd_in[n * HW + p], sg);
             sb += d;
@@ -238,17 +275,19 @@ scale_residual_bwd_kernel(const float* __restrict__ dout, const float* __restric
 }
 
 // dgamma[c] = sum over n and pixels of (s[n] * dout) * h; one workgroup per channel.
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kRedThreads)
 scale_params_kernel(const float* __restrict__ h, const float* __restrict__ dout, const float* __restrict__ scales,
                     float* __restrict__ dgamma, int N, int C, int64_t HW)
 {
-    __shared__ float red[kThreads];
+    __shared__ float red[kRedThreads];
     const int c = blockIdx.x;
     float sg = 0.f;
     for (int n = 0; n < N; ++n) {
         const float s = scales ? scales[n] : 1.f;
         const int64_t base = ((int64_t)n * C + c) * HW;
-        for (int64_t p = threadIdx.x; p < HW; p += kThreads) sg = __builtin_fmaf(s * dout[base + p], h[base + p], sg);
+#pragma unroll 4
+        for (int64_t p = threadIdx.x; p < HW; p += kRedThreads)
+            sg = __builtin_fmaf(s * dout[base + p], h[base + p], sg);
     }
     sg = block_sum(sg, red);
     if (threadIdx.x == 0) dgamma[c] = sg;
@@ -265,8 +304,8 @@ hipError_t launch_layernorm_fwd(int n, int c, int64_t hw, float eps, const float
                                 const float* beta, float* y, float* mean, float* rstd, hipStream_t st)
 {
     const int64_t npix = (int64_t)n * hw;
-    hipLaunchKernelGGL(ln_fwd_kernel, dim3(blocks(npix)), dim3(kThreads), 0, st, x, gamma, beta, y, mean, rstd, c, hw,
-                       npix, eps);
+    hipLaunchKernelGGL(ln_fwd_kernel, dim3((unsigned)((npix + kPix - 1) / kPix)), dim3(kPix * kGroups), 0, st, x,
+                       gamma, beta, y, mean, rstd, c, hw, npix, eps);
     return hipGetLastError();
 }
 
@@ -276,14 +315,14 @@ hipError_t launch_layernorm_bwd(int n, int c, int64_t hw, const float* x, const 
 {
     const int64_t npix = (int64_t)n * hw;
     if (dx) {
-        hipLaunchKernelGGL(ln_bwd_kernel, dim3(blocks(npix)), dim3(kThreads), 0, st, x, dy, gamma, mean, rstd, dx, c,
-                           hw, npix);
+        hipLaunchKernelGGL(ln_bwd_kernel, dim3((unsigned)((npix + kPix - 1) / kPix)), dim3(kPix * kGroups), 0, st,
+                           x, dy, gamma, mean, rstd, dx, c, hw, npix);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (dgamma || dbeta)
-        hipLaunchKernelGGL(ln_params_kernel, dim3(c), dim3(kThreads), 0, st, x, dy, mean, rstd, dgamma, dbeta, n, c,
-                           hw);
+        hipLaunchKernelGGL(ln_params_kernel, dim3(c), dim3(kRedThreads), 0, st, x, dy, mean, rstd, dgamma, dbeta, n,
+                           c, hw);
     return hipGetLastError();
 }
 
@@ -328,7 +367,8 @@ hipError_t launch_scale_residual_bwd(int n, int c, int64_t hw, const float* h, c
         if (e != hipSuccess) return e;
     }
     if (dgamma)
-        hipLaunchKernelGGL(scale_params_kernel, dim3(c), dim3(kThreads), 0, st, h, dout, scales, dgamma, n, c, hw);
+        hipLaunchKernelGGL(scale_params_kernel, dim3(c), dim3(kRedThreads), 0, st, h, dout, scales, dgamma, n, c,
+                           hw);
     return hipGetLastError();
 }
 
