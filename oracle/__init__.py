@@ -24,6 +24,10 @@ What is computed, and where it is defined:
   a split along H (kwkr.cn retelling, section 5.2: Shard(2) for very high
   resolutions): the row slices, the neighbours' edge rows, and the partial
   gradients summed over a shard's own output rows.
+* ``shard_block`` / ``block_halos`` / ``conv_bwd_weight_block`` -- a grid of
+  both (2-D H x W sharding): a shard's block, the rows above and below it over
+  its own columns, the columns beside it over its rows extended by the row
+  halo (corners included), and the partial gradients over its own outputs.
 * ``reduce_partials`` -- the sum that turns _Partial gradients into
   Replicate ones (blog, DTensor section; kwkr.cn retelling, section 2.2).
 * ``stack_forward`` / ``stack_backward`` -- a chain of the above for a
@@ -273,6 +277,43 @@ def conv_bwd_weight_rows(x, g, k: int, stride: int, pad: int, groups: int, rows)
     outputs is the gradient with grad_output zero elsewhere."""
     gm = np.zeros_like(np.asarray(g, dtype=np.float64))
     gm[:, :, rows[0]:rows[1], :] = np.asarray(g, dtype=np.float64)[:, :, rows[0]:rows[1], :]
+    return conv_bwd_weight(x, gm, k, stride, pad, groups)
+
+
+def shard_block(t, num_h: int, num_w: int, sh: int, sw: int) -> np.ndarray:
+    """2-D H x W sharding: the (sh, sw) block of an num_h x num_w grid of equal
+    blocks of t (kwkr.cn retelling, section 5.2 splits H or W; a grid of both
+    is the two-dimensional case of the same method)."""
+    n, c, h, w = t.shape
+    assert h % num_h == 0 and w % num_w == 0
+    bh, bw = h // num_h, w // num_w
+    return t[:, :, sh * bh:(sh + 1) * bh, sw * bw:(sw + 1) * bw]
+
+
+def block_halos(t, num_h: int, num_w: int, sh: int, sw: int, hu: int, hd: int, hl: int, hr: int):
+    """What a 2-D shard receives, straight from the global tensor: the rows
+    above and below its block over its own columns, (N, C, hu + hd, bw); and
+    the columns left and right of it over its extended rows (the block's rows
+    plus hu above and hd below, so the four corners are included),
+    (N, C, hu + bh + hd, hl + hr).  Zeros outside the image."""
+    n, c, h, w = t.shape
+    bh, bw = h // num_h, w // num_w
+    r0, c0 = sh * bh, sw * bw
+    pad = np.zeros((n, c, h + hu + hd, w + hl + hr), dtype=t.dtype)
+    pad[:, :, hu:hu + h, hl:hl + w] = t
+    rows = np.concatenate([pad[:, :, r0:r0 + hu, hl + c0:hl + c0 + bw],
+                           pad[:, :, hu + r0 + bh:hu + r0 + bh + hd, hl + c0:hl + c0 + bw]], axis=2)
+    cols = np.concatenate([pad[:, :, r0:r0 + hu + bh + hd, c0:c0 + hl],
+                           pad[:, :, r0:r0 + hu + bh + hd, hl + c0 + bw:hl + c0 + bw + hr]], axis=3)
+    return rows, cols
+
+
+def conv_bwd_weight_block(x, g, k: int, stride: int, pad: int, groups: int, rows, cols):
+    """grad_weight / grad_bias summed over the output block rows x cols only:
+    a 2-D shard's _Partial gradients (grad_output zero elsewhere)."""
+    g64 = np.asarray(g, dtype=np.float64)
+    gm = np.zeros_like(g64)
+    gm[:, :, rows[0]:rows[1], cols[0]:cols[1]] = g64[:, :, rows[0]:rows[1], cols[0]:cols[1]]
     return conv_bwd_weight(x, gm, k, stride, pad, groups)
 
 

@@ -468,3 +468,32 @@ def test_planted_oracle_mistakes_fail_a_pin(name, monkeypatch, tmp_path):
         except AssertionError:
             failed.append(fn.__name__)
     assert failed, f"no pin caught the planted mistake: {name}"
+
+
+def test_block_halos_are_the_padded_neighbourhood():
+    """2-D shards: the block, its row halo and its extended column halo tile
+    exactly the zero-padded neighbourhood of the block (checked by assembling
+    them), and the blocks' partial gradients sum to the full gradient."""
+    rng = np.random.default_rng(41)
+    t = rng.standard_normal((2, 3, 12, 20))
+    hu = hd = hl = hr = 2
+    pad = np.pad(t, ((0, 0), (0, 0), (hu, hd), (hl, hr)))
+    for sh in range(3):
+        for sw in range(4):
+            blk = oracle.shard_block(t, 3, 4, sh, sw)
+            rows, cols = oracle.block_halos(t, 3, 4, sh, sw, hu, hd, hl, hr)
+            assert rows.shape == (2, 3, hu + hd, 5) and cols.shape == (2, 3, hu + 4 + hd, hl + hr)
+            mid = np.concatenate([rows[:, :, :hu], blk, rows[:, :, hu:]], axis=2)
+            ext = np.concatenate([cols[:, :, :, :hl], mid, cols[:, :, :, hl:]], axis=3)
+            np.testing.assert_array_equal(ext, pad[:, :, sh * 4:sh * 4 + 4 + hu + hd, sw * 5:sw * 5 + 5 + hl + hr])
+            # the same halos from the one-dimensional definitions (pinned above): the row halo of the
+            # block's column slice, and the column halo of the image's rows extended around the block
+            np.testing.assert_array_equal(rows, oracle.halo_rows(oracle.shard_columns(t, 4, sw), 3, sh, hu, hd))
+            band = pad[:, :, sh * 4:sh * 4 + 4 + hu + hd, hl:hl + 20]
+            np.testing.assert_array_equal(cols, oracle.halo_columns(band, 4, sw, hl, hr))
+    g = rng.standard_normal((2, 3, 12, 20))
+    full = oracle.conv_bwd_weight(t, g, 5, 1, 2, 3)
+    parts = [oracle.conv_bwd_weight_block(t, g, 5, 1, 2, 3, (sh * 4, sh * 4 + 4), (sw * 5, sw * 5 + 5))
+             for sh in range(3) for sw in range(4)]
+    np.testing.assert_allclose(oracle.reduce_partials([p[0] for p in parts]), full[0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.reduce_partials([p[1] for p in parts]), full[1], rtol=1e-12, atol=1e-12)
