@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSCNN_ABI_VERSION 5
+#define SSCNN_ABI_VERSION 6
 
 /* Status codes. */
 #define SSCNN_OK 0
@@ -349,6 +349,71 @@ int sscnn_hconv_bwd(const sscnn_hconv_t *conv, const float *x, const float *x_ha
                     const float *grad_y, const float *grad_y_halo, const float *weight,
                     float *grad_x, float *grad_w_part, float *grad_b_part,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * 2-D H x W sharding: a grid of num_h x num_w shards, shard (shard_h,
+ * shard_w) holding rows [shard_h*h_local, ...) and columns
+ * [shard_w*w_local, ...) of every plane (the two splits of kwkr.cn retelling,
+ * section 5.2, combined).  The halo arrives in two phases, as on a 2-D mesh:
+ *   1. sscnn_grid_row_halo_gather: the `halo` rows above and below the block,
+ *      over its own columns, from the blocks above and below;
+ *   2. sscnn_grid_col_halo_gather: the `halo` columns left and right of the
+ *      block over its EXTENDED rows (halo above, the block's rows, halo below),
+ *      from the blocks left and right of it and the row halos THEY gathered
+ *      in phase 1 -- which is how the corners arrive from the diagonal blocks.
+ * Layers: depthwise (groups = c_in = c_out) stride-1 k in {3,5,7} pad k/2 with
+ * w_local % 16 == 0 and h_local >= 16 (halo = pad on every side), and layers
+ * with k = stride, pad 0, groups 1 (no halo: the block is convolved as is);
+ * anything else is SSCNN_EUNSUPPORTED.  Results equal the unsharded layer's
+ * output block, the partials sum to the full gradients.
+ */
+typedef struct sscnn_gconv {
+    /* set by the caller */
+    int32_t n, c_in, c_out;
+    int32_t h_local, w_local;     /* the block's input rows and columns */
+    int32_t k, stride, pad, groups;
+    int32_t shard_h, num_h;       /* block row index (top to bottom) and grid rows */
+    int32_t shard_w, num_w;       /* block column index (left to right) and grid columns */
+    /* filled by sscnn_gconv_init */
+    int32_t h_out_local, w_out_local;
+    int32_t halo;                 /* rows above/below and columns left/right needed (input and grad_output) */
+} sscnn_gconv_t;
+
+int sscnn_gconv_init(sscnn_gconv_t *conv);
+
+/* Phase 1: row_halo (n, c, 2*halo, w) receives the last `halo` rows of `up`
+ * then the first `halo` rows of `down` (blocks of the same shape, NULL at the
+ * image's top / bottom edge: zeros).  which = SSCNN_HALO_INPUT (c = c_in,
+ * the input block) or SSCNN_HALO_GRAD_OUTPUT (c = c_out, the output block). */
+int sscnn_grid_row_halo_gather(const sscnn_gconv_t *conv, int32_t which, const float *up,
+                               const float *down, float *row_halo, void *stream);
+
+/* Phase 2: col_halo (n, c, halo + h + halo, 2*halo) receives, for each
+ * extended row, the last `halo` columns of the left block then the first
+ * `halo` columns of the right block; rows beyond a neighbour's block come
+ * from that neighbour's phase-1 row halo.  NULL left / right (image edge):
+ * zeros; a non-NULL block needs its row halo. */
+int sscnn_grid_col_halo_gather(const sscnn_gconv_t *conv, int32_t which, const float *left,
+                               const float *left_row_halo, const float *right,
+                               const float *right_row_halo, float *col_halo, void *stream);
+
+int sscnn_gconv_fwd(const sscnn_gconv_t *conv, const float *x, const float *x_row_halo,
+                    const float *x_col_halo, const float *weight, const float *bias, float *y,
+                    void *stream);
+int sscnn_gconv_bwd_input(const sscnn_gconv_t *conv, const float *grad_y, const float *gy_row_halo,
+                          const float *gy_col_halo, const float *weight, float *grad_x,
+                          void *stream);
+size_t sscnn_gconv_bwd_weight_workspace_bytes(const sscnn_gconv_t *conv);
+/* _Partial grad_weight / grad_bias: sums over this block's own outputs. */
+int sscnn_gconv_bwd_weight_partial(const sscnn_gconv_t *conv, const float *x, const float *x_row_halo,
+                                   const float *x_col_halo, const float *grad_y, float *grad_w_part,
+                                   float *grad_b_part, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+int sscnn_gconv_bwd(const sscnn_gconv_t *conv, const float *x, const float *x_row_halo,
+                    const float *x_col_halo, const float *grad_y, const float *gy_row_halo,
+                    const float *gy_col_halo, const float *weight, float *grad_x,
+                    float *grad_w_part, float *grad_b_part, void *workspace,
+                    size_t workspace_bytes, void *stream);
 
 /*
  * Reduction of partial gradients into the replicated gradient (blog, DTensor

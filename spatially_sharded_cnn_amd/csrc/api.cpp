@@ -148,6 +148,58 @@ int check_h(const sscnn_hconv_t* conv, Geom* g)
     return SSCNN_OK;
 }
 
+// 2-D shards: the supported layers and their derived fields.
+int derive_g(const sscnn_gconv_t& c, sscnn_gconv_t* out)
+{
+    if (c.n <= 0 || c.c_in <= 0 || c.c_out <= 0 || c.h_local <= 0 || c.w_local <= 0 || c.k <= 0 || c.stride <= 0 ||
+        c.groups <= 0 || c.num_h <= 0 || c.num_w <= 0)
+        return fail(SSCNN_EINVAL, "sizes must be positive");
+    if (c.shard_h < 0 || c.shard_h >= c.num_h || c.shard_w < 0 || c.shard_w >= c.num_w)
+        return fail(SSCNN_EINVAL, "shard (%d, %d) outside the %d x %d grid", c.shard_h, c.shard_w, c.num_h, c.num_w);
+    if ((int64_t)c.n * c.c_in * c.h_local * c.w_local > ((int64_t)1 << 40)) return fail(SSCNN_EINVAL, "tensor too large");
+    sscnn_gconv_t d = c;
+    const bool dw = c.groups == c.c_in && c.c_in == c.c_out && c.stride == 1 && (c.k == 3 || c.k == 5 || c.k == 7) &&
+                    c.pad == c.k / 2;
+    const bool patch = c.k == c.stride && c.pad == 0 && c.groups == 1;
+    if (dw) {
+        if (c.w_local % 16 || c.h_local < 16)
+            return fail(SSCNN_EUNSUPPORTED, "2-D depthwise blocks need w_local %% 16 == 0 and h_local >= 16 "
+                        "(got %d x %d)", c.h_local, c.w_local);
+        if ((int64_t)c.n * c.c_in * c.h_local * c.w_local >= ((int64_t)1 << 31))
+            return fail(SSCNN_EUNSUPPORTED, "2-D depthwise block of 2^31 elements or more");
+        d.h_out_local = c.h_local;
+        d.w_out_local = c.w_local;
+        d.halo = c.pad;
+    } else if (patch) {
+        if (c.h_local % c.k || c.w_local % c.k)
+            return fail(SSCNN_EUNSUPPORTED, "block %d x %d is not a whole number of %d x %d patches", c.h_local,
+                        c.w_local, c.k, c.k);
+        d.h_out_local = c.h_local / c.k;
+        d.w_out_local = c.w_local / c.k;
+        d.halo = 0;
+    } else {
+        return fail(SSCNN_EUNSUPPORTED, "2-D shards take depthwise stride-1 k/2-padded layers and k = stride "
+                    "layers only (k=%d stride=%d pad=%d groups=%d)", c.k, c.stride, c.pad, c.groups);
+    }
+    *out = d;
+    return SSCNN_OK;
+}
+
+int check_g(const sscnn_gconv_t* conv, Geom* g)
+{
+    if (!conv) return fail(SSCNN_EINVAL, "conv is NULL");
+    sscnn_gconv_t d;
+    int st = derive_g(*conv, &d);
+    if (st) return st;
+    if (d.h_out_local != conv->h_out_local || d.w_out_local != conv->w_out_local || d.halo != conv->halo)
+        return fail(SSCNN_EINVAL, "descriptor not initialised by sscnn_gconv_init (or edited since)");
+    g->n = d.n; g->ci = d.c_in; g->co = d.c_out; g->h = d.h_local; g->wl = d.w_local; g->k = d.k;
+    g->stride = d.stride; g->pad = d.pad; g->groups = d.groups; g->ho = d.h_out_local; g->wol = d.w_out_local;
+    g->hl = g->hr = g->ghl = g->ghr = d.halo;
+    g->cig = d.c_in / d.groups; g->cog = d.c_out / d.groups;
+    return SSCNN_OK;
+}
+
 // The workspace check shared by the grad_weight calls (rows: also the
 // row-edge grad_weight's scratch, used after the interior call is done with
 // its own).
@@ -714,6 +766,173 @@ int sscnn_hconv_bwd(const sscnn_hconv_t* conv, const float* x, const float* x_ha
     if (e == hipSuccess) e = launch_row_edge_bwd_input(g, ghu, ghd, grad_y_halo, weight, grad_x, st);
     if (e == hipSuccess) e = launch_row_edge_bwd_weight(g, hu, hd, x_halo, grad_y, grad_w_part, workspace, st);
     return hip_status(e, "hconv_bwd launch");
+}
+
+// --- 2-D H x W shards ------------------------------------------------------------
+
+int sscnn_gconv_init(sscnn_gconv_t* conv)
+{
+    if (!conv) return fail(SSCNN_EINVAL, "conv is NULL");
+    sscnn_gconv_t d;
+    TRY(derive_g(*conv, &d));
+    *conv = d;
+    return SSCNN_OK;
+}
+
+int sscnn_grid_row_halo_gather(const sscnn_gconv_t* conv, int32_t which, const float* up, const float* down,
+                               float* row_halo, void* stream)
+{
+    Geom g;
+    TRY(check_g(conv, &g));
+    if (which != SSCNN_HALO_INPUT && which != SSCNN_HALO_GRAD_OUTPUT) return fail(SSCNN_EINVAL, "bad which=%d", which);
+    const int hh = conv->halo;
+    if (hh == 0) return SSCNN_OK;
+    TRY(need(row_halo, "row_halo"));
+    if ((conv->shard_h > 0) != (up != nullptr)) return fail(SSCNN_EINVAL, "up must be given exactly when shard_h > 0");
+    if ((conv->shard_h < conv->num_h - 1) != (down != nullptr))
+        return fail(SSCNN_EINVAL, "down must be given exactly when shard_h < num_h - 1");
+    TRY(optional(up, "up"));
+    TRY(optional(down, "down"));
+    const bool in = which == SSCNN_HALO_INPUT;
+    const int64_t planes = (int64_t)g.n * (in ? g.ci : g.co);
+    return hip_status(launch_row_halo_gather(up, down, planes, in ? g.h : g.ho, in ? g.wl : g.wol, hh, hh, row_halo,
+                                             (hipStream_t)stream),
+                      "grid_row_halo_gather launch");
+}
+
+int sscnn_grid_col_halo_gather(const sscnn_gconv_t* conv, int32_t which, const float* left, const float* left_row_halo,
+                               const float* right, const float* right_row_halo, float* col_halo, void* stream)
+{
+    Geom g;
+    TRY(check_g(conv, &g));
+    if (which != SSCNN_HALO_INPUT && which != SSCNN_HALO_GRAD_OUTPUT) return fail(SSCNN_EINVAL, "bad which=%d", which);
+    const int hh = conv->halo;
+    if (hh == 0) return SSCNN_OK;
+    TRY(need(col_halo, "col_halo"));
+    if ((conv->shard_w > 0) != (left != nullptr)) return fail(SSCNN_EINVAL, "left must be given exactly when shard_w > 0");
+    if ((conv->shard_w < conv->num_w - 1) != (right != nullptr))
+        return fail(SSCNN_EINVAL, "right must be given exactly when shard_w < num_w - 1");
+    if ((left && !left_row_halo) || (right && !right_row_halo))
+        return fail(SSCNN_EINVAL, "a neighbour block needs its phase-1 row halo");
+    TRY(optional(left, "left"));
+    TRY(optional(right, "right"));
+    TRY(optional(left_row_halo, "left_row_halo"));
+    TRY(optional(right_row_halo, "right_row_halo"));
+    const bool in = which == SSCNN_HALO_INPUT;
+    const int64_t planes = (int64_t)g.n * (in ? g.ci : g.co);
+    return hip_status(launch_grid_col_halo(left, left_row_halo, right, right_row_halo, planes, in ? g.h : g.ho,
+                                           in ? g.wl : g.wol, hh, hh, hh, hh, col_halo, (hipStream_t)stream),
+                      "grid_col_halo_gather launch");
+}
+
+namespace {
+
+// the row / column halos a call needs (none for k = stride layers)
+int need_grid_halos(const sscnn_gconv_t* conv, const float* rh, const float* ch, const char* rn, const char* cn)
+{
+    if (conv->halo) {
+        TRY(need(rh, rn));
+        TRY(need(ch, cn));
+    } else {
+        TRY(optional(rh, rn));
+        TRY(optional(ch, cn));
+    }
+    return SSCNN_OK;
+}
+
+}  // namespace
+
+int sscnn_gconv_fwd(const sscnn_gconv_t* conv, const float* x, const float* x_row_halo, const float* x_col_halo,
+                    const float* weight, const float* bias, float* y, void* stream)
+{
+    Geom g;
+    TRY(check_g(conv, &g));
+    TRY(need(x, "x"));
+    TRY(need_grid_halos(conv, x_row_halo, x_col_halo, "x_row_halo", "x_col_halo"));
+    TRY(need(weight, "weight"));
+    TRY(optional(bias, "bias"));
+    TRY(need(y, "y"));
+    const hipStream_t st = (hipStream_t)stream;
+    const int hh = conv->halo;
+    if (!hh) return hip_status(kernels_conv_fwd(g, x, nullptr, weight, bias, y, st), "gconv_fwd launch");
+    return hip_status(launch_dw_fwd_grid(g, x, x_row_halo, x_col_halo, hh, hh, weight, bias, y, st), "gconv_fwd launch");
+}
+
+int sscnn_gconv_bwd_input(const sscnn_gconv_t* conv, const float* grad_y, const float* gy_row_halo,
+                          const float* gy_col_halo, const float* weight, float* grad_x, void* stream)
+{
+    Geom g;
+    TRY(check_g(conv, &g));
+    TRY(need(grad_y, "grad_y"));
+    TRY(need_grid_halos(conv, gy_row_halo, gy_col_halo, "gy_row_halo", "gy_col_halo"));
+    TRY(need(weight, "weight"));
+    TRY(need(grad_x, "grad_x"));
+    const hipStream_t st = (hipStream_t)stream;
+    const int hh = conv->halo;
+    if (!hh) return hip_status(kernels_conv_bwd_input(g, grad_y, nullptr, weight, grad_x, st), "gconv_bwd_input launch");
+    return hip_status(launch_dw_bwd_input_grid(g, grad_y, gy_row_halo, gy_col_halo, hh, hh, weight, grad_x, st),
+                      "gconv_bwd_input launch");
+}
+
+size_t sscnn_gconv_bwd_weight_workspace_bytes(const sscnn_gconv_t* conv)
+{
+    Geom g;
+    if (check_g(conv, &g)) return 0;
+    return kernels_bwd_weight_workspace_bytes(g);
+}
+
+int sscnn_gconv_bwd_weight_partial(const sscnn_gconv_t* conv, const float* x, const float* x_row_halo,
+                                   const float* x_col_halo, const float* grad_y, float* grad_w_part, float* grad_b_part,
+                                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    Geom g;
+    TRY(check_g(conv, &g));
+    TRY(need(x, "x"));
+    TRY(need_grid_halos(conv, x_row_halo, x_col_halo, "x_row_halo", "x_col_halo"));
+    TRY(need(grad_y, "grad_y"));
+    TRY(need(grad_w_part, "grad_w_part"));
+    TRY(optional(grad_b_part, "grad_b_part"));
+    size_t ws_need;
+    TRY(need_workspace(g, workspace, workspace_bytes, &ws_need));
+    const hipStream_t st = (hipStream_t)stream;
+    const int hh = conv->halo;
+    void* ws = ws_need ? workspace : nullptr;
+    if (!hh)
+        return hip_status(kernels_conv_bwd_weight(g, x, nullptr, grad_y, grad_w_part, grad_b_part, ws, st),
+                          "gconv_bwd_weight_partial launch");
+    return hip_status(launch_dw_bwd_weight_grid(g, x, x_row_halo, x_col_halo, hh, hh, grad_y, grad_w_part,
+                                                grad_b_part, ws, st),
+                      "gconv_bwd_weight_partial launch");
+}
+
+int sscnn_gconv_bwd(const sscnn_gconv_t* conv, const float* x, const float* x_row_halo, const float* x_col_halo,
+                    const float* grad_y, const float* gy_row_halo, const float* gy_col_halo, const float* weight,
+                    float* grad_x, float* grad_w_part, float* grad_b_part, void* workspace, size_t workspace_bytes,
+                    void* stream)
+{
+    Geom g;
+    TRY(check_g(conv, &g));
+    TRY(need(x, "x"));
+    TRY(need_grid_halos(conv, x_row_halo, x_col_halo, "x_row_halo", "x_col_halo"));
+    TRY(need(grad_y, "grad_y"));
+    TRY(need_grid_halos(conv, gy_row_halo, gy_col_halo, "gy_row_halo", "gy_col_halo"));
+    TRY(need(weight, "weight"));
+    TRY(need(grad_x, "grad_x"));
+    TRY(need(grad_w_part, "grad_w_part"));
+    TRY(optional(grad_b_part, "grad_b_part"));
+    if (grad_x == x || grad_x == grad_y) return fail(SSCNN_EINVAL, "grad_x aliases an input");
+    size_t ws_need;
+    TRY(need_workspace(g, workspace, workspace_bytes, &ws_need));
+    const hipStream_t st = (hipStream_t)stream;
+    const int hh = conv->halo;
+    void* ws = ws_need ? workspace : nullptr;
+    if (!hh)
+        return hip_status(kernels_conv_bwd(g, x, nullptr, grad_y, nullptr, weight, grad_x, grad_w_part, grad_b_part,
+                                           ws, st),
+                          "gconv_bwd launch");
+    return hip_status(launch_dw_bwd_grid(g, x, x_row_halo, x_col_halo, hh, hh, grad_y, gy_row_halo, gy_col_halo, hh,
+                                         hh, weight, grad_x, grad_w_part, grad_b_part, ws, st),
+                      "gconv_bwd launch");
 }
 
 }  // extern "C"

@@ -32,4 +32,17 @@ hipError_t launch_dw_bwd_rows(const Geom& g, const float* x, const float* x_rh, 
                               const float* gy, const float* gy_rh, int g_up, int g_down, const float* w, float* gx,
                               float* gw, float* gb, void* ws, hipStream_t st);
 
+// 2-D shards: rows beyond the block from the row halo (N*C, up + down, W),
+// columns beside it from the column halo over the extended rows
+// (N*C, up + H + down, 2P), corners included.  Same workspace as above.
+hipError_t launch_dw_fwd_grid(const Geom& g, const float* x, const float* x_rh, const float* x_ch, int up, int down,
+                              const float* w, const float* b, float* y, hipStream_t st);
+hipError_t launch_dw_bwd_input_grid(const Geom& g, const float* gy, const float* gy_rh, const float* gy_ch, int up,
+                                    int down, const float* w, float* gx, hipStream_t st);
+hipError_t launch_dw_bwd_weight_grid(const Geom& g, const float* x, const float* x_rh, const float* x_ch, int up,
+                                     int down, const float* gy, float* gw, float* gb, void* ws, hipStream_t st);
+hipError_t launch_dw_bwd_grid(const Geom& g, const float* x, const float* x_rh, const float* x_ch, int x_up,
+                              int x_down, const float* gy, const float* gy_rh, const float* gy_ch, int g_up,
+                              int g_down, const float* w, float* gx, float* gw, float* gb, void* ws, hipStream_t st);
+
 }  // namespace sscnn

@@ -75,6 +75,17 @@ __device__ __forceinline__ RowHalo row_halo(const float* base, int64_t plane, in
     return RowHalo{base + plane * (up + down) * W, up, down};
 }
 
+// A plane's column halo, (H, 2P) per plane; with ROWH as well (2-D shards) it
+// covers the extended rows, (up + H + down, 2P) per plane, and the pointer
+// returned is that of row 0 (so rows -up .. -1 sit before it).
+template <bool HALO, bool ROWH>
+__device__ __forceinline__ const float* col_halo(const float* base, int64_t plane, int H, int up, int down, int P)
+{
+    if constexpr (!HALO) return nullptr;
+    if constexpr (ROWH) return base + plane * (up + H + down) * (2 * P) + up * (2 * P);
+    return base + plane * H * (2 * P);
+}
+
 // One tile: its plane and channel, and the rows and columns it covers.  The
 // last tile of a column is moved up to end at row H (i0 = H - TH) so every
 // row it computes is a real row and its stores need no predicate; it then
@@ -225,11 +236,34 @@ struct Tile {
     // Side columns: ordinary loads into registers, written by put_side().
     // Without a halo (HALO false: the interior half of a split convolution)
     // the columns beyond the slice are zeros.
-    // ROWH: rows beyond the slice take their columns from its row halo.
+    // ROWH: rows beyond the slice take their columns from its row halo.  Both
+    // (2-D shards): the column halo covers the extended rows -up .. H+down-1
+    // (hp points at its row 0), so the corners come from it too.
     template <bool HALO, bool ROWH>
     __device__ static void load_side(Side& S, const float* __restrict__ xp, const float* __restrict__ hp,
                                      int H, int W, int i0, int j0, int tid, const RowHalo& rh)
     {
+        if constexpr (HALO && ROWH) {
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                const int idx = tid + k * NT;
+                const int rr = idx / (2 * P), e = idx - rr * (2 * P);
+                const int r = i0 - P + rr;
+                const int xcol = j0 + (e < P ? e : TW + e) - P;
+                S.s[k] = 0.f;
+                if (idx < LH * 2 * P && r >= -rh.up && r < H + rh.down) {
+                    if (xcol < 0)
+                        S.s[k] = hp[(int64_t)r * (2 * P) + (xcol + P)];
+                    else if (xcol >= W)
+                        S.s[k] = hp[(int64_t)r * (2 * P) + P + (xcol - W)];
+                    else if (r >= 0 && r < H)
+                        S.s[k] = xp[(int64_t)r * W + xcol];
+                    else
+                        S.s[k] = rh.p[(int64_t)(r < 0 ? rh.up + r : rh.up + (r - H)) * W + xcol];
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
             const int idx = tid + k * NT;
@@ -432,8 +466,8 @@ dw_conv_kernel(DwArgs a)
         const RowHalo rh = ROWH ? row_halo(a.src_rh, e.plane, a.src_up, a.src_down, a.W) : RowHalo{};
         T::template load_main<ROWH>(b, a.src + e.plane * HW, a.H, a.W, e.i0, e.j0, tid, rh);
         T::template load_side<HALO, ROWH>(S, a.src + e.plane * HW,
-                                          HALO ? a.src_h + (int64_t)e.plane * a.H * (2 * P) : nullptr, a.H, a.W,
-                                          e.i0, e.j0, tid, rh);
+                                          col_halo<HALO, ROWH>(a.src_h, e.plane, a.H, a.src_up, a.src_down, P),
+                                          a.H, a.W, e.i0, e.j0, tid, rh);
     };
     int t = blockIdx.x;
     if (t >= a.ntiles) return;
@@ -523,8 +557,8 @@ dw_wgrad_kernel(DwArgs a)
         const RowHalo rh = ROWH ? row_halo(a.x_rh, e.plane, a.x_up, a.x_down, a.W) : RowHalo{};
         T::template load_main<ROWH>(b, a.x + e.plane * HW, a.H, a.W, e.i0, e.j0, tid, rh);
         T::template load_side<HALO, ROWH>(S, a.x + e.plane * HW,
-                                          HALO ? a.x_h + (int64_t)e.plane * a.H * (2 * P) : nullptr, a.H, a.W,
-                                          e.i0, e.j0, tid, rh);
+                                          col_halo<HALO, ROWH>(a.x_h, e.plane, a.H, a.x_up, a.x_down, P), a.H,
+                                          a.W, e.i0, e.j0, tid, rh);
         const float* gp = a.g + e.plane * HW + e.j0 + 4 * tx;
 #pragma unroll
         for (int i = 0; i < RH; ++i) {
@@ -600,7 +634,7 @@ dw_bwd_kernel(DwArgs a)
         const RowHalo rh = ROWH ? row_halo(src_rh, e.plane, up, down, a.W) : RowHalo{};
         T::template load_main<ROWH>(b, src + e.plane * HW, a.H, a.W, e.i0, e.j0, tid, rh);
         T::template load_side<HALO, ROWH>(S, src + e.plane * HW,
-                                          HALO ? src_h + (int64_t)e.plane * a.H * (2 * P) : nullptr, a.H, a.W,
+                                          col_halo<HALO, ROWH>(src_h, e.plane, a.H, up, down, P), a.H, a.W,
                                           e.i0, e.j0, tid, rh);
     };
     issue(beg, mybuf[0]);
@@ -953,6 +987,69 @@ hipError_t launch_dw_bwd_rows(const Geom& g, const float* x, const float* x_rh, 
         case 3: return launch_bwd<3, false, true>(a, planes, sh, gw, gb, st);
         case 5: return launch_bwd<5, false, true>(a, planes, sh, gw, gb, st);
         default: return launch_bwd<7, false, true>(a, planes, sh, gw, gb, st);
+    }
+}
+
+// 2-D shards: rows beyond the block from its row halo (N*C, up + down, W),
+// columns beside it from its column halo over the extended rows
+// (N*C, up + H + down, 2P), corners included.
+hipError_t launch_dw_fwd_grid(const Geom& g, const float* x, const float* x_rh, const float* x_ch, int up, int down,
+                              const float* w, const float* b, float* y, hipStream_t st)
+{
+    DwArgs a = make_args(g);
+    a.src = x; a.src_rh = x_rh; a.src_h = x_ch; a.src_up = up; a.src_down = down; a.w = w; a.b = b; a.out = y;
+    const int planes = g.n * g.ci;
+    const DwShape sh = pick_shape(g.h, g.wl);
+    switch (g.k) {
+        case 3: return launch_conv<3, false, true, true>(a, planes, sh, st);
+        case 5: return launch_conv<5, false, true, true>(a, planes, sh, st);
+        default: return launch_conv<7, false, true, true>(a, planes, sh, st);
+    }
+}
+
+hipError_t launch_dw_bwd_input_grid(const Geom& g, const float* gy, const float* gy_rh, const float* gy_ch, int up,
+                                    int down, const float* w, float* gx, hipStream_t st)
+{
+    DwArgs a = make_args(g);
+    a.src = gy; a.src_rh = gy_rh; a.src_h = gy_ch; a.src_up = up; a.src_down = down; a.w = w; a.b = nullptr;
+    a.out = gx;
+    const int planes = g.n * g.ci;
+    const DwShape sh = pick_shape(g.h, g.wl);
+    switch (g.k) {
+        case 3: return launch_conv<3, true, true, true>(a, planes, sh, st);
+        case 5: return launch_conv<5, true, true, true>(a, planes, sh, st);
+        default: return launch_conv<7, true, true, true>(a, planes, sh, st);
+    }
+}
+
+hipError_t launch_dw_bwd_weight_grid(const Geom& g, const float* x, const float* x_rh, const float* x_ch, int up,
+                                     int down, const float* gy, float* gw, float* gb, void* ws, hipStream_t st)
+{
+    DwArgs a = make_args(g);
+    a.x = x; a.x_rh = x_rh; a.x_h = x_ch; a.x_up = up; a.x_down = down; a.g = gy; a.ws = static_cast<float*>(ws);
+    const int planes = g.n * g.ci;
+    const DwShape sh = pick_shape(g.h, g.wl);
+    switch (g.k) {
+        case 3: return launch_wgrad<3, true, true>(a, planes, sh, gw, gb, st);
+        case 5: return launch_wgrad<5, true, true>(a, planes, sh, gw, gb, st);
+        default: return launch_wgrad<7, true, true>(a, planes, sh, gw, gb, st);
+    }
+}
+
+hipError_t launch_dw_bwd_grid(const Geom& g, const float* x, const float* x_rh, const float* x_ch, int x_up,
+                              int x_down, const float* gy, const float* gy_rh, const float* gy_ch, int g_up,
+                              int g_down, const float* w, float* gx, float* gw, float* gb, void* ws, hipStream_t st)
+{
+    DwArgs a = make_args(g);
+    a.src = gy; a.src_rh = gy_rh; a.src_h = gy_ch; a.src_up = g_up; a.src_down = g_down;
+    a.x = x; a.x_rh = x_rh; a.x_h = x_ch; a.x_up = x_up; a.x_down = x_down;
+    a.w = w; a.out = gx; a.ws = static_cast<float*>(ws);
+    const int planes = g.n * g.ci;
+    const DwShape sh = bwd_shape(g.h, g.wl);
+    switch (g.k) {
+        case 3: return launch_bwd<3, true, true>(a, planes, sh, gw, gb, st);
+        case 5: return launch_bwd<5, true, true>(a, planes, sh, gw, gb, st);
+        default: return launch_bwd<7, true, true>(a, planes, sh, gw, gb, st);
     }
 }
 

@@ -12,6 +12,14 @@ namespace sscnn {
 // (rows of `width` floats; zeros for a null neighbour).
 hipError_t launch_row_halo_gather(const float* up, const float* down, int64_t planes, int rows, int width, int hu,
                                   int hd, float* halo, hipStream_t st);
+// 2-D shards, second phase: out[p, e, :] = the last hl columns of the left
+// neighbour's extended row e, then the first hr columns of the right
+// neighbour's (extended rows: up rows of its row halo, its rows, down rows of
+// its row halo; (planes, up + rows + down, hl + hr); zeros for a null
+// neighbour or row halo).
+hipError_t launch_grid_col_halo(const float* left, const float* left_rh, const float* right, const float* right_rh,
+                                int64_t planes, int rows, int width, int up, int down, int hl, int hr, float* out,
+                                hipStream_t st);
 // y += the forward's terms that read an input halo row (rh: (n, ci, hu + hd, wl)).
 hipError_t launch_row_edge_fwd(const Geom& g, int hu, int hd, const float* rh, const float* w, float* y,
                                hipStream_t st);

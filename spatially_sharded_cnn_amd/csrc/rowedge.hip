@@ -353,6 +353,56 @@ void dw_row_launch(const Geom& g, const float* rh, const float* w, float* out, h
 
 }  // namespace
 
+namespace {
+
+// 2-D shards, second phase of the exchange: the columns beside a block over
+// its extended rows (the up rows above it, its own rows, the down rows below).
+// Extended row e (row r = e - up of the block) of the left neighbour is its
+// row r for 0 <= r < rows, else a row of its row halo, which its first phase
+// filled from the blocks above and below it: so the corners travel with the
+// columns.  out[p, e, :] = left columns hl, then right columns hr.
+__global__ void __launch_bounds__(256)
+grid_col_halo_kernel(const float* __restrict__ left, const float* __restrict__ left_rh,
+                     const float* __restrict__ right, const float* __restrict__ right_rh, int64_t planes, int rows,
+                     int width, int up, int down, int hl, int hr, float* __restrict__ out)
+{
+    const int ext = up + rows + down, wh = hl + hr;
+    const int64_t total = planes * ext * wh;
+    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256) {
+        const int col = (int)(t % wh);
+        const int64_t pe = t / wh;
+        const int e = (int)(pe % ext);
+        const int64_t p = pe / ext;
+        const int r = e - up;
+        const bool lft = col < hl;
+        const float* slice = lft ? left : right;
+        const float* rh = lft ? left_rh : right_rh;
+        const int x = lft ? width - hl + col : col - hl;
+        float v = 0.f;
+        if (r >= 0 && r < rows) {
+            if (slice) v = slice[(p * rows + r) * width + x];
+        } else if (rh) {
+            const int hrow = r < 0 ? up + r : up + (r - rows);
+            v = rh[(p * (up + down) + hrow) * width + x];
+        }
+        out[t] = v;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_grid_col_halo(const float* left, const float* left_rh, const float* right, const float* right_rh,
+                                int64_t planes, int rows, int width, int up, int down, int hl, int hr, float* out,
+                                hipStream_t st)
+{
+    const int64_t total = planes * (up + rows + down) * (hl + hr);
+    if (total == 0) return hipSuccess;
+    const int grid = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+    hipLaunchKernelGGL(grid_col_halo_kernel, dim3(grid), dim3(256), 0, st, left, left_rh, right, right_rh, planes,
+                       rows, width, up, down, hl, hr, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_row_halo_gather(const float* up, const float* down, int64_t planes, int rows, int width, int hu,
                                   int hd, float* halo, hipStream_t st)
 {

@@ -31,6 +31,9 @@ EXPORTED = (
     "sscnn_hconv_bwd_weight_workspace_bytes", "sscnn_hconv_bwd_weight_partial", "sscnn_hconv_bwd",
     "sscnn_layernorm_fwd", "sscnn_layernorm_bwd", "sscnn_gelu_fwd", "sscnn_gelu_bwd", "sscnn_droppath_scales",
     "sscnn_layer_scale_residual_fwd", "sscnn_layer_scale_residual_bwd",
+    "sscnn_gconv_init", "sscnn_grid_row_halo_gather", "sscnn_grid_col_halo_gather", "sscnn_gconv_fwd",
+    "sscnn_gconv_bwd_input", "sscnn_gconv_bwd_weight_workspace_bytes", "sscnn_gconv_bwd_weight_partial",
+    "sscnn_gconv_bwd",
 )
 
 
@@ -95,6 +98,36 @@ class HConv(ctypes.Structure):
         return (self.n, self.c_out, self.ghalo_u + self.ghalo_d, self.w_out)
 
 
+class GConv(ctypes.Structure):
+    """Mirror of sscnn_gconv_t (2-D H x W sharding)."""
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "n", "c_in", "c_out", "h_local", "w_local", "k", "stride", "pad", "groups", "shard_h", "num_h",
+        "shard_w", "num_w", "h_out_local", "w_out_local", "halo")]
+
+    def __repr__(self):
+        return "GConv(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+    @property
+    def x_shape(self):
+        return (self.n, self.c_in, self.h_local, self.w_local)
+
+    @property
+    def y_shape(self):
+        return (self.n, self.c_out, self.h_out_local, self.w_out_local)
+
+    @property
+    def w_shape(self):
+        return (self.c_out, self.c_in // self.groups, self.k, self.k)
+
+    def row_halo_shape(self, which: int):
+        n, c, h, w = self.x_shape if which == HALO_INPUT else self.y_shape
+        return (n, c, 2 * self.halo, w)
+
+    def col_halo_shape(self, which: int):
+        n, c, h, w = self.x_shape if which == HALO_INPUT else self.y_shape
+        return (n, c, h + 2 * self.halo, 2 * self.halo)
+
+
 _lib = None
 _vp = ctypes.c_void_p
 
@@ -133,6 +166,16 @@ def lib() -> ctypes.CDLL:
         L.sscnn_hconv_bwd_weight_workspace_bytes.restype = ctypes.c_size_t
         L.sscnn_hconv_bwd_weight_partial.argtypes = [HP, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.sscnn_hconv_bwd.argtypes = [HP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        GP = ctypes.POINTER(GConv)
+        L.sscnn_gconv_init.argtypes = [GP]
+        L.sscnn_grid_row_halo_gather.argtypes = [GP, ctypes.c_int32, _vp, _vp, _vp, _vp]
+        L.sscnn_grid_col_halo_gather.argtypes = [GP, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.sscnn_gconv_fwd.argtypes = [GP] + [_vp] * 7
+        L.sscnn_gconv_bwd_input.argtypes = [GP] + [_vp] * 6
+        L.sscnn_gconv_bwd_weight_workspace_bytes.argtypes = [GP]
+        L.sscnn_gconv_bwd_weight_workspace_bytes.restype = ctypes.c_size_t
+        L.sscnn_gconv_bwd_weight_partial.argtypes = [GP] + [_vp] * 7 + [ctypes.c_size_t, _vp]
+        L.sscnn_gconv_bwd.argtypes = [GP] + [_vp] * 11 + [ctypes.c_size_t, _vp]
         i32, i64, u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
         L.sscnn_layernorm_fwd.argtypes = [i32, i32, i32, i32, ctypes.c_float] + [_vp] * 7
         L.sscnn_layernorm_bwd.argtypes = [i32, i32, i32, i32] + [_vp] * 9
@@ -152,7 +195,9 @@ def lib() -> ctypes.CDLL:
                   "sscnn_conv_bwd_interior", "sscnn_hconv_init", "sscnn_row_halo_gather", "sscnn_hconv_fwd",
                   "sscnn_hconv_bwd_input", "sscnn_hconv_bwd_weight_partial", "sscnn_hconv_bwd",
                   "sscnn_layernorm_fwd", "sscnn_layernorm_bwd", "sscnn_gelu_fwd", "sscnn_gelu_bwd",
-                  "sscnn_droppath_scales", "sscnn_layer_scale_residual_fwd", "sscnn_layer_scale_residual_bwd"):
+                  "sscnn_droppath_scales", "sscnn_layer_scale_residual_fwd", "sscnn_layer_scale_residual_bwd",
+                  "sscnn_gconv_init", "sscnn_grid_row_halo_gather", "sscnn_grid_col_halo_gather",
+                  "sscnn_gconv_fwd", "sscnn_gconv_bwd_input", "sscnn_gconv_bwd_weight_partial", "sscnn_gconv_bwd"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -423,6 +468,95 @@ def partial_reduce(parts: Sequence, out, stream=None):
     ptrs = (_vp * len(parts))(*[_ptr(p, (n,), f"parts[{i}]") for i, p in enumerate(parts)])
     _check(lib().sscnn_partial_reduce(ptrs, len(parts), n, _ptr(out, (n,), "out"), _stream(stream)),
            "partial_reduce")
+
+
+# --- 2-D H x W shards ---------------------------------------------------------------
+
+def gconv_init(n, c_in, c_out, h_local, w_local, k, stride, pad, groups, shard_h, num_h, shard_w, num_w) -> GConv:
+    """Build and validate a 2-D shard descriptor (sscnn_gconv_init)."""
+    c = GConv(n, c_in, c_out, h_local, w_local, k, stride, pad, groups, shard_h, num_h, shard_w, num_w)
+    _check(lib().sscnn_gconv_init(ctypes.byref(c)), "gconv_init")
+    return c
+
+
+def grid_row_halo_gather(conv: GConv, which: int, up, down, row_halo, stream=None):
+    """Phase 1 (sscnn_grid_row_halo_gather): rows from the blocks above / below (None at the image edge)."""
+    blk = conv.x_shape if which == HALO_INPUT else conv.y_shape
+    opt = conv.halo == 0
+    _check(lib().sscnn_grid_row_halo_gather(ctypes.byref(conv), which, _ptr(up, blk, "up", True),
+                                            _ptr(down, blk, "down", True),
+                                            _ptr(row_halo, conv.row_halo_shape(which), "row_halo", opt),
+                                            _stream(stream)), "grid_row_halo_gather")
+
+
+def grid_col_halo_gather(conv: GConv, which: int, left, left_row_halo, right, right_row_halo, col_halo, stream=None):
+    """Phase 2 (sscnn_grid_col_halo_gather): columns over the extended rows from the blocks left / right
+    and their phase-1 row halos."""
+    blk = conv.x_shape if which == HALO_INPUT else conv.y_shape
+    rs = conv.row_halo_shape(which)
+    opt = conv.halo == 0
+    _check(lib().sscnn_grid_col_halo_gather(
+        ctypes.byref(conv), which, _ptr(left, blk, "left", True), _ptr(left_row_halo, rs, "left_row_halo", True),
+        _ptr(right, blk, "right", True), _ptr(right_row_halo, rs, "right_row_halo", True),
+        _ptr(col_halo, conv.col_halo_shape(which), "col_halo", opt), _stream(stream)), "grid_col_halo_gather")
+
+
+def gconv_fwd(conv: GConv, x, x_row_halo, x_col_halo, weight, bias, y, stream=None):
+    opt = conv.halo == 0
+    _check(lib().sscnn_gconv_fwd(
+        ctypes.byref(conv), _ptr(x, conv.x_shape, "x"),
+        _ptr(x_row_halo, conv.row_halo_shape(HALO_INPUT), "x_row_halo", opt),
+        _ptr(x_col_halo, conv.col_halo_shape(HALO_INPUT), "x_col_halo", opt), _ptr(weight, conv.w_shape, "weight"),
+        _ptr(bias, (conv.c_out,), "bias", True), _ptr(y, conv.y_shape, "y"), _stream(stream)), "gconv_fwd")
+
+
+def gconv_bwd_weight_workspace_bytes(conv: GConv) -> int:
+    return int(lib().sscnn_gconv_bwd_weight_workspace_bytes(ctypes.byref(conv)))
+
+
+def new_gworkspace(conv: GConv, device="cuda"):
+    nbytes = gconv_bwd_weight_workspace_bytes(conv)
+    if nbytes == 0:
+        return None
+    import torch
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def gconv_bwd_input(conv: GConv, grad_y, gy_row_halo, gy_col_halo, weight, grad_x, stream=None):
+    opt = conv.halo == 0
+    _check(lib().sscnn_gconv_bwd_input(
+        ctypes.byref(conv), _ptr(grad_y, conv.y_shape, "grad_y"),
+        _ptr(gy_row_halo, conv.row_halo_shape(HALO_GRAD_OUTPUT), "gy_row_halo", opt),
+        _ptr(gy_col_halo, conv.col_halo_shape(HALO_GRAD_OUTPUT), "gy_col_halo", opt),
+        _ptr(weight, conv.w_shape, "weight"), _ptr(grad_x, conv.x_shape, "grad_x"), _stream(stream)),
+        "gconv_bwd_input")
+
+
+def gconv_bwd_weight_partial(conv: GConv, x, x_row_halo, x_col_halo, grad_y, grad_w_part, grad_b_part,
+                             workspace=None, stream=None):
+    opt = conv.halo == 0
+    ws_ptr, ws_bytes = _workspace(workspace)
+    _check(lib().sscnn_gconv_bwd_weight_partial(
+        ctypes.byref(conv), _ptr(x, conv.x_shape, "x"),
+        _ptr(x_row_halo, conv.row_halo_shape(HALO_INPUT), "x_row_halo", opt),
+        _ptr(x_col_halo, conv.col_halo_shape(HALO_INPUT), "x_col_halo", opt), _ptr(grad_y, conv.y_shape, "grad_y"),
+        _ptr(grad_w_part, conv.w_shape, "grad_w_part"), _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True),
+        ws_ptr, ws_bytes, _stream(stream)), "gconv_bwd_weight_partial")
+
+
+def gconv_bwd(conv: GConv, x, x_row_halo, x_col_halo, grad_y, gy_row_halo, gy_col_halo, weight, grad_x,
+              grad_w_part, grad_b_part, workspace=None, stream=None):
+    opt = conv.halo == 0
+    ws_ptr, ws_bytes = _workspace(workspace)
+    _check(lib().sscnn_gconv_bwd(
+        ctypes.byref(conv), _ptr(x, conv.x_shape, "x"),
+        _ptr(x_row_halo, conv.row_halo_shape(HALO_INPUT), "x_row_halo", opt),
+        _ptr(x_col_halo, conv.col_halo_shape(HALO_INPUT), "x_col_halo", opt), _ptr(grad_y, conv.y_shape, "grad_y"),
+        _ptr(gy_row_halo, conv.row_halo_shape(HALO_GRAD_OUTPUT), "gy_row_halo", opt),
+        _ptr(gy_col_halo, conv.col_halo_shape(HALO_GRAD_OUTPUT), "gy_col_halo", opt),
+        _ptr(weight, conv.w_shape, "weight"), _ptr(grad_x, conv.x_shape, "grad_x"),
+        _ptr(grad_w_part, conv.w_shape, "grad_w_part"), _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True),
+        ws_ptr, ws_bytes, _stream(stream)), "gconv_bwd")
 
 
 # --- the ConvNeXt block's other steps ----------------------------------------------

@@ -368,3 +368,38 @@ def test_block_op_bindings_refuse_host_tensors():
         sscnn.layernorm_fwd(x, torch.ones(4), torch.zeros(4), x.clone(), torch.zeros(1, 2, 2), torch.zeros(1, 2, 2))
     with pytest.raises(ValueError):
         sscnn.gelu_fwd(x, x.clone())
+
+
+def test_gconv_init_and_gathers_validate():
+    """2-D shards: the supported layer kinds, the grid bounds and the
+    neighbour rules of the two exchange phases, checked before any launch."""
+    L = sscnn.lib()
+    F = FAKE
+    c = sscnn.gconv_init(2, 8, 8, 16, 32, 7, 1, 3, 8, 1, 3, 0, 2)        # depthwise 7x7, middle row, left column
+    assert (c.halo, c.h_out_local, c.w_out_local) == (3, 16, 32)
+    p = sscnn.gconv_init(1, 16, 32, 8, 16, 2, 2, 0, 1, 0, 2, 1, 2)       # 2x2/2 downsample: no halo
+    assert (p.halo, p.h_out_local, p.w_out_local) == (0, 4, 8)
+    with pytest.raises(sscnn.SscnnError) as e:
+        sscnn.gconv_init(1, 8, 8, 16, 32, 3, 1, 1, 1, 0, 2, 0, 2)        # dense 3x3: not on a 2-D grid
+    assert e.value.status == sscnn.EUNSUPPORTED
+    with pytest.raises(sscnn.SscnnError) as e:
+        sscnn.gconv_init(1, 8, 8, 16, 24, 7, 1, 3, 8, 0, 2, 0, 2)        # depthwise block width 24
+    assert e.value.status == sscnn.EUNSUPPORTED
+    with pytest.raises(sscnn.SscnnError) as e:
+        sscnn.gconv_init(1, 8, 8, 16, 32, 7, 1, 3, 8, 2, 2, 0, 2)        # shard_h outside the grid
+    assert e.value.status == sscnn.EINVAL
+    r = ctypes.byref(c)
+    # phase 1: middle row needs both up and down
+    assert L.sscnn_grid_row_halo_gather(r, 0, None, F, F, None) == sscnn.EINVAL
+    assert L.sscnn_grid_row_halo_gather(r, 0, F, None, F, None) == sscnn.EINVAL
+    # phase 2: left column has no left neighbour; a right neighbour needs its row halo
+    assert L.sscnn_grid_col_halo_gather(r, 0, F, F, F, F, F, None) == sscnn.EINVAL
+    assert L.sscnn_grid_col_halo_gather(r, 0, None, None, F, None, F, None) == sscnn.EINVAL
+    assert L.sscnn_grid_col_halo_gather(r, 2, None, None, F, F, F, None) == sscnn.EINVAL
+    # the convolution calls need both halos when the layer has one
+    assert L.sscnn_gconv_fwd(r, F, None, F, F, None, F, None) == sscnn.EINVAL
+    assert L.sscnn_gconv_fwd(r, F, F, None, F, None, F, None) == sscnn.EINVAL
+    c.halo = 1
+    assert L.sscnn_gconv_fwd(r, F, F, F, F, None, F, None) == sscnn.EINVAL      # edited descriptor
+    # no halo: the gathers have nothing to do
+    assert L.sscnn_grid_row_halo_gather(ctypes.byref(p), 0, F, None, None, None) == sscnn.OK
