@@ -32,6 +32,7 @@ for the depthwise ones.
     python bench.py --workload dw7_c256_hshard   # the same step on a split along H (row halos)
     python bench.py --workload convnext_xl_w2048|convnext_xl_w4096   # the stack, per layer
     python bench.py --workload convnext_block_c256   # a whole ConvNeXt block on the C=256 shard, per op
+    python bench.py --workload dw7_c256_grid   # the depthwise step on a 2 x 2 grid of blocks (2-D shards)
     python bench.py --summarize DIR [DIR ...] [--traffic-op OP --traffic-kernels "K1;K2"]
                                       # text summary of rocprofv3 output directories
 """
@@ -70,7 +71,7 @@ def _parse():
     ap.add_argument("--workload", default="dw7_c256",
                     help="dw7_c256 (default), dense5x5_c256, dense5x5_tiny, dw7_c256_hshard (the same "
                          "depthwise map split along H), a stack: convnext_xl_w2048, convnext_xl_w4096, or a "
-                         "ConvNeXt block: convnext_block_c256")
+                         "ConvNeXt block: convnext_block_c256, or 2-D shards: dw7_c256_grid")
     ap.add_argument("--sets", type=int, default=3, help="independent buffer sets rotated per step")
     ap.add_argument("--op-reps", type=int, default=20, help="back-to-back calls per operation timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -163,6 +164,8 @@ def main():
     wl = workloads.WORKLOADS[args.workload]
     if wl.kind == "block":
         return block_bench(args, wl)
+    if wl.kind == "grid":
+        return grid_bench(args, wl)
     if len(wl.layers) > 1:
         return stack_bench(args, wl)
     L = wl.layers[0]
@@ -494,6 +497,120 @@ def _layer_work(c, L):
             "reduce": ((c.num_shards + 1) * (w_b + b_b), 0),
             "halo_x": (2 * n * ci * h * (c.halo_l + c.halo_r) * f4, 0),
             "halo_g": (2 * n * co * ho * (c.ghalo_l + c.ghalo_r) * f4, 0)}
+
+
+def grid_bench(args, wl):
+    """2-D H x W shards on a 2 x 2 grid: one step is the measured block's
+    row-then-column halo exchange of its input, its forward, the same exchange
+    of its grad_output, its backward and the reduction of the four blocks'
+    partials.  The neighbours' blocks and their phase-1 row halos (which carry
+    the corners) are prepared untimed; so are the other blocks' partials."""
+    import torch
+    from spatially_sharded_cnn_amd import sscnn, workloads
+
+    dev = "cuda"
+    L = wl.layers[0]
+    NH = NW = 2
+    bi, bj = divmod(wl.shard, NW)
+    T = workloads.generate(wl)
+    n, C, H, W = L.in_shape
+    bh, bw = H // NH, W // NW
+    blocks = [(i, j) for i in range(NH) for j in range(NW)]
+    cv = {ij: sscnn.gconv_init(n, L.ci, L.co, bh, bw, L.k, L.stride, L.pad, L.groups, ij[0], NH, ij[1], NW)
+          for ij in blocks}
+    blk = lambda a, i, j: torch.from_numpy(np.ascontiguousarray(a[:, :, i * bh:(i + 1) * bh, j * bw:(j + 1) * bw])).to(dev)
+    X = {ij: blk(T.x, *ij) for ij in blocks}
+    G = {ij: blk(T.g, *ij) for ij in blocks}
+    wt, b = torch.from_numpy(T.weights[0]).to(dev), torch.from_numpy(T.biases[0]).to(dev)
+    c = cv[bi, bj]
+    e = lambda shape: torch.empty(shape, device=dev)
+    RX = {ij: e(cv[ij].row_halo_shape(sscnn.HALO_INPUT)) for ij in blocks}
+    RG = {ij: e(cv[ij].row_halo_shape(sscnn.HALO_GRAD_OUTPUT)) for ij in blocks}
+    nb = lambda d, i, j: d.get((i, j))
+    for (i, j) in blocks:       # phase 1 everywhere (the neighbours' row halos are phase 2's input)
+        sscnn.grid_row_halo_gather(cv[i, j], sscnn.HALO_INPUT, nb(X, i - 1, j), nb(X, i + 1, j), RX[i, j])
+        sscnn.grid_row_halo_gather(cv[i, j], sscnn.HALO_GRAD_OUTPUT, nb(G, i - 1, j), nb(G, i + 1, j), RG[i, j])
+    cx, cg = e(c.col_halo_shape(sscnn.HALO_INPUT)), e(c.col_halo_shape(sscnn.HALO_GRAD_OUTPUT))
+    y, dx = e(c.y_shape), e(c.x_shape)
+    nw_ = int(np.prod(c.w_shape))
+    parts = [e((nw_ + c.c_out,)).normal_() for _ in blocks]
+    me = blocks.index((bi, bj))
+    gw, gb = parts[me][:nw_].view(c.w_shape), parts[me][nw_:]
+    red = e((nw_ + c.c_out,))
+    ws = sscnn.new_gworkspace(c)
+    i, j = bi, bj
+    ops = [
+        ("row_halo_x", lambda: sscnn.grid_row_halo_gather(c, sscnn.HALO_INPUT, nb(X, i - 1, j), nb(X, i + 1, j),
+                                                          RX[i, j])),
+        ("col_halo_x", lambda: sscnn.grid_col_halo_gather(c, sscnn.HALO_INPUT, nb(X, i, j - 1), nb(RX, i, j - 1),
+                                                          nb(X, i, j + 1), nb(RX, i, j + 1), cx)),
+        ("conv_fwd", lambda: sscnn.gconv_fwd(c, X[i, j], RX[i, j], cx, wt, b, y)),
+        ("row_halo_g", lambda: sscnn.grid_row_halo_gather(c, sscnn.HALO_GRAD_OUTPUT, nb(G, i - 1, j),
+                                                          nb(G, i + 1, j), RG[i, j])),
+        ("col_halo_g", lambda: sscnn.grid_col_halo_gather(c, sscnn.HALO_GRAD_OUTPUT, nb(G, i, j - 1),
+                                                          nb(RG, i, j - 1), nb(G, i, j + 1), nb(RG, i, j + 1), cg)),
+        ("conv_bwd", lambda: sscnn.gconv_bwd(c, X[i, j], RX[i, j], cx, G[i, j], RG[i, j], cg, wt, dx, gw, gb, ws)),
+        ("partial_reduce", lambda: sscnn.partial_reduce(parts, red)),
+    ]
+
+    def step():
+        for _, f in ops:
+            f()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    spread = step_spread(lambda k: step(), args.steps)
+    op_us = {}
+    for name, f in ops:
+        f()
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(args.op_reps):
+            f()
+        a1.record()
+        torch.cuda.synchronize()
+        op_us[name] = round(1e3 * a0.elapsed_time(a1) / args.op_reps, 2)
+
+    f4, hh = 4, c.halo
+    x_ext = n * C * (bh + 2 * hh) * (bw + 2 * hh) * f4
+    x_b = n * C * bh * bw * f4
+    w_b, b_b = int(np.prod(c.w_shape)) * f4, c.c_out * f4
+    flops = 2 * (L.ci // L.groups) * L.k * L.k * n * L.co * bh * bw
+    work = {"conv_fwd": (x_ext + w_b + b_b + x_b, flops),
+            "conv_bwd": (2 * x_ext + w_b + x_b + w_b + b_b, 2 * flops),
+            "partial_reduce": ((len(blocks) + 1) * (w_b + b_b), 0)}
+    step_bytes = sum(v[0] for v in work.values())
+    step_flops = sum(v[1] for v in work.values())
+    t = op_us["conv_bwd"]
+    bb, ff = work["conv_bwd"]
+    roof = {"bound": "hbm", "achieved": round(bb / (t * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof.update(frac=round(roof["achieved"] / roof["peak"], 4), traffic=None, op="conv_bwd", avg_us=t,
+                algorithmic_bytes=bb, algorithmic_flops=ff)
+    step_s = ms_per_step * 1e-3
+    out = {
+        "metric": METRIC, "value": round(step_bytes / step_s / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "block": [bi, bj], "grid": [NH, NW],
+                   "shard_input": list(c.x_shape)},
+        "tflops": round(step_flops / step_s / 1e12, 2), "step_bytes": step_bytes, "step_flops": step_flops,
+        "hbm_roofline_frac": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4), "roofline": roof,
+        "ops_us": op_us, "step_spread": spread, "wall_s_timed": round(wall, 4), "gpu_clocks": gpu_clocks(),
+        "source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def block_bench(args, wl):

@@ -112,6 +112,12 @@ WORKLOADS = {
         description="ConvNeXt block at C=256 (dw 7x7, LayerNorm, 1x1 256->1024, GELU, 1x1 1024->256, layer "
                     "scale, DropPath 0.1, residual): shard (7,256,128,64) of a (7,256,128,256) map",
         kind="block"),
+    "dw7_c256_grid": Workload(
+        "dw7_c256_grid",
+        (_layer("dw", 256, 256, 7, 1, 3, 256, (7, 256, 128, 256), (7, 256, 128, 256)),),
+        num_shards=4, shard=3, seed=1002, dist="normal",
+        description="depthwise 7x7 s1 p3 C=256 on a 2x2 grid of blocks: block (1,1), (7,256,64,128), of the same "
+                    "(7,256,128,256) map, 3-row and 3-column halos with corners", kind="grid"),
     "dense5x5_c256": Workload(
         "dense5x5_c256",
         (_layer("conv", 256, 256, 5, 1, 2, 1, (7, 256, 128, 512), (7, 256, 128, 512)),),
