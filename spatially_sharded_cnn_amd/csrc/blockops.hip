@@ -6,10 +6,12 @@
 // reduced like the convolutions' (kwkr.cn retelling, section 3.1: the
 // DropPath layer is distributed with its random state kept consistent).
 //
-//  * LayerNorm: a workgroup takes 64 consecutive pixels and its 4 waves split
+//  * LayerNorm: a workgroup takes 64 consecutive pixels and its waves split
 //    the C values of each (so every load is a 256-byte run of one channel
-//    row), twice for the mean and the variance and once to write; the
-//    backward recomputes x-hat from the saved mean and rstd.  The per-channel
+//    row).  Up to C = 1024 (512 in the backward) each thread keeps its
+//    values in registers and reads them once; wider maps take them from
+//    memory again for each pass.  The backward recomputes x-hat from the
+//    saved mean and rstd.  The per-channel
 //    weight and bias gradients are a second kernel, one workgroup per
 //    channel, reduced in a fixed order (bitwise reproducible).
 //  * GELU: elementwise, 4 values per thread, with the device library's erff
@@ -37,12 +39,15 @@ constexpr int kThreads = 256;
 
 constexpr int kPix = 64, kGroups = 4;
 
-// sum over the 4 waves of v for this lane's pixel, in wave order
+// sum over the G waves of v for this lane's pixel, in wave order
+template <int G = kGroups>
 __device__ __forceinline__ float pixel_sum(float v, float (*red)[kPix], int g, int lane)
 {
     red[g][lane] = v;
     __syncthreads();
-    const float r = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    float r = red[0][lane];
+#pragma unroll
+    for (int i = 1; i < G; ++i) r += red[i][lane];
     __syncthreads();
     return r;
 }
@@ -118,6 +123,101 @@ ln_bwd_kernel(const float* __restrict__ x, const float* __restrict__ dy, const f
         const float gg = dy[base + c * HW] * gamma[c];
         const float xh = (x[base + c * HW] - mean) * rstd;
         dx[base + c * HW] = rstd * (gg - a - xh * b);
+    }
+}
+
+// The same two passes with the pixel's values held in registers, for C up to
+// G * V: G waves per 64 pixels, thread (g, lane) keeps channels g, g + G, ...
+// (at most V of them), so x -- and dy in the backward -- is read from memory
+// once.  The per-thread sums run in channel order and the per-pixel sums in
+// wave order, as above: with G = 4 the results equal the loop kernels' bit
+// for bit.  Pixels past the end read pixel 0 (in bounds) and store nothing.
+template <int G, int V>
+__global__ void __launch_bounds__(kPix * G)
+ln_fwd_reg_kernel(const float* __restrict__ x, const float* __restrict__ gamma, const float* __restrict__ beta,
+                  float* __restrict__ y, float* __restrict__ mean_out, float* __restrict__ rstd_out, int C,
+                  int64_t HW, int64_t npix, float eps)
+{
+    __shared__ float red[G][kPix];
+    const int lane = threadIdx.x % kPix;
+    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kPix);
+    const int64_t t = (int64_t)blockIdx.x * kPix + lane;
+    const bool live = t < npix;
+    const int64_t tt = live ? t : 0;
+    const int64_t n = tt / HW, p = tt - n * HW;
+    const float* xp = x + n * C * HW + p;
+    float v[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        if (g + k * G < C) v[k] = xp[(int64_t)(g + k * G) * HW];
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        if (g + k * G < C) s += v[k];
+    const float mean = pixel_sum<G>(s, red, g, lane) / (float)C;
+    float q = 0.f;
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        if (g + k * G < C) {
+            const float d = v[k] - mean;
+            q = __builtin_fmaf(d, d, q);
+        }
+    const float rstd = 1.f / sqrtf(pixel_sum<G>(q, red, g, lane) / (float)C + eps);
+    if (!live) return;
+    float* yp = y + n * C * HW + p;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const int c = g + k * G;
+        if (c < C) yp[(int64_t)c * HW] = __builtin_fmaf((v[k] - mean) * rstd, gamma[c], beta[c]);
+    }
+    if (g == 0) {
+        mean_out[t] = mean;
+        rstd_out[t] = rstd;
+    }
+}
+
+template <int G, int V>
+__global__ void __launch_bounds__(kPix * G)
+ln_bwd_reg_kernel(const float* __restrict__ x, const float* __restrict__ dy, const float* __restrict__ gamma,
+                  const float* __restrict__ mean_in, const float* __restrict__ rstd_in, float* __restrict__ dx,
+                  int C, int64_t HW, int64_t npix)
+{
+#pragma clang fp contract(off)
+    __shared__ float red[G][kPix];
+    const int lane = threadIdx.x % kPix;
+    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kPix);
+    const int64_t t = (int64_t)blockIdx.x * kPix + lane;
+    const bool live = t < npix;
+    const int64_t tt = live ? t : 0;
+    const int64_t n = tt / HW, p = tt - n * HW;
+    const int64_t base = n * C * HW + p;
+    const float mean = mean_in[tt], rstd = rstd_in[tt];
+    float xv[V], gv[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const int c = g + k * G;
+        if (c < C) {
+            xv[k] = x[base + (int64_t)c * HW];
+            gv[k] = dy[base + (int64_t)c * HW] * gamma[c];
+        }
+    }
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        if (g + k * G < C) {
+            a += gv[k];
+            b = __builtin_fmaf(gv[k], (xv[k] - mean) * rstd, b);
+        }
+    a = pixel_sum<G>(a, red, g, lane) / (float)C;
+    b = pixel_sum<G>(b, red, g, lane) / (float)C;
+    if (!live) return;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const int c = g + k * G;
+        if (c < C) {
+            const float xh = (xv[k] - mean) * rstd;
+            dx[base + (int64_t)c * HW] = rstd * (gv[k] - a - xh * b);
+        }
     }
 }
 
@@ -304,8 +404,22 @@ hipError_t launch_layernorm_fwd(int n, int c, int64_t hw, float eps, const float
                                 const float* beta, float* y, float* mean, float* rstd, hipStream_t st)
 {
     const int64_t npix = (int64_t)n * hw;
-    hipLaunchKernelGGL(ln_fwd_kernel, dim3((unsigned)((npix + kPix - 1) / kPix)), dim3(kPix * kGroups), 0, st, x,
-                       gamma, beta, y, mean, rstd, c, hw, npix, eps);
+    const dim3 grid((unsigned)((npix + kPix - 1) / kPix));
+#define SSCNN_LN_FWD(G, V)                                                                                  \
+    hipLaunchKernelGGL((ln_fwd_reg_kernel<G, V>), grid, dim3(kPix * G), 0, st, x, gamma, beta, y, mean, rstd, c, \
+                       hw, npix, eps)
+    if (c <= 64)
+        SSCNN_LN_FWD(4, 16);
+    else if (c <= 256)
+        SSCNN_LN_FWD(4, 64);
+    else if (c <= 512)
+        SSCNN_LN_FWD(8, 64);
+    else if (c <= 1024)
+        SSCNN_LN_FWD(16, 64);
+    else
+        hipLaunchKernelGGL(ln_fwd_kernel, grid, dim3(kPix * kGroups), 0, st, x, gamma, beta, y, mean, rstd, c, hw,
+                           npix, eps);
+#undef SSCNN_LN_FWD
     return hipGetLastError();
 }
 
@@ -315,8 +429,20 @@ hipError_t launch_layernorm_bwd(int n, int c, int64_t hw, const float* x, const 
 {
     const int64_t npix = (int64_t)n * hw;
     if (dx) {
-        hipLaunchKernelGGL(ln_bwd_kernel, dim3((unsigned)((npix + kPix - 1) / kPix)), dim3(kPix * kGroups), 0, st,
-                           x, dy, gamma, mean, rstd, dx, c, hw, npix);
+        const dim3 grid((unsigned)((npix + kPix - 1) / kPix));
+#define SSCNN_LN_BWD(G, V)                                                                                      \
+    hipLaunchKernelGGL((ln_bwd_reg_kernel<G, V>), grid, dim3(kPix * G), 0, st, x, dy, gamma, mean, rstd, dx, c, hw, \
+                       npix)
+        if (c <= 64)
+            SSCNN_LN_BWD(4, 16);
+        else if (c <= 256)
+            SSCNN_LN_BWD(8, 32);
+        else if (c <= 512)
+            SSCNN_LN_BWD(16, 32);
+        else
+            hipLaunchKernelGGL(ln_bwd_kernel, grid, dim3(kPix * kGroups), 0, st, x, dy, gamma, mean, rstd, dx, c,
+                               hw, npix);
+#undef SSCNN_LN_BWD
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -29,9 +29,12 @@ def _rand(shape, seed, scale=1.0, shift=0.0):
     return (np.random.default_rng(seed).standard_normal(shape) * scale + shift).astype(np.float32)
 
 
-# (name, (n, c, h, w)): the c2 block's shard shape, a ragged one, a single channel, a single pixel row
+# (name, (n, c, h, w)): the c2 block's shard shape, a ragged one, a single channel, a single pixel row,
+# and channel counts that reach each register-held kernel (up to 1024 forward, 512 backward) and the
+# loop kernels beyond them, full and ragged
 LN_SHAPES = [("c256_shard", (2, 256, 16, 64)), ("ragged", (3, 37, 5, 7)), ("one_channel", (2, 1, 4, 4)),
-             ("wide_c", (1, 1024, 2, 8))]
+             ("wide_c", (1, 1024, 2, 8)), ("c100_ragged", (2, 100, 3, 5)), ("c512", (1, 512, 3, 8)),
+             ("c768", (1, 768, 2, 5)), ("c2048", (1, 2048, 2, 4)), ("c1100_ragged", (1, 1100, 1, 7))]
 
 
 def _ln(x, gamma, beta, eps=1e-6):
