@@ -656,8 +656,8 @@ def block_bench(args, wl):
     xh, y_dw, y_ln = e(cdw.halo_shape(sscnn.HALO_INPUT)), e(cdw.y_shape), e(cdw.y_shape)
     mean, rstd = e((n, H, wl_)), e((n, H, wl_))
     y1, a1, y2, scales, out = e(c1.y_shape), e(c1.y_shape), e(c2.y_shape), e((n,)), e(c2.y_shape)
-    dh2, da1, dy1, dln, ddw, dx = e(c2.y_shape), e(c1.y_shape), e(c1.y_shape), e(cdw.y_shape), e(cdw.y_shape), e(
-        cdw.x_shape)
+    dh2, da1, dy1 = e(c2.y_shape), e(c1.y_shape), e(c1.y_shape)
+    dln, ddw, dx = e(cdw.y_shape), e(cdw.y_shape), e(cdw.x_shape)
     gh = e(cdw.halo_shape(sscnn.HALO_GRAD_OUTPUT))
     parts = {name: [e((cnt,)) for _ in range(S)] for name, cnt in
              (("gamma", C), ("pw2", int(np.prod(c2.w_shape)) + c2.c_out), ("pw1", int(np.prod(c1.w_shape)) + c1.c_out),
@@ -683,14 +683,16 @@ def block_bench(args, wl):
         ("dw.fwd", lambda: sscnn.conv_fwd(cdw, x, xh, wts[0], bss[0], y_dw), *wk["dw"]["fwd"], False),
         ("ln.fwd", lambda: sscnn.layernorm_fwd(y_dw, ln_w, ln_b, y_ln, mean, rstd), 2 * act + 2 * n * P * f4, 0,
          False),
-        ("pw1.fwd", lambda: sscnn.conv_fwd(c1, y_ln, None, wts[1], bss[1], y1), *wk["pw1"]["fwd"], True),
-        ("gelu.fwd", lambda: sscnn.gelu_fwd(y1, a1), 2 * act4, 0, False),
+        # pw1 with GELU in its epilogue: y1 (pre-activation, kept for the backward) and a1 = GELU(y1)
+        ("pw1.fwd_gelu", lambda: sscnn.pointwise_gelu_fwd(c1, y_ln, wts[1], bss[1], y1, a1),
+         wk["pw1"]["fwd"][0] + act4, wk["pw1"]["fwd"][1], True),
         ("pw2.fwd", lambda: sscnn.conv_fwd(c2, a1, None, wts[2], bss[2], y2), *wk["pw2"]["fwd"], True),
         ("droppath", lambda: sscnn.droppath_scales(wl.seed, 0, keep, scales), n * f4, 0, False),
         ("scale.fwd", lambda: sscnn.layer_scale_residual_fwd(x, y2, gamma, scales, out), 3 * act, 0, False),
         ("scale.bwd", lambda: sscnn.layer_scale_residual_bwd(y2, gout, gamma, scales, dh2, parts["gamma"][s]),
          3 * act, 0, False),
         ("scale.reduce", lambda: sscnn.partial_reduce(parts["gamma"], reds["gamma"]), *red_b("gamma"), False),
+        # (the fused sscnn_pointwise_bwd_input_gelu measured slower than these two passes)
         ("pw2.bwd", lambda: sscnn.conv_bwd(c2, a1, None, dh2, None, wts[2], da1, *wparts("pw2", c2), ws["pw2"]),
          *wk["pw2"]["bwd"], True),
         ("pw2.reduce", lambda: sscnn.partial_reduce(parts["pw2"], reds["pw2"]), *red_b("pw2"), False),

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSCNN_ABI_VERSION 6
+#define SSCNN_ABI_VERSION 7
 
 /* Status codes. */
 #define SSCNN_OK 0
@@ -457,6 +457,25 @@ int sscnn_layernorm_bwd(int32_t n, int32_t c, int32_t h, int32_t w, const float 
  * gradient dx = dy * (Phi(x) + x * phi(x)); count elements. */
 int sscnn_gelu_fwd(int64_t count, const float *x, float *y, void *stream);
 int sscnn_gelu_bwd(int64_t count, const float *x, const float *dy, float *dx, void *stream);
+
+/* The block's 1x1 expansion followed by GELU, in one pass: y = conv_fwd(x)
+ * (the pre-activation, kept for the backward) and y_act = GELU(y), both with
+ * y's shape.  conv must be pointwise (k 1, stride 1, pad 0, groups 1; it
+ * needs no halo, so it serves W-, H- or 2-D shards alike, each described as
+ * one whole slice) with c_in, c_out and w_local multiples of 16 and fewer
+ * than 2^31 elements per tensor (SSCNN_EUNSUPPORTED otherwise).  y, y_act
+ * and x must be distinct (SSCNN_EINVAL).  Equals sscnn_conv_fwd then
+ * sscnn_gelu_fwd. */
+int sscnn_pointwise_gelu_fwd(const sscnn_conv_t *conv, const float *x, const float *weight,
+                             const float *bias, float *y, float *y_act, void *stream);
+
+/* The gradient through the block's 1x1 projection and the GELU before it:
+ * grad_x = conv_bwd_input(grad_y) * GELU'(pre), pre (x's shape) being the
+ * saved pre-activation.  Same conditions as sscnn_pointwise_gelu_fwd, and
+ * grad_x distinct from every input; equals sscnn_conv_bwd_input then
+ * sscnn_gelu_bwd. */
+int sscnn_pointwise_bwd_input_gelu(const sscnn_conv_t *conv, const float *grad_y, const float *weight,
+                                   const float *pre, float *grad_x, void *stream);
 
 /* DropPath (stochastic depth) factors for n samples: scales[i] = 1 / keep_prob
  * if sample i is kept, else 0; keep_prob >= 1 gives all ones.  Sample i is

@@ -260,6 +260,85 @@ class _Gelu(torch.autograd.Function):
         return tuple(dxs)
 
 
+def _pointwise_desc(x, c_out):
+    """A 1x1 layer over one shard, described as one whole slice: a pointwise
+    layer needs no halo, so W-, H- and 2-D shards are alike to it."""
+    n, c, h, w = x.shape
+    return sscnn.conv_init(n, c, c_out, h, w, 1, 1, 0, 1, 0, 1)
+
+
+def _mlp_fusable(xs, c_in, c_hidden, c_out):
+    """Whether the fused pointwise calls take these shards (the matrix-core
+    path's conditions: channels and slice width multiples of 16)."""
+    return all(c % 16 == 0 for c in (c_in, c_hidden, c_out)) and \
+        all(x.shape[3] % 16 == 0 and x.numel() // c_in * c_hidden < 2 ** 31 for x in xs)
+
+
+class _PointwiseMLP(torch.autograd.Function):
+    """pw2(GELU(pw1(x))) on every shard, with GELU inside pw1's kernel: its
+    forward writes the pre-activation h and GELU(h) together (h is kept for
+    GELU's gradient in the backward).
+    Arguments: (w1, b1, w2, b2, *x_shards) -> tuple of output shards."""
+
+    @staticmethod
+    def forward(ctx, w1, b1, w2, b2, *xs):
+        hs, acts, outs, convs = [], [], [], []
+        for x in xs:
+            c1, c2 = _pointwise_desc(x, w1.shape[0]), None
+            h = torch.empty(c1.y_shape, device=x.device, dtype=torch.float32)
+            a = torch.empty_like(h)
+            sscnn.pointwise_gelu_fwd(c1, x, w1, b1, h, a)
+            c2 = _pointwise_desc(a, w2.shape[0])
+            out = torch.empty(c2.y_shape, device=x.device, dtype=torch.float32)
+            sscnn.conv_fwd(c2, a, None, w2, b2, out)
+            hs.append(h)
+            acts.append(a)
+            outs.append(out)
+            convs.append((c1, c2))
+        ctx.convs = convs
+        ctx.has_bias = (b1 is not None, b2 is not None)
+        ctx.save_for_backward(w1, w2, *xs, *hs, *acts)
+        return tuple(outs)
+
+    @staticmethod
+    def backward(ctx, *gos):
+        S = len(ctx.convs)
+        saved = ctx.saved_tensors
+        w1, w2 = saved[0], saved[1]
+        xs, hs, acts = saved[2:2 + S], saved[2 + S:2 + 2 * S], saved[2 + 2 * S:2 + 3 * S]
+        dev = w1.device
+        gos = [torch.zeros(c2.y_shape, device=dev, dtype=torch.float32) if g is None else g.contiguous()
+               for g, (_, c2) in zip(gos, ctx.convs)]
+        need_dx = any(ctx.needs_input_grad[4:])
+        n1, n2 = w1.numel(), w2.numel()
+        parts1 = [torch.empty(n1 + w1.shape[0], device=dev, dtype=torch.float32) for _ in range(S)]
+        parts2 = [torch.empty(n2 + w2.shape[0], device=dev, dtype=torch.float32) for _ in range(S)]
+        dxs = []
+        for s, (c1, c2) in enumerate(ctx.convs):
+            # pw2's grad_input, then GELU's gradient as a pass of its own: measured
+            # faster than the fused sscnn_pointwise_bwd_input_gelu, whose epilogue
+            # transcendentals run at the matrix kernel's low occupancy
+            da, dh = torch.empty_like(hs[s]), torch.empty_like(hs[s])
+            sscnn.conv_bwd(c2, acts[s], None, gos[s], None, w2, da, parts2[s][:n2].view(w2.shape),
+                           parts2[s][n2:], sscnn.new_workspace(c2, device=dev))
+            sscnn.gelu_bwd(hs[s], da, dh)
+            del da
+            gw1, gb1 = parts1[s][:n1].view(w1.shape), parts1[s][n1:]
+            if need_dx:
+                dx = torch.empty(c1.x_shape, device=dev, dtype=torch.float32)
+                sscnn.conv_bwd(c1, xs[s], None, dh, None, w1, dx, gw1, gb1, sscnn.new_workspace(c1, device=dev))
+                dxs.append(dx)
+            else:
+                sscnn.conv_bwd_weight_partial(c1, xs[s], None, dh, gw1, gb1, sscnn.new_workspace(c1, device=dev))
+                dxs.append(None)
+        red1 = torch.empty(n1 + w1.shape[0], device=dev, dtype=torch.float32)
+        red2 = torch.empty(n2 + w2.shape[0], device=dev, dtype=torch.float32)
+        sscnn.partial_reduce(parts1, red1)
+        sscnn.partial_reduce(parts2, red2)
+        return (red1[:n1].view(w1.shape), red1[n1:] if ctx.has_bias[0] else None,
+                red2[:n2].view(w2.shape), red2[n2:] if ctx.has_bias[1] else None, *dxs)
+
+
 class _LayerScaleResidual(torch.autograd.Function):
     """out_s = x_s + scales[n] * (gamma[c] * h_s) for every shard s."""
 
@@ -299,7 +378,10 @@ class _LayerScaleResidual(torch.autograd.Function):
 
 class ShardedConvNeXtBlock(torch.nn.Module):
     """One ConvNeXt block over a list of S shards (W slices, or H slices with
-    dim=2): x + DropPath(gamma * pw2(GELU(pw1(LN(dw7x7(x)))))).
+    dim=2): x + DropPath(gamma * pw2(GELU(pw1(LN(dw7x7(x)))))).  When the
+    channel counts and slice width are multiples of 16, the forward GELU runs
+    inside the 1x1 expansion's kernel (_PointwiseMLP); otherwise as a pass of
+    its own.
 
     DropPath is active in training mode when drop_path > 0; its per-sample
     factors come from sscnn_droppath_scales with this block's seed and a call
@@ -325,9 +407,11 @@ class ShardedConvNeXtBlock(torch.nn.Module):
         xs = list(xs)
         h = self.dwconv(xs)
         h = list(_ChannelLayerNorm.apply(self.norm_weight, self.norm_bias, self.eps, *h))
-        h = self.pwconv1(h)
-        h = list(_Gelu.apply(*h))
-        h = self.pwconv2(h)
+        p1, p2 = self.pwconv1, self.pwconv2
+        if _mlp_fusable(h, self.dim, p1.out_channels, p2.out_channels):
+            h = list(_PointwiseMLP.apply(p1.weight, p1.bias, p2.weight, p2.bias, *h))
+        else:
+            h = p2(list(_Gelu.apply(*p1(h))))
         scales = None
         if self.training and self.drop_path > 0.0:
             scales = torch.empty(xs[0].shape[0], device=xs[0].device, dtype=torch.float32)

@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "blockops.h"
+#include "patchify.h"
 #include "depthwise.h"
 #include "edge.h"
 #include "internal.h"
@@ -465,6 +466,46 @@ int sscnn_gelu_bwd(int64_t count, const float* x, const float* dy, float* dx, vo
     TRY(need(dy, "dy"));
     TRY(need(dx, "dx"));
     return hip_status(launch_gelu_bwd(count, x, dy, dx, (hipStream_t)stream), "gelu_bwd launch");
+}
+
+// The fused pointwise calls run the matrix-core kernel of 1x1 layers with its
+// GELU epilogue; any other layer is refused rather than run in two passes.
+static int check_pointwise(const sscnn_conv_t* conv, Geom* g)
+{
+    TRY(check(conv, g));
+    if (g->k != 1 || g->stride != 1 || g->pad != 0 || g->groups != 1 || !patch_supported(*g))
+        return fail(SSCNN_EUNSUPPORTED, "fused GELU needs a pointwise layer on the matrix-core path "
+                    "(k=%d stride=%d pad=%d groups=%d)", g->k, g->stride, g->pad, g->groups);
+    return SSCNN_OK;
+}
+
+int sscnn_pointwise_gelu_fwd(const sscnn_conv_t* conv, const float* x, const float* weight, const float* bias,
+                             float* y, float* y_act, void* stream)
+{
+    Geom g;
+    TRY(check_pointwise(conv, &g));
+    TRY(need(x, "x"));
+    TRY(need(weight, "weight"));
+    TRY(optional(bias, "bias"));
+    TRY(need(y, "y"));
+    TRY(need(y_act, "y_act"));
+    if (y_act == y || y == x || y_act == x) return fail(SSCNN_EINVAL, "y or y_act aliases another argument");
+    return hip_status(launch_patch_fwd(g, x, weight, bias, y, (hipStream_t)stream, y_act),
+                      "pointwise_gelu_fwd launch");
+}
+
+int sscnn_pointwise_bwd_input_gelu(const sscnn_conv_t* conv, const float* grad_y, const float* weight,
+                                   const float* pre, float* grad_x, void* stream)
+{
+    Geom g;
+    TRY(check_pointwise(conv, &g));
+    TRY(need(grad_y, "grad_y"));
+    TRY(need(weight, "weight"));
+    TRY(need(pre, "pre"));
+    TRY(need(grad_x, "grad_x"));
+    if (grad_x == grad_y || grad_x == pre || grad_x == weight) return fail(SSCNN_EINVAL, "grad_x aliases an input");
+    return hip_status(launch_patch_bwd_input(g, grad_y, weight, grad_x, (hipStream_t)stream, pre),
+                      "pointwise_bwd_input_gelu launch");
 }
 
 int sscnn_droppath_scales(uint64_t seed, uint64_t offset, int32_t n, double keep_prob, float* scales, void* stream)

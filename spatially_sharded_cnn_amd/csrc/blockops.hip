@@ -24,6 +24,7 @@
 //    Tensor Parallelism": DropPath's Bernoulli draws must agree across GPUs).
 #include "internal.h"
 #include "blockops.h"
+#include "gelu.h"
 
 namespace sscnn {
 namespace {
@@ -266,18 +267,6 @@ ln_params_kernel(const float* __restrict__ x, const float* __restrict__ dy, cons
 }
 
 // ---- GELU ---------------------------------------------------------------------
-
-__device__ __forceinline__ float gelu(float v)
-{
-    return 0.5f * v * (1.f + erff(v * 0.70710678118654752f));
-}
-
-__device__ __forceinline__ float gelu_grad(float v)
-{
-    const float cdf = 0.5f * (1.f + erff(v * 0.70710678118654752f));
-    const float pdf = 0.39894228040143268f * expf(-0.5f * v * v);
-    return __builtin_fmaf(v, pdf, cdf);
-}
 
 __global__ void __launch_bounds__(kThreads)
 gelu_fwd_kernel(const float* __restrict__ x, float* __restrict__ y, int64_t count)

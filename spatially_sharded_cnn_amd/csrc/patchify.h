@@ -10,9 +10,12 @@ namespace sscnn {
 // output width a multiple of 16.
 bool patch_supported(const Geom& g);
 size_t patch_wgrad_workspace_bytes(const Geom& g);
+// act (pointwise layers only): also write GELU(y) there.
 hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const float* b, float* y,
-                            hipStream_t st);
-hipError_t launch_patch_bwd_input(const Geom& g, const float* gy, const float* w, float* gx, hipStream_t st);
+                            hipStream_t st, float* act = nullptr);
+// pre (pointwise layers only): write dX * GELU'(pre) instead of dX.
+hipError_t launch_patch_bwd_input(const Geom& g, const float* gy, const float* w, float* gx, hipStream_t st,
+                                  const float* pre = nullptr);
 hipError_t launch_patch_bwd_weight(const Geom& g, const float* x, const float* gy, float* gw, float* gb,
                                    void* ws, hipStream_t st);
 

@@ -14,6 +14,10 @@
 // materialised: operand tiles are gathered from NCHW straight into LDS (s
 // consecutive floats per (K group, pixel)), and grad_input's result is
 // scattered back to NCHW with one s-wide store per lane.
+// For the 1x1 expansion the block follows with GELU: its forward can write
+// GELU(Y) beside Y from the same registers, and the projection's grad_input
+// can leave dX * GELU'(pre) instead of dX, reading pre at the address it
+// stores to, so the elementwise passes over the 4C-channel tensor vanish.
 //
 // One kernel template serves the three products: a 256-thread workgroup
 // computes a 128 x 128 tile of the result, each of its 4 waves a 64 x 64
@@ -31,6 +35,7 @@
 // fixed-order stages when there are many: no atomics, bitwise reproducible.
 #include "internal.h"
 #include "patchify.h"
+#include "gelu.h"
 
 namespace sscnn {
 namespace {
@@ -65,6 +70,8 @@ struct PArgs {
     int tiles_m, tiles_n;             // result tiles (columns: pixels of one image for FWD / BWI)
     int splits, chunks;               // BWW: pixel sub-chunks of kSub, split into `splits` ranges
     int with_bias;                    // BWW: also sum grad_output per channel
+    float* act;           // FWD, pointwise only: GELU(Y) as well, or null
+    const float* pre;     // BWI, pointwise only: dX is scaled by GELU'(pre) (pre shaped like X), or null
 };
 
 __device__ __forceinline__ int64_t slab_floats(const PArgs& a) { return (int64_t)a.Co * (a.Kt + 1); }
@@ -394,8 +401,11 @@ patch_kernel(PArgs a)
                         float* yp = a.out + ((int64_t)outer * a.Co) * a.P + col;
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            if (row + r < a.Co)
-                                yp[(int64_t)(row + r) * a.P] = acc[x][y][4 * q + r] + (a.b ? a.b[row + r] : 0.f);
+                            if (row + r < a.Co) {
+                                const float v = acc[x][y][4 * q + r] + (a.b ? a.b[row + r] : 0.f);
+                                yp[(int64_t)(row + r) * a.P] = v;
+                                if (a.act) a.act[((int64_t)outer * a.Co + row + r) * a.P + col] = gelu(v);
+                            }
                     }
                 } else if constexpr (MODE == BWI) {
                     // rows = K = (ci, kh, kw), kw fastest: the 4 registers are s-wide runs of kw
@@ -405,8 +415,12 @@ patch_kernel(PArgs a)
                         if constexpr (S == 1) {
                             // rows are input channels: 4 channels of one pixel
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                dxi[((int64_t)(row + r) * a.H + i) * a.W + j] = acc[x][y][4 * q + r];
+                            for (int r = 0; r < 4; ++r) {
+                                const int64_t o = ((int64_t)(row + r) * a.H + i) * a.W + j;
+                                float v = acc[x][y][4 * q + r];
+                                if (a.pre) v = v * gelu_grad(a.pre[(int64_t)outer * a.Ci * a.H * a.W + o]);
+                                dxi[o] = v;
+                            }
                         } else if constexpr (S == 4) {
                             const int ci = row / 16, kh = (row / 4) % 4;
                             *reinterpret_cast<float4*>(dxi + ((int64_t)ci * a.H + i * 4 + kh) * a.W + j * 4) =
@@ -579,18 +593,21 @@ hipError_t launch_rows(PArgs& a, int rows, int tm, int s, hipStream_t st)
 }
 
 hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const float* b, float* y,
-                            hipStream_t st)
+                            hipStream_t st, float* act)
 {
+    if (act && g.k != 1) return hipErrorInvalidValue;
     PArgs a = make_args(g);
-    a.x = x; a.w = w; a.b = b; a.out = y;
+    a.x = x; a.w = w; a.b = b; a.out = y; a.act = act;
     a.tiles_n = (a.P + 127) / 128;
     return launch_rows<FWD>(a, a.Co, row_tile(a.Co, a, false), g.k, st);
 }
 
-hipError_t launch_patch_bwd_input(const Geom& g, const float* gy, const float* w, float* gx, hipStream_t st)
+hipError_t launch_patch_bwd_input(const Geom& g, const float* gy, const float* w, float* gx, hipStream_t st,
+                                  const float* pre)
 {
+    if (pre && g.k != 1) return hipErrorInvalidValue;
     PArgs a = make_args(g);
-    a.g = gy; a.w = w; a.out = gx;
+    a.g = gy; a.w = w; a.out = gx; a.pre = pre;
     a.tiles_n = (a.P + 127) / 128;
     return launch_rows<BWI>(a, a.Kt, row_tile(a.Kt, a, a.Kt <= kNarrowK), g.k, st);
 }

@@ -33,7 +33,7 @@ EXPORTED = (
     "sscnn_layer_scale_residual_fwd", "sscnn_layer_scale_residual_bwd",
     "sscnn_gconv_init", "sscnn_grid_row_halo_gather", "sscnn_grid_col_halo_gather", "sscnn_gconv_fwd",
     "sscnn_gconv_bwd_input", "sscnn_gconv_bwd_weight_workspace_bytes", "sscnn_gconv_bwd_weight_partial",
-    "sscnn_gconv_bwd",
+    "sscnn_gconv_bwd", "sscnn_pointwise_gelu_fwd", "sscnn_pointwise_bwd_input_gelu",
 )
 
 
@@ -145,6 +145,8 @@ def lib() -> ctypes.CDLL:
         L.sscnn_halo_gather.argtypes = [P, ctypes.c_int32, _vp, _vp, _vp, _vp]
         L.sscnn_conv_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp]
         L.sscnn_conv_bwd_input.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
+        L.sscnn_pointwise_gelu_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.sscnn_pointwise_bwd_input_gelu.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
         L.sscnn_conv_bwd_weight_workspace_bytes.argtypes = [P]
         L.sscnn_conv_bwd_weight_workspace_bytes.restype = ctypes.c_size_t
         L.sscnn_conv_bwd_weight_partial.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -197,7 +199,8 @@ def lib() -> ctypes.CDLL:
                   "sscnn_layernorm_fwd", "sscnn_layernorm_bwd", "sscnn_gelu_fwd", "sscnn_gelu_bwd",
                   "sscnn_droppath_scales", "sscnn_layer_scale_residual_fwd", "sscnn_layer_scale_residual_bwd",
                   "sscnn_gconv_init", "sscnn_grid_row_halo_gather", "sscnn_grid_col_halo_gather",
-                  "sscnn_gconv_fwd", "sscnn_gconv_bwd_input", "sscnn_gconv_bwd_weight_partial", "sscnn_gconv_bwd"):
+                  "sscnn_gconv_fwd", "sscnn_gconv_bwd_input", "sscnn_gconv_bwd_weight_partial", "sscnn_gconv_bwd",
+                  "sscnn_pointwise_gelu_fwd", "sscnn_pointwise_bwd_input_gelu"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -598,6 +601,24 @@ def gelu_bwd(x, dy, dx, stream=None):
     shape = tuple(x.shape)
     _check(lib().sscnn_gelu_bwd(x.numel(), _ptr(x, shape, "x"), _ptr(dy, shape, "dy"), _ptr(dx, shape, "dx"),
                                 _stream(stream)), "gelu_bwd")
+
+
+def pointwise_gelu_fwd(conv: Conv, x, weight, bias, y, y_act, stream=None):
+    """sscnn_pointwise_gelu_fwd: y = the 1x1 conv of x (pre-activation), y_act = GELU(y)."""
+    _check(lib().sscnn_pointwise_gelu_fwd(ctypes.byref(conv), _ptr(x, conv.x_shape, "x"),
+                                          _ptr(weight, conv.w_shape, "weight"),
+                                          _ptr(bias, (conv.c_out,), "bias", True), _ptr(y, conv.y_shape, "y"),
+                                          _ptr(y_act, conv.y_shape, "y_act"), _stream(stream)),
+           "pointwise_gelu_fwd")
+
+
+def pointwise_bwd_input_gelu(conv: Conv, grad_y, weight, pre, grad_x, stream=None):
+    """sscnn_pointwise_bwd_input_gelu: grad_x = (1x1 conv grad_input of grad_y) * GELU'(pre)."""
+    _check(lib().sscnn_pointwise_bwd_input_gelu(ctypes.byref(conv), _ptr(grad_y, conv.y_shape, "grad_y"),
+                                                _ptr(weight, conv.w_shape, "weight"),
+                                                _ptr(pre, conv.x_shape, "pre"),
+                                                _ptr(grad_x, conv.x_shape, "grad_x"), _stream(stream)),
+           "pointwise_bwd_input_gelu")
 
 
 def droppath_scales(seed: int, offset: int, keep_prob: float, scales, stream=None):

@@ -361,6 +361,28 @@ def test_block_op_calls_validate_before_launching():
     assert "aliases" in sscnn.last_error()
 
 
+def test_pointwise_gelu_calls_validate_before_launching():
+    """The fused 1x1 + GELU calls take only pointwise layers on the matrix-core
+    path and need every pointer; they refuse the rest on the host."""
+    L = sscnn.lib()
+    F, G = FAKE, FAKE + (1 << 20)
+    pw = sscnn.conv_init(1, 16, 32, 4, 16, 1, 1, 0, 1, 0, 1)
+    by = ctypes.byref
+    for bad in (sscnn.conv_init(1, 16, 32, 8, 16, 3, 1, 1, 1, 0, 1),    # 3x3
+                sscnn.conv_init(1, 16, 32, 8, 16, 2, 2, 0, 1, 0, 1),    # 2x2 patchify
+                sscnn.conv_init(1, 12, 32, 4, 16, 1, 1, 0, 1, 0, 1),    # c_in not a multiple of 16
+                sscnn.conv_init(1, 16, 32, 4, 8, 1, 1, 0, 1, 0, 1)):    # slice width not a multiple of 16
+        assert L.sscnn_pointwise_gelu_fwd(by(bad), F, F, None, G, G + 4096, None) == sscnn.EUNSUPPORTED
+        assert L.sscnn_pointwise_bwd_input_gelu(by(bad), F, F, F, G, None) == sscnn.EUNSUPPORTED
+    assert L.sscnn_pointwise_gelu_fwd(by(pw), F, F, None, G, None, None) == sscnn.EINVAL       # no y_act
+    assert L.sscnn_pointwise_gelu_fwd(by(pw), None, F, None, G, G + 4096, None) == sscnn.EINVAL
+    assert L.sscnn_pointwise_bwd_input_gelu(by(pw), F, F, None, G, None) == sscnn.EINVAL      # no pre
+    assert L.sscnn_pointwise_bwd_input_gelu(by(pw), F, F, F + 4, G, None) == sscnn.EINVAL     # misaligned
+    assert L.sscnn_pointwise_gelu_fwd(by(pw), F, F, None, G, G, None) == sscnn.EINVAL         # y_act is y
+    assert L.sscnn_pointwise_bwd_input_gelu(by(pw), F, F, G, G, None) == sscnn.EINVAL         # grad_x is pre
+    assert "aliases" in sscnn.last_error()
+
+
 def test_block_op_bindings_refuse_host_tensors():
     import torch
     x = torch.zeros(1, 4, 2, 2)

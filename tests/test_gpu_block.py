@@ -55,7 +55,8 @@ def _reference(x, P, scales, dim):
 CASES = [
     ("w_shards_droppath", (4, 32, 12, 4 * 16), 4, 3, 0.5),
     ("w_shards_no_droppath_tiled", (2, 16, 32, 2 * 64), 2, 3, 0.0),
-    ("h_shards_droppath", (3, 24, 2 * 10, 16), 2, 2, 0.25),
+    ("h_shards_droppath", (3, 24, 2 * 10, 16), 2, 2, 0.25),     # 24 channels: GELU as a pass of its own
+    ("h_shards_fused_gelu", (2, 32, 2 * 8, 32), 2, 2, 0.25),
 ]
 
 

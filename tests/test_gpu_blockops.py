@@ -144,3 +144,41 @@ def test_layer_scale_residual_matches_oracle(with_scales):
     assert_close(host(dg), dg_ref, TOL_GW, "dgamma")
     if with_scales:
         assert torch.equal(out[1], xd[1]) and not dh[1].any()      # the dropped sample
+
+
+# (name, (n, c_in, c_out, h, w)): the block's expansion and projection on a c2-style shard slice, a
+# ragged pixel count (h * w not a multiple of 128) and a one-image slice
+PW_SHAPES = [("expand", (2, 64, 256, 8, 32)), ("project", (2, 256, 64, 8, 32)), ("ragged", (3, 32, 48, 5, 16)),
+             ("one_image", (1, 16, 16, 3, 16))]
+
+
+@pytest.mark.parametrize("case", PW_SHAPES, ids=[c[0] for c in PW_SHAPES])
+def test_pointwise_gelu_matches_oracle(case):
+    """The fused 1x1 + GELU forward and the fused projection grad_input times
+    GELU'(pre), against the oracle's conv and GELU in float64, and bit for bit
+    against the same steps as separate calls."""
+    from oracle import conv_bwd_input, conv_fwd
+    name, (n, ci, co, h, w) = case
+    _say(f"  pointwise gelu {name} {(n, ci, co, h, w)}")
+    x, g = _rand((n, ci, h, w), 21), _rand((n, co, h, w), 22)
+    pre = _rand((n, ci, h, w), 23, 2.0)
+    wt, b = _rand((co, ci, 1, 1), 24, 0.1), _rand(co, 25, 0.1)
+    c = sscnn.conv_init(n, ci, co, h, w, 1, 1, 0, 1, 0, 1)
+    xd, gd, pd, wd, bd = to_dev(x), to_dev(g), to_dev(pre), to_dev(wt), to_dev(b)
+    y, ya = torch.empty(c.y_shape, device="cuda"), torch.empty(c.y_shape, device="cuda")
+    dx = torch.empty(c.x_shape, device="cuda")
+    sscnn.pointwise_gelu_fwd(c, xd, wd, bd, y, ya)
+    sscnn.pointwise_bwd_input_gelu(c, gd, wd, pd, dx)
+    # the unfused steps
+    y2, ya2 = torch.empty_like(y), torch.empty_like(y)
+    dxa, dx2 = torch.empty_like(dx), torch.empty_like(dx)
+    sscnn.conv_fwd(c, xd, None, wd, bd, y2)
+    sscnn.gelu_fwd(y2, ya2)
+    sscnn.conv_bwd_input(c, gd, None, wd, dxa)
+    sscnn.gelu_bwd(pd, dxa, dx2)
+    torch.cuda.synchronize()
+    y_ref = conv_fwd(x, wt, b, 1, 0, 1)
+    assert_close(host(y), y_ref, TOL_FWD, f"{name} y")
+    assert_close(host(ya), B.gelu_fwd(y_ref), TOL_FWD, f"{name} gelu(y)")
+    assert_close(host(dx), B.gelu_bwd(pre, conv_bwd_input(g, wt, x.shape, 1, 0, 1)), TOL_DX, f"{name} dx")
+    assert torch.equal(y, y2) and torch.equal(ya, ya2) and torch.equal(dx, dx2)
