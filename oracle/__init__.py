@@ -32,6 +32,14 @@ What is computed, and where it is defined:
   Replicate ones (blog, DTensor section; kwkr.cn retelling, section 2.2).
 * ``stack_forward`` / ``stack_backward`` -- a chain of the above for a
   ConvNeXt-style convolution stack.
+* ``patchify_fwd`` / ``patchify_bwd_input`` / ``patchify_bwd_weight`` -- the
+  same three definitions for a kernel equal to its stride with no padding
+  (the stem and the downsamples), where each output reads one disjoint
+  k x k patch, with the sum over (c, kh, kw) done by one numpy matrix
+  product.
+* ``stack_shard`` -- one W-shard's share of that chain (its outputs,
+  grad_inputs and partial gradients per layer), from the global tensors,
+  evaluating only the columns those results read.
 
 The C part (``oracle.c``) is built with plain ``gcc -O2 -fopenmp``; ``build()``
 compiles it, and the loaders compile it once if it is missing.
@@ -352,3 +360,200 @@ def stack_backward(acts, layers, g_final):
         out[l] = (g, dx, gw, gb)
         g = dx
     return out
+
+
+# --- patchify layers (kernel = stride, no padding) as a product of matrices --
+
+def _is_patchify(k: int, stride: int, pad: int, groups: int) -> bool:
+    return k == stride and pad == 0 and groups == 1
+
+
+def patchify_fwd(x, wt, bias, k: int, cols=None) -> np.ndarray:
+    """Forward of a k x k / stride k / pad 0 convolution written as the sum of
+    its definition over (c, kh, kw) done by one matrix product: the patches of
+    output columns cols = (j0, j1) laid out as rows (n, i, j) x (c, kh, kw),
+    times the weight laid out as (o) x (c, kh, kw).  The same numbers as
+    ``conv_fwd`` (each output reads exactly the k x k block at (i*k, j*k)),
+    up to summation order."""
+    x, wt = _f64(x), _f64(wt)
+    n, ci, h, w = x.shape
+    co = wt.shape[0]
+    ho, wo = h // k, w // k
+    j0, j1 = (0, wo) if cols is None else cols
+    xs = x[:, :, :ho * k, j0 * k:j1 * k].reshape(n, ci, ho, k, j1 - j0, k)
+    patches = xs.transpose(0, 2, 4, 1, 3, 5).reshape(n * ho * (j1 - j0), ci * k * k)
+    y = patches @ wt.reshape(co, ci * k * k).T
+    if bias is not None:
+        y = y + _f64(bias)[None, :]
+    return np.ascontiguousarray(y.reshape(n, ho, j1 - j0, co).transpose(0, 3, 1, 2))
+
+
+def patchify_bwd_input(g, wt, in_shape, k: int, cols=None) -> np.ndarray:
+    """grad_input of the same layer over input columns cols = (x0, x1): input
+    column q gets the gradient of output column q // k through tap q % k (and
+    none when it lies beyond the last whole patch, as do rows beyond the last
+    whole patch row).  The sum over output channels is one matrix product."""
+    g, wt = _f64(g), _f64(wt)
+    n, co, ho, wo = g.shape
+    _, ci, h, w = in_shape
+    x0, x1 = (0, w) if cols is None else cols
+    dx = np.zeros((n, ci, h, x1 - x0), dtype=np.float64)
+    p0, p1 = x0 // k, min(wo, -(-x1 // k))
+    if p1 > p0:
+        gm = g[:, :, :, p0:p1].transpose(0, 2, 3, 1).reshape(n * ho * (p1 - p0), co)
+        dp = gm @ wt.reshape(co, ci * k * k)
+        blk = dp.reshape(n, ho, p1 - p0, ci, k, k).transpose(0, 3, 1, 4, 2, 5).reshape(n, ci, ho * k, (p1 - p0) * k)
+        q0 = x0 - p0 * k
+        q1 = min(x1 - p0 * k, (p1 - p0) * k)
+        dx[:, :, :ho * k, 0:q1 - q0] = blk[:, :, :, q0:q1]
+    return dx
+
+
+def patchify_bwd_weight(x, g, k: int, cols=None):
+    """(grad_weight, grad_bias) of the same layer summed over output columns
+    cols = (j0, j1): the sum over (n, i, j) of grad_output times the patch,
+    as one matrix product; grad_bias is the sum of grad_output."""
+    x, g = _f64(x), _f64(g)
+    n, ci, h, w = x.shape
+    _, co, ho, wo = g.shape
+    j0, j1 = (0, wo) if cols is None else cols
+    xs = x[:, :, :ho * k, j0 * k:j1 * k].reshape(n, ci, ho, k, j1 - j0, k)
+    patches = xs.transpose(0, 2, 4, 1, 3, 5).reshape(n * ho * (j1 - j0), ci * k * k)
+    gm = g[:, :, :, j0:j1].transpose(0, 2, 3, 1).reshape(n * ho * (j1 - j0), co)
+    gw = (gm.T @ patches).reshape(co, ci, k, k)
+    gb = gm.sum(axis=0)
+    return gw, gb
+
+
+# --- one shard's share of a convolution stack, from the global tensors -------
+
+def _shard_range(width: int, num_shards: int, shard: int):
+    """Shard(3) column range [s*W/S, (s+1)*W/S) of a width-W tensor."""
+    assert width % num_shards == 0
+    wl = width // num_shards
+    return shard * wl, (shard + 1) * wl
+
+
+def _hull(a, b):
+    return min(a[0], b[0]), max(a[1], b[1])
+
+
+def input_columns_read(out_cols, k: int, stride: int, pad: int, w: int):
+    """Input columns that the output columns [j0, j1) read: output j reads
+    j*stride - pad + kw for kw < k, clipped to the image [0, w)."""
+    j0, j1 = out_cols
+    return max(0, j0 * stride - pad), min(w, (j1 - 1) * stride - pad + k)
+
+
+def output_columns_reaching(in_cols, k: int, stride: int, pad: int, wo: int):
+    """Output columns whose receptive field meets the input columns
+    [x0, x1): output j reads input j*stride - pad + kw, so it meets [x0, x1)
+    when j*stride is in (x0 + pad - k, x1 - 1 + pad]; clipped to [0, wo)."""
+    x0, x1 = in_cols
+    lo = -((-(x0 + pad - k + 1)) // stride)     # ceil((x0 + pad - k + 1) / stride)
+    hi = (x1 - 1 + pad) // stride + 1
+    return max(0, lo), min(wo, hi)
+
+
+def stack_shard(x, layers, g_final, num_shards: int, shard: int, gw_at=None):
+    """One W-shard's share of a convolution chain, computed from the GLOBAL
+    input x and the global gradient g_final of the last output, exactly as
+    ``stack_forward`` / ``stack_backward`` would give it but without
+    evaluating columns the shard's results never read.
+
+    Layer l's output is evaluated only on the columns needed for (a) the
+    shard's own output columns and (b) the columns the next layer reads;
+    every other column stays zero and is never read (the sums of the
+    definitions above reach only the receptive field).  Backward likewise
+    evaluates each layer's grad_input only on the shard's input columns plus
+    those the layer below reads.  The chain's placements are those of the
+    pages: every activation and gradient Shard(3), weights replicated,
+    weight / bias gradients partial over the shard's own output columns
+    (NVIDIA blog "Perception Model Training for Autonomous Vehicles with
+    Tensor Parallelism", DTensor section).  Patchify layers (kernel = stride,
+    no padding) use the matrix-product form of the same definitions
+    (``patchify_*``); every other layer uses the direct loops.
+
+    layers: dicts with keys wt, b, k, stride, pad, groups (as for
+    stack_forward).  gw_at: optional per-layer list; where entry l is an
+    index array (rows of (o, c, kh, kw)), grad_weight is evaluated only there
+    (returned as a flat array), otherwise in full.
+
+    Returns per layer a dict with float64 arrays:
+      y   -- the layer's output on the shard's output columns (N, Co, Ho, Wo/S)
+      dx  -- grad of the layer's input on the shard's input columns (N, Ci, H, W/S)
+      gw  -- grad_weight partial over the shard's output columns (full or at gw_at[l])
+      gb  -- grad_bias partial over the shard's output columns (Co,)
+    """
+    nl = len(layers)
+    x = _f64(x)
+    widths, owidths = [], []
+    w = x.shape[3]
+    for L in layers:
+        widths.append(w)
+        w = out_size(w, L["k"], L["stride"], L["pad"])
+        owidths.append(w)
+    own_in = [_shard_range(widths[l], num_shards, shard) for l in range(nl)]
+    own_out = [_shard_range(owidths[l], num_shards, shard) for l in range(nl)]
+
+    # forward: the output columns each layer must produce, from the top down
+    need_out = [None] * nl
+    need_out[nl - 1] = own_out[nl - 1]
+    for l in range(nl - 1, 0, -1):
+        L = layers[l]
+        reads = input_columns_read(need_out[l], L["k"], L["stride"], L["pad"], widths[l])
+        need_out[l - 1] = _hull(own_out[l - 1], reads)
+
+    # backward: the input columns each layer's grad_input must cover, from the bottom up
+    need_dx = [None] * nl
+    need_dx[0] = own_in[0]
+    for l in range(nl - 1):
+        L = layers[l]
+        gcols = output_columns_reaching(need_dx[l], L["k"], L["stride"], L["pad"], owidths[l])
+        need_dx[l + 1] = _hull(own_in[l + 1], _hull(own_out[l], gcols))
+
+    patch = [_is_patchify(L["k"], L["stride"], L["pad"], L["groups"]) for L in layers]
+    res = [dict() for _ in range(nl)]
+    acts = [x]
+    for l, L in enumerate(layers):
+        j0, j1 = need_out[l]
+        if patch[l]:
+            yw = patchify_fwd(acts[l], L["wt"], L["b"], L["k"], cols=(j0, j1))
+        else:
+            yw = conv_fwd(acts[l], L["wt"], L["b"], L["stride"], L["pad"], L["groups"], cols=(j0, j1))
+        full = np.zeros(yw.shape[:3] + (owidths[l],), dtype=np.float64)
+        full[:, :, :, j0:j1] = yw
+        o0, o1 = own_out[l]
+        res[l]["y"] = full[:, :, :, o0:o1].copy()
+        acts.append(full)
+
+    g = _f64(g_final)
+    for l in range(nl - 1, -1, -1):
+        L = layers[l]
+        xin = acts[l]
+        x0, x1 = need_dx[l]
+        if patch[l]:
+            dxw = patchify_bwd_input(g, L["wt"], xin.shape, L["k"], cols=(x0, x1))
+        else:
+            dxw = conv_bwd_input(g, L["wt"], xin.shape, L["stride"], L["pad"], L["groups"], cols=(x0, x1))
+        full = np.zeros(xin.shape, dtype=np.float64)
+        full[:, :, :, x0:x1] = dxw
+        i0, i1 = own_in[l]
+        res[l]["dx"] = full[:, :, :, i0:i1].copy()
+        cols = own_out[l]
+        if patch[l]:
+            gw, res[l]["gb"] = patchify_bwd_weight(xin, g, L["k"], cols=cols)
+            if gw_at is not None and gw_at[l] is not None:
+                ix = _idx(gw_at[l])
+                gw = gw[ix[:, 0], ix[:, 1], ix[:, 2], ix[:, 3]]
+            res[l]["gw"] = gw
+        elif gw_at is not None and gw_at[l] is not None:
+            res[l]["gw"] = conv_bwd_weight_at(xin, g, L["k"], L["stride"], L["pad"], L["groups"],
+                                              gw_at[l], cols=cols)
+            res[l]["gb"] = conv_bwd_bias(g, cols=cols)
+        else:
+            res[l]["gw"], res[l]["gb"] = conv_bwd_weight(xin, g, L["k"], L["stride"], L["pad"],
+                                                         L["groups"], cols=cols)
+        acts[l + 1] = None            # the output of layer l is no longer needed
+        g = full
+    return res
