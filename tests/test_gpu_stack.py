@@ -6,13 +6,19 @@
   output, grad_input and grad_weight / grad_bias partials of every shard are
   compared element by element, and the reduced gradients with the full ones.
 * The full-size stacks on (7,3,512,2048) and (7,3,512,4096) inputs are run on
-  all four shards; the stem's forward is compared with the oracle at sampled
-  outputs, and every layer is checked against identities that hold exactly in
-  exact arithmetic: <Y_s - b, G_s> = <W, gW_s> per shard (the grad_weight
-  partial is the adjoint of the forward over the shard's own columns),
+  all four shards, in the launch configuration the benchmark times.  For the
+  measured shard (1 of 4) every layer's forward output, grad_input, and
+  grad_weight / grad_bias partials are compared element by element with the
+  oracle's share of the unsharded chain (``oracle.stack_shard``, computed from
+  the seeded global tensors only).  As extra checks, every layer of every
+  shard satisfies identities that hold exactly in exact arithmetic:
+  <Y_s - b, G_s> = <W, gW_s> per shard (the grad_weight partial is the
+  adjoint of the forward over the shard's own columns),
   sum_s <X_s, dX_s> = sum_s <Y_s - b, G_s> (grad_input is the adjoint of the
   whole sharded forward), and the reduced gradients equal the shard sum.
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -122,3 +128,32 @@ def test_full_size_convnext_stack_identities(name):
             acc = acc + ls.gw_parts[sh]
         assert torch.equal(torch.cat([ls.gw.reshape(-1), ls.gb]), acc), f"{name} {L.name}: reduction"
         _say(f"  {name} {L.name}: identities hold")
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", ["convnext_xl_w2048", "convnext_xl_w4096"])
+def test_full_size_convnext_stack_measured_shard_vs_oracle(name):
+    wl = workloads.WORKLOADS[name]
+    T = workloads.generate(wl)
+    S, s = wl.num_shards, wl.shard
+    _say(f"  {name}: input {wl.x_shape}, S={S}, measured shard {s}")
+    st = sstack.ShardedStack(wl.layers, S, T.weights, T.biases)
+    st.forward(slices(T.x, S))
+    st.backward(slices(T.g, S))
+    torch.cuda.synchronize()
+    got = [dict(y=host(ls.y[s]), dx=host(ls.dx[s]), part=host(ls.gw_parts[s])) for ls in st.state]
+    del st
+    torch.cuda.empty_cache()
+    t0 = time.perf_counter()
+    ref = oracle.stack_shard(T.x, _oracle_layers(wl, T), T.g, S, s)
+    _say(f"  {name}: oracle share of the chain in {time.perf_counter() - t0:.1f} s")
+    for l, L in enumerate(wl.layers):
+        r, gl = ref[l], got[l]
+        nw = r["gw"].size
+        e_y = assert_close(gl["y"], r["y"], TOL_FWD, f"{name} {L.name} forward")
+        e_dx = assert_close(gl["dx"], r["dx"], TOL_DX, f"{name} {L.name} grad_input")
+        e_gw = assert_close(gl["part"][:nw].reshape(r["gw"].shape), r["gw"], TOL_GW,
+                            f"{name} {L.name} grad_weight partial")
+        e_gb = assert_close(gl["part"][nw:], r["gb"], TOL_GW, f"{name} {L.name} grad_bias partial")
+        _say(f"  {name} {L.name}: normwise errors forward {e_y:.2e} grad_input {e_dx:.2e} "
+             f"grad_weight {e_gw:.2e} grad_bias {e_gb:.2e}")
