@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSCNN_ABI_VERSION 7
+#define SSCNN_ABI_VERSION 8
 
 /* Status codes. */
 #define SSCNN_OK 0
@@ -204,6 +204,33 @@ int sscnn_conv_bwd(const sscnn_conv_t *conv, const float *x, const float *x_halo
                    const float *grad_y, const float *grad_y_halo, const float *weight,
                    float *grad_x, float *grad_w_part, float *grad_b_part,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sscnn_conv_bwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The call itself allocates nothing (no
+ * hipMalloc, no hipFree, no allocating library routine).  Its split-reduction
+ * scratch is a device array inside the library of
+ * SSCNN_NOALLOC_SCRATCH_BYTES (8 MiB): every GPU the library runs on holds
+ * one copy from module load until the process ends.
+ *   arguments   as for sscnn_conv_bwd, minus workspace / workspace_bytes;
+ *               results are the same, bitwise
+ *   device      the scratch of the CURRENT device is used, so `stream` must
+ *               belong to the current device (SSCNN_EINVAL otherwise)
+ * Errors: as sscnn_conv_bwd, plus SSCNN_EWORKSPACE (nothing launched) when
+ * the layer needs more scratch than that,
+ * sscnn_conv_bwd_weight_workspace_bytes(conv) > SSCNN_NOALLOC_SCRATCH_BYTES
+ * (every depthwise layer of the ConvNeXt-XL shards fits; the dense and
+ * patchify layers' split-K reductions do not).
+ * Every call on one GPU shares that GPU's scratch, and the scratch keeps the
+ * last call's contents (no kernel relies on it being zero).  Calls that
+ * overlap in time on one GPU -- on two streams, or from two threads -- race
+ * on the scratch and give wrong results: order them on one stream.
+ */
+#define SSCNN_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int sscnn_conv_bwd_noalloc(const sscnn_conv_t *conv, const float *x, const float *x_halo,
+                           const float *grad_y, const float *grad_y_halo, const float *weight,
+                           float *grad_x, float *grad_w_part, float *grad_b_part, void *stream);
 
 /*
  * Split convolution: interior and edge halves (kwkr.cn retelling, section

@@ -373,6 +373,38 @@ int sscnn_conv_bwd(const sscnn_conv_t* conv, const float* x, const float* x_halo
                       "conv_bwd launch");
 }
 
+int sscnn_conv_bwd_noalloc(const sscnn_conv_t* conv, const float* x, const float* x_halo,
+                           const float* grad_y, const float* grad_y_halo, const float* weight,
+                           float* grad_x, float* grad_w_part, float* grad_b_part, void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    TRY(need(x, "x"));
+    if (g.hl + g.hr) TRY(need(x_halo, "x_halo")); else TRY(optional(x_halo, "x_halo"));
+    TRY(need(grad_y, "grad_y"));
+    if (g.ghl + g.ghr) TRY(need(grad_y_halo, "grad_y_halo")); else TRY(optional(grad_y_halo, "grad_y_halo"));
+    TRY(need(weight, "weight"));
+    TRY(need(grad_x, "grad_x"));
+    TRY(need(grad_w_part, "grad_w_part"));
+    TRY(optional(grad_b_part, "grad_b_part"));
+    if (grad_x == x || grad_x == x_halo || grad_x == grad_y || grad_x == grad_y_halo)
+        return fail(SSCNN_EINVAL, "grad_x aliases an input");
+    const size_t ws_need = kernels_bwd_weight_workspace_bytes(g);
+    if (ws_need > kNoAllocScratchBytes)
+        return fail(SSCNN_EWORKSPACE, "conv_bwd_noalloc: this layer needs %zu bytes of scratch, more than the "
+                    "library's %zu; use sscnn_conv_bwd with a workspace", ws_need, kNoAllocScratchBytes);
+    int dev = -1, sdev = -1;
+    TRY(hip_status(hipGetDevice(&dev), "conv_bwd_noalloc: hipGetDevice"));
+    TRY(hip_status(hipStreamGetDevice((hipStream_t)stream, &sdev), "conv_bwd_noalloc: hipStreamGetDevice"));
+    if (sdev != dev)
+        return fail(SSCNN_EINVAL, "conv_bwd_noalloc: stream belongs to device %d, current device is %d", sdev, dev);
+    void* scratch = nullptr;
+    TRY(hip_status(noalloc_scratch(&scratch), "conv_bwd_noalloc: scratch address"));
+    return hip_status(kernels_conv_bwd(g, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_part,
+                                       grad_b_part, ws_need ? scratch : nullptr, (hipStream_t)stream),
+                      "conv_bwd_noalloc launch");
+}
+
 int sscnn_partial_reduce(const float* const* parts, int32_t nparts, int64_t count, float* out,
                          void* stream)
 {

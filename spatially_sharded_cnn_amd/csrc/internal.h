@@ -88,4 +88,10 @@ hipError_t launch_direct_bwd_input(const Geom& g, const float* gy, const float* 
 hipError_t launch_direct_bwd_weight(const Geom& g, const float* x, const float* xh,
                                     const float* gy, float* gw, float* gb, hipStream_t st);
 
+// No-allocation entry point (noalloc.hip): the device address, on the
+// current device, of the library's file-scope scratch array of
+// kNoAllocScratchBytes (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = SSCNN_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** out);
+
 }  // namespace sscnn

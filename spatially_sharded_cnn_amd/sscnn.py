@@ -34,7 +34,9 @@ EXPORTED = (
     "sscnn_gconv_init", "sscnn_grid_row_halo_gather", "sscnn_grid_col_halo_gather", "sscnn_gconv_fwd",
     "sscnn_gconv_bwd_input", "sscnn_gconv_bwd_weight_workspace_bytes", "sscnn_gconv_bwd_weight_partial",
     "sscnn_gconv_bwd", "sscnn_pointwise_gelu_fwd", "sscnn_pointwise_bwd_input_gelu",
+    "sscnn_conv_bwd_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 8 << 20      # SSCNN_NOALLOC_SCRATCH_BYTES
 
 
 class SscnnError(RuntimeError):
@@ -151,6 +153,7 @@ def lib() -> ctypes.CDLL:
         L.sscnn_conv_bwd_weight_workspace_bytes.restype = ctypes.c_size_t
         L.sscnn_conv_bwd_weight_partial.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.sscnn_conv_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.sscnn_conv_bwd_noalloc.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.sscnn_partial_reduce.argtypes = [ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int64, _vp, _vp]
         L.sscnn_conv_fwd_interior.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
         L.sscnn_conv_fwd_edge.argtypes = [P, _vp, _vp, _vp, _vp]
@@ -200,7 +203,7 @@ def lib() -> ctypes.CDLL:
                   "sscnn_droppath_scales", "sscnn_layer_scale_residual_fwd", "sscnn_layer_scale_residual_bwd",
                   "sscnn_gconv_init", "sscnn_grid_row_halo_gather", "sscnn_grid_col_halo_gather",
                   "sscnn_gconv_fwd", "sscnn_gconv_bwd_input", "sscnn_gconv_bwd_weight_partial", "sscnn_gconv_bwd",
-                  "sscnn_pointwise_gelu_fwd", "sscnn_pointwise_bwd_input_gelu"):
+                  "sscnn_pointwise_gelu_fwd", "sscnn_pointwise_bwd_input_gelu", "sscnn_conv_bwd_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -334,6 +337,21 @@ def conv_bwd(conv: Conv, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_
         _ptr(grad_w_part, conv.w_shape, "grad_w_part"),
         _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True), ws_ptr, ws_bytes, _stream(stream)),
         "conv_bwd")
+
+
+def conv_bwd_noalloc(conv: Conv, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_part, grad_b_part,
+                     stream=None):
+    """sscnn_conv_bwd_noalloc: conv_bwd with its scratch taken from the library's
+    own device array (no workspace argument; layers needing more than
+    NOALLOC_SCRATCH_BYTES are rejected)."""
+    hs, gs = conv.halo_shape(HALO_INPUT), conv.halo_shape(HALO_GRAD_OUTPUT)
+    _check(lib().sscnn_conv_bwd_noalloc(
+        ctypes.byref(conv), _ptr(x, conv.x_shape, "x"), _ptr(x_halo, hs, "x_halo", hs[3] == 0),
+        _ptr(grad_y, conv.y_shape, "grad_y"), _ptr(grad_y_halo, gs, "grad_y_halo", gs[3] == 0),
+        _ptr(weight, conv.w_shape, "weight"), _ptr(grad_x, conv.x_shape, "grad_x"),
+        _ptr(grad_w_part, conv.w_shape, "grad_w_part"),
+        _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True), _stream(stream)),
+        "conv_bwd_noalloc")
 
 
 # --- split convolution (interior: halo read as zeros; edge: adds the halo terms) ---
