@@ -1,11 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the width-sharded convolution hot path on one MI355X.
 
-One step is one pass of the whole path for the measured shard (shard 1 of 4)
-of a layer: halo_gather(X) -> conv_fwd -> halo_gather(G) -> conv_bwd
-(grad_input and the grad_weight / grad_bias partials in one call) ->
-partial_reduce (grad_weight and grad_bias of the four shards, one call over a
-contiguous [gW | gB] buffer).  The separate conv_bwd_input and
+The default workload is the largest configuration, the ConvNeXt-XL
+convolution stack on shard 1 of 4 of a (7,3,512,4096) input (the shard of the
+pages' 4-GPU run).  One step is the shard's forward chain -- per layer
+halo_gather(X) where the layer has a halo, then conv_fwd -- and its backward
+chain in reverse -- per layer halo_gather(G), conv_bwd (grad_input and the
+grad_weight / grad_bias partials in one call) and partial_reduce of the four
+shards' [gW | gB].  `value` is the step's algorithmic GB/s; `roofline` is for
+its dominant operation; `layers` gives every layer's operations and roofline
+fraction.  The same JSON line carries `sub_records` for the other full-size
+configurations, each timed on its own with its own roofline: dense5x5_c256
+(one 5x5 256->256 layer), dw7_c256 (one depthwise 7x7 C=256 layer) and
+convnext_xl_w2048 (the stack on a (7,3,512,2048) input).
+
+For one layer, one step is halo_gather(X) -> conv_fwd -> halo_gather(G) ->
+conv_bwd -> partial_reduce.  The separate conv_bwd_input and
 conv_bwd_weight_partial calls are timed on their own as well ("ops_us"), and so
 is the layer as an interior/edge split ("split": each interior and edge call,
 the split step on one stream, and with the halo gathers on a second stream
@@ -14,7 +24,7 @@ synthetic tensors already resident in HBM; each step uses the next of several
 independent buffer sets so that the 256 MB last-level cache cannot hand one
 step's data to the next.
 
-Prints ONE JSON line.  `value` is the algorithmic GB/s of a step:
+Algorithmic bytes:
   forward   X_ext + W + b + Y
   backward  G_ext + X_ext + W + dX + gW + gB
   reduce    (S + 1) * (|gW| + |gB|)
@@ -28,12 +38,13 @@ for the dense layers, the FP32 vector FMA (157.3 TFLOP/s published; plain
 v_fmac_f32 with vector-register operands reaches it without packed math)
 for the depthwise ones.
 
-    python bench.py [--workload dw7_c256|dense5x5_c256|dense5x5_tiny] [--steps K] [--warmup W]
-    python bench.py --workload dw7_c256_hshard   # the same step on a split along H (row halos)
-    python bench.py --workload convnext_xl_w2048|convnext_xl_w4096   # the stack, per layer
+    python bench.py [--steps K] [--warmup W] [--no-sub]    # convnext_xl_w4096 + sub-records
+    python bench.py --workload dw7_c256|dense5x5_c256|dense5x5_tiny|convnext_xl_w2048
+    python bench.py --workload dw7_c256_hshard   # the depthwise step on a split along H (row halos)
     python bench.py --workload convnext_block_c256   # a whole ConvNeXt block on the C=256 shard, per op
     python bench.py --workload dw7_c256_grid   # the depthwise step on a 2 x 2 grid of blocks (2-D shards)
-    python bench.py --summarize DIR [DIR ...] [--traffic-op OP --traffic-kernels "K1;K2"]
+    python bench.py --workload convnext_xl_w4096 --profile-op ds3.conv_bwd   # one operation, for counters
+    python bench.py --summarize DIR [DIR ...] [--traffic-op OP --traffic-kernels "K1;K2" [--after-calibration]]
                                       # text summary of rocprofv3 output directories
 """
 from __future__ import annotations
@@ -61,17 +72,28 @@ COPY_CAL_BYTES = 256 << 20       # plain device copy used to calibrate FETCH_SIZ
 
 STEPS_DEFAULT, WARMUP_DEFAULT = 50, 5
 STACK_STEPS, STACK_WARMUP = 5, 2   # stack steps run for milliseconds each
+DEFAULT_WORKLOAD = "convnext_xl_w4096"
+# timed beside the default workload, each as its own record in the same line
+SUB_WORKLOADS = ("dense5x5_c256", "dw7_c256", "convnext_xl_w2048")
 
 
 def _parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=STEPS_DEFAULT)
-    ap.add_argument("--warmup", type=int, default=WARMUP_DEFAULT)
-    ap.add_argument("--workload", default="dw7_c256",
-                    help="dw7_c256 (default), dense5x5_c256, dense5x5_tiny, dw7_c256_hshard (the same "
-                         "depthwise map split along H), a stack: convnext_xl_w2048, convnext_xl_w4096, or a "
-                         "ConvNeXt block: convnext_block_c256, or 2-D shards: dw7_c256_grid")
+    ap.add_argument("--steps", type=int, default=None,
+                    help=f"timed steps (default {STEPS_DEFAULT} for one layer, {STACK_STEPS} for a stack)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help=f"untimed steps first (default {WARMUP_DEFAULT} for one layer, {STACK_WARMUP} for a stack)")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help=f"{DEFAULT_WORKLOAD} (default; the largest configuration), convnext_xl_w2048, "
+                         "dense5x5_c256, dw7_c256, dense5x5_tiny, dw7_c256_hshard (the depthwise map split "
+                         "along H), convnext_block_c256 (a ConvNeXt block), dw7_c256_grid (2-D shards)")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="with the default workload: skip the sub-records of " + ", ".join(SUB_WORKLOADS))
+    ap.add_argument("--profile-op", metavar="OP",
+                    help="stack workloads: after the set-up, run only operation OP (e.g. ds3.conv_bwd) "
+                         "--profile-reps times and exit (for counter runs of one operation)")
+    ap.add_argument("--profile-reps", type=int, default=10)
     ap.add_argument("--sets", type=int, default=3, help="independent buffer sets rotated per step")
     ap.add_argument("--op-reps", type=int, default=20, help="back-to-back calls per operation timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -81,6 +103,9 @@ def _parse():
     ap.add_argument("--traffic-op", help="with --summarize over FETCH_SIZE / WRITE_SIZE runs: the operation "
                     "whose kernels' calibrated HBM bytes per launch are recorded")
     ap.add_argument("--traffic-kernels", help="semicolon-separated substrings naming that operation's kernels")
+    ap.add_argument("--after-calibration", action="store_true",
+                    help="with --summarize: the operation's figures from the dispatches after the last device "
+                         "copy only (in a --profile-op run: the operation's repetitions)")
     return ap.parse_args()
 
 
@@ -146,7 +171,7 @@ def recorded_traffic(workload: str):
 def main():
     args = _parse()
     if args.summarize:
-        return summarize(args.summarize, args.traffic_op, args.traffic_kernels)
+        return summarize(args.summarize, args.traffic_op, args.traffic_kernels, args.after_calibration)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU's share of the sharded path; --gpus {args.gpus} "
@@ -155,19 +180,56 @@ def main():
         return 2
 
     import torch
-    from spatially_sharded_cnn_amd import sscnn, workloads
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    dev = "cuda"
-    wl = workloads.WORKLOADS[args.workload]
+    out = run_workload(args, args.workload)
+    if out is None:                 # --profile-op: the run printed its own line
+        return 0
+    if args.workload == DEFAULT_WORKLOAD and not args.no_sub and not args.profile_op:
+        # The other full-size configurations, each timed on its own with its own
+        # defaults for steps and warmup, and with its own roofline.
+        out["sub_records"] = {}
+        for name in SUB_WORKLOADS:
+            sub = argparse.Namespace(**vars(args))
+            sub.steps = sub.warmup = None
+            sub.no_cpu_baseline = args.no_cpu_baseline or name == "convnext_xl_w2048"
+            rec = run_workload(sub, name)
+            for k in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data", "source_hash",
+                      "gpu_clocks"):
+                rec.pop(k, None)
+            out["sub_records"][name] = rec
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def run_workload(args, name):
+    """Benchmark one workload; returns its record (None in --profile-op mode)."""
+    from spatially_sharded_cnn_amd import workloads
+    wl = workloads.WORKLOADS[name]
+    a = argparse.Namespace(**vars(args))
+    a.workload = name
+    stack = wl.kind == "conv" and len(wl.layers) > 1
+    if a.steps is None:
+        a.steps = STACK_STEPS if stack else (20 if wl.kind == "block" else STEPS_DEFAULT)
+    if a.warmup is None:
+        a.warmup = STACK_WARMUP if stack else WARMUP_DEFAULT
     if wl.kind == "block":
-        return block_bench(args, wl)
+        return block_bench(a, wl)
     if wl.kind == "grid":
-        return grid_bench(args, wl)
-    if len(wl.layers) > 1:
-        return stack_bench(args, wl)
+        return grid_bench(a, wl)
+    if stack:
+        return stack_bench(a, wl)
+    return layer_bench(a, wl)
+
+
+def layer_bench(args, wl):
+    """One layer's step on the measured shard (see the module docstring)."""
+    import torch
+    from spatially_sharded_cnn_amd import sscnn, workloads
+
+    dev = "cuda"
     L = wl.layers[0]
     S, s = wl.num_shards, wl.shard
     T = workloads.generate(wl)
@@ -384,8 +446,7 @@ def main():
     }
     if not args.no_cpu_baseline and not hsplit:
         out["cpu_baseline"] = cpu_baseline(wl, T, L, S, s)
-    print(json.dumps(out), flush=True)
-    return 0
+    return out
 
 
 class _WOps:
@@ -609,8 +670,7 @@ def grid_bench(args, wl):
         "ops_us": op_us, "step_spread": spread, "wall_s_timed": round(wall, 4), "gpu_clocks": gpu_clocks(),
         "source_hash": kernel_source_hash(),
     }
-    print(json.dumps(out), flush=True)
-    return 0
+    return out
 
 
 def block_bench(args, wl):
@@ -625,7 +685,7 @@ def block_bench(args, wl):
 
     dev = "cuda"
     S, s = wl.num_shards, wl.shard
-    steps = args.steps if args.steps != STEPS_DEFAULT else 20
+    steps = args.steps
     warmup = args.warmup
     T = workloads.generate(wl)
     dw, pw1, pw2 = wl.layers
@@ -771,8 +831,7 @@ def block_bench(args, wl):
         "roofline": roof, "ops": rows, "step_spread": spread, "wall_s_timed": round(wall, 4),
         "gpu_clocks": gpu_clocks(), "source_hash": kernel_source_hash(),
     }
-    print(json.dumps(out_d), flush=True)
-    return 0
+    return out_d
 
 
 def stack_bench(args, wl):
@@ -788,8 +847,7 @@ def stack_bench(args, wl):
 
     dev = "cuda"
     S, s = wl.num_shards, wl.shard
-    steps = args.steps if args.steps != STEPS_DEFAULT else STACK_STEPS
-    warmup = args.warmup if args.warmup != WARMUP_DEFAULT else STACK_WARMUP
+    steps, warmup = args.steps, args.warmup
     T = workloads.generate(wl)
 
     def slices(a):
@@ -840,6 +898,30 @@ def stack_bench(args, wl):
     def step():
         for _, _, f in ops:
             f()
+
+    # A plain device copy of known size (untimed): the reference that calibrates
+    # the FETCH_SIZE / WRITE_SIZE counters in a counter run of this command.
+    cal_src = torch.empty(COPY_CAL_BYTES // 4, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+
+    if args.profile_op:
+        # Counter runs of one operation: its launches are the dispatches after
+        # the calibration copy just made (bench.py --summarize --after-calibration).
+        sel = [(l, name, f) for l, name, f in ops if f"{wl.layers[l].name}.conv_{name}" == args.profile_op
+               or f"{wl.layers[l].name}.{name}" == args.profile_op]
+        if not sel:
+            raise SystemExit(f"--profile-op {args.profile_op}: no such operation (layer.conv_fwd, "
+                             "layer.conv_bwd, layer.halo_x, layer.halo_g, layer.reduce)")
+        f = sel[0][2]
+        for _ in range(args.profile_reps):
+            f()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_op": args.profile_op, "reps": args.profile_reps, "workload": wl.name}),
+              flush=True)
+        return None
 
     for _ in range(warmup):
         step()
@@ -908,8 +990,9 @@ def stack_bench(args, wl):
     else:
         roof = {"bound": "hbm", "achieved": round(b_ / (t * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
     roof["op"] = f"{wl.layers[l].name}.conv_{name}"
+    tr = recorded_traffic(wl.name)
+    roof["traffic"] = (tr["fetch_bytes"] + tr["write_bytes"]) if tr and tr.get("op") == roof["op"] else None
     roof["avg_us"] = round(t, 2)
     roof["algorithmic_bytes"] = b_
     roof["algorithmic_flops"] = f_
@@ -933,8 +1016,7 @@ def stack_bench(args, wl):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_stack(wl, convs, step_flops)
-    print(json.dumps(out), flush=True)
-    return 0
+    return out
 
 
 def cpu_baseline_stack(wl, convs, step_flops):
@@ -1005,21 +1087,43 @@ def cpu_baseline(wl, T, L, S, s):
             "cpu": platform.processor() or platform.machine()}
 
 
-def summarize(dirs, traffic_op=None, traffic_kernels=None):
-    """Text summary of rocprofv3 output directories (kernel stats and/or
-    counter collection CSVs), for the files committed under profiles/.
+def summarize(dirs, traffic_op=None, traffic_kernels=None, after_cal=False):
+    """Text summary of rocprofv3 output directories (kernel stats, kernel
+    traces and/or counter collection CSVs), for the files committed under
+    profiles/.
 
-    With traffic_op / traffic_kernels and FETCH_SIZE / WRITE_SIZE runs of a
-    bench.py command, also the HBM traffic per launch of that operation: each
-    counter's KB per dispatch, scaled by what the same counter reads for the
-    plain device copy of COPY_CAL_BYTES each way that the command runs
-    (`__amd_rocclr_copyBuffer`), summed over the operation's kernels, as a
-    `traffic_json:` line that bench.py reads back while the sources match."""
-    stats, cc = [], []
+    Kernel traces are also grouped by kernel and grid size, which tells apart
+    the launches of one kernel template for layers of different shapes.
+
+    With traffic_op / traffic_kernels (semicolon-separated substrings of the
+    operation's kernel names): the operation's per-launch figures.  With
+    after_cal they come only from the dispatches after the last device copy
+    -- in a `bench.py --profile-op OP` run, the calibration copy made just
+    before the operation's repetitions.  From a kernel trace: the operation's kernels, grids and mean
+    durations.  From FETCH_SIZE / WRITE_SIZE counter runs: the HBM traffic per
+    launch -- each counter's KB per dispatch, scaled by what the same counter
+    reads for the plain device copy of COPY_CAL_BYTES each way that the
+    command runs (`__amd_rocclr_copyBuffer`), summed over the operation's
+    kernels -- as a `traffic_json:` line that bench.py reads back while the
+    sources match."""
+    stats, cc, kt = [], [], []
     for d in dirs:
         d = pathlib.Path(d)
         stats += sorted(glob.glob(str(d / "**" / "*kernel_stats.csv"), recursive=True))
         cc += sorted(glob.glob(str(d / "**" / "*counter_collection.csv"), recursive=True))
+        kt += sorted(glob.glob(str(d / "**" / "*kernel_trace.csv"), recursive=True))
+    subs = [t for t in (traffic_kernels or "").split(";") if t]
+
+    def picks(name):
+        return any(t in name for t in subs)
+
+    def after_marker(rows):
+        """Rows (sorted by dispatch) after the last device copy, if after_cal."""
+        if not after_cal:
+            return rows
+        marks = [i for i, r in enumerate(rows) if "copyBuffer" in r["Kernel_Name"]]
+        return rows[marks[-1] + 1:] if marks else rows
+
     for f in stats:
         print(f"## kernel statistics ({pathlib.Path(f).name})\n")
         print("| kernel | calls | average us | min us | max us | share |")
@@ -1028,24 +1132,66 @@ def summarize(dirs, traffic_op=None, traffic_kernels=None):
             print(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
         print()
+    for f in kt:
+        rows = list(csv.DictReader(open(f)))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        groups = {}
+        for r in rows:
+            grid = tuple(int(r[f"Grid_Size_{a}"]) for a in "XYZ")
+            wg = tuple(int(r[f"Workgroup_Size_{a}"]) for a in "XYZ")
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups.setdefault((r["Kernel_Name"], grid, wg), []).append(dur)
+        print(f"## kernel trace by kernel and launch shape ({pathlib.Path(f).name})\n")
+        print("| kernel | workgroups | threads | calls | average us | min us | max us |")
+        print("|---|---:|---:|---:|---:|---:|---:|")
+        for (kname, grid, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            nwg = (grid[0] // max(1, wg[0])) * (grid[1] // max(1, wg[1])) * (grid[2] // max(1, wg[2]))
+            print(f"| `{kname[:100]}` | {nwg} | {wg[0] * wg[1] * wg[2]} | {len(v)} | {sum(v) / len(v):.2f} | "
+                  f"{min(v):.2f} | {max(v):.2f} |")
+        print()
+        if traffic_op and subs:
+            byk = {}
+            for r in after_marker(rows):
+                if picks(r["Kernel_Name"]):
+                    byk.setdefault(r["Kernel_Name"], []).append(r)
+            print(f"Operation `{traffic_op}`" + (", dispatches after the calibration copy" if after_cal else "")
+                  + ":\n")
+            print("| kernel | workgroups | dispatches | average us |")
+            print("|---|---:|---:|---:|")
+            tot = 0.0
+            for kname, rs in sorted(byk.items()):
+                durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
+                nwg = sorted({(int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))) *
+                              int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) for r in rs})
+                avg = sum(durs) / len(durs)
+                tot += avg
+                print(f"| `{kname[:100]}` | {'/'.join(map(str, nwg))} | {len(durs)} | {avg:.2f} |")
+            print(f"\nSum of the kernels' mean durations: {tot:.2f} us per launch of `{traffic_op}`.\n")
+            print("op_trace_json: " + json.dumps({"op": traffic_op, "us_per_launch": round(tot, 2),
+                                                 "source_hash": kernel_source_hash()}))
+            print()
     if not cc:
         return 0
-    agg = {}
+    agg, op_agg = {}, {}
     for f in cc:
-        for r in csv.DictReader(open(f)):
+        rows = list(csv.DictReader(open(f)))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        for r in rows:
             k = (r["Kernel_Name"], r["Counter_Name"])
             agg.setdefault(k, []).append(float(r["Counter_Value"]))
-    mean = {k: sum(v) / len(v) for k, v in agg.items()}
+        for r in after_marker(rows):
+            k = (r["Kernel_Name"], r["Counter_Name"])
+            op_agg.setdefault(k, []).append(float(r["Counter_Value"]))
     print("## counters (mean per dispatch)\n")
     print("| kernel | counter | mean | dispatches |")
     print("|---|---|---:|---:|")
     for (kname, cname), v in sorted(agg.items()):
         print(f"| `{kname[:110]}` | {cname} | {sum(v) / len(v):.1f} | {len(v)} |")
     print()
-    if not (traffic_op and traffic_kernels):
+    if not (traffic_op and subs):
         return 0
     cal = COPY_CAL_BYTES / 1024
-    copy = [k for (k, c) in mean if "copyBuffer" in k]
+    copy = [k for (k, c) in agg if "copyBuffer" in k]
     if not copy:
         print("no calibration copy kernel found")
         return 1
@@ -1053,19 +1199,24 @@ def summarize(dirs, traffic_op=None, traffic_kernels=None):
     big = {c: max(agg[(copy[0], c)]) for c in ("FETCH_SIZE", "WRITE_SIZE") if (copy[0], c) in agg}
     fs = cal / big["FETCH_SIZE"] if "FETCH_SIZE" in big else None
     wsc = cal / big["WRITE_SIZE"] if "WRITE_SIZE" in big else None
-    subs = [t for t in traffic_kernels.split(";") if t]
-    names = sorted({k for (k, c) in mean if any(t in k for t in subs)})
-    fetch = sum(mean.get((k, "FETCH_SIZE"), 0.0) for k in names) * 1024 * (fs or 0)
-    write = sum(mean.get((k, "WRITE_SIZE"), 0.0) for k in names) * 1024 * (wsc or 0)
+    names = sorted({k for (k, c) in op_agg if picks(k)})
+
+    def per_launch(k, c):
+        v = op_agg.get((k, c), [])
+        return sum(v) / len(v) if v else 0.0
+
+    fetch = sum(per_launch(k, "FETCH_SIZE") for k in names) * 1024 * (fs or 0)
+    write = sum(per_launch(k, "WRITE_SIZE") for k in names) * 1024 * (wsc or 0)
     print(f"Calibration: the {COPY_CAL_BYTES >> 20} MiB device copy reads FETCH_SIZE "
           f"{big.get('FETCH_SIZE', float('nan')):.1f} KB and WRITE_SIZE "
           f"{big.get('WRITE_SIZE', float('nan')):.1f} KB, so counter KB are scaled by "
           f"{fs or float('nan'):.4f} (reads) and {wsc or float('nan'):.4f} (writes).\n")
     print(f"Operation `{traffic_op}` = " + " + ".join(f"`{k[:80]}`" for k in names) +
+          (" (dispatches after the calibration copy)" if after_cal else "") +
           f": {fetch / 1e6:.1f} MB read + {write / 1e6:.1f} MB written per launch.\n")
     rec = {"op": traffic_op, "kernels": [k[:120] for k in names], "fetch_bytes": round(fetch),
            "write_bytes": round(write), "fetch_scale": round(fs or 0, 4), "write_scale": round(wsc or 0, 4),
-           "source_hash": kernel_source_hash()}
+           "after_calibration": bool(after_cal), "source_hash": kernel_source_hash()}
     print("traffic_json: " + json.dumps(rec))
     return 0
 
