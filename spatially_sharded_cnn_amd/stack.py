@@ -15,6 +15,7 @@ every operation runs in the library's kernels.
 """
 from __future__ import annotations
 
+import contextlib
 import dataclasses
 from typing import List, Optional
 
@@ -39,7 +40,12 @@ class LayerState:
 
 
 class ShardedStack:
-    """Runs a chain of convolutions (workloads.Layer list) on S W-shards."""
+    """Runs a chain of convolutions (workloads.Layer list) on S W-shards.
+
+    With a stream, every kernel runs on it and every temporary (halos, the
+    grad_weight workspace, outputs) is allocated while it is torch's current
+    stream, so the caching allocator never hands a buffer still in use on it
+    to work on another stream."""
 
     def __init__(self, layers, num_shards: int, weights, biases, device="cuda", stream=None):
         self.layers = list(layers)
@@ -58,12 +64,19 @@ class ShardedStack:
         return [sscnn.conv_init(n, ci, L.co, h, w // self.S, L.k, L.stride, L.pad, L.groups, s, self.S)
                 for s in range(self.S)]
 
+    def _on_stream(self):
+        return torch.cuda.stream(self.stream) if self.stream is not None else contextlib.nullcontext()
+
     def _nbrs(self, lst, s):
         return (lst[s - 1] if s > 0 else None), (lst[s + 1] if s < self.S - 1 else None)
 
     def forward(self, x_slices):
         """x_slices: per shard (N, 3, H, W/S) device tensors.  Returns the last
         layer's per-shard outputs."""
+        with self._on_stream():
+            return self._forward(x_slices)
+
+    def _forward(self, x_slices):
         cur = list(x_slices)
         for l, L in enumerate(self.layers):
             convs = self._convs(L)
@@ -86,6 +99,10 @@ class ShardedStack:
         """g_slices: per shard grad of the last output.  Fills each layer's
         dx, partial and reduced weight / bias gradients.  The first layer's
         dx is computed too when need_input_grad."""
+        with self._on_stream():
+            return self._backward(g_slices, need_input_grad)
+
+    def _backward(self, g_slices, need_input_grad):
         cur = list(g_slices)
         for l in range(len(self.layers) - 1, -1, -1):
             st = self.state[l]

@@ -73,6 +73,27 @@ def test_reduced_convnext_stack_all_layers_vs_oracle():
         assert_close(host(ls.gb), gb_full, TOL_GW, f"{L.name} reduced grad_bias")
 
 
+def test_stack_on_a_side_stream_equals_default_stream():
+    """The same small stack run on a stream of its own (kernels and every
+    temporary on that stream) gives bitwise the results of the default stream."""
+    layers = workloads.convnext_stack(1, 512, h=128, dims=(16, 32, 64, 128))
+    wl = workloads.stack("convnext_small", layers, num_shards=4, seed=2002)
+    T = workloads.generate(wl)
+    S = wl.num_shards
+    runs = []
+    for stream in (None, torch.cuda.Stream()):
+        st = sstack.ShardedStack(wl.layers, S, T.weights, T.biases, stream=stream)
+        xs, gs = slices(T.x, S), slices(T.g, S)
+        torch.cuda.synchronize()
+        st.forward(xs)
+        st.backward(gs)
+        torch.cuda.synchronize()
+        runs.append([(torch.cat(ls.y, 3), torch.cat(ls.dx, 3), ls.gw.clone(), ls.gb.clone()) for ls in st.state])
+    for l, (a, b) in enumerate(zip(*runs)):
+        for t0, t1 in zip(a, b):
+            assert torch.equal(t0, t1), f"layer {l} differs between the default and a side stream"
+
+
 def _dot(a, b):
     return float(torch.sum(a.double() * b.double()))
 
