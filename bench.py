@@ -43,6 +43,7 @@ for the depthwise ones.
     python bench.py --workload dw7_c256_hshard   # the depthwise step on a split along H (row halos)
     python bench.py --workload convnext_block_c256   # a whole ConvNeXt block on the C=256 shard, per op
     python bench.py --workload dw7_c256_grid   # the depthwise step on a 2 x 2 grid of blocks (2-D shards)
+    python bench.py --workload dense5x5_c256_hshard|dense5x5_c256_grid   # the dense 5x5 step split along H / 2-D
     python bench.py --workload convnext_xl_w4096 --profile-op ds3.conv_bwd   # one operation, for counters
     python bench.py --summarize DIR [DIR ...] [--traffic-op OP --traffic-kernels "K1;K2" [--after-calibration]]
                                       # text summary of rocprofv3 output directories
@@ -154,6 +155,36 @@ def gpu_clocks():
     return out or None
 
 
+def hbm_ceiling(nbytes=1 << 30, reps=10):
+    """The copy rate of this device: the library's plain streaming kernel
+    (sscnn_stream_copy) and torch's copy_, each over nbytes one way (a read
+    and a write of every byte, so 2 * nbytes of HBM traffic per copy), far
+    larger than the 256 MB last-level cache; GB/s from events around reps
+    back-to-back copies."""
+    import torch
+    from spatially_sharded_cnn_amd import sscnn
+    src = torch.empty(nbytes // 4, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    res = {}
+    for name, f in (("stream_copy_gbs", lambda: sscnn.stream_copy(src, dst)),
+                    ("torch_copy_gbs", lambda: dst.copy_(src))):
+        f()
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(reps):
+            f()
+        a1.record()
+        torch.cuda.synchronize()
+        res[name] = round(2 * nbytes * reps / (a0.elapsed_time(a1) * 1e-3) / 1e9, 1)
+    ok = bool(torch.equal(src, dst))
+    del src, dst
+    torch.cuda.empty_cache()
+    res.update(bytes_each_way=nbytes, copy_correct=ok, peak_gbs=HBM_PEAK_GBS,
+               stream_copy_frac_of_peak=round(res["stream_copy_gbs"] / HBM_PEAK_GBS, 4))
+    return res
+
+
 def recorded_traffic(workload: str):
     """Counter-measured HBM bytes per launch of the dominant operation, from
     profiles/traffic_<workload>.md, if recorded for the current sources."""
@@ -187,6 +218,7 @@ def main():
     out = run_workload(args, args.workload)
     if out is None:                 # --profile-op: the run printed its own line
         return 0
+    out["hbm_ceiling"] = hbm_ceiling()
     if args.workload == DEFAULT_WORKLOAD and not args.no_sub and not args.profile_op:
         # The other full-size configurations, each timed on its own with its own
         # defaults for steps and warmup, and with its own roofline.
@@ -655,7 +687,13 @@ def grid_bench(args, wl):
     step_flops = sum(v[1] for v in work.values())
     t = op_us["conv_bwd"]
     bb, ff = work["conv_bwd"]
-    roof = {"bound": "hbm", "achieved": round(bb / (t * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    dense = L.groups == 1 and min(L.ci, L.co) >= 16
+    peak = MFMA_F32_PEAK_TFLOPS if dense else VALU_F32_PEAK_TFLOPS
+    if ff / (peak * 1e12) > bb / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma" if dense else "alu", "achieved": round(ff / (t * 1e-6) / 1e12, 2), "peak": peak,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(bb / (t * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof.update(frac=round(roof["achieved"] / roof["peak"], 4), traffic=None, op="conv_bwd", avg_us=t,
                 algorithmic_bytes=bb, algorithmic_flops=ff)
     step_s = ms_per_step * 1e-3
@@ -666,7 +704,8 @@ def grid_bench(args, wl):
         "config": {"workload": wl.name, "description": wl.description, "block": [bi, bj], "grid": [NH, NW],
                    "shard_input": list(c.x_shape)},
         "tflops": round(step_flops / step_s / 1e12, 2), "step_bytes": step_bytes, "step_flops": step_flops,
-        "hbm_roofline_frac": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4), "roofline": roof,
+        "hbm_roofline_frac": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "compute_roofline_frac": round(step_flops / (peak * 1e12) / step_s, 4), "roofline": roof,
         "ops_us": op_us, "step_spread": spread, "wall_s_timed": round(wall, 4), "gpu_clocks": gpu_clocks(),
         "source_hash": kernel_source_hash(),
     }

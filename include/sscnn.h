@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSCNN_ABI_VERSION 8
+#define SSCNN_ABI_VERSION 9
 
 /* Status codes. */
 #define SSCNN_OK 0
@@ -301,11 +301,13 @@ int sscnn_conv_bwd_interior(const sscnn_conv_t *conv, const float *x, const floa
  * activation's rows are split into num_shards equal slices of full width;
  * weight and bias stay replicated; a shard exchanges ROWS with the shards
  * above and below it: the row halo.  Rows are contiguous in memory, so the
- * exchange moves whole rows.  Each call convolves the local slice as its own
- * image (the interior) and then adds the terms that read a row halo; results
- * equal the unsharded layer's rows [s*h_out_local, (s+1)*h_out_local) up to
- * float32 rounding, and the grad_weight / grad_bias partials sum, over the
- * shards, to the full gradients.  Conventions are those of the calls above.
+ * exchange moves whole rows.  Depthwise layers, and dense stride-1 3x3 /
+ * 5x5 k/2-padded layers on the matrix cores, read the row halo inside their
+ * tiles; any other layer convolves the local slice as its own image (the
+ * interior) and then adds the terms that read a row halo.  Results equal the
+ * unsharded layer's rows [s*h_out_local, (s+1)*h_out_local) up to float32
+ * rounding, and the grad_weight / grad_bias partials sum, over the shards, to
+ * the full gradients.  Conventions are those of the calls above.
  */
 typedef struct sscnn_hconv {
     /* set by the caller */
@@ -389,9 +391,13 @@ int sscnn_hconv_bwd(const sscnn_hconv_t *conv, const float *x, const float *x_ha
  *      from the blocks left and right of it and the row halos THEY gathered
  *      in phase 1 -- which is how the corners arrive from the diagonal blocks.
  * Layers: depthwise (groups = c_in = c_out) stride-1 k in {3,5,7} pad k/2 with
- * w_local % 16 == 0 and h_local >= 16 (halo = pad on every side), and layers
- * with k = stride, pad 0, groups 1 (no halo: the block is convolved as is);
- * anything else is SSCNN_EUNSUPPORTED.  Results equal the unsharded layer's
+ * w_local % 16 == 0 and h_local >= 16; dense (groups 1) stride-1 k in {3,5}
+ * pad k/2 -- the pages' 5x5 pad-2 example -- with c_in and c_out multiples
+ * of 4 (at least 16), w_local % 4 == 0 and a block at least pad wide and
+ * tall (both on the matrix cores: their tiles read the row halo and the
+ * column halo over the extended rows directly); halo = pad on every side for
+ * both.  And layers with k = stride, pad 0, groups 1 (no halo: the block is
+ * convolved as is).  Anything else is SSCNN_EUNSUPPORTED.  Results equal the unsharded layer's
  * output block, the partials sum to the full gradients.
  */
 typedef struct sscnn_gconv {
@@ -452,6 +458,17 @@ int sscnn_gconv_bwd(const sscnn_gconv_t *conv, const float *x, const float *x_ro
  */
 int sscnn_partial_reduce(const float *const *parts, int32_t nparts, int64_t count,
                          float *out, void *stream);
+
+/*
+ * A plain streaming copy, dst[i] = src[i] for 0 <= i < count: one read and
+ * one write of every element with nothing else in the kernel.  Its rate is
+ * the practical HBM ceiling of this device for the bandwidth-bound steps
+ * (the depthwise layers, the halo gathers, the reductions), measured beside
+ * the published peak.
+ *   src, dst  device, count floats each, 16-byte aligned, not overlapping
+ *             (SSCNN_EINVAL otherwise); count >= 0 (0 launches nothing)
+ */
+int sscnn_stream_copy(const float *src, float *dst, int64_t count, void *stream);
 
 /*
  * The ConvNeXt block's other steps, on one shard's activations.  They look at

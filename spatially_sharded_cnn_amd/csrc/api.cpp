@@ -12,6 +12,7 @@
 #include "edge.h"
 #include "internal.h"
 #include "kernels.h"
+#include "mfma_conv.h"
 #include "rowedge.h"
 
 namespace sscnn {
@@ -162,6 +163,7 @@ int derive_g(const sscnn_gconv_t& c, sscnn_gconv_t* out)
     const bool dw = c.groups == c.c_in && c.c_in == c.c_out && c.stride == 1 && (c.k == 3 || c.k == 5 || c.k == 7) &&
                     c.pad == c.k / 2;
     const bool patch = c.k == c.stride && c.pad == 0 && c.groups == 1;
+    const bool dense = c.groups == 1 && c.stride == 1 && (c.k == 3 || c.k == 5) && c.pad == c.k / 2;
     if (dw) {
         if (c.w_local % 16 || c.h_local < 16)
             return fail(SSCNN_EUNSUPPORTED, "2-D depthwise blocks need w_local %% 16 == 0 and h_local >= 16 "
@@ -178,9 +180,19 @@ int derive_g(const sscnn_gconv_t& c, sscnn_gconv_t* out)
         d.h_out_local = c.h_local / c.k;
         d.w_out_local = c.w_local / c.k;
         d.halo = 0;
+    } else if (dense) {
+        if (c.c_in < 16 || c.c_out < 16 || c.c_in % 4 || c.c_out % 4 || c.w_local % 4)
+            return fail(SSCNN_EUNSUPPORTED, "2-D dense blocks need c_in, c_out multiples of 4 and at least 16, and "
+                        "w_local %% 4 == 0 (got c_in=%d c_out=%d w_local=%d)", c.c_in, c.c_out, c.w_local);
+        if (c.h_local < c.pad || c.w_local < c.pad)
+            return fail(SSCNN_EUNSUPPORTED, "block %d x %d is smaller than the halo %d", c.h_local, c.w_local, c.pad);
+        d.h_out_local = c.h_local;
+        d.w_out_local = c.w_local;
+        d.halo = c.pad;
     } else {
-        return fail(SSCNN_EUNSUPPORTED, "2-D shards take depthwise stride-1 k/2-padded layers and k = stride "
-                    "layers only (k=%d stride=%d pad=%d groups=%d)", c.k, c.stride, c.pad, c.groups);
+        return fail(SSCNN_EUNSUPPORTED, "2-D shards take depthwise stride-1 k/2-padded layers, dense stride-1 "
+                    "3x3 / 5x5 k/2-padded layers and k = stride layers only (k=%d stride=%d pad=%d groups=%d)",
+                    c.k, c.stride, c.pad, c.groups);
     }
     *out = d;
     return SSCNN_OK;
@@ -403,6 +415,18 @@ int sscnn_conv_bwd_noalloc(const sscnn_conv_t* conv, const float* x, const float
     return hip_status(kernels_conv_bwd(g, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_part,
                                        grad_b_part, ws_need ? scratch : nullptr, (hipStream_t)stream),
                       "conv_bwd_noalloc launch");
+}
+
+int sscnn_stream_copy(const float* src, float* dst, int64_t count, void* stream)
+{
+    if (count < 0) return fail(SSCNN_EINVAL, "count=%lld is negative", (long long)count);
+    if (count == 0) return SSCNN_OK;
+    TRY(need(src, "src"));
+    TRY(need(dst, "dst"));
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    const uintptr_t bytes = (uintptr_t)count * sizeof(float);
+    if (a < b + bytes && b < a + bytes) return fail(SSCNN_EINVAL, "src and dst overlap");
+    return hip_status(launch_stream_copy(src, dst, count, (hipStream_t)stream), "stream_copy launch");
 }
 
 int sscnn_partial_reduce(const float* const* parts, int32_t nparts, int64_t count, float* out,
@@ -702,6 +726,28 @@ int sscnn_conv_bwd_interior(const sscnn_conv_t* conv, const float* x, const floa
 
 // --- height sharding -----------------------------------------------------
 
+namespace {
+
+// The row halo buffer (planes, up + down, width) of a height or 2-D shard as
+// the rows above and below each plane of the slice, for the matrix-core
+// kernels; crh = rows of the column halo above row 0 (2-D shards).
+RowHalo row_halo(const float* rh, int up, int down, int width, int crh)
+{
+    RowHalo r;
+    r.up = rh;
+    r.down = rh ? rh + (int64_t)up * width : nullptr;
+    r.rplane = (int64_t)(up + down) * width;
+    r.rh = up;
+    r.crh = crh;
+    return r;
+}
+
+// Dense stride-1 layers whose row halo is as tall above as below take the
+// matrix-core kernels reading the row halo directly.
+bool mfma_rows(const Geom& g, int up, int down) { return mfma_conv_supported(g) && up == down; }
+
+}  // namespace
+
 int sscnn_hconv_init(sscnn_hconv_t* conv)
 {
     if (!conv) return fail(SSCNN_EINVAL, "conv is NULL");
@@ -753,6 +799,9 @@ int sscnn_hconv_fwd(const sscnn_hconv_t* conv, const float* x, const float* x_ha
     const hipStream_t st = (hipStream_t)stream;
     if (dw_supported(g))   // depthwise: the tiles read the row halo themselves
         return hip_status(launch_dw_fwd_rows(g, x, x_halo, hu, hd, weight, bias, y, st), "hconv_fwd launch");
+    if (mfma_rows(g, hu, hd))
+        return hip_status(launch_mfma_fwd_rows(g, x, nullptr, row_halo(x_halo, hu, hd, g.wl, 0), weight, bias, y, st),
+                          "hconv_fwd launch");
     hipError_t e = kernels_conv_fwd(g, x, nullptr, weight, bias, y, st);
     if (e == hipSuccess) e = launch_row_edge_fwd(g, hu, hd, x_halo, weight, y, st);
     return hip_status(e, "hconv_fwd launch");
@@ -771,6 +820,10 @@ int sscnn_hconv_bwd_input(const sscnn_hconv_t* conv, const float* grad_y, const 
     const hipStream_t st = (hipStream_t)stream;
     if (dw_supported(g))
         return hip_status(launch_dw_bwd_input_rows(g, grad_y, grad_y_halo, ghu, ghd, weight, grad_x, st),
+                          "hconv_bwd_input launch");
+    if (mfma_rows(g, ghu, ghd))
+        return hip_status(launch_mfma_bwd_input_rows(g, grad_y, nullptr, row_halo(grad_y_halo, ghu, ghd, g.wol, 0),
+                                                     weight, grad_x, st),
                           "hconv_bwd_input launch");
     hipError_t e = kernels_conv_bwd_input(g, grad_y, nullptr, weight, grad_x, st);
     if (e == hipSuccess) e = launch_row_edge_bwd_input(g, ghu, ghd, grad_y_halo, weight, grad_x, st);
@@ -804,6 +857,10 @@ int sscnn_hconv_bwd_weight_partial(const sscnn_hconv_t* conv, const float* x, co
         return hip_status(launch_dw_bwd_weight_rows(g, x, x_halo, hu, hd, grad_y, grad_w_part, grad_b_part,
                                                     workspace, st),
                           "hconv_bwd_weight_partial launch");
+    if (mfma_rows(g, hu, hd))
+        return hip_status(launch_mfma_bwd_weight_rows(g, x, nullptr, row_halo(x_halo, hu, hd, g.wl, 0), grad_y,
+                                                      grad_w_part, grad_b_part, ws_need ? workspace : nullptr, st),
+                          "hconv_bwd_weight_partial launch");
     hipError_t e = kernels_conv_bwd_weight(g, x, nullptr, grad_y, grad_w_part, grad_b_part,
                                            ws_need ? workspace : nullptr, st);
     if (e == hipSuccess) e = launch_row_edge_bwd_weight(g, hu, hd, x_halo, grad_y, grad_w_part, workspace, st);
@@ -834,6 +891,14 @@ int sscnn_hconv_bwd(const sscnn_hconv_t* conv, const float* x, const float* x_ha
         return hip_status(launch_dw_bwd_rows(g, x, x_halo, hu, hd, grad_y, grad_y_halo, ghu, ghd, weight, grad_x,
                                              grad_w_part, grad_b_part, workspace, st),
                           "hconv_bwd launch");
+    if (mfma_rows(g, hu, hd) && ghu == ghd) {
+        hipError_t e = launch_mfma_bwd_input_rows(g, grad_y, nullptr, row_halo(grad_y_halo, ghu, ghd, g.wol, 0),
+                                                  weight, grad_x, st);
+        if (e == hipSuccess)
+            e = launch_mfma_bwd_weight_rows(g, x, nullptr, row_halo(x_halo, hu, hd, g.wl, 0), grad_y, grad_w_part,
+                                            grad_b_part, ws_need ? workspace : nullptr, st);
+        return hip_status(e, "hconv_bwd launch");
+    }
     hipError_t e = kernels_conv_bwd(g, x, nullptr, grad_y, nullptr, weight, grad_x, grad_w_part, grad_b_part,
                                     ws_need ? workspace : nullptr, st);
     if (e == hipSuccess) e = launch_row_edge_bwd_input(g, ghu, ghd, grad_y_halo, weight, grad_x, st);
@@ -928,6 +993,10 @@ int sscnn_gconv_fwd(const sscnn_gconv_t* conv, const float* x, const float* x_ro
     const hipStream_t st = (hipStream_t)stream;
     const int hh = conv->halo;
     if (!hh) return hip_status(kernels_conv_fwd(g, x, nullptr, weight, bias, y, st), "gconv_fwd launch");
+    if (mfma_conv_supported(g))
+        return hip_status(launch_mfma_fwd_rows(g, x, x_col_halo, row_halo(x_row_halo, hh, hh, g.wl, hh), weight, bias,
+                                               y, st),
+                          "gconv_fwd launch");
     return hip_status(launch_dw_fwd_grid(g, x, x_row_halo, x_col_halo, hh, hh, weight, bias, y, st), "gconv_fwd launch");
 }
 
@@ -943,6 +1012,10 @@ int sscnn_gconv_bwd_input(const sscnn_gconv_t* conv, const float* grad_y, const 
     const hipStream_t st = (hipStream_t)stream;
     const int hh = conv->halo;
     if (!hh) return hip_status(kernels_conv_bwd_input(g, grad_y, nullptr, weight, grad_x, st), "gconv_bwd_input launch");
+    if (mfma_conv_supported(g))
+        return hip_status(launch_mfma_bwd_input_rows(g, grad_y, gy_col_halo, row_halo(gy_row_halo, hh, hh, g.wol, hh),
+                                                     weight, grad_x, st),
+                          "gconv_bwd_input launch");
     return hip_status(launch_dw_bwd_input_grid(g, grad_y, gy_row_halo, gy_col_halo, hh, hh, weight, grad_x, st),
                       "gconv_bwd_input launch");
 }
@@ -972,6 +1045,10 @@ int sscnn_gconv_bwd_weight_partial(const sscnn_gconv_t* conv, const float* x, co
     void* ws = ws_need ? workspace : nullptr;
     if (!hh)
         return hip_status(kernels_conv_bwd_weight(g, x, nullptr, grad_y, grad_w_part, grad_b_part, ws, st),
+                          "gconv_bwd_weight_partial launch");
+    if (mfma_conv_supported(g))
+        return hip_status(launch_mfma_bwd_weight_rows(g, x, x_col_halo, row_halo(x_row_halo, hh, hh, g.wl, hh), grad_y,
+                                                      grad_w_part, grad_b_part, ws, st),
                           "gconv_bwd_weight_partial launch");
     return hip_status(launch_dw_bwd_weight_grid(g, x, x_row_halo, x_col_halo, hh, hh, grad_y, grad_w_part,
                                                 grad_b_part, ws, st),
@@ -1003,6 +1080,14 @@ int sscnn_gconv_bwd(const sscnn_gconv_t* conv, const float* x, const float* x_ro
         return hip_status(kernels_conv_bwd(g, x, nullptr, grad_y, nullptr, weight, grad_x, grad_w_part, grad_b_part,
                                            ws, st),
                           "gconv_bwd launch");
+    if (mfma_conv_supported(g)) {
+        hipError_t e = launch_mfma_bwd_input_rows(g, grad_y, gy_col_halo, row_halo(gy_row_halo, hh, hh, g.wol, hh),
+                                                  weight, grad_x, st);
+        if (e == hipSuccess)
+            e = launch_mfma_bwd_weight_rows(g, x, x_col_halo, row_halo(x_row_halo, hh, hh, g.wl, hh), grad_y,
+                                            grad_w_part, grad_b_part, ws, st);
+        return hip_status(e, "gconv_bwd launch");
+    }
     return hip_status(launch_dw_bwd_grid(g, x, x_row_halo, x_col_halo, hh, hh, grad_y, gy_row_halo, gy_col_halo, hh,
                                          hh, weight, grad_x, grad_w_part, grad_b_part, ws, st),
                       "gconv_bwd launch");

@@ -88,6 +88,9 @@ hipError_t launch_direct_bwd_input(const Geom& g, const float* gy, const float* 
 hipError_t launch_direct_bwd_weight(const Geom& g, const float* x, const float* xh,
                                     const float* gy, float* gw, float* gb, hipStream_t st);
 
+// Streaming copy of count floats (stream.hip); src and dst 16-byte aligned.
+hipError_t launch_stream_copy(const float* src, float* dst, int64_t count, hipStream_t st);
+
 // No-allocation entry point (noalloc.hip): the device address, on the
 // current device, of the library's file-scope scratch array of
 // kNoAllocScratchBytes (looked up once per device).

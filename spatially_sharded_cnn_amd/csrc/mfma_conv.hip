@@ -42,7 +42,11 @@ constexpr int kCK = 4;      // reduction channels per chunk
 
 struct MfArgs {
     const float* x;      // GEMM input activation (N, C, H, W): X (forward) or G (grad_input)
-    const float* halo;   // (N, C, H, hl + hr); null with hl = hr = 0 when absent
+    const float* halo;   // (N, C, H + 2 crh, hl + hr); null with hl = hr = 0 when absent
+    const float* up;     // rows above / below the slice (height and 2-D sharding), null when absent:
+    const float* down;   //   rh rows per plane each, rplane floats between planes
+    int64_t rplane;
+    int rh, crh;         // row-halo height; rows of the column halo above row 0
     const float* w;      // weight (Co, Ci, k, k) as given
     const float* b;      // bias (O) or null
     float* y;            // (N, O, H, W)
@@ -84,15 +88,28 @@ struct Regs {
     float s[Shape<K>::NXS];
 };
 
-// Extended-row value: column xcol of the shard (may lie in the halo), zero
-// outside [-hl, W + hr) and outside the image rows.
-__device__ __forceinline__ float ext_at(const MfArgs& a, const float* xp, const float* hp, int r, int xcol)
+// Row r of plane pl over the slice's own columns: the slice for 0 <= r < H,
+// the row halos for the rh rows beyond it; null (zeros) elsewhere.
+__device__ __forceinline__ const float* row_at(const MfArgs& a, int64_t pl, int r)
 {
-    if (r < 0 || r >= a.H) return 0.f;
+    if (r >= 0 && r < a.H) return a.x + (pl * a.H + r) * a.W;
+    if (r < 0) return (a.up && r >= -a.rh) ? a.up + pl * a.rplane + (int64_t)(r + a.rh) * a.W : nullptr;
+    return (a.down && r < a.H + a.rh) ? a.down + pl * a.rplane + (int64_t)(r - a.H) * a.W : nullptr;
+}
+
+// Extended-row value: column xcol of the shard (may lie in the column halo),
+// zero outside [-hl, W + hr) and outside the rows there are data for.
+__device__ __forceinline__ float ext_at(const MfArgs& a, int64_t pl, int r, int xcol)
+{
+    if (xcol >= 0 && xcol < a.W) {
+        const float* p = row_at(a, pl, r);
+        return p ? p[xcol] : 0.f;
+    }
+    if (r < -a.crh || r >= a.H + a.crh) return 0.f;
     const int hw = a.hl + a.hr;
-    if (xcol < 0) return xcol >= -a.hl ? hp[(int64_t)r * hw + a.hl + xcol] : 0.f;
-    if (xcol < a.W) return xp[(int64_t)r * a.W + xcol];
-    return xcol < a.W + a.hr ? hp[(int64_t)r * hw + a.hl + (xcol - a.W)] : 0.f;
+    const float* hp = a.halo + (pl * (a.H + 2 * a.crh) + (r + a.crh)) * hw;
+    if (xcol < 0) return xcol >= -a.hl ? hp[a.hl + xcol] : 0.f;
+    return xcol < a.W + a.hr ? hp[a.hl + (xcol - a.W)] : 0.f;
 }
 
 template <int K, bool TRANS>
@@ -149,16 +166,15 @@ __device__ __forceinline__ void fetch(Regs<K>& R, const MfArgs& a, int n, int o0
             const int rem = g - cl * ((kTH + K - 1) * Q);
             const int rr = rem / Q, q = rem - rr * Q;
             const int r = i0 - P + rr, col = j0 + 4 * q;
-            const float* xp = a.x + (plane0 + cl) * a.H * a.W;
-            const float* hp = a.halo + (plane0 + cl) * a.H * (a.hl + a.hr);
-            if (c0 + cl < a.C && r >= 0 && r < a.H) {
+            if (c0 + cl < a.C) {
                 if (col + 3 < a.W) {
-                    R.x[k] = *reinterpret_cast<const float4*>(xp + (int64_t)r * a.W + col);
+                    const float* rp = row_at(a, plane0 + cl, r);
+                    if (rp) R.x[k] = *reinterpret_cast<const float4*>(rp + col);
                 } else {
-                    R.x[k].x = ext_at(a, xp, hp, r, col);
-                    R.x[k].y = ext_at(a, xp, hp, r, col + 1);
-                    R.x[k].z = ext_at(a, xp, hp, r, col + 2);
-                    R.x[k].w = ext_at(a, xp, hp, r, col + 3);
+                    R.x[k].x = ext_at(a, plane0 + cl, r, col);
+                    R.x[k].y = ext_at(a, plane0 + cl, r, col + 1);
+                    R.x[k].z = ext_at(a, plane0 + cl, r, col + 2);
+                    R.x[k].w = ext_at(a, plane0 + cl, r, col + 3);
                 }
             }
         }
@@ -172,9 +188,7 @@ __device__ __forceinline__ void fetch(Regs<K>& R, const MfArgs& a, int n, int o0
             const int rem = g - cl * ((kTH + K - 1) * 2 * P);
             const int rr = rem / (2 * P), e = rem - rr * (2 * P);
             const int xcol = e < P ? j0 - P + e : j0 + kTW + (e - P);
-            const float* xp = a.x + (plane0 + cl) * a.H * a.W;
-            const float* hp = a.halo + (plane0 + cl) * a.H * (a.hl + a.hr);
-            if (c0 + cl < a.C) R.s[k] = ext_at(a, xp, hp, i0 - P + rr, xcol);
+            if (c0 + cl < a.C) R.s[k] = ext_at(a, plane0 + cl, i0 - P + rr, xcol);
         }
     }
 }
@@ -361,19 +375,33 @@ bool mfma_conv_supported(const Geom& g)
 hipError_t launch_mfma_fwd(const Geom& g, const float* x, const float* xh, const float* w,
                            const float* b, float* y, hipStream_t st)
 {
+    return launch_mfma_fwd_rows(g, x, xh, RowHalo{}, w, b, y, st);
+}
+
+hipError_t launch_mfma_bwd_input(const Geom& g, const float* gy, const float* gyh, const float* w,
+                                 float* gx, hipStream_t st)
+{
+    return launch_mfma_bwd_input_rows(g, gy, gyh, RowHalo{}, w, gx, st);
+}
+
+hipError_t launch_mfma_fwd_rows(const Geom& g, const float* x, const float* xh, const RowHalo& rows,
+                                const float* w, const float* b, float* y, hipStream_t st)
+{
     MfArgs a{};
     a.x = x; a.halo = xh; a.w = w; a.b = b; a.y = y;
+    a.up = rows.up; a.down = rows.down; a.rplane = rows.rplane; a.rh = rows.rh; a.crh = xh ? rows.crh : 0;
     a.N = g.n; a.C = g.ci; a.O = g.co; a.H = g.h; a.W = g.wl;
     a.hl = xh ? g.hl : 0; a.hr = xh ? g.hr : 0;     // no halo: ext_at() reads zeros beyond the slice
     a.wci = g.ci;
     return launch_k<false>(a, g.k, st);
 }
 
-hipError_t launch_mfma_bwd_input(const Geom& g, const float* gy, const float* gyh, const float* w,
-                                 float* gx, hipStream_t st)
+hipError_t launch_mfma_bwd_input_rows(const Geom& g, const float* gy, const float* gyh, const RowHalo& rows,
+                                      const float* w, float* gx, hipStream_t st)
 {
     MfArgs a{};
     a.x = gy; a.halo = gyh; a.w = w; a.b = nullptr; a.y = gx;
+    a.up = rows.up; a.down = rows.down; a.rplane = rows.rplane; a.rh = rows.rh; a.crh = gyh ? rows.crh : 0;
     a.N = g.n; a.C = g.co; a.O = g.ci; a.H = g.ho; a.W = g.wol;
     a.hl = gyh ? g.ghl : 0; a.hr = gyh ? g.ghr : 0;
     a.wci = g.ci;

@@ -39,7 +39,11 @@ constexpr int kSW = 128;    // pixels of a row per stage
 
 struct WgArgs {
     const float* x;      // (N, Ci, H, W) input slice
-    const float* halo;   // (N, Ci, H, hl + hr); null with hl = hr = 0 when absent
+    const float* halo;   // (N, Ci, H + 2 crh, hl + hr); null with hl = hr = 0 when absent
+    const float* up;     // input rows above / below the slice (height and 2-D sharding), null when
+    const float* down;   //   absent: rh rows per plane each, rplane floats between planes
+    int64_t rplane;
+    int rh, crh;         // row-halo height; rows of the column halo above row 0
     const float* g;      // (N, Co, H, W) grad_output slice
     float* ws;           // [splits][k*k][Co][Ci] partial grad_weight, then [splits][Co] grad_bias
     int N, Ci, Co, H, W, hl, hr;
@@ -66,15 +70,28 @@ struct WRegs {
     float s[WShape<K>::NS];
 };
 
-// Extended input value at shard column xcol of row r (halo outside the
-// slice, zero beyond the halo or outside the image).
-__device__ __forceinline__ float xext(const WgArgs& a, const float* xp, const float* hp, int r, int xcol)
+// Input row r of plane pl over the slice's own columns: the slice for
+// 0 <= r < H, the row halos for the rh rows beyond it; null (zeros) elsewhere.
+__device__ __forceinline__ const float* xrow(const WgArgs& a, int64_t pl, int r)
 {
-    if (r < 0 || r >= a.H) return 0.f;
+    if (r >= 0 && r < a.H) return a.x + (pl * a.H + r) * a.W;
+    if (r < 0) return (a.up && r >= -a.rh) ? a.up + pl * a.rplane + (int64_t)(r + a.rh) * a.W : nullptr;
+    return (a.down && r < a.H + a.rh) ? a.down + pl * a.rplane + (int64_t)(r - a.H) * a.W : nullptr;
+}
+
+// Extended input value at shard column xcol of row r (column halo outside
+// the slice, zero beyond it or outside the rows there are data for).
+__device__ __forceinline__ float xext(const WgArgs& a, int64_t pl, int r, int xcol)
+{
+    if (xcol >= 0 && xcol < a.W) {
+        const float* p = xrow(a, pl, r);
+        return p ? p[xcol] : 0.f;
+    }
+    if (r < -a.crh || r >= a.H + a.crh) return 0.f;
     const int hw = a.hl + a.hr;
-    if (xcol < 0) return xcol >= -a.hl ? hp[(int64_t)r * hw + a.hl + xcol] : 0.f;
-    if (xcol < a.W) return xp[(int64_t)r * a.W + xcol];
-    return xcol < a.W + a.hr ? hp[(int64_t)r * hw + a.hl + (xcol - a.W)] : 0.f;
+    const float* hp = a.halo + (pl * (a.H + 2 * a.crh) + (r + a.crh)) * hw;
+    if (xcol < 0) return xcol >= -a.hl ? hp[a.hl + xcol] : 0.f;
+    return xcol < a.W + a.hr ? hp[a.hl + (xcol - a.W)] : 0.f;
 }
 
 // Stage s of a split: flattened (image row, column segment).
@@ -104,22 +121,20 @@ __device__ __forceinline__ void fetch(WRegs<K>& R, const WgArgs& a, int stage, i
     {
         const int q = tid % 32, cl = tid / 32;
         const int col = j0 + 4 * q;
-        const float* xp = a.x + (((int64_t)n * a.Ci + c0 + cl) * a.H + r) * a.W + col;
 #pragma unroll
         for (int k = 0; k < S::NX; ++k) {
             const int c = c0 + cl + 8 * k;
+            const int64_t pl = (int64_t)n * a.Ci + c;
             R.x[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (c < a.Ci && r >= 0 && r < a.H) {
+            if (c < a.Ci) {
                 if (col + 3 < a.W) {
-                    R.x[k] = *reinterpret_cast<const float4*>(xp + (int64_t)8 * k * a.H * a.W);
+                    const float* rp = xrow(a, pl, r);
+                    if (rp) R.x[k] = *reinterpret_cast<const float4*>(rp + col);
                 } else {
-                    const int64_t pl = (int64_t)n * a.Ci + c;
-                    const float* xb = a.x + pl * a.H * a.W;
-                    const float* hb = a.halo + pl * a.H * (a.hl + a.hr);
-                    R.x[k].x = xext(a, xb, hb, r, col);
-                    R.x[k].y = xext(a, xb, hb, r, col + 1);
-                    R.x[k].z = xext(a, xb, hb, r, col + 2);
-                    R.x[k].w = xext(a, xb, hb, r, col + 3);
+                    R.x[k].x = xext(a, pl, r, col);
+                    R.x[k].y = xext(a, pl, r, col + 1);
+                    R.x[k].z = xext(a, pl, r, col + 2);
+                    R.x[k].w = xext(a, pl, r, col + 3);
                 }
             }
         }
@@ -133,10 +148,7 @@ __device__ __forceinline__ void fetch(WRegs<K>& R, const WgArgs& a, int stage, i
             const int cl = idx / (2 * P), e = idx - cl * (2 * P);
             const int c = c0 + cl;
             const int xcol = e < P ? j0 - P + e : j0 + kSW + (e - P);
-            if (c < a.Ci) {
-                const int64_t pl = (int64_t)n * a.Ci + c;
-                R.s[k] = xext(a, a.x + pl * a.H * a.W, a.halo + pl * a.H * (a.hl + a.hr), r, xcol);
-            }
+            if (c < a.Ci) R.s[k] = xext(a, (int64_t)n * a.Ci + c, r, xcol);
         }
     }
 }
@@ -308,12 +320,13 @@ Plan plan(const Geom& g)
 }
 
 template <int K>
-hipError_t launch(const Geom& g, const float* x, const float* xh, const float* gy, float* gw,
-                  float* gb, float* ws, hipStream_t st)
+hipError_t launch(const Geom& g, const float* x, const float* xh, const RowHalo& rows, const float* gy,
+                  float* gw, float* gb, float* ws, hipStream_t st)
 {
     const Plan p = plan(g);
     WgArgs a{};
     a.x = x; a.halo = xh; a.g = gy; a.ws = ws;
+    a.up = rows.up; a.down = rows.down; a.rplane = rows.rplane; a.rh = rows.rh; a.crh = xh ? rows.crh : 0;
     a.N = g.n; a.Ci = g.ci; a.Co = g.co; a.H = g.h; a.W = g.wl;
     a.hl = xh ? g.hl : 0; a.hr = xh ? g.hr : 0;     // no halo: xext() reads zeros beyond the slice
     a.tiles_o = p.tiles_o; a.tiles_c = p.tiles_c; a.segs = p.segs; a.rows = p.rows;
@@ -339,8 +352,14 @@ size_t mfma_wgrad_workspace_bytes(const Geom& g)
 hipError_t launch_mfma_bwd_weight(const Geom& g, const float* x, const float* xh, const float* gy,
                                   float* gw, float* gb, void* ws, hipStream_t st)
 {
+    return launch_mfma_bwd_weight_rows(g, x, xh, RowHalo{}, gy, gw, gb, ws, st);
+}
+
+hipError_t launch_mfma_bwd_weight_rows(const Geom& g, const float* x, const float* xh, const RowHalo& rows,
+                                       const float* gy, float* gw, float* gb, void* ws, hipStream_t st)
+{
     float* w = static_cast<float*>(ws);
-    return g.k == 3 ? launch<3>(g, x, xh, gy, gw, gb, w, st) : launch<5>(g, x, xh, gy, gw, gb, w, st);
+    return g.k == 3 ? launch<3>(g, x, xh, rows, gy, gw, gb, w, st) : launch<5>(g, x, xh, rows, gy, gw, gb, w, st);
 }
 
 }  // namespace sscnn

@@ -34,7 +34,7 @@ EXPORTED = (
     "sscnn_gconv_init", "sscnn_grid_row_halo_gather", "sscnn_grid_col_halo_gather", "sscnn_gconv_fwd",
     "sscnn_gconv_bwd_input", "sscnn_gconv_bwd_weight_workspace_bytes", "sscnn_gconv_bwd_weight_partial",
     "sscnn_gconv_bwd", "sscnn_pointwise_gelu_fwd", "sscnn_pointwise_bwd_input_gelu",
-    "sscnn_conv_bwd_noalloc",
+    "sscnn_conv_bwd_noalloc", "sscnn_stream_copy",
 )
 NOALLOC_SCRATCH_BYTES = 8 << 20      # SSCNN_NOALLOC_SCRATCH_BYTES
 
@@ -154,6 +154,7 @@ def lib() -> ctypes.CDLL:
         L.sscnn_conv_bwd_weight_partial.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.sscnn_conv_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.sscnn_conv_bwd_noalloc.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.sscnn_stream_copy.argtypes = [_vp, _vp, ctypes.c_int64, _vp]
         L.sscnn_partial_reduce.argtypes = [ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int64, _vp, _vp]
         L.sscnn_conv_fwd_interior.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
         L.sscnn_conv_fwd_edge.argtypes = [P, _vp, _vp, _vp, _vp]
@@ -203,7 +204,8 @@ def lib() -> ctypes.CDLL:
                   "sscnn_droppath_scales", "sscnn_layer_scale_residual_fwd", "sscnn_layer_scale_residual_bwd",
                   "sscnn_gconv_init", "sscnn_grid_row_halo_gather", "sscnn_grid_col_halo_gather",
                   "sscnn_gconv_fwd", "sscnn_gconv_bwd_input", "sscnn_gconv_bwd_weight_partial", "sscnn_gconv_bwd",
-                  "sscnn_pointwise_gelu_fwd", "sscnn_pointwise_bwd_input_gelu", "sscnn_conv_bwd_noalloc"):
+                  "sscnn_pointwise_gelu_fwd", "sscnn_pointwise_bwd_input_gelu", "sscnn_conv_bwd_noalloc",
+                  "sscnn_stream_copy"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -337,6 +339,14 @@ def conv_bwd(conv: Conv, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_
         _ptr(grad_w_part, conv.w_shape, "grad_w_part"),
         _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True), ws_ptr, ws_bytes, _stream(stream)),
         "conv_bwd")
+
+
+def stream_copy(src, dst, stream=None):
+    """sscnn_stream_copy: dst[:] = src[:] by the library's plain streaming kernel
+    (the HBM ceiling bench.py reports)."""
+    n = src.numel()
+    _check(lib().sscnn_stream_copy(_ptr(src, (n,), "src"), _ptr(dst, (n,), "dst"), n, _stream(stream)),
+           "stream_copy")
 
 
 def conv_bwd_noalloc(conv: Conv, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_part, grad_b_part,

@@ -123,6 +123,18 @@ WORKLOADS = {
         (_layer("conv", 256, 256, 5, 1, 2, 1, (7, 256, 128, 512), (7, 256, 128, 512)),),
         num_shards=4, shard=1, seed=1003, dist="normal",
         description="dense 5x5 s1 p2 conv 256->256: shard (7,256,128,128) of a (7,256,128,512) map, 2-column halos"),
+    "dense5x5_c256_hshard": Workload(
+        "dense5x5_c256_hshard",
+        (_layer("conv", 256, 256, 5, 1, 2, 1, (7, 256, 128, 512), (7, 256, 128, 512)),),
+        num_shards=4, shard=1, seed=1003, dist="normal",
+        description="dense 5x5 s1 p2 conv 256->256 split along H: shard (7,256,32,512) of a (7,256,128,512) "
+                    "map, 2-row halos", axis=2),
+    "dense5x5_c256_grid": Workload(
+        "dense5x5_c256_grid",
+        (_layer("conv", 256, 256, 5, 1, 2, 1, (7, 256, 128, 512), (7, 256, 128, 512)),),
+        num_shards=4, shard=3, seed=1003, dist="normal",
+        description="dense 5x5 s1 p2 conv 256->256 on a 2x2 grid of blocks: block (1,1), (7,256,64,256), of a "
+                    "(7,256,128,512) map, 2-row and 2-column halos with corners", kind="grid"),
     "convnext_xl_w2048": Workload(
         "convnext_xl_w2048", convnext_stack(7, 2048),
         num_shards=4, shard=1, seed=1004, dist="normal",

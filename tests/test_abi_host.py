@@ -400,9 +400,11 @@ def test_gconv_init_and_gathers_validate():
     c = sscnn.gconv_init(2, 8, 8, 16, 32, 7, 1, 3, 8, 1, 3, 0, 2)        # depthwise 7x7, middle row, left column
     assert (c.halo, c.h_out_local, c.w_out_local) == (3, 16, 32)
     p = sscnn.gconv_init(1, 16, 32, 8, 16, 2, 2, 0, 1, 0, 2, 1, 2)       # 2x2/2 downsample: no halo
+    d = sscnn.gconv_init(1, 16, 24, 12, 20, 5, 1, 2, 1, 1, 2, 1, 2)      # dense 5x5 pad 2: the pages' example
+    assert (d.halo, d.h_out_local, d.w_out_local) == (2, 12, 20)
     assert (p.halo, p.h_out_local, p.w_out_local) == (0, 4, 8)
     with pytest.raises(sscnn.SscnnError) as e:
-        sscnn.gconv_init(1, 8, 8, 16, 32, 3, 1, 1, 1, 0, 2, 0, 2)        # dense 3x3: not on a 2-D grid
+        sscnn.gconv_init(1, 8, 8, 16, 32, 3, 1, 1, 1, 0, 2, 0, 2)        # dense 3x3 with 8 channels (< 16)
     assert e.value.status == sscnn.EUNSUPPORTED
     with pytest.raises(sscnn.SscnnError) as e:
         sscnn.gconv_init(1, 8, 8, 16, 24, 7, 1, 3, 8, 0, 2, 0, 2)        # depthwise block width 24
@@ -425,3 +427,14 @@ def test_gconv_init_and_gathers_validate():
     assert L.sscnn_gconv_fwd(r, F, F, F, F, None, F, None) == sscnn.EINVAL      # edited descriptor
     # no halo: the gathers have nothing to do
     assert L.sscnn_grid_row_halo_gather(ctypes.byref(p), 0, F, None, None, None) == sscnn.OK
+
+
+def test_stream_copy_validation():
+    L = sscnn.lib()
+    assert L.sscnn_stream_copy(FAKE, FAKE + 4096, 0, None) == sscnn.OK          # nothing to do
+    assert L.sscnn_stream_copy(FAKE, FAKE + 4096, -1, None) == sscnn.EINVAL
+    assert L.sscnn_stream_copy(None, FAKE + 4096, 16, None) == sscnn.EINVAL
+    assert L.sscnn_stream_copy(FAKE, None, 16, None) == sscnn.EINVAL
+    assert L.sscnn_stream_copy(FAKE + 4, FAKE + 4096, 16, None) == sscnn.EINVAL   # misaligned
+    assert L.sscnn_stream_copy(FAKE, FAKE + 32, 16, None) == sscnn.EINVAL         # overlapping
+    assert "overlap" in sscnn.last_error()

@@ -4,7 +4,9 @@ Every block of a num_h x num_w grid runs the two exchange phases (rows from
 the blocks above and below, then columns over the extended rows from the
 blocks beside it and their row halos, so the corners come from the diagonal
 blocks), then the forward, grad_input and grad_weight partial, against the
-oracle on the global tensors:
+oracle on the global tensors, for depthwise, patchify and dense 3x3 / 5x5
+layers (the dense ones on the matrix cores, whose tiles read the row halo
+and the column halo over the extended rows directly):
 * both halos bit-exact against the zero-padded neighbourhood of the block;
 * forward and grad_input within 1e-5 of the unsharded layer's block,
   grad_weight / grad_bias partials within 1e-4 of the sums over the block's
@@ -33,6 +35,11 @@ CASES = [
     ("dw7_2x2_64rows", 1, 4, 4, 2 * 64, 2 * 64, 7, 1, 3, 4, 2, 2),     # 64-row blocks: 4 rows per thread
     ("patch2_2x2_no_halo", 1, 16, 32, 2 * 8, 2 * 32, 2, 2, 0, 1, 2, 2),
     ("pw1x1_2x2_no_halo", 2, 16, 48, 2 * 8, 2 * 32, 1, 1, 0, 1, 2, 2),
+    # dense layers on the matrix cores, reading both halos (the 5x5 pad-2 example of the pages)
+    ("mfma5x5_2x2", 1, 24, 32, 2 * 12, 2 * 64, 5, 1, 2, 1, 2, 2),
+    ("mfma3x3_3x2_ragged", 2, 20, 36, 3 * 10, 2 * 36, 3, 1, 1, 1, 3, 2),      # ragged row, column, channel tiles
+    ("mfma5x5_2x3_tiles", 1, 64, 72, 2 * 20, 3 * 132, 5, 1, 2, 1, 2, 3),      # several tiles per block
+    ("mfma5x5_2x2_c128", 2, 128, 128, 2 * 32, 2 * 128, 5, 1, 2, 1, 2, 2),
 ]
 
 

@@ -37,6 +37,8 @@ CASES = [
     ("dw5_w40_direct", 1, 6, 6, 3 * 10, 40, 5, 1, 2, 6, 3),
     ("mfma5x5", 1, 24, 32, 2 * 12, 64, 5, 1, 2, 1, 2),
     ("mfma3x3", 1, 16, 20, 3 * 8, 32, 3, 1, 1, 1, 3),
+    ("mfma5x5_tiles_ragged", 2, 36, 68, 2 * 22, 100, 5, 1, 2, 1, 2),     # ragged row, column, channel tiles
+    ("mfma5x5_c128", 2, 128, 128, 4 * 16, 128, 5, 1, 2, 1, 4),
     ("direct5x5_example", 1, 3, 8, 4 * 8, 64, 5, 1, 2, 1, 4),
     ("grouped3x3", 1, 8, 12, 3 * 10, 12, 3, 1, 1, 4, 3),
     ("strided3x3p1", 1, 6, 10, 2 * 16, 22, 3, 2, 1, 1, 2),
