@@ -876,10 +876,12 @@ def block_bench(args, wl):
 def stack_bench(args, wl):
     """A ConvNeXt-style stack (on (7,3,512,2048) or (7,3,512,4096) inputs): one step is the
     measured shard's forward chain (halo_gather + conv_fwd per layer, each
-    layer's output feeding the next) and its backward chain in reverse
-    (halo_gather(G) + conv_bwd + partial_reduce per layer, each grad_input
-    feeding the layer below).  The neighbours' activations and gradients and
-    the other shards' partials come from an untimed run of all shards."""
+    layer's output feeding the next), its backward chain in reverse
+    (halo_gather(G) + conv_bwd per layer, each grad_input feeding the layer
+    below, each layer's grad_weight / grad_bias partials written into the
+    shard's gradient bucket), and one partial_reduce of the four shards'
+    buckets.  The neighbours' activations and gradients and the other shards'
+    buckets come from an untimed run of all shards."""
     import torch
     from spatially_sharded_cnn_amd import sscnn, workloads
     from spatially_sharded_cnn_amd.stack import ShardedStack
@@ -906,9 +908,11 @@ def stack_bench(args, wl):
     xhs = [torch.empty(c.halo_shape(sscnn.HALO_INPUT), device=dev) if c.halo_l + c.halo_r else None for c in convs]
     ghs = [torch.empty(c.halo_shape(sscnn.HALO_GRAD_OUTPUT), device=dev) if c.ghalo_l + c.ghalo_r else None
            for c in convs]
-    nws = [int(np.prod(c.w_shape)) for c in convs]
-    bufs = [torch.empty(nws[l] + convs[l].c_out, device=dev) for l in range(nl)]
-    reds = [torch.empty_like(b) for b in bufs]
+    offs, total = st.offsets
+    bucket = torch.zeros(total, device=dev)       # this shard's partials of every layer
+    reduced = torch.zeros(total, device=dev)
+    gws = [bucket[offs[l][0]:offs[l][0] + offs[l][2]].view(c.w_shape) for l, c in enumerate(convs)]
+    gbs = [bucket[offs[l][1]:offs[l][1] + offs[l][3]] for l in range(nl)]
     wss = [sscnn.new_workspace(c) for c in convs]
     ins = [xs[s]] + ys[:-1]                       # each layer's input: the previous layer's output
     gouts = dxs[1:] + [gs[s]]                     # each layer's grad_output: the next layer's grad_input
@@ -926,10 +930,9 @@ def stack_bench(args, wl):
                 ops.append((l, "halo_g", lambda l=l, c=c: sscnn.halo_gather(
                     c, sscnn.HALO_GRAD_OUTPUT, *nbr(st.state[l].g), ghs[l])))
             ops.append((l, "bwd", lambda l=l, c=c: sscnn.conv_bwd(
-                c, ins[l], xhs[l], gouts[l], ghs[l], st.w[l], dxs[l], bufs[l][:nws[l]].view(c.w_shape),
-                bufs[l][nws[l]:], wss[l])))
-            ops.append((l, "reduce", lambda l=l: sscnn.partial_reduce(
-                [bufs[l] if i == s else st.state[l].gw_parts[i] for i in range(S)], reds[l])))
+                c, ins[l], xhs[l], gouts[l], ghs[l], st.w[l], dxs[l], gws[l], gbs[l], wss[l])))
+        ops.append((-1, "reduce", lambda: sscnn.partial_reduce(
+            [bucket if i == s else st.buckets[i] for i in range(S)], reduced)))
         return ops
 
     ops = op_list()
@@ -949,11 +952,11 @@ def stack_bench(args, wl):
     if args.profile_op:
         # Counter runs of one operation: its launches are the dispatches after
         # the calibration copy just made (bench.py --summarize --after-calibration).
-        sel = [(l, name, f) for l, name, f in ops if f"{wl.layers[l].name}.conv_{name}" == args.profile_op
-               or f"{wl.layers[l].name}.{name}" == args.profile_op]
+        sel = [(l, name, f) for l, name, f in ops if (l >= 0 and (f"{wl.layers[l].name}.conv_{name}" == args.profile_op
+               or f"{wl.layers[l].name}.{name}" == args.profile_op)) or (l < 0 and name == args.profile_op)]
         if not sel:
             raise SystemExit(f"--profile-op {args.profile_op}: no such operation (layer.conv_fwd, "
-                             "layer.conv_bwd, layer.halo_x, layer.halo_g, layer.reduce)")
+                             "layer.conv_bwd, layer.halo_x, layer.halo_g, reduce)")
         f = sel[0][2]
         for _ in range(args.profile_reps):
             f()
@@ -1001,14 +1004,14 @@ def stack_bench(args, wl):
         row = {"layer": L.name, "shard_input": list(c.x_shape), "k": c.k, "stride": c.stride,
                "groups": c.groups, "bound_unit": "mfma" if dense else "alu"}
         lay_t = lay_roof = 0.0
-        for name in ("halo_x", "fwd", "halo_g", "bwd", "reduce"):
+        for name in ("halo_x", "fwd", "halo_g", "bwd"):
             if (l, name) not in op_us:
                 continue
             b_, f_ = work[name]
             t = op_us[(l, name)]
             row[name + "_us"] = round(t, 2)
             lay_t += t
-            if name in ("fwd", "bwd", "reduce"):
+            if name in ("fwd", "bwd"):
                 step_bytes += b_
                 step_flops += f_
             lay_roof += max(b_ / (HBM_PEAK_GBS * 1e9), f_ / (peak * 1e12)) * 1e6
@@ -1017,9 +1020,18 @@ def stack_bench(args, wl):
         row["us"] = round(lay_t, 2)
         row["roofline_us"] = round(lay_roof, 2)
         row["roofline_frac"] = round(lay_roof / lay_t, 4) if lay_t else None
-        row["gbs"] = round((work["fwd"][0] + work["bwd"][0] + work["reduce"][0]) / (lay_t * 1e-6) / 1e9, 1)
+        row["gbs"] = round((work["fwd"][0] + work["bwd"][0]) / (lay_t * 1e-6) / 1e9, 1)
         row["tflops"] = round((work["fwd"][1] + work["bwd"][1]) / (lay_t * 1e-6) / 1e12, 2)
         layers.append(row)
+
+    # the bucketed reduction of every layer's partials, once per step
+    red_bytes = (S + 1) * total * 4
+    red_t = op_us[(-1, "reduce")]
+    red_roof_us = red_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
+    step_bytes += red_bytes
+    bucket_reduce = {"us": round(red_t, 2), "bucket_floats": total, "algorithmic_bytes": red_bytes,
+                     "gbs": round(red_bytes / (red_t * 1e-6) / 1e9, 1), "roofline_us": round(red_roof_us, 2),
+                     "roofline_frac": round(red_roof_us / red_t, 4)}
 
     l, name, b_, f_, dense, peak = dom
     t = op_us[(l, name)]
@@ -1045,9 +1057,10 @@ def stack_bench(args, wl):
                    "shard_input": list(convs[0].x_shape), "layers": len(convs)},
         "tflops": round(step_flops / step_s / 1e12, 2),
         "step_bytes": step_bytes, "step_flops": step_flops,
-        "roofline_frac_step": round(sum(r["roofline_us"] for r in layers) * 1e-6 / step_s, 4),
+        "roofline_frac_step": round((sum(r["roofline_us"] for r in layers) + red_roof_us) * 1e-6 / step_s, 4),
         "roofline": roof,
         "layers": layers,
+        "bucket_reduce": bucket_reduce,
         "step_spread": spread,
         "wall_s_timed": round(wall, 4),
         "gpu_clocks": gpu_clocks(),

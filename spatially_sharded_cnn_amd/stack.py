@@ -7,8 +7,11 @@ weights Replicate).  Here all S shards of every activation are separate
 buffers of one device.  Forward runs layer by layer, each layer on all shards
 before the next (so every shard's halo is gathered from its neighbours' real
 outputs); backward runs the layers in reverse from the last layer's
-grad_output, reusing each layer's saved input halo, and reduces the shards'
-partial weight / bias gradients.
+grad_output, reusing each layer's saved input halo.  Each shard writes the
+partial weight / bias gradients of every layer into one bucket of its own,
+and one reduction over the shards' buckets at the end of backward turns them
+into the replicated gradients (the bucketed gradient all-reduce of
+data-parallel training, here a single call).
 
 This module only sequences calls of the C ABI (spatially_sharded_cnn_amd.sscnn);
 every operation runs in the library's kernels.
@@ -33,10 +36,26 @@ class LayerState:
     g: list = None              # per shard grad of the output
     g_halo: list = None
     dx: list = None             # per shard grad of the input
-    gw_parts: list = None       # per shard partial grad_weight
-    gb_parts: list = None       # per shard partial grad_bias
-    gw: torch.Tensor = None     # reduced grad_weight
+    gw_parts: list = None       # per shard partial grad_weight (a view of the shard's bucket)
+    gb_parts: list = None       # per shard partial grad_bias (a view of the shard's bucket)
+    gw: torch.Tensor = None     # reduced grad_weight (a view of the reduced bucket)
     gb: torch.Tensor = None     # reduced grad_bias
+
+
+def _up4(n: int) -> int:
+    return (n + 3) // 4 * 4
+
+
+def bucket_offsets(layers):
+    """Layout of a gradient bucket: per layer (offset of gW, offset of gB,
+    gW size, gB size), each piece starting on a 16-byte boundary; and the
+    bucket's total size in floats."""
+    off, out = 0, []
+    for L in layers:
+        nw, nb = L.co * (L.ci // L.groups) * L.k * L.k, L.co
+        out.append((off, off + _up4(nw), nw, nb))
+        off += _up4(nw) + _up4(nb)
+    return out, off
 
 
 class ShardedStack:
@@ -56,6 +75,10 @@ class ShardedStack:
         self.b = [None if t is None else (t if isinstance(t, torch.Tensor) else torch.from_numpy(t).to(device))
                   for t in biases]
         self.state: List[Optional[LayerState]] = [None] * len(self.layers)
+        self.buckets = None         # per shard: every layer's [gW | gB] partial
+        self.reduced = None         # their sum over the shards
+        self.offsets = bucket_offsets(self.layers)
+
 
     def _convs(self, L):
         n, ci, h, w = L.in_shape
@@ -104,6 +127,11 @@ class ShardedStack:
 
     def _backward(self, g_slices, need_input_grad):
         cur = list(g_slices)
+        offs, total = self.offsets
+        if self.buckets is None:
+            # zeroed once: the padding between pieces stays zero through the reductions
+            self.buckets = [torch.zeros(total, device=self.device) for _ in range(self.S)]
+            self.reduced = torch.zeros(total, device=self.device)
         for l in range(len(self.layers) - 1, -1, -1):
             st = self.state[l]
             convs = st.convs
@@ -115,21 +143,21 @@ class ShardedStack:
                 sscnn.halo_gather(c, sscnn.HALO_GRAD_OUTPUT, left, right, h, self.stream)
                 st.g_halo.append(h)
             ws = sscnn.new_workspace(c0, self.device)
-            nw = c0.w_shape[0] * c0.w_shape[1] * c0.w_shape[2] * c0.w_shape[3]
+            ow, ob, nw, nb = offs[l]
             for s, c in enumerate(convs):
-                buf = torch.empty(nw + c0.c_out, device=self.device)    # [gW | gB]
+                gw, gb = self.buckets[s][ow:ow + nw].view(c0.w_shape), self.buckets[s][ob:ob + nb]
                 if l > 0 or need_input_grad:
                     # grad_input and the weight / bias partials in one call
                     dx = torch.empty(c0.x_shape, device=self.device)
-                    sscnn.conv_bwd(c, st.x[s], st.x_halo[s], cur[s], st.g_halo[s], self.w[l], dx,
-                                   buf[:nw].view(c0.w_shape), buf[nw:], ws, self.stream)
+                    sscnn.conv_bwd(c, st.x[s], st.x_halo[s], cur[s], st.g_halo[s], self.w[l], dx, gw, gb, ws,
+                                   self.stream)
                     st.dx.append(dx)
                 else:
-                    sscnn.conv_bwd_weight_partial(c, st.x[s], st.x_halo[s], cur[s], buf[:nw].view(c0.w_shape),
-                                                  buf[nw:], ws, self.stream)
-                st.gw_parts.append(buf)
-            red = torch.empty(nw + c0.c_out, device=self.device)
-            sscnn.partial_reduce(st.gw_parts, red, self.stream)
-            st.gw, st.gb = red[:nw].view(c0.w_shape), red[nw:]
+                    sscnn.conv_bwd_weight_partial(c, st.x[s], st.x_halo[s], cur[s], gw, gb, ws, self.stream)
+                st.gw_parts.append(gw)
+                st.gb_parts.append(gb)
+            st.gw, st.gb = self.reduced[ow:ow + nw].view(c0.w_shape), self.reduced[ob:ob + nb]
             cur = st.dx
+        # the bucketed reduction of every layer's partials
+        sscnn.partial_reduce(self.buckets, self.reduced, self.stream)
         return cur

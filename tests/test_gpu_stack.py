@@ -65,10 +65,8 @@ def test_reduced_convnext_stack_all_layers_vs_oracle():
             assert_close(host(ls.y[s]), acts[l + 1][..., co[0]:co[1]], TOL_FWD, f"{L.name} shard {s} forward")
             assert_close(host(ls.dx[s]), dx_full[..., ci[0]:ci[1]], TOL_DX, f"{L.name} shard {s} grad_input")
             gw_s, gb_s = oracle.conv_bwd_weight(acts[l], g_out, L.k, L.stride, L.pad, L.groups, cols=co)
-            nw = gw_s.size
-            part = host(ls.gw_parts[s])
-            assert_close(part[:nw].reshape(gw_s.shape), gw_s, TOL_GW, f"{L.name} shard {s} grad_weight partial")
-            assert_close(part[nw:], gb_s, TOL_GW, f"{L.name} shard {s} grad_bias partial")
+            assert_close(host(ls.gw_parts[s]), gw_s, TOL_GW, f"{L.name} shard {s} grad_weight partial")
+            assert_close(host(ls.gb_parts[s]), gb_s, TOL_GW, f"{L.name} shard {s} grad_bias partial")
         assert_close(host(ls.gw), gw_full, TOL_GW, f"{L.name} reduced grad_weight")
         assert_close(host(ls.gb), gb_full, TOL_GW, f"{L.name} reduced grad_bias")
 
@@ -129,12 +127,11 @@ def test_full_size_convnext_stack_identities(name):
         ls = st.state[l]
         b = st.b[l].double().view(1, -1, 1, 1)
         w = st.w[l]
-        nw = w.numel()
         total_yg = total_xdx = scale_all = 0.0
         for sh in range(S):
             ym = ls.y[sh].double() - b
             lhs = _dot(ym, ls.g[sh])
-            gw_s = ls.gw_parts[sh][:nw].view_as(w)
+            gw_s = ls.gw_parts[sh]
             rhs = _dot(w, gw_s)
             scale = _absdot(w, gw_s) + 1e-30
             assert abs(lhs - rhs) <= 1e-5 * scale, f"{name} {L.name} shard {sh}: <Y-b,G>={lhs} <W,gW>={rhs}"
@@ -144,10 +141,10 @@ def test_full_size_convnext_stack_identities(name):
             assert torch.isfinite(ls.dx[sh]).all() and torch.isfinite(ls.y[sh]).all()
         assert abs(total_yg - total_xdx) <= 1e-5 * (scale_all + 1e-30), \
             f"{name} {L.name}: sum <Y-b,G> = {total_yg}, sum <X,dX> = {total_xdx}"
-        acc = ls.gw_parts[0].clone()
+        acc_w, acc_b = ls.gw_parts[0].clone(), ls.gb_parts[0].clone()
         for sh in range(1, S):
-            acc = acc + ls.gw_parts[sh]
-        assert torch.equal(torch.cat([ls.gw.reshape(-1), ls.gb]), acc), f"{name} {L.name}: reduction"
+            acc_w, acc_b = acc_w + ls.gw_parts[sh], acc_b + ls.gb_parts[sh]
+        assert torch.equal(ls.gw, acc_w) and torch.equal(ls.gb, acc_b), f"{name} {L.name}: bucketed reduction"
         _say(f"  {name} {L.name}: identities hold")
 
 
@@ -162,7 +159,8 @@ def test_full_size_convnext_stack_measured_shard_vs_oracle(name):
     st.forward(slices(T.x, S))
     st.backward(slices(T.g, S))
     torch.cuda.synchronize()
-    got = [dict(y=host(ls.y[s]), dx=host(ls.dx[s]), part=host(ls.gw_parts[s])) for ls in st.state]
+    got = [dict(y=host(ls.y[s]), dx=host(ls.dx[s]), gw=host(ls.gw_parts[s]), gb=host(ls.gb_parts[s]))
+           for ls in st.state]
     del st
     torch.cuda.empty_cache()
     t0 = time.perf_counter()
@@ -170,11 +168,9 @@ def test_full_size_convnext_stack_measured_shard_vs_oracle(name):
     _say(f"  {name}: oracle share of the chain in {time.perf_counter() - t0:.1f} s")
     for l, L in enumerate(wl.layers):
         r, gl = ref[l], got[l]
-        nw = r["gw"].size
         e_y = assert_close(gl["y"], r["y"], TOL_FWD, f"{name} {L.name} forward")
         e_dx = assert_close(gl["dx"], r["dx"], TOL_DX, f"{name} {L.name} grad_input")
-        e_gw = assert_close(gl["part"][:nw].reshape(r["gw"].shape), r["gw"], TOL_GW,
-                            f"{name} {L.name} grad_weight partial")
-        e_gb = assert_close(gl["part"][nw:], r["gb"], TOL_GW, f"{name} {L.name} grad_bias partial")
+        e_gw = assert_close(gl["gw"], r["gw"], TOL_GW, f"{name} {L.name} grad_weight partial")
+        e_gb = assert_close(gl["gb"], r["gb"], TOL_GW, f"{name} {L.name} grad_bias partial")
         _say(f"  {name} {L.name}: normwise errors forward {e_y:.2e} grad_input {e_dx:.2e} "
              f"grad_weight {e_gw:.2e} grad_bias {e_gb:.2e}")
