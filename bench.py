@@ -95,6 +95,8 @@ def _parse():
                     help="stack workloads: after the set-up, run only operation OP (e.g. ds3.conv_bwd) "
                          "--profile-reps times and exit (for counter runs of one operation)")
     ap.add_argument("--profile-reps", type=int, default=10)
+    ap.add_argument("--no-push", action="store_true",
+                    help="stack workloads: every layer gathers its halos (no push form from the layer before)")
     ap.add_argument("--sets", type=int, default=3, help="independent buffer sets rotated per step")
     ap.add_argument("--op-reps", type=int, default=20, help="back-to-back calls per operation timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -880,7 +882,9 @@ def stack_bench(args, wl):
     (halo_gather(G) + conv_bwd per layer, each grad_input feeding the layer
     below, each layer's grad_weight / grad_bias partials written into the
     shard's gradient bucket), and one partial_reduce of the four shards'
-    buckets.  The neighbours' activations and gradients and the other shards'
+    buckets.  A stem or downsample followed by a layer with a halo pushes that
+    halo from its epilogue (conv_fwd_push / conv_bwd_push) instead of the
+    consumer gathering it.  The neighbours' activations and gradients and the other shards'
     buckets come from an untimed run of all shards."""
     import torch
     from spatially_sharded_cnn_amd import sscnn, workloads
@@ -896,7 +900,7 @@ def stack_bench(args, wl):
         return [torch.from_numpy(np.ascontiguousarray(a[:, :, :, i * w:(i + 1) * w])).to(dev) for i in range(S)]
 
     xs, gs = slices(T.x), slices(T.g)
-    st = ShardedStack(wl.layers, S, T.weights, T.biases)
+    st = ShardedStack(wl.layers, S, T.weights, T.biases, push=not args.no_push)
     st.forward(xs)
     st.backward(gs)
     torch.cuda.synchronize()
@@ -916,21 +920,51 @@ def stack_bench(args, wl):
     wss = [sscnn.new_workspace(c) for c in convs]
     ins = [xs[s]] + ys[:-1]                       # each layer's input: the previous layer's output
     gouts = dxs[1:] + [gs[s]]                     # each layer's grad_output: the next layer's grad_input
+    # Push-form halos (a stem / downsample writing the next layer's halos from its epilogue): this
+    # shard's step pushes into its neighbours' halo buffers (those of the untimed all-shard run); its
+    # own halos, which its neighbours push, are copied from that run once, before timing.
+    fpush = [st.pushes_forward(l) for l in range(nl)]
+    bpush = [st.pushes_backward(l) for l in range(nl)]
+    for l in range(nl):
+        if fpush[l]:
+            xhs[l + 1].copy_(st.state[l + 1].x_halo[s])
+        if bpush[l]:
+            ghs[l - 1].copy_(st.state[l - 1].g_halo[s])
+    torch.cuda.synchronize()
+
+    def fwd_push(l):
+        lft, rgt = nbr(st.state[l + 1].x_halo)
+        return sscnn.make_push(convs[l + 1], sscnn.HALO_INPUT, lft, rgt, xhs[l + 1])
+
+    def bwd_push(l):
+        lft, rgt = nbr(st.state[l - 1].g_halo)
+        return sscnn.make_push(convs[l - 1], sscnn.HALO_GRAD_OUTPUT, lft, rgt, ghs[l - 1])
 
     def op_list():
         ops = []
         for l, c in enumerate(convs):
-            if xhs[l] is not None:
+            if xhs[l] is not None and not (l > 0 and fpush[l - 1]):
                 ops.append((l, "halo_x", lambda l=l, c=c: sscnn.halo_gather(
                     c, sscnn.HALO_INPUT, *nbr(st.state[l].x), xhs[l])))
-            ops.append((l, "fwd", lambda l=l, c=c: sscnn.conv_fwd(c, ins[l], xhs[l], st.w[l], st.b[l], ys[l])))
+            if fpush[l]:
+                p = fwd_push(l)
+                ops.append((l, "fwd", lambda l=l, c=c, p=p: sscnn.conv_fwd_push(
+                    c, ins[l], xhs[l], st.w[l], st.b[l], ys[l], p)))
+            else:
+                ops.append((l, "fwd", lambda l=l, c=c: sscnn.conv_fwd(c, ins[l], xhs[l], st.w[l], st.b[l],
+                                                                      ys[l])))
         for l in range(nl - 1, -1, -1):
             c = convs[l]
-            if ghs[l] is not None:
+            if ghs[l] is not None and not (l + 1 < nl and bpush[l + 1]):
                 ops.append((l, "halo_g", lambda l=l, c=c: sscnn.halo_gather(
                     c, sscnn.HALO_GRAD_OUTPUT, *nbr(st.state[l].g), ghs[l])))
-            ops.append((l, "bwd", lambda l=l, c=c: sscnn.conv_bwd(
-                c, ins[l], xhs[l], gouts[l], ghs[l], st.w[l], dxs[l], gws[l], gbs[l], wss[l])))
+            if bpush[l]:
+                p = bwd_push(l)
+                ops.append((l, "bwd", lambda l=l, c=c, p=p: sscnn.conv_bwd_push(
+                    c, ins[l], xhs[l], gouts[l], ghs[l], st.w[l], dxs[l], gws[l], gbs[l], p, wss[l])))
+            else:
+                ops.append((l, "bwd", lambda l=l, c=c: sscnn.conv_bwd(
+                    c, ins[l], xhs[l], gouts[l], ghs[l], st.w[l], dxs[l], gws[l], gbs[l], wss[l])))
         ops.append((-1, "reduce", lambda: sscnn.partial_reduce(
             [bucket if i == s else st.buckets[i] for i in range(S)], reduced)))
         return ops
@@ -1054,7 +1088,8 @@ def stack_bench(args, wl):
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description, "shard": f"{s} of {S}",
-                   "shard_input": list(convs[0].x_shape), "layers": len(convs)},
+                   "shard_input": list(convs[0].x_shape), "layers": len(convs),
+                   "halos": "gathered" if args.no_push else "pushed where the layer before is a stem or downsample"},
         "tflops": round(step_flops / step_s / 1e12, 2),
         "step_bytes": step_bytes, "step_flops": step_flops,
         "roofline_frac_step": round((sum(r["roofline_us"] for r in layers) + red_roof_us) * 1e-6 / step_s, 4),

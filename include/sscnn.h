@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSCNN_ABI_VERSION 9
+#define SSCNN_ABI_VERSION 10
 
 /* Status codes. */
 #define SSCNN_OK 0
@@ -204,6 +204,55 @@ int sscnn_conv_bwd(const sscnn_conv_t *conv, const float *x, const float *x_halo
                    const float *grad_y, const float *grad_y_halo, const float *weight,
                    float *grad_x, float *grad_w_part, float *grad_b_part,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Push form of the halo exchange, for a layer whose output (or grad_input)
+ * the next layer convolves with a halo: the producing call writes, besides
+ * its own slice, its first hr columns into the left neighbour's halo buffer
+ * and its last hl columns into the right neighbour's -- the columns the
+ * neighbours' halos need (blog, Figure 1 text; kwkr.cn retelling, section
+ * 2.2) -- from the registers that hold them, instead of the consumer
+ * gathering them from the neighbours' slices afterwards (one 128-byte line
+ * fetched per few-byte row piece).  On several GPUs these are the stores a
+ * shard makes into its neighbours' memory over the fabric.
+ *   hl, hr     the NEXT layer's halo widths (its sscnn_conv_t halo_l / halo_r
+ *              for a forward, ghalo_l / ghalo_r for a grad_input), each at
+ *              most the pushed slice's width
+ *   to_left    the left neighbour's halo buffer (n, c, rows, hl + hr): this
+ *              slice's columns [0, hr) land in its columns [hl, hl + hr);
+ *              NULL exactly when shard == 0
+ *   to_right   the right neighbour's halo buffer: this slice's last hl
+ *              columns land in its columns [0, hl); NULL exactly when
+ *              shard == num_shards - 1
+ *   own        this shard's own halo buffer, whose side without a neighbour
+ *              (left at shard 0, right at the last shard) is zeroed; may be
+ *              NULL when both neighbours exist
+ * After every shard's producing call, each shard's halo equals what
+ * sscnn_halo_gather would have written.  The halo buffers are written, never
+ * read; they may not alias any other argument.
+ */
+typedef struct sscnn_push {
+    int32_t hl, hr;
+    float *to_left;
+    float *to_right;
+    float *own;
+} sscnn_push_t;
+
+/* sscnn_conv_fwd that also pushes y's edge columns.  Layers on the
+ * matrix-core patchify path (k == stride, pad 0, groups 1: the stem and the
+ * downsamples) push from the kernel's epilogue; any other layer runs
+ * sscnn_conv_fwd and then copies its edge columns (at the cost of a gather).
+ * push may be NULL (then it is sscnn_conv_fwd). */
+int sscnn_conv_fwd_push(const sscnn_conv_t *conv, const float *x, const float *x_halo,
+                        const float *weight, const float *bias, float *y,
+                        const sscnn_push_t *push, void *stream);
+
+/* sscnn_conv_bwd that also pushes grad_x's edge columns (same paths). */
+int sscnn_conv_bwd_push(const sscnn_conv_t *conv, const float *x, const float *x_halo,
+                        const float *grad_y, const float *grad_y_halo, const float *weight,
+                        float *grad_x, float *grad_w_part, float *grad_b_part,
+                        void *workspace, size_t workspace_bytes, const sscnn_push_t *push,
+                        void *stream);
 
 /*
  * sscnn_conv_bwd without a workspace argument, for callers that cannot

@@ -385,6 +385,104 @@ int sscnn_conv_bwd(const sscnn_conv_t* conv, const float* x, const float* x_halo
                       "conv_bwd launch");
 }
 
+namespace {
+
+// Validates a push descriptor for a producer whose pushed slice is `width`
+// columns wide; fills *out and *active (false: nothing to push).
+int check_push(const sscnn_conv_t* conv, const Geom& g, const sscnn_push_t* push, int width, const void* const* others,
+               int nothers, Push* out, bool* active)
+{
+    *active = false;
+    if (!push) return SSCNN_OK;
+    if (push->hl < 0 || push->hr < 0 || push->hl > width || push->hr > width)
+        return fail(SSCNN_EINVAL, "push widths hl=%d hr=%d must lie in [0, %d]", push->hl, push->hr, width);
+    if (push->hl + push->hr == 0) return SSCNN_OK;
+    const bool first = conv->shard == 0, last = conv->shard == conv->num_shards - 1;
+    if (first != (push->to_left == nullptr))
+        return fail(SSCNN_EINVAL, "push to_left must be NULL exactly for shard 0 (shard=%d)", conv->shard);
+    if (last != (push->to_right == nullptr))
+        return fail(SSCNN_EINVAL, "push to_right must be NULL exactly for the last shard (shard=%d)", conv->shard);
+    if ((first && push->hl > 0) || (last && push->hr > 0)) TRY(need(push->own, "push own"));
+    else TRY(optional(push->own, "push own"));
+    TRY(optional(push->to_left, "push to_left"));
+    TRY(optional(push->to_right, "push to_right"));
+    const void* bufs[3] = {push->to_left, push->to_right, push->own};
+    for (const void* b : bufs) {
+        if (!b) continue;
+        for (int k = 0; k < nothers; ++k)
+            if (b == others[k]) return fail(SSCNN_EINVAL, "a push halo buffer aliases another argument");
+    }
+    out->to_left = push->to_left;
+    out->to_right = push->to_right;
+    out->own = push->own;
+    out->hl = push->hl;
+    out->hr = push->hr;
+    *active = true;
+    return SSCNN_OK;
+}
+
+}  // namespace
+
+int sscnn_conv_fwd_push(const sscnn_conv_t* conv, const float* x, const float* x_halo, const float* weight,
+                        const float* bias, float* y, const sscnn_push_t* push, void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    TRY(need(x, "x"));
+    if (g.hl + g.hr) TRY(need(x_halo, "x_halo")); else TRY(optional(x_halo, "x_halo"));
+    TRY(need(weight, "weight"));
+    TRY(optional(bias, "bias"));
+    TRY(need(y, "y"));
+    Push P;
+    bool active;
+    const void* others[5] = {x, x_halo, weight, bias, y};
+    TRY(check_push(conv, g, push, g.wol, others, 5, &P, &active));
+    const hipStream_t st = (hipStream_t)stream;
+    if (active && patch_supported(g))     // pushed from the matrix kernel's epilogue
+        return hip_status(launch_patch_fwd(g, x, weight, bias, y, st, nullptr, &P), "conv_fwd_push launch");
+    hipError_t e = kernels_conv_fwd(g, x, x_halo, weight, bias, y, st);
+    if (e == hipSuccess && active)
+        e = launch_push_edges(y, (int64_t)g.n * g.co, g.ho, g.wol, P.hl, P.hr, P.to_left, P.to_right, P.own, st);
+    return hip_status(e, "conv_fwd_push launch");
+}
+
+int sscnn_conv_bwd_push(const sscnn_conv_t* conv, const float* x, const float* x_halo, const float* grad_y,
+                        const float* grad_y_halo, const float* weight, float* grad_x, float* grad_w_part,
+                        float* grad_b_part, void* workspace, size_t workspace_bytes, const sscnn_push_t* push,
+                        void* stream)
+{
+    Geom g;
+    TRY(check(conv, &g));
+    TRY(need(x, "x"));
+    if (g.hl + g.hr) TRY(need(x_halo, "x_halo")); else TRY(optional(x_halo, "x_halo"));
+    TRY(need(grad_y, "grad_y"));
+    if (g.ghl + g.ghr) TRY(need(grad_y_halo, "grad_y_halo")); else TRY(optional(grad_y_halo, "grad_y_halo"));
+    TRY(need(weight, "weight"));
+    TRY(need(grad_x, "grad_x"));
+    TRY(need(grad_w_part, "grad_w_part"));
+    TRY(optional(grad_b_part, "grad_b_part"));
+    if (grad_x == x || grad_x == x_halo || grad_x == grad_y || grad_x == grad_y_halo)
+        return fail(SSCNN_EINVAL, "grad_x aliases an input");
+    size_t ws_need;
+    TRY(need_workspace(g, workspace, workspace_bytes, &ws_need));
+    Push P;
+    bool active;
+    const void* others[9] = {x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_part, grad_b_part, workspace};
+    TRY(check_push(conv, g, push, g.wl, others, 9, &P, &active));
+    const hipStream_t st = (hipStream_t)stream;
+    void* ws = ws_need ? workspace : nullptr;
+    hipError_t e;
+    if (active && patch_supported(g)) {   // pushed from the matrix kernel's epilogue
+        e = launch_patch_bwd_input(g, grad_y, weight, grad_x, st, nullptr, &P);
+        if (e == hipSuccess) e = kernels_conv_bwd_weight(g, x, x_halo, grad_y, grad_w_part, grad_b_part, ws, st);
+        return hip_status(e, "conv_bwd_push launch");
+    }
+    e = kernels_conv_bwd(g, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_part, grad_b_part, ws, st);
+    if (e == hipSuccess && active)
+        e = launch_push_edges(grad_x, (int64_t)g.n * g.ci, g.h, g.wl, P.hl, P.hr, P.to_left, P.to_right, P.own, st);
+    return hip_status(e, "conv_bwd_push launch");
+}
+
 int sscnn_conv_bwd_noalloc(const sscnn_conv_t* conv, const float* x, const float* x_halo,
                            const float* grad_y, const float* grad_y_halo, const float* weight,
                            float* grad_x, float* grad_w_part, float* grad_b_part, void* stream)

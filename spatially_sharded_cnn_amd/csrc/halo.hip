@@ -42,6 +42,32 @@ halo_gather_kernel(const float* __restrict__ left, const float* __restrict__ rig
     }
 }
 
+// Push form of the exchange for layers whose kernels do not push from their
+// epilogue: after the layer wrote its slice t, one thread per (row, halo
+// column) copies the slice's last hl columns into the right neighbour's halo
+// (its columns [0, hl)) and its first hr columns into the left neighbour's
+// (columns [hl, hl + hr)), and zeros the own halo's sides without a
+// neighbour.  Reads hit one 128-byte line per few-byte row piece, like the
+// gather it replaces.
+__global__ void __launch_bounds__(256)
+push_edges_kernel(const float* __restrict__ t, int64_t total_rows, int width, int hl, int hr,
+                  float* __restrict__ to_left, float* __restrict__ to_right, float* __restrict__ own)
+{
+    const int hw = hl + hr;
+    const int64_t total = total_rows * hw;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = i / hw;
+        const int e = (int)(i - row * hw);
+        if (e < hl) {                    // the slice's column width - hl + e
+            if (to_right) to_right[row * hw + e] = t[row * width + (width - hl + e)];
+            if (!to_left) own[row * hw + e] = 0.f;
+        } else {                         // the slice's column e - hl
+            if (to_left) to_left[row * hw + e] = t[row * width + (e - hl)];
+            if (!to_right) own[row * hw + e] = 0.f;
+        }
+    }
+}
+
 struct PartPtrs {
     const float* p[kMaxParts];
 };
@@ -114,6 +140,16 @@ hipError_t launch_halo_gather(const float* left, const float* right, int64_t pla
             hipLaunchKernelGGL(halo_gather_kernel<0>, dim3(grid), dim3(256), 0, st, left, right,
                                total_rows, width, hl, hw, halo);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_push_edges(const float* t, int64_t planes, int rows, int width, int hl, int hr, float* to_left,
+                             float* to_right, float* own, hipStream_t st)
+{
+    const int64_t total_rows = planes * rows;
+    if (total_rows == 0 || hl + hr == 0) return hipSuccess;
+    hipLaunchKernelGGL(push_edges_kernel, dim3(grid_for(total_rows * (hl + hr), 256)), dim3(256), 0, st, t,
+                       total_rows, width, hl, hr, to_left, to_right, own);
     return hipGetLastError();
 }
 

@@ -88,6 +88,11 @@ hipError_t launch_direct_bwd_input(const Geom& g, const float* gy, const float* 
 hipError_t launch_direct_bwd_weight(const Geom& g, const float* x, const float* xh,
                                     const float* gy, float* gw, float* gb, hipStream_t st);
 
+// Push form of the halo exchange for a slice t (planes, rows, width) written by a kernel that does not
+// push from its epilogue (halo.hip): its edge columns into the neighbours' halos, zeros on the open sides.
+hipError_t launch_push_edges(const float* t, int64_t planes, int rows, int width, int hl, int hr, float* to_left,
+                             float* to_right, float* own, hipStream_t st);
+
 // Streaming copy of count floats (stream.hip); src and dst 16-byte aligned.
 hipError_t launch_stream_copy(const float* src, float* dst, int64_t count, hipStream_t st);
 

@@ -72,9 +72,38 @@ struct PArgs {
     int with_bias;                    // BWW: also sum grad_output per channel
     float* act;           // FWD, pointwise only: GELU(Y) as well, or null
     const float* pre;     // BWI, pointwise only: dX is scaled by GELU'(pre) (pre shaped like X), or null
+    // FWD, BWI: the push form of the next layer's halo exchange (all null: none), for the pushed
+    // tensor Y (FWD) or dX (BWI); the halo buffers have rows ph_l + ph_r wide.
+    float* push_l;        // left neighbour's halo: this slice's first ph_r columns go to [ph_l, ph_l + ph_r)
+    float* push_r;        // right neighbour's halo: this slice's last ph_l columns go to [0, ph_l)
+    float* push_own;      // own halo: the side without a neighbour is zeroed
+    int ph_l, ph_r;
 };
 
 __device__ __forceinline__ int64_t slab_floats(const PArgs& a) { return (int64_t)a.Co * (a.Kt + 1); }
+
+__device__ __forceinline__ bool pushes(const PArgs& a) { return a.push_l || a.push_r || a.push_own; }
+
+// Value v at column j of row (plane, i) of the pushed tensor (rows of w columns, rows_per_plane rows):
+// the copies the neighbours' halos need, and the zeros of the own halo's sides that have no
+// neighbour (columns j < ph_l stand for the left side's ph_l halo columns, the last ph_r for the
+// right side's, so each is written once per row).
+__device__ __forceinline__ void push_value(const PArgs& a, int64_t plane, int rows_per_plane, int i, int j, int w,
+                                           float v)
+{
+    const int hw = a.ph_l + a.ph_r;
+    const int64_t base = (plane * rows_per_plane + i) * hw;
+    if (a.push_l) {
+        if (j < a.ph_r) a.push_l[base + a.ph_l + j] = v;                   // left neighbour's right side
+    } else if (j < a.ph_l) {
+        a.push_own[base + j] = 0.f;                                        // no left neighbour
+    }
+    if (a.push_r) {
+        if (j >= w - a.ph_l) a.push_r[base + (j - (w - a.ph_l))] = v;      // right neighbour's left side
+    } else if (j >= w - a.ph_r) {
+        a.push_own[base + a.ph_l + (j - (w - a.ph_r))] = 0.f;              // no right neighbour
+    }
+}
 
 // Global -> registers for one sub-chunk of kSub reduction rows (8 A values
 // and 8 B values per thread), then registers -> LDS.  Each mode gathers its
@@ -393,6 +422,12 @@ patch_kernel(PArgs a)
         for (int y = 0; y < YB; ++y) {
             const int rb = m0 + wm * (TM / 2) + x * 32;     // block's first row (a multiple of 4)
             const int col = n0 + wn * (TN / 2) + y * 32 + l32;
+            // the lane's pixel, and whether its column (or, for grad_input, one of its s input
+            // columns) lies within the pushed halo widths of either edge: only such lanes push
+            const int pi = col / a.Wo, pj = col - pi * a.Wo;
+            const int pmax = a.ph_l > a.ph_r ? a.ph_l : a.ph_r;
+            const int pw = MODE == FWD ? a.Wo : a.W, c0 = MODE == FWD ? pj : pj * S;
+            const bool edge = pushes(a) && (c0 < pmax || c0 + (MODE == FWD ? 0 : S - 1) >= pw - pmax);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int row = rb + 4 * hi + 8 * q;  // rows row .. row + 3 in registers 4q .. 4q + 3
@@ -405,6 +440,7 @@ patch_kernel(PArgs a)
                                 const float v = acc[x][y][4 * q + r] + (a.b ? a.b[row + r] : 0.f);
                                 yp[(int64_t)(row + r) * a.P] = v;
                                 if (a.act) a.act[((int64_t)outer * a.Co + row + r) * a.P + col] = gelu(v);
+                                if (edge) push_value(a, (int64_t)outer * a.Co + row + r, a.Ho, pi, pj, a.Wo, v);
                             }
                     }
                 } else if constexpr (MODE == BWI) {
@@ -420,12 +456,19 @@ patch_kernel(PArgs a)
                                 float v = acc[x][y][4 * q + r];
                                 if (a.pre) v = v * gelu_grad(a.pre[(int64_t)outer * a.Ci * a.H * a.W + o]);
                                 dxi[o] = v;
+                                if (edge) push_value(a, (int64_t)outer * a.Ci + row + r, a.H, i, j, a.W, v);
                             }
                         } else if constexpr (S == 4) {
                             const int ci = row / 16, kh = (row / 4) % 4;
                             *reinterpret_cast<float4*>(dxi + ((int64_t)ci * a.H + i * 4 + kh) * a.W + j * 4) =
                                 make_float4(acc[x][y][4 * q], acc[x][y][4 * q + 1], acc[x][y][4 * q + 2],
                                             acc[x][y][4 * q + 3]);
+                            if (edge) {
+#pragma unroll
+                                for (int kw = 0; kw < 4; ++kw)
+                                    push_value(a, (int64_t)outer * a.Ci + ci, a.H, i * 4 + kh, j * 4 + kw, a.W,
+                                               acc[x][y][4 * q + kw]);
+                            }
                         } else {
 #pragma unroll
                             for (int h = 0; h < 2; ++h) {
@@ -433,6 +476,12 @@ patch_kernel(PArgs a)
                                 const int ci = rr / 4, kh = (rr / 2) % 2;
                                 *reinterpret_cast<float2*>(dxi + ((int64_t)ci * a.H + i * 2 + kh) * a.W + j * 2) =
                                     make_float2(acc[x][y][4 * q + 2 * h], acc[x][y][4 * q + 2 * h + 1]);
+                                if (edge) {
+#pragma unroll
+                                    for (int kw = 0; kw < 2; ++kw)
+                                        push_value(a, (int64_t)outer * a.Ci + ci, a.H, i * 2 + kh, j * 2 + kw, a.W,
+                                                   acc[x][y][4 * q + 2 * h + kw]);
+                                }
                             }
                         }
                     }
@@ -592,22 +641,34 @@ hipError_t launch_rows(PArgs& a, int rows, int tm, int s, hipStream_t st)
     return tm == 64 ? launch<MODE, 64, 128>(a, s, grid, st) : launch<MODE, 128, 128>(a, s, grid, st);
 }
 
+static void set_push(PArgs& a, const Push* push)
+{
+    if (!push) return;
+    a.push_l = push->to_left;
+    a.push_r = push->to_right;
+    a.push_own = push->own;
+    a.ph_l = push->hl;
+    a.ph_r = push->hr;
+}
+
 hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const float* b, float* y,
-                            hipStream_t st, float* act)
+                            hipStream_t st, float* act, const Push* push)
 {
     if (act && g.k != 1) return hipErrorInvalidValue;
     PArgs a = make_args(g);
     a.x = x; a.w = w; a.b = b; a.out = y; a.act = act;
+    set_push(a, push);
     a.tiles_n = (a.P + 127) / 128;
     return launch_rows<FWD>(a, a.Co, row_tile(a.Co, a, false), g.k, st);
 }
 
 hipError_t launch_patch_bwd_input(const Geom& g, const float* gy, const float* w, float* gx, hipStream_t st,
-                                  const float* pre)
+                                  const float* pre, const Push* push)
 {
     if (pre && g.k != 1) return hipErrorInvalidValue;
     PArgs a = make_args(g);
     a.g = gy; a.w = w; a.out = gx; a.pre = pre;
+    set_push(a, push);
     a.tiles_n = (a.P + 127) / 128;
     return launch_rows<BWI>(a, a.Kt, row_tile(a.Kt, a, a.Kt <= kNarrowK), g.k, st);
 }

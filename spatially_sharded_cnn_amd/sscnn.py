@@ -34,7 +34,7 @@ EXPORTED = (
     "sscnn_gconv_init", "sscnn_grid_row_halo_gather", "sscnn_grid_col_halo_gather", "sscnn_gconv_fwd",
     "sscnn_gconv_bwd_input", "sscnn_gconv_bwd_weight_workspace_bytes", "sscnn_gconv_bwd_weight_partial",
     "sscnn_gconv_bwd", "sscnn_pointwise_gelu_fwd", "sscnn_pointwise_bwd_input_gelu",
-    "sscnn_conv_bwd_noalloc", "sscnn_stream_copy",
+    "sscnn_conv_bwd_noalloc", "sscnn_stream_copy", "sscnn_conv_fwd_push", "sscnn_conv_bwd_push",
 )
 NOALLOC_SCRATCH_BYTES = 8 << 20      # SSCNN_NOALLOC_SCRATCH_BYTES
 
@@ -71,6 +71,12 @@ class Conv(ctypes.Structure):
         if which == HALO_INPUT:
             return (self.n, self.c_in, self.h, self.halo_l + self.halo_r)
         return (self.n, self.c_out, self.h_out, self.ghalo_l + self.ghalo_r)
+
+
+class Push(ctypes.Structure):
+    """Mirror of sscnn_push_t."""
+    _fields_ = [("hl", ctypes.c_int32), ("hr", ctypes.c_int32), ("to_left", ctypes.c_void_p),
+                ("to_right", ctypes.c_void_p), ("own", ctypes.c_void_p)]
 
 
 class HConv(ctypes.Structure):
@@ -155,6 +161,9 @@ def lib() -> ctypes.CDLL:
         L.sscnn_conv_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.sscnn_conv_bwd_noalloc.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.sscnn_stream_copy.argtypes = [_vp, _vp, ctypes.c_int64, _vp]
+        PP = ctypes.POINTER(Push)
+        L.sscnn_conv_fwd_push.argtypes = [P, _vp, _vp, _vp, _vp, _vp, PP, _vp]
+        L.sscnn_conv_bwd_push.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, PP, _vp]
         L.sscnn_partial_reduce.argtypes = [ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int64, _vp, _vp]
         L.sscnn_conv_fwd_interior.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
         L.sscnn_conv_fwd_edge.argtypes = [P, _vp, _vp, _vp, _vp]
@@ -205,7 +214,7 @@ def lib() -> ctypes.CDLL:
                   "sscnn_gconv_init", "sscnn_grid_row_halo_gather", "sscnn_grid_col_halo_gather",
                   "sscnn_gconv_fwd", "sscnn_gconv_bwd_input", "sscnn_gconv_bwd_weight_partial", "sscnn_gconv_bwd",
                   "sscnn_pointwise_gelu_fwd", "sscnn_pointwise_bwd_input_gelu", "sscnn_conv_bwd_noalloc",
-                  "sscnn_stream_copy"):
+                  "sscnn_stream_copy", "sscnn_conv_fwd_push", "sscnn_conv_bwd_push"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -347,6 +356,48 @@ def stream_copy(src, dst, stream=None):
     n = src.numel()
     _check(lib().sscnn_stream_copy(_ptr(src, (n,), "src"), _ptr(dst, (n,), "dst"), n, _stream(stream)),
            "stream_copy")
+
+
+def make_push(which_conv: Conv, which: int, to_left, to_right, own):
+    """A push descriptor for the next layer's halo of kind `which` (HALO_INPUT:
+    its input halo, widths halo_l / halo_r; HALO_GRAD_OUTPUT: its grad_output
+    halo, ghalo_l / ghalo_r), described by that layer's descriptor
+    which_conv on THIS shard; to_left / to_right / own are the halo buffers
+    of the left neighbour, the right neighbour and this shard (None where
+    there is no such neighbour / no open side)."""
+    hl, hr = (which_conv.halo_l, which_conv.halo_r) if which == HALO_INPUT else (which_conv.ghalo_l,
+                                                                               which_conv.ghalo_r)
+    hs = which_conv.halo_shape(which)
+    return Push(hl, hr, _ptr(to_left, hs, "to_left", True), _ptr(to_right, hs, "to_right", True),
+                _ptr(own, hs, "own", True))
+
+
+def conv_fwd_push(conv: Conv, x, x_halo, weight, bias, y, push: Optional[Push], stream=None):
+    """sscnn_conv_fwd_push: conv_fwd that also writes y's edge columns into the
+    next layer's halo buffers (push from make_push, or None)."""
+    hs = conv.halo_shape(HALO_INPUT)
+    _check(lib().sscnn_conv_fwd_push(ctypes.byref(conv), _ptr(x, conv.x_shape, "x"),
+                                     _ptr(x_halo, hs, "x_halo", hs[3] == 0),
+                                     _ptr(weight, conv.w_shape, "weight"),
+                                     _ptr(bias, (conv.c_out,), "bias", True), _ptr(y, conv.y_shape, "y"),
+                                     ctypes.byref(push) if push is not None else None, _stream(stream)),
+           "conv_fwd_push")
+
+
+def conv_bwd_push(conv: Conv, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_part, grad_b_part,
+                  push: Optional[Push], workspace=None, stream=None):
+    """sscnn_conv_bwd_push: conv_bwd that also writes grad_x's edge columns into
+    the previous layer's grad_output halo buffers."""
+    hs, gs = conv.halo_shape(HALO_INPUT), conv.halo_shape(HALO_GRAD_OUTPUT)
+    ws_ptr, ws_bytes = _workspace(workspace)
+    _check(lib().sscnn_conv_bwd_push(
+        ctypes.byref(conv), _ptr(x, conv.x_shape, "x"), _ptr(x_halo, hs, "x_halo", hs[3] == 0),
+        _ptr(grad_y, conv.y_shape, "grad_y"), _ptr(grad_y_halo, gs, "grad_y_halo", gs[3] == 0),
+        _ptr(weight, conv.w_shape, "weight"), _ptr(grad_x, conv.x_shape, "grad_x"),
+        _ptr(grad_w_part, conv.w_shape, "grad_w_part"),
+        _ptr(grad_b_part, (conv.c_out,), "grad_b_part", True), ws_ptr, ws_bytes,
+        ctypes.byref(push) if push is not None else None, _stream(stream)),
+        "conv_bwd_push")
 
 
 def conv_bwd_noalloc(conv: Conv, x, x_halo, grad_y, grad_y_halo, weight, grad_x, grad_w_part, grad_b_part,

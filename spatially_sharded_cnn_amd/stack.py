@@ -7,7 +7,11 @@ weights Replicate).  Here all S shards of every activation are separate
 buffers of one device.  Forward runs layer by layer, each layer on all shards
 before the next (so every shard's halo is gathered from its neighbours' real
 outputs); backward runs the layers in reverse from the last layer's
-grad_output, reusing each layer's saved input halo.  Each shard writes the
+grad_output, reusing each layer's saved input halo.  Where a layer with
+k == stride (the stem, a downsample) feeds a layer with a halo, it pushes the
+halo instead (sscnn_conv_fwd_push / sscnn_conv_bwd_push): its epilogue writes
+its edge columns straight into the neighbours' halo buffers, and the
+consumer's gather is skipped.  Each shard writes the
 partial weight / bias gradients of every layer into one bucket of its own,
 and one reduction over the shards' buckets at the end of backward turns them
 into the replicated gradients (the bucketed gradient all-reduce of
@@ -66,8 +70,9 @@ class ShardedStack:
     stream, so the caching allocator never hands a buffer still in use on it
     to work on another stream."""
 
-    def __init__(self, layers, num_shards: int, weights, biases, device="cuda", stream=None):
+    def __init__(self, layers, num_shards: int, weights, biases, device="cuda", stream=None, push=True):
         self.layers = list(layers)
+        self.push = push
         self.S = num_shards
         self.device = device
         self.stream = stream
@@ -93,6 +98,31 @@ class ShardedStack:
     def _nbrs(self, lst, s):
         return (lst[s - 1] if s > 0 else None), (lst[s + 1] if s < self.S - 1 else None)
 
+    @staticmethod
+    def _patchify(L):
+        return L.k == L.stride and L.pad == 0 and L.groups == 1
+
+    def pushes_forward(self, l):
+        """Does layer l's forward push layer l+1's input halo?"""
+        if not self.push or l + 1 >= len(self.layers) or not self._patchify(self.layers[l]):
+            return False
+        c = self._convs(self.layers[l + 1])[0]
+        return c.halo_l + c.halo_r > 0
+
+    def pushes_backward(self, l):
+        """Does layer l's backward push layer l-1's grad_output halo?"""
+        if not self.push or l == 0 or not self._patchify(self.layers[l]):
+            return False
+        c = self._convs(self.layers[l - 1])[0]
+        return c.ghalo_l + c.ghalo_r > 0
+
+    def _halos(self, convs, which):
+        return [torch.empty(c.halo_shape(which), device=self.device) for c in convs]
+
+    def _push(self, nconvs, which, halos, s):
+        left, right = self._nbrs(halos, s)
+        return sscnn.make_push(nconvs[s], which, left, right, halos[s])
+
     def forward(self, x_slices):
         """x_slices: per shard (N, 3, H, W/S) device tensors.  Returns the last
         layer's per-shard outputs."""
@@ -101,18 +131,30 @@ class ShardedStack:
 
     def _forward(self, x_slices):
         cur = list(x_slices)
+        pushed = None                      # this layer's input halos, pushed by the layer before
         for l, L in enumerate(self.layers):
             convs = self._convs(L)
             c0 = convs[0]
             st = LayerState(convs=convs, x=cur, x_halo=[], y=[])
-            for s, c in enumerate(convs):
-                h = torch.empty(c.halo_shape(sscnn.HALO_INPUT), device=self.device)
-                left, right = self._nbrs(cur, s)
-                sscnn.halo_gather(c, sscnn.HALO_INPUT, left, right, h, self.stream)
-                st.x_halo.append(h)
+            if pushed is not None:
+                st.x_halo = pushed
+            else:
+                for s, c in enumerate(convs):
+                    h = torch.empty(c.halo_shape(sscnn.HALO_INPUT), device=self.device)
+                    left, right = self._nbrs(cur, s)
+                    sscnn.halo_gather(c, sscnn.HALO_INPUT, left, right, h, self.stream)
+                    st.x_halo.append(h)
+            pushed = None
+            if self.pushes_forward(l):
+                nconvs = self._convs(self.layers[l + 1])
+                pushed = self._halos(nconvs, sscnn.HALO_INPUT)
             for s, c in enumerate(convs):
                 y = torch.empty(c0.y_shape, device=self.device)
-                sscnn.conv_fwd(c, cur[s], st.x_halo[s], self.w[l], self.b[l], y, self.stream)
+                if pushed is not None:
+                    sscnn.conv_fwd_push(c, cur[s], st.x_halo[s], self.w[l], self.b[l], y,
+                                        self._push(nconvs, sscnn.HALO_INPUT, pushed, s), self.stream)
+                else:
+                    sscnn.conv_fwd(c, cur[s], st.x_halo[s], self.w[l], self.b[l], y, self.stream)
                 st.y.append(y)
             self.state[l] = st
             cur = st.y
@@ -132,16 +174,24 @@ class ShardedStack:
             # zeroed once: the padding between pieces stays zero through the reductions
             self.buckets = [torch.zeros(total, device=self.device) for _ in range(self.S)]
             self.reduced = torch.zeros(total, device=self.device)
+        pushed = None                      # this layer's grad_output halos, pushed by the layer above
         for l in range(len(self.layers) - 1, -1, -1):
             st = self.state[l]
             convs = st.convs
             c0 = convs[0]
             st.g, st.g_halo, st.dx, st.gw_parts, st.gb_parts = cur, [], [], [], []
-            for s, c in enumerate(convs):
-                h = torch.empty(c.halo_shape(sscnn.HALO_GRAD_OUTPUT), device=self.device)
-                left, right = self._nbrs(cur, s)
-                sscnn.halo_gather(c, sscnn.HALO_GRAD_OUTPUT, left, right, h, self.stream)
-                st.g_halo.append(h)
+            if pushed is not None:
+                st.g_halo = pushed
+            else:
+                for s, c in enumerate(convs):
+                    h = torch.empty(c.halo_shape(sscnn.HALO_GRAD_OUTPUT), device=self.device)
+                    left, right = self._nbrs(cur, s)
+                    sscnn.halo_gather(c, sscnn.HALO_GRAD_OUTPUT, left, right, h, self.stream)
+                    st.g_halo.append(h)
+            pushed = None
+            if self.pushes_backward(l):
+                pconvs = self.state[l - 1].convs
+                pushed = self._halos(pconvs, sscnn.HALO_GRAD_OUTPUT)
             ws = sscnn.new_workspace(c0, self.device)
             ow, ob, nw, nb = offs[l]
             for s, c in enumerate(convs):
@@ -149,8 +199,13 @@ class ShardedStack:
                 if l > 0 or need_input_grad:
                     # grad_input and the weight / bias partials in one call
                     dx = torch.empty(c0.x_shape, device=self.device)
-                    sscnn.conv_bwd(c, st.x[s], st.x_halo[s], cur[s], st.g_halo[s], self.w[l], dx, gw, gb, ws,
-                                   self.stream)
+                    if pushed is not None:
+                        sscnn.conv_bwd_push(c, st.x[s], st.x_halo[s], cur[s], st.g_halo[s], self.w[l], dx, gw, gb,
+                                            self._push(pconvs, sscnn.HALO_GRAD_OUTPUT, pushed, s), ws,
+                                            self.stream)
+                    else:
+                        sscnn.conv_bwd(c, st.x[s], st.x_halo[s], cur[s], st.g_halo[s], self.w[l], dx, gw, gb, ws,
+                                       self.stream)
                     st.dx.append(dx)
                 else:
                     sscnn.conv_bwd_weight_partial(c, st.x[s], st.x_halo[s], cur[s], gw, gb, ws, self.stream)

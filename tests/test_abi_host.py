@@ -438,3 +438,29 @@ def test_stream_copy_validation():
     assert L.sscnn_stream_copy(FAKE + 4, FAKE + 4096, 16, None) == sscnn.EINVAL   # misaligned
     assert L.sscnn_stream_copy(FAKE, FAKE + 32, 16, None) == sscnn.EINVAL         # overlapping
     assert "overlap" in sscnn.last_error()
+
+
+def test_push_validation():
+    L = sscnn.lib()
+    F = FAKE
+    first, mid, last = (sscnn.conv_init(1, 16, 32, 16, 32, 2, 2, 0, 1, s, 4) for s in (0, 1, 3))
+    args = (F, None, F + 4096, F + 8192, F + 12288)            # x, x_halo, weight, bias, y
+    P = sscnn.Push
+    # the neighbour pointers must match the shard's position
+    assert L.sscnn_conv_fwd_push(ctypes.byref(mid), *args, ctypes.byref(P(3, 3, None, F + 16384, None)), None) \
+        == sscnn.EINVAL
+    assert L.sscnn_conv_fwd_push(ctypes.byref(first), *args, ctypes.byref(P(3, 3, F + 16384, F + 20480, F)), None) \
+        == sscnn.EINVAL
+    # an edge shard needs its own halo for the open side
+    assert L.sscnn_conv_fwd_push(ctypes.byref(last), *args, ctypes.byref(P(3, 3, F + 16384, None, None)), None) \
+        == sscnn.EINVAL
+    # widths beyond the pushed slice (16 output columns)
+    assert L.sscnn_conv_fwd_push(ctypes.byref(mid), *args, ctypes.byref(P(17, 3, F + 16384, F + 20480, None)),
+                                 None) == sscnn.EINVAL
+    # a halo buffer aliasing the output
+    assert L.sscnn_conv_fwd_push(ctypes.byref(mid), *args, ctypes.byref(P(3, 3, F + 12288, F + 20480, None)),
+                                 None) == sscnn.EINVAL
+    assert "alias" in sscnn.last_error()
+    # negative widths
+    assert L.sscnn_conv_fwd_push(ctypes.byref(mid), *args, ctypes.byref(P(-1, 3, F + 16384, F + 20480, None)),
+                                 None) == sscnn.EINVAL

@@ -40,15 +40,17 @@ def _oracle_layers(wl, T):
             for l, L in enumerate(wl.layers)]
 
 
-def test_reduced_convnext_stack_all_layers_vs_oracle():
+@pytest.mark.parametrize("push", [True, False], ids=["push_halos", "gather_halos"])
+def test_reduced_convnext_stack_all_layers_vs_oracle(push):
     """Stem -> dw -> ds -> dw -> ds -> dw -> ds -> dw on a (1,3,256,1024) input
-    split four ways, channels 32/64/128/256."""
+    split four ways, channels 32/64/128/256; the depthwise layers' halos
+    pushed by the layers before them, or gathered by the layers themselves."""
     layers = workloads.convnext_stack(1, 1024, h=256, dims=(32, 64, 128, 256))
     wl = workloads.stack("convnext_reduced", layers, num_shards=4, seed=2001)
     T = workloads.generate(wl)
     S = wl.num_shards
-    _say(f"  reduced stack: input {wl.x_shape}, S={S}")
-    st = sstack.ShardedStack(wl.layers, S, T.weights, T.biases)
+    _say(f"  reduced stack: input {wl.x_shape}, S={S}, push={push}")
+    st = sstack.ShardedStack(wl.layers, S, T.weights, T.biases, push=push)
     st.forward(slices(T.x, S))
     st.backward(slices(T.g, S))
     torch.cuda.synchronize()
