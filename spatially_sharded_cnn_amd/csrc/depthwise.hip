@@ -40,6 +40,7 @@
 //    returns together).
 #include "internal.h"
 #include "depthwise.h"
+#include "lds_dma.h"
 #include "wavesum.h"
 
 namespace sscnn {
@@ -130,40 +131,6 @@ __device__ __forceinline__ TileIdx decode_channel_major(const DwArgs& a, int t, 
     d.c = t / a.N;
     place(d, a, trow, tcol, th, tw);
     return d;
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer resource of a plane (stride 0, num_records = bytes): loads at
-// offsets outside [0, bytes) return zeros.  Wave-uniform, in scalar registers.
-__device__ __forceinline__ i32x4 plane_rsrc(const float* base, int bytes)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    i32x4 r;
-    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
-    r.z = __builtin_amdgcn_readfirstlane(bytes);
-    r.w = 0x00020000;
-    return r;
-}
-
-// 16 bytes per lane from the buffer at byte offset voff straight into LDS at
-// lds + 16 * lane (lds wave-uniform).  Issued as inline assembly so that the
-// compiler does not treat every later LDS read as depending on it (it would
-// wait for all outstanding loads first); the kernels wait for these loads
-// themselves with s_waitcnt vmcnt(0) before the barrier that publishes a tile.
-// s_nop: one wait state between writing M0 and the load that reads it.
-__device__ __forceinline__ void dma16(const i32x4& rs, const float* lds, int voff)
-{
-    const int l = __builtin_amdgcn_readfirstlane((int)(uint32_t)reinterpret_cast<uintptr_t>(lds));
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                 :: "v"(voff), "s"(l), "s"(rs) : "memory", "m0");
-}
-
-__device__ __forceinline__ void wait_vmem()
-{
-    // gfx9 s_waitcnt: vmcnt = 0, expcnt[6:4] = 7 and lgkmcnt[11:8] = 15 (no wait on those)
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
 // The extended input of one tile in LDS, for a 256-thread group (TX x TY

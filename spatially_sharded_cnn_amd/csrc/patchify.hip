@@ -33,9 +33,13 @@
 // count; grad_bias fused into the first column tile).  Each split writes one
 // slab of partials, and the slabs are summed in split order, in two
 // fixed-order stages when there are many: no atomics, bitwise reproducible.
+#include <cstdlib>
+#include <cstring>
+
 #include "internal.h"
 #include "patchify.h"
 #include "gelu.h"
+#include "lds_dma.h"
 
 namespace sscnn {
 namespace {
@@ -499,6 +503,135 @@ patch_kernel(PArgs a)
         a.out[outer * slab_floats(a) + (int64_t)a.Co * a.Kt + m0 + threadIdx.x] = bias_acc;
 }
 
+// Forward of a 2x2/2 layer in wide tiles.  The product runs over the pixels
+// of all the images at once, in result tiles of 128 output channels x 224
+// pixels (7 MFMA blocks of 32) that may straddle two images: the
+// ConvNeXt-style stack's downsamples have 7 x 2^j output pixels per channel,
+// so 224-pixel tiles divide them into a whole multiple of the CU count, where
+// 128-pixel tiles per image leave the last round of workgroups partly empty.
+// Wave w computes rows 32 w .. 32 w + 31 of the tile against all 7 pixel
+// blocks.  A stage is 4 input channels (16 reduction rows), loaded from HBM
+// straight into LDS (buffer_load ... lds, no registers) one stage ahead:
+//   A  W[m0 + m][(4 c .. 4 c + 3) + 16 s]: 16-byte units, unit (m, c) at
+//      slot m * 4 + (c ^ ((m >> 2) & 3)) (the swizzle spreads a wave's reads
+//      of one c over the banks);
+//   B  per (c, kh), the input rows 2 i + kh of the tile's pixels as they lie
+//      in memory: pixel n's two columns kw at 2 n + kw of a 512-float segment.
+// MFMA step (c, kh) pairs k-slot 0 with kw = 0 and k-slot 1 with kw = 1, so
+// the B operand of lane (hi, n) is segment word 2 n + hi (64 consecutive
+// words per wave) and the A operand is word 2 kh + hi of unit (m, c).
+constexpr int kWideTM = 128, kWideNB = 7, kWideTN = 32 * kWideNB, kWideSeg = 512;
+constexpr int kWideAF = kWideTM * 16, kWideBF = 8 * kWideSeg, kWideST = kWideAF + kWideBF;
+constexpr int kWideLoads = 6;      // LDS-direct loads per wave and stage: 2 for A, 4 for B
+
+__global__ void __launch_bounds__(kNT, 3)
+wide_fwd_kernel(PArgs a, int ntot)
+{
+    __shared__ __align__(16) float lds[2 * kWideST];
+    __shared__ float bias_s[kWideTM];
+    const int bid = xcd_order(blockIdx.x, gridDim.x);   // output-channel tiles of one pixel tile side by side
+    const int mt = bid % a.tiles_m, nt = bid / a.tiles_m;
+    const int m0 = mt * kWideTM, n0 = nt * kWideTN;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    if (t < kWideTM) bias_s[t] = (a.b && m0 + t < a.Co) ? a.b[m0 + t] : 0.f;
+    const int nstage = a.Ci / 4;
+
+    // A: instruction i of wave w covers LDS units 64 (2 w + i) + lane
+    const i32x4 ra = plane_rsrc(a.w, a.Co * a.Kt * 4);
+    int avoff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int m = 16 * (2 * wave + i) + lane / 4;
+        const int c = (lane & 3) ^ ((m >> 2) & 3);
+        avoff[i] = ((m0 + m) * a.Kt + 4 * c) * 4;
+    }
+    // B: wave w loads channel 4 s + w, rows kh = 0, 1, in two halves of 64 units (pixel pairs);
+    // pixels past the tile or past the last image read as zeros
+    const i32x4 rb = plane_rsrc(a.x, a.N * a.Ci * a.H * a.W * 4);
+    int bvoff[2][2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const int n = 2 * (64 * hf + lane);
+        const int gp = n0 + n;
+        const int img = gp / a.P, pl = gp - img * a.P;
+        const int i = pl / a.Wo, j = pl - i * a.Wo;
+        const bool ok = n < kWideTN && gp < ntot;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+            bvoff[hf][kh] = ok ? (((img * a.Ci + wave) * a.H + 2 * i + kh) * a.W + 2 * j) * 4 : (int)0x80000000;
+    }
+    const int a_step = 64, b_step = 4 * a.H * a.W * 4;
+    auto issue = [&](int s) {
+        float* st = lds + (s & 1) * kWideST;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma16(ra, st + (2 * wave + i) * 256, avoff[i] + s * a_step);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                dma16(rb, st + kWideAF + (2 * wave + kh) * kWideSeg + 256 * hf, bvoff[hf][kh] + s * b_step);
+    };
+
+    const int hi = lane >> 5, l32 = lane & 31;
+    f32x16 acc[kWideNB];
+#pragma unroll
+    for (int b = 0; b < kWideNB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+    const int sw = (l32 >> 2) & 3;
+    const int arow = (32 * wave + l32) * 4;
+    const int boff = kWideAF + 2 * l32 + hi;
+
+    issue(0);
+    for (int s = 0; s < nstage; ++s) {
+        // stage s has landed (this wave's loads, then everyone's); the other buffer is free
+        wait_vmem();
+        lds_barrier();
+        if (s + 1 < nstage) issue(s + 1);
+        const float* st = lds + (s & 1) * kWideST;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int ao = (arow + (c ^ sw)) * 4 + hi;
+            const float a0 = st[ao], a1 = st[ao + 2];
+            float b0[kWideNB], b1[kWideNB];
+#pragma unroll
+            for (int yb = 0; yb < kWideNB; ++yb) {
+                b0[yb] = st[boff + (2 * c) * kWideSeg + 64 * yb];
+                b1[yb] = st[boff + (2 * c + 1) * kWideSeg + 64 * yb];
+            }
+#pragma unroll
+            for (int yb = 0; yb < kWideNB; ++yb)
+                acc[yb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0[yb], acc[yb], 0, 0, 0);
+#pragma unroll
+            for (int yb = 0; yb < kWideNB; ++yb)
+                acc[yb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1[yb], acc[yb], 0, 0, 0);
+        }
+    }
+
+    // D block yb: register 4 q + r holds row 8 q + 4 hi + r of the wave's 32, column l32
+    const int pmax = a.ph_l > a.ph_r ? a.ph_l : a.ph_r;
+#pragma unroll
+    for (int yb = 0; yb < kWideNB; ++yb) {
+        const int gp = n0 + 32 * yb + l32;
+        if (gp >= ntot) continue;
+        const int img = gp / a.P, pl = gp - img * a.P;
+        const int pi = pl / a.Wo, pj = pl - pi * a.Wo;
+        const bool edge = pushes(a) && (pj < pmax || pj >= a.Wo - pmax);
+        float* yp = a.out + (int64_t)img * a.Co * a.P + pl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + 32 * wave + 8 * q + 4 * hi + r;
+                if (row < a.Co) {
+                    const float v = acc[yb][4 * q + r] + bias_s[row - m0];
+                    yp[(int64_t)row * a.P] = v;
+                    if (edge) push_value(a, (int64_t)img * a.Co + row, a.Ho, pi, pj, a.Wo, v);
+                }
+            }
+    }
+}
+
 // dst[grp][e] = sum of src[k][e] over the slabs k of group grp (slabs
 // [grp * per, min(n, (grp + 1) * per))), added in slab order, in float4
 // units.  The loads of 8 slabs are issued before their adds so that they are
@@ -651,6 +784,32 @@ static void set_push(PArgs& a, const Push* push)
     a.ph_r = push->hr;
 }
 
+// Wide forward tiles (wide_fwd_kernel): 2x2/2 layers whose operands fit
+// 32-bit byte offsets, when the tile count is a whole multiple of the CU
+// count (the 7 x 2^j-pixel downsamples of the stack) -- elsewhere the
+// per-image tiles balance as well or better.  SSCNN_PATCH_FWD=wide forces
+// them wherever they apply, =tiled never.
+static int wide_fwd_tiles(const PArgs& a)
+{
+    const int64_t ntot = (int64_t)a.N * a.P;
+    if (a.Kt != 4 * a.Ci || a.Ci % 4 || (int64_t)a.N * a.Ci * a.H * a.W * 4 >= ((int64_t)1 << 31) ||
+        (int64_t)(a.Co + kWideTM) * a.Kt * 4 >= ((int64_t)1 << 31) || ntot >= ((int64_t)1 << 31))
+        return 0;
+    return (int)(((a.Co + kWideTM - 1) / kWideTM) * ((ntot + kWideTN - 1) / kWideTN));
+}
+
+static bool use_wide_fwd(const PArgs& a)
+{
+    const int tiles = wide_fwd_tiles(a);
+    if (tiles == 0) return false;
+    const char* env = getenv("SSCNN_PATCH_FWD");
+    if (env && !strcmp(env, "wide")) return true;
+    if (env && !strcmp(env, "tiled")) return false;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return cus > 0 && tiles % cus == 0;
+}
+
 hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const float* b, float* y,
                             hipStream_t st, float* act, const Push* push)
 {
@@ -658,6 +817,12 @@ hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const
     PArgs a = make_args(g);
     a.x = x; a.w = w; a.b = b; a.out = y; a.act = act;
     set_push(a, push);
+    if (g.k == 2 && use_wide_fwd(a)) {
+        a.tiles_m = (a.Co + kWideTM - 1) / kWideTM;
+        const int grid = wide_fwd_tiles(a);
+        hipLaunchKernelGGL(wide_fwd_kernel, dim3(grid), dim3(kNT), 0, st, a, a.N * a.P);
+        return hipGetLastError();
+    }
     a.tiles_n = (a.P + 127) / 128;
     return launch_rows<FWD>(a, a.Co, row_tile(a.Co, a, false), g.k, st);
 }

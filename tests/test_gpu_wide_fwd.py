@@ -1,0 +1,95 @@
+"""GPU parity of the wide-tile forward of 2x2/2 layers (needs an MI355X).
+
+The forward of a k = s = 2 layer can run as one product over the pixels of
+all the images, in tiles of 128 output channels x 224 pixels that may
+straddle two images.  The library picks it when the tile count is a whole
+multiple of the CU count (the ConvNeXt-style stack's downsamples);
+SSCNN_PATCH_FWD=wide forces it wherever it applies and =tiled switches it
+off, so these cases run both forms on shapes chosen for their edges:
+output channels that are not a multiple of 128, pixel counts that are not a
+multiple of 224, tiles that straddle images, a single image, and the push
+form of the next layer's halo exchange.  Every shard's output is compared
+with the oracle (1e-5 normwise), the two forms with each other, and the
+pushed halos bit for bit with sscnn_halo_gather of the outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from shard_harness import TOL_FWD, assert_close, host, slices, to_dev
+from spatially_sharded_cnn_amd import sscnn
+
+pytestmark = pytest.mark.gpu
+
+# (name, n, ci, co, h, w, shards)
+CASES = [
+    ("co80_ragged_pixels", 3, 8, 80, 20, 2 * 32, 2),          # 160 pixels per image and shard: tiles straddle images
+    ("co144_one_image", 1, 16, 144, 24, 4 * 32, 4),            # two channel tiles, the second 16 rows
+    ("co256_ci64", 2, 64, 256, 28, 2 * 64, 2),                 # 16 reduction stages, 448 pixels per image
+    ("co512_ci256_many_tiles", 7, 256, 512, 16, 4 * 64, 4),    # the stack's shape class, 7 images
+]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _fwd(monkeypatch, mode, conv, x, wd, bd, push=None):
+    monkeypatch.setenv("SSCNN_PATCH_FWD", mode)
+    y = torch.empty(conv.y_shape, device="cuda")
+    if push is None:
+        sscnn.conv_fwd(conv, x, None, wd, bd, y)
+    else:
+        sscnn.conv_fwd_push(conv, x, None, wd, bd, y, push)
+    return y
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_wide_forward_matches_oracle_and_tiled(case, monkeypatch):
+    name, n, ci, co, h, w, S = case
+    _say(f"  wide fwd {name}: ({n},{ci},{h},{w}) -> {co} channels, {S} shards")
+    rng = np.random.default_rng(4700 + CASES.index(case))
+    x = rng.standard_normal((n, ci, h, w)).astype(np.float32)
+    wt = (rng.standard_normal((co, ci, 2, 2)) * 0.05).astype(np.float32)
+    b = (rng.standard_normal(co) * 0.1).astype(np.float32)
+    xs = slices(x, S)
+    wd, bd = to_dev(wt), to_dev(b)
+    convs = [sscnn.conv_init(n, ci, co, h, w // S, 2, 2, 0, 1, s, S) for s in range(S)]
+    # the consumer of the outputs: a depthwise 7x7 pad 3, whose input halo the push form fills
+    cons = [sscnn.conv_init(n, co, co, h // 2, w // 2 // S, 7, 1, 3, co, s, S) for s in range(S)]
+    y_full = oracle.conv_fwd(x, wt, b, 2, 0, 1)
+    wol = w // 2 // S
+    ys_wide, halos = [], [torch.full(c.halo_shape(sscnn.HALO_INPUT), float("nan"), device="cuda") for c in cons]
+    nb = lambda lst, s: (lst[s - 1] if s > 0 else None, lst[s + 1] if s < S - 1 else None)
+    for s in range(S):
+        y_wide = _fwd(monkeypatch, "wide", convs[s], xs[s], wd, bd)
+        y_tiled = _fwd(monkeypatch, "tiled", convs[s], xs[s], wd, bd)
+        p = sscnn.make_push(cons[s], sscnn.HALO_INPUT, *nb(halos, s), halos[s])
+        y_push = _fwd(monkeypatch, "wide", convs[s], xs[s], wd, bd, push=p)
+        torch.cuda.synchronize()
+        ref = y_full[:, :, :, s * wol:(s + 1) * wol]
+        assert_close(host(y_wide), ref, TOL_FWD, f"{name} shard {s}: wide forward vs oracle")
+        assert_close(host(y_tiled), ref, TOL_FWD, f"{name} shard {s}: tiled forward vs oracle")
+        assert_close(host(y_wide), host(y_tiled), TOL_FWD, f"{name} shard {s}: wide vs tiled")
+        assert torch.equal(y_push, y_wide), f"{name} shard {s}: pushing changed the wide forward's output"
+        ys_wide.append(y_wide)
+    for s in range(S):
+        gathered = torch.empty(cons[s].halo_shape(sscnn.HALO_INPUT), device="cuda")
+        sscnn.halo_gather(cons[s], sscnn.HALO_INPUT, *nb(ys_wide, s), gathered)
+        torch.cuda.synchronize()
+        assert torch.equal(halos[s], gathered), f"{name} shard {s}: pushed halo != gathered halo"
+
+
+def test_wide_forward_is_reproducible(monkeypatch):
+    """Two runs of the wide forward give the same bits (fixed reduction order, no atomics)."""
+    rng = np.random.default_rng(4750)
+    n, ci, co, h, w = 2, 32, 128, 16, 128
+    x = to_dev(rng.standard_normal((n, ci, h, w)).astype(np.float32))
+    wd = to_dev((rng.standard_normal((co, ci, 2, 2)) * 0.05).astype(np.float32))
+    bd = to_dev((rng.standard_normal(co) * 0.1).astype(np.float32))
+    c = sscnn.conv_init(n, ci, co, h, w, 2, 2, 0, 1, 0, 1)
+    a = _fwd(monkeypatch, "wide", c, x, wd, bd)
+    b2 = _fwd(monkeypatch, "wide", c, x, wd, bd)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b2)
