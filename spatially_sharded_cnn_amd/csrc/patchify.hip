@@ -632,6 +632,122 @@ wide_fwd_kernel(PArgs a, int ntot)
     }
 }
 
+// grad_input of a 2x2/2 layer in wide tiles: dXp[K][p] = sum_co W[co][K]
+// G[co][p] over the pixels of all the images, result tiles of 128 rows of
+// K = (ci, kh, kw) x 224 pixels, 16 output channels (reduction rows) per
+// stage, loaded straight into LDS one stage ahead.  Both operands are rows of
+// memory that are contiguous along the tile's own index (W rows along K,
+// grad_output rows along the pixels), so LDS holds them k-major:
+//   A  16 rows of 128 floats, W[k0 + kr][m0 .. m0 + 127];
+//   B  16 rows of 256 floats, G[co = k0 + kr][the tile's 224 pixels] (the
+//      last 32 floats zero);
+// 16-byte unit u of row kr sits at slot u ^ (8 (kr >> 3 & 1)).  MFMA step t
+// pairs k-slot 0 with row t and k-slot 1 with row t + 8, whose slots the
+// swizzle puts 32 banks apart, so a wave's 64 reads of one step never share a
+// bank.  The result's rows come in groups of 4 = (kh, kw) of one input
+// channel: each lane scatters two 2-float runs back to NCHW.
+constexpr int kWiBF = 16 * 256, kWiAF = 16 * kWideTM, kWiST = kWiAF + kWiBF;
+
+__global__ void __launch_bounds__(kNT, 3)
+wide_bwi_kernel(PArgs a, int ntot)
+{
+    __shared__ __align__(16) float lds[2 * kWiST];
+    const int bid = xcd_order(blockIdx.x, gridDim.x);   // K tiles of one pixel tile side by side
+    const int mt = bid % a.tiles_m, nt = bid / a.tiles_m;
+    const int m0 = mt * kWideTM, n0 = nt * kWideTN;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int nstage = a.Co / 16;
+
+    // A: instruction i of wave w fills rows kr = 2 (2 w + i) + lane / 32; lane's slot lane % 32
+    const i32x4 ra = plane_rsrc(a.w, a.Co * a.Kt * 4);
+    int avoff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int kr = 2 * (2 * wave + i) + lane / 32;
+        const int u = (lane & 31) ^ (8 * ((kr >> 3) & 1));
+        const int m = m0 + 4 * u;
+        avoff[i] = m < a.Kt ? (kr * a.Kt + m) * 4 : (int)0x80000000;
+    }
+    // B: wave w fills rows kr = 4 w .. 4 w + 3, one instruction each; lane's slot lane
+    const i32x4 rb = plane_rsrc(a.g, a.N * a.Co * a.P * 4);
+    int bvoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int kr = 4 * wave + i;
+        const int n = 4 * (lane ^ (8 * ((kr >> 3) & 1)));
+        const int gp = n0 + n;
+        const int img = gp / a.P, pl = gp - img * a.P;
+        bvoff[i] = (n < kWideTN && gp < ntot) ? (((img * a.Co) + kr) * a.P + pl) * 4 : (int)0x80000000;
+    }
+    const int a_step = 16 * a.Kt * 4, b_step = 16 * a.P * 4;
+    auto issue = [&](int s) {
+        float* st = lds + (s & 1) * kWiST;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma16(ra, st + (2 * wave + i) * 256, avoff[i] + s * a_step);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(rb, st + kWiAF + (4 * wave + i) * 256, bvoff[i] + s * b_step);
+    };
+
+    const int hi = lane >> 5, l32 = lane & 31;
+    f32x16 acc[kWideNB];
+#pragma unroll
+    for (int b = 0; b < kWideNB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+    // lane's A word in row t + 8 hi: m = 32 w + l32 at slot (m >> 2) ^ 8 hi; its B word for pixel
+    // block yb: n = 32 yb + l32 at slot (n >> 2) ^ 8 hi, i.e. word 32 (yb ^ hi) + l32
+    const int aw = 4 * (((32 * wave + l32) >> 2) ^ (8 * hi)) + (l32 & 3) + 8 * hi * 128;
+    int bw[kWideNB];
+#pragma unroll
+    for (int yb = 0; yb < kWideNB; ++yb) bw[yb] = kWiAF + 8 * hi * 256 + 32 * (yb ^ hi) + l32;
+
+    issue(0);
+    for (int s = 0; s < nstage; ++s) {
+        wait_vmem();
+        lds_barrier();
+        if (s + 1 < nstage) issue(s + 1);
+        const float* st = lds + (s & 1) * kWiST;
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+            const float av = st[aw + tt * 128];
+            float bv[kWideNB];
+#pragma unroll
+            for (int yb = 0; yb < kWideNB; ++yb) bv[yb] = st[bw[yb] + tt * 256];
+#pragma unroll
+            for (int yb = 0; yb < kWideNB; ++yb)
+                acc[yb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv[yb], acc[yb], 0, 0, 0);
+        }
+    }
+
+    // D block yb: register 4 q + r holds K row 32 w + 8 q + 4 hi + r, pixel column l32;
+    // K = 4 ci + 2 kh + kw, so registers 4 q .. 4 q + 3 are (kh, kw) of one input channel
+    const int pmax = a.ph_l > a.ph_r ? a.ph_l : a.ph_r;
+#pragma unroll
+    for (int yb = 0; yb < kWideNB; ++yb) {
+        const int gp = n0 + 32 * yb + l32;
+        if (gp >= ntot) continue;
+        const int img = gp / a.P, pl = gp - img * a.P;
+        const int i = pl / a.Wo, j = pl - i * a.Wo;
+        const bool edge = pushes(a) && (2 * j < pmax || 2 * j + 1 >= a.W - pmax);
+        float* dxi = a.out + (int64_t)img * a.Ci * a.H * a.W;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = m0 + 32 * wave + 8 * q + 4 * hi;
+            if (row >= a.Kt) continue;
+            const int ci = row / 4;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const float v0 = acc[yb][4 * q + 2 * kh], v1 = acc[yb][4 * q + 2 * kh + 1];
+                *reinterpret_cast<float2*>(dxi + ((int64_t)ci * a.H + 2 * i + kh) * a.W + 2 * j) = make_float2(v0, v1);
+                if (edge) {
+                    push_value(a, (int64_t)img * a.Ci + ci, a.H, 2 * i + kh, 2 * j, a.W, v0);
+                    push_value(a, (int64_t)img * a.Ci + ci, a.H, 2 * i + kh, 2 * j + 1, a.W, v1);
+                }
+            }
+        }
+    }
+}
+
 // dst[grp][e] = sum of src[k][e] over the slabs k of group grp (slabs
 // [grp * per, min(n, (grp + 1) * per))), added in slab order, in float4
 // units.  The loads of 8 slabs are issued before their adds so that they are
@@ -787,8 +903,9 @@ static void set_push(PArgs& a, const Push* push)
 // Wide forward tiles (wide_fwd_kernel): 2x2/2 layers whose operands fit
 // 32-bit byte offsets, when the tile count is a whole multiple of the CU
 // count (the 7 x 2^j-pixel downsamples of the stack) -- elsewhere the
-// per-image tiles balance as well or better.  SSCNN_PATCH_FWD=wide forces
-// them wherever they apply, =tiled never.
+// per-image tiles balance as well or better.  The environment variable
+// (SSCNN_PATCH_FWD for the forward) set to wide forces them wherever they
+// apply, set to tiled never.
 static int wide_fwd_tiles(const PArgs& a)
 {
     const int64_t ntot = (int64_t)a.N * a.P;
@@ -798,11 +915,10 @@ static int wide_fwd_tiles(const PArgs& a)
     return (int)(((a.Co + kWideTM - 1) / kWideTM) * ((ntot + kWideTN - 1) / kWideTN));
 }
 
-static bool use_wide_fwd(const PArgs& a)
+static bool use_wide(int tiles, const char* var)
 {
-    const int tiles = wide_fwd_tiles(a);
     if (tiles == 0) return false;
-    const char* env = getenv("SSCNN_PATCH_FWD");
+    const char* env = getenv(var);
     if (env && !strcmp(env, "wide")) return true;
     if (env && !strcmp(env, "tiled")) return false;
     int dev = 0, cus = 256;
@@ -817,7 +933,7 @@ hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const
     PArgs a = make_args(g);
     a.x = x; a.w = w; a.b = b; a.out = y; a.act = act;
     set_push(a, push);
-    if (g.k == 2 && use_wide_fwd(a)) {
+    if (g.k == 2 && use_wide(wide_fwd_tiles(a), "SSCNN_PATCH_FWD")) {
         a.tiles_m = (a.Co + kWideTM - 1) / kWideTM;
         const int grid = wide_fwd_tiles(a);
         hipLaunchKernelGGL(wide_fwd_kernel, dim3(grid), dim3(kNT), 0, st, a, a.N * a.P);
@@ -827,6 +943,19 @@ hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const
     return launch_rows<FWD>(a, a.Co, row_tile(a.Co, a, false), g.k, st);
 }
 
+// Wide grad_input tiles (wide_bwi_kernel), chosen like the forward's: 2x2/2
+// layers whose operands fit 32-bit byte offsets, when the tile count is a
+// whole multiple of the CU count; SSCNN_PATCH_BWI=wide / =tiled force the
+// choice.
+static int wide_bwi_tiles(const PArgs& a)
+{
+    const int64_t ntot = (int64_t)a.N * a.P;
+    if (a.Kt != 4 * a.Ci || a.Co % 16 || (int64_t)a.N * a.Co * a.P * 4 >= ((int64_t)1 << 31) ||
+        (int64_t)a.Co * a.Kt * 4 >= ((int64_t)1 << 31) || (int64_t)a.N * a.Ci * a.H * a.W >= ((int64_t)1 << 31))
+        return 0;
+    return (int)(((a.Kt + kWideTM - 1) / kWideTM) * ((ntot + kWideTN - 1) / kWideTN));
+}
+
 hipError_t launch_patch_bwd_input(const Geom& g, const float* gy, const float* w, float* gx, hipStream_t st,
                                   const float* pre, const Push* push)
 {
@@ -834,6 +963,11 @@ hipError_t launch_patch_bwd_input(const Geom& g, const float* gy, const float* w
     PArgs a = make_args(g);
     a.g = gy; a.w = w; a.out = gx; a.pre = pre;
     set_push(a, push);
+    if (g.k == 2 && use_wide(wide_bwi_tiles(a), "SSCNN_PATCH_BWI")) {
+        a.tiles_m = (a.Kt + kWideTM - 1) / kWideTM;
+        hipLaunchKernelGGL(wide_bwi_kernel, dim3(wide_bwi_tiles(a)), dim3(kNT), 0, st, a, a.N * a.P);
+        return hipGetLastError();
+    }
     a.tiles_n = (a.P + 127) / 128;
     return launch_rows<BWI>(a, a.Kt, row_tile(a.Kt, a, a.Kt <= kNarrowK), g.k, st);
 }

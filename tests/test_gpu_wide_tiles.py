@@ -1,23 +1,25 @@
-"""GPU parity of the wide-tile forward of 2x2/2 layers (needs an MI355X).
+"""GPU parity of the wide-tile forward and grad_input of 2x2/2 layers (needs
+an MI355X).
 
-The forward of a k = s = 2 layer can run as one product over the pixels of
-all the images, in tiles of 128 output channels x 224 pixels that may
-straddle two images.  The library picks it when the tile count is a whole
-multiple of the CU count (the ConvNeXt-style stack's downsamples);
-SSCNN_PATCH_FWD=wide forces it wherever it applies and =tiled switches it
-off, so these cases run both forms on shapes chosen for their edges:
-output channels that are not a multiple of 128, pixel counts that are not a
-multiple of 224, tiles that straddle images, a single image, and the push
-form of the next layer's halo exchange.  Every shard's output is compared
-with the oracle (1e-5 normwise), the two forms with each other, and the
-pushed halos bit for bit with sscnn_halo_gather of the outputs.
+The forward and the grad_input of a k = s = 2 layer can run as one product
+over the pixels of all the images, in tiles of 128 rows (output channels,
+or K = (ci, kh, kw)) x 224 pixels that may straddle two images.  The library
+picks them when the tile count is a whole multiple of the CU count (the
+ConvNeXt-style stack's downsamples); SSCNN_PATCH_FWD / SSCNN_PATCH_BWI=wide
+force them wherever they apply and =tiled switch them off, so these cases
+run both forms on shapes chosen for their edges: channel counts that are not
+a multiple of 128 rows, pixel counts that are not a multiple of 224, tiles
+that straddle images, a single image, and the push form of the halo
+exchange.  Every shard's result is compared with the oracle (1e-5
+normwise), the two forms with each other, and the pushed halos bit for bit
+with sscnn_halo_gather of the results.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from shard_harness import TOL_FWD, assert_close, host, slices, to_dev
+from shard_harness import TOL_DX, TOL_FWD, assert_close, host, slices, to_dev
 from spatially_sharded_cnn_amd import sscnn
 
 pytestmark = pytest.mark.gpu
@@ -28,6 +30,7 @@ CASES = [
     ("co144_one_image", 1, 16, 144, 24, 4 * 32, 4),            # two channel tiles, the second 16 rows
     ("co256_ci64", 2, 64, 256, 28, 2 * 64, 2),                 # 16 reduction stages, 448 pixels per image
     ("co512_ci256_many_tiles", 7, 256, 512, 16, 4 * 64, 4),    # the stack's shape class, 7 images
+    ("ci40_co32_ragged_k", 2, 40, 32, 12, 2 * 32, 2),          # K = 160 rows: a 32-row second K tile
 ]
 
 
@@ -93,3 +96,47 @@ def test_wide_forward_is_reproducible(monkeypatch):
     b2 = _fwd(monkeypatch, "wide", c, x, wd, bd)
     torch.cuda.synchronize()
     assert torch.equal(a, b2)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_wide_grad_input_matches_oracle_and_tiled(case, monkeypatch):
+    name, n, ci, co, h, w, S = case
+    _say(f"  wide grad_input {name}: ({n},{ci},{h},{w}) <- {co} channels, {S} shards")
+    rng = np.random.default_rng(4800 + CASES.index(case))
+    x_shape = (n, ci, h, w)
+    g = rng.standard_normal((n, co, h // 2, w // 2)).astype(np.float32)
+    wt = (rng.standard_normal((co, ci, 2, 2)) * 0.05).astype(np.float32)
+    gs = slices(g, S)
+    wd = to_dev(wt)
+    convs = [sscnn.conv_init(n, ci, co, h, w // S, 2, 2, 0, 1, s, S) for s in range(S)]
+    # the layer below: a depthwise 7x7 pad 3 on ci channels, whose grad_output halo the push form fills
+    below = [sscnn.conv_init(n, ci, ci, h, w // S, 7, 1, 3, ci, s, S) for s in range(S)]
+    dx_full = oracle.conv_bwd_input(g, wt, x_shape, 2, 0, 1)
+    wl = w // S
+    x_dummy = [torch.zeros(c.x_shape, device="cuda") for c in convs]
+    halos = [torch.full(c.halo_shape(sscnn.HALO_GRAD_OUTPUT), float("nan"), device="cuda") for c in below]
+    nb = lambda lst, s: (lst[s - 1] if s > 0 else None, lst[s + 1] if s < S - 1 else None)
+    dxs = []
+    for s in range(S):
+        c = convs[s]
+        out = {}
+        for mode in ("wide", "tiled"):
+            monkeypatch.setenv("SSCNN_PATCH_BWI", mode)
+            out[mode] = torch.empty(c.x_shape, device="cuda")
+            sscnn.conv_bwd_input(c, gs[s], None, wd, out[mode])
+        monkeypatch.setenv("SSCNN_PATCH_BWI", "wide")
+        dx_push = torch.empty(c.x_shape, device="cuda")
+        gw, gb = torch.empty(c.w_shape, device="cuda"), torch.empty(co, device="cuda")
+        p = sscnn.make_push(below[s], sscnn.HALO_GRAD_OUTPUT, *nb(halos, s), halos[s])
+        sscnn.conv_bwd_push(c, x_dummy[s], None, gs[s], None, wd, dx_push, gw, gb, p, sscnn.new_workspace(c))
+        torch.cuda.synchronize()
+        ref = dx_full[:, :, :, s * wl:(s + 1) * wl]
+        assert_close(host(out["wide"]), ref, TOL_DX, f"{name} shard {s}: wide grad_input vs oracle")
+        assert_close(host(out["tiled"]), ref, TOL_DX, f"{name} shard {s}: tiled grad_input vs oracle")
+        assert torch.equal(dx_push, out["wide"]), f"{name} shard {s}: conv_bwd_push grad_input != wide conv_bwd_input"
+        dxs.append(out["wide"])
+    for s in range(S):
+        gathered = torch.empty(below[s].halo_shape(sscnn.HALO_GRAD_OUTPUT), device="cuda")
+        sscnn.halo_gather(below[s], sscnn.HALO_GRAD_OUTPUT, *nb(dxs, s), gathered)
+        torch.cuda.synchronize()
+        assert torch.equal(halos[s], gathered), f"{name} shard {s}: pushed grad_output halo != gathered halo"
