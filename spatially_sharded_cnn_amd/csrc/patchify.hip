@@ -82,6 +82,9 @@ struct PArgs {
     float* push_r;        // right neighbour's halo: this slice's last ph_l columns go to [0, ph_l)
     float* push_own;      // own halo: the side without a neighbour is zeroed
     int ph_l, ph_r;
+    // BWW with a single split (dma_bww_kernel): the sums go straight to grad_weight / grad_bias
+    float* gw_out;
+    float* gb_out;
 };
 
 __device__ __forceinline__ int64_t slab_floats(const PArgs& a) { return (int64_t)a.Co * (a.Kt + 1); }
@@ -748,6 +751,150 @@ wide_bwi_kernel(PArgs a, int ntot)
     }
 }
 
+// grad_weight of a 2x2/2 layer with its operands loaded straight into LDS:
+// gW[co][K] = sum_p G[co][p] Xp[K][p] over the pixels of all the images,
+// result tiles of 128 output channels x 128 of K = (ci, kh, kw).  The pixel
+// reduction is split into `splits` ranges of 16-pixel chunks (a chunk lies in
+// one output row of one image), so that tiles x splits is a multiple of the
+// CU count; with one split the sums go straight to grad_weight, otherwise to
+// per-split slabs that slab_sum_kernel adds in split order.  A stage is one
+// chunk, loaded one stage ahead:
+//   A  G[img][m0 + m][the chunk's 16 pixels]: 128 rows of 4 units, unit u of
+//      row m at slot u ^ ((m >> 2) & 3);
+//   B  x[img][ci][2 i + kh][2 j0 .. 2 j0 + 31] for the tile's 32 input
+//      channels and kh = 0, 1, as they lie in memory (pixel pairs x kw):
+//      64 segments of 8 units, unit u of segment sg = 2 ci + kh at slot
+//      u ^ ((sg >> 1) & 7).
+// Step group tg (4 MFMA steps e) pairs k-slot 0 with pixel 8 tg + e and
+// k-slot 1 with pixel 8 tg + 4 + e: lane (hi, m) reads unit 2 tg + hi of its
+// A row with one 16-byte read, lane (hi, n = 4 ci + 2 kh + kw) words kw and
+// kw + 2 of units 4 tg + 2 hi and 4 tg + 2 hi + 1 of its B segment.  The
+// swizzles keep both kinds of read off shared banks.  grad_bias: the first K
+// tile's threads t < 128 add row t of each A stage.
+constexpr int kBwwAF = 128 * 16, kBwwBF = 64 * 32, kBwwST = kBwwAF + kBwwBF;
+
+__global__ void __launch_bounds__(kNT, 2)
+dma_bww_kernel(PArgs a)
+{
+    __shared__ __align__(16) float lds[2 * kBwwST];
+    int bid = xcd_order(blockIdx.x, gridDim.x);   // output-channel tiles of one (K tile, split) side by side
+    const int mt = bid % a.tiles_m;
+    bid /= a.tiles_m;
+    const int nt = bid % a.tiles_n;
+    const int split = bid / a.tiles_n;
+    const int m0 = mt * 128, n0 = nt * 128;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int c_beg = (int)((int64_t)split * a.chunks / a.splits);
+    const int nst = (int)((int64_t)(split + 1) * a.chunks / a.splits) - c_beg;
+
+    const i32x4 ra = plane_rsrc(a.g, a.N * a.Co * a.P * 4);
+    const i32x4 rb = plane_rsrc(a.x, a.N * a.Ci * a.H * a.W * 4);
+    int avoff[2], bvoff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int pos = 64 * (2 * wave + i) + lane;
+        const int m = pos >> 2, u = (pos & 3) ^ ((m >> 2) & 3);
+        avoff[i] = m0 + m < a.Co ? ((m0 + m) * a.P + 4 * u) * 4 : (int)0x80000000;
+        const int sg = pos >> 3, ub = (pos & 7) ^ ((sg >> 1) & 7);
+        const int ci = n0 / 4 + sg / 2, kh = sg & 1;
+        bvoff[i] = ci < a.Ci ? ((ci * a.H + kh) * a.W + 4 * ub) * 4 : (int)0x80000000;
+    }
+    // chunk c: its first pixel's image, row and column give the two operands' byte offsets
+    auto issue = [&](int s) {
+        const int gp = 16 * (c_beg + s);
+        const int img = gp / a.P, pl = gp - img * a.P;
+        const int i = pl / a.Wo, j0 = pl - i * a.Wo;
+        const int abase = (img * a.Co * a.P + pl) * 4;
+        const int bbase = ((img * a.Ci * a.H + 2 * i) * a.W + 2 * j0) * 4;
+        float* st = lds + (s & 1) * kBwwST;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) dma16(ra, st + (2 * wave + k) * 256, avoff[k] + abase);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) dma16(rb, st + kBwwAF + (2 * wave + k) * 256, bvoff[k] + bbase);
+    };
+
+    const int hi = lane >> 5, l32 = lane & 31;
+    const int wm = wave >> 1, wn = wave & 1;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
+    float bias_acc = 0.f;
+    const bool with_bias = a.with_bias && nt == 0;
+    const int asw = (l32 >> 2) & 3, bsw = (l32 >> 2) & 7;
+    // lane's B segment (n = 64 wn + 32 yb + l32): 2 (n >> 2) + ((n >> 1) & 1), word kw = n & 1
+    int bseg[2];
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+        const int n = 64 * wn + 32 * y + l32;
+        bseg[y] = kBwwAF + 32 * (2 * (n >> 2) + ((n >> 1) & 1)) + (n & 1);
+    }
+
+    if (nst > 0) issue(0);
+    for (int s = 0; s < nst; ++s) {
+        wait_vmem();
+        lds_barrier();
+        if (s + 1 < nst) issue(s + 1);
+        const float* st = lds + (s & 1) * kBwwST;
+        if (with_bias && t < 128) {
+            const int bs = (t >> 2) & 3;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float4 v = *reinterpret_cast<const float4*>(st + 16 * t + 4 * (u ^ bs));
+                bias_acc += v.x; bias_acc += v.y; bias_acc += v.z; bias_acc += v.w;
+            }
+        }
+#pragma unroll
+        for (int tg = 0; tg < 2; ++tg) {
+            float4 av[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+                av[x] = *reinterpret_cast<const float4*>(st + 16 * (64 * wm + 32 * x + l32) + 4 * ((2 * tg + hi) ^ asw));
+            float bv[2][4];
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const float* bp = st + bseg[y] + 4 * ((4 * tg + 2 * hi + d) ^ bsw);
+                    bv[y][2 * d] = bp[0];
+                    bv[y][2 * d + 1] = bp[2];
+                }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a0 = e == 0 ? av[0].x : e == 1 ? av[0].y : e == 2 ? av[0].z : av[0].w;
+                const float a1 = e == 0 ? av[1].x : e == 1 ? av[1].y : e == 2 ? av[1].z : av[1].w;
+#pragma unroll
+                for (int y = 0; y < 2; ++y) {
+                    acc[0][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, bv[y][e], acc[0][y], 0, 0, 0);
+                    acc[1][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, bv[y][e], acc[1][y], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    float* wo = a.splits == 1 ? a.gw_out : a.out + split * slab_floats(a);
+    float* bo = a.splits == 1 ? a.gb_out : a.out + split * slab_floats(a) + (int64_t)a.Co * a.Kt;
+    // D block (x, y): register 4 q + r holds row 8 q + 4 hi + r, column l32
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+            const int col = n0 + 64 * wn + 32 * y + l32;
+            if (col >= a.Kt) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = m0 + 64 * wm + 32 * x + 8 * q + 4 * hi + r;
+                    if (row < a.Co) wo[(int64_t)row * a.Kt + col] = acc[x][y][4 * q + r];
+                }
+        }
+    if (with_bias && t < 128 && m0 + t < a.Co && bo) bo[m0 + t] = bias_acc;
+}
+
 // dst[grp][e] = sum of src[k][e] over the slabs k of group grp (slabs
 // [grp * per, min(n, (grp + 1) * per))), added in slab order, in float4
 // units.  The loads of 8 slabs are issued before their adds so that they are
@@ -866,12 +1013,44 @@ bool patch_supported(const Geom& g)
            (int64_t)g.n * g.co * p < ((int64_t)1 << 31);
 }
 
+// dma_bww_kernel's split count for 2x2/2 layers whose operands fit 32-bit
+// byte offsets: tiles x splits a multiple of the CU count, about two
+// workgroups per CU (0: not taken).  SSCNN_PATCH_BWW=dma / =tiled force the
+// choice, =dma1 the kernel with a single split.
+static int dma_bww_splits(const PArgs& a)
+{
+    if (a.Kt != 4 * a.Ci || a.P % kSub || a.Wo % kSub || (int64_t)a.N * a.Co * a.P * 4 >= ((int64_t)1 << 31) ||
+        (int64_t)a.N * a.Ci * a.H * a.W * 4 >= ((int64_t)1 << 31))
+        return 0;
+    const char* env = getenv("SSCNN_PATCH_BWW");
+    if (env && !strcmp(env, "tiled")) return 0;
+    if (env && !strcmp(env, "dma1")) return 1;      // one split: the sums go straight to grad_weight
+    const bool force = env && !strcmp(env, "dma");
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int tiles = ((a.Co + 127) / 128) * ((a.Kt + 127) / 128);
+    const int chunks = a.N * a.P / kSub;
+    int splits = 0;
+    if (cus > 0 && tiles % cus == 0) splits = 1;
+    else if (cus > 0 && (2 * cus) % tiles == 0) splits = 2 * cus / tiles;
+    else if (force) splits = (2 * cus + tiles - 1) / tiles;
+    if (splits > chunks) splits = force ? chunks : 0;
+    return splits;
+}
+
 size_t patch_wgrad_workspace_bytes(const Geom& g)
 {
     const PArgs a = make_args(g);
-    const int64_t s = wgrad_plan(a).splits;
     const int64_t slab = (int64_t)a.Co * (a.Kt + 1);
-    return (size_t)((s + split_groups((int)s)) * slab) * sizeof(float);
+    // enough for either plan, so that the choice made at launch always fits
+    const int64_t s = wgrad_plan(a).splits;
+    int64_t floats = (s + split_groups((int)s)) * slab;
+    if (g.k == 2) {
+        const int64_t d = dma_bww_splits(a);
+        const int64_t fd = d > 1 ? (d + split_groups((int)d)) * slab : 0;
+        if (fd > floats) floats = fd;
+    }
+    return (size_t)floats * sizeof(float);
 }
 
 // Rows of the result tile of the forward (output channels) and grad_input (K).
@@ -977,19 +1156,32 @@ hipError_t launch_patch_bwd_weight(const Geom& g, const float* x, const float* g
 {
     PArgs a = make_args(g);
     a.x = x; a.g = gy;
-    const WgradPlan plan = wgrad_plan(a);
-    a.tiles_m = plan.tiles_m;
-    a.tiles_n = plan.tiles_n;
     a.chunks = a.N * (a.P / kSub);
-    a.splits = plan.splits;
     a.with_bias = gb != nullptr;
     float* slabs = static_cast<float*>(ws);
     a.out = slabs;
-    const int grid = a.tiles_m * a.tiles_n * a.splits;
-    hipError_t e = plan.tn == kNarrowK ? launch<BWW, 128, kNarrowK>(a, g.k, grid, st)
-                   : plan.tm == 256    ? launch<BWW, 256, 128>(a, g.k, grid, st)
-                                       : launch<BWW, 128, 128>(a, g.k, grid, st);
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    const int dma_splits = g.k == 2 ? dma_bww_splits(a) : 0;
+    if (dma_splits > 0) {
+        a.tiles_m = (a.Co + 127) / 128;
+        a.tiles_n = (a.Kt + 127) / 128;
+        a.splits = dma_splits;
+        a.gw_out = gw;
+        a.gb_out = gb;
+        hipLaunchKernelGGL(dma_bww_kernel, dim3(a.tiles_m * a.tiles_n * a.splits), dim3(kNT), 0, st, a);
+        e = hipGetLastError();
+        if (e != hipSuccess || a.splits == 1) return e;
+    } else {
+        const WgradPlan plan = wgrad_plan(a);
+        a.tiles_m = plan.tiles_m;
+        a.tiles_n = plan.tiles_n;
+        a.splits = plan.splits;
+        const int grid = a.tiles_m * a.tiles_n * a.splits;
+        e = plan.tn == kNarrowK ? launch<BWW, 128, kNarrowK>(a, g.k, grid, st)
+            : plan.tm == 256    ? launch<BWW, 256, 128>(a, g.k, grid, st)
+                                : launch<BWW, 128, 128>(a, g.k, grid, st);
+        if (e != hipSuccess) return e;
+    }
 
     // slab sums: count4 float4 per slab (Co * Kt weights, then Co biases)
     const int64_t slab = (int64_t)a.Co * (a.Kt + 1);

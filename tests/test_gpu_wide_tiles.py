@@ -1,5 +1,5 @@
-"""GPU parity of the wide-tile forward and grad_input of 2x2/2 layers (needs
-an MI355X).
+"""GPU parity of the wide-tile forward and grad_input, and of the LDS-direct
+grad_weight, of 2x2/2 layers (needs an MI355X).
 
 The forward and the grad_input of a k = s = 2 layer can run as one product
 over the pixels of all the images, in tiles of 128 rows (output channels,
@@ -12,14 +12,17 @@ a multiple of 128 rows, pixel counts that are not a multiple of 224, tiles
 that straddle images, a single image, and the push form of the halo
 exchange.  Every shard's result is compared with the oracle (1e-5
 normwise), the two forms with each other, and the pushed halos bit for bit
-with sscnn_halo_gather of the results.
+with sscnn_halo_gather of the results.  The grad_weight kernel
+(SSCNN_PATCH_BWW=dma with per-split slabs, =dma1 with one split written
+straight to grad_weight) is compared the same way, partials within 1e-4 of
+the oracle's sums over the shard's own output columns.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from shard_harness import TOL_DX, TOL_FWD, assert_close, host, slices, to_dev
+from shard_harness import TOL_DX, TOL_FWD, TOL_GW, assert_close, host, slices, to_dev
 from spatially_sharded_cnn_amd import sscnn
 
 pytestmark = pytest.mark.gpu
@@ -140,3 +143,40 @@ def test_wide_grad_input_matches_oracle_and_tiled(case, monkeypatch):
         sscnn.halo_gather(below[s], sscnn.HALO_GRAD_OUTPUT, *nb(dxs, s), gathered)
         torch.cuda.synchronize()
         assert torch.equal(halos[s], gathered), f"{name} shard {s}: pushed grad_output halo != gathered halo"
+
+
+@pytest.mark.parametrize("mode", ["dma", "dma1"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_dma_grad_weight_matches_oracle_and_tiled(case, mode, monkeypatch):
+    name, n, ci, co, h, w, S = case
+    _say(f"  grad_weight {mode} {name}: ({n},{ci},{h},{w}) x {co} channels, {S} shards")
+    rng = np.random.default_rng(4900 + CASES.index(case))
+    x = rng.standard_normal((n, ci, h, w)).astype(np.float32)
+    g = rng.standard_normal((n, co, h // 2, w // 2)).astype(np.float32)
+    wt = (rng.standard_normal((co, ci, 2, 2)) * 0.05).astype(np.float32)
+    xs, gs = slices(x, S), slices(g, S)
+    wd = to_dev(wt)
+    wol = w // 2 // S
+    for s in range(S):
+        c = sscnn.conv_init(n, ci, co, h, w // S, 2, 2, 0, 1, s, S)
+        gw_ref, gb_ref = oracle.conv_bwd_weight(x, g, 2, 2, 0, 1, cols=(s * wol, (s + 1) * wol))
+        res = {}
+        for m in (mode, "tiled"):
+            monkeypatch.setenv("SSCNN_PATCH_BWW", m)
+            ws = sscnn.new_workspace(c)
+            gw, gb = torch.empty(c.w_shape, device="cuda"), torch.empty(co, device="cuda")
+            sscnn.conv_bwd_weight_partial(c, xs[s], None, gs[s], gw, gb, ws)
+            dx2 = torch.empty(c.x_shape, device="cuda")
+            gw2, gb2 = torch.empty_like(gw), torch.empty_like(gb)
+            sscnn.conv_bwd(c, xs[s], None, gs[s], None, wd, dx2, gw2, gb2, ws)
+            # without grad_bias
+            gw3 = torch.empty_like(gw)
+            sscnn.conv_bwd_weight_partial(c, xs[s], None, gs[s], gw3, None, ws)
+            torch.cuda.synchronize()
+            res[m] = (gw, gb, gw2, gb2, gw3)
+        gw, gb, gw2, gb2, gw3 = res[mode]
+        assert_close(host(gw), gw_ref, TOL_GW, f"{name} shard {s}: {mode} grad_weight partial vs oracle")
+        assert_close(host(gb), gb_ref, TOL_GW, f"{name} shard {s}: {mode} grad_bias partial vs oracle")
+        assert torch.equal(gw2, gw) and torch.equal(gb2, gb), f"{name} shard {s}: conv_bwd partials != conv_bwd_weight_partial"
+        assert torch.equal(gw3, gw), f"{name} shard {s}: grad_weight without grad_bias differs"
+        assert_close(host(gw), host(res["tiled"][0]), TOL_GW, f"{name} shard {s}: {mode} vs tiled grad_weight")
