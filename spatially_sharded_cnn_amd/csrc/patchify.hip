@@ -895,6 +895,143 @@ dma_bww_kernel(PArgs a)
     if (with_bias && t < 128 && m0 + t < a.Co && bo) bo[m0 + t] = bias_acc;
 }
 
+// Forward of a 4x4/4 stem (k = s = 4, CI input channels, 16 CI <= 64
+// reduction rows, at most 256 output channels).  Its reduction is too short
+// to amortise staging a weight tile per pixel tile, so each workgroup of 8
+// waves keeps the weights in registers (wave w: output channels 32 w .. 32 w
+// + 31, as the MFMA A operand of all 8 CI k-steps) and walks pixel tiles of
+// 64 (persistent: tile blockIdx.x, then + gridDim.x, ...).  A tile's input --
+// for each of the 4 CI rows (ci, kh) of its pixels, the 4 columns kw of each
+// pixel (16 bytes) -- is loaded straight into LDS one tile ahead, one row per
+// instruction with lane = pixel.  MFMA step (ci, kh, kwp) pairs k-slot 0 with
+// kw = kwp and k-slot 1 with kw = kwp + 2, so one 8-byte read per lane and
+// row serves two steps.  The epilogue stores 32 consecutive pixels per row
+// and instruction through a buffer resource (row offsets in scalar
+// registers); the push form's halo writes run only for the lanes holding
+// edge columns, after the block's stores.  The store-heavy epilogue is
+// overlapped by the other workgroups on the CU: a wave's wait for its next
+// tile's input also waits for its stores (one vector-memory counter).
+constexpr int kStemNT = 512;
+
+template <int CI, bool PUSH>
+__global__ void __launch_bounds__(kStemNT, 4)
+stem_fwd_kernel(PArgs a, int ntot)
+{
+    constexpr int ROWS = 4 * CI, TN = 64, SEG = 4 * TN, KS = 8 * CI;
+    __shared__ __align__(16) float xs[2][ROWS * SEG];
+    __shared__ float bias_s[256];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int hi = lane >> 5, l32 = lane & 31;
+    const int ntiles = (ntot + TN - 1) / TN;
+
+    const i32x4 rx = plane_rsrc(a.x, a.N * CI * a.H * a.W * 4);
+    // pixel tile -> its 64 pixels, one per lane, in the DMA; row r by wave r % 8
+    auto issue = [&](int tile, int buf) {
+        const int gp = tile * TN + lane;
+        const int img = gp / a.P, pl = gp - img * a.P;
+        const int i = pl / a.Wo, j = pl - i * a.Wo;
+        const int base = gp < ntot ? (((img * CI) * a.H + 4 * i) * a.W + 4 * j) * 4 : (int)0x80000000;
+#pragma unroll
+        for (int r = wave; r < ROWS; r += 8) {
+            const int ci = r / 4, kh = r % 4;
+            dma16(rx, &xs[buf][r * SEG], base + ((ci * a.H + kh) * a.W) * 4);
+        }
+    };
+
+    int tile = blockIdx.x;
+    // the lane's weights (A operand): step (ci, kh, kwp) of row m = W[m][16 ci + 4 kh + kwp + 2 hi]
+    const int m = 32 * wave + l32;
+    float wa[KS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        float2 v = make_float2(0.f, 0.f);
+        if (m < a.Co) v = *reinterpret_cast<const float2*>(a.w + (int64_t)m * a.Kt + 4 * r + 2 * hi);
+        wa[2 * r] = v.x;
+        wa[2 * r + 1] = v.y;
+    }
+    if (t < 256) bias_s[t] = (a.b && t < a.Co) ? a.b[t] : 0.f;
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, a.N * a.Co * a.P * 4, 0x00020000);
+    const int hbytes = a.N * a.Co * a.Ho * (a.ph_l + a.ph_r) * 4;
+    const __amdgpu_buffer_rsrc_t hl = __builtin_amdgcn_make_buffer_rsrc(a.push_l, 0, a.push_l ? hbytes : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(a.push_r, 0, a.push_r ? hbytes : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t hown = __builtin_amdgcn_make_buffer_rsrc(a.push_own, 0, a.push_own ? hbytes : 0, 0x00020000);
+    if (tile < ntiles) issue(tile, 0);
+    const int pmax = a.ph_l > a.ph_r ? a.ph_l : a.ph_r;
+    for (int it = 0; tile < ntiles; ++it, tile += gridDim.x) {
+        const int buf = it & 1;
+        wait_vmem();
+        lds_barrier();
+        if (tile + (int)gridDim.x < ntiles) issue(tile + gridDim.x, buf ^ 1);
+
+        f32x16 acc[2];
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[y][r] = 0.f;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            float2 bv[2];
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+                bv[y] = *reinterpret_cast<const float2*>(&xs[buf][r * SEG + 4 * (32 * y + l32) + 2 * hi]);
+#pragma unroll
+            for (int y = 0; y < 2; ++y) {
+                acc[y] = __builtin_amdgcn_mfma_f32_32x32x2f32(wa[2 * r], bv[y].x, acc[y], 0, 0, 0);
+                acc[y] = __builtin_amdgcn_mfma_f32_32x32x2f32(wa[2 * r + 1], bv[y].y, acc[y], 0, 0, 0);
+            }
+        }
+
+        // D block y: register 4 q + r holds channel 32 w + 8 q + 4 hi + r, pixel 32 y + l32.
+        // Stored through a buffer resource: the lane's part of the offset (image, 4 hi, pixel) in a
+        // vector register, the channel's part 4 P (32 w + 8 q + r) in a scalar one.
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+            const int gp = tile * TN + 32 * y + l32;
+            if (gp >= ntot) continue;
+            const int img = gp / a.P, pl = gp - img * a.P;
+            const int voff = ((img * a.Co + 4 * hi) * a.P + pl) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int cu = 32 * wave + 8 * q + r;
+                    if (cu + 4 * hi < a.Co)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[y][4 * q + r] + bias_s[cu + 4 * hi]),
+                                                              ry, voff, __builtin_amdgcn_readfirstlane(cu * a.P * 4), 0);
+                }
+            if (PUSH) {
+                // the push of push_value, through buffer resources (a missing buffer has no
+                // records, so its stores drop): the lane's column offsets into the left and right
+                // neighbours' halos and its own halo's two zeroed sides (or out of range)
+                const int pi = pl / a.Wo, pj = pl - pi * a.Wo;
+                if (pj < pmax || pj >= a.Wo - pmax) {
+                    const int hw = a.ph_l + a.ph_r;
+                    const int row0 = ((img * a.Co + 4 * hi) * a.Ho + pi) * hw;
+                    constexpr int kOut = (int)0x80000000;
+                    const int ol = a.push_l ? (pj < a.ph_r ? (row0 + a.ph_l + pj) * 4 : kOut)
+                                            : (pj < a.ph_l ? (row0 + pj) * 4 : kOut);
+                    const int rj = pj - (a.Wo - a.ph_l), oj = pj - (a.Wo - a.ph_r);
+                    const int orr = a.push_r ? (rj >= 0 ? (row0 + rj) * 4 : kOut)
+                                             : (oj >= 0 ? (row0 + a.ph_l + oj) * 4 : kOut);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int cu = 32 * wave + 8 * q + r;
+                            if (cu + 4 * hi >= a.Co) continue;
+                            const float v = acc[y][4 * q + r] + bias_s[cu + 4 * hi];
+                            const int so = __builtin_amdgcn_readfirstlane(cu * a.Ho * hw * 4);
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a.push_l ? v : 0.f),
+                                                                  a.push_l ? hl : hown, ol, so, 0);
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a.push_r ? v : 0.f),
+                                                                  a.push_r ? hr : hown, orr, so, 0);
+                        }
+                }
+            }
+        }
+    }
+}
+
 // dst[grp][e] = sum of src[k][e] over the slabs k of group grp (slabs
 // [grp * per, min(n, (grp + 1) * per))), added in slab order, in float4
 // units.  The loads of 8 slabs are issued before their adds so that they are
@@ -1094,6 +1231,17 @@ static int wide_fwd_tiles(const PArgs& a)
     return (int)(((a.Co + kWideTM - 1) / kWideTM) * ((ntot + kWideTN - 1) / kWideTN));
 }
 
+// The stem kernel (stem_fwd_kernel): 4x4/4 layers on 3 input channels whose
+// input and output fit 32-bit byte offsets; SSCNN_PATCH_STEM=tiled switches
+// it off.
+static bool use_stem_fwd(const PArgs& a)
+{
+    if ((int64_t)a.N * a.Ci * a.H * a.W * 4 >= ((int64_t)1 << 31) || (int64_t)a.N * a.Co * a.P * 4 >= ((int64_t)1 << 31))
+        return false;
+    const char* env = getenv("SSCNN_PATCH_STEM");
+    return !(env && !strcmp(env, "tiled"));
+}
+
 static bool use_wide(int tiles, const char* var)
 {
     if (tiles == 0) return false;
@@ -1112,6 +1260,16 @@ hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const
     PArgs a = make_args(g);
     a.x = x; a.w = w; a.b = b; a.out = y; a.act = act;
     set_push(a, push);
+    if (g.k == 4 && g.ci == 3 && g.co <= 256 && use_stem_fwd(a)) {
+        const int tiles = (int)(((int64_t)a.N * a.P + 63) / 64);
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        const bool push_ = push && (push->to_left || push->to_right || push->own);
+        const int grid = tiles < 2 * cus ? tiles : 2 * cus;
+        if (push_) hipLaunchKernelGGL((stem_fwd_kernel<3, true>), dim3(grid), dim3(kStemNT), 0, st, a, a.N * a.P);
+        else hipLaunchKernelGGL((stem_fwd_kernel<3, false>), dim3(grid), dim3(kStemNT), 0, st, a, a.N * a.P);
+        return hipGetLastError();
+    }
     if (g.k == 2 && use_wide(wide_fwd_tiles(a), "SSCNN_PATCH_FWD")) {
         a.tiles_m = (a.Co + kWideTM - 1) / kWideTM;
         const int grid = wide_fwd_tiles(a);

@@ -15,7 +15,9 @@ normwise), the two forms with each other, and the pushed halos bit for bit
 with sscnn_halo_gather of the results.  The grad_weight kernel
 (SSCNN_PATCH_BWW=dma with per-split slabs, =dma1 with one split written
 straight to grad_weight) is compared the same way, partials within 1e-4 of
-the oracle's sums over the shard's own output columns.
+the oracle's sums over the shard's own output columns.  The 4x4/4 stem's
+forward kernel (weights in registers, persistent over 64-pixel tiles;
+SSCNN_PATCH_STEM=tiled switches it off) is checked the same way.
 """
 import numpy as np
 import pytest
@@ -180,3 +182,51 @@ def test_dma_grad_weight_matches_oracle_and_tiled(case, mode, monkeypatch):
         assert torch.equal(gw2, gw) and torch.equal(gb2, gb), f"{name} shard {s}: conv_bwd partials != conv_bwd_weight_partial"
         assert torch.equal(gw3, gw), f"{name} shard {s}: grad_weight without grad_bias differs"
         assert_close(host(gw), host(res["tiled"][0]), TOL_GW, f"{name} shard {s}: {mode} vs tiled grad_weight")
+
+
+# (name, n, co, h, w, shards): the 4x4/4 stem on 3 input channels
+STEM_CASES = [
+    ("stem_co256", 2, 256, 32, 4 * 128, 4),
+    ("stem_co48_ragged_tiles", 3, 48, 24, 2 * 64, 2),     # 96 pixels per image: 64-pixel tiles straddle images
+    ("stem_co96_one_row", 1, 96, 4, 4 * 64, 4),           # one output row per image
+]
+
+
+@pytest.mark.parametrize("case", STEM_CASES, ids=[c[0] for c in STEM_CASES])
+def test_stem_forward_matches_oracle_and_tiled(case, monkeypatch):
+    name, n, co, h, w, S = case
+    _say(f"  stem fwd {name}: ({n},3,{h},{w}) -> {co} channels, {S} shards")
+    rng = np.random.default_rng(5000 + STEM_CASES.index(case))
+    x = rng.standard_normal((n, 3, h, w)).astype(np.float32)
+    wt = (rng.standard_normal((co, 3, 4, 4)) * 0.1).astype(np.float32)
+    b = (rng.standard_normal(co) * 0.1).astype(np.float32)
+    xs = slices(x, S)
+    wd, bd = to_dev(wt), to_dev(b)
+    convs = [sscnn.conv_init(n, 3, co, h, w // S, 4, 4, 0, 1, s, S) for s in range(S)]
+    cons = [sscnn.conv_init(n, co, co, h // 4, w // 4 // S, 7, 1, 3, co, s, S) for s in range(S)]
+    y_full = oracle.conv_fwd(x, wt, b, 4, 0, 1)
+    wol = w // 4 // S
+    halos = [torch.full(c.halo_shape(sscnn.HALO_INPUT), float("nan"), device="cuda") for c in cons]
+    nb = lambda lst, s: (lst[s - 1] if s > 0 else None, lst[s + 1] if s < S - 1 else None)
+    ys = []
+    for s in range(S):
+        monkeypatch.setenv("SSCNN_PATCH_STEM", "tiled")
+        y_tiled = torch.empty(convs[s].y_shape, device="cuda")
+        sscnn.conv_fwd(convs[s], xs[s], None, wd, bd, y_tiled)
+        monkeypatch.delenv("SSCNN_PATCH_STEM")
+        y = torch.empty(convs[s].y_shape, device="cuda")
+        sscnn.conv_fwd(convs[s], xs[s], None, wd, bd, y)
+        y_push = torch.empty(convs[s].y_shape, device="cuda")
+        p = sscnn.make_push(cons[s], sscnn.HALO_INPUT, *nb(halos, s), halos[s])
+        sscnn.conv_fwd_push(convs[s], xs[s], None, wd, bd, y_push, p)
+        torch.cuda.synchronize()
+        ref = y_full[:, :, :, s * wol:(s + 1) * wol]
+        assert_close(host(y), ref, TOL_FWD, f"{name} shard {s}: stem forward vs oracle")
+        assert_close(host(y_tiled), ref, TOL_FWD, f"{name} shard {s}: tiled forward vs oracle")
+        assert torch.equal(y_push, y), f"{name} shard {s}: pushing changed the stem forward's output"
+        ys.append(y)
+    for s in range(S):
+        gathered = torch.empty(cons[s].halo_shape(sscnn.HALO_INPUT), device="cuda")
+        sscnn.halo_gather(cons[s], sscnn.HALO_INPUT, *nb(ys, s), gathered)
+        torch.cuda.synchronize()
+        assert torch.equal(halos[s], gathered), f"{name} shard {s}: pushed halo != gathered halo"
