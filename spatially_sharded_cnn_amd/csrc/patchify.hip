@@ -1309,6 +1309,33 @@ hipError_t launch_patch_bwd_input(const Geom& g, const float* gy, const float* w
     return launch_rows<BWI>(a, a.Kt, row_tile(a.Kt, a, a.Kt <= kNarrowK), g.k, st);
 }
 
+// grad_weight / grad_bias = the sum of n slabs of partials (each Co * Kt
+// weights, then Co biases), added in slab order: one pass for n <= 32, else
+// groups of 16, then the groups.
+static hipError_t sum_slabs(const PArgs& a, float* slabs, int n, float* gw, float* gb, hipStream_t st)
+{
+    hipError_t e;
+    const int64_t slab = (int64_t)a.Co * (a.Kt + 1);
+    const int64_t count4 = slab / 4, nw4 = (int64_t)a.Co * a.Kt / 4;
+    const unsigned bx = (unsigned)((count4 + 255) / 256);
+    float4* dw = reinterpret_cast<float4*>(gw);
+    float4* db = reinterpret_cast<float4*>(gb);
+    const int groups = split_groups(n);
+    if (groups == 0) {
+        hipLaunchKernelGGL(slab_sum_kernel, dim3(bx, 1), dim3(256), 0, st, reinterpret_cast<const float4*>(slabs),
+                           count4, n, n, nullptr, dw, db, nw4);
+        return hipGetLastError();
+    }
+    float4* mid = reinterpret_cast<float4*>(slabs + n * slab);
+    hipLaunchKernelGGL(slab_sum_kernel, dim3(bx, groups), dim3(256), 0, st, reinterpret_cast<const float4*>(slabs),
+                       count4, n, kSlabsPerGroup, mid, nullptr, nullptr, nw4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(slab_sum_kernel, dim3(bx, 1), dim3(256), 0, st, static_cast<const float4*>(mid), count4,
+                       groups, groups, nullptr, dw, db, nw4);
+    return hipGetLastError();
+}
+
 hipError_t launch_patch_bwd_weight(const Geom& g, const float* x, const float* gy, float* gw, float* gb,
                                    void* ws, hipStream_t st)
 {
@@ -1341,26 +1368,7 @@ hipError_t launch_patch_bwd_weight(const Geom& g, const float* x, const float* g
         if (e != hipSuccess) return e;
     }
 
-    // slab sums: count4 float4 per slab (Co * Kt weights, then Co biases)
-    const int64_t slab = (int64_t)a.Co * (a.Kt + 1);
-    const int64_t count4 = slab / 4, nw4 = (int64_t)a.Co * a.Kt / 4;
-    const unsigned bx = (unsigned)((count4 + 255) / 256);
-    float4* dw = reinterpret_cast<float4*>(gw);
-    float4* db = reinterpret_cast<float4*>(gb);
-    const int groups = split_groups(a.splits);
-    if (groups == 0) {
-        hipLaunchKernelGGL(slab_sum_kernel, dim3(bx, 1), dim3(256), 0, st, reinterpret_cast<const float4*>(slabs),
-                           count4, a.splits, a.splits, nullptr, dw, db, nw4);
-        return hipGetLastError();
-    }
-    float4* mid = reinterpret_cast<float4*>(slabs + a.splits * slab);
-    hipLaunchKernelGGL(slab_sum_kernel, dim3(bx, groups), dim3(256), 0, st, reinterpret_cast<const float4*>(slabs),
-                       count4, a.splits, kSlabsPerGroup, mid, nullptr, nullptr, nw4);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(slab_sum_kernel, dim3(bx, 1), dim3(256), 0, st, static_cast<const float4*>(mid), count4,
-                       groups, groups, nullptr, dw, db, nw4);
-    return hipGetLastError();
+    return sum_slabs(a, slabs, a.splits, gw, gb, st);
 }
 
 }  // namespace sscnn

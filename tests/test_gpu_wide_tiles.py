@@ -17,7 +17,8 @@ with sscnn_halo_gather of the results.  The grad_weight kernel
 straight to grad_weight) is compared the same way, partials within 1e-4 of
 the oracle's sums over the shard's own output columns.  The 4x4/4 stem's
 forward kernel (weights in registers, persistent over 64-pixel tiles;
-SSCNN_PATCH_STEM=tiled switches it off) is checked the same way.
+SSCNN_PATCH_STEM=tiled switches it off) is checked the same way, and the
+stem's backward against the oracle on the same shapes.
 """
 import numpy as np
 import pytest
@@ -230,3 +231,37 @@ def test_stem_forward_matches_oracle_and_tiled(case, monkeypatch):
         sscnn.halo_gather(cons[s], sscnn.HALO_INPUT, *nb(ys, s), gathered)
         torch.cuda.synchronize()
         assert torch.equal(halos[s], gathered), f"{name} shard {s}: pushed halo != gathered halo"
+
+
+@pytest.mark.parametrize("case", STEM_CASES, ids=[c[0] for c in STEM_CASES])
+def test_stem_backward_matches_oracle(case):
+    """The stem's backward (grad_input, grad_weight / grad_bias partials) on the same shapes:
+    against the oracle, conv_bwd's grad_input bit for bit against conv_bwd_input's, and
+    grad_weight computed with and without grad_bias equal."""
+    name, n, co, h, w, S = case
+    _say(f"  stem bwd {name}: ({n},3,{h},{w}) <- {co} channels, {S} shards")
+    rng = np.random.default_rng(5100 + STEM_CASES.index(case))
+    x = rng.standard_normal((n, 3, h, w)).astype(np.float32)
+    g = rng.standard_normal((n, co, h // 4, w // 4)).astype(np.float32)
+    wt = (rng.standard_normal((co, 3, 4, 4)) * 0.1).astype(np.float32)
+    xs, gs = slices(x, S), slices(g, S)
+    wd = to_dev(wt)
+    dx_full = oracle.conv_bwd_input(g, wt, x.shape, 4, 0, 1)
+    wl, wol = w // S, w // 4 // S
+    for s in range(S):
+        c = sscnn.conv_init(n, 3, co, h, wl, 4, 4, 0, 1, s, S)
+        gw_ref, gb_ref = oracle.conv_bwd_weight(x, g, 4, 4, 0, 1, cols=(s * wol, (s + 1) * wol))
+        ws = sscnn.new_workspace(c)
+        dx = torch.empty(c.x_shape, device="cuda")
+        gw, gb = torch.empty(c.w_shape, device="cuda"), torch.empty(co, device="cuda")
+        sscnn.conv_bwd(c, xs[s], None, gs[s], None, wd, dx, gw, gb, ws)
+        dx1 = torch.empty(c.x_shape, device="cuda")
+        sscnn.conv_bwd_input(c, gs[s], None, wd, dx1)
+        gw_nb = torch.empty_like(gw)
+        sscnn.conv_bwd(c, xs[s], None, gs[s], None, wd, torch.empty_like(dx), gw_nb, None, ws)
+        torch.cuda.synchronize()
+        assert_close(host(dx), dx_full[:, :, :, s * wl:(s + 1) * wl], TOL_DX, f"{name} shard {s}: grad_input vs oracle")
+        assert_close(host(gw), gw_ref, TOL_GW, f"{name} shard {s}: grad_weight partial vs oracle")
+        assert_close(host(gb), gb_ref, TOL_GW, f"{name} shard {s}: grad_bias partial vs oracle")
+        assert torch.equal(dx, dx1), f"{name} shard {s}: conv_bwd grad_input != conv_bwd_input"
+        assert torch.equal(gw_nb, gw), f"{name} shard {s}: grad_weight without grad_bias differs"
