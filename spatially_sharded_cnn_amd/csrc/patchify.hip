@@ -1032,6 +1032,206 @@ stem_fwd_kernel(PArgs a, int ntot)
     }
 }
 
+// grad_input of the 4x4/4 stem on 3 channels (K = 48): dXp[K][p] =
+// sum_co W[co][K] G[co][p] over the pixels of all the images, in tiles of all
+// 48 rows of K x 128 pixels, 16 output channels (reduction rows) per stage,
+// loaded straight into LDS one stage ahead.  16 x 16 x 4 MFMA blocks fit K =
+// 48 exactly; wave w owns pixel blocks 2 w, 2 w + 1 and all three K blocks.
+//   A  W[k0 .. k0 + 15][0 .. 47] as it lies in memory (rows 48 floats apart,
+//      which puts a step's 4 rows in different banks);
+//   B  G[k0 + kr][the tile's 128 pixels], 16-byte unit u of row kr at slot
+//      u ^ 4 (kr & 3), so a step's 4 rows x 16 pixels hit distinct banks.
+// The 4 registers of a lane are kw = 0..3 of one (ci, kh, pixel): one 16-byte
+// store each.
+constexpr int kSiTN = 128, kSiAF = 16 * 48, kSiBF = 16 * kSiTN, kSiST = kSiAF + kSiBF;
+
+__global__ void __launch_bounds__(kNT, 4)
+stem_bwi_kernel(PArgs a, int ntot)
+{
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    __shared__ __align__(16) float lds[2 * kSiST];
+    const int n0 = blockIdx.x * kSiTN;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int nstage = a.Co / 16;
+
+    // A: 768 floats per stage = 3 instructions (waves 0-2); B: 16 rows of 32 units = 8 instructions, 2 per wave
+    const i32x4 ra = plane_rsrc(a.w, a.Co * 48 * 4);
+    const i32x4 rb = plane_rsrc(a.g, a.N * a.Co * a.P * 4);
+    int bvoff[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int pos = 64 * (2 * wave + k) + lane;
+        const int kr = pos >> 5, u = (pos & 31) ^ (4 * (kr & 3));
+        const int gp = n0 + 4 * u;
+        const int img = gp / a.P, pl = gp - img * a.P;
+        bvoff[k] = gp < ntot ? ((img * a.Co + kr) * a.P + pl) * 4 : (int)0x80000000;
+    }
+    auto issue = [&](int s) {
+        float* st = lds + (s & 1) * kSiST;
+        if (wave < 3) dma16(ra, st + wave * 256, (s * 16 * 48 + 4 * (64 * wave + lane)) * 4);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) dma16(rb, st + kSiAF + (2 * wave + k) * 256, bvoff[k] + s * 16 * a.P * 4);
+    };
+
+    f32x4 acc[3][2];
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc[m][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the lane's B word in row kr = 4 q + lq of a step q: pixel n = 32 w + 16 h + l16 at slot (n >> 2) ^ 4 lq
+    int bw[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int n = 32 * wave + 16 * h + l16;
+        bw[h] = kSiAF + lq * kSiTN + 4 * ((n >> 2) ^ (4 * lq)) + (n & 3);
+    }
+
+    issue(0);
+    for (int s = 0; s < nstage; ++s) {
+        wait_vmem();
+        lds_barrier();
+        if (s + 1 < nstage) issue(s + 1);
+        const float* st = lds + (s & 1) * kSiST;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float av[3], bv[2];
+#pragma unroll
+            for (int m = 0; m < 3; ++m) av[m] = st[(4 * q + lq) * 48 + 16 * m + l16];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) bv[h] = st[bw[h] + 4 * q * kSiTN];
+#pragma unroll
+            for (int m = 0; m < 3; ++m)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    acc[m][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m], bv[h], acc[m][h], 0, 0, 0);
+        }
+    }
+
+    // block (m, h): register r of lane (lq, l16) is K row 16 m + 4 lq + r = (ci = m, kh = lq, kw = r)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int gp = n0 + 32 * wave + 16 * h + l16;
+        if (gp >= ntot) continue;
+        const int img = gp / a.P, pl = gp - img * a.P;
+        const int i = pl / a.Wo, j = pl - i * a.Wo;
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+            *reinterpret_cast<float4*>(a.out + (((int64_t)(img * 3 + m) * a.H + 4 * i + lq) * a.W + 4 * j)) =
+                make_float4(acc[m][h][0], acc[m][h][1], acc[m][h][2], acc[m][h][3]);
+    }
+}
+
+// grad_weight / grad_bias partials of the 4x4/4 stem on 3 channels (K = 48,
+// at most 256 output channels): gW[co][K] = sum_p G[co][p] Xp[K][p].  The
+// whole result is 16 x 3 blocks of 16 x 16 (16 x 16 x 4 MFMA blocks fit K =
+// 48 exactly); each workgroup sums a contiguous range of 16-pixel chunks (a
+// chunk lies in one output row of one image) into its own slab, and the slabs
+// are added in workgroup order afterwards.  Wave w owns output-channel blocks
+// 4 w .. 4 w + 3 and all three K blocks.  A stage is one chunk, loaded
+// straight into LDS one stage ahead:
+//   A  G[img][co][the chunk's 16 pixels]: 256 rows of 4 units, unit u of row
+//      co at slot u ^ ((co >> 2) & 3);
+//   B  x[img][ci][4 i + kh][the chunk's 16 pixels x 4 kw]: 12 rows (ci, kh),
+//      pixel u of row r at slot u ^ 4 (r & 3).
+// The swizzles put a step's 16 rows x 4 pixels (A) and 4 rows x 4 pixels x 4
+// kw (B) in distinct banks.  Threads t < Co add row t of each A stage for
+// grad_bias.
+constexpr int kSwAF = 256 * 16, kSwBF = 12 * 64, kSwST = kSwAF + kSwBF;
+
+__global__ void __launch_bounds__(kNT, 2)
+stem_bww_kernel(PArgs a, float* slabs)
+{
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    __shared__ __align__(16) float lds[2 * kSwST];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
+    const int c_beg = (int)((int64_t)blockIdx.x * a.chunks / gridDim.x);
+    const int nst = (int)((int64_t)(blockIdx.x + 1) * a.chunks / gridDim.x) - c_beg;
+
+    const i32x4 rg = plane_rsrc(a.g, a.N * a.Co * a.P * 4);
+    const i32x4 rx = plane_rsrc(a.x, a.N * 3 * a.H * a.W * 4);
+    int gvoff[4], xvoff = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int pos = 64 * (4 * wave + k) + lane;
+        const int co = pos >> 2, u = (pos & 3) ^ ((co >> 2) & 3);
+        gvoff[k] = co < a.Co ? (co * a.P + 4 * u) * 4 : (int)0x80000000;
+    }
+    if (wave < 3) {
+        const int pos = 64 * wave + lane;
+        const int r = pos >> 4, u = (pos & 15) ^ (4 * (r & 3));
+        xvoff = (((r / 4) * a.H + r % 4) * a.W + 4 * u) * 4;
+    }
+    auto issue = [&](int s) {
+        const int gp = 16 * (c_beg + s);
+        const int img = gp / a.P, pl = gp - img * a.P;
+        const int i = pl / a.Wo, j0 = pl - i * a.Wo;
+        const int gbase = (img * a.Co * a.P + pl) * 4;
+        const int xbase = ((img * 3 * a.H + 4 * i) * a.W + 4 * j0) * 4;
+        float* st = lds + (s & 1) * kSwST;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dma16(rg, st + (4 * wave + k) * 256, gvoff[k] + gbase);
+        if (wave < 3) dma16(rx, st + kSwAF + wave * 256, xvoff + xbase);
+    };
+
+    f32x4 acc[4][3];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) acc[c][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float bsum = 0.f;
+    const bool bias_thread = t < a.Co && a.with_bias;
+
+    if (nst > 0) issue(0);
+    for (int s = 0; s < nst; ++s) {
+        wait_vmem();
+        lds_barrier();
+        if (s + 1 < nst) issue(s + 1);
+        const float* st = lds + (s & 1) * kSwST;
+        if (bias_thread) {
+            const int f = (t >> 2) & 3;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float4 v = *reinterpret_cast<const float4*>(st + 16 * t + 4 * (u ^ f));
+                bsum += v.x; bsum += v.y; bsum += v.z; bsum += v.w;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            // step q: k-slot lq is pixel 4 q + lq
+            float av[4], bv[3];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int co = 16 * (4 * wave + c) + l16;
+                av[c] = st[16 * co + 4 * (q ^ ((co >> 2) & 3)) + lq];
+            }
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const int r = 4 * k + (l16 >> 2);
+                bv[k] = st[kSwAF + 64 * r + 4 * ((4 * q + lq) ^ (4 * (r & 3))) + (l16 & 3)];
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    acc[c][k] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c], bv[k], acc[c][k], 0, 0, 0);
+        }
+    }
+
+    // block (c, k): register r of lane (lq, l16) is output channel 16 (4 w + c) + 4 lq + r, K = 16 k + l16
+    float* slab = slabs + (int64_t)blockIdx.x * a.Co * 49;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if (16 * (4 * wave + c) >= a.Co) continue;
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) slab[(16 * (4 * wave + c) + 4 * lq + r) * 48 + 16 * k + l16] = acc[c][k][r];
+    }
+    if (bias_thread) slab[a.Co * 48 + t] = bsum;
+}
+
 // dst[grp][e] = sum of src[k][e] over the slabs k of group grp (slabs
 // [grp * per, min(n, (grp + 1) * per))), added in slab order, in float4
 // units.  The loads of 8 slabs are issued before their adds so that they are
@@ -1175,6 +1375,23 @@ static int dma_bww_splits(const PArgs& a)
     return splits;
 }
 
+// The stem's grad_weight kernel (stem_bww_kernel): 4x4/4 layers on 3 input
+// channels with at most 256 outputs whose tensors fit 32-bit byte offsets,
+// two workgroups per CU, each one slab (0: not taken; SSCNN_PATCH_STEM=tiled
+// switches it off).
+static int stem_bww_grid(const Geom& g, const PArgs& a)
+{
+    if (g.k != 4 || g.ci != 3 || g.co > 256 || g.co % 16 || (int64_t)a.N * a.Co * a.P * 4 >= ((int64_t)1 << 31) ||
+        (int64_t)a.N * 3 * a.H * a.W * 4 >= ((int64_t)1 << 31) || a.Wo % kSub)
+        return 0;
+    const char* env = getenv("SSCNN_PATCH_STEM");
+    if (env && !strcmp(env, "tiled")) return 0;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int chunks = a.N * a.P / kSub;
+    return chunks < 2 * cus ? chunks : 2 * cus;
+}
+
 size_t patch_wgrad_workspace_bytes(const Geom& g)
 {
     const PArgs a = make_args(g);
@@ -1187,6 +1404,8 @@ size_t patch_wgrad_workspace_bytes(const Geom& g)
         const int64_t fd = d > 1 ? (d + split_groups((int)d)) * slab : 0;
         if (fd > floats) floats = fd;
     }
+    const int64_t sw = stem_bww_grid(g, a);
+    if (sw > 0 && (sw + split_groups((int)sw)) * slab > floats) floats = (sw + split_groups((int)sw)) * slab;
     return (size_t)floats * sizeof(float);
 }
 
@@ -1205,6 +1424,8 @@ hipError_t launch_rows(PArgs& a, int rows, int tm, int s, hipStream_t st)
     const int grid = a.tiles_m * a.tiles_n * a.N;
     return tm == 64 ? launch<MODE, 64, 128>(a, s, grid, st) : launch<MODE, 128, 128>(a, s, grid, st);
 }
+
+static bool pushes_any(const Push* push) { return push && (push->to_left || push->to_right || push->own); }
 
 static void set_push(PArgs& a, const Push* push)
 {
@@ -1300,6 +1521,17 @@ hipError_t launch_patch_bwd_input(const Geom& g, const float* gy, const float* w
     PArgs a = make_args(g);
     a.g = gy; a.w = w; a.out = gx; a.pre = pre;
     set_push(a, push);
+    if (g.k == 4 && g.ci == 3 && g.co % 16 == 0 && !pre && use_stem_fwd(a)) {
+        // the stem: 48 x 128-pixel tiles on 16 x 16 MFMA blocks (SSCNN_PATCH_STEM=tiled switches them
+        // off); a push form copies the edge columns afterwards
+        hipLaunchKernelGGL(stem_bwi_kernel, dim3((unsigned)(((int64_t)a.N * a.P + kSiTN - 1) / kSiTN)), dim3(kNT), 0, st,
+                           a, a.N * a.P);
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess && pushes_any(push))
+            e = launch_push_edges(gx, (int64_t)g.n * g.ci, g.h, g.wl, push->hl, push->hr, push->to_left, push->to_right,
+                                  push->own, st);
+        return e;
+    }
     if (g.k == 2 && use_wide(wide_bwi_tiles(a), "SSCNN_PATCH_BWI")) {
         a.tiles_m = (a.Kt + kWideTM - 1) / kWideTM;
         hipLaunchKernelGGL(wide_bwi_kernel, dim3(wide_bwi_tiles(a)), dim3(kNT), 0, st, a, a.N * a.P);
@@ -1346,6 +1578,12 @@ hipError_t launch_patch_bwd_weight(const Geom& g, const float* x, const float* g
     float* slabs = static_cast<float*>(ws);
     a.out = slabs;
     hipError_t e;
+    if (const int sw = stem_bww_grid(g, a)) {
+        hipLaunchKernelGGL(stem_bww_kernel, dim3(sw), dim3(kNT), 0, st, a, slabs);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return sum_slabs(a, slabs, sw, gw, gb, st);
+    }
     const int dma_splits = g.k == 2 ? dma_bww_splits(a) : 0;
     if (dma_splits > 0) {
         a.tiles_m = (a.Co + 127) / 128;
