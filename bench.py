@@ -101,6 +101,9 @@ def _parse():
     ap.add_argument("--op-reps", type=int, default=20, help="back-to-back calls per operation timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-split", action="store_true", help="skip the interior/edge split timings")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the HBM ceiling measurement (for counter runs: its 1 GiB copy would otherwise be "
+                         "taken for the 256 MiB calibration copy)")
     ap.add_argument("--summarize", metavar="DIR", nargs="+",
                     help="summarize rocprofv3 output directories and exit")
     ap.add_argument("--traffic-op", help="with --summarize over FETCH_SIZE / WRITE_SIZE runs: the operation "
@@ -220,7 +223,8 @@ def main():
     out = run_workload(args, args.workload)
     if out is None:                 # --profile-op: the run printed its own line
         return 0
-    out["hbm_ceiling"] = hbm_ceiling()
+    if not args.no_ceiling:
+        out["hbm_ceiling"] = hbm_ceiling()
     if args.workload == DEFAULT_WORKLOAD and not args.no_sub and not args.profile_op:
         # The other full-size configurations, each timed on its own with its own
         # defaults for steps and warmup, and with its own roofline.
