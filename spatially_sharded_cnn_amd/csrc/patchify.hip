@@ -507,13 +507,15 @@ patch_kernel(PArgs a)
 }
 
 // Forward of a 2x2/2 layer in wide tiles.  The product runs over the pixels
-// of all the images at once, in result tiles of 128 output channels x 224
-// pixels (7 MFMA blocks of 32) that may straddle two images: the
+// of all the images at once, in result tiles of 128 output channels x 32 NB
+// pixels (NB MFMA blocks of 32) that may straddle two images: the
 // ConvNeXt-style stack's downsamples have 7 x 2^j output pixels per channel,
-// so 224-pixel tiles divide them into a whole multiple of the CU count, where
-// 128-pixel tiles per image leave the last round of workgroups partly empty.
-// Wave w computes rows 32 w .. 32 w + 31 of the tile against all 7 pixel
-// blocks.  A stage is 4 input channels (16 reduction rows), loaded from HBM
+// so 224-pixel tiles (NB = 7) divide them into a whole multiple of the CU
+// count, where 128-pixel tiles per image leave the last round of workgroups
+// partly empty.  Where 224-pixel tiles are fewer than the CUs (the deepest
+// downsample of a narrow shard: 128 tiles), 128-pixel tiles (NB = 4) give
+// each CU at most one tile of 4/7 the work.  Wave w computes rows
+// 32 w .. 32 w + 31 of the tile against all NB pixel blocks.  A stage is 4 input channels (16 reduction rows), loaded from HBM
 // straight into LDS (buffer_load ... lds, no registers) one stage ahead:
 //   A  W[m0 + m][(4 c .. 4 c + 3) + 16 s]: 16-byte units, unit (m, c) at
 //      slot m * 4 + (c ^ ((m >> 2) & 3)) (the swizzle spreads a wave's reads
@@ -525,16 +527,19 @@ patch_kernel(PArgs a)
 // words per wave) and the A operand is word 2 kh + hi of unit (m, c).
 constexpr int kWideTM = 128, kWideNB = 7, kWideTN = 32 * kWideNB, kWideSeg = 512;
 constexpr int kWideAF = kWideTM * 16, kWideBF = 8 * kWideSeg, kWideST = kWideAF + kWideBF;
-constexpr int kWideLoads = 6;      // LDS-direct loads per wave and stage: 2 for A, 4 for B
 
+template <int NB>
 __global__ void __launch_bounds__(kNT, 3)
 wide_fwd_kernel(PArgs a, int ntot)
 {
+    constexpr int TN = 32 * NB;                  // the tile's pixels
+    constexpr int NH = (2 * TN + 255) / 256;     // 64-lane B loads per (channel, kh): 256 floats each
+    static_assert(NB <= kWideNB, "B segments hold 512 floats");
     __shared__ __align__(16) float lds[2 * kWideST];
     __shared__ float bias_s[kWideTM];
     const int bid = xcd_order(blockIdx.x, gridDim.x);   // output-channel tiles of one pixel tile side by side
     const int mt = bid % a.tiles_m, nt = bid / a.tiles_m;
-    const int m0 = mt * kWideTM, n0 = nt * kWideTN;
+    const int m0 = mt * kWideTM, n0 = nt * TN;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     if (t < kWideTM) bias_s[t] = (a.b && m0 + t < a.Co) ? a.b[m0 + t] : 0.f;
     const int nstage = a.Ci / 4;
@@ -551,14 +556,14 @@ wide_fwd_kernel(PArgs a, int ntot)
     // B: wave w loads channel 4 s + w, rows kh = 0, 1, in two halves of 64 units (pixel pairs);
     // pixels past the tile or past the last image read as zeros
     const i32x4 rb = plane_rsrc(a.x, a.N * a.Ci * a.H * a.W * 4);
-    int bvoff[2][2];
+    int bvoff[NH][2];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
+    for (int hf = 0; hf < NH; ++hf) {
         const int n = 2 * (64 * hf + lane);
         const int gp = n0 + n;
         const int img = gp / a.P, pl = gp - img * a.P;
         const int i = pl / a.Wo, j = pl - i * a.Wo;
-        const bool ok = n < kWideTN && gp < ntot;
+        const bool ok = n < TN && gp < ntot;
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
             bvoff[hf][kh] = ok ? (((img * a.Ci + wave) * a.H + 2 * i + kh) * a.W + 2 * j) * 4 : (int)0x80000000;
@@ -571,14 +576,14 @@ wide_fwd_kernel(PArgs a, int ntot)
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
+            for (int hf = 0; hf < NH; ++hf)
                 dma16(rb, st + kWideAF + (2 * wave + kh) * kWideSeg + 256 * hf, bvoff[hf][kh] + s * b_step);
     };
 
     const int hi = lane >> 5, l32 = lane & 31;
-    f32x16 acc[kWideNB];
+    f32x16 acc[NB];
 #pragma unroll
-    for (int b = 0; b < kWideNB; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
     const int sw = (l32 >> 2) & 3;
@@ -596,17 +601,17 @@ wide_fwd_kernel(PArgs a, int ntot)
         for (int c = 0; c < 4; ++c) {
             const int ao = (arow + (c ^ sw)) * 4 + hi;
             const float a0 = st[ao], a1 = st[ao + 2];
-            float b0[kWideNB], b1[kWideNB];
+            float b0[NB], b1[NB];
 #pragma unroll
-            for (int yb = 0; yb < kWideNB; ++yb) {
+            for (int yb = 0; yb < NB; ++yb) {
                 b0[yb] = st[boff + (2 * c) * kWideSeg + 64 * yb];
                 b1[yb] = st[boff + (2 * c + 1) * kWideSeg + 64 * yb];
             }
 #pragma unroll
-            for (int yb = 0; yb < kWideNB; ++yb)
+            for (int yb = 0; yb < NB; ++yb)
                 acc[yb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0[yb], acc[yb], 0, 0, 0);
 #pragma unroll
-            for (int yb = 0; yb < kWideNB; ++yb)
+            for (int yb = 0; yb < NB; ++yb)
                 acc[yb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1[yb], acc[yb], 0, 0, 0);
         }
     }
@@ -614,7 +619,7 @@ wide_fwd_kernel(PArgs a, int ntot)
     // D block yb: register 4 q + r holds row 8 q + 4 hi + r of the wave's 32, column l32
     const int pmax = a.ph_l > a.ph_r ? a.ph_l : a.ph_r;
 #pragma unroll
-    for (int yb = 0; yb < kWideNB; ++yb) {
+    for (int yb = 0; yb < NB; ++yb) {
         const int gp = n0 + 32 * yb + l32;
         if (gp >= ntot) continue;
         const int img = gp / a.P, pl = gp - img * a.P;
@@ -1443,13 +1448,34 @@ static void set_push(PArgs& a, const Push* push)
 // per-image tiles balance as well or better.  The environment variable
 // (SSCNN_PATCH_FWD for the forward) set to wide forces them wherever they
 // apply, set to tiled never.
-static int wide_fwd_tiles(const PArgs& a)
+static int wide_fwd_tiles(const PArgs& a, int nb = kWideNB)
 {
     const int64_t ntot = (int64_t)a.N * a.P;
     if (a.Kt != 4 * a.Ci || a.Ci % 4 || (int64_t)a.N * a.Ci * a.H * a.W * 4 >= ((int64_t)1 << 31) ||
         (int64_t)(a.Co + kWideTM) * a.Kt * 4 >= ((int64_t)1 << 31) || ntot >= ((int64_t)1 << 31))
         return 0;
-    return (int)(((a.Co + kWideTM - 1) / kWideTM) * ((ntot + kWideTN - 1) / kWideTN));
+    return (int)(((a.Co + kWideTM - 1) / kWideTM) * ((ntot + 32 * nb - 1) / (32 * nb)));
+}
+
+static int cu_count()
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return cus > 0 ? cus : 256;
+}
+
+// 128-pixel wide forward tiles (NB = 4) where 224-pixel ones would leave
+// CUs without a tile and the 128-pixel ones still fit in one round
+// (SSCNN_PATCH_FWD=wide4 forces them, =wide or =tiled the other forms).
+static bool use_wide4(const PArgs& a)
+{
+    const int t7 = wide_fwd_tiles(a, 7), t4 = wide_fwd_tiles(a, 4);
+    if (t7 == 0) return false;
+    const char* env = getenv("SSCNN_PATCH_FWD");
+    if (env && !strcmp(env, "wide4")) return true;
+    if (env && (!strcmp(env, "wide") || !strcmp(env, "tiled"))) return false;
+    const int cus = cu_count();
+    return t7 < cus && t4 <= cus;
 }
 
 // The stem kernel (stem_fwd_kernel): 4x4/4 layers on 3 input channels whose
@@ -1491,10 +1517,15 @@ hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const
         else hipLaunchKernelGGL((stem_fwd_kernel<3, false>), dim3(grid), dim3(kStemNT), 0, st, a, a.N * a.P);
         return hipGetLastError();
     }
+    if (g.k == 2 && use_wide4(a)) {
+        a.tiles_m = (a.Co + kWideTM - 1) / kWideTM;
+        hipLaunchKernelGGL(wide_fwd_kernel<4>, dim3(wide_fwd_tiles(a, 4)), dim3(kNT), 0, st, a, a.N * a.P);
+        return hipGetLastError();
+    }
     if (g.k == 2 && use_wide(wide_fwd_tiles(a), "SSCNN_PATCH_FWD")) {
         a.tiles_m = (a.Co + kWideTM - 1) / kWideTM;
         const int grid = wide_fwd_tiles(a);
-        hipLaunchKernelGGL(wide_fwd_kernel, dim3(grid), dim3(kNT), 0, st, a, a.N * a.P);
+        hipLaunchKernelGGL(wide_fwd_kernel<kWideNB>, dim3(grid), dim3(kNT), 0, st, a, a.N * a.P);
         return hipGetLastError();
     }
     a.tiles_n = (a.P + 127) / 128;

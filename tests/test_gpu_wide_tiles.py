@@ -5,8 +5,10 @@ The forward and the grad_input of a k = s = 2 layer can run as one product
 over the pixels of all the images, in tiles of 128 rows (output channels,
 or K = (ci, kh, kw)) x 224 pixels that may straddle two images.  The library
 picks them when the tile count is a whole multiple of the CU count (the
-ConvNeXt-style stack's downsamples); SSCNN_PATCH_FWD / SSCNN_PATCH_BWI=wide
-force them wherever they apply and =tiled switch them off, so these cases
+ConvNeXt-style stack's downsamples), and 128-pixel forward tiles where the
+224-pixel ones would be fewer than the CUs; SSCNN_PATCH_FWD=wide / =wide4 /
+SSCNN_PATCH_BWI=wide force them wherever they apply and =tiled switch them
+off, so these cases
 run both forms on shapes chosen for their edges: channel counts that are not
 a multiple of 128 rows, pixel counts that are not a multiple of 224, tiles
 that straddle images, a single image, and the push form of the halo
@@ -54,10 +56,11 @@ def _fwd(monkeypatch, mode, conv, x, wd, bd, push=None):
     return y
 
 
+@pytest.mark.parametrize("wmode", ["wide", "wide4"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_wide_forward_matches_oracle_and_tiled(case, monkeypatch):
+def test_wide_forward_matches_oracle_and_tiled(case, wmode, monkeypatch):
     name, n, ci, co, h, w, S = case
-    _say(f"  wide fwd {name}: ({n},{ci},{h},{w}) -> {co} channels, {S} shards")
+    _say(f"  wide fwd {name} ({wmode}): ({n},{ci},{h},{w}) -> {co} channels, {S} shards")
     rng = np.random.default_rng(4700 + CASES.index(case))
     x = rng.standard_normal((n, ci, h, w)).astype(np.float32)
     wt = (rng.standard_normal((co, ci, 2, 2)) * 0.05).astype(np.float32)
@@ -72,10 +75,10 @@ def test_wide_forward_matches_oracle_and_tiled(case, monkeypatch):
     ys_wide, halos = [], [torch.full(c.halo_shape(sscnn.HALO_INPUT), float("nan"), device="cuda") for c in cons]
     nb = lambda lst, s: (lst[s - 1] if s > 0 else None, lst[s + 1] if s < S - 1 else None)
     for s in range(S):
-        y_wide = _fwd(monkeypatch, "wide", convs[s], xs[s], wd, bd)
+        y_wide = _fwd(monkeypatch, wmode, convs[s], xs[s], wd, bd)
         y_tiled = _fwd(monkeypatch, "tiled", convs[s], xs[s], wd, bd)
         p = sscnn.make_push(cons[s], sscnn.HALO_INPUT, *nb(halos, s), halos[s])
-        y_push = _fwd(monkeypatch, "wide", convs[s], xs[s], wd, bd, push=p)
+        y_push = _fwd(monkeypatch, wmode, convs[s], xs[s], wd, bd, push=p)
         torch.cuda.synchronize()
         ref = y_full[:, :, :, s * wol:(s + 1) * wol]
         assert_close(host(y_wide), ref, TOL_FWD, f"{name} shard {s}: wide forward vs oracle")
