@@ -104,32 +104,67 @@ __device__ __forceinline__ void place(TileIdx& d, const DwArgs& a, int trow, int
     d.j0 = tcol * tw;
 }
 
-// Plane-major order (forward and grad_input): t = (plane, row, column).
-__device__ __forceinline__ TileIdx decode_plane_major(const DwArgs& a, int t, int th, int tw)
+// A tile number as four mixed-radix digits (d0 fastest): plane-major order
+// (forward and grad_input) is t = (n, c, row, column), channel-major order
+// (grad_weight, fused backward) t = (c, n, row, column), so that a
+// contiguous run of tiles mostly stays on one channel.  The digits are split
+// once per workgroup and then advanced by carries: the runtime divisions of
+// a decode cost ~20 scalar instructions each, which a wave would otherwise
+// issue on every tile in place of its FMAs.
+struct TileDigits {
+    int d0, d1, d2, d3;     // column tile, row tile, then (c, n) or (n, c)
+};
+
+__device__ __forceinline__ TileDigits split_tile(int t, int r0, int r1, int r2)
+{
+    TileDigits g;
+    g.d0 = t % r0;
+    t /= r0;
+    g.d1 = t % r1;
+    t /= r1;
+    g.d2 = t % r2;
+    g.d3 = t / r2;
+    return g;
+}
+
+// a + g digit by digit with carries (every digit of both below its radix, so
+// one subtraction per digit suffices).
+__device__ __forceinline__ TileDigits add_tile(TileDigits a, const TileDigits& g, int r0, int r1, int r2)
+{
+    int x = a.d0 + g.d0;
+    int cy = x >= r0;
+    a.d0 = cy ? x - r0 : x;
+    x = a.d1 + g.d1 + cy;
+    cy = x >= r1;
+    a.d1 = cy ? x - r1 : x;
+    x = a.d2 + g.d2 + cy;
+    cy = x >= r2;
+    a.d2 = cy ? x - r2 : x;
+    a.d3 += g.d3 + cy;
+    return a;
+}
+
+// The next tile, one step along the list.
+__device__ __forceinline__ TileDigits next_tile(TileDigits a, int r0, int r1, int r2)
+{
+    return add_tile(a, TileDigits{1, 0, 0, 0}, r0, r1, r2);
+}
+
+__device__ __forceinline__ TileIdx plane_major_idx(const DwArgs& a, const TileDigits& g, int th, int tw)
 {
     TileIdx d;
-    const int tcol = t % a.tiles_w;
-    t /= a.tiles_w;
-    const int trow = t % a.tiles_h;
-    const int plane = t / a.tiles_h;
-    d.c = plane % a.C;
-    d.n = plane / a.C;
-    place(d, a, trow, tcol, th, tw);
+    d.c = g.d2;
+    d.n = g.d3;
+    place(d, a, g.d1, g.d0, th, tw);
     return d;
 }
 
-// Channel-major order (grad_weight): t = (c, n, row, column), so a
-// contiguous run of tiles mostly stays on one channel.
-__device__ __forceinline__ TileIdx decode_channel_major(const DwArgs& a, int t, int th, int tw)
+__device__ __forceinline__ TileIdx channel_major_idx(const DwArgs& a, const TileDigits& g, int th, int tw)
 {
     TileIdx d;
-    const int tcol = t % a.tiles_w;
-    t /= a.tiles_w;
-    const int trow = t % a.tiles_h;
-    t /= a.tiles_h;
-    d.n = t % a.N;
-    d.c = t / a.N;
-    place(d, a, trow, tcol, th, tw);
+    d.n = g.d2;
+    d.c = g.d3;
+    place(d, a, g.d1, g.d0, th, tw);
     return d;
 }
 
@@ -428,8 +463,7 @@ dw_conv_kernel(DwArgs a)
     const int tid = threadIdx.x;
     const int tx = tid % TX, ty = tid / TX;
     const int64_t HW = (int64_t)a.H * a.W;
-    auto issue = [&](int t, float* b) {
-        const TileIdx e = decode_plane_major(a, t, T::TH, T::TW);
+    auto issue = [&](const TileIdx& e, float* b) {
         const RowHalo rh = ROWH ? row_halo(a.src_rh, e.plane, a.src_up, a.src_down, a.W) : RowHalo{};
         T::template load_main<ROWH>(b, a.src + e.plane * HW, a.H, a.W, e.i0, e.j0, tid, rh);
         T::template load_side<HALO, ROWH>(S, a.src + e.plane * HW,
@@ -438,21 +472,30 @@ dw_conv_kernel(DwArgs a)
     };
     int t = blockIdx.x;
     if (t >= a.ntiles) return;
-    issue(t, buf[0]);
+    // Tiles t, t + G, t + 2G, ... (G = gridDim.x): the digits of t and of the
+    // stride G are split once, then added.
+    TileDigits cur = split_tile(t, a.tiles_w, a.tiles_h, a.C);
+    const TileDigits step = split_tile(gridDim.x, a.tiles_w, a.tiles_h, a.C);
+    issue(plane_major_idx(a, cur, T::TH, T::TW), buf[0]);
     // A tile's stores are issued after the next tile's barrier, so the wait
     // before that barrier only covers operations a whole tile old.
     float acc[RH][4];
     TileIdx dprev{};
+    float wr[K * K];
+    int wc = -1;                     // channel whose weights wr holds
     for (int it = 0; t < a.ntiles; t += gridDim.x, ++it) {
         float* cb = buf[it & 1];
-        const TileIdx d = decode_plane_major(a, t, T::TH, T::TW);
+        const TileIdx d = plane_major_idx(a, cur, T::TH, T::TW);
+        cur = add_tile(cur, step, a.tiles_w, a.tiles_h, a.C);
         T::put_side(cb, S, tid);
         wait_vmem();
         lds_barrier();
         if (it > 0) store_rows<RH>(a.out, dprev, a.H, a.W, tx, ty, acc);
-        if (t + (int)gridDim.x < a.ntiles) issue(t + gridDim.x, buf[(it + 1) & 1]);
-        float wr[K * K];
-        load_weights<K, FLIP>(a.w, d.c, wr);
+        if (t + (int)gridDim.x < a.ntiles) issue(plane_major_idx(a, cur, T::TH, T::TW), buf[(it + 1) & 1]);
+        if (d.c != wc) {             // consecutive tiles often share a channel
+            load_weights<K, FLIP>(a.w, d.c, wr);
+            wc = d.c;
+        }
         const float bias = a.b ? as_const(a.b)[d.c] : 0.f;
 #pragma unroll
         for (int i = 0; i < RH; ++i)
@@ -519,8 +562,7 @@ dw_wgrad_kernel(DwArgs a)
     const int beg = (int)((int64_t)blockIdx.x * a.ntiles / G);
     const int end = (int)((int64_t)(blockIdx.x + 1) * a.ntiles / G);
     if (beg >= end) return;
-    auto issue = [&](int t, float* b) {
-        const TileIdx e = decode_channel_major(a, t, T::TH, T::TW);
+    auto issue = [&](const TileIdx& e, float* b) {
         const RowHalo rh = ROWH ? row_halo(a.x_rh, e.plane, a.x_up, a.x_down, a.W) : RowHalo{};
         T::template load_main<ROWH>(b, a.x + e.plane * HW, a.H, a.W, e.i0, e.j0, tid, rh);
         T::template load_side<HALO, ROWH>(S, a.x + e.plane * HW,
@@ -535,10 +577,11 @@ dw_wgrad_kernel(DwArgs a)
             gnext[i].x *= m; gnext[i].y *= m; gnext[i].z *= m; gnext[i].w *= m;
         }
     };
-    issue(beg, buf[0]);
+    TileDigits cur = split_tile(beg, a.tiles_w, a.tiles_h, a.N);    // tile t, channel-major
+    issue(channel_major_idx(a, cur, T::TH, T::TW), buf[0]);
     int it = 0;
     for (int t = beg; t < end;) {
-        const int c = t / tiles_c;
+        const int c = cur.d3;
         const int run_end = min(end, (c + 1) * tiles_c);
         float acc[NV];
 #pragma unroll
@@ -554,7 +597,8 @@ dw_wgrad_kernel(DwArgs a)
             }
             wait_vmem();
             lds_barrier();
-            if (t + 1 < end) issue(t + 1, buf[(it + 1) & 1]);
+            cur = next_tile(cur, a.tiles_w, a.tiles_h, a.N);
+            if (t + 1 < end) issue(channel_major_idx(a, cur, T::TH, T::TW), buf[(it + 1) & 1]);
             wgrad_tile<K, TX, TY, RH>(cb, gv, acc, tx, ty);
         }
         flush_write<NV, NWAVE>(acc, red, tid);
@@ -596,33 +640,34 @@ dw_bwd_kernel(DwArgs a)
     const float* const src_rh = wgrad_half ? a.x_rh : a.src_rh;
     const int up = wgrad_half ? a.x_up : a.src_up, down = wgrad_half ? a.x_down : a.src_down;
     float (*const mybuf)[T::FLOATS] = wgrad_half ? bufx : bufg;
-    auto issue = [&](int t, float* b) {
-        const TileIdx e = decode_channel_major(a, t, T::TH, T::TW);
+    auto issue = [&](const TileIdx& e, float* b) {
         const RowHalo rh = ROWH ? row_halo(src_rh, e.plane, up, down, a.W) : RowHalo{};
         T::template load_main<ROWH>(b, src + e.plane * HW, a.H, a.W, e.i0, e.j0, tid, rh);
         T::template load_side<HALO, ROWH>(S, src + e.plane * HW,
                                           col_halo<HALO, ROWH>(src_h, e.plane, a.H, up, down, P), a.H, a.W,
                                           e.i0, e.j0, tid, rh);
     };
-    issue(beg, mybuf[0]);
+    TileDigits cur = split_tile(beg, a.tiles_w, a.tiles_h, a.N);    // tile t, channel-major
+    issue(channel_major_idx(a, cur, T::TH, T::TW), mybuf[0]);
 
     if (!wgrad_half) {
         int it = 0;
         float acc[RH][4];
         TileIdx dprev{};
         for (int t = beg; t < end;) {
-            const int c = t / tiles_c;
+            const int c = cur.d3;
             const int run_end = min(end, (c + 1) * tiles_c);
             float wr[KK];
             load_weights<K, true>(a.w, c, wr);
             for (; t < run_end; ++t, ++it) {
                 float* cb = bufg[it & 1];
-                const TileIdx d = decode_channel_major(a, t, T::TH, T::TW);
+                const TileIdx d = channel_major_idx(a, cur, T::TH, T::TW);
+                cur = next_tile(cur, a.tiles_w, a.tiles_h, a.N);
                 T::put_side(cb, S, tid);
                 wait_vmem();
                 lds_barrier();
                 if (it > 0) store_rows<RH>(a.out, dprev, a.H, a.W, tx, ty, acc);   // previous tile's
-                if (t + 1 < end) issue(t + 1, bufg[(it + 1) & 1]);
+                if (t + 1 < end) issue(channel_major_idx(a, cur, T::TH, T::TW), bufg[(it + 1) & 1]);
 #pragma unroll
                 for (int i = 0; i < RH; ++i)
 #pragma unroll
@@ -636,18 +681,19 @@ dw_bwd_kernel(DwArgs a)
     } else {
         int it = 0;
         for (int t = beg; t < end;) {
-            const int c = t / tiles_c;
+            const int c = cur.d3;
             const int run_end = min(end, (c + 1) * tiles_c);
             float acc[NV];
 #pragma unroll
             for (int k = 0; k < NV; ++k) acc[k] = 0.f;
             for (; t < run_end; ++t, ++it) {
                 float* cb = bufx[it & 1];
-                const TileIdx d = decode_channel_major(a, t, T::TH, T::TW);
+                const TileIdx d = channel_major_idx(a, cur, T::TH, T::TW);
+                cur = next_tile(cur, a.tiles_w, a.tiles_h, a.N);
                 T::put_side(cb, S, tid);
                 wait_vmem();
                 lds_barrier();
-                if (t + 1 < end) issue(t + 1, bufx[(it + 1) & 1]);
+                if (t + 1 < end) issue(channel_major_idx(a, cur, T::TH, T::TW), bufx[(it + 1) & 1]);
                 // grad_output at the thread's outputs: the centre of this
                 // tile's grad_output buffer (main region row P + i, column j)
                 float gv[RH][4];
