@@ -44,6 +44,13 @@
 namespace sscnn {
 namespace {
 
+// Outputs leave with non-temporal stores (the buffer-store cache-policy bit
+// for it, and __builtin_nontemporal_store): no kernel here reads them back,
+// and streaming them past the caches measured faster for the bandwidth-heavy
+// epilogues.
+constexpr int kNonTemporal = 2;
+typedef float f2v __attribute__((ext_vector_type(2)));
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kNT = 256;
@@ -633,7 +640,7 @@ wide_fwd_kernel(PArgs a, int ntot)
                 const int row = m0 + 32 * wave + 8 * q + 4 * hi + r;
                 if (row < a.Co) {
                     const float v = acc[yb][4 * q + r] + bias_s[row - m0];
-                    yp[(int64_t)row * a.P] = v;
+                    __builtin_nontemporal_store(v, yp + (int64_t)row * a.P);
                     if (edge) push_value(a, (int64_t)img * a.Co + row, a.Ho, pi, pj, a.Wo, v);
                 }
             }
@@ -746,7 +753,8 @@ wide_bwi_kernel(PArgs a, int ntot)
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 const float v0 = acc[yb][4 * q + 2 * kh], v1 = acc[yb][4 * q + 2 * kh + 1];
-                *reinterpret_cast<float2*>(dxi + ((int64_t)ci * a.H + 2 * i + kh) * a.W + 2 * j) = make_float2(v0, v1);
+                const f2v v01 = {v0, v1};
+                __builtin_nontemporal_store(v01, reinterpret_cast<f2v*>(dxi + ((int64_t)ci * a.H + 2 * i + kh) * a.W + 2 * j));
                 if (edge) {
                     push_value(a, (int64_t)img * a.Ci + ci, a.H, 2 * i + kh, 2 * j, a.W, v0);
                     push_value(a, (int64_t)img * a.Ci + ci, a.H, 2 * i + kh, 2 * j + 1, a.W, v1);
@@ -1002,7 +1010,8 @@ stem_fwd_kernel(PArgs a, int ntot)
                     const int cu = 32 * wave + 8 * q + r;
                     if (cu + 4 * hi < a.Co)
                         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[y][4 * q + r] + bias_s[cu + 4 * hi]),
-                                                              ry, voff, __builtin_amdgcn_readfirstlane(cu * a.P * 4), 0);
+                                                              ry, voff, __builtin_amdgcn_readfirstlane(cu * a.P * 4),
+                                                              kNonTemporal);
                 }
             if (PUSH) {
                 // the push of push_value, through buffer resources (a missing buffer has no
@@ -1122,8 +1131,8 @@ stem_bwi_kernel(PArgs a, int ntot)
         const int i = pl / a.Wo, j = pl - i * a.Wo;
 #pragma unroll
         for (int m = 0; m < 3; ++m)
-            *reinterpret_cast<float4*>(a.out + (((int64_t)(img * 3 + m) * a.H + 4 * i + lq) * a.W + 4 * j)) =
-                make_float4(acc[m][h][0], acc[m][h][1], acc[m][h][2], acc[m][h][3]);
+            __builtin_nontemporal_store(acc[m][h], reinterpret_cast<f32x4*>(
+                                                       a.out + (((int64_t)(img * 3 + m) * a.H + 4 * i + lq) * a.W + 4 * j)));
     }
 }
 
