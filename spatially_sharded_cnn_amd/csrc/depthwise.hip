@@ -722,7 +722,11 @@ dw_bwd_kernel(DwArgs a)
 
 // Second pass: grad_w[c, tap] = sum of channel c's partials in workgroup
 // order (one per workgroup whose run of tiles meets the channel).
-template <int K>
+// The owners are computed in 32-bit arithmetic (U32) whenever
+// (ntiles + 1) * grid fits in 32 bits, as it does for every layer here: the
+// 64-bit division is a long software sequence that dominated this small
+// kernel.
+template <int K, bool U32>
 __global__ void __launch_bounds__(256)
 dw_wgrad_reduce_kernel(const float* __restrict__ ws, int C, int tiles_c, int64_t ntiles, int64_t grid,
                        float* __restrict__ gw, float* __restrict__ gb)
@@ -731,8 +735,15 @@ dw_wgrad_reduce_kernel(const float* __restrict__ ws, int C, int tiles_c, int64_t
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= C * NV) return;
     const int c = idx / NV, t = idx - c * NV;
-    const int64_t w0 = tile_owner((int64_t)c * tiles_c, ntiles, grid);
-    const int64_t w1 = tile_owner((int64_t)(c + 1) * tiles_c - 1, ntiles, grid);
+    int64_t w0, w1;
+    if constexpr (U32) {
+        const uint32_t T = (uint32_t)ntiles, G = (uint32_t)grid;
+        w0 = (((uint32_t)c * tiles_c + 1) * G - 1) / T;
+        w1 = (((uint32_t)(c + 1) * tiles_c) * G - 1) / T;
+    } else {
+        w0 = tile_owner((int64_t)c * tiles_c, ntiles, grid);
+        w1 = tile_owner((int64_t)(c + 1) * tiles_c - 1, ntiles, grid);
+    }
     const float* p = ws + (int64_t)c * tiles_c * NV + t;
     float s = 0.f;
     for (int64_t k = 0; k <= w1 - w0; ++k) s += p[k * NV];
@@ -799,8 +810,12 @@ hipError_t launch_reduce(const DwArgs& a, int grid, float* gw, float* gb, hipStr
 {
     const int tiles_c = a.ntiles / a.C;
     const int total = a.C * (K * K + 1);
-    hipLaunchKernelGGL((dw_wgrad_reduce_kernel<K>), dim3((total + 255) / 256), dim3(256), 0, st, a.ws, a.C,
-                       tiles_c, (int64_t)a.ntiles, (int64_t)grid, gw, gb);
+    if (((int64_t)a.ntiles + 1) * grid < ((int64_t)1 << 32))
+        hipLaunchKernelGGL((dw_wgrad_reduce_kernel<K, true>), dim3((total + 255) / 256), dim3(256), 0, st, a.ws,
+                           a.C, tiles_c, (int64_t)a.ntiles, (int64_t)grid, gw, gb);
+    else
+        hipLaunchKernelGGL((dw_wgrad_reduce_kernel<K, false>), dim3((total + 255) / 256), dim3(256), 0, st, a.ws,
+                           a.C, tiles_c, (int64_t)a.ntiles, (int64_t)grid, gw, gb);
     return hipGetLastError();
 }
 
