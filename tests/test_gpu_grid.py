@@ -33,6 +33,7 @@ CASES = [
     ("dw3_3x3", 1, 6, 6, 3 * 16, 3 * 16, 3, 1, 1, 6, 3, 3),
     ("dw5_2x3_tall", 1, 4, 4, 2 * 40, 3 * 64, 5, 1, 2, 4, 2, 3),
     ("dw7_2x2_64rows", 1, 4, 4, 2 * 64, 2 * 64, 7, 1, 3, 4, 2, 2),     # 64-row blocks: 4 rows per thread
+    ("dw7_2x2_w32_h45", 1, 4, 4, 2 * 45, 2 * 32, 7, 1, 3, 4, 2, 2),    # 32-wide blocks, 32-row tiles, ragged rows
     ("patch2_2x2_no_halo", 1, 16, 32, 2 * 8, 2 * 32, 2, 2, 0, 1, 2, 2),
     ("pw1x1_2x2_no_halo", 2, 16, 48, 2 * 8, 2 * 32, 1, 1, 0, 1, 2, 2),
     # dense layers on the matrix cores, reading both halos (the 5x5 pad-2 example of the pages)

@@ -34,6 +34,8 @@ CASES = [
     ("dw7", 2, 16, 16, 4 * 16, 64, 7, 1, 3, 16, 4),
     ("dw3", 1, 8, 8, 4 * 8, 48, 3, 1, 1, 8, 4),
     ("dw7_64rows", 1, 4, 4, 2 * 64, 128, 7, 1, 3, 4, 2),    # 64-row slices: 4 rows per thread, 2 column tiles
+    ("dw5_w32_rows24", 1, 6, 6, 2 * 24, 32, 5, 1, 2, 6, 2),   # 32 wide: 16-row tiles, the last moved up
+    ("dw7_w32_rows40", 1, 5, 5, 2 * 40, 32, 7, 1, 3, 5, 2),   # 32 wide: 32-row tiles, the last moved up
     ("dw5_w40_direct", 1, 6, 6, 3 * 10, 40, 5, 1, 2, 6, 3),
     ("mfma5x5", 1, 24, 32, 2 * 12, 64, 5, 1, 2, 1, 2),
     ("mfma3x3", 1, 16, 20, 3 * 8, 32, 3, 1, 1, 1, 3),

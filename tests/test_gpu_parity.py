@@ -45,6 +45,11 @@ SMALL = [
     ("dw7_h16_w16", 2, 24, 24, 16, 4 * 16, 7, 1, 3, 24, 4),
     ("dw7_h16_w32", 2, 12, 12, 16, 3 * 32, 7, 1, 3, 12, 3),
     ("dw5_h20_w16", 1, 9, 9, 20, 2 * 16, 5, 1, 2, 9, 2),
+    # 32-wide slices 16..63 rows high (two rows per thread in 32- and 16-row tiles), with a
+    # last row tile moved up over its neighbour: rows 45 = 32 + 13, 20 = 16 + 4, 33 = 32 + 1
+    ("dw7_w32_h45", 2, 11, 11, 45, 3 * 32, 7, 1, 3, 11, 3),
+    ("dw5_w32_h20", 1, 9, 9, 20, 2 * 32, 5, 1, 2, 9, 2),
+    ("dw3_w32_h33", 2, 6, 6, 33, 2 * 32, 3, 1, 1, 6, 2),
     # widths that are multiples of 64 (the register-window kernels): k = 3, a slice
     # of three 64-column blocks with a ragged strip group, a plane under one strip
     ("dw3_w64", 2, 6, 6, 23, 2 * 64, 3, 1, 1, 6, 2),
