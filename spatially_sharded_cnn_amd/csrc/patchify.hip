@@ -770,8 +770,12 @@ wide_bwi_kernel(PArgs a, int ntot)
 // reduction is split into `splits` ranges of 16-pixel chunks (a chunk lies in
 // one output row of one image), so that tiles x splits is a multiple of the
 // CU count; with one split the sums go straight to grad_weight, otherwise to
-// per-split slabs that slab_sum_kernel adds in split order.  A stage is one
-// chunk, loaded one stage ahead:
+// per-split slabs that slab_sum_kernel adds in split order.  A stage is two
+// chunks (64 KB of LDS for the two stages in flight, which the two
+// workgroups per CU that the split count aims for still fit; against one
+// chunk per stage, half the barriers per product: c5 downsample backward
+// 978/939/919 -> 953/930/908 us, same box), loaded one stage ahead; each
+// chunk's operands:
 //   A  G[img][m0 + m][the chunk's 16 pixels]: 128 rows of 4 units, unit u of
 //      row m at slot u ^ ((m >> 2) & 3);
 //   B  x[img][ci][2 i + kh][2 j0 .. 2 j0 + 31] for the tile's 32 input
@@ -789,7 +793,8 @@ constexpr int kBwwAF = 128 * 16, kBwwBF = 64 * 32, kBwwST = kBwwAF + kBwwBF;
 __global__ void __launch_bounds__(kNT, 2)
 dma_bww_kernel(PArgs a)
 {
-    __shared__ __align__(16) float lds[2 * kBwwST];
+    constexpr int CPS = 2;   // chunks per stage
+    __shared__ __align__(16) float lds[2 * CPS * kBwwST];
     int bid = xcd_order(blockIdx.x, gridDim.x);   // output-channel tiles of one (K tile, split) side by side
     const int mt = bid % a.tiles_m;
     bid /= a.tiles_m;
@@ -813,17 +818,22 @@ dma_bww_kernel(PArgs a)
         bvoff[i] = ci < a.Ci ? ((ci * a.H + kh) * a.W + 4 * ub) * 4 : (int)0x80000000;
     }
     // chunk c: its first pixel's image, row and column give the two operands' byte offsets
-    auto issue = [&](int s) {
-        const int gp = 16 * (c_beg + s);
-        const int img = gp / a.P, pl = gp - img * a.P;
-        const int i = pl / a.Wo, j0 = pl - i * a.Wo;
-        const int abase = (img * a.Co * a.P + pl) * 4;
-        const int bbase = ((img * a.Ci * a.H + 2 * i) * a.W + 2 * j0) * 4;
-        float* st = lds + (s & 1) * kBwwST;
+    auto issue = [&](int s) {          // stage s: chunks CPS s .. CPS s + CPS - 1 (those below nst)
 #pragma unroll
-        for (int k = 0; k < 2; ++k) dma16(ra, st + (2 * wave + k) * 256, avoff[k] + abase);
+        for (int cc = 0; cc < CPS; ++cc) {
+            const int ch = CPS * s + cc;
+            if (ch >= nst) break;
+            const int gp = 16 * (c_beg + ch);
+            const int img = gp / a.P, pl = gp - img * a.P;
+            const int i = pl / a.Wo, j0 = pl - i * a.Wo;
+            const int abase = (img * a.Co * a.P + pl) * 4;
+            const int bbase = ((img * a.Ci * a.H + 2 * i) * a.W + 2 * j0) * 4;
+            float* st = lds + ((s & 1) * CPS + cc) * kBwwST;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) dma16(rb, st + kBwwAF + (2 * wave + k) * 256, bvoff[k] + bbase);
+            for (int k = 0; k < 2; ++k) dma16(ra, st + (2 * wave + k) * 256, avoff[k] + abase);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) dma16(rb, st + kBwwAF + (2 * wave + k) * 256, bvoff[k] + bbase);
+        }
     };
 
     const int hi = lane >> 5, l32 = lane & 31;
@@ -846,43 +856,48 @@ dma_bww_kernel(PArgs a)
         bseg[y] = kBwwAF + 32 * (2 * (n >> 2) + ((n >> 1) & 1)) + (n & 1);
     }
 
-    if (nst > 0) issue(0);
-    for (int s = 0; s < nst; ++s) {
+    const int nstg = (nst + CPS - 1) / CPS;
+    if (nstg > 0) issue(0);
+    for (int s = 0; s < nstg; ++s) {
         wait_vmem();
         lds_barrier();
-        if (s + 1 < nst) issue(s + 1);
-        const float* st = lds + (s & 1) * kBwwST;
-        if (with_bias && t < 128) {
-            const int bs = (t >> 2) & 3;
+        if (s + 1 < nstg) issue(s + 1);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float4 v = *reinterpret_cast<const float4*>(st + 16 * t + 4 * (u ^ bs));
-                bias_acc += v.x; bias_acc += v.y; bias_acc += v.z; bias_acc += v.w;
-            }
-        }
+        for (int cc = 0; cc < CPS; ++cc) {
+            if (CPS * s + cc >= nst) break;
+            const float* st = lds + ((s & 1) * CPS + cc) * kBwwST;
+            if (with_bias && t < 128) {
+                const int bs = (t >> 2) & 3;
 #pragma unroll
-        for (int tg = 0; tg < 2; ++tg) {
-            float4 av[2];
-#pragma unroll
-            for (int x = 0; x < 2; ++x)
-                av[x] = *reinterpret_cast<const float4*>(st + 16 * (64 * wm + 32 * x + l32) + 4 * ((2 * tg + hi) ^ asw));
-            float bv[2][4];
-#pragma unroll
-            for (int y = 0; y < 2; ++y)
-#pragma unroll
-                for (int d = 0; d < 2; ++d) {
-                    const float* bp = st + bseg[y] + 4 * ((4 * tg + 2 * hi + d) ^ bsw);
-                    bv[y][2 * d] = bp[0];
-                    bv[y][2 * d + 1] = bp[2];
+                for (int u = 0; u < 4; ++u) {
+                    const float4 v = *reinterpret_cast<const float4*>(st + 16 * t + 4 * (u ^ bs));
+                    bias_acc += v.x; bias_acc += v.y; bias_acc += v.z; bias_acc += v.w;
                 }
+            }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float a0 = e == 0 ? av[0].x : e == 1 ? av[0].y : e == 2 ? av[0].z : av[0].w;
-                const float a1 = e == 0 ? av[1].x : e == 1 ? av[1].y : e == 2 ? av[1].z : av[1].w;
+            for (int tg = 0; tg < 2; ++tg) {
+                float4 av[2];
 #pragma unroll
-                for (int y = 0; y < 2; ++y) {
-                    acc[0][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, bv[y][e], acc[0][y], 0, 0, 0);
-                    acc[1][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, bv[y][e], acc[1][y], 0, 0, 0);
+                for (int x = 0; x < 2; ++x)
+                    av[x] = *reinterpret_cast<const float4*>(st + 16 * (64 * wm + 32 * x + l32) + 4 * ((2 * tg + hi) ^ asw));
+                float bv[2][4];
+#pragma unroll
+                for (int y = 0; y < 2; ++y)
+#pragma unroll
+                    for (int d = 0; d < 2; ++d) {
+                        const float* bp = st + bseg[y] + 4 * ((4 * tg + 2 * hi + d) ^ bsw);
+                        bv[y][2 * d] = bp[0];
+                        bv[y][2 * d + 1] = bp[2];
+                    }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float a0 = e == 0 ? av[0].x : e == 1 ? av[0].y : e == 2 ? av[0].z : av[0].w;
+                    const float a1 = e == 0 ? av[1].x : e == 1 ? av[1].y : e == 2 ? av[1].z : av[1].w;
+#pragma unroll
+                    for (int y = 0; y < 2; ++y) {
+                        acc[0][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, bv[y][e], acc[0][y], 0, 0, 0);
+                        acc[1][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, bv[y][e], acc[1][y], 0, 0, 0);
+                    }
                 }
             }
         }
