@@ -209,7 +209,7 @@ struct Tile {
         const i32x4 rs = plane_rsrc(plane, H * W * 4);
         i32x4 rsh{};
         if constexpr (ROWH) rsh = plane_rsrc(rh.p, (rh.up + rh.down) * W * 4);
-        const int wave = tid >> 6, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 #pragma unroll
         for (int k = 0; k < (NLOAD + NWAVE - 1) / NWAVE; ++k) {
             const int m = wave + k * NWAVE;                    // wave-uniform

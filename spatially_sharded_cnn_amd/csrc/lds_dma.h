@@ -35,6 +35,18 @@ __device__ __forceinline__ void dma16(const i32x4& rs, const float* lds, int vof
                  :: "v"(voff), "s"(l), "s"(rs) : "memory", "m0");
 }
 
+// The same load with the LDS destination given as an LDS (address space 3)
+// pointer, whose value is the byte address itself; used where the compiler
+// fails to select the generic-to-LDS conversion of the form above.
+typedef __attribute__((address_space(3))) float lds_float;
+
+__device__ __forceinline__ void dma16_lds(const i32x4& rs, lds_float* lds, int voff)
+{
+    const int l = __builtin_amdgcn_readfirstlane((int)(uint32_t)reinterpret_cast<uintptr_t>(lds));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :: "v"(voff), "s"(l), "s"(rs) : "memory", "m0");
+}
+
 // Wait until at most N of this wave's vector memory operations are
 // outstanding (gfx9 s_waitcnt: vmcnt in bits 3:0, expcnt 6:4 and lgkmcnt
 // 11:8 left at their maxima, i.e. not waited for).

@@ -277,7 +277,7 @@ mfma_conv_kernel(MfArgs a)
     const int n = mt / a.tiles_h;
     const int o0 = ot * kBN, i0 = th * kTH, j0 = tw * kTW;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wo = 0, wp = wave;   // all 64 output channels, pixel row = wave
     const int lhalf = lane >> 5, l32 = lane & 31;
 

@@ -208,7 +208,7 @@ mfma_wgrad_kernel(WgArgs a)
     const int o0 = ot * kBO, c0 = ct * kBC;
     const bool do_bias = (ct == 0 && kh == 0);
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ob = wave >> 1, cb = wave & 1;
     const int lhalf = lane >> 5, l32 = lane & 31;
 

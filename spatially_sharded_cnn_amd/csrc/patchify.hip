@@ -369,7 +369,7 @@ patch_kernel(PArgs a)
         }
     };
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int hi = lane >> 5, l32 = lane & 31;
     f32x16 acc[XB][YB];
@@ -547,7 +547,7 @@ wide_fwd_kernel(PArgs a, int ntot)
     const int bid = xcd_order(blockIdx.x, gridDim.x);   // output-channel tiles of one pixel tile side by side
     const int mt = bid % a.tiles_m, nt = bid / a.tiles_m;
     const int m0 = mt * kWideTM, n0 = nt * TN;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     if (t < kWideTM) bias_s[t] = (a.b && m0 + t < a.Co) ? a.b[m0 + t] : 0.f;
     const int nstage = a.Ci / 4;
 
@@ -670,7 +670,7 @@ wide_bwi_kernel(PArgs a, int ntot)
     const int bid = xcd_order(blockIdx.x, gridDim.x);   // K tiles of one pixel tile side by side
     const int mt = bid % a.tiles_m, nt = bid / a.tiles_m;
     const int m0 = mt * kWideTM, n0 = nt * kWideTN;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int nstage = a.Co / 16;
 
     // A: instruction i of wave w fills rows kr = 2 (2 w + i) + lane / 32; lane's slot lane % 32
@@ -801,7 +801,7 @@ dma_bww_kernel(PArgs a)
     const int nt = bid % a.tiles_n;
     const int split = bid / a.tiles_n;
     const int m0 = mt * 128, n0 = nt * 128;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int c_beg = (int)((int64_t)split * a.chunks / a.splits);
     const int nst = (int)((int64_t)(split + 1) * a.chunks / a.splits) - c_beg;
 
@@ -924,7 +924,7 @@ dma_bww_kernel(PArgs a)
 }
 
 // Forward of a 4x4/4 stem (k = s = 4, CI input channels, 16 CI <= 64
-// reduction rows, at most 256 output channels).  Its reduction is too short
+// reduction rows, at most 256 output channels, a multiple of 8).  Its reduction is too short
 // to amortise staging a weight tile per pixel tile, so each workgroup of 8
 // waves keeps the weights in registers (wave w: output channels 32 w .. 32 w
 // + 31, as the MFMA A operand of all 8 CI k-steps) and walks pixel tiles of
@@ -935,10 +935,12 @@ dma_bww_kernel(PArgs a)
 // kw = kwp and k-slot 1 with kw = kwp + 2, so one 8-byte read per lane and
 // row serves two steps.  The epilogue stores 32 consecutive pixels per row
 // and instruction through a buffer resource (row offsets in scalar
-// registers); the push form's halo writes run only for the lanes holding
-// edge columns, after the block's stores.  The store-heavy epilogue is
-// overlapped by the other workgroups on the CU: a wave's wait for its next
-// tile's input also waits for its stores (one vector-memory counter).
+// registers, no store under a per-lane branch but the push's); the push
+// form's halo writes run only for the lanes holding edge columns, after the
+// block's stores.  A tile's stores are issued after the next tile's barrier:
+// a wave's wait for its next tile's input also waits for its own stores (one
+// vector-memory counter), so storing right after the products would put the
+// whole drain of the stores under that wait.
 constexpr int kStemNT = 512;
 
 template <int CI, bool PUSH>
@@ -947,8 +949,8 @@ stem_fwd_kernel(PArgs a, int ntot)
 {
     constexpr int ROWS = 4 * CI, TN = 64, SEG = 4 * TN, KS = 8 * CI;
     __shared__ __align__(16) float xs[2][ROWS * SEG];
-    __shared__ float bias_s[256];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    __shared__ __align__(16) float bias_s[256];
+    const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int hi = lane >> 5, l32 = lane & 31;
     const int ntiles = (ntot + TN - 1) / TN;
 
@@ -962,7 +964,7 @@ stem_fwd_kernel(PArgs a, int ntot)
 #pragma unroll
         for (int r = wave; r < ROWS; r += 8) {
             const int ci = r / 4, kh = r % 4;
-            dma16(rx, &xs[buf][r * SEG], base + ((ci * a.H + kh) * a.W) * 4);
+            dma16_lds(rx, (lds_float*)&xs[buf][r * SEG], base + ((ci * a.H + kh) * a.W) * 4);
         }
     };
 
@@ -983,15 +985,86 @@ stem_fwd_kernel(PArgs a, int ntot)
     const __amdgpu_buffer_rsrc_t hl = __builtin_amdgcn_make_buffer_rsrc(a.push_l, 0, a.push_l ? hbytes : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(a.push_r, 0, a.push_r ? hbytes : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t hown = __builtin_amdgcn_make_buffer_rsrc(a.push_own, 0, a.push_own ? hbytes : 0, 0x00020000);
-    if (tile < ntiles) issue(tile, 0);
     const int pmax = a.ph_l > a.ph_r ? a.ph_l : a.ph_r;
+    constexpr int kOut = (int)0x80000000;     // an offset beyond every buffer here: the store drops
+
+    // One tile's results.  D block y: register 4 q + r holds channel 32 w + 8 q + 4 hi + r, pixel
+    // 32 y + l32.  Stored through a buffer resource: the lane's part of the offset (image, 4 hi,
+    // pixel) in a vector register, the channel's part 4 P (32 w + 8 q + r) in a scalar one.  Lanes
+    // past the last pixel take an offset the buffer drops; the output channel count is a multiple
+    // of 8, so whether channels 32 w + 8 q .. + 7 exist is the same for the whole wave.
+    // The lane's 16 channels (32 w + 8 q + 4 hi + r at [4 q + r]) take their biases from LDS in four
+    // 16-byte reads per tile; the bias is added in place (the accumulators are cleared after the
+    // stores), so the halo pushes reuse the sums instead of holding a second copy of them.
+    auto store_tile = [&](int tl, f32x16 (&ac)[2]) {
+        float bl[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(&bias_s[32 * wave + 8 * q + 4 * hi]);
+            bl[4 * q] = v.x; bl[4 * q + 1] = v.y; bl[4 * q + 2] = v.z; bl[4 * q + 3] = v.w;
+        }
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+            const int gp = tl * TN + 32 * y + l32;
+            const bool live = gp < ntot;
+            const int img = gp / a.P, pl = gp - img * a.P;
+            const int voff = live ? ((img * a.Co + 4 * hi) * a.P + pl) * 4 : kOut;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) ac[y][k] += bl[k];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (32 * wave + 8 * q >= a.Co) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int cu = 32 * wave + 8 * q + r;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ac[y][4 * q + r]), ry, voff, cu * a.P * 4,
+                                                          kNonTemporal);
+                }
+            }
+            if (PUSH) {
+                // the push of push_value, through buffer resources (a missing buffer has no
+                // records, so its stores drop): the lane's column offsets into the left and right
+                // neighbours' halos and its own halo's two zeroed sides (or out of range)
+                const int pi = pl / a.Wo, pj = pl - pi * a.Wo;
+                if (live && (pj < pmax || pj >= a.Wo - pmax)) {
+                    const int hw = a.ph_l + a.ph_r;
+                    const int row0 = ((img * a.Co + 4 * hi) * a.Ho + pi) * hw;
+                    const int ol = a.push_l ? (pj < a.ph_r ? (row0 + a.ph_l + pj) * 4 : kOut)
+                                            : (pj < a.ph_l ? (row0 + pj) * 4 : kOut);
+                    const int rj = pj - (a.Wo - a.ph_l), oj = pj - (a.Wo - a.ph_r);
+                    const int orr = a.push_r ? (rj >= 0 ? (row0 + rj) * 4 : kOut)
+                                             : (oj >= 0 ? (row0 + a.ph_l + oj) * 4 : kOut);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (32 * wave + 8 * q >= a.Co) continue;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int cu = 32 * wave + 8 * q + r;
+                            const float v = ac[y][4 * q + r];
+                            const int so = cu * a.Ho * hw * 4;
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a.push_l ? v : 0.f),
+                                                                  a.push_l ? hl : hown, ol, so, 0);
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a.push_r ? v : 0.f),
+                                                                  a.push_r ? hr : hown, orr, so, 0);
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    // A tile's results are stored after the next tile's barrier, so that the stores drain while
+    // the waves compute that tile instead of under the wait for its input.
+    if (tile < ntiles) issue(tile, 0);
+    f32x16 acc[2];
+    int prev = -1;
     for (int it = 0; tile < ntiles; ++it, tile += gridDim.x) {
         const int buf = it & 1;
         wait_vmem();
         lds_barrier();
+        if (prev >= 0) store_tile(prev, acc);
+        __builtin_amdgcn_sched_barrier(0);   // the stores read acc before it is cleared
         if (tile + (int)gridDim.x < ntiles) issue(tile + gridDim.x, buf ^ 1);
-
-        f32x16 acc[2];
 #pragma unroll
         for (int y = 0; y < 2; ++y)
 #pragma unroll
@@ -1008,57 +1081,9 @@ stem_fwd_kernel(PArgs a, int ntot)
                 acc[y] = __builtin_amdgcn_mfma_f32_32x32x2f32(wa[2 * r + 1], bv[y].y, acc[y], 0, 0, 0);
             }
         }
-
-        // D block y: register 4 q + r holds channel 32 w + 8 q + 4 hi + r, pixel 32 y + l32.
-        // Stored through a buffer resource: the lane's part of the offset (image, 4 hi, pixel) in a
-        // vector register, the channel's part 4 P (32 w + 8 q + r) in a scalar one.
-#pragma unroll
-        for (int y = 0; y < 2; ++y) {
-            const int gp = tile * TN + 32 * y + l32;
-            if (gp >= ntot) continue;
-            const int img = gp / a.P, pl = gp - img * a.P;
-            const int voff = ((img * a.Co + 4 * hi) * a.P + pl) * 4;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int cu = 32 * wave + 8 * q + r;
-                    if (cu + 4 * hi < a.Co)
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[y][4 * q + r] + bias_s[cu + 4 * hi]),
-                                                              ry, voff, __builtin_amdgcn_readfirstlane(cu * a.P * 4),
-                                                              kNonTemporal);
-                }
-            if (PUSH) {
-                // the push of push_value, through buffer resources (a missing buffer has no
-                // records, so its stores drop): the lane's column offsets into the left and right
-                // neighbours' halos and its own halo's two zeroed sides (or out of range)
-                const int pi = pl / a.Wo, pj = pl - pi * a.Wo;
-                if (pj < pmax || pj >= a.Wo - pmax) {
-                    const int hw = a.ph_l + a.ph_r;
-                    const int row0 = ((img * a.Co + 4 * hi) * a.Ho + pi) * hw;
-                    constexpr int kOut = (int)0x80000000;
-                    const int ol = a.push_l ? (pj < a.ph_r ? (row0 + a.ph_l + pj) * 4 : kOut)
-                                            : (pj < a.ph_l ? (row0 + pj) * 4 : kOut);
-                    const int rj = pj - (a.Wo - a.ph_l), oj = pj - (a.Wo - a.ph_r);
-                    const int orr = a.push_r ? (rj >= 0 ? (row0 + rj) * 4 : kOut)
-                                             : (oj >= 0 ? (row0 + a.ph_l + oj) * 4 : kOut);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int cu = 32 * wave + 8 * q + r;
-                            if (cu + 4 * hi >= a.Co) continue;
-                            const float v = acc[y][4 * q + r] + bias_s[cu + 4 * hi];
-                            const int so = __builtin_amdgcn_readfirstlane(cu * a.Ho * hw * 4);
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a.push_l ? v : 0.f),
-                                                                  a.push_l ? hl : hown, ol, so, 0);
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a.push_r ? v : 0.f),
-                                                                  a.push_r ? hr : hown, orr, so, 0);
-                        }
-                }
-            }
-        }
+        prev = tile;
     }
+    if (prev >= 0) store_tile(prev, acc);
 }
 
 // grad_input of the 4x4/4 stem on 3 channels (K = 48): dXp[K][p] =
@@ -1080,7 +1105,7 @@ stem_bwi_kernel(PArgs a, int ntot)
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     __shared__ __align__(16) float lds[2 * kSiST];
     const int n0 = blockIdx.x * kSiTN;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int l16 = lane & 15, lq = lane >> 4;
     const int nstage = a.Co / 16;
 
@@ -1173,7 +1198,7 @@ stem_bww_kernel(PArgs a, float* slabs)
 {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     __shared__ __align__(16) float lds[2 * kSwST];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int l16 = lane & 15, lq = lane >> 4;
     const int c_beg = (int)((int64_t)blockIdx.x * a.chunks / gridDim.x);
     const int nst = (int)((int64_t)(blockIdx.x + 1) * a.chunks / gridDim.x) - c_beg;
@@ -1531,7 +1556,7 @@ hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const
     PArgs a = make_args(g);
     a.x = x; a.w = w; a.b = b; a.out = y; a.act = act;
     set_push(a, push);
-    if (g.k == 4 && g.ci == 3 && g.co <= 256 && use_stem_fwd(a)) {
+    if (g.k == 4 && g.ci == 3 && g.co <= 256 && g.co % 8 == 0 && use_stem_fwd(a)) {
         const int tiles = (int)(((int64_t)a.N * a.P + 63) / 64);
         int dev = 0, cus = 256;
         if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
