@@ -193,6 +193,8 @@ STEM_CASES = [
     ("stem_co256", 2, 256, 32, 4 * 128, 4),
     ("stem_co48_ragged_tiles", 3, 48, 24, 2 * 64, 2),     # 96 pixels per image: 64-pixel tiles straddle images
     ("stem_co96_one_row", 1, 96, 4, 4 * 64, 4),           # one output row per image
+    ("stem_co40_one_group", 2, 40, 16, 2 * 64, 2),        # wave 1 stores one group of 8 channels
+    ("stem_co20_other_path", 2, 20, 16, 2 * 64, 2),       # not a multiple of 8: the general kernels
 ]
 
 
