@@ -31,7 +31,8 @@ Algorithmic bytes:
 (halo copies are inside the timed step but not counted as useful bytes).
 
 `roofline` is for the dominant operation of the step, timed on its own over
-back-to-back calls with events on the stream the kernels run on; its bound is
+back-to-back calls with events on the stream the kernels run on (after
+OP_WARM_CALLS untimed calls of it); its bound is
 whichever of HBM bytes / 8 TB/s and FLOPs / compute peak is larger, with the
 compute peak of the unit it runs on: the FP32 matrix cores (157.3 TFLOP/s)
 for the dense layers, the FP32 vector FMA (157.3 TFLOP/s published; plain
@@ -72,6 +73,10 @@ COPY_CAL_BYTES = 256 << 20       # plain device copy used to calibrate FETCH_SIZ
 
 
 STEPS_DEFAULT, WARMUP_DEFAULT = 50, 5
+# Untimed calls of an operation before it is timed on its own: the matrix-core
+# kernels start ~15% slower right after memory-bound work while the shader
+# clock comes back up (the chained step's `value` keeps that cost).
+OP_WARM_CALLS = 3
 STACK_STEPS, STACK_WARMUP = 5, 2   # stack steps run for milliseconds each
 DEFAULT_WORKLOAD = "convnext_xl_w4096"
 # timed beside the default workload, each as its own record in the same line
@@ -387,7 +392,8 @@ def layer_bench(args, wl):
     # Each operation on its own: back-to-back calls between two events.
     op_us = {}
     for name, f in list(ops.items()) + list(extra_ops.items()):
-        f(sets[0])
+        for i in range(OP_WARM_CALLS):
+            f(sets[i % len(sets)])
         torch.cuda.synchronize()
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a0.record()
@@ -671,7 +677,8 @@ def grid_bench(args, wl):
     spread = step_spread(lambda k: step(), args.steps)
     op_us = {}
     for name, f in ops:
-        f()
+        for _ in range(OP_WARM_CALLS):
+            f()
         torch.cuda.synchronize()
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a0.record()
@@ -835,7 +842,8 @@ def block_bench(args, wl):
 
     rows, step_bytes, step_flops, dom = [], 0, 0, None
     for name, f, b_, f_, dense in ops:
-        f()
+        for _ in range(OP_WARM_CALLS):
+            f()
         torch.cuda.synchronize()
         reps = max(2, min(args.op_reps, 20))
         a0, a1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -1021,7 +1029,8 @@ def stack_bench(args, wl):
     # each operation on its own, back to back
     op_us = {}
     for l, name, f in ops:
-        f()
+        for _ in range(OP_WARM_CALLS):
+            f()
         torch.cuda.synchronize()
         reps = max(2, min(args.op_reps, 20))
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
