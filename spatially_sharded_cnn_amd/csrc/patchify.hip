@@ -535,21 +535,29 @@ patch_kernel(PArgs a)
 constexpr int kWideTM = 128, kWideNB = 7, kWideTN = 32 * kWideNB, kWideSeg = 512;
 constexpr int kWideAF = kWideTM * 16, kWideBF = 8 * kWideSeg, kWideST = kWideAF + kWideBF;
 
-template <int NB>
-__global__ void __launch_bounds__(kNT, 3)
+// KS = 2 (launches with no more tiles than CUs, where one 256-thread
+// workgroup per CU would leave one wave per SIMD): 512 threads, whose halves
+// take the even and the odd stages, each with its own two stage buffers;
+// at the end the second half hands its sums to the first through LDS and the
+// first adds them (the same order for every tile) and stores.
+template <int NB, int KS>
+__global__ void __launch_bounds__(kNT * KS, KS == 1 ? 3 : 2)
 wide_fwd_kernel(PArgs a, int ntot)
 {
     constexpr int TN = 32 * NB;                  // the tile's pixels
     constexpr int NH = (2 * TN + 255) / 256;     // 64-lane B loads per (channel, kh): 256 floats each
     static_assert(NB <= kWideNB, "B segments hold 512 floats");
-    __shared__ __align__(16) float lds[2 * kWideST];
+    static_assert(KS == 1 || KS == 2, "one or two reduction halves");
+    __shared__ __align__(16) float lds[2 * KS * kWideST];
     __shared__ float bias_s[kWideTM];
     const int bid = xcd_order(blockIdx.x, gridDim.x);   // output-channel tiles of one pixel tile side by side
     const int mt = bid % a.tiles_m, nt = bid / a.tiles_m;
     const int m0 = mt * kWideTM, n0 = nt * TN;
-    const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane((t >> 6) & 3);
+    const int half = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(t >> 8);
     if (t < kWideTM) bias_s[t] = (a.b && m0 + t < a.Co) ? a.b[m0 + t] : 0.f;
     const int nstage = a.Ci / 4;
+    const int njs = (nstage + KS - 1) / KS;       // iterations; iteration j is stage KS j + half
 
     // A: instruction i of wave w covers LDS units 64 (2 w + i) + lane
     const i32x4 ra = plane_rsrc(a.w, a.Co * a.Kt * 4);
@@ -576,8 +584,10 @@ wide_fwd_kernel(PArgs a, int ntot)
             bvoff[hf][kh] = ok ? (((img * a.Ci + wave) * a.H + 2 * i + kh) * a.W + 2 * j) * 4 : (int)0x80000000;
     }
     const int a_step = 64, b_step = 4 * a.H * a.W * 4;
-    auto issue = [&](int s) {
-        float* st = lds + (s & 1) * kWideST;
+    // stage KS j + half into this half's buffer j & 1
+    auto issue = [&](int j) {
+        const int s = KS * j + half;
+        float* st = lds + (2 * half + (j & 1)) * kWideST;
 #pragma unroll
         for (int i = 0; i < 2; ++i) dma16(ra, st + (2 * wave + i) * 256, avoff[i] + s * a_step);
 #pragma unroll
@@ -597,13 +607,14 @@ wide_fwd_kernel(PArgs a, int ntot)
     const int arow = (32 * wave + l32) * 4;
     const int boff = kWideAF + 2 * l32 + hi;
 
-    issue(0);
-    for (int s = 0; s < nstage; ++s) {
-        // stage s has landed (this wave's loads, then everyone's); the other buffer is free
+    if (half < nstage) issue(0);
+    for (int j = 0; j < njs; ++j) {
+        // iteration j's stage has landed (this wave's loads, then everyone's); the other buffer is free
         wait_vmem();
         lds_barrier();
-        if (s + 1 < nstage) issue(s + 1);
-        const float* st = lds + (s & 1) * kWideST;
+        if (KS * (j + 1) + half < nstage) issue(j + 1);
+        if (KS * j + half >= nstage) continue;   // the second half's last iteration when nstage is odd
+        const float* st = lds + (2 * half + (j & 1)) * kWideST;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int ao = (arow + (c ^ sw)) * 4 + hi;
@@ -621,6 +632,29 @@ wide_fwd_kernel(PArgs a, int ntot)
             for (int yb = 0; yb < NB; ++yb)
                 acc[yb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1[yb], acc[yb], 0, 0, 0);
         }
+    }
+    if constexpr (KS == 2) {
+        // the odd stages' sums into the first half: up to 4 blocks per lane and round, laid out
+        // [wave][block][register][lane] so that a wave's 64 lanes write and read 64 consecutive floats
+        lds_barrier();   // every wave is past its last products; the stage buffers are free
+#pragma unroll
+        for (int r0 = 0; r0 < NB; r0 += 4) {
+            if (half == 1) {
+#pragma unroll
+                for (int yb = r0; yb < NB && yb < r0 + 4; ++yb)
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) lds[((wave * 4 + yb - r0) * 16 + k) * 64 + lane] = acc[yb][k];
+            }
+            lds_barrier();
+            if (half == 0) {
+#pragma unroll
+                for (int yb = r0; yb < NB && yb < r0 + 4; ++yb)
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) acc[yb][k] += lds[((wave * 4 + yb - r0) * 16 + k) * 64 + lane];
+            }
+            lds_barrier();
+        }
+        if (half == 1) return;
     }
 
     // D block yb: register 4 q + r holds row 8 q + 4 hi + r of the wave's 32, column l32
@@ -1538,6 +1572,17 @@ static bool use_stem_fwd(const PArgs& a)
     return !(env && !strcmp(env, "tiled"));
 }
 
+// The wide forward with two reduction halves per workgroup (KS = 2) where the
+// tiles are no more than the CUs, so that each CU still runs two waves per
+// SIMD; SSCNN_WIDE_HALVES=1 / =0 forces the choice.
+static bool wide_halves(int tiles)
+{
+    const char* env = getenv("SSCNN_WIDE_HALVES");
+    if (env && !strcmp(env, "1")) return true;
+    if (env && !strcmp(env, "0")) return false;
+    return tiles <= cu_count();
+}
+
 static bool use_wide(int tiles, const char* var)
 {
     if (tiles == 0) return false;
@@ -1568,13 +1613,20 @@ hipError_t launch_patch_fwd(const Geom& g, const float* x, const float* w, const
     }
     if (g.k == 2 && use_wide4(a)) {
         a.tiles_m = (a.Co + kWideTM - 1) / kWideTM;
-        hipLaunchKernelGGL(wide_fwd_kernel<4>, dim3(wide_fwd_tiles(a, 4)), dim3(kNT), 0, st, a, a.N * a.P);
+        const int grid = wide_fwd_tiles(a, 4);
+        if (wide_halves(grid))
+            hipLaunchKernelGGL((wide_fwd_kernel<4, 2>), dim3(grid), dim3(2 * kNT), 0, st, a, a.N * a.P);
+        else
+            hipLaunchKernelGGL((wide_fwd_kernel<4, 1>), dim3(grid), dim3(kNT), 0, st, a, a.N * a.P);
         return hipGetLastError();
     }
     if (g.k == 2 && use_wide(wide_fwd_tiles(a), "SSCNN_PATCH_FWD")) {
         a.tiles_m = (a.Co + kWideTM - 1) / kWideTM;
         const int grid = wide_fwd_tiles(a);
-        hipLaunchKernelGGL(wide_fwd_kernel<kWideNB>, dim3(grid), dim3(kNT), 0, st, a, a.N * a.P);
+        if (wide_halves(grid))
+            hipLaunchKernelGGL((wide_fwd_kernel<kWideNB, 2>), dim3(grid), dim3(2 * kNT), 0, st, a, a.N * a.P);
+        else
+            hipLaunchKernelGGL((wide_fwd_kernel<kWideNB, 1>), dim3(grid), dim3(kNT), 0, st, a, a.N * a.P);
         return hipGetLastError();
     }
     a.tiles_n = (a.P + 127) / 128;

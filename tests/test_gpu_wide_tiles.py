@@ -39,6 +39,8 @@ CASES = [
     ("co256_ci64", 2, 64, 256, 28, 2 * 64, 2),                 # 16 reduction stages, 448 pixels per image
     ("co512_ci256_many_tiles", 7, 256, 512, 16, 4 * 64, 4),    # the stack's shape class, 7 images
     ("ci40_co32_ragged_k", 2, 40, 32, 12, 2 * 32, 2),          # K = 160 rows: a 32-row second K tile
+    ("ci12_odd_stages", 2, 12, 64, 16, 2 * 32, 2),             # 3 reduction stages: the halves take 2 and 1
+    ("ci4_one_stage", 1, 4, 32, 8, 2 * 32, 2),                 # 1 stage: the second half adds zeros
 ]
 
 
@@ -56,11 +58,17 @@ def _fwd(monkeypatch, mode, conv, x, wd, bd, push=None):
     return y
 
 
+@pytest.mark.parametrize("halves", ["1", "0"], ids=["two_halves", "one_half"])
 @pytest.mark.parametrize("wmode", ["wide", "wide4"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_wide_forward_matches_oracle_and_tiled(case, wmode, monkeypatch):
+def test_wide_forward_matches_oracle_and_tiled(case, wmode, halves, monkeypatch):
+    """The wide forward against the oracle and the tiled kernel, in both of its forms: the
+    reduction in one 256-thread half (every stage in order) and split between two halves of a
+    512-thread workgroup (even / odd stages, added at the end), which launches with no more
+    tiles than CUs take."""
     name, n, ci, co, h, w, S = case
-    _say(f"  wide fwd {name} ({wmode}): ({n},{ci},{h},{w}) -> {co} channels, {S} shards")
+    monkeypatch.setenv("SSCNN_WIDE_HALVES", halves)
+    _say(f"  wide fwd {name} ({wmode}, halves={halves}): ({n},{ci},{h},{w}) -> {co} channels, {S} shards")
     rng = np.random.default_rng(4700 + CASES.index(case))
     x = rng.standard_normal((n, ci, h, w)).astype(np.float32)
     wt = (rng.standard_normal((co, ci, 2, 2)) * 0.05).astype(np.float32)
