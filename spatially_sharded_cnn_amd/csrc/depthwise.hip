@@ -443,7 +443,7 @@ __device__ __forceinline__ void load_weights(const float* w, int c, float (&wr)[
 
 // Results leave with non-temporal stores: nothing in these kernels reads
 // them back, and streaming them past the caches took 8-16% off the forward
-// (same-box A/B, depthwise 7x7 shards of 16x32 to 128x256 planes).
+// (A/B on one GPU, depthwise 7x7 shards of 16x32 to 128x256 planes).
 template <int RH>
 __device__ __forceinline__ void store_rows(float* out, const TileIdx& d, int H, int W, int tx, int ty,
                                            const float (&acc)[RH][4])
@@ -766,7 +766,7 @@ DwShape pick_shape(int H, int W)
         // Two rows per thread where the plane is 32 or 16 rows high: each
         // input row read from LDS feeds two output rows, and the workgroups
         // get smaller (128 or 64 threads).  Against one row per thread in
-        // 256- or 128-thread groups, same-box: (7,1024,32,32) forward
+        // 256- or 128-thread groups, on one GPU: (7,1024,32,32) forward
         // 17.5 -> 15.7 us, fused backward 35.8 -> 29.8 us; (7,2048,16,32)
         // 17.8 -> 16.0 and 35.8 -> 30.9 us.
         if (H >= 32) return {8, 16, 2};

@@ -808,7 +808,7 @@ wide_bwi_kernel(PArgs a, int ntot)
 // chunks (64 KB of LDS for the two stages in flight, which the two
 // workgroups per CU that the split count aims for still fit; against one
 // chunk per stage, half the barriers per product: c5 downsample backward
-// 978/939/919 -> 953/930/908 us, same box), loaded one stage ahead; each
+// 978/939/919 -> 953/930/908 us, one GPU), loaded one stage ahead; each
 // chunk's operands:
 //   A  G[img][m0 + m][the chunk's 16 pixels]: 128 rows of 4 units, unit u of
 //      row m at slot u ^ ((m >> 2) & 3);
